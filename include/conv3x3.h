@@ -1,0 +1,144 @@
+/*
+ * conv3x3.h -- C ABI of the MI355X (gfx950) pad-1 3x3 / 3x3x3 convolution library.
+ *
+ * The operation (cited by page title and section):
+ *   2D  [musetalk-bench patches/taesd_conv.cuh.new, header comment and taesd_conv3x3_impl]:
+ *       y[n,co,oh,ow] = E( b[co] + sum_{ci,ky,kx} w[co,ci,ky,kx] * X[n,ci, s*oh-1+ky, s*ow-1+kx] )
+ *   3D  [FastVideo fastvideo-kernel/wan22_vae_decode/solution/head.cu, header comment: the
+ *       27-tap output convolution]:
+ *       y[n,co,d,oh,ow] = E( b[co] + sum_{ci,kd,ky,kx} w[co,ci,kd,ky,kx]
+ *                                        * X[n,ci, d-1+kd, s*oh-1+ky, s*ow-1+kx] )
+ *   X is zero outside the tensor (pad 1 in every convolved dimension; one zero frame at each
+ *   temporal end, so D_out = D).  Cross-correlation (no kernel flip).  H_out = (H-1)/s + 1 and
+ *   W_out likewise (integer division).  b = 0 when bias is NULL.  E is the fused epilogue:
+ *   identity, ReLU (v < 0 ? 0 : v) or clamp to [-1, 1].  Inputs, weights, bias and outputs are
+ *   fp16 or bf16; products are accumulated in fp32 and rounded once, to nearest-even, on the
+ *   store -- except the split head (CONV_ALGO_SPLIT_HEAD), which rounds the 3x1x1 temporal
+ *   partial sums to the activation dtype once in its intermediate plane, as the head.cu page
+ *   describes for its value path.
+ *
+ * Conventions
+ *   - Every pointer is a device pointer the caller allocated (the library allocates no device
+ *     memory and keeps no per-call state; calls are thread-safe).  x, w/w_packed, y and the
+ *     workspace must be 16-byte aligned; bias 2-byte aligned.  x and y must not overlap.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work is enqueued
+ *     on it and the call returns without synchronising.  Multi-launch algorithms order their
+ *     launches on that stream.
+ *   - All argument checks happen before anything is enqueued; on error nothing is launched
+ *     and conv_last_error() returns a message.  A kernel fault surfaces at the caller's next
+ *     synchronisation, as with any HIP launch.
+ *   - An empty output (N, C_out, D, H or W equal to 0) is a no-op that returns CONV_OK.
+ */
+#ifndef CONV3X3_H_
+#define CONV3X3_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CONV_ABI_VERSION 1
+
+/* storage dtypes */
+enum { CONV_DTYPE_F16 = 0, CONV_DTYPE_BF16 = 1 };
+/* layouts: 2D channels-first = NCHW, channels-last = NHWC;
+ *          3D channels-first = NCDHW, channels-last = NDHWC */
+enum { CONV_LAYOUT_CHANNELS_FIRST = 0, CONV_LAYOUT_CHANNELS_LAST = 1 };
+/* fused epilogues (applied after the bias) */
+enum { CONV_EPI_NONE = 0, CONV_EPI_RELU = 1, CONV_EPI_CLAMP1 = 2 };
+/* algorithms.  AUTO resolves deterministically from the shape (conv3x3x3_select_algo).
+ *   SIMT        2D: direct LDS-halo kernel on the vector ALUs (fp32 accumulation via dot2).
+ *   MFMA        3D: implicit GEMM on the matrix cores, 27 taps in one fp32 accumulator.
+ *   SPLIT_HEAD  3D, C_out <= 12, stride 1: 3x1x1 temporal conv into 9*C_out tap channels of a
+ *               112-channel bf16/fp16 plane in the workspace, then a nine-tap stencil + bias +
+ *               epilogue [head.cu, header comment and head_stencil_kernel]. */
+enum {
+    CONV_ALGO_AUTO = 0,
+    CONV_ALGO_SIMT = 1,
+    CONV_ALGO_MFMA = 2,
+    CONV_ALGO_SPLIT_HEAD = 3
+};
+/* status codes */
+enum {
+    CONV_OK = 0,
+    CONV_E_INVAL = -1,       /* bad pointer, size, enum, alignment or overlap */
+    CONV_E_UNSUPPORTED = -2, /* valid request this library does not implement */
+    CONV_E_WORKSPACE = -3,   /* workspace missing or smaller than the query returned */
+    CONV_E_NODEVICE = -4,    /* no HIP device visible */
+    CONV_E_LAUNCH = -5       /* the HIP runtime rejected a launch */
+};
+
+/* ABI version of the loaded library (CONV_ABI_VERSION it was built with). */
+int conv_abi_version(void);
+
+/* Static text for a status code. */
+const char *conv_status_str(int status);
+
+/* Detail of the last error on the calling thread ("" after a successful call). */
+const char *conv_last_error(void);
+
+/* Output extent of a pad-1, 3-tap dimension: (in-1)/stride + 1 for in >= 1; 0 for in == 0;
+ * -1 for a negative size or a stride outside {1, 2}. */
+int conv_out_size(int in, int stride);
+
+/* ------------------------------------------------------------------------------------------
+ * 2D: x (N,C_in,H,W) NCHW, w (C_out,C_in,3,3) OIHW as stored by PyTorch (no packing), bias
+ * (C_out) or NULL, y (N,C_out,H_out,W_out) NCHW; all of `dtype`.  stride 1 or 2.
+ * Supported: layout CHANNELS_FIRST, dtype F16 or BF16, algo AUTO or SIMT, any C_in/C_out >= 1.
+ * [taesd_conv.cuh.new: operator contract in the header comment; the kernels' argument lists]
+ * ---------------------------------------------------------------------------------------- */
+int conv3x3_fwd(const void *x, const void *w, const void *bias, void *y, int N, int C_in,
+                int C_out, int H, int W, int stride, int layout, int dtype, int epilogue,
+                int algo, void *stream);
+
+/* CONV_OK if conv3x3_fwd would accept this request (pointers aside), else the status it
+ * would return. */
+int conv3x3_is_supported(int N, int C_in, int C_out, int H, int W, int stride, int layout,
+                         int dtype, int epilogue, int algo);
+
+/* ------------------------------------------------------------------------------------------
+ * 3D: x (N,D,H,W,C_in) NDHWC, w_packed from conv3x3x3_pack_weights, bias (C_out) or NULL,
+ * y (N,D,H_out,W_out,C_out) NDHWC.  Supported: layout CHANNELS_LAST, dtype BF16 or F16,
+ * stride 1 (stride 2 returns CONV_E_UNSUPPORTED), C_in a multiple of 8.
+ *   algo MFMA: any C_out >= 1.  algo SPLIT_HEAD: C_out <= 12.  AUTO: see select_algo.
+ * workspace: at least conv3x3x3_workspace_bytes(...) bytes (may be NULL when that is 0).
+ * The same (shape, dtype, algo) arguments must be given to the size queries, to
+ * conv3x3x3_pack_weights and to conv3x3x3_fwd.
+ * ---------------------------------------------------------------------------------------- */
+int conv3x3x3_fwd(const void *x, const void *w_packed, const void *bias, void *y, int N,
+                  int C_in, int C_out, int D, int H, int W, int stride, int layout, int dtype,
+                  int epilogue, int algo, void *workspace, size_t workspace_bytes, void *stream);
+
+/* The concrete algorithm conv3x3x3_fwd runs for `algo` (AUTO resolved), or a negative status
+ * if the request is unsupported. */
+int conv3x3x3_select_algo(int N, int C_in, int C_out, int D, int H, int W, int stride,
+                          int layout, int dtype, int algo);
+
+/* CONV_OK if conv3x3x3_fwd would accept this request (pointers aside), else its status. */
+int conv3x3x3_is_supported(int N, int C_in, int C_out, int D, int H, int W, int stride,
+                           int layout, int dtype, int epilogue, int algo);
+
+/* Bytes of workspace conv3x3x3_fwd needs: the split head's intermediate plane
+ * (N*D*H*W*112 elements of dtype), the split-K partial sums of the MFMA path for small
+ * position counts (fp32), or 0.  Returns 0 for an unsupported request as well. */
+size_t conv3x3x3_workspace_bytes(int N, int C_in, int C_out, int D, int H, int W, int stride,
+                                 int layout, int dtype, int algo);
+
+/* Bytes of the packed weight buffer for this request (0 if unsupported). */
+size_t conv3x3x3_packed_weight_bytes(int N, int C_in, int C_out, int D, int H, int W,
+                                     int stride, int layout, int dtype, int algo);
+
+/* One-time repack of PyTorch Conv3d weights w_oidhw (C_out,C_in,3,3,3) of `dtype` (device
+ * memory) into w_packed (device memory of conv3x3x3_packed_weight_bytes bytes), enqueued on
+ * `stream`.  Weights are constant across passes, so this runs outside the timed pass. */
+int conv3x3x3_pack_weights(const void *w_oidhw, void *w_packed, int N, int C_in, int C_out,
+                           int D, int H, int W, int stride, int layout, int dtype, int algo,
+                           void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONV3X3_H_ */

@@ -1,0 +1,178 @@
+"""The C ABI on the host: the library loads, exports every entry point its header declares, and
+rejects every invalid request before it enqueues anything.  No compute calls (no GPU needed);
+fake device addresses are only passed on paths that fail validation or return before a launch.
+"""
+import os
+import re
+
+import pytest
+import torch
+
+import x3x3_convolution_amd as cx
+from x3x3_convolution_amd import conv as C
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "conv3x3.h")
+
+A = 1 << 20           # a fake, 16-byte aligned "device address" (never dereferenced)
+B = 1 << 30
+WS = 1 << 34
+HAS_GPU = torch.cuda.device_count() > 0
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(conv\w*)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = cx.library()
+    declared = header_functions()
+    assert len(declared) >= 12
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(n for n, _, _ in C.EXPORTS) == declared
+
+
+def test_version_and_status_strings():
+    assert cx.conv_abi_version() == C.ABI_VERSION == 1
+    for st in (C.OK, C.E_INVAL, C.E_UNSUPPORTED, C.E_WORKSPACE, C.E_NODEVICE, C.E_LAUNCH):
+        assert cx.conv_status_str(st) not in ("", "unknown status")
+    assert cx.conv_status_str(12345) == "unknown status"
+
+
+def test_out_size():
+    for n in range(0, 40):
+        for s in (1, 2):
+            assert cx.conv_out_size(n, s) == (0 if n == 0 else (n - 1) // s + 1)
+    assert cx.conv_out_size(256, 2) == 128 and cx.conv_out_size(255, 2) == 128
+    assert cx.conv_out_size(-1, 1) == -1 and cx.conv_out_size(5, 3) == -1
+
+
+def _st(fn, *a):
+    try:
+        fn(*a)
+    except C.ConvError as e:
+        return e.status
+    return C.OK
+
+
+def f2d(**kw):
+    a = dict(x=A, w=B, bias=None, y=A + (1 << 28), N=1, C_in=16, C_out=16, H=8, W=8, stride=1,
+             layout=0, dtype=0, epilogue=1, algo=0, stream=0)
+    a.update(kw)
+    return _st(cx.conv3x3_fwd, a["x"], a["w"], a["bias"], a["y"], a["N"], a["C_in"], a["C_out"],
+               a["H"], a["W"], a["stride"], a["layout"], a["dtype"], a["epilogue"], a["algo"],
+               a["stream"])
+
+
+def f3d(**kw):
+    a = dict(x=A, w=B, bias=None, y=A + (1 << 28), N=1, C_in=32, C_out=12, D=2, H=8, W=8,
+             stride=1, layout=1, dtype=1, epilogue=2, algo=C.ALGO_MFMA, ws=None, wsb=0,
+             stream=0)
+    a.update(kw)
+    return _st(cx.conv3x3x3_fwd, a["x"], a["w"], a["bias"], a["y"], a["N"], a["C_in"],
+               a["C_out"], a["D"], a["H"], a["W"], a["stride"], a["layout"], a["dtype"],
+               a["epilogue"], a["algo"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_2d_invalid_arguments():
+    assert f2d(x=None) == C.E_INVAL
+    assert f2d(w=None) == C.E_INVAL
+    assert f2d(y=None) == C.E_INVAL
+    assert f2d(stride=3) == C.E_INVAL
+    assert f2d(stride=0) == C.E_INVAL
+    assert f2d(dtype=7) == C.E_INVAL
+    assert f2d(epilogue=3) == C.E_INVAL
+    assert f2d(layout=5) == C.E_INVAL
+    assert f2d(algo=9) == C.E_INVAL
+    assert f2d(N=-1) == C.E_INVAL
+    assert f2d(C_in=0) == C.E_INVAL
+    assert f2d(x=A + 2) == C.E_INVAL            # misaligned
+    assert f2d(bias=A + 1) == C.E_INVAL         # misaligned bias
+    assert f2d(y=A + 64) == C.E_INVAL           # overlaps x
+    assert "overlap" in cx.conv_last_error()
+    assert f2d(layout=1) == C.E_UNSUPPORTED     # NHWC
+    assert f2d(algo=C.ALGO_MFMA) == C.E_UNSUPPORTED
+    assert f2d(algo=C.ALGO_SPLIT_HEAD) == C.E_UNSUPPORTED
+
+
+def test_2d_empty_is_noop():
+    for kw in (dict(N=0), dict(C_out=0), dict(H=0), dict(W=0)):
+        assert f2d(x=None, y=None, **kw) == C.OK
+
+
+def test_3d_invalid_and_unsupported():
+    assert f3d(x=None) == C.E_INVAL
+    assert f3d(w=None) == C.E_INVAL
+    assert f3d(y=None) == C.E_INVAL
+    assert f3d(epilogue=-1) == C.E_INVAL
+    assert f3d(algo=17) == C.E_INVAL
+    assert f3d(D=-2) == C.E_INVAL
+    assert f3d(C_in=0) == C.E_INVAL
+    assert f3d(y=A + 16) == C.E_INVAL
+    assert f3d(w=B + 8) == C.E_INVAL
+    assert f3d(layout=0) == C.E_UNSUPPORTED     # NCDHW
+    assert f3d(stride=2) == C.E_UNSUPPORTED
+    assert f3d(C_in=20) == C.E_UNSUPPORTED      # not a multiple of 8
+    assert f3d(algo=C.ALGO_SIMT) == C.E_UNSUPPORTED
+    assert f3d(algo=C.ALGO_SPLIT_HEAD, C_out=13) == C.E_UNSUPPORTED
+    # the split head needs its plane in the workspace
+    assert f3d(algo=C.ALGO_SPLIT_HEAD) == C.E_WORKSPACE
+    need = cx.conv3x3x3_workspace_bytes(1, 32, 12, 2, 8, 8, 1, 1, 1, C.ALGO_SPLIT_HEAD)
+    assert need == 2 * 8 * 8 * 112 * 2
+    assert f3d(algo=C.ALGO_SPLIT_HEAD, ws=WS, wsb=need - 1) == C.E_WORKSPACE
+    assert f3d(algo=C.ALGO_SPLIT_HEAD, ws=WS + 4, wsb=need) == C.E_INVAL   # misaligned
+    assert f3d(algo=C.ALGO_SPLIT_HEAD, ws=A, wsb=need) == C.E_INVAL        # overlaps x
+
+
+def test_3d_empty_is_noop():
+    for kw in (dict(N=0), dict(C_out=0), dict(D=0), dict(H=0), dict(W=0)):
+        assert f3d(x=None, y=None, w=None, **kw) == C.OK
+
+
+def test_is_supported_matches_fwd_checks():
+    assert cx.conv3x3_is_supported(8, 64, 64, 256, 256, 2, 0, 0, 1, 0) == C.OK
+    assert cx.conv3x3_is_supported(8, 64, 64, 256, 256, 2, 1, 0, 1, 0) == C.E_UNSUPPORTED
+    assert cx.conv3x3x3_is_supported(1, 256, 12, 16, 352, 624, 1, 1, 1, 2, 0) == C.OK
+    assert cx.conv3x3x3_is_supported(1, 256, 12, 16, 352, 624, 1, 1, 1, 2, C.ALGO_SPLIT_HEAD) == C.OK
+    assert cx.conv3x3x3_is_supported(1, 256, 256, 16, 176, 312, 1, 1, 1, 0, C.ALGO_SPLIT_HEAD) == C.E_UNSUPPORTED
+    assert cx.conv3x3x3_is_supported(1, 256, 256, 16, 176, 312, 2, 1, 1, 0, 0) == C.E_UNSUPPORTED
+
+
+def test_algo_selection_and_buffer_sizes():
+    # the output head: AUTO resolves to a concrete algorithm; split head needs its plane
+    a = cx.conv3x3x3_select_algo(1, 256, 12, 16, 352, 624, 1, 1, 1, 0)
+    assert a in (C.ALGO_MFMA, C.ALGO_SPLIT_HEAD)
+    assert cx.conv3x3x3_workspace_bytes(1, 256, 12, 16, 352, 624, 1, 1, 1,
+                                        C.ALGO_SPLIT_HEAD) == 787218432
+    # packed weights: 8 channel chunks x 27 taps x 16 rows x 32 (direct head)
+    assert cx.conv3x3x3_packed_weight_bytes(1, 256, 12, 16, 352, 624, 1, 1, 1,
+                                            C.ALGO_MFMA) == 8 * 27 * 16 * 32 * 2
+    # split head: 8 chunks x 3 temporal taps x 112 rows x 32
+    assert cx.conv3x3x3_packed_weight_bytes(1, 256, 12, 16, 352, 624, 1, 1, 1,
+                                            C.ALGO_SPLIT_HEAD) == 8 * 3 * 112 * 32 * 2
+    # mid-decoder conv fills the chip without split-K: no workspace
+    assert cx.conv3x3x3_workspace_bytes(1, 256, 256, 16, 176, 312, 1, 1, 1, 0) == 0
+    # the small low-res conv splits K over channel chunks: fp32 partials
+    ws = cx.conv3x3x3_workspace_bytes(1, 512, 512, 4, 44, 78, 1, 1, 1, 0)
+    assert ws > 0 and ws % (4 * 44 * 78 * 512 * 4) == 0
+    assert cx.conv3x3x3_workspace_bytes(1, 512, 512, 4, 44, 78, 1, 1, 1, 9) == 0  # invalid
+    assert cx.conv3x3x3_packed_weight_bytes(1, 20, 12, 1, 4, 4, 1, 1, 1, 0) == 0  # unsupported
+
+
+def test_pack_invalid():
+    st = _st(cx.conv3x3x3_pack_weights, None, B, 1, 32, 12, 2, 8, 8, 1, 1, 1, 0, 0)
+    assert st == C.E_INVAL
+    st = _st(cx.conv3x3x3_pack_weights, A, B + 8, 1, 32, 12, 2, 8, 8, 1, 1, 1, 0, 0)
+    assert st == C.E_INVAL
+    st = _st(cx.conv3x3x3_pack_weights, A, A, 1, 32, 12, 2, 8, 8, 1, 1, 1, 0, 0)
+    assert st == C.E_INVAL
+
+
+@pytest.mark.skipif(HAS_GPU, reason="checks the no-device path; a GPU is visible")
+def test_no_device_reported_after_validation():
+    assert f2d() == C.E_NODEVICE
+    assert f3d() == C.E_NODEVICE
+    assert "device" in cx.conv_last_error()

@@ -1,0 +1,171 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on an MI355X.
+
+* integer-valued inputs: every partial sum is exact in fp32 and in the storage dtype, so every
+  kernel must reproduce the oracle bit for bit (index, halo, padding, tail and race bugs show);
+* random inputs at small sizes spanning several tiles and ragged tails: full tensors within the
+  fp16/bf16 tolerances;
+* the workloads at full size, in the launch configuration the benchmark times: sampled outputs
+  within the tolerances, plus guard-band / NaN-poison and run-twice determinism checks.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic_inputs as si
+from gpu_support import (DEV, assert_bit_exact, assert_within, bits, gather_2d, gather_3d,
+                         metrics, oracle_2d, oracle_3d, run_2d, run_3d, sample_points_2d,
+                         sample_points_3d)
+from x3x3_convolution_amd import conv as C
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# ------------------------------------------------------------------------------------------
+# integer-exact parity
+# ------------------------------------------------------------------------------------------
+CASES_2D_INT = [
+    # N, Ci, Co, H, W, stride, dtype, epilogue
+    (1, 16, 16, 64, 64, 1, "f16", "relu"),
+    (2, 5, 7, 13, 37, 1, "f16", "none"),
+    (2, 5, 7, 13, 37, 2, "f16", "clamp1"),
+    (1, 64, 64, 19, 45, 1, "bf16", "relu"),
+    (1, 33, 40, 20, 70, 2, "f16", "relu"),
+    (3, 3, 130, 9, 10, 1, "bf16", "none"),
+    (1, 17, 24, 33, 1, 2, "f16", "none"),
+    (1, 1, 1, 1, 1, 1, "f16", "relu"),
+    (2, 64, 64, 32, 64, 2, "f16", "relu"),
+]
+
+
+@pytest.mark.parametrize("case", CASES_2D_INT, ids=[str(c) for c in CASES_2D_INT])
+def test_simt2d_integer_exact(case):
+    N, Ci, Co, H, W, s, dt, epi = case
+    _say("simt2d int %s" % (case,))
+    x, w, b = si.integer_case("2d", N, Ci, Co, H, W, dtype=dt, seed=CASES_2D_INT.index(case),
+                              device=DEV)
+    y = run_2d(x, w, b, s, epi, guarded=True)
+    assert_bit_exact(y, oracle_2d(x, w, b, s, epi), x.dtype)
+
+
+CASES_3D_INT = [
+    # N, Ci, Co, D, H, W, dtype, epilogue, algo
+    (1, 32, 12, 3, 9, 35, "bf16", "clamp1", C.ALGO_MFMA),
+    (2, 40, 20, 2, 11, 19, "bf16", "none", C.ALGO_MFMA),
+    (1, 8, 1, 1, 5, 5, "bf16", "relu", C.ALGO_MFMA),
+    (1, 64, 130, 4, 9, 17, "f16", "none", C.ALGO_MFMA),
+    (1, 8, 12, 16, 128, 128, "bf16", "clamp1", C.ALGO_MFMA),     # no split-K, narrow tiles
+    (1, 8, 129, 16, 64, 64, "bf16", "relu", C.ALGO_MFMA),        # no split-K, wide tiles
+    (1, 32, 12, 3, 9, 50, "bf16", "clamp1", C.ALGO_SPLIT_HEAD),
+    (2, 64, 5, 1, 7, 130, "bf16", "none", C.ALGO_SPLIT_HEAD),
+    (1, 8, 12, 4, 70, 64, "f16", "clamp1", C.ALGO_SPLIT_HEAD),
+    (1, 16, 12, 16, 40, 100, "bf16", "relu", C.ALGO_SPLIT_HEAD),
+]
+
+
+@pytest.mark.parametrize("case", CASES_3D_INT, ids=[str(c) for c in CASES_3D_INT])
+def test_conv3d_integer_exact(case):
+    N, Ci, Co, D, H, W, dt, epi, algo = case
+    _say("conv3d int %s" % (case,))
+    x, w, b = si.integer_case("3d", N, Ci, Co, H, W, D=D, dtype=dt, seed=CASES_3D_INT.index(case),
+                              device=DEV)
+    y = run_3d(x, w, b, epi, algo, guarded=True)
+    assert_bit_exact(y, oracle_3d(x, w, b, epi), x.dtype)
+
+
+def test_conv3d_no_bias_integer_exact():
+    x, w, _ = si.integer_case("3d", 1, 32, 12, 5, 9, D=2, dtype="bf16", seed=3, device=DEV,
+                              with_bias=False)
+    for algo in (C.ALGO_MFMA, C.ALGO_SPLIT_HEAD):
+        y = run_3d(x, w, None, "clamp1", algo)
+        assert_bit_exact(y, oracle_3d(x, w, None, "clamp1"), x.dtype)
+    x, w, _ = si.integer_case("2d", 2, 6, 9, 11, 13, dtype="f16", seed=4, device=DEV,
+                              with_bias=False)
+    y = run_2d(x, w, None, 1, "relu")
+    assert_bit_exact(y, oracle_2d(x, w, None, 1, "relu"), x.dtype)
+
+
+# ------------------------------------------------------------------------------------------
+# random inputs at small sizes, whole tensors within tolerance
+# ------------------------------------------------------------------------------------------
+def test_simt2d_random_tolerance():
+    for s in (1, 2):
+        x, w, b = si.random_case("2d", 2, 64, 64, 40, 72, dtype="f16", seed=s, device=DEV)
+        x = torch.relu(x)
+        y = run_2d(x, w, b, s, "relu")
+        m = metrics(bits(y), oracle_2d(x, w, b, s, "relu"), x.dtype)
+        _say("simt2d random s=%d %s" % (s, m))
+        assert_within(m, activated=True)
+
+
+@pytest.mark.parametrize("algo", [C.ALGO_MFMA, C.ALGO_SPLIT_HEAD])
+def test_head_random_tolerance(algo):
+    x, w, b = si.random_case("3d", 1, 256, 12, 12, 40, D=3, dtype="bf16", seed=5, device=DEV)
+    y = run_3d(x, w, b, "clamp1", algo)
+    m = metrics(bits(y), oracle_3d(x, w, b, "clamp1"), x.dtype)
+    _say("head random algo=%d %s" % (algo, m))
+    assert_within(m, activated=True)
+
+
+@pytest.mark.parametrize("Ci,Co,D,H,W", [(256, 64, 3, 10, 20), (512, 512, 2, 6, 10)])
+def test_mfma_random_tolerance(Ci, Co, D, H, W):
+    x, w, b = si.random_case("3d", 1, Ci, Co, H, W, D=D, dtype="bf16", seed=6, device=DEV)
+    y = run_3d(x, w, b, "none", C.ALGO_MFMA)
+    m = metrics(bits(y), oracle_3d(x, w, b, "none"), x.dtype)
+    _say("mfma random %s %s" % ((Ci, Co, D, H, W), m))
+    assert_within(m, activated=False)
+
+
+# ------------------------------------------------------------------------------------------
+# the workloads at full size
+# ------------------------------------------------------------------------------------------
+def test_c1_full_tensor():
+    wl = si.WORKLOADS["c1"]
+    x, w, b = si.make_inputs(wl, device=DEV)
+    y = run_2d(x, w, b, wl.stride, wl.epilogue, guarded=True)
+    m = metrics(bits(y), oracle_2d(x, w, b, wl.stride, wl.epilogue), x.dtype)
+    _say("c1 %s" % m)
+    assert_within(m, activated=True)
+
+
+@pytest.mark.parametrize("name", ["c2", "c2s2"])
+def test_c2_full_size_sampled(name):
+    wl = si.WORKLOADS[name]
+    x, w, b = si.make_inputs(wl, device=DEV)
+    y = run_2d(x, w, b, wl.stride, wl.epilogue, guarded=True)
+    y2 = run_2d(x, w, b, wl.stride, wl.epilogue)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "not deterministic"
+    pts = sample_points_2d(wl.N, wl.H_out, wl.W_out, 400, seed=1)
+    ref = oracle.conv2d_points(bits(x), bits(w), bits(b), pts, wl.stride, oracle.F16,
+                               oracle.EPI_RELU, oracle.CHANNELS_FIRST)
+    m = metrics(gather_2d(y, pts), ref, x.dtype)
+    _say("%s sampled %d %s" % (name, len(pts), m))
+    assert_within(m, activated=True)
+
+
+@pytest.mark.parametrize("name,algo", [("c3", C.ALGO_MFMA), ("c3", C.ALGO_SPLIT_HEAD),
+                                       ("c4", C.ALGO_MFMA), ("c5", C.ALGO_MFMA),
+                                       ("c5d1", C.ALGO_MFMA)])
+def test_3d_full_size_sampled(name, algo):
+    wl = si.WORKLOADS[name]
+    _say("full size %s algo %d" % (name, algo))
+    x, w, b = si.make_inputs(wl, device=DEV)
+    y = run_3d(x, w, b, wl.epilogue, algo, guarded=True)
+    y2 = run_3d(x, w, b, wl.epilogue, algo)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "not deterministic"
+    del y2
+    n_rand = 300 if wl.C_out * wl.C_in <= 256 * 256 else 120
+    pts = sample_points_3d(wl.N, wl.D, wl.H, wl.W, n_rand, seed=2)
+    epi = {"none": oracle.EPI_NONE, "relu": oracle.EPI_RELU, "clamp1": oracle.EPI_CLAMP1}
+    ref = oracle.conv3d_points(bits(x), bits(w), bits(b), pts, 1, oracle.BF16,
+                               epi[wl.epilogue], oracle.CHANNELS_LAST)
+    m = metrics(gather_3d(y, pts), ref, x.dtype)
+    _say("%s algo %d sampled %d %s" % (name, algo, len(pts), m))
+    assert_within(m, activated=wl.epilogue != "none")

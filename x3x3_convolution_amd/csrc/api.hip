@@ -1,0 +1,284 @@
+// The C ABI (include/conv3x3.h): argument validation, algorithm selection and dispatch to the
+// gfx950 kernels.  Nothing is enqueued unless every check passes; errors carry a thread-local
+// message (the role the TORCH_CHECK strings play in FastVideo head.cu's head_stencil wrapper).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/conv3x3.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return CONV_OK;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+int device_present() {
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+        (void)hipGetLastError();  // clear the sticky "no device" error
+        return fail(CONV_E_NODEVICE, "no HIP device is visible");
+    }
+    return CONV_OK;
+}
+
+int check_common(int stride, int layout, int dtype, int epilogue) {
+    if (stride != 1 && stride != 2) return fail(CONV_E_INVAL, "stride must be 1 or 2 (got %d)", stride);
+    if (layout != CONV_LAYOUT_CHANNELS_FIRST && layout != CONV_LAYOUT_CHANNELS_LAST)
+        return fail(CONV_E_INVAL, "unknown layout %d", layout);
+    if (dtype != CONV_DTYPE_F16 && dtype != CONV_DTYPE_BF16)
+        return fail(CONV_E_INVAL, "unknown dtype %d", dtype);
+    if (epilogue < CONV_EPI_NONE || epilogue > CONV_EPI_CLAMP1)
+        return fail(CONV_E_INVAL, "unknown epilogue %d", epilogue);
+    return CONV_OK;
+}
+
+// ---- 2D ------------------------------------------------------------------------------------
+int check_2d(int N, int C_in, int C_out, int H, int W, int stride, int layout, int dtype,
+             int epilogue, int algo) {
+    int st = check_common(stride, layout, dtype, epilogue);
+    if (st) return st;
+    if (N < 0 || C_out < 0 || H < 0 || W < 0)
+        return fail(CONV_E_INVAL, "negative size (N=%d C_out=%d H=%d W=%d)", N, C_out, H, W);
+    if (C_in < 1) return fail(CONV_E_INVAL, "C_in must be >= 1 (got %d)", C_in);
+    if (algo != CONV_ALGO_AUTO && algo != CONV_ALGO_SIMT) {
+        if (algo < CONV_ALGO_AUTO || algo > CONV_ALGO_SPLIT_HEAD)
+            return fail(CONV_E_INVAL, "unknown algo %d", algo);
+        return fail(CONV_E_UNSUPPORTED, "2D convolution supports algo AUTO or SIMT (got %d)", algo);
+    }
+    if (layout != CONV_LAYOUT_CHANNELS_FIRST)
+        return fail(CONV_E_UNSUPPORTED, "2D convolution supports the NCHW layout only");
+    const long long ho = (H - 1) / stride + 1, wo = (W - 1) / stride + 1;
+    if ((long long)N * ((H + 31) / 32 + 1) * ((W + 31) / 32 + 1) * ((C_out + 15) / 16 + 1) >= (1ll << 31))
+        return fail(CONV_E_UNSUPPORTED, "problem too large for one launch");
+    (void)ho;
+    (void)wo;
+    return CONV_OK;
+}
+
+// ---- 3D ------------------------------------------------------------------------------------
+constexpr int kSplitHeadMaxCout = 12;  // 9 * C_out tap channels must fit the 112-channel plane
+
+int select_3d(int N, int C_in, int C_out, int D, int H, int W, int stride, int layout, int dtype,
+              int algo) {
+    int st = check_common(stride, layout, dtype, CONV_EPI_NONE);
+    if (st) return st;
+    if (N < 0 || C_out < 0 || D < 0 || H < 0 || W < 0)
+        return fail(CONV_E_INVAL, "negative size (N=%d C_out=%d D=%d H=%d W=%d)", N, C_out, D, H, W);
+    if (C_in < 1) return fail(CONV_E_INVAL, "C_in must be >= 1 (got %d)", C_in);
+    if (algo < CONV_ALGO_AUTO || algo > CONV_ALGO_SPLIT_HEAD)
+        return fail(CONV_E_INVAL, "unknown algo %d", algo);
+    if (layout != CONV_LAYOUT_CHANNELS_LAST)
+        return fail(CONV_E_UNSUPPORTED, "3D convolution supports the NDHWC layout only");
+    if (stride != 1) return fail(CONV_E_UNSUPPORTED, "3D convolution supports stride 1 only");
+    if (C_in % 8 != 0)
+        return fail(CONV_E_UNSUPPORTED, "3D convolution needs C_in a multiple of 8 (got %d)", C_in);
+    if (algo == CONV_ALGO_SIMT)
+        return fail(CONV_E_UNSUPPORTED, "3D convolution has no SIMT algorithm");
+    if (algo == CONV_ALGO_SPLIT_HEAD && C_out > kSplitHeadMaxCout)
+        return fail(CONV_E_UNSUPPORTED, "SPLIT_HEAD needs C_out <= %d (got %d)", kSplitHeadMaxCout, C_out);
+    const long long pos = (long long)N * D * H * W;
+    if (pos >= (1ll << 31) / 8 || (long long)C_out * 27 * C_in >= (1ll << 31))
+        return fail(CONV_E_UNSUPPORTED, "problem too large for one launch");
+    if (algo == CONV_ALGO_AUTO) return CONV_ALGO_MFMA;
+    return algo;
+}
+
+int family_for(int algo, int C_out) {
+    if (algo == CONV_ALGO_SPLIT_HEAD) return cx::IG_TEMPORAL;
+    return C_out <= 16 ? cx::IG_NARROW : cx::IG_WIDE;
+}
+
+size_t elem_bytes() { return 2; }
+
+}  // namespace
+
+extern "C" {
+
+int conv_abi_version(void) { return CONV_ABI_VERSION; }
+
+const char *conv_status_str(int status) {
+    switch (status) {
+        case CONV_OK: return "ok";
+        case CONV_E_INVAL: return "invalid argument";
+        case CONV_E_UNSUPPORTED: return "unsupported request";
+        case CONV_E_WORKSPACE: return "workspace missing or too small";
+        case CONV_E_NODEVICE: return "no HIP device";
+        case CONV_E_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+const char *conv_last_error(void) { return g_err; }
+
+int conv_out_size(int in, int stride) {
+    if (in < 0 || (stride != 1 && stride != 2)) return -1;
+    if (in == 0) return 0;
+    return (in - 1) / stride + 1;
+}
+
+int conv3x3_is_supported(int N, int C_in, int C_out, int H, int W, int stride, int layout,
+                         int dtype, int epilogue, int algo) {
+    const int st = check_2d(N, C_in, C_out, H, W, stride, layout, dtype, epilogue, algo);
+    return st ? st : ok();
+}
+
+int conv3x3_fwd(const void *x, const void *w, const void *bias, void *y, int N, int C_in,
+                int C_out, int H, int W, int stride, int layout, int dtype, int epilogue,
+                int algo, void *stream) {
+    int st = check_2d(N, C_in, C_out, H, W, stride, layout, dtype, epilogue, algo);
+    if (st) return st;
+    if (N == 0 || C_out == 0 || H == 0 || W == 0) return ok();
+    const int Ho = (H - 1) / stride + 1, Wo = (W - 1) / stride + 1;
+    if (!x || !w || !y) return fail(CONV_E_INVAL, "x, w and y must be non-NULL");
+    if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16))
+        return fail(CONV_E_INVAL, "x, w and y must be 16-byte aligned");
+    if (bias && !aligned(bias, 2)) return fail(CONV_E_INVAL, "bias must be 2-byte aligned");
+    const size_t xb = (size_t)N * C_in * H * W * elem_bytes();
+    const size_t yb = (size_t)N * C_out * Ho * Wo * elem_bytes();
+    if (overlaps(x, xb, y, yb)) return fail(CONV_E_INVAL, "x and y overlap (in-place is unsupported)");
+    if (overlaps(w, (size_t)C_out * C_in * 9 * elem_bytes(), y, yb))
+        return fail(CONV_E_INVAL, "w and y overlap");
+    if (bias && overlaps(bias, (size_t)C_out * elem_bytes(), y, yb))
+        return fail(CONV_E_INVAL, "bias and y overlap");
+    st = device_present();
+    if (st) return st;
+    cx::Simt2dParams p{};
+    p.x = x, p.w = w, p.bias = bias, p.y = y;
+    p.N = N, p.C_in = C_in, p.C_out = C_out, p.H = H, p.W = W, p.Hout = Ho, p.Wout = Wo;
+    p.stride = stride, p.bf16 = dtype == CONV_DTYPE_BF16, p.epilogue = epilogue;
+    const hipError_t e = cx::launch_simt2d(p, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(CONV_E_LAUNCH, "SIMT 2D launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int conv3x3x3_select_algo(int N, int C_in, int C_out, int D, int H, int W, int stride,
+                          int layout, int dtype, int algo) {
+    const int a = select_3d(N, C_in, C_out, D, H, W, stride, layout, dtype, algo);
+    if (a < 0) return a;
+    ok();
+    return a;
+}
+
+int conv3x3x3_is_supported(int N, int C_in, int C_out, int D, int H, int W, int stride,
+                           int layout, int dtype, int epilogue, int algo) {
+    if (epilogue < CONV_EPI_NONE || epilogue > CONV_EPI_CLAMP1)
+        return fail(CONV_E_INVAL, "unknown epilogue %d", epilogue);
+    const int a = select_3d(N, C_in, C_out, D, H, W, stride, layout, dtype, algo);
+    return a < 0 ? a : ok();
+}
+
+size_t conv3x3x3_workspace_bytes(int N, int C_in, int C_out, int D, int H, int W, int stride,
+                                 int layout, int dtype, int algo) {
+    const int a = select_3d(N, C_in, C_out, D, H, W, stride, layout, dtype, algo);
+    if (a < 0) return 0;
+    ok();
+    if (a == CONV_ALGO_SPLIT_HEAD)
+        return (size_t)N * D * H * W * cx::kHeadPlaneChannels * elem_bytes();
+    const cx::IgemmPlan pl = cx::plan_igemm(family_for(a, C_out), N, C_in, C_out, D, H, W);
+    return cx::splitk_workspace_bytes(pl, N, D, H, W, C_out);
+}
+
+size_t conv3x3x3_packed_weight_bytes(int N, int C_in, int C_out, int D, int H, int W,
+                                     int stride, int layout, int dtype, int algo) {
+    const int a = select_3d(N, C_in, C_out, D, H, W, stride, layout, dtype, algo);
+    if (a < 0) return 0;
+    ok();
+    return cx::packed_bytes(cx::plan_igemm(family_for(a, C_out), N, C_in, C_out, D, H, W));
+}
+
+int conv3x3x3_pack_weights(const void *w_oidhw, void *w_packed, int N, int C_in, int C_out,
+                           int D, int H, int W, int stride, int layout, int dtype, int algo,
+                           void *stream) {
+    const int a = select_3d(N, C_in, C_out, D, H, W, stride, layout, dtype, algo);
+    if (a < 0) return a;
+    if (C_out == 0) return ok();
+    if (!w_oidhw || !w_packed) return fail(CONV_E_INVAL, "w_oidhw and w_packed must be non-NULL");
+    if (!aligned(w_oidhw, 2) || !aligned(w_packed, 16))
+        return fail(CONV_E_INVAL, "w_oidhw must be 2-byte and w_packed 16-byte aligned");
+    const cx::IgemmPlan pl = cx::plan_igemm(family_for(a, C_out), N, C_in, C_out, D, H, W);
+    if (overlaps(w_oidhw, (size_t)C_out * C_in * 27 * elem_bytes(), w_packed, cx::packed_bytes(pl)))
+        return fail(CONV_E_INVAL, "w_oidhw and w_packed overlap");
+    int st = device_present();
+    if (st) return st;
+    const hipError_t e = cx::launch_pack3d(pl, w_oidhw, w_packed, C_in, C_out, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(CONV_E_LAUNCH, "weight pack launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int conv3x3x3_fwd(const void *x, const void *w_packed, const void *bias, void *y, int N,
+                  int C_in, int C_out, int D, int H, int W, int stride, int layout, int dtype,
+                  int epilogue, int algo, void *workspace, size_t workspace_bytes, void *stream) {
+    if (epilogue < CONV_EPI_NONE || epilogue > CONV_EPI_CLAMP1)
+        return fail(CONV_E_INVAL, "unknown epilogue %d", epilogue);
+    const int a = select_3d(N, C_in, C_out, D, H, W, stride, layout, dtype, algo);
+    if (a < 0) return a;
+    if (N == 0 || C_out == 0 || D == 0 || H == 0 || W == 0) return ok();
+    if (!x || !w_packed || !y) return fail(CONV_E_INVAL, "x, w_packed and y must be non-NULL");
+    if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(y, 16))
+        return fail(CONV_E_INVAL, "x, w_packed and y must be 16-byte aligned");
+    if (bias && !aligned(bias, 2)) return fail(CONV_E_INVAL, "bias must be 2-byte aligned");
+    const size_t P = (size_t)N * D * H * W;
+    const size_t xb = P * C_in * elem_bytes(), yb = P * C_out * elem_bytes();
+    if (overlaps(x, xb, y, yb)) return fail(CONV_E_INVAL, "x and y overlap (in-place is unsupported)");
+    const size_t need = conv3x3x3_workspace_bytes(N, C_in, C_out, D, H, W, stride, layout, dtype, a);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(CONV_E_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (!aligned(workspace, 16)) return fail(CONV_E_INVAL, "workspace must be 16-byte aligned");
+        if (overlaps(workspace, need, x, xb) || overlaps(workspace, need, y, yb))
+            return fail(CONV_E_INVAL, "workspace overlaps x or y");
+    }
+    int st = device_present();
+    if (st) return st;
+    const bool bf = dtype == CONV_DTYPE_BF16;
+    hipStream_t s = (hipStream_t)stream;
+    if (a == CONV_ALGO_SPLIT_HEAD) {
+        const cx::IgemmPlan pl = cx::plan_igemm(cx::IG_TEMPORAL, N, C_in, C_out, D, H, W);
+        cx::IgemmParams ip{};
+        ip.x = x, ip.wp = w_packed, ip.bias = nullptr, ip.y = workspace, ip.partial = nullptr;
+        ip.N = N, ip.C_in = C_in, ip.D = D, ip.H = H, ip.W = W;
+        ip.Cy = cx::kHeadPlaneChannels, ip.bf16 = bf, ip.epilogue = CONV_EPI_NONE;
+        hipError_t e = cx::launch_igemm3d(pl, ip, s);
+        if (e != hipSuccess) return fail(CONV_E_LAUNCH, "split-head temporal launch failed: %s", hipGetErrorString(e));
+        cx::StencilParams sp{};
+        sp.g = workspace, sp.bias = bias, sp.y = y;
+        sp.N = N, sp.D = D, sp.H = H, sp.W = W, sp.C_out = C_out, sp.bf16 = bf, sp.epilogue = epilogue;
+        e = cx::launch_head_stencil(sp, s);
+        if (e != hipSuccess) return fail(CONV_E_LAUNCH, "split-head stencil launch failed: %s", hipGetErrorString(e));
+        return ok();
+    }
+    const cx::IgemmPlan pl = cx::plan_igemm(family_for(a, C_out), N, C_in, C_out, D, H, W);
+    cx::IgemmParams ip{};
+    ip.x = x, ip.wp = w_packed, ip.bias = bias, ip.y = y;
+    ip.partial = static_cast<float *>(pl.splits > 1 ? workspace : nullptr);
+    ip.N = N, ip.C_in = C_in, ip.D = D, ip.H = H, ip.W = W;
+    ip.Cy = C_out, ip.bf16 = bf, ip.epilogue = epilogue;
+    const hipError_t e = cx::launch_igemm3d(pl, ip, s);
+    if (e != hipSuccess) return fail(CONV_E_LAUNCH, "MFMA 3D launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// Shared device-side helpers of the gfx950 convolution kernels: storage-type traits, the
+// fp32 <-> fp16/bf16 conversions and the fused epilogue (bias is folded into the accumulator's
+// initial value by each kernel; the epilogue is applied to the fp32 sum before the one
+// round-to-nearest-even on the store).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cx {
+
+typedef uint16_t u16;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+enum { EPI_NONE = 0, EPI_RELU = 1, EPI_CLAMP1 = 2 };
+
+// bf16 is the upper half of an IEEE binary32.
+__device__ __forceinline__ float bf16_bits_to_f32(u16 b) {
+    return __uint_as_float((uint32_t)b << 16);
+}
+// Round to nearest, ties to even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ u16 f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u16)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (u16)(u >> 16);
+}
+__device__ __forceinline__ float f16_bits_to_f32(u16 h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+// v_cvt_f16_f32 rounds to nearest-even in the default mode; overflow gives infinity.
+__device__ __forceinline__ u16 f32_to_f16_bits(float f) {
+    return __builtin_bit_cast(u16, (_Float16)f);
+}
+
+// Storage-type traits: IS_BF16 selects the conversions and the matrix-core/dot instructions.
+template <bool IS_BF16>
+struct Elem;
+
+template <>
+struct Elem<false> {  // IEEE binary16
+    typedef f16x8_t vec8;
+    typedef f16x2_t vec2;
+    static __device__ __forceinline__ float to_f32(u16 b) { return f16_bits_to_f32(b); }
+    static __device__ __forceinline__ u16 from_f32(float f) { return f32_to_f16_bits(f); }
+    static __device__ __forceinline__ f32x4_t mfma16x16x32(vec8 a, vec8 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+    // a.x*b.x + a.y*b.y + c with an fp32 accumulator
+    static __device__ __forceinline__ float dot2(vec2 a, vec2 b, float c) {
+        return __builtin_amdgcn_fdot2(a, b, c, false);
+    }
+};
+
+template <>
+struct Elem<true> {  // bfloat16
+    typedef bf16x8_t vec8;
+    typedef bf16x2_t vec2;
+    static __device__ __forceinline__ float to_f32(u16 b) { return bf16_bits_to_f32(b); }
+    static __device__ __forceinline__ u16 from_f32(float f) { return f32_to_bf16_bits(f); }
+    static __device__ __forceinline__ f32x4_t mfma16x16x32(vec8 a, vec8 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ float dot2(vec2 a, vec2 b, float c) {
+        return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+    }
+};
+
+// The fused epilogue on the fp32 sum (bias already included).  ReLU keeps NaN (the compare is
+// false); the clamp is min(1, max(-1, v)).
+template <int EPI>
+__device__ __forceinline__ float epilogue(float v) {
+    if constexpr (EPI == EPI_RELU) return v < 0.f ? 0.f : v;
+    if constexpr (EPI == EPI_CLAMP1) return fminf(1.f, fmaxf(-1.f, v));
+    return v;
+}
+
+// Remaps a linear workgroup id so that consecutive logical tiles run on the same XCD: the
+// dispatcher hands workgroup i to XCD i % 8, and each XCD has its own L2.  Bijective on
+// [0, total).
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t i, uint32_t total) {
+    const uint32_t q = total / 8u, r = total % 8u;
+    const uint32_t xcd = i % 8u, k = i / 8u;
+    const uint32_t start = xcd < r ? xcd * (q + 1u) : r * (q + 1u) + (xcd - r) * q;
+    return start + k;
+}
+
+}  // namespace cx

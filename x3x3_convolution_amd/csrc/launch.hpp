@@ -1,0 +1,77 @@
+// Host-side launchers of the gfx950 kernels.  Shapes are validated by the C ABI layer before any
+// of these is called; each launcher only derives its grid and enqueues on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace cx {
+
+// ---- 2D direct SIMT kernel (NCHW) ----------------------------------------------------------
+struct Simt2dParams {
+    const void *x, *w, *bias;
+    void *y;
+    int N, C_in, C_out, H, W, Hout, Wout, stride;
+    bool bf16;
+    int epilogue;
+};
+hipError_t launch_simt2d(const Simt2dParams &p, hipStream_t stream);
+
+// ---- 3D MFMA implicit GEMM (NDHWC) ---------------------------------------------------------
+// Tile families; the host picks one per request.
+enum IgemmFamily {
+    IG_WIDE = 0,   // 128 output rows x 128 positions per workgroup: C_out > 16
+    IG_NARROW = 1, // 16 output rows x 256 positions: C_out <= 16 (the direct head)
+    IG_TEMPORAL = 2 // 112 rows (9 taps x 12 channels) x 192 positions, 3x1x1 taps: split head
+};
+
+struct IgemmPlan {
+    int family;
+    int BM;            // output rows per workgroup
+    int TH, TW;        // output positions per workgroup (rows x columns of one frame)
+    int ntaps;         // 27 or 3
+    int Mrows;         // rows that exist (C_out, or 112 for the split head's plane)
+    int Mpad;          // packed rows = round_up(Mrows, BM)
+    int nchunks;       // ceil(C_in / 32)
+    int splits;        // split-K factor (1 = none)
+    int chunks_per_split;
+    int tiles_h, tiles_w, mtiles;
+    long long workgroups;
+};
+
+// Plans the MFMA launch (tile family, split-K) for a request.  Pure host arithmetic.
+IgemmPlan plan_igemm(int family, int N, int C_in, int C_out, int D, int H, int W);
+
+size_t packed_bytes(const IgemmPlan &pl);
+// fp32 split-K partial sums, or 0 when splits == 1.
+size_t splitk_workspace_bytes(const IgemmPlan &pl, int N, int D, int H, int W, int C_out);
+
+struct IgemmParams {
+    const void *x, *wp, *bias;
+    void *y;           // output (C_out channels) or the split head's plane (112 channels)
+    float *partial;    // split-K partials (splits > 1)
+    int N, C_in, D, H, W;
+    int Cy;            // channel stride of y
+    bool bf16;
+    int epilogue;
+};
+hipError_t launch_igemm3d(const IgemmPlan &pl, const IgemmParams &p, hipStream_t stream);
+
+// Repack OIDHW weights for `pl` (family decides the row order).
+hipError_t launch_pack3d(const IgemmPlan &pl, const void *w, void *wp, int C_in, int C_out,
+                         hipStream_t stream);
+
+// ---- split head, stage 2: nine-tap stencil over the 112-channel plane ----------------------
+struct StencilParams {
+    const void *g, *bias;
+    void *y;
+    int N, D, H, W, C_out;
+    bool bf16;
+    int epilogue;
+};
+hipError_t launch_head_stencil(const StencilParams &p, hipStream_t stream);
+
+constexpr int kHeadPlaneChannels = 112;  // 9 taps x 12 channels = 108, padded to 7 x 16
+
+}  // namespace cx

@@ -1,0 +1,80 @@
+"""Convenience owners of the buffers the C ABI asks the caller for (plumbing only).
+
+``Conv3x3x3`` packs a weight tensor once and keeps the packed copy and the workspace the chosen
+algorithm needs; calling it runs ``conv3x3x3_fwd``.  ``Conv3x3`` does the same for the 2D call,
+which needs neither.  Device memory comes from torch; every computation runs in libconv3x3.so.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import conv as C
+
+_DT = {torch.float16: C.DTYPE_F16, torch.bfloat16: C.DTYPE_BF16}
+_EPI = {"none": C.EPI_NONE, "relu": C.EPI_RELU, "clamp1": C.EPI_CLAMP1}
+
+
+def dtype_code(t: torch.dtype) -> int:
+    if t not in _DT:
+        raise TypeError("conv3x3 supports float16 and bfloat16 storage, got %s" % t)
+    return _DT[t]
+
+
+def epi_code(e) -> int:
+    return _EPI[e] if isinstance(e, str) else int(e)
+
+
+class Conv3x3:
+    """2D pad-1 3x3 convolution over NCHW tensors of one fixed shape."""
+
+    def __init__(self, w, bias, N, H, W, stride=1, epilogue="none", algo=C.ALGO_AUTO):
+        self.w, self.bias = w.contiguous(), None if bias is None else bias.contiguous()
+        self.C_out, self.C_in = w.shape[0], w.shape[1]
+        self.N, self.H, self.W, self.stride = N, H, W, stride
+        self.dtype = dtype_code(w.dtype)
+        self.epi = epi_code(epilogue)
+        self.algo = algo
+        self.H_out, self.W_out = C.conv_out_size(H, stride), C.conv_out_size(W, stride)
+
+    def out_shape(self):
+        return (self.N, self.C_out, self.H_out, self.W_out)
+
+    def __call__(self, x, y=None, stream=None):
+        if y is None:
+            y = torch.empty(self.out_shape(), dtype=self.w.dtype, device=x.device)
+        C.conv3x3_fwd(x, self.w, self.bias, y, self.N, self.C_in, self.C_out, self.H, self.W,
+                      self.stride, C.LAYOUT_CHANNELS_FIRST, self.dtype, self.epi, self.algo,
+                      stream)
+        return y
+
+
+class Conv3x3x3:
+    """3D pad-1 3x3x3 convolution over NDHWC tensors of one fixed shape (stride 1)."""
+
+    def __init__(self, w, bias, N, D, H, W, epilogue="none", algo=C.ALGO_AUTO, stream=None):
+        self.C_out, self.C_in = w.shape[0], w.shape[1]
+        self.N, self.D, self.H, self.W = N, D, H, W
+        self.dtype = dtype_code(w.dtype)
+        self.torch_dtype = w.dtype
+        self.epi = epi_code(epilogue)
+        self.bias = None if bias is None else bias.contiguous()
+        shape = (N, self.C_in, self.C_out, D, H, W, 1, C.LAYOUT_CHANNELS_LAST, self.dtype)
+        self.algo = C.conv3x3x3_select_algo(*shape, algo)
+        nbytes = C.conv3x3x3_packed_weight_bytes(*shape, self.algo)
+        self.w_packed = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+        C.conv3x3x3_pack_weights(w.contiguous(), self.w_packed, *shape, self.algo, stream=stream)
+        self.ws_bytes = C.conv3x3x3_workspace_bytes(*shape, self.algo)
+        self.workspace = (torch.empty(self.ws_bytes, dtype=torch.uint8, device=w.device)
+                          if self.ws_bytes else None)
+        self._shape = shape
+
+    def out_shape(self):
+        return (self.N, self.D, self.H, self.W, self.C_out)
+
+    def __call__(self, x, y=None, stream=None):
+        if y is None:
+            y = torch.empty(self.out_shape(), dtype=self.torch_dtype, device=x.device)
+        N, Ci, Co, D, H, W, s, lay, dt = self._shape
+        C.conv3x3x3_fwd(x, self.w_packed, self.bias, y, N, Ci, Co, D, H, W, s, lay, dt, self.epi,
+                        self.algo, self.workspace, self.ws_bytes, stream)
+        return y
