@@ -1,0 +1,344 @@
+#!/usr/bin/env python3
+"""Benchmark of the 3x3x3 video output head on one MI355X: ms per 704x1248 VAE-head pass.
+
+The workload is the Wan2.2-style output head at its full size: x [1,16,352,624,256] bf16 NDHWC
+(channels-last) -> y [1,16,352,624,12], bias, clamp to [-1,1], seeded synthetic N(0,1)
+activations and N(0, 1/(27*256)) weights (no trained weights or real latents exist here).  One
+step is one head pass, computed by the algorithm AUTO selects; both head algorithms -- the direct
+27-tap MFMA implicit GEMM and the split head (3x1x1 temporal conv into a 112-channel plane, then
+the nine-tap stencil) -- are timed and reported.  Inputs are resident in HBM before the timed
+region; each step's launches run back to back on one stream.
+
+Prints one JSON line (see --help).  `--workload` times another of the synthetic workloads with
+the same protocol (for measurements outside the default line).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "conv TFLOP/s + HBM GB/s (roofline %), ms per 704x1248 VAE-head pass"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2516.6    # MI355X dense bf16 matrix-core peak
+VALU_FP32_PEAK_TFS = 157.3     # MI355X fp32 vector peak (dot2/packed rate)
+KERNEL_SOURCES = {             # dominant-kernel name -> the source file it is built from
+    "igemm3d": "x3x3_convolution_amd/csrc/igemm3d.hip",
+    "head_stencil": "x3x3_convolution_amd/csrc/head.hip",
+    "head_fused": "x3x3_convolution_amd/csrc/head.hip",
+    "simt2d": "x3x3_convolution_amd/csrc/simt2d.hip",
+}
+
+
+def live_taps(n, stride=1):
+    """Sum over output coordinates of the taps that land inside a pad-1 3-tap dimension."""
+    nout = (n - 1) // stride + 1
+    return sum(sum(1 for t in range(3) if 0 <= stride * o - 1 + t < n) for o in range(nout))
+
+
+def source_sha(kernel):
+    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel, workload, algo):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the current
+    kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh).get("%s/%s/%s" % (kernel, workload, algo))
+    if not rec or rec.get("source_sha") != source_sha(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c3",
+                    choices=["c3", "c4", "c5", "c5d1", "c1", "c2", "c2s2"])
+    ap.add_argument("--algo", default="auto", choices=["auto", "mfma", "split", "fused"],
+                    help="auto: time every head algorithm and report AUTO's choice; otherwise "
+                         "time only the named one")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (used for profiler runs)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration) and exit")
+    return ap.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.ones(n // 2, dtype=torch.int16, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n}))
+
+
+class Timer:
+    """HIP events on one stream around a sequence of launches."""
+
+    def __init__(self, stream):
+        import torch
+        self.torch = torch
+        self.stream = stream
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        return e
+
+    def stop(self, name, s):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        self.pairs.append((name, s, e))
+
+    def summary(self):
+        out = {}
+        for name, s, e in self.pairs:
+            out.setdefault(name, []).append(s.elapsed_time(e))
+        return {k: sum(v) / len(v) for k, v in out.items()}
+
+
+def run_head(args, wl, stream):
+    """Times every head algorithm; returns per-algorithm results and the AUTO choice."""
+    import torch
+
+    import synthetic_inputs as si
+    from x3x3_convolution_amd import conv as C
+    from x3x3_convolution_amd.plan import Conv3x3x3
+
+    x, w, b = si.make_inputs(wl, device="cuda")
+    P = wl.N * wl.D * wl.H * wl.W
+    y = torch.empty(wl.y_shape(), dtype=wl.torch_dtype, device="cuda")
+    shape = (wl.N, wl.C_in, wl.C_out, wl.D, wl.H, wl.W)
+    auto = C.conv3x3x3_select_algo(*shape, 1, C.LAYOUT_CHANNELS_LAST, C.DTYPE_BF16, C.ALGO_AUTO)
+    algos = {"mfma": C.ALGO_MFMA, "split": C.ALGO_SPLIT_HEAD, "fused": C.ALGO_FUSED_HEAD}
+    if args.algo != "auto":   # time only the requested algorithm (profiler runs)
+        auto = algos[args.algo]
+        algos = {args.algo: auto}
+    flop_live = 2.0 * wl.C_in * wl.C_out * live_taps(wl.D) * live_taps(wl.H) * live_taps(wl.W)
+    xb, yb = P * wl.C_in * 2, P * wl.C_out * 2
+    wb, bb = wl.C_out * wl.C_in * 27 * 2, wl.C_out * 2
+    gb = P * 112 * 2
+    results = {}
+    for name, code in algos.items():
+        op = Conv3x3x3(w, b, wl.N, wl.D, wl.H, wl.W, epilogue=wl.epilogue, algo=code)
+        torch.cuda.synchronize()
+        if code == C.ALGO_SPLIT_HEAD:
+            g = op.workspace
+
+            def step(tm=None):
+                s0 = tm.start() if tm else None
+                C.conv_head_temporal(x, op.w_packed, g, wl.N, wl.C_in, wl.C_out, wl.D, wl.H,
+                                     wl.W, C.DTYPE_BF16, stream)
+                if tm:
+                    tm.stop("head_temporal", s0)
+                    s1 = tm.start()
+                C.conv_head_stencil(g, b, y, wl.N, wl.D, wl.H, wl.W, wl.C_out, C.DTYPE_BF16,
+                                    C.EPI_CLAMP1, stream)
+                if tm:
+                    tm.stop("head_stencil", s1)
+        else:
+            kname = "head_fused" if code == C.ALGO_FUSED_HEAD else "igemm3d_direct"
+
+            def step(tm=None, kname=kname, op=op):
+                s0 = tm.start() if tm else None
+                op(x, y, stream=stream)
+                if tm:
+                    tm.stop(kname, s0)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        tm = Timer(torch.cuda.current_stream())
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step(tm)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        k = tm.summary()
+        results[name] = dict(ms_per_pass=wall_ms, kernel_ms=k)
+        del op
+        torch.cuda.empty_cache()
+
+    # roofline of the dominant kernel of the chosen algorithm
+    flop_t = 2.0 * wl.C_in * 9 * wl.C_out * live_taps(wl.D) * wl.H * wl.W   # temporal GEMM
+    if auto == C.ALGO_FUSED_HEAD:
+        kms = results["fused"]["kernel_ms"]["head_fused"]
+        bytes_f = xb + yb + wl.C_out * wl.C_in * 27 * 2 + bb
+        ach = bytes_f / (kms * 1e-3) / 1e9
+        roof = dict(kernel="head_gemm_kernel (fused: temporal GEMM + LDS stencil + clamp)",
+                    bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=ach / HBM_PEAK_GBS, mfma_tflops=flop_t / (kms * 1e-3) / 1e12,
+                    mfma_frac=flop_t / (kms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
+                    algorithmic_bytes=bytes_f, algorithmic_flop=flop_t, avg_launch_ms=kms,
+                    traffic=traffic_from_profiles("head_fused", wl.name, "fused"))
+    elif auto == C.ALGO_SPLIT_HEAD:
+        kms = results["split"]["kernel_ms"]["head_temporal"]
+        bytes_t = xb + gb + wl.C_out * wl.C_in * 27 * 2
+        ach = bytes_t / (kms * 1e-3) / 1e9
+        roof = dict(kernel="head_gemm_kernel (split-head temporal 3x1x1, 112-channel plane)",
+                    bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=ach / HBM_PEAK_GBS, mfma_tflops=flop_t / (kms * 1e-3) / 1e12,
+                    algorithmic_bytes=bytes_t, algorithmic_flop=flop_t, avg_launch_ms=kms,
+                    traffic=traffic_from_profiles("head_fused", wl.name, "split"))
+    else:
+        kms = results["mfma"]["kernel_ms"]["igemm3d_direct"]
+        ach = flop_live / (kms * 1e-3) / 1e12
+        bytes_d = xb + yb + wb + bb
+        roof = dict(kernel="igemm3d (direct 27-tap head, 16-row tiles)", bound="mfma",
+                    achieved=ach, peak=MFMA_BF16_PEAK_TFS, unit="TFLOP/s",
+                    frac=ach / MFMA_BF16_PEAK_TFS,
+                    hbm_gbs=bytes_d / (kms * 1e-3) / 1e9,
+                    hbm_frac=bytes_d / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    algorithmic_bytes=bytes_d, algorithmic_flop=flop_live, avg_launch_ms=kms,
+                    traffic=traffic_from_profiles("igemm3d", wl.name, "mfma"))
+    chosen = {C.ALGO_SPLIT_HEAD: "split", C.ALGO_FUSED_HEAD: "fused"}.get(auto, "mfma")
+    pass_ms = results[chosen]["ms_per_pass"]
+    extra = dict(
+        pass_tflops=flop_live / (pass_ms * 1e-3) / 1e12,
+        pass_gbs=((xb + 2 * gb + yb + wb + bb) if chosen == "split" else (xb + yb + wb + bb))
+        / (pass_ms * 1e-3) / 1e9,
+        algos={k: dict(ms_per_pass=round(v["ms_per_pass"], 4),
+                       kernel_ms={kk: round(vv, 4) for kk, vv in v["kernel_ms"].items()})
+               for k, v in results.items()})
+    return chosen, pass_ms, roof, extra, (x, w, b)
+
+
+def cpu_baseline(wl, tensors, target_s):
+    """The oracle timed on the host cores over a bounded random sample of output positions,
+    extrapolated to ms per full pass."""
+    import numpy as np
+
+    import oracle
+    import synthetic_inputs as si
+
+    x, w, b = tensors
+    xb, wbits, bbits = si.bits(x), si.bits(w), si.bits(b)
+    P = wl.N * wl.D * wl.H * wl.W
+    rng = np.random.default_rng(0)
+
+    def sample(n):
+        return np.stack([rng.integers(0, wl.N, n), rng.integers(0, wl.D, n),
+                         rng.integers(0, wl.H, n), rng.integers(0, wl.W, n)], 1).astype(np.int32)
+    epi = {"none": oracle.EPI_NONE, "relu": oracle.EPI_RELU, "clamp1": oracle.EPI_CLAMP1}
+    cal = sample(256)
+    t0 = time.perf_counter()
+    oracle.conv3d_points(xb, wbits, bbits, cal, 1, oracle.BF16, epi[wl.epilogue],
+                         oracle.CHANNELS_LAST)
+    per_pt = max((time.perf_counter() - t0) / len(cal), 1e-7)
+    n = int(min(P, max(1024, target_s / per_pt)))
+    pts = sample(n)
+    t0 = time.perf_counter()
+    oracle.conv3d_points(xb, wbits, bbits, pts, 1, oracle.BF16, epi[wl.epilogue],
+                         oracle.CHANNELS_LAST)
+    dt = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
+    return dict(value=dt / n * P * 1e3, unit="ms", cores=cores, kind="oracle",
+                sample="%d random output positions of the head pass (all 12 channels each), "
+                       "%.1f s wall, extrapolated to the %d positions of one pass" % (n, dt, P))
+
+
+def run_other(args, wl, stream):
+    """Same timing protocol for the other workloads (one algorithm each)."""
+    import torch
+
+    import synthetic_inputs as si
+    from x3x3_convolution_amd.plan import Conv3x3, Conv3x3x3
+
+    x, w, b = si.make_inputs(wl, device="cuda")
+    if wl.kind == "2d":
+        op = Conv3x3(w, b, wl.N, wl.H, wl.W, stride=wl.stride, epilogue=wl.epilogue)
+        P = wl.N * wl.H_out * wl.W_out
+        flop = 2.0 * wl.C_in * wl.C_out * wl.N * live_taps(wl.H, wl.stride) * live_taps(wl.W, wl.stride)
+        kname, bound, peak, unit = "simt2d", "alu", VALU_FP32_PEAK_TFS, "TFLOP/s"
+    else:
+        op = Conv3x3x3(w, b, wl.N, wl.D, wl.H, wl.W, epilogue=wl.epilogue)
+        P = wl.N * wl.D * wl.H * wl.W
+        flop = 2.0 * wl.C_in * wl.C_out * wl.N * live_taps(wl.D) * live_taps(wl.H) * live_taps(wl.W)
+        kname, bound, peak, unit = "igemm3d", "mfma", MFMA_BF16_PEAK_TFS, "TFLOP/s"
+    y = torch.empty(op.out_shape(), dtype=wl.torch_dtype, device="cuda")
+    nbytes = (x.numel() + y.numel() + w.numel() + b.numel()) * 2
+    for _ in range(args.warmup):
+        op(x, y, stream=stream)
+    torch.cuda.synchronize()
+    tm = Timer(torch.cuda.current_stream())
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        s = tm.start()
+        op(x, y, stream=stream)
+        tm.stop(kname, s)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    kms = tm.summary()[kname]
+    ach = flop / (kms * 1e-3) / 1e12
+    roof = dict(kernel=kname, bound=bound, achieved=ach, peak=peak, unit=unit, frac=ach / peak,
+                hbm_gbs=nbytes / (kms * 1e-3) / 1e9, algorithmic_flop=flop,
+                algorithmic_bytes=nbytes, avg_launch_ms=kms, positions=P,
+                traffic=traffic_from_profiles(kname, wl.name, "auto"))
+    return wall_ms, roof
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    import torch
+
+    import synthetic_inputs as si
+
+    torch.cuda.set_device(0)
+    # a dedicated stream (default priority): the library's launches and the timing events
+    # both go on it
+    strm = torch.cuda.Stream()
+    torch.cuda.set_stream(strm)
+    stream = strm.cuda_stream
+    wl = si.WORKLOADS[args.workload]
+    line = dict(metric=METRIC, n_gpus=1, steps=args.steps, warmup=args.warmup,
+                higher_is_better=False, scaling="weak", vs_baseline=None, dtype=wl.dtype,
+                data="synthetic (seeded; no trained weights or real activations)")
+    if wl.name == "c3":
+        chosen, pass_ms, roof, extra, tensors = run_head(args, wl, stream)
+        line.update(value=round(pass_ms, 4), unit="ms", ms_per_step=round(pass_ms, 4),
+                    config=dict(workload="wan2.2 output head 3x3x3 256->12, x [1,16,352,624,256] "
+                                "bf16 NDHWC, bias + clamp[-1,1], one 704x1248 head pass",
+                                algo=chosen, N=wl.N, C_in=wl.C_in, C_out=wl.C_out, D=wl.D,
+                                H=wl.H, W=wl.W),
+                    roofline={k: (round(v, 6) if isinstance(v, float) else v)
+                              for k, v in roof.items()})
+        line.update({k: (round(v, 4) if isinstance(v, float) else v) for k, v in extra.items()})
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline(wl, tensors, args.cpu_seconds)
+    else:
+        wall_ms, roof = run_other(args, wl, stream)
+        line.update(value=round(wall_ms, 4), unit="ms", ms_per_step=round(wall_ms, 4),
+                    config=dict(workload=wl.name, N=wl.N, C_in=wl.C_in, C_out=wl.C_out, D=wl.D,
+                                H=wl.H, W=wl.W, stride=wl.stride, epilogue=wl.epilogue),
+                    roofline={k: (round(v, 6) if isinstance(v, float) else v)
+                              for k, v in roof.items()})
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -53,12 +53,17 @@ enum { CONV_EPI_NONE = 0, CONV_EPI_RELU = 1, CONV_EPI_CLAMP1 = 2 };
  *   MFMA        3D: implicit GEMM on the matrix cores, 27 taps in one fp32 accumulator.
  *   SPLIT_HEAD  3D, C_out <= 12, stride 1: 3x1x1 temporal conv into 9*C_out tap channels of a
  *               112-channel bf16/fp16 plane in the workspace, then a nine-tap stencil + bias +
- *               epilogue [head.cu, header comment and head_stencil_kernel]. */
+ *               epilogue [head.cu, header comment and head_stencil_kernel].
+ *   FUSED_HEAD  3D, C_out <= 12, stride 1: the same temporal GEMM and the same two roundings as
+ *               SPLIT_HEAD, but the tap-channel rows stay in LDS and the stencil + bias +
+ *               epilogue run in the same kernel, so the plane never goes to HBM; no workspace.
+ *   AUTO: FUSED_HEAD when it applies, else MFMA. */
 enum {
     CONV_ALGO_AUTO = 0,
     CONV_ALGO_SIMT = 1,
     CONV_ALGO_MFMA = 2,
-    CONV_ALGO_SPLIT_HEAD = 3
+    CONV_ALGO_SPLIT_HEAD = 3,
+    CONV_ALGO_FUSED_HEAD = 4
 };
 /* status codes */
 enum {
@@ -102,7 +107,8 @@ int conv3x3_is_supported(int N, int C_in, int C_out, int H, int W, int stride, i
  * 3D: x (N,D,H,W,C_in) NDHWC, w_packed from conv3x3x3_pack_weights, bias (C_out) or NULL,
  * y (N,D,H_out,W_out,C_out) NDHWC.  Supported: layout CHANNELS_LAST, dtype BF16 or F16,
  * stride 1 (stride 2 returns CONV_E_UNSUPPORTED), C_in a multiple of 8.
- *   algo MFMA: any C_out >= 1.  algo SPLIT_HEAD: C_out <= 12.  AUTO: see select_algo.
+ *   algo MFMA: any C_out >= 1.  algo SPLIT_HEAD / FUSED_HEAD: C_out <= 12 and one sample of x
+ *   (D*H*W*C_in elements) below 2 GiB.  AUTO: see select_algo.
  * workspace: at least conv3x3x3_workspace_bytes(...) bytes (may be NULL when that is 0).
  * The same (shape, dtype, algo) arguments must be given to the size queries, to
  * conv3x3x3_pack_weights and to conv3x3x3_fwd.
@@ -136,6 +142,24 @@ size_t conv3x3x3_packed_weight_bytes(int N, int C_in, int C_out, int D, int H, i
 int conv3x3x3_pack_weights(const void *w_oidhw, void *w_packed, int N, int C_in, int C_out,
                            int D, int H, int W, int stride, int layout, int dtype, int algo,
                            void *stream);
+
+/* ------------------------------------------------------------------------------------------
+ * The split head's two stages as separate calls (conv3x3x3_fwd with CONV_ALGO_SPLIT_HEAD runs
+ * both on one stream).  [head.cu: the temporal 3x1x1 convolution that writes the plane, and the
+ * host function head_stencil(g, bias, out, ...) that sums it.]
+ *
+ * conv_head_temporal: x (N,D,H,W,C_in) NDHWC, w_packed packed with CONV_ALGO_SPLIT_HEAD for
+ *   this shape, g (N,D,H,W,112) channels-last of `dtype`:
+ *     g[n,d,h,w,(ky*3+kx)*C_out+co] = round( sum_{ci,kd} w[co,ci,kd,ky,kx] * X[n,ci,d-1+kd,h,w] )
+ *   channels 9*C_out..111 are written as zero.  No bias.  C_out <= 12, C_in % 8 == 0.
+ * conv_head_stencil: g as above, bias (C_out) or NULL, y (N,D,H,W,C_out) NDHWC:
+ *     y[n,d,h,w,co] = round( E( b[co] + sum_{ky,kx} g[n,d,h+ky-1,w+kx-1,(ky*3+kx)*C_out+co] ) )
+ *   with g zero outside the plane.  g and y must not overlap.
+ * ---------------------------------------------------------------------------------------- */
+int conv_head_temporal(const void *x, const void *w_packed, void *g, int N, int C_in, int C_out,
+                       int D, int H, int W, int dtype, void *stream);
+int conv_head_stencil(const void *g, const void *bias, void *y, int N, int D, int H, int W,
+                      int C_out, int dtype, int epilogue, void *stream);
 
 #ifdef __cplusplus
 }

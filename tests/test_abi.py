@@ -118,6 +118,10 @@ def test_3d_invalid_and_unsupported():
     assert f3d(C_in=20) == C.E_UNSUPPORTED      # not a multiple of 8
     assert f3d(algo=C.ALGO_SIMT) == C.E_UNSUPPORTED
     assert f3d(algo=C.ALGO_SPLIT_HEAD, C_out=13) == C.E_UNSUPPORTED
+    assert f3d(algo=C.ALGO_FUSED_HEAD, C_out=13) == C.E_UNSUPPORTED
+    # one sample of x must stay below 2 GiB for the head kernels' buffer addressing
+    assert cx.conv3x3x3_is_supported(1, 256, 12, 32, 352, 624, 1, 1, 1, 2, C.ALGO_FUSED_HEAD) == C.E_UNSUPPORTED
+    assert cx.conv3x3x3_select_algo(1, 256, 12, 32, 352, 624, 1, 1, 1, 0) == C.ALGO_MFMA
     # the split head needs its plane in the workspace
     assert f3d(algo=C.ALGO_SPLIT_HEAD) == C.E_WORKSPACE
     need = cx.conv3x3x3_workspace_bytes(1, 32, 12, 2, 8, 8, 1, 1, 1, C.ALGO_SPLIT_HEAD)
@@ -144,15 +148,18 @@ def test_is_supported_matches_fwd_checks():
 def test_algo_selection_and_buffer_sizes():
     # the output head: AUTO resolves to a concrete algorithm; split head needs its plane
     a = cx.conv3x3x3_select_algo(1, 256, 12, 16, 352, 624, 1, 1, 1, 0)
-    assert a in (C.ALGO_MFMA, C.ALGO_SPLIT_HEAD)
+    assert a == C.ALGO_FUSED_HEAD
+    assert cx.conv3x3x3_workspace_bytes(1, 256, 12, 16, 352, 624, 1, 1, 1, 0) == 0
+    assert cx.conv3x3x3_select_algo(1, 256, 256, 16, 176, 312, 1, 1, 1, 0) == C.ALGO_MFMA
     assert cx.conv3x3x3_workspace_bytes(1, 256, 12, 16, 352, 624, 1, 1, 1,
                                         C.ALGO_SPLIT_HEAD) == 787218432
     # packed weights: 8 channel chunks x 27 taps x 16 rows x 32 (direct head)
     assert cx.conv3x3x3_packed_weight_bytes(1, 256, 12, 16, 352, 624, 1, 1, 1,
                                             C.ALGO_MFMA) == 8 * 27 * 16 * 32 * 2
-    # split head: 8 chunks x 3 temporal taps x 112 rows x 32
-    assert cx.conv3x3x3_packed_weight_bytes(1, 256, 12, 16, 352, 624, 1, 1, 1,
-                                            C.ALGO_SPLIT_HEAD) == 8 * 3 * 112 * 32 * 2
+    # split and fused head: 8 chunks x 3 temporal taps x 112 rows x 32
+    for algo in (C.ALGO_SPLIT_HEAD, C.ALGO_FUSED_HEAD):
+        assert cx.conv3x3x3_packed_weight_bytes(1, 256, 12, 16, 352, 624, 1, 1, 1,
+                                                algo) == 8 * 3 * 112 * 32 * 2
     # mid-decoder conv fills the chip without split-K: no workspace
     assert cx.conv3x3x3_workspace_bytes(1, 256, 256, 16, 176, 312, 1, 1, 1, 0) == 0
     # the small low-res conv splits K over channel chunks: fp32 partials

@@ -67,6 +67,12 @@ CASES_3D_INT = [
     (2, 64, 5, 1, 7, 130, "bf16", "none", C.ALGO_SPLIT_HEAD),
     (1, 8, 12, 4, 70, 64, "f16", "clamp1", C.ALGO_SPLIT_HEAD),
     (1, 16, 12, 16, 40, 100, "bf16", "relu", C.ALGO_SPLIT_HEAD),
+    (1, 32, 12, 3, 9, 50, "bf16", "clamp1", C.ALGO_FUSED_HEAD),
+    (2, 64, 5, 1, 7, 130, "bf16", "none", C.ALGO_FUSED_HEAD),
+    (1, 8, 12, 4, 70, 64, "f16", "clamp1", C.ALGO_FUSED_HEAD),
+    (1, 16, 12, 16, 40, 100, "bf16", "relu", C.ALGO_FUSED_HEAD),
+    (1, 40, 7, 2, 33, 157, "bf16", "clamp1", C.ALGO_FUSED_HEAD),
+    (1, 8, 12, 1, 1, 1, "bf16", "clamp1", C.ALGO_FUSED_HEAD),
 ]
 
 
@@ -83,7 +89,7 @@ def test_conv3d_integer_exact(case):
 def test_conv3d_no_bias_integer_exact():
     x, w, _ = si.integer_case("3d", 1, 32, 12, 5, 9, D=2, dtype="bf16", seed=3, device=DEV,
                               with_bias=False)
-    for algo in (C.ALGO_MFMA, C.ALGO_SPLIT_HEAD):
+    for algo in (C.ALGO_MFMA, C.ALGO_SPLIT_HEAD, C.ALGO_FUSED_HEAD):
         y = run_3d(x, w, None, "clamp1", algo)
         assert_bit_exact(y, oracle_3d(x, w, None, "clamp1"), x.dtype)
     x, w, _ = si.integer_case("2d", 2, 6, 9, 11, 13, dtype="f16", seed=4, device=DEV,
@@ -105,7 +111,7 @@ def test_simt2d_random_tolerance():
         assert_within(m, activated=True)
 
 
-@pytest.mark.parametrize("algo", [C.ALGO_MFMA, C.ALGO_SPLIT_HEAD])
+@pytest.mark.parametrize("algo", [C.ALGO_MFMA, C.ALGO_SPLIT_HEAD, C.ALGO_FUSED_HEAD])
 def test_head_random_tolerance(algo):
     x, w, b = si.random_case("3d", 1, 256, 12, 12, 40, D=3, dtype="bf16", seed=5, device=DEV)
     y = run_3d(x, w, b, "clamp1", algo)
@@ -151,6 +157,7 @@ def test_c2_full_size_sampled(name):
 
 
 @pytest.mark.parametrize("name,algo", [("c3", C.ALGO_MFMA), ("c3", C.ALGO_SPLIT_HEAD),
+                                       ("c3", C.ALGO_FUSED_HEAD),
                                        ("c4", C.ALGO_MFMA), ("c5", C.ALGO_MFMA),
                                        ("c5d1", C.ALGO_MFMA)])
 def test_3d_full_size_sampled(name, algo):
@@ -169,3 +176,33 @@ def test_3d_full_size_sampled(name, algo):
     m = metrics(gather_3d(y, pts), ref, x.dtype)
     _say("%s algo %d sampled %d %s" % (name, algo, len(pts), m))
     assert_within(m, activated=wl.epilogue != "none")
+
+
+def test_fused_head_equals_split_head_bitwise():
+    """The fused head keeps the split head's value path (the same temporal GEMM, the same bf16
+    rounding of the tap-channel plane, the same nine-tap sum order): full-size outputs must be
+    identical bit for bit."""
+    wl = si.WORKLOADS["c3"]
+    x, w, b = si.make_inputs(wl, device=DEV)
+    ys = run_3d(x, w, b, wl.epilogue, C.ALGO_SPLIT_HEAD)
+    yf = run_3d(x, w, b, wl.epilogue, C.ALGO_FUSED_HEAD, guarded=True)
+    diff = (ys.view(torch.int16) != yf.view(torch.int16)).sum().item()
+    assert diff == 0, "%d outputs differ between the split and the fused head" % diff
+
+
+def test_split_head_plane_stage_matches_oracle_plane():
+    """The split head's first stage on its own (conv_head_temporal): the 112-channel plane must
+    equal the oracle's split-mode plane rounded to bf16, channels 108..111 zero (integer inputs,
+    so every sum is exact)."""
+    N, Ci, Co, D, H, W = 1, 32, 12, 3, 9, 50
+    x, w, b = si.integer_case("3d", N, Ci, Co, H, W, D=D, dtype="bf16", seed=77, device=DEV)
+    from x3x3_convolution_amd.plan import Conv3x3x3
+    op = Conv3x3x3(w, b, N, D, H, W, epilogue="clamp1", algo=C.ALGO_SPLIT_HEAD)
+    g = torch.full((N, D, H, W, 112), 0x7FFF, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    C.conv_head_temporal(x, op.w_packed, g, N, Ci, Co, D, H, W, C.DTYPE_BF16)
+    torch.cuda.synchronize()
+    _, gref = oracle.head_split(bits(x), bits(w), bits(b), oracle.BF16, oracle.EPI_CLAMP1,
+                                oracle.CHANNELS_LAST, round_g=True, return_g=True)
+    got = bits(g)
+    assert np.array_equal(got[..., :108], oracle.encode(gref, oracle.BF16))
+    assert np.all(got[..., 108:] == 0)

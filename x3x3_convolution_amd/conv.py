@@ -15,7 +15,7 @@ ABI_VERSION = 1
 DTYPE_F16, DTYPE_BF16 = 0, 1
 LAYOUT_CHANNELS_FIRST, LAYOUT_CHANNELS_LAST = 0, 1
 EPI_NONE, EPI_RELU, EPI_CLAMP1 = 0, 1, 2
-ALGO_AUTO, ALGO_SIMT, ALGO_MFMA, ALGO_SPLIT_HEAD = 0, 1, 2, 3
+ALGO_AUTO, ALGO_SIMT, ALGO_MFMA, ALGO_SPLIT_HEAD, ALGO_FUSED_HEAD = 0, 1, 2, 3, 4
 OK, E_INVAL, E_UNSUPPORTED, E_WORKSPACE, E_NODEVICE, E_LAUNCH = 0, -1, -2, -3, -4, -5
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -38,6 +38,8 @@ EXPORTS = [
     ("conv3x3x3_workspace_bytes", _SZ, [_I] * 10),
     ("conv3x3x3_packed_weight_bytes", _SZ, [_I] * 10),
     ("conv3x3x3_pack_weights", _I, [_P, _P] + [_I] * 10 + [_P]),
+    ("conv_head_temporal", _I, [_P, _P, _P] + [_I] * 7 + [_P]),
+    ("conv_head_stencil", _I, [_P, _P, _P] + [_I] * 7 + [_P]),
 ]
 
 
@@ -173,3 +175,14 @@ def conv3x3x3_fwd(x, w_packed, bias, y, N, C_in, C_out, D, H, W, stride=1,
     return _check(library().conv3x3x3_fwd(_ptr(x), _ptr(w_packed), _ptr(bias), _ptr(y), N, C_in,
                                           C_out, D, H, W, stride, layout, dtype, epilogue, algo,
                                           _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def conv_head_temporal(x, w_packed, g, N, C_in, C_out, D, H, W, dtype=DTYPE_BF16, stream=None):
+    return _check(library().conv_head_temporal(_ptr(x), _ptr(w_packed), _ptr(g), N, C_in, C_out,
+                                               D, H, W, dtype, _stream(stream)))
+
+
+def conv_head_stencil(g, bias, y, N, D, H, W, C_out, dtype=DTYPE_BF16, epilogue=EPI_CLAMP1,
+                      stream=None):
+    return _check(library().conv_head_stencil(_ptr(g), _ptr(bias), _ptr(y), N, D, H, W, C_out,
+                                              dtype, epilogue, _stream(stream)))

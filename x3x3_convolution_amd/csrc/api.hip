@@ -7,7 +7,7 @@
 #include <cstdio>
 #include <cstring>
 
-#include "../../include/conv3x3.h"
+#include "conv3x3.h"
 #include "launch.hpp"
 
 namespace {
@@ -63,7 +63,7 @@ int check_2d(int N, int C_in, int C_out, int H, int W, int stride, int layout, i
         return fail(CONV_E_INVAL, "negative size (N=%d C_out=%d H=%d W=%d)", N, C_out, H, W);
     if (C_in < 1) return fail(CONV_E_INVAL, "C_in must be >= 1 (got %d)", C_in);
     if (algo != CONV_ALGO_AUTO && algo != CONV_ALGO_SIMT) {
-        if (algo < CONV_ALGO_AUTO || algo > CONV_ALGO_SPLIT_HEAD)
+        if (algo < CONV_ALGO_AUTO || algo > CONV_ALGO_FUSED_HEAD)
             return fail(CONV_E_INVAL, "unknown algo %d", algo);
         return fail(CONV_E_UNSUPPORTED, "2D convolution supports algo AUTO or SIMT (got %d)", algo);
     }
@@ -87,7 +87,7 @@ int select_3d(int N, int C_in, int C_out, int D, int H, int W, int stride, int l
     if (N < 0 || C_out < 0 || D < 0 || H < 0 || W < 0)
         return fail(CONV_E_INVAL, "negative size (N=%d C_out=%d D=%d H=%d W=%d)", N, C_out, D, H, W);
     if (C_in < 1) return fail(CONV_E_INVAL, "C_in must be >= 1 (got %d)", C_in);
-    if (algo < CONV_ALGO_AUTO || algo > CONV_ALGO_SPLIT_HEAD)
+    if (algo < CONV_ALGO_AUTO || algo > CONV_ALGO_FUSED_HEAD)
         return fail(CONV_E_INVAL, "unknown algo %d", algo);
     if (layout != CONV_LAYOUT_CHANNELS_LAST)
         return fail(CONV_E_UNSUPPORTED, "3D convolution supports the NDHWC layout only");
@@ -96,21 +96,45 @@ int select_3d(int N, int C_in, int C_out, int D, int H, int W, int stride, int l
         return fail(CONV_E_UNSUPPORTED, "3D convolution needs C_in a multiple of 8 (got %d)", C_in);
     if (algo == CONV_ALGO_SIMT)
         return fail(CONV_E_UNSUPPORTED, "3D convolution has no SIMT algorithm");
-    if (algo == CONV_ALGO_SPLIT_HEAD && C_out > kSplitHeadMaxCout)
-        return fail(CONV_E_UNSUPPORTED, "SPLIT_HEAD needs C_out <= %d (got %d)", kSplitHeadMaxCout, C_out);
+    const bool head_algo = algo == CONV_ALGO_SPLIT_HEAD || algo == CONV_ALGO_FUSED_HEAD;
+    if (head_algo && C_out > kSplitHeadMaxCout)
+        return fail(CONV_E_UNSUPPORTED, "the head algorithms need C_out <= %d (got %d)", kSplitHeadMaxCout, C_out);
     const long long pos = (long long)N * D * H * W;
     if (pos >= (1ll << 31) / 8 || (long long)C_out * 27 * C_in >= (1ll << 31))
         return fail(CONV_E_UNSUPPORTED, "problem too large for one launch");
-    if (algo == CONV_ALGO_AUTO) return CONV_ALGO_MFMA;
+    // the head kernels address one sample of x through a 32-bit buffer range
+    const bool sample_fits = (long long)D * H * W * C_in * 2 < (1ll << 31);
+    if (head_algo && !sample_fits)
+        return fail(CONV_E_UNSUPPORTED, "the head algorithms need one sample of x below 2 GiB");
+    if (algo == CONV_ALGO_AUTO)
+        return (C_out <= kSplitHeadMaxCout && sample_fits) ? CONV_ALGO_FUSED_HEAD : CONV_ALGO_MFMA;
     return algo;
 }
 
 int family_for(int algo, int C_out) {
-    if (algo == CONV_ALGO_SPLIT_HEAD) return cx::IG_TEMPORAL;
+    if (algo == CONV_ALGO_SPLIT_HEAD || algo == CONV_ALGO_FUSED_HEAD) return cx::IG_TEMPORAL;
     return C_out <= 16 ? cx::IG_NARROW : cx::IG_WIDE;
 }
 
 size_t elem_bytes() { return 2; }
+
+hipError_t launch_head(const void *x, const void *w_packed, const void *bias, void *out, int N,
+                       int C_in, int C_out, int D, int H, int W, bool bf, bool fused, int epilogue,
+                       hipStream_t s) {
+    cx::HeadGemmParams hp{};
+    hp.x = x, hp.wp = w_packed, hp.bias = bias, hp.out = out;
+    hp.N = N, hp.C_in = C_in, hp.C_out = C_out, hp.D = D, hp.H = H, hp.W = W;
+    hp.bf16 = bf, hp.fused = fused, hp.epilogue = epilogue;
+    return cx::launch_head_gemm(hp, s);
+}
+
+hipError_t launch_stencil(const void *g, const void *bias, void *y, int N, int D, int H, int W,
+                          int C_out, bool bf, int epilogue, hipStream_t s) {
+    cx::StencilParams sp{};
+    sp.g = g, sp.bias = bias, sp.y = y;
+    sp.N = N, sp.D = D, sp.H = H, sp.W = W, sp.C_out = C_out, sp.bf16 = bf, sp.epilogue = epilogue;
+    return cx::launch_head_stencil(sp, s);
+}
 
 }  // namespace
 
@@ -256,18 +280,15 @@ int conv3x3x3_fwd(const void *x, const void *w_packed, const void *bias, void *y
     const bool bf = dtype == CONV_DTYPE_BF16;
     hipStream_t s = (hipStream_t)stream;
     if (a == CONV_ALGO_SPLIT_HEAD) {
-        const cx::IgemmPlan pl = cx::plan_igemm(cx::IG_TEMPORAL, N, C_in, C_out, D, H, W);
-        cx::IgemmParams ip{};
-        ip.x = x, ip.wp = w_packed, ip.bias = nullptr, ip.y = workspace, ip.partial = nullptr;
-        ip.N = N, ip.C_in = C_in, ip.D = D, ip.H = H, ip.W = W;
-        ip.Cy = cx::kHeadPlaneChannels, ip.bf16 = bf, ip.epilogue = CONV_EPI_NONE;
-        hipError_t e = cx::launch_igemm3d(pl, ip, s);
+        hipError_t e = launch_head(x, w_packed, nullptr, workspace, N, C_in, C_out, D, H, W, bf, false, CONV_EPI_NONE, s);
         if (e != hipSuccess) return fail(CONV_E_LAUNCH, "split-head temporal launch failed: %s", hipGetErrorString(e));
-        cx::StencilParams sp{};
-        sp.g = workspace, sp.bias = bias, sp.y = y;
-        sp.N = N, sp.D = D, sp.H = H, sp.W = W, sp.C_out = C_out, sp.bf16 = bf, sp.epilogue = epilogue;
-        e = cx::launch_head_stencil(sp, s);
+        e = launch_stencil(workspace, bias, y, N, D, H, W, C_out, bf, epilogue, s);
         if (e != hipSuccess) return fail(CONV_E_LAUNCH, "split-head stencil launch failed: %s", hipGetErrorString(e));
+        return ok();
+    }
+    if (a == CONV_ALGO_FUSED_HEAD) {
+        const hipError_t e = launch_head(x, w_packed, bias, y, N, C_in, C_out, D, H, W, bf, true, epilogue, s);
+        if (e != hipSuccess) return fail(CONV_E_LAUNCH, "fused head launch failed: %s", hipGetErrorString(e));
         return ok();
     }
     const cx::IgemmPlan pl = cx::plan_igemm(family_for(a, C_out), N, C_in, C_out, D, H, W);
@@ -278,6 +299,50 @@ int conv3x3x3_fwd(const void *x, const void *w_packed, const void *bias, void *y
     ip.Cy = C_out, ip.bf16 = bf, ip.epilogue = epilogue;
     const hipError_t e = cx::launch_igemm3d(pl, ip, s);
     if (e != hipSuccess) return fail(CONV_E_LAUNCH, "MFMA 3D launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int conv_head_temporal(const void *x, const void *w_packed, void *g, int N, int C_in, int C_out,
+                       int D, int H, int W, int dtype, void *stream) {
+    const int a = select_3d(N, C_in, C_out, D, H, W, 1, CONV_LAYOUT_CHANNELS_LAST, dtype,
+                            CONV_ALGO_SPLIT_HEAD);
+    if (a < 0) return a;
+    if (N == 0 || C_out == 0 || D == 0 || H == 0 || W == 0) return ok();
+    if (!x || !w_packed || !g) return fail(CONV_E_INVAL, "x, w_packed and g must be non-NULL");
+    if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(g, 16))
+        return fail(CONV_E_INVAL, "x, w_packed and g must be 16-byte aligned");
+    const size_t P = (size_t)N * D * H * W;
+    if (overlaps(x, P * C_in * elem_bytes(), g, P * cx::kHeadPlaneChannels * elem_bytes()))
+        return fail(CONV_E_INVAL, "x and g overlap");
+    int st = device_present();
+    if (st) return st;
+    const hipError_t e = launch_head(x, w_packed, nullptr, g, N, C_in, C_out, D, H, W,
+                                     dtype == CONV_DTYPE_BF16, false, CONV_EPI_NONE, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(CONV_E_LAUNCH, "head temporal launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int conv_head_stencil(const void *g, const void *bias, void *y, int N, int D, int H, int W,
+                      int C_out, int dtype, int epilogue, void *stream) {
+    int st = check_common(1, CONV_LAYOUT_CHANNELS_LAST, dtype, epilogue);
+    if (st) return st;
+    if (N < 0 || D < 0 || H < 0 || W < 0 || C_out < 0)
+        return fail(CONV_E_INVAL, "negative size (N=%d D=%d H=%d W=%d C_out=%d)", N, D, H, W, C_out);
+    if (C_out > kSplitHeadMaxCout)
+        return fail(CONV_E_UNSUPPORTED, "the head stencil needs C_out <= %d (got %d)", kSplitHeadMaxCout, C_out);
+    const long long pos = (long long)N * D * H * W;
+    if (pos >= (1ll << 31) / 8) return fail(CONV_E_UNSUPPORTED, "problem too large for one launch");
+    if (pos == 0 || C_out == 0) return ok();
+    if (!g || !y) return fail(CONV_E_INVAL, "g and y must be non-NULL");
+    if (!aligned(g, 16) || !aligned(y, 16)) return fail(CONV_E_INVAL, "g and y must be 16-byte aligned");
+    if (bias && !aligned(bias, 2)) return fail(CONV_E_INVAL, "bias must be 2-byte aligned");
+    if (overlaps(g, (size_t)pos * cx::kHeadPlaneChannels * elem_bytes(), y, (size_t)pos * C_out * elem_bytes()))
+        return fail(CONV_E_INVAL, "g and y overlap");
+    st = device_present();
+    if (st) return st;
+    const hipError_t e = launch_stencil(g, bias, y, N, D, H, W, C_out, dtype == CONV_DTYPE_BF16,
+                                        epilogue, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(CONV_E_LAUNCH, "head stencil launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 

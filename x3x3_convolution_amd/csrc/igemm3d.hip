@@ -9,13 +9,14 @@
 // convolution and its split into a temporal conv whose output channels are the spatial taps.)
 //
 // Per workgroup (256 threads, 4 waves): a TH x TW block of output positions of one frame times
-// BM output rows.  The K loop runs over input-channel chunks of 32.  For each chunk the input
-// window -- 3 frames x (TH+2) x (TW+2) positions x 32 channels, zero outside the tensor -- is
-// staged once in LDS with coalesced 16-byte loads, and all 27 taps read their B fragments from it
-// by address offset (the 27-fold reuse the per-position form lacks).  A fragments (weights) come
-// straight from global memory, where they are L2-resident, in an order packed so that one
-// 16-row fragment is 1 KiB contiguous.  Taps whose frame lies in the temporal padding are
-// skipped (they only ever multiply zeros).
+// BM output rows.  The K loop runs over (input-channel chunk of 32, live temporal tap) stages;
+// each stage stages one input frame's window -- (TH+2) x (TW+2) positions x 32 channels, zero
+// outside the tensor -- in LDS with coalesced 16-byte loads, and its nine spatial taps read their
+// B fragments from it by address offset (the reuse the per-position form lacks).  A fragments
+// (weights) come from global memory, where they are L2-resident, in an order packed so that one
+// 16-row fragment is 1 KiB contiguous.  Stages whose frame lies in the temporal padding are
+// skipped (they only ever multiply zeros).  Small problems split K over channel chunks and
+// reduce fp32 partials in a second kernel.
 //
 // Matrix-core operand layout used (v_mfma_f32_16x16x32_{bf16,f16}): lane l supplies row l%16 of A
 // and column l%16 of B, each with the 8 consecutive k values 8*(l/16)..8*(l/16)+7; it receives
@@ -46,9 +47,52 @@ struct IgemmKArgs {
     uint32_t total_wg;
 };
 
-template <bool BF, int MB, int NBW, int WM, int WN, int TH, int TW, bool SPATIAL, int EPI,
-          bool SPLITK>
-__global__ __launch_bounds__(256) void igemm3d_kernel(IgemmKArgs a) {
+// Stores the four rows (m0..m0+3) of one accumulator column: fp32 partials for split-K, or the
+// bias + epilogue + one rounding to the storage type.
+template <bool BF, int EPI, bool SPLITK>
+__device__ __forceinline__ void store_col(const IgemmKArgs &a, f32x4_t v, size_t pos, int split,
+                                          size_t P, int m0) {
+    using E = Elem<BF>;
+    if (m0 >= a.Mrows) return;
+    if constexpr (SPLITK) {
+        float *dst = a.partial + ((size_t)split * P + pos) * a.Cy + m0;
+        if (m0 + 3 < a.Mrows && (a.Cy & 3) == 0) {
+            *reinterpret_cast<f32x4_t *>(dst) = v;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (m0 + i < a.Mrows) dst[i] = v[i];
+        }
+    } else {
+        u16 o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float s = v[i];
+            if (a.bias != nullptr && m0 + i < a.Mrows) s += E::to_f32(a.bias[m0 + i]);
+            o[i] = E::from_f32(epilogue<EPI>(s));
+        }
+        u16 *dst = a.y + pos * a.Cy + m0;
+        if (m0 + 3 < a.Mrows && (a.Cy & 3) == 0) {
+            uint2 pk;
+            pk.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
+            pk.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
+            *reinterpret_cast<uint2 *>(dst) = pk;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (m0 + i < a.Mrows) dst[i] = o[i];
+        }
+    }
+}
+
+// The 27-tap convolution.  K is walked in stages s = (input-channel chunk cc, live temporal tap
+// kd): each stage stages ONE input frame's window -- (TH+2) x (TW+2) positions x 32 channels --
+// in LDS and runs its nine spatial taps from it.  The window is double-buffered: the next
+// stage's 16-byte global loads are issued into registers before the current stage's MFMAs and
+// written to the other LDS buffer after them, so one barrier per stage suffices.  Weight
+// fragments stream from global memory (L2-resident) through a 3-tap-deep register ring.
+template <bool BF, int MB, int NBW, int WM, int WN, int TH, int TW, int EPI, bool SPLITK>
+__global__ __launch_bounds__(256, 2) void igemm3d_kernel(IgemmKArgs a) {
     using E = Elem<BF>;
     typedef typename E::vec8 vec8;
     constexpr int BM = WM * MB * 16;
@@ -56,12 +100,12 @@ __global__ __launch_bounds__(256) void igemm3d_kernel(IgemmKArgs a) {
     static_assert(TW % 16 == 0, "tile width must be a multiple of 16");
     static_assert(TH * NBLK_ROW == WN * NBW, "each wave owns NBW of the tile's 16-position blocks");
     static_assert(WM * WN == 4, "four waves per workgroup");
-    constexpr int HALO = SPATIAL ? 1 : 0;
-    constexpr int WH = TH + 2 * HALO, WW = TW + 2 * HALO;
-    constexpr int NT = SPATIAL ? 27 : 3;
-    constexpr int NKHW = SPATIAL ? 3 : 1;
-    constexpr int PIECES = 3 * WH * WW * 4;  // 16-byte pieces in one window
-    __shared__ __attribute__((aligned(16))) u16 win[3 * WH * WW * kPosStride];
+    constexpr int WH = TH + 2, WW = TW + 2;
+    constexpr int FPOS = WH * WW;          // window positions of one frame
+    constexpr int PIECES = FPOS * 4;       // 16-byte pieces of one staged window
+    constexpr int PPT = (PIECES + 255) / 256;
+    constexpr int PD = 3;                  // weight-fragment prefetch distance (taps)
+    __shared__ __attribute__((aligned(16))) u16 win[2][FPOS * kPosStride];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -83,9 +127,10 @@ __global__ __launch_bounds__(256) void igemm3d_kernel(IgemmKArgs a) {
     const int oh0 = th * TH, ow0 = tw * TW;
     const int c_begin = split * a.chunks_per_split;
     const int c_end = min(a.nchunks, c_begin + a.chunks_per_split);
-    // live temporal taps: frame od-1+kd inside [0, D)
-    const int kd_lo = od == 0 ? 1 : 0;
+    const int kd_lo = od == 0 ? 1 : 0;            // live temporal taps: frame od-1+kd in [0, D)
     const int kd_hi = od == a.D - 1 ? 1 : 2;
+    const int nkd = kd_hi - kd_lo + 1;
+    const int nst = (c_end - c_begin) * nkd;
 
     f32x4_t acc[MB][NBW];
 #pragma unroll
@@ -95,98 +140,91 @@ __global__ __launch_bounds__(256) void igemm3d_kernel(IgemmKArgs a) {
 
     const int mrow_lane = mt * BM + wm * MB * 16 + (lane & 15);
     const int kofs = (lane >> 4) * 8;
+    const size_t frame_elems = (size_t)a.H * a.W * a.C_in;
 
-    for (int cc = c_begin; cc < c_end; ++cc) {
-        __syncthreads();  // the previous chunk's fragments have been read
-        for (int i = tid; i < PIECES; i += 256) {
-            const int q = i & 3, pos = i >> 2;
-            const int f = pos / (WH * WW);
-            const int rem = pos - f * (WH * WW);
-            const int wh = rem / WW, ww = rem - wh * WW;
-            const int d = od - 1 + f, h = oh0 - HALO + wh, w = ow0 - HALO + ww;
-            const int ci = cc * 32 + q * 8;
+    uint4 stg[PPT];
+    auto fetch = [&](int s) {
+        const int cc = c_begin + s / nkd, kd = kd_lo + s % nkd;
+        const u16 *base = a.x + ((size_t)n * a.D + (od - 1 + kd)) * frame_elems + cc * 32;
+#pragma unroll
+        for (int j = 0; j < PPT; ++j) {
+            const int i = tid + j * 256;
             uint4 v = {0u, 0u, 0u, 0u};
-            if (f >= kd_lo && f <= kd_hi && (unsigned)h < (unsigned)a.H &&
-                (unsigned)w < (unsigned)a.W && ci < a.C_in)
-                v = *reinterpret_cast<const uint4 *>(
-                    a.x + ((((size_t)n * a.D + d) * a.H + h) * a.W + w) * a.C_in + ci);
-            *reinterpret_cast<uint4 *>(win + pos * kPosStride + q * 8) = v;
-        }
-        __syncthreads();
-
-        for (int kd = kd_lo; kd <= kd_hi; ++kd) {
-#pragma unroll
-            for (int ky = 0; ky < NKHW; ++ky) {
-#pragma unroll
-                for (int kx = 0; kx < NKHW; ++kx) {
-                    const int tap = SPATIAL ? kd * 9 + ky * 3 + kx : kd;
-                    const u16 *wb =
-                        a.wp + ((size_t)(cc * NT + tap) * a.Mpad + mrow_lane) * 32 + kofs;
-                    vec8 A[MB];
-#pragma unroll
-                    for (int mb = 0; mb < MB; ++mb)
-                        A[mb] = *reinterpret_cast<const vec8 *>(wb + mb * 16 * 32);
-#pragma unroll
-                    for (int nb = 0; nb < NBW; ++nb) {
-                        const int j = wn * NBW + nb;
-                        const int r = j / NBLK_ROW, c0 = (j % NBLK_ROW) * 16;
-                        const u16 *bp =
-                            win + ((kd * WH + r + ky) * WW + c0 + (lane & 15) + kx) * kPosStride +
-                            kofs;
-                        const vec8 B = *reinterpret_cast<const vec8 *>(bp);
-#pragma unroll
-                        for (int mb = 0; mb < MB; ++mb)
-                            acc[mb][nb] = E::mfma16x16x32(A[mb], B, acc[mb][nb]);
-                    }
-                }
+            if (PIECES % 256 == 0 || i < PIECES) {
+                const int q = i & 3, pos = i >> 2;
+                const int wh = pos / WW, ww = pos - wh * WW;
+                const int h = oh0 - 1 + wh, w = ow0 - 1 + ww;
+                if ((unsigned)h < (unsigned)a.H && (unsigned)w < (unsigned)a.W &&
+                    cc * 32 + q * 8 < a.C_in)
+                    v = *reinterpret_cast<const uint4 *>(base + ((size_t)h * a.W + w) * a.C_in + q * 8);
             }
+            stg[j] = v;
         }
+    };
+    auto commit = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < PPT; ++j) {
+            const int i = tid + j * 256;
+            if (PIECES % 256 == 0 || i < PIECES)
+                *reinterpret_cast<uint4 *>(&win[buf][(i >> 2) * kPosStride + (i & 3) * 8]) = stg[j];
+        }
+    };
+    auto load_a = [&](int s, int j, vec8 *dst) {
+        const int cc = c_begin + s / nkd, kd = kd_lo + s % nkd;
+        const u16 *wb = a.wp + ((size_t)(cc * 27 + kd * 9 + j) * a.Mpad + mrow_lane) * 32 + kofs;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) dst[mb] = *reinterpret_cast<const vec8 *>(wb + mb * 16 * 32);
+    };
+
+    vec8 aq[PD][MB];
+    if (nst > 0) {
+        fetch(0);
+        commit(0);
+#pragma unroll
+        for (int p = 0; p < PD; ++p) load_a(0, p, aq[p]);
+    }
+    __syncthreads();
+
+    for (int s = 0; s < nst; ++s) {
+        const int buf = s & 1;
+        const bool more = s + 1 < nst;
+        if (more) fetch(s + 1);
+        const u16 *wsrc = win[buf];
+#pragma unroll
+        for (int j = 0; j < 9; ++j) {
+            const int ky = j / 3, kx = j % 3;
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb) {
+                const int blk = wn * NBW + nb;
+                const int r = blk / NBLK_ROW, c0 = (blk % NBLK_ROW) * 16;
+                const vec8 B = *reinterpret_cast<const vec8 *>(
+                    wsrc + ((r + ky) * WW + c0 + (lane & 15) + kx) * kPosStride + kofs);
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    acc[mb][nb] = E::mfma16x16x32(aq[j % PD][mb], B, acc[mb][nb]);
+            }
+            // refill this slot with the tap PD ahead (possibly in the next stage)
+            if (j + PD < 9)
+                load_a(s, j + PD, aq[j % PD]);
+            else if (more)
+                load_a(s + 1, j + PD - 9, aq[j % PD]);
+        }
+        if (more) commit(buf ^ 1);
+        __syncthreads();
     }
 
-    // ---- epilogue: bias + activation + one rounding, or fp32 partials for split-K ----
     const size_t P = (size_t)a.N * a.D * a.H * a.W;
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) {
-        const int j = wn * NBW + nb;
-        const int r = j / NBLK_ROW, c0 = (j % NBLK_ROW) * 16;
+        const int blk = wn * NBW + nb;
+        const int r = blk / NBLK_ROW, c0 = (blk % NBLK_ROW) * 16;
         const int oh = oh0 + r, ow = ow0 + c0 + (lane & 15);
         if (oh >= a.H || ow >= a.W) continue;
         const size_t pos = (((size_t)n * a.D + od) * a.H + oh) * a.W + ow;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            const int m0 = mt * BM + wm * MB * 16 + mb * 16 + 4 * (lane >> 4);
-            if (m0 >= a.Mrows) continue;
-            const f32x4_t v = acc[mb][nb];
-            if constexpr (SPLITK) {
-                float *dst = a.partial + ((size_t)split * P + pos) * a.Cy + m0;
-                if (m0 + 3 < a.Mrows && (a.Cy & 3) == 0) {
-                    *reinterpret_cast<f32x4_t *>(dst) = v;
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (m0 + i < a.Mrows) dst[i] = v[i];
-                }
-            } else {
-                u16 o[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float s = v[i];
-                    if (a.bias != nullptr && m0 + i < a.Mrows) s += E::to_f32(a.bias[m0 + i]);
-                    o[i] = E::from_f32(epilogue<EPI>(s));
-                }
-                u16 *dst = a.y + pos * a.Cy + m0;
-                if (m0 + 3 < a.Mrows && (a.Cy & 3) == 0) {
-                    uint2 pk;
-                    pk.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
-                    pk.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
-                    *reinterpret_cast<uint2 *>(dst) = pk;
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (m0 + i < a.Mrows) dst[i] = o[i];
-                }
-            }
-        }
+        for (int mb = 0; mb < MB; ++mb)
+            store_col<BF, EPI, SPLITK>(a, acc[mb][nb], pos, split, P,
+                                       mt * BM + wm * MB * 16 + mb * 16 + 4 * (lane >> 4));
     }
 }
 
@@ -253,12 +291,11 @@ __global__ __launch_bounds__(256) void pack3d_kernel(const u16 *w, u16 *wp, int 
     wp[idx] = v;
 }
 
-template <bool BF, int MB, int NBW, int WM, int WN, int TH, int TW, bool SPATIAL>
+template <bool BF, int MB, int NBW, int WM, int WN, int TH, int TW>
 hipError_t launch_family(const IgemmPlan &pl, const IgemmKArgs &ka, int epi, bool splitk,
                          hipStream_t s) {
     const dim3 grid((unsigned)pl.workgroups), block(256);
-#define CX_IG(EPIV, SK)                                                                       \
-    igemm3d_kernel<BF, MB, NBW, WM, WN, TH, TW, SPATIAL, EPIV, SK><<<grid, block, 0, s>>>(ka)
+#define CX_IG(EPIV, SK) igemm3d_kernel<BF, MB, NBW, WM, WN, TH, TW, EPIV, SK><<<grid, block, 0, s>>>(ka)
     if (splitk) {
         CX_IG(EPI_NONE, true);
     } else if (epi == EPI_RELU) {
@@ -277,11 +314,9 @@ hipError_t launch_igemm_dtype(const IgemmPlan &pl, const IgemmKArgs &ka, int epi
                               hipStream_t s) {
     switch (pl.family) {
         case IG_WIDE:
-            return launch_family<BF, 4, 4, 2, 2, 8, 16, true>(pl, ka, epi, splitk, s);
+            return launch_family<BF, 4, 4, 2, 2, 8, 16>(pl, ka, epi, splitk, s);
         case IG_NARROW:
-            return launch_family<BF, 1, 4, 1, 4, 8, 32, true>(pl, ka, epi, splitk, s);
-        case IG_TEMPORAL:
-            return launch_family<BF, 7, 3, 1, 4, 4, 48, false>(pl, ka, epi, splitk, s);
+            return launch_family<BF, 1, 4, 1, 4, 8, 32>(pl, ka, epi, splitk, s);
     }
     return hipErrorInvalidValue;
 }
@@ -301,15 +336,21 @@ IgemmPlan plan_igemm(int family, int N, int C_in, int C_out, int D, int H, int W
             pl.Mrows = C_out;
             break;
         default:
-            pl.BM = 112, pl.TH = 4, pl.TW = 48, pl.ntaps = 3;
+            pl.BM = 112, pl.TH = 1, pl.TW = 256, pl.ntaps = 3;
             pl.Mrows = kHeadPlaneChannels;
             break;
     }
     pl.Mpad = (pl.Mrows + pl.BM - 1) / pl.BM * pl.BM;
     pl.mtiles = pl.Mpad / pl.BM;
     pl.nchunks = (C_in + 31) / 32;
-    pl.tiles_h = (H + pl.TH - 1) / pl.TH;
-    pl.tiles_w = (W + pl.TW - 1) / pl.TW;
+    if (family == IG_TEMPORAL) {
+        // 256 consecutive positions of one frame per workgroup (no spatial structure needed)
+        pl.tiles_h = 1;
+        pl.tiles_w = (int)(((long long)H * W + 255) / 256);
+    } else {
+        pl.tiles_h = (H + pl.TH - 1) / pl.TH;
+        pl.tiles_w = (W + pl.TW - 1) / pl.TW;
+    }
     const long long base = (long long)N * D * pl.tiles_h * pl.tiles_w * pl.mtiles;
     // Split K when the output alone cannot fill the 256 compute units a few times over.
     int splits = 1;

@@ -23,7 +23,7 @@ hipError_t launch_simt2d(const Simt2dParams &p, hipStream_t stream);
 enum IgemmFamily {
     IG_WIDE = 0,   // 128 output rows x 128 positions per workgroup: C_out > 16
     IG_NARROW = 1, // 16 output rows x 256 positions: C_out <= 16 (the direct head)
-    IG_TEMPORAL = 2 // 112 rows (9 taps x 12 channels) x 192 positions, 3x1x1 taps: split head
+    IG_TEMPORAL = 2 // packing only: 3 temporal taps x 112 rows (9 taps x 12 channels), head kernels
 };
 
 struct IgemmPlan {
@@ -73,5 +73,15 @@ struct StencilParams {
 hipError_t launch_head_stencil(const StencilParams &p, hipStream_t stream);
 
 constexpr int kHeadPlaneChannels = 112;  // 9 taps x 12 channels = 108, padded to 7 x 16
+
+// ---- the head's temporal GEMM (packed like IG_TEMPORAL): plane output or fused stencil -----
+struct HeadGemmParams {
+    const void *x, *wp, *bias;
+    void *out;         // the 112-channel plane (fused = false) or y (fused = true)
+    int N, C_in, C_out, D, H, W;
+    bool bf16, fused;
+    int epilogue;      // fused only
+};
+hipError_t launch_head_gemm(const HeadGemmParams &p, hipStream_t stream);
 
 }  // namespace cx
