@@ -156,10 +156,10 @@ def test_algo_selection_and_buffer_sizes():
     # packed weights: 8 channel chunks x 27 taps x 16 rows x 32 (direct head)
     assert cx.conv3x3x3_packed_weight_bytes(1, 256, 12, 16, 352, 624, 1, 1, 1,
                                             C.ALGO_MFMA) == 8 * 27 * 16 * 32 * 2
-    # split and fused head: 8 chunks x 3 temporal taps x 112 rows x 32
+    # split and fused head: 8 chunks x 3 temporal taps x 128 rows (108 used) x 32
     for algo in (C.ALGO_SPLIT_HEAD, C.ALGO_FUSED_HEAD):
         assert cx.conv3x3x3_packed_weight_bytes(1, 256, 12, 16, 352, 624, 1, 1, 1,
-                                                algo) == 8 * 3 * 112 * 32 * 2
+                                                algo) == 8 * 3 * 128 * 32 * 2
     # mid-decoder conv fills the chip without split-K: no workspace
     assert cx.conv3x3x3_workspace_bytes(1, 256, 256, 16, 176, 312, 1, 1, 1, 0) == 0
     # the small low-res conv splits K over channel chunks: fp32 partials

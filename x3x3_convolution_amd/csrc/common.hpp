@@ -13,6 +13,7 @@ typedef uint16_t u16;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -50,6 +51,9 @@ struct Elem<false> {  // IEEE binary16
     static __device__ __forceinline__ f32x4_t mfma16x16x32(vec8 a, vec8 b, f32x4_t c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
     }
+    static __device__ __forceinline__ f32x16_t mfma32x32x16(vec8 a, vec8 b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
     // a.x*b.x + a.y*b.y + c with an fp32 accumulator
     static __device__ __forceinline__ float dot2(vec2 a, vec2 b, float c) {
         return __builtin_amdgcn_fdot2(a, b, c, false);
@@ -64,6 +68,9 @@ struct Elem<true> {  // bfloat16
     static __device__ __forceinline__ u16 from_f32(float f) { return f32_to_bf16_bits(f); }
     static __device__ __forceinline__ f32x4_t mfma16x16x32(vec8 a, vec8 b, f32x4_t c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x16_t mfma32x32x16(vec8 a, vec8 b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
     static __device__ __forceinline__ float dot2(vec2 a, vec2 b, float c) {
         return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);

@@ -138,43 +138,47 @@ __global__ __launch_bounds__(256) void head_stencil_kernel(StencilKArgs a) {
 
 // ---------------------------------------------------------------------------------------------
 // The head's temporal GEMM: Z[p, m] = sum_{kd, ci} Wt[m, (kd, ci)] * X[frame(p)-1+kd, h(p), w(p), ci]
-// with m = (ky*3+kx)*C_out + co over 112 rows (108 used), K = 3 * C_in.  [head.cu, header
+// with m = (ky*3+kx)*C_out + co (108 rows used, padded to 128), K = 3 * C_in.  [head.cu, header
 // comment: the 3x1x1 convolution whose output channels are the nine spatial taps.]
 //
-// A workgroup (4 waves) owns a strip of 80 computed columns of one frame and walks down a band
-// of rows, four rows (one per wave) per step.  Per step each wave accumulates a 112 x 80 tile
-// (7 x 5 MFMA 16x16x32 blocks) over K.  The K loop is one continuous pipeline over all steps of
-// the band: 32-channel chunks, each with its three temporal taps as k32 steps.
-//   * B (activations): every lane fetches its 16-byte fragment slices with raw buffer loads --
-//     out-of-range positions, frames and channels read as zero without branches (the
-//     convolution's zero padding) -- three k-steps ahead of use into a register ring.
-//   * A (weights, 3 taps x 112 rows x 32 channels = 21 KiB per chunk): fetched one chunk ahead
-//     into registers and written to one of two LDS buffers (rows of 64 B with an XOR swizzle of
-//     the 16-byte slots, so the 16 rows one fragment read touches fall on distinct banks).
+// Matrix cores: v_mfma_f32_32x32x16 -- on gfx950 a single wave keeps the matrix pipe full with
+// this shape, while the 16x16x32 shape needs two waves per SIMD.  Operand layout used: lane l
+// supplies row (A) / column (B) l%32 with the 8 consecutive k values 8*(l/32)..+7; it receives
+// accumulator element i at row 8*(i/4) + 4*(l/32) + i%4, column l%32.  (A and B share the k
+// assignment, so only the row/column assignment matters.)
+//
+// A workgroup (4 waves) owns a strip of 128 computed columns of one frame and walks a band of
+// rows two rows per step: wave w computes row (w/2) of the step, columns 64*(w%2) .. +63, as a
+// 128 x 64 tile (4 x 2 blocks of 32 x 32, 128 accumulators).  K runs as one pipeline over the
+// whole band: 32-channel chunks, each with its three temporal taps as k-steps (2 MFMA k16 each).
+//   * B (activations): raw buffer loads straight into registers -- rows, columns, frames and
+//     channels outside the tensor read as zero without branches (the convolution's zero
+//     padding) -- into a ring that runs three k-steps ahead of use.
+//   * A (weights, 3 taps x 128 rows x 32 channels = 24 KiB per chunk): staged through registers
+//     into LDS buffers (rows of 64 B, 16-byte slots XOR-swizzled so fragment reads spread over
+//     the banks), NABUF-1 chunks ahead; the next k-step's fragments are read into registers
+//     before the current k-step's MFMAs are issued.
 //
 // PLANE mode writes Z rounded to the storage type into the 112-channel plane of the split head.
-// FUSED mode keeps the last six Z rows of the strip (rounded the same way, 108 channels) in an LDS
-// ring and applies the nine-tap stencil + bias + epilogue itself: output row h needs Z rows
-// h-1..h+1 and columns w-1..w+1, so a strip computes 80 columns for 78 outputs and a band
-// computes two extra rows.  The split head's 787 MB plane never touches HBM.
+// FUSED mode keeps the last four Z rows of the strip (rounded the same way, 108 channels) in an
+// LDS ring and applies the nine-tap stencil + bias + epilogue itself: output row h needs Z rows
+// h-1..h+1 and columns w-1..w+1, so a strip computes 128 columns for 126 outputs and a band two
+// extra rows.  The split head's 787 MB plane never touches HBM.
 // ---------------------------------------------------------------------------------------------
-constexpr int kRows = 112;                 // 7 x 16 A rows
-constexpr int kMB = 7;
-constexpr int kNBW = 5;                    // 5 x 16 = 80 positions per wave
-constexpr int kStripPos = kNBW * 16;       // computed columns per strip
-constexpr int kAChunkPieces = 3 * kRows * 4;                 // 1344 16-byte pieces per chunk
-constexpr int kWavesPerRow = 1;           // 1: a wave owns all 112 rows of its Z row;
-                                           // 2: two waves split them as 4 + 3 blocks
-constexpr int kThreads = 256 * kWavesPerRow;
-constexpr int kAPPT = (kAChunkPieces + kThreads - 1) / kThreads;   // A pieces per thread
-constexpr int kABufPieces = kAPPT * kThreads;                      // room for the over-fetch
-constexpr int kMBW = kWavesPerRow == 1 ? kMB : 4;                  // A row blocks per wave
+constexpr int kRows = 128;                 // A rows per temporal tap: 4 x 32 (108 used)
+constexpr int kMB = 4;                     // 32-row blocks
+constexpr int kNB = 2;                     // 32-column blocks per wave
+constexpr int kWaveCols = kNB * 32;        // 64 positions per wave
+constexpr int kStripPos = 2 * kWaveCols;   // 128 computed columns per strip (two waves)
+constexpr int kStepRows = 2;               // Z rows per step (two waves each)
+constexpr int kAChunkPieces = 3 * kRows * 4;                 // 1536 16-byte pieces per chunk
+constexpr int kAPPT = kAChunkPieces / 256;                   // 6 per thread
+constexpr int kPlaneCh = 112;              // rows stored into the split head's plane
 constexpr int kZCh = 108;                  // Z channels kept for the stencil (9 taps x 12)
 constexpr int kZPosBytes = kZCh * 2;
-constexpr int kZRing = 6;
+constexpr int kZRing = 4;                  // Z rows kept: two old + two new
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;  // a buffer offset past any resource range
-constexpr int kChunksPerIter = 2;          // chunks of B fragments in flight
-constexpr int kBRing = 3 * kChunksPerIter; // ring slots, one per k-step (chunk, temporal tap)
+constexpr int kBRing = 3;                  // B ring slots, one per k-step of a chunk
 
 struct HeadGemmKArgs {
     const u16 *x;
@@ -192,20 +196,21 @@ struct HeadGemmKArgs {
 __device__ __forceinline__ int aswz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
 template <bool BF, bool FUSED, int EPI>
-__global__ __launch_bounds__(kThreads, 1) void head_gemm_kernel(HeadGemmKArgs a) {
+__global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
     using E = Elem<BF>;
     typedef typename E::vec8 vec8;
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    __shared__ __attribute__((aligned(16))) uint4 As[2][kABufPieces];
+    // Weight chunks staged in LDS: three buffers let a chunk be staged two chunks ahead with one
+    // barrier per chunk; the fused kernel's LDS also holds the Z ring, so it uses two.
+    constexpr int NABUF = FUSED ? 2 : 3;
+    __shared__ __attribute__((aligned(16))) uint4 As[NABUF][kAChunkPieces];
     __shared__ __attribute__((aligned(16))) uint8_t Zr[FUSED ? kZRing * kStripPos * kZPosBytes : 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int zrw = wave & 3;                 // Z row of the step this wave computes
-    const int mhalf = wave >> 2;              // with two waves per row: blocks 0-3 or 4-6
-    const int mb0 = mhalf * kMBW;
-    const int mcnt = mhalf == 0 ? kMBW : kMB - kMBW;
+    const int zrw = wave >> 1;                // Z row of the step this wave computes
+    const int half = wave & 1;                // which 64 columns of the strip
 
     uint32_t lin = xcd_remap(blockIdx.x, a.total_wg);
     const int od = lin % a.D;          // frames of one (strip, band) are consecutive: they share
@@ -216,13 +221,13 @@ __global__ __launch_bounds__(kThreads, 1) void head_gemm_kernel(HeadGemmKArgs a)
     const int n = lin / a.bands;
 
     const int HW = a.H * a.W;
-    const int col0 = FUSED ? strip * a.strip_out - 1 : strip * kStripPos;
+    const int col0 = (FUSED ? strip * a.strip_out - 1 : strip * kStripPos) + half * kWaveCols;
     const int h_begin = band * a.rows_per_band;
     const int h_end = min(a.H, h_begin + a.rows_per_band);
     const int zrow0 = FUSED ? h_begin - 1 : h_begin;
     const int zrows = FUSED ? h_end - h_begin + 2 : h_end - h_begin;
-    const int nsteps = (zrows + 3) / 4;
-    const int kofs = (lane >> 4) * 8;
+    const int nsteps = (zrows + kStepRows - 1) / kStepRows;
+    const int kofs = (lane >> 5) * 8;         // channel offset of this lane's k slice
 
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(a.x + (size_t)n * a.D * HW * a.C_in), (short)0, (int)a.sample_bytes, 0x00020000);
@@ -230,143 +235,172 @@ __global__ __launch_bounds__(kThreads, 1) void head_gemm_kernel(HeadGemmKArgs a)
         (void *)a.wp, (short)0, (int)a.wp_bytes, 0x00020000);
 
     // Byte offset of this lane's B slice = a per-lane column part (fixed for the whole band)
-    // + a wave-uniform part for (row, frame, chunk).  Anything outside the tensor -- rows,
-    // columns, frames in the temporal padding, channels past C_in -- gets an offset past the
-    // buffer range and reads as zero.
-    uint32_t colpart[kNBW];
+    // + a wave-uniform part for (row, frame, chunk).  Anything outside the tensor gets an offset
+    // past the buffer range and reads as zero.
+    uint32_t colpart[kNB];
 #pragma unroll
-    for (int nb = 0; nb < kNBW; ++nb) {
-        const int w = col0 + nb * 16 + (lane & 15);
+    for (int nb = 0; nb < kNB; ++nb) {
+        const int w = col0 + nb * 32 + (lane & 31);
         colpart[nb] = (unsigned)w < (unsigned)a.W ? (uint32_t)(w * a.C_in + kofs) * 2u : kOutOfRange;
     }
-    auto load_b = [&](int s, vec8 (&dst)[kNBW]) {   // k-step s = 3 * (global chunk) + kd
+    // B slices of k-step s = 3 * (global chunk) + kd: [block][k16 half]
+    auto load_b = [&](int s, vec8 (&dst)[kNB][2]) {
         const int g = s / 3, kd = s - 3 * g;
         const int st = g / a.nchunks, c = g - st * a.nchunks;
-        const int h = zrow0 + st * 4 + zrw;
+        const int h = zrow0 + st * kStepRows + zrw;
         const int f = od - 1 + kd;
-        const bool ok = (unsigned)h < (unsigned)a.H && (unsigned)f < (unsigned)a.D &&
-                        c * 32 + kofs < a.C_in;
         const uint32_t upart = (uint32_t)(((size_t)f * HW + (size_t)h * a.W) * a.C_in + c * 32) * 2u;
 #pragma unroll
-        for (int nb = 0; nb < kNBW; ++nb) {
-            const uint32_t off = (ok && colpart[nb] != kOutOfRange) ? upart + colpart[nb] : kOutOfRange;
-            dst[nb] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
-        }
+        for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                const bool ok = (unsigned)h < (unsigned)a.H && (unsigned)f < (unsigned)a.D &&
+                                c * 32 + k2 * 16 + kofs < a.C_in && colpart[nb] != kOutOfRange;
+                const uint32_t off = ok ? upart + colpart[nb] + k2 * 32u : kOutOfRange;
+                dst[nb][k2] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+            }
     };
-    auto stage_a = [&](int cc, uint4 (&dst)[kAPPT]) {
+    uint4 ast[kAPPT];
+    auto stage_a = [&](int cc) {
 #pragma unroll
         for (int j = 0; j < kAPPT; ++j) {
             const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
-                wr, (uint32_t)(cc * kAChunkPieces + tid + j * kThreads) * 16u, 0, 0);
-            dst[j] = uint4{v.x, v.y, v.z, v.w};
+                wr, (uint32_t)(cc * kAChunkPieces + tid + j * 256) * 16u, 0, 0);
+            ast[j] = uint4{v.x, v.y, v.z, v.w};
         }
     };
-    auto publish_a = [&](int buf, const uint4 (&src)[kAPPT]) {
+    auto publish_a = [&](int buf) {
 #pragma unroll
         for (int j = 0; j < kAPPT; ++j) {
-            const int i = tid + j * kThreads, r = i >> 2;
-            As[buf][r * 4 + ((i & 3) ^ aswz(r))] = src[j];
+            const int i = tid + j * 256, r = i >> 2;
+            As[buf][r * 4 + ((i & 3) ^ aswz(r))] = ast[j];
         }
     };
+    // A fragments of one k-step: [block][k16 half]
+    auto read_a = [&](int buf, int kd, vec8 (&dst)[kMB][2]) {
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                const int r = kd * kRows + mb * 32 + (lane & 31);
+                const int q = k2 * 2 + (lane >> 5);
+                dst[mb][k2] = __builtin_bit_cast(vec8, As[buf][r * 4 + (q ^ aswz(r))]);
+            }
+    };
 
-    f32x4_t acc[kMBW][kNBW];
-    vec8 bq[kBRing][kNBW];       // B ring over k-steps (k-step = (chunk, temporal tap))
-    uint4 ast[kAPPT];
+    f32x16_t acc[kMB][kNB];
+    vec8 bq[kBRing][kNB][2];
+    vec8 af[2][kMB][2];
 
-    // prologue: weights of chunk 0, B of k-steps 0 .. kBRing-1
-    stage_a(0, ast);
+    // prologue: weights of chunks 0 .. NABUF-2 published, B of k-steps 0 .. 2 in flight, A
+    // fragments of k-step 0 in registers
+#pragma unroll
+    for (int c = 0; c < NABUF - 1; ++c) {
+        stage_a(c % a.nchunks);
+        publish_a(c);
+    }
 #pragma unroll
     for (int u = 0; u < kBRing; ++u) load_b(u, bq[u]);
-    publish_a(0, ast);
     __syncthreads();
+    read_a(0, 0, af[0]);
 
-    // Per step: a 112 x 80 x (4 rows) Z tile, K walked kChunksPerIter chunks per iteration so
-    // that ring slots and temporal taps are compile-time constants.  After k-step s's MFMAs its
-    // ring slot is refilled with k-step s + kBRing -- the next step's first k-steps are already
-    // in flight while this step's epilogue runs.  Loads past the band's last k-step are harmless
-    // (they fetch rows of the next band, or read as zero past the tensor), so there are no
-    // per-lane branches in the pipeline.  nchunks is a multiple of kChunksPerIter (the host pads
-    // C_in with zero chunks).
 #pragma unroll 1
     for (int step = 0; step < nsteps; ++step) {
 #pragma unroll
-        for (int i = 0; i < kMBW; ++i)
+        for (int i = 0; i < kMB; ++i)
 #pragma unroll
-            for (int j = 0; j < kNBW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < kNB; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 #pragma unroll 1
-        for (int cp = 0; cp < a.nchunks; cp += kChunksPerIter) {
-            const int g0 = step * a.nchunks + cp;
+        for (int cc = 0; cc < a.nchunks; ++cc) {
+            const int g = step * a.nchunks + cc;
+            const int buf = g % NABUF;
 #pragma unroll
-            for (int u = 0; u < kBRing; ++u) {
-                const int kd = u % 3;
-                const int cc = cp + u / 3;
-                const int buf = (g0 + u / 3) & 1;
-                if (kd == 0) stage_a(cc + 1 == a.nchunks ? 0 : cc + 1, ast);
+            for (int kd = 0; kd < 3; ++kd) {
+                if (kd == 0) stage_a((cc + NABUF - 1) % a.nchunks);
+                // the next k-step's A fragments (for kd == 2 the next chunk's, when it is
+                // already published) are read before this k-step's MFMAs
+                if (kd < 2)
+                    read_a(buf, kd + 1, af[(kd + 1) & 1]);
+                else if (NABUF == 3)
+                    read_a((g + 1) % NABUF, 0, af[1]);
 #pragma unroll
-                for (int mb = 0; mb < kMBW; ++mb) {
-                    if (mb < mcnt) {
-                        const int r = kd * kRows + (mb0 + mb) * 16 + (lane & 15);
-                        const vec8 A = __builtin_bit_cast(vec8, As[buf][r * 4 + ((lane >> 4) ^ aswz(r))]);
+                for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-                        for (int nb = 0; nb < kNBW; ++nb)
-                            acc[mb][nb] = E::mfma16x16x32(A, bq[u][nb], acc[mb][nb]);
-                    }
-                }
-                load_b(3 * g0 + u + kBRing, bq[u]);
-                if (kd == 2) {   // end of a chunk: publish the next chunk's weights
-                    publish_a(buf ^ 1, ast);
+                    for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+                        for (int nb = 0; nb < kNB; ++nb)
+                            acc[mb][nb] = E::mfma32x32x16(af[kd & 1][mb][k2], bq[kd][nb][k2], acc[mb][nb]);
+                load_b(3 * g + kd + kBRing, bq[kd]);
+                if (kd == 2) {   // end of a chunk: publish the chunk NABUF-1 ahead
+                    publish_a((g + NABUF - 1) % NABUF);
                     __syncthreads();
-                }
-            }
-        }
-
-        // ---- the step's Z tile is complete ----
-        const int zr = zrow0 + step * 4 + zrw;   // this wave's Z row
-        if constexpr (!FUSED) {
+                    if (NABUF == 2) read_a((g + 1) % NABUF, 0, af[0]);
+                    else {
 #pragma unroll
-            for (int nb = 0; nb < kNBW; ++nb) {
-                const int w = col0 + nb * 16 + (lane & 15);
-                if (zr < h_end && w < a.W) {
-                    u16 *dst = a.out + (((size_t)n * a.D + od) * HW + (size_t)zr * a.W + w) * kHeadPlaneChannels;
-#pragma unroll
-                    for (int mb = 0; mb < kMBW; ++mb) {
-                        if (mb < mcnt) {
-                            const int m0 = (mb0 + mb) * 16 + 4 * (lane >> 4);
-                            const f32x4_t v = acc[mb][nb];
-                            uint2 pk;
-                            pk.x = (uint32_t)E::from_f32(v[0]) | ((uint32_t)E::from_f32(v[1]) << 16);
-                            pk.y = (uint32_t)E::from_f32(v[2]) | ((uint32_t)E::from_f32(v[3]) << 16);
-                            *reinterpret_cast<uint2 *>(dst + m0) = pk;
+                        for (int mb = 0; mb < kMB; ++mb) {
+                            af[0][mb][0] = af[1][mb][0];
+                            af[0][mb][1] = af[1][mb][1];
                         }
                     }
                 }
             }
-        } else {
-            // Z rows -> ring slot ((zr - zrow0) mod 6), rounded once to the storage type
-            uint8_t *zrow = Zr + ((step * 4 + zrw) % kZRing) * (kStripPos * kZPosBytes);
+        }
+
+        // ---- the step's Z tile is complete: this wave holds rows 0..127 of 64 columns ----
+        const int zr = zrow0 + step * kStepRows + zrw;   // this wave's Z row
+        if constexpr (!FUSED) {
+            if (zr < h_end) {
 #pragma unroll
-            for (int nb = 0; nb < kNBW; ++nb) {
-                const int pos = nb * 16 + (lane & 15);
+                for (int nb = 0; nb < kNB; ++nb) {
+                    const int w = col0 + nb * 32 + (lane & 31);
+                    if (w < a.W) {
+                        u16 *dst = a.out + (((size_t)n * a.D + od) * HW + (size_t)zr * a.W + w) * kPlaneCh;
 #pragma unroll
-                for (int mb = 0; mb < kMBW; ++mb) {
-                    const int m0 = (mb0 + mb) * 16 + 4 * (lane >> 4);
-                    if (mb < mcnt && m0 < kZCh) {
-                        const f32x4_t v = acc[mb][nb];
-                        uint2 pk;
-                        pk.x = (uint32_t)E::from_f32(v[0]) | ((uint32_t)E::from_f32(v[1]) << 16);
-                        pk.y = (uint32_t)E::from_f32(v[2]) | ((uint32_t)E::from_f32(v[3]) << 16);
-                        *reinterpret_cast<uint2 *>(zrow + pos * kZPosBytes + m0 * 2) = pk;
+                        for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                const int m0 = mb * 32 + 8 * j + 4 * (lane >> 5);
+                                if (m0 < kPlaneCh) {
+                                    const f32x16_t v = acc[mb][nb];
+                                    uint2 pk;
+                                    pk.x = (uint32_t)E::from_f32(v[4 * j]) | ((uint32_t)E::from_f32(v[4 * j + 1]) << 16);
+                                    pk.y = (uint32_t)E::from_f32(v[4 * j + 2]) | ((uint32_t)E::from_f32(v[4 * j + 3]) << 16);
+                                    *reinterpret_cast<uint2 *>(dst + m0) = pk;
+                                }
+                            }
                     }
                 }
             }
+        } else {
+            // Z rows -> ring slot ((zr - zrow0) mod 4), rounded once to the storage type
+            uint8_t *zrow = Zr + ((step * kStepRows + zrw) % kZRing) * (kStripPos * kZPosBytes);
+#pragma unroll
+            for (int nb = 0; nb < kNB; ++nb) {
+                const int pos = half * kWaveCols + nb * 32 + (lane & 31);
+#pragma unroll
+                for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int m0 = mb * 32 + 8 * j + 4 * (lane >> 5);
+                        if (m0 < kZCh) {
+                            const f32x16_t v = acc[mb][nb];
+                            uint2 pk;
+                            pk.x = (uint32_t)E::from_f32(v[4 * j]) | ((uint32_t)E::from_f32(v[4 * j + 1]) << 16);
+                            pk.y = (uint32_t)E::from_f32(v[4 * j + 2]) | ((uint32_t)E::from_f32(v[4 * j + 3]) << 16);
+                            *reinterpret_cast<uint2 *>(zrow + pos * kZPosBytes + m0 * 2) = pk;
+                        }
+                    }
+            }
             __syncthreads();
-            // output rows completed by this step: h in [h_begin+4*step-2, h_begin+4*step+1]
-            const int hlo = max(h_begin, h_begin + 4 * step - 2);
-            const int hhi = min(h_end, h_begin + 4 * step + 2);
+            // output rows completed by this step: h in [h_begin+2*step-2, h_begin+2*step-1]
+            const int hlo = max(h_begin, h_begin + kStepRows * step - 2);
+            const int hhi = min(h_end, h_begin + kStepRows * step);
             const int groups = (a.C_out + 3) / 4;
             const int per_row = a.strip_out * groups;
             const bool vec = (a.C_out & 3) == 0;
-            for (int item = tid; item < (hhi - hlo) * per_row; item += kThreads) {
+            for (int item = tid; item < (hhi - hlo) * per_row; item += 256) {
                 const int hr = item / per_row;
                 const int rem = item - hr * per_row;
                 const int c = rem / groups, grp = rem - c * groups;
@@ -461,22 +495,28 @@ hipError_t launch_head_gemm(const HeadGemmParams &p, hipStream_t stream) {
     a.out = static_cast<u16 *>(p.out);
     a.N = p.N, a.C_in = p.C_in, a.C_out = p.C_out, a.D = p.D, a.H = p.H, a.W = p.W;
     a.nchunks = (p.C_in + 31) / 32;
-    a.nchunks = (a.nchunks + kChunksPerIter - 1) / kChunksPerIter * kChunksPerIter;
     a.strip_out = p.fused ? kStripPos - 2 : kStripPos;
     a.strips = (p.W + a.strip_out - 1) / a.strip_out;
-    // one workgroup per CU is resident (LDS and registers); aim for about one full wave of
-    // workgroups, each band long enough that its two halo rows are a small overhead
+    // One workgroup per CU is resident (LDS and registers).  Pick the band count that minimises
+    // (rounds of 256 workgroups) x (rows a workgroup computes, halo included).
     const long long cols = (long long)p.N * p.D * a.strips;
-    int bands = (int)((256 + cols - 1) / cols);
-    if (bands < 1) bands = 1;
-    if (bands > p.H) bands = p.H;
-    a.rows_per_band = (p.H + bands - 1) / bands;
+    const int halo = p.fused ? 2 : 0;
+    long long best = -1;
+    int best_bands = 1;
+    for (int bands = 1; bands <= p.H && bands <= 64; ++bands) {
+        const int rpb = (p.H + bands - 1) / bands;
+        const int real_bands = (p.H + rpb - 1) / rpb;
+        const long long rounds = (cols * real_bands + 255) / 256;
+        const long long cost = rounds * (((rpb + halo) + kStepRows - 1) / kStepRows);
+        if (best < 0 || cost < best) best = cost, best_bands = real_bands;
+    }
+    a.rows_per_band = (p.H + best_bands - 1) / best_bands;
     a.bands = (p.H + a.rows_per_band - 1) / a.rows_per_band;
     a.sample_bytes = (uint32_t)((size_t)p.D * p.H * p.W * p.C_in * 2);
-    a.wp_bytes = (uint32_t)((size_t)((p.C_in + 31) / 32) * kAChunkPieces * 16);
+    a.wp_bytes = (uint32_t)((size_t)a.nchunks * kAChunkPieces * 16);
     const long long wgs = cols * a.bands;
     a.total_wg = (uint32_t)wgs;
-    const dim3 grid((unsigned)wgs), block(kThreads);
+    const dim3 grid((unsigned)wgs), block(256);
 #define CX_HG(BFV, FV, EPIV) head_gemm_kernel<BFV, FV, EPIV><<<grid, block, 0, stream>>>(a)
     if (!p.fused) {
         if (p.bf16) CX_HG(true, false, EPI_NONE);

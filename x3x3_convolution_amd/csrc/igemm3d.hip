@@ -335,9 +335,9 @@ IgemmPlan plan_igemm(int family, int N, int C_in, int C_out, int D, int H, int W
             pl.BM = 16, pl.TH = 8, pl.TW = 32, pl.ntaps = 27;
             pl.Mrows = C_out;
             break;
-        default:
-            pl.BM = 112, pl.TH = 1, pl.TW = 256, pl.ntaps = 3;
-            pl.Mrows = kHeadPlaneChannels;
+        default:   // the head kernels: 3 temporal taps x 128 rows (9 * C_out used)
+            pl.BM = 128, pl.TH = 1, pl.TW = 256, pl.ntaps = 3;
+            pl.Mrows = 128;
             break;
     }
     pl.Mpad = (pl.Mrows + pl.BM - 1) / pl.BM * pl.BM;
