@@ -183,7 +183,7 @@ def run_head(args, wl, stream):
         kms = results["fused"]["kernel_ms"]["head_fused"]
         bytes_f = xb + yb + wl.C_out * wl.C_in * 27 * 2 + bb
         ach = bytes_f / (kms * 1e-3) / 1e9
-        roof = dict(kernel="head_gemm_kernel (fused: temporal GEMM + LDS stencil + clamp)",
+        roof = dict(kernel="head_gemm_kernel (fused: temporal GEMM + in-register nine-tap stencil + clamp)",
                     bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=ach / HBM_PEAK_GBS, mfma_tflops=flop_t / (kms * 1e-3) / 1e12,
                     mfma_frac=flop_t / (kms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,

@@ -178,16 +178,24 @@ def test_3d_full_size_sampled(name, algo):
     assert_within(m, activated=wl.epilogue != "none")
 
 
-def test_fused_head_equals_split_head_bitwise():
-    """The fused head keeps the split head's value path (the same temporal GEMM, the same bf16
-    rounding of the tap-channel plane, the same nine-tap sum order): full-size outputs must be
-    identical bit for bit."""
+def test_fused_head_at_least_as_accurate_as_split_head():
+    """The fused head keeps the temporal GEMM's fp32 sums through the nine-tap stencil, the split
+    head rounds them to bf16 in its plane.  On the full-size head the fused outputs must be
+    within tolerance of the oracle and no less accurate than the split head's, at the same
+    sampled points (errors against the unrounded fp64 oracle value)."""
     wl = si.WORKLOADS["c3"]
     x, w, b = si.make_inputs(wl, device=DEV)
-    ys = run_3d(x, w, b, wl.epilogue, C.ALGO_SPLIT_HEAD)
-    yf = run_3d(x, w, b, wl.epilogue, C.ALGO_FUSED_HEAD, guarded=True)
-    diff = (ys.view(torch.int16) != yf.view(torch.int16)).sum().item()
-    assert diff == 0, "%d outputs differ between the split and the fused head" % diff
+    pts = sample_points_3d(wl.N, wl.D, wl.H, wl.W, 2000, seed=5)
+    ref = oracle.conv3d_points(bits(x), bits(w), bits(b), pts, 1, oracle.BF16,
+                               oracle.EPI_CLAMP1, oracle.CHANNELS_LAST)
+    errs = {}
+    for algo in (C.ALGO_SPLIT_HEAD, C.ALGO_FUSED_HEAD):
+        y = run_3d(x, w, b, wl.epilogue, algo, guarded=algo == C.ALGO_FUSED_HEAD)
+        got = oracle.decode(gather_3d(y, pts), oracle.BF16).reshape(ref.shape)
+        errs[algo] = float(np.sqrt(np.mean((got - ref) ** 2)))
+        del y
+    _say("rms error vs fp64: split %.3e fused %.3e" % (errs[C.ALGO_SPLIT_HEAD], errs[C.ALGO_FUSED_HEAD]))
+    assert errs[C.ALGO_FUSED_HEAD] <= errs[C.ALGO_SPLIT_HEAD] * 1.02
 
 
 def test_split_head_plane_stage_matches_oracle_plane():

@@ -23,12 +23,10 @@ enum { EPI_NONE = 0, EPI_RELU = 1, EPI_CLAMP1 = 2 };
 __device__ __forceinline__ float bf16_bits_to_f32(u16 b) {
     return __uint_as_float((uint32_t)b << 16);
 }
-// Round to nearest, ties to even; NaN stays a (quiet) NaN.
+// v_cvt_pk_bf16_f32: round to nearest, ties to even (the kernels run in the default round mode
+// with fp32 denormals kept), overflow gives infinity, NaN stays a quiet NaN.  Branch-free.
 __device__ __forceinline__ u16 f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u16)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (u16)(u >> 16);
+    return __builtin_bit_cast(u16, (__bf16)f);
 }
 __device__ __forceinline__ float f16_bits_to_f32(u16 h) {
     return (float)__builtin_bit_cast(_Float16, h);

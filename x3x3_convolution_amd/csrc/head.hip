@@ -138,47 +138,67 @@ __global__ __launch_bounds__(256) void head_stencil_kernel(StencilKArgs a) {
 
 // ---------------------------------------------------------------------------------------------
 // The head's temporal GEMM: Z[p, m] = sum_{kd, ci} Wt[m, (kd, ci)] * X[frame(p)-1+kd, h(p), w(p), ci]
-// with m = (ky*3+kx)*C_out + co (108 rows used, padded to 128), K = 3 * C_in.  [head.cu, header
-// comment: the 3x1x1 convolution whose output channels are the nine spatial taps.]
+// where GEMM row m stands for one spatial tap (ky, kx) of one output channel co (108 of 128 rows
+// used), K = 3 * C_in.  [head.cu, header comment: the 3x1x1 convolution whose output channels
+// are the nine spatial taps.]
 //
-// Matrix cores: v_mfma_f32_32x32x16 -- on gfx950 a single wave keeps the matrix pipe full with
-// this shape, while the 16x16x32 shape needs two waves per SIMD.  Operand layout used: lane l
-// supplies row (A) / column (B) l%32 with the 8 consecutive k values 8*(l/32)..+7; it receives
-// accumulator element i at row 8*(i/4) + 4*(l/32) + i%4, column l%32.  (A and B share the k
-// assignment, so only the row/column assignment matters.)
+// Matrix cores: v_mfma_f32_32x32x16 (one wave per SIMD keeps the pipe full with this shape).
+// Lane l supplies row (A) / column (B) l%32 with 8 k values (the k half l/32) of a 16-wide k
+// slice, and receives accumulator element i at row 8*(i/4) + 4*(l/32) + i%4, column l%32.
 //
-// A workgroup (4 waves) owns a strip of 128 computed columns of one frame and walks a band of
-// rows two rows per step: wave w computes row (w/2) of the step, columns 64*(w%2) .. +63, as a
-// 128 x 64 tile (4 x 2 blocks of 32 x 32, 128 accumulators).  K runs as one pipeline over the
-// whole band: 32-channel chunks, each with its three temporal taps as k-steps (2 MFMA k16 each).
-//   * B (activations): raw buffer loads straight into registers -- rows, columns, frames and
-//     channels outside the tensor read as zero without branches (the convolution's zero
-//     padding) -- into a ring that runs three k-steps ahead of use.
-//   * A (weights, 3 taps x 128 rows x 32 channels = 24 KiB per chunk): staged through registers
-//     into LDS buffers (rows of 64 B, 16-byte slots XOR-swizzled so fragment reads spread over
-//     the banks), NABUF-1 chunks ahead; the next k-step's fragments are read into registers
-//     before the current k-step's MFMAs are issued.
+// Work split: a workgroup is four waves on four consecutive output frames of one (band, strip);
+// each wave walks its band one row at a time.  Per row a wave computes a 128 x 128 tile (GEMM rows
+// x 128 columns of the row): 4 x 4 blocks of 32 x 32, all 256 accumulators.  Column block nb,
+// lane column j holds position p = 4*j + nb of the wave's strip, so the horizontal neighbours of
+// a position sit in the same lane (blocks nb-1, nb+1) except at nb = 0 / 3, where they are one
+// lane away (a DPP wavefront shift).
 //
-// PLANE mode writes Z rounded to the storage type into the 112-channel plane of the split head.
-// FUSED mode keeps the last four Z rows of the strip (rounded the same way, 108 channels) in an
-// LDS ring and applies the nine-tap stencil + bias + epilogue itself: output row h needs Z rows
-// h-1..h+1 and columns w-1..w+1, so a strip computes 128 columns for 126 outputs and a band two
-// extra rows.  The split head's 787 MB plane never touches HBM.
+// Row roles (set by the weight packing): accumulator register i of block mb in lane half h is
+// slot t = 16*mb + i of that half; slot t < 54 holds spatial tap t/6 of output channel 6*h + t%6.
+// So every lane owns six output channels of its four positions, with all nine taps in registers.
+//
+// K order: 64-channel chunks (one 128-byte cache line of a position), and in a chunk the three
+// temporal taps one after the other, each as four k16 slices.  Slice s takes channels
+// 32*h + 8*s .. +7 from lane half h, so for one tap the four slices of a position are the four
+// consecutive 16-byte pieces of the lane's half line.  A tap runs as two half-taps (column blocks
+// 0-1, then 2-3), each four slices of 4 x 2 MFMAs.
+//   * B (activations): raw buffer loads straight into registers; the four pieces of a lane's
+//     half line are loaded back to back, so every cache line is fetched whole, once.  Rows,
+//     columns, frames and channels outside the tensor read as zero without branches (the
+//     convolution's zero padding).  A ring of four half-taps: each half-tap starts by loading
+//     the half-tap three ahead.
+//   * A (weights, 3 taps x 128 rows x 64 channels = 48 KiB per chunk): copied global -> LDS by
+//     the buffer unit itself (LDS DMA, no registers), two buffers, each chunk issued a whole
+//     chunk before it is needed.  The packing stores every 128-byte row with its eight 16-byte
+//     pieces already XOR-permuted, so the fragment reads spread over the LDS banks.
+//
+// PLANE mode stores Z, rounded to the storage type, as the 112-channel plane of the split head.
+// FUSED mode applies the nine-tap stencil in registers: the horizontal taps combine neighbouring
+// positions, the vertical taps are carried from row to row (two fp32 partial sums per output),
+// and bias + epilogue are applied once per output.  Output row h needs Z rows h-1 .. h+1 and
+// columns w-1 .. w+1, so a strip computes 128 columns for 126 outputs and a band two extra rows.
+// Nothing of Z is rounded or stored: the fused head keeps fp32 from the GEMM to the epilogue.
 // ---------------------------------------------------------------------------------------------
-constexpr int kRows = 128;                 // A rows per temporal tap: 4 x 32 (108 used)
-constexpr int kMB = 4;                     // 32-row blocks
-constexpr int kNB = 2;                     // 32-column blocks per wave
-constexpr int kWaveCols = kNB * 32;        // 64 positions per wave
-constexpr int kStripPos = 2 * kWaveCols;   // 128 computed columns per strip (two waves)
-constexpr int kStepRows = 2;               // Z rows per step (two waves each)
-constexpr int kAChunkPieces = 3 * kRows * 4;                 // 1536 16-byte pieces per chunk
-constexpr int kAPPT = kAChunkPieces / 256;                   // 6 per thread
-constexpr int kPlaneCh = 112;              // rows stored into the split head's plane
-constexpr int kZCh = 108;                  // Z channels kept for the stencil (9 taps x 12)
-constexpr int kZPosBytes = kZCh * 2;
-constexpr int kZRing = 4;                  // Z rows kept: two old + two new
-constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;  // a buffer offset past any resource range
-constexpr int kBRing = 3;                  // B ring slots, one per k-step of a chunk
+constexpr int kMB = 4;                  // 32-row blocks: 128 GEMM rows per temporal tap
+constexpr int kNB = 4;                  // 32-column blocks per wave
+constexpr int kWavePos = 32 * kNB;      // 128 positions per wave and row
+constexpr int kSlices = 4;              // k16 slices per tap of a 64-channel chunk
+constexpr int kHalves = 6;              // half-taps per chunk
+constexpr int kRing = 4;                // B ring depth in half-taps
+constexpr int kLoadsPerHalf = 2 * kSlices;   // B loads per half-tap
+constexpr int kDmaPerWave = kHeadChunkPieces / 256;  // 12 LDS-DMA copies of 1 KiB per wave
+constexpr int kHalfCo = 6;              // output channels per lane half
+constexpr int kPlaneCh = kHeadPlaneChannels;
+constexpr uint32_t kOff = 0xFFFFFFFFu;  // an offset past any buffer range; saturating adds keep it
+
+// s_waitcnt immediates: vmcnt is split over bits 3:0 and 15:14; expcnt / lgkmcnt left open.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
+// Every half-tap starts with its B loads.  The copy of chunk g+1 is issued at the barrier before
+// the last slice of chunk g-1 and must be complete at the same point of chunk g: the operations
+// a wave issues in between are the B loads of the six half-taps of chunk g.
+constexpr int kVmAfterCopy = kLoadsPerHalf * kHalves;
+static_assert(kVmAfterCopy < 64, "vmcnt holds 6 bits");
 
 struct HeadGemmKArgs {
     const u16 *x;
@@ -186,267 +206,344 @@ struct HeadGemmKArgs {
     const u16 *bias;
     u16 *out;          // the plane (PLANE) or y (FUSED)
     int N, C_in, C_out, D, H, W;
-    int nchunks;
-    int rows_per_band, bands, strips, strip_out;
+    int nchunks;       // 64-channel chunks per Z row, even (the padding reads zeros)
+    int rows_per_band, bands, strips, strip_out, fgroups;
     uint32_t sample_bytes;  // bytes of one sample of x (buffer-resource range)
     uint32_t wp_bytes;
     uint32_t total_wg;
 };
 
-__device__ __forceinline__ int aswz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+// Workgroup barrier without a memory fence (the waits before it are explicit), kept in place
+// by the compiler.
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// Marks an accumulator block as redefined here (no code): values of the block are unpacked into
+// VGPRs only after this point, so an epilogue that walks the blocks in order keeps one or a few
+// blocks unpacked at a time instead of all 256 accumulators.
+__device__ __forceinline__ void touch(f32x16_t &v) { asm volatile("" : "+a"(v)::"memory"); }
 
-template <bool BF, bool FUSED, int EPI>
+// CO12: C_out == 12, every lane stores its six channels as one 12-byte vector.
+template <bool BF, bool FUSED, int EPI, bool CO12>
 __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
     using E = Elem<BF>;
     typedef typename E::vec8 vec8;
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    // Weight chunks staged in LDS: three buffers let a chunk be staged two chunks ahead with one
-    // barrier per chunk; the fused kernel's LDS also holds the Z ring, so it uses two.
-    constexpr int NABUF = FUSED ? 2 : 3;
-    __shared__ __attribute__((aligned(16))) uint4 As[NABUF][kAChunkPieces];
-    __shared__ __attribute__((aligned(16))) uint8_t Zr[FUSED ? kZRing * kStripPos * kZPosBytes : 16];
+    typedef __attribute__((address_space(3))) void lds_void;
+    // Two weight buffers (even / odd chunks), separate objects so the compiler can tell that the
+    // copy into one never overlaps the fragment reads from the other.
+    __shared__ __attribute__((aligned(16))) uint4 As0[kHeadChunkPieces];
+    __shared__ __attribute__((aligned(16))) uint4 As1[kHeadChunkPieces];
+    // FUSED: the two carried partial sums of every lane's 6 channels x 4 positions, per wave
+    // (cA: the output row before the next Z row, cB: the output row of the next Z row), as
+    // float4 {cA0..3}, {cA4, cA5, cB0, cB1}, {cB2..5}.  Private to each wave.
+    __shared__ float4 carry[FUSED ? 4 : 1][kNB][3][64];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int zrw = wave >> 1;                // Z row of the step this wave computes
-    const int half = wave & 1;                // which 64 columns of the strip
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int j = lane & 31, hh = lane >> 5;
 
     uint32_t lin = xcd_remap(blockIdx.x, a.total_wg);
-    const int od = lin % a.D;          // frames of one (strip, band) are consecutive: they share
-    lin /= a.D;                        // input frames, so they run on one XCD's L2
+    const int fg = lin % a.fgroups;    // frame groups of one (strip, band) are consecutive: they
+    lin /= a.fgroups;                  // share input frames, so they run on one XCD's L2
     const int strip = lin % a.strips;
     lin /= a.strips;
     const int band = lin % a.bands;
     const int n = lin / a.bands;
+    const int od = fg * 4 + wave;      // this wave's output frame (>= D: computes, stores nothing)
 
     const int HW = a.H * a.W;
-    const int col0 = (FUSED ? strip * a.strip_out - 1 : strip * kStripPos) + half * kWaveCols;
+    const int w0 = FUSED ? strip * a.strip_out - 1 : strip * kWavePos;   // column of position 0
     const int h_begin = band * a.rows_per_band;
     const int h_end = min(a.H, h_begin + a.rows_per_band);
     const int zrow0 = FUSED ? h_begin - 1 : h_begin;
-    const int zrows = FUSED ? h_end - h_begin + 2 : h_end - h_begin;
-    const int nsteps = (zrows + kStepRows - 1) / kStepRows;
-    const int kofs = (lane >> 5) * 8;         // channel offset of this lane's k slice
+    const int nsteps = (h_end - h_begin) + (FUSED ? 2 : 0);   // Z rows, the same in every wave
+    const int nch = a.nchunks;
 
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(a.x + (size_t)n * a.D * HW * a.C_in), (short)0, (int)a.sample_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
         (void *)a.wp, (short)0, (int)a.wp_bytes, 0x00020000);
 
-    // Byte offset of this lane's B slice = a per-lane column part (fixed for the whole band)
-    // + a wave-uniform part for (row, frame, chunk).  Anything outside the tensor gets an offset
-    // past the buffer range and reads as zero.
+    // Byte offset of a B piece = a per-lane column part (fixed for the whole band) + a part for
+    // (row, frame, chunk, lane half, slice), added with saturation so that either part out of
+    // range makes the load read zero.
     uint32_t colpart[kNB];
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
-        const int w = col0 + nb * 32 + (lane & 31);
-        colpart[nb] = (unsigned)w < (unsigned)a.W ? (uint32_t)(w * a.C_in + kofs) * 2u : kOutOfRange;
+        const int w = w0 + 4 * j + nb;
+        colpart[nb] = (unsigned)w < (unsigned)a.W ? (uint32_t)(w * a.C_in) * 2u : kOff;
     }
-    // B slices of k-step s = 3 * (global chunk) + kd: [block][k16 half]
-    auto load_b = [&](int s, vec8 (&dst)[kNB][2]) {
-        const int g = s / 3, kd = s - 3 * g;
-        const int st = g / a.nchunks, c = g - st * a.nchunks;
-        const int h = zrow0 + st * kStepRows + zrw;
-        const int f = od - 1 + kd;
-        const uint32_t upart = (uint32_t)(((size_t)f * HW + (size_t)h * a.W) * a.C_in + c * 32) * 2u;
+    // per-slice offsets of one tap (Z row st, chunk c, tap kd) for this lane
+    auto tap_offsets = [&](int st, int c, int kd, uint32_t (&up)[kSlices]) {
+        const int row = zrow0 + st, f = od - 1 + kd;
+        const bool ok = (unsigned)row < (unsigned)a.H && (unsigned)f < (unsigned)a.D;
+        const uint32_t base = (uint32_t)((((size_t)f * HW + (size_t)row * a.W) * a.C_in + c * 64 + 32 * hh) * 2u);
 #pragma unroll
-        for (int nb = 0; nb < kNB; ++nb)
-#pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) {
-                const bool ok = (unsigned)h < (unsigned)a.H && (unsigned)f < (unsigned)a.D &&
-                                c * 32 + k2 * 16 + kofs < a.C_in && colpart[nb] != kOutOfRange;
-                const uint32_t off = ok ? upart + colpart[nb] + k2 * 32u : kOutOfRange;
-                dst[nb][k2] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
-            }
+        for (int sl = 0; sl < kSlices; ++sl)
+            up[sl] = ok && c * 64 + 32 * hh + 8 * sl < a.C_in ? base + 16u * sl : kOff;
     };
-    uint4 ast[kAPPT];
-    auto stage_a = [&](int cc) {
+    // B of a half-tap: blocks 2*hp and 2*hp+1, each the four slices of the lane's half line
+    // back to back
+    auto load_half = [&](int st, int c, int kd, int hp, vec8 (&dst)[2][kSlices]) {
+        uint32_t up[kSlices];
+        tap_offsets(st, c, kd, up);
 #pragma unroll
-        for (int j = 0; j < kAPPT; ++j) {
-            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
-                wr, (uint32_t)(cc * kAChunkPieces + tid + j * 256) * 16u, 0, 0);
-            ast[j] = uint4{v.x, v.y, v.z, v.w};
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int sl = 0; sl < kSlices; ++sl)
+                dst[b][sl] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(
+                    xr, __builtin_elementwise_add_sat(up[sl], colpart[2 * hp + b]), 0, 0));
+    };
+    // LDS DMA of packed weight chunk cc into buffer dstbuf: each wave copies 12 KiB.  Chunks past
+    // the packed ones (the even padding) lie past the resource range and copy zeros.
+    auto copy_a = [&](int cc, uint4 *dstbuf) {
+#pragma unroll
+        for (int q = 0; q < kDmaPerWave; ++q) {
+            const int piece = wave * (kDmaPerWave * 64) + q * 64;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                wr, (lds_void *)&dstbuf[piece], 16,
+                (uint32_t)((cc * kHeadChunkPieces + piece + lane) * 16), 0, 0, 0);
         }
     };
-    auto publish_a = [&](int buf) {
+    const int swz = head_lds_swizzle(j);   // the swizzle of rows kd*128 + mb*32 + j
+    // A fragments of tap kd, slice sl: piece 4*hh + sl of each row
+    auto read_a = [&](const uint4 *srcbuf, int kd, int sl, vec8 (&dst)[kMB]) {
 #pragma unroll
-        for (int j = 0; j < kAPPT; ++j) {
-            const int i = tid + j * 256, r = i >> 2;
-            As[buf][r * 4 + ((i & 3) ^ aswz(r))] = ast[j];
+        for (int mb = 0; mb < kMB; ++mb) {
+            const int r = kd * 128 + mb * 32 + j;
+            dst[mb] = __builtin_bit_cast(vec8, srcbuf[r * 8 + ((4 * hh + sl) ^ swz)]);
         }
-    };
-    // A fragments of one k-step: [block][k16 half]
-    auto read_a = [&](int buf, int kd, vec8 (&dst)[kMB][2]) {
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) {
-                const int r = kd * kRows + mb * 32 + (lane & 31);
-                const int q = k2 * 2 + (lane >> 5);
-                dst[mb][k2] = __builtin_bit_cast(vec8, As[buf][r * 4 + (q ^ aswz(r))]);
-            }
     };
 
     f32x16_t acc[kMB][kNB];
-    vec8 bq[kBRing][kNB][2];
-    vec8 af[2][kMB][2];
+    vec8 bq[kRing][2][kSlices];   // [half-tap slot][block of the pair][slice]
+    vec8 af[2][kMB];
+    const f32x16_t zero = {};
 
-    // prologue: weights of chunks 0 .. NABUF-2 published, B of k-steps 0 .. 2 in flight, A
-    // fragments of k-step 0 in registers
+    // FUSED: the bias of the lane's six output channels; carried sums start at zero
+    float b6[kHalfCo];
 #pragma unroll
-    for (int c = 0; c < NABUF - 1; ++c) {
-        stage_a(c % a.nchunks);
-        publish_a(c);
+    for (int c = 0; c < kHalfCo; ++c) {
+        const int co = kHalfCo * hh + c;
+        b6[c] = (FUSED && a.bias != nullptr && co < a.C_out) ? E::to_f32(a.bias[co]) : 0.f;
     }
+    if constexpr (FUSED) {
 #pragma unroll
-    for (int u = 0; u < kBRing; ++u) load_b(u, bq[u]);
-    __syncthreads();
-    read_a(0, 0, af[0]);
+        for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+            for (int k = 0; k < 3; ++k) carry[wave][nb][k][lane] = float4{0.f, 0.f, 0.f, 0.f};
+    }
 
+    // (row, chunk, tap) of the tap `ahead` taps after tap kd of chunk c of Z row st
+    auto tap_after = [&](int st, int c, int kd, int ahead, int &ost, int &oc, int &okd) {
+        okd = kd + ahead;
+        oc = c;
+        ost = st;
+        while (okd >= 3) {
+            okd -= 3;
+            if (++oc == nch) oc = 0, ++ost;
+        }
+    };
+
+    // ---- prologue: weight chunks 0 and 1 copied (0 complete), B of half-taps 0..2 loading ----
+    copy_a(0, As0);
+    copy_a(1, As1);
+    load_half(0, 0, 0, 0, bq[0]);
+    load_half(0, 0, 0, 1, bq[1]);
+    load_half(0, 0, 1, 0, bq[2]);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDmaPerWave + (kRing - 1) * kLoadsPerHalf));
+    wg_barrier();
+    read_a(As0, 0, 0, af[0]);
+
+    // Chunk g of the band is channel chunk g % nch of Z row g / nch.  Each pass of the loop body
+    // runs one even chunk (buffer As0) and the following odd chunk (As1): twelve half-taps; the
+    // ring slot of half-tap i of the pass is i % 4.
 #pragma unroll 1
-    for (int step = 0; step < nsteps; ++step) {
-#pragma unroll
-        for (int i = 0; i < kMB; ++i)
-#pragma unroll
-            for (int j = 0; j < kNB; ++j)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    for (int st = 0; st < nsteps; ++st) {
 #pragma unroll 1
-        for (int cc = 0; cc < a.nchunks; ++cc) {
-            const int g = step * a.nchunks + cc;
-            const int buf = g % NABUF;
+        for (int c2 = 0; c2 < nch; c2 += 2) {
 #pragma unroll
-            for (int kd = 0; kd < 3; ++kd) {
-                if (kd == 0) stage_a((cc + NABUF - 1) % a.nchunks);
-                // the next k-step's A fragments (for kd == 2 the next chunk's, when it is
-                // already published) are read before this k-step's MFMAs
-                if (kd < 2)
-                    read_a(buf, kd + 1, af[(kd + 1) & 1]);
-                else if (NABUF == 3)
-                    read_a((g + 1) % NABUF, 0, af[1]);
+          for (int i = 0; i < 2 * kHalves; ++i) {
+            const int half = i / kHalves;                 // even / odd chunk of the pass
+            const int kd = (i % kHalves) / 2, hp = i % 2;
+            uint4 *const cbuf = half == 0 ? As0 : As1;   // this chunk's weights
+            uint4 *const nbuf = half == 0 ? As1 : As0;   // the next chunk's
+            {   // half-tap i+3 into the slot half-tap i-1 has finished with
+                const int ahead_hp = (hp + kRing - 1) % 2;
+                const int ahead_taps = (hp + kRing - 1) / 2;
+                int lst, lc, lkd;
+                tap_after(st, c2 + half, kd, ahead_taps, lst, lc, lkd);
+                load_half(lst, lc, lkd, ahead_hp, bq[(i + kRing - 1) % kRing]);
+            }
 #pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2)
+            for (int sl = 0; sl < kSlices; ++sl) {
+                const int u = 2 * kSlices * kd + kSlices * hp + sl;   // 0 .. 23 within the chunk
+                const bool last = u == 2 * kSlices * 3 - 1;
+                const int cur = sl & 1;
+                if (last) {
+                    // Publish chunk g+1: its copy (issued one chunk ago, here) is complete once at
+                    // most kVmAfterCopy younger operations are outstanding.  This wave's reads of
+                    // chunk g are done (the last ones were issued in the previous slice), so
+                    // after the barrier chunk g's buffer takes chunk g+2.
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kVmAfterCopy));
+                    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+                    wg_barrier();
+                    const int wc = c2 + half + 2;    // weight chunk of chunk g+2
+                    copy_a(wc < nch ? wc : wc - nch, cbuf);
+                }
+                // the next slice's A fragments: of this half-tap, the next half-tap (same tap:
+                // the same fragments again for blocks 2-3; next tap), or the next chunk's
+                if (!last) {
+                    const int nsl = (sl + 1) % kSlices;
+                    const int nkd = sl + 1 < kSlices ? kd : (hp == 1 ? kd + 1 : kd);
+                    read_a(cbuf, nkd, nsl, af[cur ^ 1]);
+                } else {
+                    read_a(nbuf, 0, 0, af[cur ^ 1]);
+                }
+                if (i == 0 && sl == 0 && c2 == 0) {
 #pragma unroll
                     for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-                        for (int nb = 0; nb < kNB; ++nb)
-                            acc[mb][nb] = E::mfma32x32x16(af[kd & 1][mb][k2], bq[kd][nb][k2], acc[mb][nb]);
-                load_b(3 * g + kd + kBRing, bq[kd]);
-                if (kd == 2) {   // end of a chunk: publish the chunk NABUF-1 ahead
-                    publish_a((g + NABUF - 1) % NABUF);
-                    __syncthreads();
-                    if (NABUF == 2) read_a((g + 1) % NABUF, 0, af[0]);
-                    else {
+                        for (int b = 0; b < 2; ++b)
+                            acc[mb][2 * hp + b] = E::mfma32x32x16(af[cur][mb], bq[i % kRing][b][sl], zero);
+                } else if (i == 1 && sl == 0 && c2 == 0) {
 #pragma unroll
-                        for (int mb = 0; mb < kMB; ++mb) {
-                            af[0][mb][0] = af[1][mb][0];
-                            af[0][mb][1] = af[1][mb][1];
-                        }
-                    }
+                    for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+                        for (int b = 0; b < 2; ++b)
+                            acc[mb][2 * hp + b] = E::mfma32x32x16(af[cur][mb], bq[i % kRing][b][sl], zero);
+                } else {
+#pragma unroll
+                    for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+                        for (int b = 0; b < 2; ++b)
+                            acc[mb][2 * hp + b] = E::mfma32x32x16(af[cur][mb], bq[i % kRing][b][sl], acc[mb][2 * hp + b]);
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
+          }
         }
 
-        // ---- the step's Z tile is complete: this wave holds rows 0..127 of 64 columns ----
-        const int zr = zrow0 + step * kStepRows + zrw;   // this wave's Z row
+        // ---- row zr of Z is complete in this wave's accumulators ----
+        // The epilogues walk the accumulator blocks in order and read each value once, so only
+        // one or two blocks are unpacked into registers at a time.
+        const int zr = zrow0 + st;
+        const size_t frame = (size_t)n * a.D + od;
         if constexpr (!FUSED) {
-            if (zr < h_end) {
+            if (zr < h_end && od < a.D) {
 #pragma unroll
                 for (int nb = 0; nb < kNB; ++nb) {
-                    const int w = col0 + nb * 32 + (lane & 31);
-                    if (w < a.W) {
-                        u16 *dst = a.out + (((size_t)n * a.D + od) * HW + (size_t)zr * a.W + w) * kPlaneCh;
+                    const int w = w0 + 4 * j + nb;
+                    u16 *dst = a.out + (frame * HW + (size_t)zr * a.W + w) * kPlaneCh;
 #pragma unroll
-                        for (int mb = 0; mb < kMB; ++mb)
+                    for (int mb = 0; mb < kMB; ++mb) touch(acc[mb][nb]);
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                const int m0 = mb * 32 + 8 * j + 4 * (lane >> 5);
-                                if (m0 < kPlaneCh) {
-                                    const f32x16_t v = acc[mb][nb];
-                                    uint2 pk;
-                                    pk.x = (uint32_t)E::from_f32(v[4 * j]) | ((uint32_t)E::from_f32(v[4 * j + 1]) << 16);
-                                    pk.y = (uint32_t)E::from_f32(v[4 * j + 2]) | ((uint32_t)E::from_f32(v[4 * j + 3]) << 16);
-                                    *reinterpret_cast<uint2 *>(dst + m0) = pk;
+                    for (int tap = 0; tap < 9; ++tap) {
+                        u16 r6[kHalfCo];
+#pragma unroll
+                        for (int c = 0; c < kHalfCo; ++c) {
+                            const int t = tap * kHalfCo + c;
+                            r6[c] = E::from_f32(acc[t >> 4][nb][t & 15]);
+                        }
+                        if (w < a.W) {
+                            if constexpr (CO12) {
+                                uint3 v;
+                                v.x = (uint32_t)r6[0] | ((uint32_t)r6[1] << 16);
+                                v.y = (uint32_t)r6[2] | ((uint32_t)r6[3] << 16);
+                                v.z = (uint32_t)r6[4] | ((uint32_t)r6[5] << 16);
+                                *reinterpret_cast<uint3 *>(dst + tap * 12 + kHalfCo * hh) = v;
+                            } else {
+#pragma unroll
+                                for (int c = 0; c < kHalfCo; ++c) {
+                                    const int co = kHalfCo * hh + c;
+                                    if (co < a.C_out) dst[tap * a.C_out + co] = r6[c];
                                 }
                             }
+                        }
                     }
+                    if (CO12 && w < a.W && hh == 0) *reinterpret_cast<uint2 *>(dst + 108) = uint2{0u, 0u};
                 }
             }
         } else {
-            // Z rows -> ring slot ((zr - zrow0) mod 4), rounded once to the storage type
-            uint8_t *zrow = Zr + ((step * kStepRows + zrw) % kZRing) * (kStripPos * kZPosBytes);
+            // Output row zr-1 = cA + taps ky=2 of row zr; the next cA = cB + taps ky=1; the next
+            // cB = taps ky=0.  Position p takes tap (ky, kx) from position p + kx - 1: block
+            // nb + kx - 1 of the same lane, or across a lane (wavefront shift) from block 3 for
+            // kx = 0 at block 0, and from block 0 for kx = 2 at block 3.  The lanes that cross a
+            // lane half or the wave hold halo columns, which are not stored.
+            const int ho = zr - 1;   // the output row this Z row completes
+            const bool emit = ho >= h_begin && ho < h_end && od < a.D;
 #pragma unroll
             for (int nb = 0; nb < kNB; ++nb) {
-                const int pos = half * kWaveCols + nb * 32 + (lane & 31);
+                float sum[3][kHalfCo];   // [ky]: this row's taps ky for this block's positions
 #pragma unroll
-                for (int mb = 0; mb < kMB; ++mb)
+                for (int ky = 0; ky < 3; ++ky)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int m0 = mb * 32 + 8 * j + 4 * (lane >> 5);
-                        if (m0 < kZCh) {
-                            const f32x16_t v = acc[mb][nb];
-                            uint2 pk;
-                            pk.x = (uint32_t)E::from_f32(v[4 * j]) | ((uint32_t)E::from_f32(v[4 * j + 1]) << 16);
-                            pk.y = (uint32_t)E::from_f32(v[4 * j + 2]) | ((uint32_t)E::from_f32(v[4 * j + 3]) << 16);
-                            *reinterpret_cast<uint2 *>(zrow + pos * kZPosBytes + m0 * 2) = pk;
+                    for (int c = 0; c < kHalfCo; ++c) sum[ky][c] = 0.f;
+#pragma unroll
+                for (int kx = 0; kx < 3; ++kx) {
+                    const int src = nb + kx - 1;
+                    const int sb = src < 0 ? kNB - 1 : (src >= kNB ? 0 : src);
+#pragma unroll
+                    for (int mb = 0; mb < kMB; ++mb) {
+                        bool used = false;   // does block (mb, sb) hold a slot with this kx?
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const int t = 16 * mb + i;
+                            if (t < 9 * kHalfCo && (t / kHalfCo) % 3 == kx) used = true;
                         }
-                    }
-            }
-            __syncthreads();
-            // output rows completed by this step: h in [h_begin+2*step-2, h_begin+2*step-1]
-            const int hlo = max(h_begin, h_begin + kStepRows * step - 2);
-            const int hhi = min(h_end, h_begin + kStepRows * step);
-            const int groups = (a.C_out + 3) / 4;
-            const int per_row = a.strip_out * groups;
-            const bool vec = (a.C_out & 3) == 0;
-            for (int item = tid; item < (hhi - hlo) * per_row; item += 256) {
-                const int hr = item / per_row;
-                const int rem = item - hr * per_row;
-                const int c = rem / groups, grp = rem - c * groups;
-                const int h = hlo + hr;
-                const int w = strip * a.strip_out + c;
-                if (w >= a.W) continue;
-                const int c0 = grp * 4;
-                float s4[4];
+                        if (!used) continue;
+                        touch(acc[mb][sb]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    s4[i] = (a.bias != nullptr && c0 + i < a.C_out) ? E::to_f32(a.bias[c0 + i]) : 0.f;
-#pragma unroll
-                for (int ky = 0; ky < 3; ++ky) {
-                    const uint8_t *zrow2 = Zr + ((h - h_begin + ky) % kZRing) * (kStripPos * kZPosBytes);
-#pragma unroll
-                    for (int kx = 0; kx < 3; ++kx) {
-                        const u16 *src = reinterpret_cast<const u16 *>(zrow2 + (c + kx) * kZPosBytes) +
-                                         (ky * 3 + kx) * a.C_out + c0;
-                        if (vec) {
-                            const uint2 v = *reinterpret_cast<const uint2 *>(src);
-                            s4[0] += E::to_f32((u16)(v.x & 0xffffu));
-                            s4[1] += E::to_f32((u16)(v.x >> 16));
-                            s4[2] += E::to_f32((u16)(v.y & 0xffffu));
-                            s4[3] += E::to_f32((u16)(v.y >> 16));
-                        } else {
-                            for (int i = 0; i < 4; ++i)
-                                if (c0 + i < a.C_out) s4[i] += E::to_f32(src[i]);
+                        for (int i = 0; i < 16; ++i) {
+                            const int t = 16 * mb + i;
+                            if (t >= 9 * kHalfCo || (t / kHalfCo) % 3 != kx) continue;
+                            const int ky = t / kHalfCo / 3, c = t % kHalfCo;
+                            float v = acc[mb][sb][i];
+                            if (src < 0)   // left neighbour: lane l-1
+                                v = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                    0, __builtin_bit_cast(int, v), 0x138, 0xF, 0xF, false));
+                            else if (src >= kNB)   // right neighbour: lane l+1
+                                v = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                    0, __builtin_bit_cast(int, v), 0x130, 0xF, 0xF, false));
+                            sum[ky][c] += v;
                         }
                     }
                 }
-                u16 o[4];
+                const float4 k0 = carry[wave][nb][0][lane], k1 = carry[wave][nb][1][lane],
+                             k2 = carry[wave][nb][2][lane];
+                const float cA[kHalfCo] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y};
+                const float cB[kHalfCo] = {k1.z, k1.w, k2.x, k2.y, k2.z, k2.w};
+                float o[kHalfCo], nA[kHalfCo];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[i] = E::from_f32(epilogue<EPI>(s4[i]));
-                u16 *dst = a.out + (((size_t)n * a.D + od) * HW + (size_t)h * a.W + w) * a.C_out + c0;
-                if (vec) {
-                    uint2 pk;
-                    pk.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
-                    pk.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
-                    *reinterpret_cast<uint2 *>(dst) = pk;
-                } else {
-                    for (int i = 0; i < 4; ++i)
-                        if (c0 + i < a.C_out) dst[i] = o[i];
+                for (int c = 0; c < kHalfCo; ++c) {
+                    o[c] = cA[c] + sum[2][c];
+                    nA[c] = cB[c] + sum[1][c];
+                }
+                carry[wave][nb][0][lane] = float4{nA[0], nA[1], nA[2], nA[3]};
+                carry[wave][nb][1][lane] = float4{nA[4], nA[5], sum[0][0], sum[0][1]};
+                carry[wave][nb][2][lane] = float4{sum[0][2], sum[0][3], sum[0][4], sum[0][5]};
+                const int p = 4 * j + nb;
+                const int w = w0 + p;
+                if (emit && p >= 1 && p <= a.strip_out && w < a.W) {
+                    u16 r6[kHalfCo];
+#pragma unroll
+                    for (int c = 0; c < kHalfCo; ++c) r6[c] = E::from_f32(epilogue<EPI>(o[c] + b6[c]));
+                    u16 *dst = a.out + (frame * HW + (size_t)ho * a.W + w) * a.C_out;
+                    if constexpr (CO12) {
+                        uint3 v;
+                        v.x = (uint32_t)r6[0] | ((uint32_t)r6[1] << 16);
+                        v.y = (uint32_t)r6[2] | ((uint32_t)r6[3] << 16);
+                        v.z = (uint32_t)r6[4] | ((uint32_t)r6[5] << 16);
+                        *reinterpret_cast<uint3 *>(dst + kHalfCo * hh) = v;
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < kHalfCo; ++c)
+                            if (kHalfCo * hh + c < a.C_out) dst[kHalfCo * hh + c] = r6[c];
+                    }
                 }
             }
         }
     }
+    // no LDS copy may still be in flight when the workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
 
 }  // namespace
@@ -494,30 +591,36 @@ hipError_t launch_head_gemm(const HeadGemmParams &p, hipStream_t stream) {
     a.bias = static_cast<const u16 *>(p.bias);
     a.out = static_cast<u16 *>(p.out);
     a.N = p.N, a.C_in = p.C_in, a.C_out = p.C_out, a.D = p.D, a.H = p.H, a.W = p.W;
-    a.nchunks = (p.C_in + 31) / 32;
-    a.strip_out = p.fused ? kStripPos - 2 : kStripPos;
+    const int packed_chunks = (p.C_in + 63) / 64;
+    a.nchunks = (packed_chunks + 1) & ~1;   // the kernel runs chunks in pairs
+    a.strip_out = p.fused ? kWavePos - 2 : kWavePos;
     a.strips = (p.W + a.strip_out - 1) / a.strip_out;
-    // One workgroup per CU is resident (LDS and registers).  Pick the band count that minimises
-    // (rounds of 256 workgroups) x (rows a workgroup computes, halo included).
-    const long long cols = (long long)p.N * p.D * a.strips;
+    a.fgroups = (p.D + 3) / 4;
+    // One workgroup per CU is resident (accumulators fill the register file).  Pick the band count
+    // that minimises (rounds of 256 workgroups) x (rows a wave computes, halo included).
+    const long long cols = (long long)p.N * a.fgroups * a.strips;
     const int halo = p.fused ? 2 : 0;
     long long best = -1;
     int best_bands = 1;
-    for (int bands = 1; bands <= p.H && bands <= 64; ++bands) {
+    for (int bands = 1; bands <= p.H && bands <= 256; ++bands) {
         const int rpb = (p.H + bands - 1) / bands;
         const int real_bands = (p.H + rpb - 1) / rpb;
         const long long rounds = (cols * real_bands + 255) / 256;
-        const long long cost = rounds * (((rpb + halo) + kStepRows - 1) / kStepRows);
+        const long long cost = rounds * (rpb + halo);
         if (best < 0 || cost < best) best = cost, best_bands = real_bands;
     }
     a.rows_per_band = (p.H + best_bands - 1) / best_bands;
     a.bands = (p.H + a.rows_per_band - 1) / a.rows_per_band;
     a.sample_bytes = (uint32_t)((size_t)p.D * p.H * p.W * p.C_in * 2);
-    a.wp_bytes = (uint32_t)((size_t)a.nchunks * kAChunkPieces * 16);
+    a.wp_bytes = (uint32_t)((size_t)packed_chunks * kHeadChunkPieces * 16);
     const long long wgs = cols * a.bands;
     a.total_wg = (uint32_t)wgs;
     const dim3 grid((unsigned)wgs), block(256);
-#define CX_HG(BFV, FV, EPIV) head_gemm_kernel<BFV, FV, EPIV><<<grid, block, 0, stream>>>(a)
+#define CX_HG(BFV, FV, EPIV)                                                          \
+    do {                                                                              \
+        if (p.C_out == 12) head_gemm_kernel<BFV, FV, EPIV, true><<<grid, block, 0, stream>>>(a);  \
+        else head_gemm_kernel<BFV, FV, EPIV, false><<<grid, block, 0, stream>>>(a);    \
+    } while (0)
     if (!p.fused) {
         if (p.bf16) CX_HG(true, false, EPI_NONE);
         else CX_HG(false, false, EPI_NONE);

@@ -263,30 +263,38 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *part, c
     }
 }
 
-// wp[((cc*NT + tap)*Mpad + m)*32 + k] <- w[co, ci = 32*cc + k, kd, ky, kx]
-//   direct: NT = 27, tap = kd*9+ky*3+kx, co = m;
-//   temporal (split head): NT = 3, tap = kd, m = (ky*3+kx)*C_out + co.
+// Direct (27 taps): wp[((cc*27 + tap)*Mpad + m)*32 + k] <- w[co = m, ci = 32*cc + k, tap].
+// Temporal (head kernels): 64-channel chunk c holds 3072 16-byte pieces in LDS order -- slot
+// s = r*8 + q' of row r = kd*128 + m holds channels 64*c + 8*q .. +7, q = q' ^ head_lds_swizzle(r),
+// of the weight for temporal tap kd and the (spatial tap, output channel) head_row_role(m) names.
 // Rows past the real ones and channels past C_in are zero.
 __global__ __launch_bounds__(256) void pack3d_kernel(const u16 *w, u16 *wp, int C_in, int C_out,
                                                      int NT, int Mpad, bool temporal,
                                                      long long total) {
     const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
     if (idx >= total) return;
-    const int k = (int)(idx & 31);
-    long long r = idx >> 5;
-    const int m = (int)(r % Mpad);
-    r /= Mpad;
-    const int tap = (int)(r % NT);
-    const int cc = (int)(r / NT);
-    const int ci = cc * 32 + k;
     u16 v = 0;
-    if (ci < C_in) {
-        if (!temporal) {
-            if (m < C_out) v = w[((size_t)m * C_in + ci) * 27 + tap];
-        } else if (m < 9 * C_out) {
-            const int s = m / C_out, co = m % C_out;
-            v = w[((size_t)co * C_in + ci) * 27 + tap * 9 + s];
-        }
+    if (!temporal) {
+        const int k = (int)(idx & 31);
+        long long r = idx >> 5;
+        const int m = (int)(r % Mpad);
+        r /= Mpad;
+        const int tap = (int)(r % NT);
+        const int cc = (int)(r / NT);
+        const int ci = cc * 32 + k;
+        if (ci < C_in && m < C_out) v = w[((size_t)m * C_in + ci) * 27 + tap];
+    } else {
+        const int cc = (int)(idx / (kHeadChunkPieces * 8));
+        const int rem = (int)(idx - (long long)cc * (kHeadChunkPieces * 8));
+        const int slot = rem >> 3, e = rem & 7;
+        const int r = slot >> 3;
+        const int q = (slot & 7) ^ head_lds_swizzle(r);
+        const int kd = r >> 7, m = r & 127;
+        const int ci = cc * 64 + 8 * q + e;
+        int tap, co;
+        head_row_role(m, tap, co);
+        if (ci < C_in && tap >= 0 && co < C_out)
+            v = w[((size_t)co * C_in + ci) * 27 + kd * 9 + tap];
     }
     wp[idx] = v;
 }
@@ -342,7 +350,8 @@ IgemmPlan plan_igemm(int family, int N, int C_in, int C_out, int D, int H, int W
     }
     pl.Mpad = (pl.Mrows + pl.BM - 1) / pl.BM * pl.BM;
     pl.mtiles = pl.Mpad / pl.BM;
-    pl.nchunks = (C_in + 31) / 32;
+    // 32-channel chunks; the head kernels pack whole 64-channel chunks (an even count)
+    pl.nchunks = family == IG_TEMPORAL ? (C_in + 63) / 64 * 2 : (C_in + 31) / 32;
     if (family == IG_TEMPORAL) {
         // 256 consecutive positions of one frame per workgroup (no spatial structure needed)
         pl.tiles_h = 1;

@@ -23,7 +23,7 @@ hipError_t launch_simt2d(const Simt2dParams &p, hipStream_t stream);
 enum IgemmFamily {
     IG_WIDE = 0,   // 128 output rows x 128 positions per workgroup: C_out > 16
     IG_NARROW = 1, // 16 output rows x 256 positions: C_out <= 16 (the direct head)
-    IG_TEMPORAL = 2 // packing only: 3 temporal taps x 112 rows (9 taps x 12 channels), head kernels
+    IG_TEMPORAL = 2 // packing only: 3 temporal taps x 128 rows (9 taps x 12 channels), head kernels
 };
 
 struct IgemmPlan {
@@ -73,6 +73,24 @@ struct StencilParams {
 hipError_t launch_head_stencil(const StencilParams &p, hipStream_t stream);
 
 constexpr int kHeadPlaneChannels = 112;  // 9 taps x 12 channels = 108, padded to 7 x 16
+
+// Packed weights of the head's temporal GEMM, per 64-channel chunk: 3 temporal taps x 128 GEMM
+// rows x 64 channels = 3072 pieces of 16 bytes (8 channels), stored in the order the kernel's LDS
+// holds them: piece slot s = r*8 + q' of row r = kd*128 + m holds channels 8*q .. 8*q+7 of the
+// chunk with q = q' ^ head_lds_swizzle(r).
+constexpr int kHeadChunkPieces = 3 * 128 * 8;
+__host__ __device__ inline int head_lds_swizzle(int r) { return (r >> 1) & 7; }
+// Role of GEMM row m (0..127): the matrix-core accumulator layout puts row m into register
+// i = 4*((m%32)/8) + m%4 of 32-row block m/32 in lane half h = (m%8)/4; slot t = 16*(m/32) + i of
+// half h carries spatial tap t/6 (ky*3 + kx) of output channel 6*h + t%6.  Rows with t >= 54 are
+// padding (tap = -1).
+__host__ __device__ inline void head_row_role(int m, int &tap, int &co) {
+    const int mb = m >> 5, rr = m & 31;
+    const int h = (rr >> 2) & 1;
+    const int t = 16 * mb + 4 * (rr >> 3) + (rr & 3);
+    tap = t < 54 ? t / 6 : -1;
+    co = 6 * h + t % 6;
+}
 
 // ---- the head's temporal GEMM (packed like IG_TEMPORAL): plane output or fused stencil -----
 struct HeadGemmParams {
