@@ -111,9 +111,10 @@ int select_3d(int N, int C_in, int C_out, int D, int H, int W, int stride, int l
     return algo;
 }
 
-int family_for(int algo, int C_out) {
+int family_for(int algo, int C_in, int C_out, int H, int W) {
     if (algo == CONV_ALGO_SPLIT_HEAD || algo == CONV_ALGO_FUSED_HEAD) return cx::IG_TEMPORAL;
-    return C_out <= 16 ? cx::IG_NARROW : cx::IG_WIDE;
+    if (C_out <= 16) return cx::IG_NARROW;
+    return (long long)H * W * C_in * 2 < (1ll << 31) ? cx::IG_W32 : cx::IG_WIDE;
 }
 
 size_t elem_bytes() { return 2; }
@@ -220,7 +221,7 @@ size_t conv3x3x3_workspace_bytes(int N, int C_in, int C_out, int D, int H, int W
     ok();
     if (a == CONV_ALGO_SPLIT_HEAD)
         return (size_t)N * D * H * W * cx::kHeadPlaneChannels * elem_bytes();
-    const cx::IgemmPlan pl = cx::plan_igemm(family_for(a, C_out), N, C_in, C_out, D, H, W);
+    const cx::IgemmPlan pl = cx::plan_igemm(family_for(a, C_in, C_out, H, W), N, C_in, C_out, D, H, W);
     return cx::splitk_workspace_bytes(pl, N, D, H, W, C_out);
 }
 
@@ -229,7 +230,7 @@ size_t conv3x3x3_packed_weight_bytes(int N, int C_in, int C_out, int D, int H, i
     const int a = select_3d(N, C_in, C_out, D, H, W, stride, layout, dtype, algo);
     if (a < 0) return 0;
     ok();
-    return cx::packed_bytes(cx::plan_igemm(family_for(a, C_out), N, C_in, C_out, D, H, W));
+    return cx::packed_bytes(cx::plan_igemm(family_for(a, C_in, C_out, H, W), N, C_in, C_out, D, H, W));
 }
 
 int conv3x3x3_pack_weights(const void *w_oidhw, void *w_packed, int N, int C_in, int C_out,
@@ -241,7 +242,7 @@ int conv3x3x3_pack_weights(const void *w_oidhw, void *w_packed, int N, int C_in,
     if (!w_oidhw || !w_packed) return fail(CONV_E_INVAL, "w_oidhw and w_packed must be non-NULL");
     if (!aligned(w_oidhw, 2) || !aligned(w_packed, 16))
         return fail(CONV_E_INVAL, "w_oidhw must be 2-byte and w_packed 16-byte aligned");
-    const cx::IgemmPlan pl = cx::plan_igemm(family_for(a, C_out), N, C_in, C_out, D, H, W);
+    const cx::IgemmPlan pl = cx::plan_igemm(family_for(a, C_in, C_out, H, W), N, C_in, C_out, D, H, W);
     if (overlaps(w_oidhw, (size_t)C_out * C_in * 27 * elem_bytes(), w_packed, cx::packed_bytes(pl)))
         return fail(CONV_E_INVAL, "w_oidhw and w_packed overlap");
     int st = device_present();
@@ -291,7 +292,7 @@ int conv3x3x3_fwd(const void *x, const void *w_packed, const void *bias, void *y
         if (e != hipSuccess) return fail(CONV_E_LAUNCH, "fused head launch failed: %s", hipGetErrorString(e));
         return ok();
     }
-    const cx::IgemmPlan pl = cx::plan_igemm(family_for(a, C_out), N, C_in, C_out, D, H, W);
+    const cx::IgemmPlan pl = cx::plan_igemm(family_for(a, C_in, C_out, H, W), N, C_in, C_out, D, H, W);
     cx::IgemmParams ip{};
     ip.x = x, ip.wp = w_packed, ip.bias = bias, ip.y = y;
     ip.partial = static_cast<float *>(pl.splits > 1 ? workspace : nullptr);

@@ -45,12 +45,13 @@ struct IgemmKArgs {
     int nchunks, chunks_per_split, splits;
     int tiles_h, tiles_w, mtiles;
     uint32_t total_wg;
+    uint32_t wp_bytes;   // packed weights (buffer-resource range of the 32x32 kernel)
 };
 
-// Stores the four rows (m0..m0+3) of one accumulator column: fp32 partials for split-K, or the
-// bias + epilogue + one rounding to the storage type.
+// Stores four rows m0..m0+3 of one accumulator column (bias already added): fp32 partials for
+// split-K, else epilogue + one rounding to the storage type.
 template <bool BF, int EPI, bool SPLITK>
-__device__ __forceinline__ void store_col(const IgemmKArgs &a, f32x4_t v, size_t pos, int split,
+__device__ __forceinline__ void store_rows(const IgemmKArgs &a, f32x4_t v, size_t pos, int split,
                                           size_t P, int m0) {
     using E = Elem<BF>;
     if (m0 >= a.Mrows) return;
@@ -66,11 +67,7 @@ __device__ __forceinline__ void store_col(const IgemmKArgs &a, f32x4_t v, size_t
     } else {
         u16 o[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float s = v[i];
-            if (a.bias != nullptr && m0 + i < a.Mrows) s += E::to_f32(a.bias[m0 + i]);
-            o[i] = E::from_f32(epilogue<EPI>(s));
-        }
+        for (int i = 0; i < 4; ++i) o[i] = E::from_f32(epilogue<EPI>(v[i]));
         u16 *dst = a.y + pos * a.Cy + m0;
         if (m0 + 3 < a.Mrows && (a.Cy & 3) == 0) {
             uint2 pk;
@@ -106,6 +103,7 @@ __global__ __launch_bounds__(256, 2) void igemm3d_kernel(IgemmKArgs a) {
     constexpr int PPT = (PIECES + 255) / 256;
     constexpr int PD = 3;                  // weight-fragment prefetch distance (taps)
     __shared__ __attribute__((aligned(16))) u16 win[2][FPOS * kPosStride];
+    __shared__ float bias_s[BM];   // this workgroup's output rows (0 past C_out / no bias)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -176,6 +174,10 @@ __global__ __launch_bounds__(256, 2) void igemm3d_kernel(IgemmKArgs a) {
         for (int mb = 0; mb < MB; ++mb) dst[mb] = *reinterpret_cast<const vec8 *>(wb + mb * 16 * 32);
     };
 
+    for (int i = tid; i < BM; i += 256) {
+        const int m = mt * BM + i;
+        bias_s[i] = (!SPLITK && a.bias != nullptr && m < a.Mrows) ? E::to_f32(a.bias[m]) : 0.f;
+    }
     vec8 aq[PD][MB];
     if (nst > 0) {
         fetch(0);
@@ -222,9 +224,245 @@ __global__ __launch_bounds__(256, 2) void igemm3d_kernel(IgemmKArgs a) {
         if (oh >= a.H || ow >= a.W) continue;
         const size_t pos = (((size_t)n * a.D + od) * a.H + oh) * a.W + ow;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-            store_col<BF, EPI, SPLITK>(a, acc[mb][nb], pos, split, P,
-                                       mt * BM + wm * MB * 16 + mb * 16 + 4 * (lane >> 4));
+        for (int mb = 0; mb < MB; ++mb) {
+            const int r0 = wm * MB * 16 + mb * 16 + 4 * (lane >> 4);
+            const float4 bv = *reinterpret_cast<const float4 *>(&bias_s[r0]);
+            const f32x4_t v = acc[mb][nb];
+            store_rows<BF, EPI, SPLITK>(a, f32x4_t{v[0] + bv.x, v[1] + bv.y, v[2] + bv.z, v[3] + bv.w},
+                                       pos, split, P, mt * BM + r0);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// The 27-tap convolution for wide outputs (C_out > 16) on v_mfma_f32_32x32x16: one wave per SIMD
+// keeps that pipe full, and a 128 x 128 tile per wave (4 x 4 blocks, all 256 accumulators) reads
+// a quarter of an A and a quarter of a B fragment per MFMA.  Operand layout: lane l supplies row
+// (A) / column (B) l%32 with the 8 k values of half l/32 of a 16-wide k slice, and receives
+// accumulator element i at row 8*(i/4) + 4*(l/32) + i%4, column l%32.
+//
+// Workgroup: 256 output rows (two waves along M) x an 8 x 32 block of positions of one frame (two
+// waves along N, four rows each).  K runs in stages (32-channel chunk, live temporal tap); a
+// stage's input window -- 10 x 34 positions x 32 channels, zero outside the tensor -- is copied
+// global -> LDS by the buffer unit (LDS DMA, 16 positions x 64 bytes per copy, no registers),
+// double-buffered a whole stage ahead, and its nine spatial taps read their B fragments from it by
+// address offset.  Window rows are 36 positions apart (34 used) and each 64-byte position holds
+// its four 16-byte pieces XOR-permuted by (column/4) % 4: any 16 consecutive columns of a row then
+// fall on distinct LDS bank groups, and a fragment address is a per-lane part (column, piece)
+// plus a row part that fits the instruction's offset field.  Weight
+// fragments (1 KiB contiguous each in the packing) stream from L2 into a register ring three taps
+// deep.  The compiler cannot see that a DMA copy into one window buffer never overlaps reads from
+// the other, so the two buffers are separate objects and the stage loop is unrolled by two.
+// ---------------------------------------------------------------------------------------------
+constexpr int kW32TH = 8, kW32TW = 32;
+constexpr int kW32WW = kW32TW + 2;                      // 34 window columns used
+constexpr int kW32RowPos = 36;                          // window row stride in positions
+constexpr int kW32Pos = (kW32TH + 2) * kW32RowPos;     // 360 window positions (10 rows)
+constexpr int kW32Copies = (kW32Pos * 4 + 63) / 64;    // 23 copies of 16 positions
+constexpr int kW32CopiesPerWave = (kW32Copies + 3) / 4; // at most 6 per wave
+constexpr int kW32Slots = kW32Copies * 64;             // 16-byte pieces per window buffer
+constexpr int kW32Slices = 18;                          // k16 slices per stage: 9 taps x 2 halves
+constexpr int kW32PD = 6;                               // weight prefetch distance in slices
+
+// slot of (window row r, column c, piece): the row part is a multiple of 16 slots
+__device__ __forceinline__ int w32_slot(int r, int c, int piece) {
+    return (r * kW32RowPos + c) * 4 + (piece ^ ((c >> 2) & 3));
+}
+__device__ __forceinline__ void w32_barrier() { asm volatile("s_barrier" ::: "memory"); }
+__device__ __forceinline__ void w32_touch(f32x16_t &v) { asm volatile("" : "+a"(v)::"memory"); }
+__device__ constexpr int w32_waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kW32WaitLgkm0 = 15 | (3 << 14) | (7 << 4);
+
+template <bool BF, int EPI, bool SPLITK>
+__global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
+    using E = Elem<BF>;
+    typedef typename E::vec8 vec8;
+    typedef __attribute__((address_space(3))) void lds_void;
+    __shared__ __attribute__((aligned(16))) uint4 Win0[kW32Slots];
+    __shared__ __attribute__((aligned(16))) uint4 Win1[kW32Slots];
+    __shared__ float bias_s[256];   // this workgroup's 256 output rows (0 past C_out / no bias)
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int j = lane & 31, hh = lane >> 5;
+    const int wm = wave & 1, wn = wave >> 1;
+
+    uint32_t lin = xcd_remap(blockIdx.x, a.total_wg);
+    const int mt = lin % a.mtiles;
+    lin /= a.mtiles;
+    const int tw = lin % a.tiles_w;
+    lin /= a.tiles_w;
+    const int th = lin % a.tiles_h;
+    lin /= a.tiles_h;
+    const int od = lin % a.D;
+    lin /= a.D;
+    const int n = lin % a.N;
+    const int split = lin / a.N;
+
+    const int oh0 = th * kW32TH, ow0 = tw * kW32TW;
+    const int c_begin = split * a.chunks_per_split;
+    const int c_end = min(a.nchunks, c_begin + a.chunks_per_split);
+    const int kd_lo = od == 0 ? 1 : 0;            // live temporal taps: frame od-1+kd in [0, D)
+    const int kd_hi = od == a.D - 1 ? 1 : 2;
+    const int nkd = kd_hi - kd_lo + 1;
+    const int nst = max(0, (c_end - c_begin) * nkd);
+    const int mbase = mt * 256 + wm * 128;        // this wave's first GEMM row
+    const bool mlive = mbase < a.Mrows;           // all-padding waves skip their MFMAs
+
+    const size_t frame_elems = (size_t)a.H * a.W * a.C_in;
+    const uint32_t frame_bytes = (uint32_t)(frame_elems * 2);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)a.wp, (short)0, (int)(a.wp_bytes), 0x00020000);
+
+    auto stage_coords = [&](int s, int &cc, int &kd) {
+        cc = c_begin + s / nkd;
+        kd = kd_lo + s % nkd;
+    };
+    // Window copies: this wave issues copies k = wave + 4*t; lane i of copy k fills slot 64k + i
+    // = position 16k + i/4 (row, column = position / 36, % 36), piece (i%4) ^ ((column/4) % 4).
+    // The source offsets are recomputed per stage (a few ALU operations) rather than kept live.
+    auto copy_window = [&](int s, uint4 *dst) {
+        int cc, kd;
+        stage_coords(s, cc, kd);
+        const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(a.x + ((size_t)n * a.D + (od - 1 + kd)) * frame_elems), (short)0,
+            (int)frame_bytes, 0x00020000);
+#pragma unroll
+        for (int t = 0; t < kW32CopiesPerWave; ++t) {
+            const int k = wave + 4 * t;
+            if (kW32Copies % 4 != 0 && k >= kW32Copies) break;   // wave-uniform
+            const int pos = 16 * k + (lane >> 2);
+            const int wh = pos / kW32RowPos, ww = pos - wh * kW32RowPos;
+            const int piece = (lane & 3) ^ ((ww >> 2) & 3);
+            const int h = oh0 - 1 + wh, w = ow0 - 1 + ww;
+            const bool ok = ww < kW32WW && (unsigned)h < (unsigned)a.H && (unsigned)w < (unsigned)a.W &&
+                            cc * 32 + 8 * piece < a.C_in;
+            const uint32_t off = ok ? (uint32_t)(((h * a.W + w) * a.C_in + cc * 32 + 8 * piece) * 2) : 0xFFFFFFFFu;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)&dst[k * 64], 16, off, 0, 0, 0);
+        }
+    };
+    // weight fragments of slice q (tap q/2, k half q%2) of stage s: 4 blocks of 32 rows; the
+    // per-lane part of the offset is fixed, the rest is wave-uniform (scalar offset)
+    const uint32_t alane = (uint32_t)((mbase + j) * 32 + 16 * hh);
+    auto load_a = [&](int s, int q, vec8 (&dst)[4]) {
+        int cc, kd;
+        stage_coords(s, cc, kd);
+        const int tap = kd * 9 + q / 2, k2 = q % 2;
+        const uint32_t sbase = (uint32_t)(((size_t)(cc * 27 + tap) * 2 + k2) * a.Mpad * 32);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+            dst[mb] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(
+                wr, alane + mb * 1024u, __builtin_amdgcn_readfirstlane(sbase), 0));
+    };
+    // B fragment of slice q, block nb (tile row 4*wn + nb) from a window buffer: a per-lane slot
+    // for (kx, k half) -- six values -- plus a compile-time row offset
+    int lslot[3][2];
+#pragma unroll
+    for (int kx = 0; kx < 3; ++kx)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) lslot[kx][k2] = w32_slot(4 * wn, j + kx, 2 * k2 + hh);
+    auto read_b = [&](const uint4 *win, int q, int nb) {
+        const int tap = q / 2, ky = tap / 3, kx = tap % 3;
+        return __builtin_bit_cast(vec8, win[lslot[kx][q % 2] + (nb + ky) * (kW32RowPos * 4)]);
+    };
+
+    // (every launched workgroup has at least one stage: splits are never empty and every
+    // output frame has a live temporal tap; the first slice starts the accumulators at zero)
+    f32x16_t acc[4][4];
+    const f32x16_t zero = {};
+    vec8 aq[kW32PD][4];
+    vec8 bq[2][4];
+
+    {
+        const int m = mt * 256 + threadIdx.x;
+        bias_s[threadIdx.x] = (!SPLITK && a.bias != nullptr && m < a.Mrows) ? E::to_f32(a.bias[m]) : 0.f;
+    }
+    copy_window(0, Win0);
+    if (nst > 1) copy_window(1, Win1);
+#pragma unroll
+    for (int q = 0; q < kW32PD; ++q) load_a(0, q, aq[q]);
+    // windows 0 and 1 complete: younger than them are only the weight loads
+    __builtin_amdgcn_s_waitcnt(w32_waitcnt_vm(kW32PD * 4));
+    w32_barrier();
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) bq[0][nb] = read_b(Win0, 0, nb);
+
+    // Stage s computes from window buffer s % 2 and, at its start, has window s+1 in flight.
+    // After its last slice: wait for window s+1, barrier (every wave done with window s), copy
+    // window s+2 into window s's buffer.
+#pragma unroll 1
+    for (int s0 = 0; s0 < nst; s0 += 2) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int s = s0 + half;
+            if (half == 1 && s >= nst) break;              // odd stage count: uniform
+            uint4 *const cur = half == 0 ? Win0 : Win1;
+            uint4 *const nxt = half == 0 ? Win1 : Win0;
+            const bool more = s + 1 < nst;
+#pragma unroll
+            for (int q = 0; q < kW32Slices; ++q) {
+                const int cb = q & 1;
+                if (q + 1 < kW32Slices) {
+#pragma unroll
+                    for (int nb = 0; nb < 4; ++nb) bq[cb ^ 1][nb] = read_b(cur, q + 1, nb);
+                }
+                if (mlive) {
+                    if (half == 0 && q == 0 && s0 == 0) {
+#pragma unroll
+                        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                            for (int nb = 0; nb < 4; ++nb)
+                                acc[mb][nb] = E::mfma32x32x16(aq[q % kW32PD][mb], bq[cb][nb], zero);
+                    } else {
+#pragma unroll
+                        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                            for (int nb = 0; nb < 4; ++nb)
+                                acc[mb][nb] = E::mfma32x32x16(aq[q % kW32PD][mb], bq[cb][nb], acc[mb][nb]);
+                    }
+                }
+                // refill the ring slot with the slice kW32PD ahead (in the next stage when past
+                // this one; a stage past the last re-reads valid weights, never used)
+                if (q + kW32PD < kW32Slices) load_a(s, q + kW32PD, aq[q % kW32PD]);
+                else load_a(more ? s + 1 : s, q + kW32PD - kW32Slices, aq[q % kW32PD]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (more) {
+                // window s+1 complete (its copies were issued at the start of this stage, with
+                // this stage's weight loads -- 4 per slice -- after them); every wave is done
+                // with window s before it takes window s+2
+                __builtin_amdgcn_s_waitcnt(w32_waitcnt_vm(63));
+                __builtin_amdgcn_s_waitcnt(kW32WaitLgkm0);
+                w32_barrier();
+                if (s + 2 < nst) copy_window(s + 2, cur);
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) bq[0][nb] = read_b(nxt, 0, nb);
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(w32_waitcnt_vm(0));
+
+    const size_t P = (size_t)a.N * a.D * a.H * a.W;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+        const int oh = oh0 + 4 * wn + nb, ow = ow0 + j;
+        const bool inside = oh < a.H && ow < a.W;
+        const size_t pos = (((size_t)n * a.D + od) * a.H + oh) * a.W + ow;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            w32_touch(acc[mb][nb]);
+            if (inside && mlive) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x16_t v = acc[mb][nb];
+                    const int m0 = mbase + mb * 32 + 8 * g + 4 * hh;
+                    const float4 bv = *reinterpret_cast<const float4 *>(&bias_s[m0 - mt * 256]);
+                    store_rows<BF, EPI, SPLITK>(a, f32x4_t{v[4 * g] + bv.x, v[4 * g + 1] + bv.y,
+                                                          v[4 * g + 2] + bv.z, v[4 * g + 3] + bv.w},
+                                               pos, split, P, m0);
+                }
+            }
+        }
     }
 }
 
@@ -264,17 +502,30 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *part, c
 }
 
 // Direct (27 taps): wp[((cc*27 + tap)*Mpad + m)*32 + k] <- w[co = m, ci = 32*cc + k, tap].
+// Direct for the 32x32 kernel: wp[(((cc*27 + tap)*2 + k2)*Mpad + m)*16 + k] <- w[m, 32*cc + 16*k2
+// + k, tap]: one 32-row fragment of one k16 slice is 1 KiB contiguous.
 // Temporal (head kernels): 64-channel chunk c holds 3072 16-byte pieces in LDS order -- slot
 // s = r*8 + q' of row r = kd*128 + m holds channels 64*c + 8*q .. +7, q = q' ^ head_lds_swizzle(r),
 // of the weight for temporal tap kd and the (spatial tap, output channel) head_row_role(m) names.
 // Rows past the real ones and channels past C_in are zero.
 __global__ __launch_bounds__(256) void pack3d_kernel(const u16 *w, u16 *wp, int C_in, int C_out,
-                                                     int NT, int Mpad, bool temporal,
+                                                     int NT, int Mpad, int family,
                                                      long long total) {
     const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
     if (idx >= total) return;
     u16 v = 0;
-    if (!temporal) {
+    if (family == IG_W32) {
+        const int k = (int)(idx & 15);
+        long long r = idx >> 4;
+        const int m = (int)(r % Mpad);
+        r /= Mpad;
+        const int k2 = (int)(r & 1);
+        r >>= 1;
+        const int tap = (int)(r % 27);
+        const int cc = (int)(r / 27);
+        const int ci = cc * 32 + k2 * 16 + k;
+        if (ci < C_in && m < C_out) v = w[((size_t)m * C_in + ci) * 27 + tap];
+    } else if (family != IG_TEMPORAL) {
         const int k = (int)(idx & 31);
         long long r = idx >> 5;
         const int m = (int)(r % Mpad);
@@ -321,6 +572,14 @@ template <bool BF>
 hipError_t launch_igemm_dtype(const IgemmPlan &pl, const IgemmKArgs &ka, int epi, bool splitk,
                               hipStream_t s) {
     switch (pl.family) {
+        case IG_W32: {
+            const dim3 grid((unsigned)pl.workgroups), block(256);
+            if (splitk) igemm32_kernel<BF, EPI_NONE, true><<<grid, block, 0, s>>>(ka);
+            else if (epi == EPI_RELU) igemm32_kernel<BF, EPI_RELU, false><<<grid, block, 0, s>>>(ka);
+            else if (epi == EPI_CLAMP1) igemm32_kernel<BF, EPI_CLAMP1, false><<<grid, block, 0, s>>>(ka);
+            else igemm32_kernel<BF, EPI_NONE, false><<<grid, block, 0, s>>>(ka);
+            return hipGetLastError();
+        }
         case IG_WIDE:
             return launch_family<BF, 4, 4, 2, 2, 8, 16>(pl, ka, epi, splitk, s);
         case IG_NARROW:
@@ -343,6 +602,10 @@ IgemmPlan plan_igemm(int family, int N, int C_in, int C_out, int D, int H, int W
             pl.BM = 16, pl.TH = 8, pl.TW = 32, pl.ntaps = 27;
             pl.Mrows = C_out;
             break;
+        case IG_W32:
+            pl.BM = 256, pl.TH = 8, pl.TW = 32, pl.ntaps = 27;
+            pl.Mrows = C_out;
+            break;
         default:   // the head kernels: 3 temporal taps x 128 rows (9 * C_out used)
             pl.BM = 128, pl.TH = 1, pl.TW = 256, pl.ntaps = 3;
             pl.Mrows = 128;
@@ -363,8 +626,10 @@ IgemmPlan plan_igemm(int family, int N, int C_in, int C_out, int D, int H, int W
     const long long base = (long long)N * D * pl.tiles_h * pl.tiles_w * pl.mtiles;
     // Split K when the output alone cannot fill the 256 compute units a few times over.
     int splits = 1;
-    if (family != IG_TEMPORAL && base > 0 && base < 1024) {
-        splits = (int)((1024 + base - 1) / base);
+    // (The 32x32 kernel runs one workgroup per CU, the 16x16 ones two.)
+    const long long fill = family == IG_W32 ? 512 : 1024;
+    if (family != IG_TEMPORAL && base > 0 && base < fill) {
+        splits = (int)((fill + base - 1) / base);
         if (splits > pl.nchunks) splits = pl.nchunks;
     }
     pl.chunks_per_split = (pl.nchunks + splits - 1) / splits;
@@ -394,6 +659,7 @@ hipError_t launch_igemm3d(const IgemmPlan &pl, const IgemmParams &p, hipStream_t
     ka.nchunks = pl.nchunks, ka.chunks_per_split = pl.chunks_per_split, ka.splits = pl.splits;
     ka.tiles_h = pl.tiles_h, ka.tiles_w = pl.tiles_w, ka.mtiles = pl.mtiles;
     ka.total_wg = (uint32_t)pl.workgroups;
+    ka.wp_bytes = (uint32_t)packed_bytes(pl);
     const bool splitk = pl.splits > 1;
     hipError_t e = p.bf16 ? launch_igemm_dtype<true>(pl, ka, p.epilogue, splitk, stream)
                           : launch_igemm_dtype<false>(pl, ka, p.epilogue, splitk, stream);
@@ -424,7 +690,7 @@ hipError_t launch_pack3d(const IgemmPlan &pl, const void *w, void *wp, int C_in,
     if (total == 0) return hipSuccess;
     pack3d_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream>>>(
         static_cast<const u16 *>(w), static_cast<u16 *>(wp), C_in, C_out, pl.ntaps, pl.Mpad,
-        pl.family == IG_TEMPORAL, total);
+        pl.family, total);
     return hipGetLastError();
 }
 

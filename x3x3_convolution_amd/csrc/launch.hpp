@@ -23,7 +23,9 @@ hipError_t launch_simt2d(const Simt2dParams &p, hipStream_t stream);
 enum IgemmFamily {
     IG_WIDE = 0,   // 128 output rows x 128 positions per workgroup: C_out > 16
     IG_NARROW = 1, // 16 output rows x 256 positions: C_out <= 16 (the direct head)
-    IG_TEMPORAL = 2 // packing only: 3 temporal taps x 128 rows (9 taps x 12 channels), head kernels
+    IG_TEMPORAL = 2, // packing only: 3 temporal taps x 128 rows (9 taps x 12 channels), head kernels
+    IG_W32 = 3      // 256 output rows x 8x32 positions on 32x32x16 MFMA: C_out > 16, one frame of
+                    // x below 2 GiB (addressed through a 32-bit buffer range)
 };
 
 struct IgemmPlan {
