@@ -254,37 +254,48 @@ __global__ __launch_bounds__(256, 2) void igemm3d_kernel(IgemmKArgs a) {
 // deep.  The compiler cannot see that a DMA copy into one window buffer never overlaps reads from
 // the other, so the two buffers are separate objects and the stage loop is unrolled by two.
 // ---------------------------------------------------------------------------------------------
-constexpr int kW32TH = 8, kW32TW = 32;
-constexpr int kW32WW = kW32TW + 2;                      // 34 window columns used
-constexpr int kW32RowPos = 36;                          // window row stride in positions
-constexpr int kW32Pos = (kW32TH + 2) * kW32RowPos;     // 360 window positions (10 rows)
-constexpr int kW32Copies = (kW32Pos * 4 + 63) / 64;    // 23 copies of 16 positions
-constexpr int kW32CopiesPerWave = (kW32Copies + 3) / 4; // at most 6 per wave
-constexpr int kW32Slots = kW32Copies * 64;             // 16-byte pieces per window buffer
+// Tile geometry by LW, the columns one 32-lane block spans: LW = 32 gives 8 x 32 positions per
+// workgroup (one row per block), LW = 16 gives 16 x 16 (two rows per block) for narrow frames.
+template <int LW>
+struct W32Geom {
+    static constexpr int R = 32 / LW;                    // rows per 32-position block
+    static constexpr int WR = 4 * R;                     // rows per wave (4 blocks)
+    static constexpr int TH = 2 * WR, TW = LW;           // workgroup tile (two waves along N)
+    static constexpr int WW = TW + 2;                    // window columns used
+    static constexpr int RowPos = (WW + 3) / 4 * 4;      // window row stride (positions)
+    static constexpr int Pos = (TH + 2) * RowPos;        // window positions
+    static constexpr int Copies = (Pos * 4 + 63) / 64;   // DMA copies of 16 positions
+    static constexpr int CopiesPerWave = (Copies + 3) / 4;
+    static constexpr int Slots = Copies * 64;            // 16-byte pieces per window buffer
+};
 constexpr int kW32Slices = 18;                          // k16 slices per stage: 9 taps x 2 halves
 constexpr int kW32PD = 6;                               // weight prefetch distance in slices
 
-// slot of (window row r, column c, piece): the row part is a multiple of 16 slots
+// slot of (window row r, column c, piece); with RowPos a multiple of 4 the row part is a
+// multiple of 16 slots
+template <int RowPos>
 __device__ __forceinline__ int w32_slot(int r, int c, int piece) {
-    return (r * kW32RowPos + c) * 4 + (piece ^ ((c >> 2) & 3));
+    return (r * RowPos + c) * 4 + (piece ^ ((c >> 2) & 3));
 }
 __device__ __forceinline__ void w32_barrier() { asm volatile("s_barrier" ::: "memory"); }
 __device__ __forceinline__ void w32_touch(f32x16_t &v) { asm volatile("" : "+a"(v)::"memory"); }
 __device__ constexpr int w32_waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int kW32WaitLgkm0 = 15 | (3 << 14) | (7 << 4);
 
-template <bool BF, int EPI, bool SPLITK>
+template <bool BF, int EPI, bool SPLITK, int LW>
 __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
     using E = Elem<BF>;
+    using G = W32Geom<LW>;
     typedef typename E::vec8 vec8;
     typedef __attribute__((address_space(3))) void lds_void;
-    __shared__ __attribute__((aligned(16))) uint4 Win0[kW32Slots];
-    __shared__ __attribute__((aligned(16))) uint4 Win1[kW32Slots];
+    __shared__ __attribute__((aligned(16))) uint4 Win0[G::Slots];
+    __shared__ __attribute__((aligned(16))) uint4 Win1[G::Slots];
     __shared__ float bias_s[256];   // this workgroup's 256 output rows (0 past C_out / no bias)
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int j = lane & 31, hh = lane >> 5;
+    const int pr = j / LW, pc = j % LW;      // row / column of lane column j in its block
     const int wm = wave & 1, wn = wave >> 1;
 
     uint32_t lin = xcd_remap(blockIdx.x, a.total_wg);
@@ -299,7 +310,7 @@ __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
     const int n = lin % a.N;
     const int split = lin / a.N;
 
-    const int oh0 = th * kW32TH, ow0 = tw * kW32TW;
+    const int oh0 = th * G::TH, ow0 = tw * G::TW;
     const int c_begin = split * a.chunks_per_split;
     const int c_end = min(a.nchunks, c_begin + a.chunks_per_split);
     const int kd_lo = od == 0 ? 1 : 0;            // live temporal taps: frame od-1+kd in [0, D)
@@ -307,7 +318,7 @@ __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
     const int nkd = kd_hi - kd_lo + 1;
     const int nst = max(0, (c_end - c_begin) * nkd);
     const int mbase = mt * 256 + wm * 128;        // this wave's first GEMM row
-    const bool mlive = mbase < a.Mrows;           // all-padding waves skip their MFMAs
+    const bool mlive = mbase < a.Mrows;           // (all-padding waves compute zeros, store none)
 
     const size_t frame_elems = (size_t)a.H * a.W * a.C_in;
     const uint32_t frame_bytes = (uint32_t)(frame_elems * 2);
@@ -319,7 +330,8 @@ __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
         kd = kd_lo + s % nkd;
     };
     // Window copies: this wave issues copies k = wave + 4*t; lane i of copy k fills slot 64k + i
-    // = position 16k + i/4 (row, column = position / 36, % 36), piece (i%4) ^ ((column/4) % 4).
+    // = position 16k + i/4 (row, column = position / RowPos, % RowPos), piece (i%4) ^
+    // ((column/4) % 4).
     // The source offsets are recomputed per stage (a few ALU operations) rather than kept live.
     auto copy_window = [&](int s, uint4 *dst) {
         int cc, kd;
@@ -328,48 +340,58 @@ __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
             (void *)(a.x + ((size_t)n * a.D + (od - 1 + kd)) * frame_elems), (short)0,
             (int)frame_bytes, 0x00020000);
 #pragma unroll
-        for (int t = 0; t < kW32CopiesPerWave; ++t) {
+        for (int t = 0; t < G::CopiesPerWave; ++t) {
             const int k = wave + 4 * t;
-            if (kW32Copies % 4 != 0 && k >= kW32Copies) break;   // wave-uniform
+            if (G::Copies % 4 != 0 && k >= G::Copies) break;   // wave-uniform
             const int pos = 16 * k + (lane >> 2);
-            const int wh = pos / kW32RowPos, ww = pos - wh * kW32RowPos;
+            const int wh = pos / G::RowPos, ww = pos - wh * G::RowPos;
             const int piece = (lane & 3) ^ ((ww >> 2) & 3);
             const int h = oh0 - 1 + wh, w = ow0 - 1 + ww;
-            const bool ok = ww < kW32WW && (unsigned)h < (unsigned)a.H && (unsigned)w < (unsigned)a.W &&
+            const bool ok = ww < G::WW && pos < G::Pos && (unsigned)h < (unsigned)a.H && (unsigned)w < (unsigned)a.W &&
                             cc * 32 + 8 * piece < a.C_in;
             const uint32_t off = ok ? (uint32_t)(((h * a.W + w) * a.C_in + cc * 32 + 8 * piece) * 2) : 0xFFFFFFFFu;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)&dst[k * 64], 16, off, 0, 0, 0);
         }
     };
-    // weight fragments of slice q (tap q/2, k half q%2) of stage s: 4 blocks of 32 rows; the
-    // per-lane part of the offset is fixed, the rest is wave-uniform (scalar offset)
+    // weight fragments of slice q (tap q/2, k half q%2) of the stage whose first slice starts at
+    // scalar offset sb: 4 blocks of 32 rows; the per-lane part of the offset is fixed
     const uint32_t alane = (uint32_t)((mbase + j) * 32 + 16 * hh);
-    auto load_a = [&](int s, int q, vec8 (&dst)[4]) {
+    auto stage_abase = [&](int s) {
         int cc, kd;
         stage_coords(s, cc, kd);
-        const int tap = kd * 9 + q / 2, k2 = q % 2;
-        const uint32_t sbase = (uint32_t)(((size_t)(cc * 27 + tap) * 2 + k2) * a.Mpad * 32);
+        return (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(cc * 27 + kd * 9) * 2u * a.Mpad * 32u));
+    };
+    const uint32_t slice_bytes = (uint32_t)a.Mpad * 32u;   // one k16 slice of all rows
+    auto load_a = [&](uint32_t sb, int q, vec8 (&dst)[4]) {
+        const uint32_t sbase = sb + (uint32_t)q * slice_bytes;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
             dst[mb] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(
-                wr, alane + mb * 1024u, __builtin_amdgcn_readfirstlane(sbase), 0));
+                wr, alane + mb * 1024u, sbase, 0));
     };
-    // B fragment of slice q, block nb (tile row 4*wn + nb) from a window buffer: a per-lane slot
-    // for (kx, k half) -- six values -- plus a compile-time row offset
+    // B fragment of slice q, block nb (rows WR*wn + R*nb .. +R-1 of the tile) from a window
+    // buffer: a per-lane slot for (kx, k half) -- six values -- plus a compile-time row offset
     int lslot[3][2];
 #pragma unroll
     for (int kx = 0; kx < 3; ++kx)
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) lslot[kx][k2] = w32_slot(4 * wn, j + kx, 2 * k2 + hh);
+        for (int k2 = 0; k2 < 2; ++k2)
+            lslot[kx][k2] = w32_slot<G::RowPos>(G::WR * wn + pr, pc + kx, 2 * k2 + hh);
     auto read_b = [&](const uint4 *win, int q, int nb) {
         const int tap = q / 2, ky = tap / 3, kx = tap % 3;
-        return __builtin_bit_cast(vec8, win[lslot[kx][q % 2] + (nb + ky) * (kW32RowPos * 4)]);
+        return __builtin_bit_cast(vec8, win[lslot[kx][q % 2] + (G::R * nb + ky) * (G::RowPos * 4)]);
     };
 
     // (every launched workgroup has at least one stage: splits are never empty and every
-    // output frame has a live temporal tap; the first slice starts the accumulators at zero)
+    // output frame has a live temporal tap)
     f32x16_t acc[4][4];
-    const f32x16_t zero = {};
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            acc[mb][nb] = f32x16_t{};
+            w32_touch(acc[mb][nb]);   // keeps the accumulators in AGPRs from the start
+        }
     vec8 aq[kW32PD][4];
     vec8 bq[2][4];
 
@@ -379,8 +401,9 @@ __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
     }
     copy_window(0, Win0);
     if (nst > 1) copy_window(1, Win1);
+    uint32_t sb_cur = stage_abase(0);
 #pragma unroll
-    for (int q = 0; q < kW32PD; ++q) load_a(0, q, aq[q]);
+    for (int q = 0; q < kW32PD; ++q) load_a(sb_cur, q, aq[q]);
     // windows 0 and 1 complete: younger than them are only the weight loads
     __builtin_amdgcn_s_waitcnt(w32_waitcnt_vm(kW32PD * 4));
     w32_barrier();
@@ -399,6 +422,8 @@ __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
             uint4 *const cur = half == 0 ? Win0 : Win1;
             uint4 *const nxt = half == 0 ? Win1 : Win0;
             const bool more = s + 1 < nst;
+            // weights of the next stage (a stage past the last re-reads this one's, never used)
+            const uint32_t sb_next = more ? stage_abase(s + 1) : sb_cur;
 #pragma unroll
             for (int q = 0; q < kW32Slices; ++q) {
                 const int cb = q & 1;
@@ -406,25 +431,15 @@ __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
 #pragma unroll
                     for (int nb = 0; nb < 4; ++nb) bq[cb ^ 1][nb] = read_b(cur, q + 1, nb);
                 }
-                if (mlive) {
-                    if (half == 0 && q == 0 && s0 == 0) {
 #pragma unroll
-                        for (int mb = 0; mb < 4; ++mb)
+                for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-                            for (int nb = 0; nb < 4; ++nb)
-                                acc[mb][nb] = E::mfma32x32x16(aq[q % kW32PD][mb], bq[cb][nb], zero);
-                    } else {
-#pragma unroll
-                        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-                            for (int nb = 0; nb < 4; ++nb)
-                                acc[mb][nb] = E::mfma32x32x16(aq[q % kW32PD][mb], bq[cb][nb], acc[mb][nb]);
-                    }
-                }
+                    for (int nb = 0; nb < 4; ++nb)
+                        acc[mb][nb] = E::mfma32x32x16(aq[q % kW32PD][mb], bq[cb][nb], acc[mb][nb]);
                 // refill the ring slot with the slice kW32PD ahead (in the next stage when past
-                // this one; a stage past the last re-reads valid weights, never used)
-                if (q + kW32PD < kW32Slices) load_a(s, q + kW32PD, aq[q % kW32PD]);
-                else load_a(more ? s + 1 : s, q + kW32PD - kW32Slices, aq[q % kW32PD]);
+                // this one)
+                if (q + kW32PD < kW32Slices) load_a(sb_cur, q + kW32PD, aq[q % kW32PD]);
+                else load_a(sb_next, q + kW32PD - kW32Slices, aq[q % kW32PD]);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (more) {
@@ -438,6 +453,7 @@ __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
 #pragma unroll
                 for (int nb = 0; nb < 4; ++nb) bq[0][nb] = read_b(nxt, 0, nb);
             }
+            sb_cur = sb_next;
         }
     }
     __builtin_amdgcn_s_waitcnt(w32_waitcnt_vm(0));
@@ -445,7 +461,7 @@ __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
     const size_t P = (size_t)a.N * a.D * a.H * a.W;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-        const int oh = oh0 + 4 * wn + nb, ow = ow0 + j;
+        const int oh = oh0 + G::WR * wn + G::R * nb + pr, ow = ow0 + pc;
         const bool inside = oh < a.H && ow < a.W;
         const size_t pos = (((size_t)n * a.D + od) * a.H + oh) * a.W + ow;
 #pragma unroll
@@ -568,17 +584,24 @@ hipError_t launch_family(const IgemmPlan &pl, const IgemmKArgs &ka, int epi, boo
     return hipGetLastError();
 }
 
+template <bool BF, int LW>
+hipError_t launch_w32(const IgemmKArgs &ka, int epi, bool splitk, dim3 grid, hipStream_t s) {
+    const dim3 block(256);
+    if (splitk) igemm32_kernel<BF, EPI_NONE, true, LW><<<grid, block, 0, s>>>(ka);
+    else if (epi == EPI_RELU) igemm32_kernel<BF, EPI_RELU, false, LW><<<grid, block, 0, s>>>(ka);
+    else if (epi == EPI_CLAMP1) igemm32_kernel<BF, EPI_CLAMP1, false, LW><<<grid, block, 0, s>>>(ka);
+    else igemm32_kernel<BF, EPI_NONE, false, LW><<<grid, block, 0, s>>>(ka);
+    return hipGetLastError();
+}
+
 template <bool BF>
 hipError_t launch_igemm_dtype(const IgemmPlan &pl, const IgemmKArgs &ka, int epi, bool splitk,
                               hipStream_t s) {
     switch (pl.family) {
         case IG_W32: {
-            const dim3 grid((unsigned)pl.workgroups), block(256);
-            if (splitk) igemm32_kernel<BF, EPI_NONE, true><<<grid, block, 0, s>>>(ka);
-            else if (epi == EPI_RELU) igemm32_kernel<BF, EPI_RELU, false><<<grid, block, 0, s>>>(ka);
-            else if (epi == EPI_CLAMP1) igemm32_kernel<BF, EPI_CLAMP1, false><<<grid, block, 0, s>>>(ka);
-            else igemm32_kernel<BF, EPI_NONE, false><<<grid, block, 0, s>>>(ka);
-            return hipGetLastError();
+            const dim3 grid((unsigned)pl.workgroups);
+            if (pl.TW == 32) return launch_w32<BF, 32>(ka, epi, splitk, grid, s);
+            return launch_w32<BF, 16>(ka, epi, splitk, grid, s);
         }
         case IG_WIDE:
             return launch_family<BF, 4, 4, 2, 2, 8, 16>(pl, ka, epi, splitk, s);
@@ -602,10 +625,16 @@ IgemmPlan plan_igemm(int family, int N, int C_in, int C_out, int D, int H, int W
             pl.BM = 16, pl.TH = 8, pl.TW = 32, pl.ntaps = 27;
             pl.Mrows = C_out;
             break;
-        case IG_W32:
-            pl.BM = 256, pl.TH = 8, pl.TW = 32, pl.ntaps = 27;
+        case IG_W32: {
+            // 8 x 32 tiles, or 16 x 16 when those compute fewer padded positions (narrow frames)
+            pl.BM = 256, pl.ntaps = 27;
             pl.Mrows = C_out;
+            const long long a32 = (long long)((H + 7) / 8) * 8 * ((W + 31) / 32) * 32;
+            const long long a16 = (long long)((H + 15) / 16) * 16 * ((W + 15) / 16) * 16;
+            if (a16 < a32) pl.TH = 16, pl.TW = 16;
+            else pl.TH = 8, pl.TW = 32;
             break;
+        }
         default:   // the head kernels: 3 temporal taps x 128 rows (9 * C_out used)
             pl.BM = 128, pl.TH = 1, pl.TW = 256, pl.ntaps = 3;
             pl.Mrows = 128;
@@ -626,10 +655,24 @@ IgemmPlan plan_igemm(int family, int N, int C_in, int C_out, int D, int H, int W
     const long long base = (long long)N * D * pl.tiles_h * pl.tiles_w * pl.mtiles;
     // Split K when the output alone cannot fill the 256 compute units a few times over.
     int splits = 1;
-    // (The 32x32 kernel runs one workgroup per CU, the 16x16 ones two.)
-    const long long fill = family == IG_W32 ? 512 : 1024;
-    if (family != IG_TEMPORAL && base > 0 && base < fill) {
-        splits = (int)((fill + base - 1) / base);
+    if (family == IG_W32 && base > 0) {
+        // One workgroup per CU: pick the split count minimising rounds of 256 workgroups x
+        // (stages per workgroup + about one stage of prologue/epilogue) plus the fp32 partials'
+        // round trip (8 bytes per partial element at HBM speed: about one stage per 3.75 M).
+        const double taps = D >= 3 ? (3.0 * D - 2.0) / D : (D == 2 ? 2.0 : 1.0);
+        const double part = (double)N * D * H * W * C_out / 3.75e6;
+        double best = -1.0;
+        for (int sp = 1; sp <= pl.nchunks; ++sp) {
+            const int cps = (pl.nchunks + sp - 1) / sp;
+            const int se = (pl.nchunks + cps - 1) / cps;
+            if (se != sp) continue;
+            const long long rounds = (base * se + 255) / 256;
+            const double cost = rounds * (cps * taps + 1.0) + (se > 1 ? se * part : 0.0);
+            if (best < 0 || cost < best) best = cost, splits = se;
+        }
+    } else if (family != IG_TEMPORAL && base > 0 && base < 1024) {
+        // (the 16x16 kernels run two workgroups per CU)
+        splits = (int)((1024 + base - 1) / base);
         if (splits > pl.nchunks) splits = pl.nchunks;
     }
     pl.chunks_per_split = (pl.nchunks + splits - 1) / splits;
