@@ -236,31 +236,33 @@ __global__ __launch_bounds__(256, 2) void igemm3d_kernel(IgemmKArgs a) {
 
 // ---------------------------------------------------------------------------------------------
 // The 27-tap convolution for wide outputs (C_out > 16) on v_mfma_f32_32x32x16: one wave per SIMD
-// keeps that pipe full, and a 128 x 128 tile per wave (4 x 4 blocks, all 256 accumulators) reads
-// a quarter of an A and a quarter of a B fragment per MFMA.  Operand layout: lane l supplies row
-// (A) / column (B) l%32 with the 8 k values of half l/32 of a 16-wide k slice, and receives
-// accumulator element i at row 8*(i/4) + 4*(l/32) + i%4, column l%32.
+// keeps that pipe full.  Each wave owns a 64 x 256 tile (2 x 8 blocks, all 256 accumulators): per
+// k16 slice it takes two weight fragments from L2 and eight input fragments from LDS, so the four
+// waves of a workgroup fetch disjoint weight rows and every weight byte leaves L2 once per
+// workgroup.  Operand layout: lane l supplies row (A) / column (B) l%32 with the 8 k values of
+// half l/32 of a 16-wide k slice, and receives accumulator element i at row 8*(i/4) + 4*(l/32) +
+// i%4, column l%32.
 //
-// Workgroup: 256 output rows (two waves along M) x an 8 x 32 block of positions of one frame (two
-// waves along N, four rows each).  K runs in stages (32-channel chunk, live temporal tap); a
-// stage's input window -- 10 x 34 positions x 32 channels, zero outside the tensor -- is copied
-// global -> LDS by the buffer unit (LDS DMA, 16 positions x 64 bytes per copy, no registers),
-// double-buffered a whole stage ahead, and its nine spatial taps read their B fragments from it by
-// address offset.  Window rows are 36 positions apart (34 used) and each 64-byte position holds
-// its four 16-byte pieces XOR-permuted by (column/4) % 4: any 16 consecutive columns of a row then
-// fall on distinct LDS bank groups, and a fragment address is a per-lane part (column, piece)
-// plus a row part that fits the instruction's offset field.  Weight
-// fragments (1 KiB contiguous each in the packing) stream from L2 into a register ring three taps
-// deep.  The compiler cannot see that a DMA copy into one window buffer never overlaps reads from
-// the other, so the two buffers are separate objects and the stage loop is unrolled by two.
+// Workgroup: 256 output rows (four waves along M) x an 8 x 32 block of positions of one frame.
+// K runs in stages (32-channel chunk, live temporal tap); a stage's input window -- 10 x 34
+// positions x 32 channels, zero outside the tensor -- is copied global -> LDS by the buffer unit
+// (LDS DMA, 16 positions x 64 bytes per copy, no registers) into one of three buffers, two
+// stages ahead, and its nine spatial taps read their B fragments from it by address offset.  Window rows are 36
+// positions apart (34 used) and each 64-byte position holds its four 16-byte pieces XOR-permuted
+// by (column/4) % 4: any 16 consecutive columns of a row then fall on distinct LDS bank groups,
+// and a fragment address is a per-lane part (column, piece) plus a row part that fits the
+// instruction's offset field.  Weight fragments (1 KiB contiguous each in the packing) stream
+// from L2 into a register ring half a stage deep.  The compiler cannot see that a DMA copy into
+// one window buffer never overlaps reads from another, so the three buffers are separate objects
+// and the stage loop is unrolled by three.
 // ---------------------------------------------------------------------------------------------
 // Tile geometry by LW, the columns one 32-lane block spans: LW = 32 gives 8 x 32 positions per
 // workgroup (one row per block), LW = 16 gives 16 x 16 (two rows per block) for narrow frames.
 template <int LW>
 struct W32Geom {
     static constexpr int R = 32 / LW;                    // rows per 32-position block
-    static constexpr int WR = 4 * R;                     // rows per wave (4 blocks)
-    static constexpr int TH = 2 * WR, TW = LW;           // workgroup tile (two waves along N)
+    static constexpr int NB = 8;                         // 32-position blocks per tile
+    static constexpr int TH = NB * R, TW = LW;           // workgroup tile = every wave's tile
     static constexpr int WW = TW + 2;                    // window columns used
     static constexpr int RowPos = (WW + 3) / 4 * 4;      // window row stride (positions)
     static constexpr int Pos = (TH + 2) * RowPos;        // window positions
@@ -269,7 +271,7 @@ struct W32Geom {
     static constexpr int Slots = Copies * 64;            // 16-byte pieces per window buffer
 };
 constexpr int kW32Slices = 18;                          // k16 slices per stage: 9 taps x 2 halves
-constexpr int kW32PD = 6;                               // weight prefetch distance in slices
+constexpr int kW32PD = 9;                               // weight prefetch distance in slices
 
 // slot of (window row r, column c, piece); with RowPos a multiple of 4 the row part is a
 // multiple of 16 slots
@@ -282,6 +284,35 @@ __device__ __forceinline__ void w32_touch(f32x16_t &v) { asm volatile("" : "+a"(
 __device__ constexpr int w32_waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int kW32WaitLgkm0 = 15 | (3 << 14) | (7 << 4);
 
+// Block order.  Workgroups dispatch round-robin over the 8 XCDs (block b to XCD b % 8), each XCD
+// with its own L2.  XCD x takes a contiguous share of the tiles whose frame has all three temporal
+// taps, in tile-major order with the frame innermost (neighbouring frames share two of their
+// three input frames), and after them a share of the first / last frames, which have two taps:
+// the short workgroups run last and fill the final round.  Returns the tile index (all
+// coordinates but the frame) and sets the frame od.
+__device__ __forceinline__ uint32_t w32_block_order(uint32_t b, uint32_t total, int D, int &od) {
+    const uint32_t xcd = b % 8u, k = b / 8u;
+    const uint32_t q8 = total / 8u, r8 = total % 8u;
+    const uint32_t s0 = xcd * q8 + min(xcd, r8), cnt = q8 + (xcd < r8 ? 1u : 0u);
+    const uint32_t inner = D >= 3 ? (uint32_t)(D - 2) : 0u;
+    const uint64_t interior = (uint64_t)(total / (uint32_t)D) * inner;
+    // this XCD's interior share: [c0, c1) of the interior list, proportional to its block count
+    const uint32_t c0 = (uint32_t)((uint64_t)s0 * interior / total);
+    const uint32_t c1 = (uint32_t)((uint64_t)(s0 + cnt) * interior / total);
+    if (k < c1 - c0) {
+        const uint32_t li = c0 + k;
+        od = 1 + (int)(li % inner);
+        return li / inner;
+    }
+    const uint32_t le = (s0 - c0) + (k - (c1 - c0));
+    if (D >= 3) {
+        od = (le & 1u) ? D - 1 : 0;
+        return le >> 1;
+    }
+    od = (int)(le % (uint32_t)D);
+    return le / (uint32_t)D;
+}
+
 template <bool BF, int EPI, bool SPLITK, int LW>
 __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
     using E = Elem<BF>;
@@ -290,23 +321,22 @@ __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
     typedef __attribute__((address_space(3))) void lds_void;
     __shared__ __attribute__((aligned(16))) uint4 Win0[G::Slots];
     __shared__ __attribute__((aligned(16))) uint4 Win1[G::Slots];
+    __shared__ __attribute__((aligned(16))) uint4 Win2[G::Slots];
     __shared__ float bias_s[256];   // this workgroup's 256 output rows (0 past C_out / no bias)
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int j = lane & 31, hh = lane >> 5;
     const int pr = j / LW, pc = j % LW;      // row / column of lane column j in its block
-    const int wm = wave & 1, wn = wave >> 1;
 
-    uint32_t lin = xcd_remap(blockIdx.x, a.total_wg);
+    int od;
+    uint32_t lin = w32_block_order(blockIdx.x, a.total_wg, a.D, od);
     const int mt = lin % a.mtiles;
     lin /= a.mtiles;
     const int tw = lin % a.tiles_w;
     lin /= a.tiles_w;
     const int th = lin % a.tiles_h;
     lin /= a.tiles_h;
-    const int od = lin % a.D;
-    lin /= a.D;
     const int n = lin % a.N;
     const int split = lin / a.N;
 
@@ -317,7 +347,7 @@ __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
     const int kd_hi = od == a.D - 1 ? 1 : 2;
     const int nkd = kd_hi - kd_lo + 1;
     const int nst = max(0, (c_end - c_begin) * nkd);
-    const int mbase = mt * 256 + wm * 128;        // this wave's first GEMM row
+    const int mbase = mt * 256 + wave * 64;       // this wave's first GEMM row
     const bool mlive = mbase < a.Mrows;           // (all-padding waves compute zeros, store none)
 
     const size_t frame_elems = (size_t)a.H * a.W * a.C_in;
@@ -354,7 +384,7 @@ __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
         }
     };
     // weight fragments of slice q (tap q/2, k half q%2) of the stage whose first slice starts at
-    // scalar offset sb: 4 blocks of 32 rows; the per-lane part of the offset is fixed
+    // scalar offset sb: 2 blocks of 32 rows; the per-lane part of the offset is fixed
     const uint32_t alane = (uint32_t)((mbase + j) * 32 + 16 * hh);
     auto stage_abase = [&](int s) {
         int cc, kd;
@@ -362,21 +392,21 @@ __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
         return (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(cc * 27 + kd * 9) * 2u * a.Mpad * 32u));
     };
     const uint32_t slice_bytes = (uint32_t)a.Mpad * 32u;   // one k16 slice of all rows
-    auto load_a = [&](uint32_t sb, int q, vec8 (&dst)[4]) {
+    auto load_a = [&](uint32_t sb, int q, vec8 (&dst)[2]) {
         const uint32_t sbase = sb + (uint32_t)q * slice_bytes;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+        for (int mb = 0; mb < 2; ++mb)
             dst[mb] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(
                 wr, alane + mb * 1024u, sbase, 0));
     };
-    // B fragment of slice q, block nb (rows WR*wn + R*nb .. +R-1 of the tile) from a window
+    // B fragment of slice q, block nb (rows R*nb .. +R-1 of the tile) from a window
     // buffer: a per-lane slot for (kx, k half) -- six values -- plus a compile-time row offset
     int lslot[3][2];
 #pragma unroll
     for (int kx = 0; kx < 3; ++kx)
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2)
-            lslot[kx][k2] = w32_slot<G::RowPos>(G::WR * wn + pr, pc + kx, 2 * k2 + hh);
+            lslot[kx][k2] = w32_slot<G::RowPos>(pr, pc + kx, 2 * k2 + hh);
     auto read_b = [&](const uint4 *win, int q, int nb) {
         const int tap = q / 2, ky = tap / 3, kx = tap % 3;
         return __builtin_bit_cast(vec8, win[lslot[kx][q % 2] + (G::R * nb + ky) * (G::RowPos * 4)]);
@@ -384,16 +414,16 @@ __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
 
     // (every launched workgroup has at least one stage: splits are never empty and every
     // output frame has a live temporal tap)
-    f32x16_t acc[4][4];
+    f32x16_t acc[2][G::NB];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
+        for (int nb = 0; nb < G::NB; ++nb) {
             acc[mb][nb] = f32x16_t{};
             w32_touch(acc[mb][nb]);   // keeps the accumulators in AGPRs from the start
         }
-    vec8 aq[kW32PD][4];
-    vec8 bq[2][4];
+    vec8 aq[kW32PD][2];
+    vec8 bq[2][G::NB];
 
     {
         const int m = mt * 256 + threadIdx.x;
@@ -401,26 +431,29 @@ __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
     }
     copy_window(0, Win0);
     if (nst > 1) copy_window(1, Win1);
+    if (nst > 2) copy_window(2, Win2);
     uint32_t sb_cur = stage_abase(0);
 #pragma unroll
     for (int q = 0; q < kW32PD; ++q) load_a(sb_cur, q, aq[q]);
-    // windows 0 and 1 complete: younger than them are only the weight loads
-    __builtin_amdgcn_s_waitcnt(w32_waitcnt_vm(kW32PD * 4));
+    // windows 0..2 complete: younger than them are only the weight loads
+    __builtin_amdgcn_s_waitcnt(w32_waitcnt_vm(kW32PD * 2));
     w32_barrier();
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) bq[0][nb] = read_b(Win0, 0, nb);
+    for (int nb = 0; nb < G::NB; ++nb) bq[0][nb] = read_b(Win0, 0, nb);
 
-    // Stage s computes from window buffer s % 2 and, at its start, has window s+1 in flight.
-    // After its last slice: wait for window s+1, barrier (every wave done with window s), copy
-    // window s+2 into window s's buffer.
+    // Stage s computes from window buffer s % 3.  Window s+1 is complete for every wave from the
+    // barrier that ends stage s-1 on, so the last slice of stage s already reads the first
+    // fragments of stage s+1 and the MFMA pipe runs through the stage boundary.  The barrier that
+    // ends stage s says every wave is done with window s (its buffer then takes window s+3) and
+    // has its own copies of window s+2 complete.
 #pragma unroll 1
-    for (int s0 = 0; s0 < nst; s0 += 2) {
+    for (int s0 = 0; s0 < nst; s0 += 3) {
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int s = s0 + half;
-            if (half == 1 && s >= nst) break;              // odd stage count: uniform
-            uint4 *const cur = half == 0 ? Win0 : Win1;
-            uint4 *const nxt = half == 0 ? Win1 : Win0;
+        for (int third = 0; third < 3; ++third) {
+            const int s = s0 + third;
+            if (third > 0 && s >= nst) break;              // uniform
+            uint4 *const cur = third == 0 ? Win0 : third == 1 ? Win1 : Win2;
+            uint4 *const nxt = third == 0 ? Win1 : third == 1 ? Win2 : Win0;
             const bool more = s + 1 < nst;
             // weights of the next stage (a stage past the last re-reads this one's, never used)
             const uint32_t sb_next = more ? stage_abase(s + 1) : sb_cur;
@@ -429,12 +462,20 @@ __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
                 const int cb = q & 1;
                 if (q + 1 < kW32Slices) {
 #pragma unroll
-                    for (int nb = 0; nb < 4; ++nb) bq[cb ^ 1][nb] = read_b(cur, q + 1, nb);
+                    for (int nb = 0; nb < G::NB; ++nb) bq[cb ^ 1][nb] = read_b(cur, q + 1, nb);
+                } else {
+                    // (after the last stage these reads are of a stale buffer and never used;
+                    // issuing them anyway keeps the wait counts the same on every path)
+#pragma unroll
+                    for (int nb = 0; nb < G::NB; ++nb) bq[cb ^ 1][nb] = read_b(nxt, 0, nb);
                 }
+                // the next slice's reads go out before this slice's MFMAs (left to itself the
+                // scheduler sinks them behind the MFMAs and single-buffers the fragments)
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int mb = 0; mb < 4; ++mb)
+                for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                    for (int nb = 0; nb < 4; ++nb)
+                    for (int nb = 0; nb < G::NB; ++nb)
                         acc[mb][nb] = E::mfma32x32x16(aq[q % kW32PD][mb], bq[cb][nb], acc[mb][nb]);
                 // refill the ring slot with the slice kW32PD ahead (in the next stage when past
                 // this one)
@@ -443,15 +484,12 @@ __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (more) {
-                // window s+1 complete (its copies were issued at the start of this stage, with
-                // this stage's weight loads -- 4 per slice -- after them); every wave is done
-                // with window s before it takes window s+2
-                __builtin_amdgcn_s_waitcnt(w32_waitcnt_vm(63));
+                // own copies of window s+2 complete: they were issued after the previous
+                // barrier, and only this stage's weight loads (2 per slice) came after them
+                __builtin_amdgcn_s_waitcnt(w32_waitcnt_vm(2 * kW32Slices));
                 __builtin_amdgcn_s_waitcnt(kW32WaitLgkm0);
                 w32_barrier();
-                if (s + 2 < nst) copy_window(s + 2, cur);
-#pragma unroll
-                for (int nb = 0; nb < 4; ++nb) bq[0][nb] = read_b(nxt, 0, nb);
+                if (s + 3 < nst) copy_window(s + 3, cur);
             }
             sb_cur = sb_next;
         }
@@ -460,12 +498,12 @@ __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
 
     const size_t P = (size_t)a.N * a.D * a.H * a.W;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-        const int oh = oh0 + G::WR * wn + G::R * nb + pr, ow = ow0 + pc;
+    for (int nb = 0; nb < G::NB; ++nb) {
+        const int oh = oh0 + G::R * nb + pr, ow = ow0 + pc;
         const bool inside = oh < a.H && ow < a.W;
         const size_t pos = (((size_t)n * a.D + od) * a.H + oh) * a.W + ow;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
+        for (int mb = 0; mb < 2; ++mb) {
             w32_touch(acc[mb][nb]);
             if (inside && mlive) {
 #pragma unroll
