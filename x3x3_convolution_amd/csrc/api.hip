@@ -102,10 +102,10 @@ int select_3d(int N, int C_in, int C_out, int D, int H, int W, int stride, int l
     const long long pos = (long long)N * D * H * W;
     if (pos >= (1ll << 31) / 8 || (long long)C_out * 27 * C_in >= (1ll << 31))
         return fail(CONV_E_UNSUPPORTED, "problem too large for one launch");
-    // the head kernels address one sample of x through a 32-bit buffer range
-    const bool sample_fits = (long long)D * H * W * C_in * 2 < (1ll << 31);
+    // the head kernels address one sample of x and of y through 32-bit buffer ranges
+    const bool sample_fits = (long long)D * H * W * (C_in > C_out ? C_in : C_out) * 2 < (1ll << 31);
     if (head_algo && !sample_fits)
-        return fail(CONV_E_UNSUPPORTED, "the head algorithms need one sample of x below 2 GiB");
+        return fail(CONV_E_UNSUPPORTED, "the head algorithms need one sample of x and of y below 2 GiB");
     if (algo == CONV_ALGO_AUTO)
         return (C_out <= kSplitHeadMaxCout && sample_fits) ? CONV_ALGO_FUSED_HEAD : CONV_ALGO_MFMA;
     return algo;

@@ -157,36 +157,42 @@ __global__ __launch_bounds__(256) void head_stencil_kernel(StencilKArgs a) {
 // slot t = 16*mb + i of that half; slot t < 54 holds spatial tap t/6 of output channel 6*h + t%6.
 // So every lane owns six output channels of its four positions, with all nine taps in registers.
 //
-// K order: 64-channel chunks (one 128-byte cache line of a position), and in a chunk the three
-// temporal taps one after the other, each as four k16 slices.  Slice s takes channels
-// 32*h + 8*s .. +7 from lane half h, so for one tap the four slices of a position are the four
-// consecutive 16-byte pieces of the lane's half line.  A tap runs as two half-taps (column blocks
-// 0-1, then 2-3), each four slices of 4 x 2 MFMAs.
-//   * B (activations): raw buffer loads straight into registers; the four pieces of a lane's
-//     half line are loaded back to back, so every cache line is fetched whole, once.  Rows,
-//     columns, frames and channels outside the tensor read as zero without branches (the
-//     convolution's zero padding).  A ring of four half-taps: each half-tap starts by loading
-//     the half-tap three ahead.
-//   * A (weights, 3 taps x 128 rows x 64 channels = 48 KiB per chunk): copied global -> LDS by
-//     the buffer unit itself (LDS DMA, no registers), two buffers, each chunk issued a whole
-//     chunk before it is needed.  The packing stores every 128-byte row with its eight 16-byte
-//     pieces already XOR-permuted, so the fragment reads spread over the LDS banks.
+// K runs in stages of 32 channels; a stage holds the three temporal taps, each as two k16 slices
+// (six steps of 4 x 4 MFMAs).  Both operands of a stage are copied global -> LDS by the buffer
+// unit itself (LDS DMA: no registers, 1 KiB per instruction) into one of two buffer pairs:
+//   * A (weights): 3 taps x 128 rows x 32 channels = 24 KiB, contiguous in the packing, which
+//     already holds the LDS order.
+//   * B (activations): the 128 positions of the row in the six input frames the four output
+//     frames read (frames f0-1 .. f0+4), 32 channels each = 48 KiB.  Output frame f0+w reads
+//     input frames w, w+1, w+2 of the window, so the three waves that share an input frame
+//     share one copy of it.  Rows, columns, frames and channels outside the tensor copy zeros
+//     (the convolution's zero padding); the copies need no branches.
+// An A or B row is 64 bytes = four 16-byte pieces, stored XOR-permuted by (row/4) % 4 (A) or
+// (column j/4) % 4 (B): the 32 rows / columns a fragment read takes fall on distinct LDS banks.
+// A fragment read is a per-lane part (row or column, piece) plus a compile-time offset.
+//
+// A wave never waits for a copy it just issued: the copies of stage g+1 are issued one stage
+// ahead, and a single barrier per stage, placed before the stage's last step, publishes them to
+// every wave (each wave first waits for its own copies) and frees the buffers of stage g (every
+// wave has its last fragments of stage g in registers): the copies of stage g+2 go out right after
+// it, and the first fragments of stage g+1 are read while the last step's MFMAs run.
 //
 // PLANE mode stores Z, rounded to the storage type, as the 112-channel plane of the split head.
 // FUSED mode applies the nine-tap stencil in registers: the horizontal taps combine neighbouring
-// positions, the vertical taps are carried from row to row (two fp32 partial sums per output),
-// and bias + epilogue are applied once per output.  Output row h needs Z rows h-1 .. h+1 and
-// columns w-1 .. w+1, so a strip computes 128 columns for 126 outputs and a band two extra rows.
-// Nothing of Z is rounded or stored: the fused head keeps fp32 from the GEMM to the epilogue.
+// positions, the vertical taps are carried from row to row (two fp32 partial sums per output,
+// in registers), and bias + epilogue are applied once per output.  Output row h needs Z rows
+// h-1 .. h+1 and columns w-1 .. w+1, so a strip computes 128 columns for 126 outputs and a band
+// two extra rows.  Nothing of Z is rounded or stored: the fused head keeps fp32 from the GEMM to
+// the epilogue.
 // ---------------------------------------------------------------------------------------------
 constexpr int kMB = 4;                  // 32-row blocks: 128 GEMM rows per temporal tap
 constexpr int kNB = 4;                  // 32-column blocks per wave
 constexpr int kWavePos = 32 * kNB;      // 128 positions per wave and row
-constexpr int kSlices = 4;              // k16 slices per tap of a 64-channel chunk
-constexpr int kHalves = 6;              // half-taps per chunk
-constexpr int kRing = 4;                // B ring depth in half-taps
-constexpr int kLoadsPerHalf = 2 * kSlices;   // B loads per half-tap
-constexpr int kDmaPerWave = kHeadChunkPieces / 256;  // 12 LDS-DMA copies of 1 KiB per wave
+constexpr int kSteps = 6;               // k16 steps per stage: 3 temporal taps x 2 slices
+constexpr int kInFrames = 6;            // input frames of a workgroup's four output frames
+constexpr int kBPieces = kInFrames * kWavePos * 4;   // 16-byte pieces of a stage's B window
+constexpr int kCopyA = kHeadChunkPieces / 256;       // LDS-DMA copies of 1 KiB per wave: 6
+constexpr int kCopyB = kBPieces / 256;               // 12
 constexpr int kHalfCo = 6;              // output channels per lane half
 constexpr int kPlaneCh = kHeadPlaneChannels;
 constexpr uint32_t kOff = 0xFFFFFFFFu;  // an offset past any buffer range; saturating adds keep it
@@ -194,11 +200,7 @@ constexpr uint32_t kOff = 0xFFFFFFFFu;  // an offset past any buffer range; satu
 // s_waitcnt immediates: vmcnt is split over bits 3:0 and 15:14; expcnt / lgkmcnt left open.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
-// Every half-tap starts with its B loads.  The copy of chunk g+1 is issued at the barrier before
-// the last slice of chunk g-1 and must be complete at the same point of chunk g: the operations
-// a wave issues in between are the B loads of the six half-taps of chunk g.
-constexpr int kVmAfterCopy = kLoadsPerHalf * kHalves;
-static_assert(kVmAfterCopy < 64, "vmcnt holds 6 bits");
+static_assert(kCopyA + kCopyB < 64, "vmcnt holds 6 bits");
 
 struct HeadGemmKArgs {
     const u16 *x;
@@ -206,7 +208,7 @@ struct HeadGemmKArgs {
     const u16 *bias;
     u16 *out;          // the plane (PLANE) or y (FUSED)
     int N, C_in, C_out, D, H, W;
-    int nchunks;       // 64-channel chunks per Z row, even (the padding reads zeros)
+    int nchunks;       // 32-channel stages per Z row, even (the padding reads zeros)
     int rows_per_band, bands, strips, strip_out, fgroups;
     uint32_t sample_bytes;  // bytes of one sample of x (buffer-resource range)
     uint32_t wp_bytes;
@@ -227,14 +229,12 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
     using E = Elem<BF>;
     typedef typename E::vec8 vec8;
     typedef __attribute__((address_space(3))) void lds_void;
-    // Two weight buffers (even / odd chunks), separate objects so the compiler can tell that the
-    // copy into one never overlaps the fragment reads from the other.
+    // Two buffer pairs (even / odd stages), separate objects so the compiler can tell that the
+    // copies into one never overlap the fragment reads from the other.
     __shared__ __attribute__((aligned(16))) uint4 As0[kHeadChunkPieces];
     __shared__ __attribute__((aligned(16))) uint4 As1[kHeadChunkPieces];
-    // FUSED: the two carried partial sums of every lane's 6 channels x 4 positions, per wave
-    // (cA: the output row before the next Z row, cB: the output row of the next Z row), as
-    // float4 {cA0..3}, {cA4, cA5, cB0, cB1}, {cB2..5}.  Private to each wave.
-    __shared__ float4 carry[FUSED ? 4 : 1][kNB][3][64];
+    __shared__ __attribute__((aligned(16))) uint4 Bs0[kBPieces];
+    __shared__ __attribute__((aligned(16))) uint4 Bs1[kBPieces];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -247,7 +247,8 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
     lin /= a.strips;
     const int band = lin % a.bands;
     const int n = lin / a.bands;
-    const int od = fg * 4 + wave;      // this wave's output frame (>= D: computes, stores nothing)
+    const int f0 = fg * 4;             // the group's first output frame
+    const int od = f0 + wave;          // this wave's output frame (>= D: computes, stores nothing)
 
     const int HW = a.H * a.W;
     const int w0 = FUSED ? strip * a.strip_out - 1 : strip * kWavePos;   // column of position 0
@@ -256,175 +257,156 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
     const int zrow0 = FUSED ? h_begin - 1 : h_begin;
     const int nsteps = (h_end - h_begin) + (FUSED ? 2 : 0);   // Z rows, the same in every wave
     const int nch = a.nchunks;
+    const int nstages = nsteps * nch;
 
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(a.x + (size_t)n * a.D * HW * a.C_in), (short)0, (int)a.sample_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
         (void *)a.wp, (short)0, (int)a.wp_bytes, 0x00020000);
+    // FUSED: one sample of y
+    const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.out + (size_t)n * a.D * HW * a.C_out), (short)0, (int)(a.D * HW * a.C_out * 2),
+        0x00020000);
 
-    // Byte offset of a B piece = a per-lane column part (fixed for the whole band) + a part for
-    // (row, frame, chunk, lane half, slice), added with saturation so that either part out of
-    // range makes the load read zero.
-    uint32_t colpart[kNB];
+    // B window copies: this wave issues copies k = wave + 4*t; lane i of copy k fills slot
+    // 64*k + i = ((frame*4 + nb)*32 + column j)*4 + piece', with frame = k/8, nb = (k/2) % 4,
+    // j = 16*(k%2) + i/4 and piece' = piece ^ ((j/4) % 4) -- the piece of lane i is therefore
+    // (i%4) ^ ((i/16) % 4) in every copy, and its column w0 + 4*(i/4) plus a part that depends
+    // on k alone.
+    const int bpiece = (lane & 3) ^ ((lane >> 4) & 3);
+    const int bw = w0 + 4 * (lane >> 2);
+    const uint32_t bcolpart = (uint32_t)(bw * a.C_in + 8 * bpiece) * 2u;
+    // Copies of stage g (Z row g / nch, channel chunk g % nch) into one buffer pair.  Weight
+    // chunks past the packed ones (the even padding) lie past the resource range and copy zeros.
+    auto copy_stage = [&](int g, uint4 *abuf, uint4 *bbuf) {
+        const int st = g / nch, c = g - st * nch;
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
-        const int w = w0 + 4 * j + nb;
-        colpart[nb] = (unsigned)w < (unsigned)a.W ? (uint32_t)(w * a.C_in) * 2u : kOff;
-    }
-    // per-slice offsets of one tap (Z row st, chunk c, tap kd) for this lane
-    auto tap_offsets = [&](int st, int c, int kd, uint32_t (&up)[kSlices]) {
-        const int row = zrow0 + st, f = od - 1 + kd;
-        const bool ok = (unsigned)row < (unsigned)a.H && (unsigned)f < (unsigned)a.D;
-        const uint32_t base = (uint32_t)((((size_t)f * HW + (size_t)row * a.W) * a.C_in + c * 64 + 32 * hh) * 2u);
-#pragma unroll
-        for (int sl = 0; sl < kSlices; ++sl)
-            up[sl] = ok && c * 64 + 32 * hh + 8 * sl < a.C_in ? base + 16u * sl : kOff;
-    };
-    // B of a half-tap: blocks 2*hp and 2*hp+1, each the four slices of the lane's half line
-    // back to back
-    auto load_half = [&](int st, int c, int kd, int hp, vec8 (&dst)[2][kSlices]) {
-        uint32_t up[kSlices];
-        tap_offsets(st, c, kd, up);
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int sl = 0; sl < kSlices; ++sl)
-                dst[b][sl] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(
-                    xr, __builtin_elementwise_add_sat(up[sl], colpart[2 * hp + b]), 0, 0));
-    };
-    // LDS DMA of packed weight chunk cc into buffer dstbuf: each wave copies 12 KiB.  Chunks past
-    // the packed ones (the even padding) lie past the resource range and copy zeros.
-    auto copy_a = [&](int cc, uint4 *dstbuf) {
-#pragma unroll
-        for (int q = 0; q < kDmaPerWave; ++q) {
-            const int piece = wave * (kDmaPerWave * 64) + q * 64;
+        for (int q = 0; q < kCopyA; ++q) {
+            const int piece = (wave * kCopyA + q) * 64;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                wr, (lds_void *)&dstbuf[piece], 16,
-                (uint32_t)((cc * kHeadChunkPieces + piece + lane) * 16), 0, 0, 0);
+                wr, (lds_void *)&abuf[piece], 16,
+                (uint32_t)((c * kHeadChunkPieces + piece + lane) * 16), 0, 0, 0);
+        }
+        const int row = zrow0 + st;
+        const bool rok = (unsigned)row < (unsigned)a.H;
+        const bool cok = 32 * c + 8 * bpiece < a.C_in;
+#pragma unroll
+        for (int t = 0; t < kCopyB; ++t) {
+            const int k = wave + 4 * t;
+            const int f = f0 - 1 + (k >> 3);
+            const int dw = 64 * (k & 1) + ((k >> 1) & 3);   // column of lane 0
+            const uint32_t up = rok && (unsigned)f < (unsigned)a.D
+                                    ? (uint32_t)((((size_t)f * a.H + row) * a.W * a.C_in + 32 * c) * 2u)
+                                    : kOff;
+            const bool ok = cok && (unsigned)(bw + dw) < (unsigned)a.W;
+            const uint32_t off =
+                ok ? __builtin_elementwise_add_sat(bcolpart + (uint32_t)(dw * a.C_in * 2), up) : kOff;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)&bbuf[k * 64], 16, off, 0, 0, 0);
         }
     };
-    const int swz = head_lds_swizzle(j);   // the swizzle of rows kd*128 + mb*32 + j
-    // A fragments of tap kd, slice sl: piece 4*hh + sl of each row
-    auto read_a = [&](const uint4 *srcbuf, int kd, int sl, vec8 (&dst)[kMB]) {
+    // Fragment reads of step u (temporal tap u/2, k16 slice u%2): the per-lane part of the slot
+    // (row / column j, piece 2*slice + hh, permuted) plus a compile-time offset; B adds this
+    // wave's first window frame.
+    int lbase[2], lbaseB[2];
 #pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) {
-            const int r = kd * 128 + mb * 32 + j;
-            dst[mb] = __builtin_bit_cast(vec8, srcbuf[r * 8 + ((4 * hh + sl) ^ swz)]);
-        }
+    for (int sl = 0; sl < 2; ++sl) {
+        lbase[sl] = j * 4 + ((2 * sl + hh) ^ ((j >> 2) & 3));
+        lbaseB[sl] = lbase[sl] + wave * (kNB * 32 * 4);
+    }
+    auto read_frags = [&](const uint4 *abuf, const uint4 *bbuf, int u, vec8 (&fa)[kMB],
+                          vec8 (&fb)[kNB]) {
+        const int kd = u >> 1, sl = u & 1;
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb)
+            fa[mb] = __builtin_bit_cast(vec8, abuf[lbase[sl] + (kd * 128 + mb * 32) * 4]);
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb)
+            fb[nb] = __builtin_bit_cast(vec8, bbuf[lbaseB[sl] + (kd * kNB + nb) * 128]);
     };
 
     f32x16_t acc[kMB][kNB];
-    vec8 bq[kRing][2][kSlices];   // [half-tap slot][block of the pair][slice]
-    vec8 af[2][kMB];
+    vec8 af[2][kMB], bf[2][kNB];
     const f32x16_t zero = {};
 
-    // FUSED: the bias of the lane's six output channels; carried sums start at zero
+    // FUSED: the bias of the lane's six output channels; the carried partial sums of every
+    // output (cA: the output row before the next Z row, cB: the output row of the next Z row)
     float b6[kHalfCo];
 #pragma unroll
     for (int c = 0; c < kHalfCo; ++c) {
         const int co = kHalfCo * hh + c;
         b6[c] = (FUSED && a.bias != nullptr && co < a.C_out) ? E::to_f32(a.bias[co]) : 0.f;
     }
-    if constexpr (FUSED) {
+    float cA[kNB][kHalfCo], cB[kNB][kHalfCo];
 #pragma unroll
-        for (int nb = 0; nb < kNB; ++nb)
+    for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
-            for (int k = 0; k < 3; ++k) carry[wave][nb][k][lane] = float4{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < kHalfCo; ++c) cA[nb][c] = cB[nb][c] = 0.f;
+
+    // ---- prologue: stages 0 and 1 copied, stage 0 complete and published ----
+    copy_stage(0, As0, Bs0);
+    if (nstages > 1) {
+        copy_stage(1, As1, Bs1);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kCopyA + kCopyB));
+    } else {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
-
-    // (row, chunk, tap) of the tap `ahead` taps after tap kd of chunk c of Z row st
-    auto tap_after = [&](int st, int c, int kd, int ahead, int &ost, int &oc, int &okd) {
-        okd = kd + ahead;
-        oc = c;
-        ost = st;
-        while (okd >= 3) {
-            okd -= 3;
-            if (++oc == nch) oc = 0, ++ost;
-        }
-    };
-
-    // ---- prologue: weight chunks 0 and 1 copied (0 complete), B of half-taps 0..2 loading ----
-    copy_a(0, As0);
-    copy_a(1, As1);
-    load_half(0, 0, 0, 0, bq[0]);
-    load_half(0, 0, 0, 1, bq[1]);
-    load_half(0, 0, 1, 0, bq[2]);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDmaPerWave + (kRing - 1) * kLoadsPerHalf));
     wg_barrier();
-    read_a(As0, 0, 0, af[0]);
+    read_frags(As0, Bs0, 0, af[0], bf[0]);
 
-    // Chunk g of the band is channel chunk g % nch of Z row g / nch.  Each pass of the loop body
-    // runs one even chunk (buffer As0) and the following odd chunk (As1): twelve half-taps; the
-    // ring slot of half-tap i of the pass is i % 4.
+    // Stage g = st*nch + c uses buffer pair g % 2; each pass of the chunk loop runs an even and
+    // the following odd stage.
 #pragma unroll 1
     for (int st = 0; st < nsteps; ++st) {
 #pragma unroll 1
         for (int c2 = 0; c2 < nch; c2 += 2) {
 #pragma unroll
-          for (int i = 0; i < 2 * kHalves; ++i) {
-            const int half = i / kHalves;                 // even / odd chunk of the pass
-            const int kd = (i % kHalves) / 2, hp = i % 2;
-            uint4 *const cbuf = half == 0 ? As0 : As1;   // this chunk's weights
-            uint4 *const nbuf = half == 0 ? As1 : As0;   // the next chunk's
-            {   // half-tap i+3 into the slot half-tap i-1 has finished with
-                const int ahead_hp = (hp + kRing - 1) % 2;
-                const int ahead_taps = (hp + kRing - 1) / 2;
-                int lst, lc, lkd;
-                tap_after(st, c2 + half, kd, ahead_taps, lst, lc, lkd);
-                load_half(lst, lc, lkd, ahead_hp, bq[(i + kRing - 1) % kRing]);
+            for (int half = 0; half < 2; ++half) {
+                const int g = st * nch + c2 + half;
+                uint4 *const ca = half == 0 ? As0 : As1;
+                uint4 *const cbb = half == 0 ? Bs0 : Bs1;
+                uint4 *const na = half == 0 ? As1 : As0;
+                uint4 *const nbb = half == 0 ? Bs1 : Bs0;
+#pragma unroll
+                for (int u = 0; u < kSteps; ++u) {
+                    const int cur = u & 1;
+                    if (u + 1 < kSteps) {
+                        read_frags(ca, cbb, u + 1, af[cur ^ 1], bf[cur ^ 1]);
+                    } else {
+                        // Publish stage g+1 (its copies were issued one stage ago) and release
+                        // stage g: this wave's last fragments of stage g are in registers once
+                        // its reads are complete.  (Past the last stage the reads below are of a
+                        // stale buffer and never used; they keep every path's waits the same.)
+                        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+                        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+                        wg_barrier();
+                        if (g + 2 < nstages) copy_stage(g + 2, ca, cbb);
+                        read_frags(na, nbb, 0, af[cur ^ 1], bf[cur ^ 1]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (half == 0 && u == 0 && c2 == 0) {
+                        // first step of a Z row: the accumulators start from zero
+#pragma unroll
+                        for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+                            for (int nb = 0; nb < kNB; ++nb)
+                                acc[mb][nb] = E::mfma32x32x16(af[cur][mb], bf[cur][nb], zero);
+                    } else {
+#pragma unroll
+                        for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+                            for (int nb = 0; nb < kNB; ++nb)
+                                acc[mb][nb] = E::mfma32x32x16(af[cur][mb], bf[cur][nb], acc[mb][nb]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
-#pragma unroll
-            for (int sl = 0; sl < kSlices; ++sl) {
-                const int u = 2 * kSlices * kd + kSlices * hp + sl;   // 0 .. 23 within the chunk
-                const bool last = u == 2 * kSlices * 3 - 1;
-                const int cur = sl & 1;
-                if (last) {
-                    // Publish chunk g+1: its copy (issued one chunk ago, here) is complete once at
-                    // most kVmAfterCopy younger operations are outstanding.  This wave's reads of
-                    // chunk g are done (the last ones were issued in the previous slice), so
-                    // after the barrier chunk g's buffer takes chunk g+2.
-                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kVmAfterCopy));
-                    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-                    wg_barrier();
-                    const int wc = c2 + half + 2;    // weight chunk of chunk g+2
-                    copy_a(wc < nch ? wc : wc - nch, cbuf);
-                }
-                // the next slice's A fragments: of this half-tap, the next half-tap (same tap:
-                // the same fragments again for blocks 2-3; next tap), or the next chunk's
-                if (!last) {
-                    const int nsl = (sl + 1) % kSlices;
-                    const int nkd = sl + 1 < kSlices ? kd : (hp == 1 ? kd + 1 : kd);
-                    read_a(cbuf, nkd, nsl, af[cur ^ 1]);
-                } else {
-                    read_a(nbuf, 0, 0, af[cur ^ 1]);
-                }
-                if (i == 0 && sl == 0 && c2 == 0) {
-#pragma unroll
-                    for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-                        for (int b = 0; b < 2; ++b)
-                            acc[mb][2 * hp + b] = E::mfma32x32x16(af[cur][mb], bq[i % kRing][b][sl], zero);
-                } else if (i == 1 && sl == 0 && c2 == 0) {
-#pragma unroll
-                    for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-                        for (int b = 0; b < 2; ++b)
-                            acc[mb][2 * hp + b] = E::mfma32x32x16(af[cur][mb], bq[i % kRing][b][sl], zero);
-                } else {
-#pragma unroll
-                    for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-                        for (int b = 0; b < 2; ++b)
-                            acc[mb][2 * hp + b] = E::mfma32x32x16(af[cur][mb], bq[i % kRing][b][sl], acc[mb][2 * hp + b]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-          }
         }
 
         // ---- row zr of Z is complete in this wave's accumulators ----
         // The epilogues walk the accumulator blocks in order and read each value once, so only
-        // one or two blocks are unpacked into registers at a time.
+        // one or two blocks are unpacked into registers at a time.  The next row's first
+        // fragments (stage buffer pair 0, published and not yet reused) are read again after the
+        // epilogue, so that they need no registers during it.
         const int zr = zrow0 + st;
         const size_t frame = (size_t)n * a.D + od;
         if constexpr (!FUSED) {
@@ -464,83 +446,81 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
             }
         } else {
             // Output row zr-1 = cA + taps ky=2 of row zr; the next cA = cB + taps ky=1; the next
-            // cB = taps ky=0.  Position p takes tap (ky, kx) from position p + kx - 1: block
-            // nb + kx - 1 of the same lane, or across a lane (wavefront shift) from block 3 for
-            // kx = 0 at block 0, and from block 0 for kx = 2 at block 3.  The lanes that cross a
-            // lane half or the wave hold halo columns, which are not stored.
+            // cB = taps ky=0.  Position p takes tap (ky, kx) from position p + kx - 1, so the value
+            // of tap (ky, kx) in block sb feeds the position of block sb + 1 - kx of the same lane,
+            // or across a lane (wavefront shift): block 3 with kx = 0 feeds block 0 of the next
+            // lane, block 0 with kx = 2 block 3 of the previous lane.  The lanes that cross a lane
+            // half or the wave hold halo columns, which are not stored.  Every accumulator is read
+            // once, block by block, and added straight into the carried sums.
             const int ho = zr - 1;   // the output row this Z row completes
             const bool emit = ho >= h_begin && ho < h_end && od < a.D;
+            float n0[kNB][kHalfCo];
 #pragma unroll
-            for (int nb = 0; nb < kNB; ++nb) {
-                float sum[3][kHalfCo];   // [ky]: this row's taps ky for this block's positions
+            for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
-                for (int ky = 0; ky < 3; ++ky)
+                for (int c = 0; c < kHalfCo; ++c) n0[nb][c] = 0.f;
 #pragma unroll
-                    for (int c = 0; c < kHalfCo; ++c) sum[ky][c] = 0.f;
+            for (int mb = 0; mb < kMB; ++mb) {
+                if (16 * mb >= 9 * kHalfCo) continue;   // padding rows only
 #pragma unroll
-                for (int kx = 0; kx < 3; ++kx) {
-                    const int src = nb + kx - 1;
-                    const int sb = src < 0 ? kNB - 1 : (src >= kNB ? 0 : src);
+                for (int sb = 0; sb < kNB; ++sb) {
+                    touch(acc[mb][sb]);
 #pragma unroll
-                    for (int mb = 0; mb < kMB; ++mb) {
-                        bool used = false;   // does block (mb, sb) hold a slot with this kx?
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const int t = 16 * mb + i;
-                            if (t < 9 * kHalfCo && (t / kHalfCo) % 3 == kx) used = true;
+                    for (int i = 0; i < 16; ++i) {
+                        const int t = 16 * mb + i;
+                        if (t >= 9 * kHalfCo) continue;
+                        const int tap = t / kHalfCo, ky = tap / 3, kx = tap % 3, c = t % kHalfCo;
+                        int nb = sb + 1 - kx;
+                        float v = acc[mb][sb][i];
+                        if (nb >= kNB) {   // to the next lane (it takes lane l-1)
+                            nb = 0;
+                            v = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                0, __builtin_bit_cast(int, v), 0x138, 0xF, 0xF, false));
+                        } else if (nb < 0) {   // to the previous lane (it takes lane l+1)
+                            nb = kNB - 1;
+                            v = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                0, __builtin_bit_cast(int, v), 0x130, 0xF, 0xF, false));
                         }
-                        if (!used) continue;
-                        touch(acc[mb][sb]);
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const int t = 16 * mb + i;
-                            if (t >= 9 * kHalfCo || (t / kHalfCo) % 3 != kx) continue;
-                            const int ky = t / kHalfCo / 3, c = t % kHalfCo;
-                            float v = acc[mb][sb][i];
-                            if (src < 0)   // left neighbour: lane l-1
-                                v = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                    0, __builtin_bit_cast(int, v), 0x138, 0xF, 0xF, false));
-                            else if (src >= kNB)   // right neighbour: lane l+1
-                                v = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                    0, __builtin_bit_cast(int, v), 0x130, 0xF, 0xF, false));
-                            sum[ky][c] += v;
-                        }
-                    }
-                }
-                const float4 k0 = carry[wave][nb][0][lane], k1 = carry[wave][nb][1][lane],
-                             k2 = carry[wave][nb][2][lane];
-                const float cA[kHalfCo] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y};
-                const float cB[kHalfCo] = {k1.z, k1.w, k2.x, k2.y, k2.z, k2.w};
-                float o[kHalfCo], nA[kHalfCo];
-#pragma unroll
-                for (int c = 0; c < kHalfCo; ++c) {
-                    o[c] = cA[c] + sum[2][c];
-                    nA[c] = cB[c] + sum[1][c];
-                }
-                carry[wave][nb][0][lane] = float4{nA[0], nA[1], nA[2], nA[3]};
-                carry[wave][nb][1][lane] = float4{nA[4], nA[5], sum[0][0], sum[0][1]};
-                carry[wave][nb][2][lane] = float4{sum[0][2], sum[0][3], sum[0][4], sum[0][5]};
-                const int p = 4 * j + nb;
-                const int w = w0 + p;
-                if (emit && p >= 1 && p <= a.strip_out && w < a.W) {
-                    u16 r6[kHalfCo];
-#pragma unroll
-                    for (int c = 0; c < kHalfCo; ++c) r6[c] = E::from_f32(epilogue<EPI>(o[c] + b6[c]));
-                    u16 *dst = a.out + (frame * HW + (size_t)ho * a.W + w) * a.C_out;
-                    if constexpr (CO12) {
-                        uint3 v;
-                        v.x = (uint32_t)r6[0] | ((uint32_t)r6[1] << 16);
-                        v.y = (uint32_t)r6[2] | ((uint32_t)r6[3] << 16);
-                        v.z = (uint32_t)r6[4] | ((uint32_t)r6[5] << 16);
-                        *reinterpret_cast<uint3 *>(dst + kHalfCo * hh) = v;
-                    } else {
-#pragma unroll
-                        for (int c = 0; c < kHalfCo; ++c)
-                            if (kHalfCo * hh + c < a.C_out) dst[kHalfCo * hh + c] = r6[c];
+                        if (ky == 2) cA[nb][c] += v;
+                        else if (ky == 1) cB[nb][c] += v;
+                        else n0[nb][c] += v;
                     }
                 }
             }
+#pragma unroll
+            for (int nb = 0; nb < kNB; ++nb) {
+                float o[kHalfCo];
+#pragma unroll
+                for (int c = 0; c < kHalfCo; ++c) {
+                    o[c] = cA[nb][c];
+                    cA[nb][c] = cB[nb][c];
+                    cB[nb][c] = n0[nb][c];
+                }
+                const int p = 4 * j + nb;
+                const int w = w0 + p;
+                const bool st_ok = emit && p >= 1 && p <= a.strip_out && w < a.W;
+                u16 r6[kHalfCo];
+#pragma unroll
+                for (int c = 0; c < kHalfCo; ++c) r6[c] = E::from_f32(epilogue<EPI>(o[c] + b6[c]));
+                // 32-bit offsets into the sample (below 2 GiB), no branches: a store that must
+                // not happen goes to an offset past the buffer range, where it is dropped
+                const uint32_t yoff =
+                    (uint32_t)(((od * a.H + ho) * a.W + w) * a.C_out + kHalfCo * hh) * 2u;
+                if constexpr (CO12) {
+                    typedef uint32_t v3u __attribute__((ext_vector_type(3)));
+                    const v3u v = {(uint32_t)r6[0] | ((uint32_t)r6[1] << 16),
+                                   (uint32_t)r6[2] | ((uint32_t)r6[3] << 16),
+                                   (uint32_t)r6[4] | ((uint32_t)r6[5] << 16)};
+                    __builtin_amdgcn_raw_buffer_store_b96(v, yr, st_ok ? yoff : kOff, 0, 0);
+                } else {
+#pragma unroll
+                    for (int c = 0; c < kHalfCo; ++c)
+                        __builtin_amdgcn_raw_buffer_store_b16(
+                            r6[c], yr, st_ok && kHalfCo * hh + c < a.C_out ? yoff + 2u * c : kOff, 0, 0);
+                }
+            }
         }
+        read_frags(As0, Bs0, 0, af[0], bf[0]);
     }
     // no LDS copy may still be in flight when the workgroup's LDS is released
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -591,8 +571,8 @@ hipError_t launch_head_gemm(const HeadGemmParams &p, hipStream_t stream) {
     a.bias = static_cast<const u16 *>(p.bias);
     a.out = static_cast<u16 *>(p.out);
     a.N = p.N, a.C_in = p.C_in, a.C_out = p.C_out, a.D = p.D, a.H = p.H, a.W = p.W;
-    const int packed_chunks = (p.C_in + 63) / 64;
-    a.nchunks = (packed_chunks + 1) & ~1;   // the kernel runs chunks in pairs
+    const int packed_chunks = (p.C_in + 31) / 32;
+    a.nchunks = (packed_chunks + 1) & ~1;   // the kernel runs stages in pairs
     a.strip_out = p.fused ? kWavePos - 2 : kWavePos;
     a.strips = (p.W + a.strip_out - 1) / a.strip_out;
     a.fgroups = (p.D + 3) / 4;

@@ -558,8 +558,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *part, c
 // Direct (27 taps): wp[((cc*27 + tap)*Mpad + m)*32 + k] <- w[co = m, ci = 32*cc + k, tap].
 // Direct for the 32x32 kernel: wp[(((cc*27 + tap)*2 + k2)*Mpad + m)*16 + k] <- w[m, 32*cc + 16*k2
 // + k, tap]: one 32-row fragment of one k16 slice is 1 KiB contiguous.
-// Temporal (head kernels): 64-channel chunk c holds 3072 16-byte pieces in LDS order -- slot
-// s = r*8 + q' of row r = kd*128 + m holds channels 64*c + 8*q .. +7, q = q' ^ head_lds_swizzle(r),
+// Temporal (head kernels): 32-channel chunk c holds 1536 16-byte pieces in LDS order -- slot
+// s = r*4 + q' of row r = kd*128 + m holds channels 32*c + 8*q .. +7, q = q' ^ head_lds_swizzle(r),
 // of the weight for temporal tap kd and the (spatial tap, output channel) head_row_role(m) names.
 // Rows past the real ones and channels past C_in are zero.
 __global__ __launch_bounds__(256) void pack3d_kernel(const u16 *w, u16 *wp, int C_in, int C_out,
@@ -592,10 +592,10 @@ __global__ __launch_bounds__(256) void pack3d_kernel(const u16 *w, u16 *wp, int 
         const int cc = (int)(idx / (kHeadChunkPieces * 8));
         const int rem = (int)(idx - (long long)cc * (kHeadChunkPieces * 8));
         const int slot = rem >> 3, e = rem & 7;
-        const int r = slot >> 3;
-        const int q = (slot & 7) ^ head_lds_swizzle(r);
+        const int r = slot >> 2;
+        const int q = (slot & 3) ^ head_lds_swizzle(r);
         const int kd = r >> 7, m = r & 127;
-        const int ci = cc * 64 + 8 * q + e;
+        const int ci = cc * 32 + 8 * q + e;
         int tap, co;
         head_row_role(m, tap, co);
         if (ci < C_in && tap >= 0 && co < C_out)
@@ -680,8 +680,8 @@ IgemmPlan plan_igemm(int family, int N, int C_in, int C_out, int D, int H, int W
     }
     pl.Mpad = (pl.Mrows + pl.BM - 1) / pl.BM * pl.BM;
     pl.mtiles = pl.Mpad / pl.BM;
-    // 32-channel chunks; the head kernels pack whole 64-channel chunks (an even count)
-    pl.nchunks = family == IG_TEMPORAL ? (C_in + 63) / 64 * 2 : (C_in + 31) / 32;
+    // 32-channel chunks
+    pl.nchunks = (C_in + 31) / 32;
     if (family == IG_TEMPORAL) {
         // 256 consecutive positions of one frame per workgroup (no spatial structure needed)
         pl.tiles_h = 1;

@@ -76,12 +76,12 @@ hipError_t launch_head_stencil(const StencilParams &p, hipStream_t stream);
 
 constexpr int kHeadPlaneChannels = 112;  // 9 taps x 12 channels = 108, padded to 7 x 16
 
-// Packed weights of the head's temporal GEMM, per 64-channel chunk: 3 temporal taps x 128 GEMM
-// rows x 64 channels = 3072 pieces of 16 bytes (8 channels), stored in the order the kernel's LDS
-// holds them: piece slot s = r*8 + q' of row r = kd*128 + m holds channels 8*q .. 8*q+7 of the
+// Packed weights of the head's temporal GEMM, per 32-channel chunk: 3 temporal taps x 128 GEMM
+// rows x 32 channels = 1536 pieces of 16 bytes (8 channels), stored in the order the kernel's LDS
+// holds them: piece slot s = r*4 + q' of row r = kd*128 + m holds channels 8*q .. 8*q+7 of the
 // chunk with q = q' ^ head_lds_swizzle(r).
-constexpr int kHeadChunkPieces = 3 * 128 * 8;
-__host__ __device__ inline int head_lds_swizzle(int r) { return (r >> 1) & 7; }
+constexpr int kHeadChunkPieces = 3 * 128 * 4;
+__host__ __device__ inline int head_lds_swizzle(int r) { return (r >> 2) & 3; }
 // Role of GEMM row m (0..127): the matrix-core accumulator layout puts row m into register
 // i = 4*((m%32)/8) + m%4 of 32-row block m/32 in lane half h = (m%8)/4; slot t = 16*(m/32) + i of
 // half h carries spatial tap t/6 (ky*3 + kx) of output channel 6*h + t%6.  Rows with t >= 54 are
