@@ -404,9 +404,7 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
 
         // ---- row zr of Z is complete in this wave's accumulators ----
         // The epilogues walk the accumulator blocks in order and read each value once, so only
-        // one or two blocks are unpacked into registers at a time.  The next row's first
-        // fragments (stage buffer pair 0, published and not yet reused) are read again after the
-        // epilogue, so that they need no registers during it.
+        // one or two blocks are unpacked into registers at a time.
         const int zr = zrow0 + st;
         const size_t frame = (size_t)n * a.D + od;
         if constexpr (!FUSED) {
@@ -520,7 +518,6 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
                 }
             }
         }
-        read_frags(As0, Bs0, 0, af[0], bf[0]);
     }
     // no LDS copy may still be in flight when the workgroup's LDS is released
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
