@@ -48,9 +48,14 @@ enum { CONV_DTYPE_F16 = 0, CONV_DTYPE_BF16 = 1 };
 enum { CONV_LAYOUT_CHANNELS_FIRST = 0, CONV_LAYOUT_CHANNELS_LAST = 1 };
 /* fused epilogues (applied after the bias) */
 enum { CONV_EPI_NONE = 0, CONV_EPI_RELU = 1, CONV_EPI_CLAMP1 = 2 };
-/* algorithms.  AUTO resolves deterministically from the shape (conv3x3x3_select_algo).
+/* algorithms.  AUTO resolves deterministically from the shape (conv3x3_select_algo,
+ * conv3x3x3_select_algo).
  *   SIMT        2D: direct LDS-halo kernel on the vector ALUs (fp32 accumulation via dot2).
- *   MFMA        3D: implicit GEMM on the matrix cores, 27 taps in one fp32 accumulator.
+ *   MFMA        2D: the same sum on the matrix cores (9 taps x C_in in one fp32 accumulator)
+ *               for C_in a multiple of 8 up to 64, C_out up to 64, W a multiple of 8 [the
+ *               contraction the taesd_conv.cuh.new header comment defines; the matrix-core route
+ *               its rationale argues against, measured here].  AUTO picks it when it applies.
+ *               3D: implicit GEMM on the matrix cores, 27 taps in one fp32 accumulator.
  *   SPLIT_HEAD  3D, C_out <= 12, stride 1: 3x1x1 temporal conv into 9*C_out tap channels of a
  *               112-channel bf16/fp16 plane in the workspace, then a nine-tap stencil + bias +
  *               epilogue [head.cu, header comment and head_stencil_kernel].
@@ -91,7 +96,9 @@ int conv_out_size(int in, int stride);
 /* ------------------------------------------------------------------------------------------
  * 2D: x (N,C_in,H,W) NCHW, w (C_out,C_in,3,3) OIHW as stored by PyTorch (no packing), bias
  * (C_out) or NULL, y (N,C_out,H_out,W_out) NCHW; all of `dtype`.  stride 1 or 2.
- * Supported: layout CHANNELS_FIRST, dtype F16 or BF16, algo AUTO or SIMT, any C_in/C_out >= 1.
+ * Supported: layout CHANNELS_FIRST, dtype F16 or BF16; algo SIMT: any C_in/C_out >= 1; algo
+ * MFMA: C_in % 8 == 0, C_in <= 64, C_out <= 64, W % 8 == 0, one image of x and of y below 2 GiB
+ * (else CONV_E_UNSUPPORTED); AUTO: MFMA when it applies, else SIMT.
  * [taesd_conv.cuh.new: operator contract in the header comment; the kernels' argument lists]
  * ---------------------------------------------------------------------------------------- */
 int conv3x3_fwd(const void *x, const void *w, const void *bias, void *y, int N, int C_in,
@@ -102,6 +109,11 @@ int conv3x3_fwd(const void *x, const void *w, const void *bias, void *y, int N, 
  * would return. */
 int conv3x3_is_supported(int N, int C_in, int C_out, int H, int W, int stride, int layout,
                          int dtype, int epilogue, int algo);
+
+/* The concrete 2D algorithm (CONV_ALGO_SIMT or CONV_ALGO_MFMA) conv3x3_fwd runs for this
+ * request, or a negative status if it would reject it. */
+int conv3x3_select_algo(int N, int C_in, int C_out, int H, int W, int stride, int layout,
+                        int dtype, int algo);
 
 /* ------------------------------------------------------------------------------------------
  * 3D: x (N,D,H,W,C_in) NDHWC, w_packed from conv3x3x3_pack_weights, bias (C_out) or NULL,

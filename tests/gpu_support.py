@@ -40,9 +40,9 @@ def check_guards(buf, n, guard=256, fill_bits=0x7FFF):
     assert np.all(g[guard + n:] == fill_bits), "write past the output buffer"
 
 
-def run_2d(x, w, b, stride, epilogue, guarded=False):
+def run_2d(x, w, b, stride, epilogue, guarded=False, algo=C.ALGO_SIMT):
     N, Ci, H, W = x.shape
-    op = Conv3x3(w, b, N, H, W, stride=stride, epilogue=epilogue, algo=C.ALGO_SIMT)
+    op = Conv3x3(w, b, N, H, W, stride=stride, epilogue=epilogue, algo=algo)
     if guarded:
         buf, y = alloc_guarded(op.out_shape(), x.dtype)
         op(x, y)

@@ -94,7 +94,10 @@ def test_2d_invalid_arguments():
     assert f2d(y=A + 64) == C.E_INVAL           # overlaps x
     assert "overlap" in cx.conv_last_error()
     assert f2d(layout=1) == C.E_UNSUPPORTED     # NHWC
-    assert f2d(algo=C.ALGO_MFMA) == C.E_UNSUPPORTED
+    assert f2d(algo=C.ALGO_MFMA, C_in=12) == C.E_UNSUPPORTED     # C_in not a multiple of 8
+    assert f2d(algo=C.ALGO_MFMA, C_in=72) == C.E_UNSUPPORTED     # C_in above 64
+    assert f2d(algo=C.ALGO_MFMA, C_out=65) == C.E_UNSUPPORTED
+    assert f2d(algo=C.ALGO_MFMA, W=12) == C.E_UNSUPPORTED        # W not a multiple of 8
     assert f2d(algo=C.ALGO_SPLIT_HEAD) == C.E_UNSUPPORTED
 
 
@@ -134,6 +137,19 @@ def test_3d_invalid_and_unsupported():
 def test_3d_empty_is_noop():
     for kw in (dict(N=0), dict(C_out=0), dict(D=0), dict(H=0), dict(W=0)):
         assert f3d(x=None, y=None, w=None, **kw) == C.OK
+
+
+def test_2d_algo_selection():
+    assert cx.conv3x3_select_algo(8, 64, 64, 256, 256, 1, 0, 0, C.ALGO_AUTO) == C.ALGO_MFMA
+    assert cx.conv3x3_select_algo(8, 64, 64, 256, 256, 2, 0, 0, C.ALGO_AUTO) == C.ALGO_MFMA
+    assert cx.conv3x3_select_algo(1, 16, 16, 64, 64, 1, 0, 0, C.ALGO_AUTO) == C.ALGO_MFMA
+    assert cx.conv3x3_select_algo(2, 5, 7, 13, 37, 1, 0, 0, C.ALGO_AUTO) == C.ALGO_SIMT
+    assert cx.conv3x3_select_algo(1, 64, 128, 32, 32, 1, 0, 0, C.ALGO_AUTO) == C.ALGO_SIMT
+    assert cx.conv3x3_select_algo(8, 64, 64, 256, 256, 1, 0, 0, C.ALGO_SIMT) == C.ALGO_SIMT
+    assert cx.conv3x3_is_supported(8, 64, 64, 256, 256, 1, 0, 0, 1, C.ALGO_MFMA) == C.OK
+    assert cx.conv3x3_is_supported(1, 8, 8, 8, 20, 1, 0, 0, 1, C.ALGO_MFMA) == C.E_UNSUPPORTED
+    with pytest.raises(C.ConvError):
+        cx.conv3x3_select_algo(1, 8, 8, 8, 20, 1, 0, 0, C.ALGO_MFMA)
 
 
 def test_is_supported_matches_fwd_checks():

@@ -55,6 +55,33 @@ def test_simt2d_integer_exact(case):
     assert_bit_exact(y, oracle_2d(x, w, b, s, epi), x.dtype)
 
 
+CASES_2D_MFMA_INT = [
+    # N, Ci, Co, H, W, stride, dtype, epilogue  (C_in % 8 == 0, C_in, C_out <= 64, W % 8 == 0)
+    (1, 16, 16, 64, 64, 1, "f16", "relu"),
+    (2, 8, 7, 13, 40, 1, "f16", "none"),        # ragged rows, a partial column tile
+    (2, 8, 7, 13, 40, 2, "f16", "clamp1"),
+    (1, 64, 64, 19, 48, 1, "bf16", "relu"),
+    (1, 40, 40, 20, 72, 2, "f16", "relu"),
+    (3, 24, 64, 9, 16, 1, "bf16", "none"),
+    (1, 64, 33, 33, 8, 2, "f16", "none"),       # W = 8: one column group
+    (1, 8, 1, 1, 8, 1, "f16", "relu"),
+    (2, 64, 64, 32, 64, 2, "f16", "relu"),
+    (1, 64, 64, 70, 264, 1, "f16", "relu"),
+    (5, 16, 16, 128, 256, 1, "f16", "relu"),    # 320 tiles: workgroups run two
+    (9, 16, 24, 64, 256, 2, "bf16", "clamp1"),  # 288 tiles at stride 2
+]
+
+
+@pytest.mark.parametrize("case", CASES_2D_MFMA_INT, ids=[str(c) for c in CASES_2D_MFMA_INT])
+def test_mfma2d_integer_exact(case):
+    N, Ci, Co, H, W, s, dt, epi = case
+    _say("mfma2d int %s" % (case,))
+    x, w, b = si.integer_case("2d", N, Ci, Co, H, W, dtype=dt,
+                              seed=100 + CASES_2D_MFMA_INT.index(case), device=DEV)
+    y = run_2d(x, w, b, s, epi, guarded=True, algo=C.ALGO_MFMA)
+    assert_bit_exact(y, oracle_2d(x, w, b, s, epi), x.dtype)
+
+
 CASES_3D_INT = [
     # N, Ci, Co, D, H, W, dtype, epilogue, algo
     (1, 32, 12, 3, 9, 35, "bf16", "clamp1", C.ALGO_MFMA),
@@ -96,18 +123,23 @@ def test_conv3d_no_bias_integer_exact():
                               with_bias=False)
     y = run_2d(x, w, None, 1, "relu")
     assert_bit_exact(y, oracle_2d(x, w, None, 1, "relu"), x.dtype)
+    x, w, _ = si.integer_case("2d", 2, 16, 9, 11, 16, dtype="f16", seed=4, device=DEV,
+                              with_bias=False)
+    y = run_2d(x, w, None, 1, "relu", algo=C.ALGO_MFMA)
+    assert_bit_exact(y, oracle_2d(x, w, None, 1, "relu"), x.dtype)
 
 
 # ------------------------------------------------------------------------------------------
 # random inputs at small sizes, whole tensors within tolerance
 # ------------------------------------------------------------------------------------------
-def test_simt2d_random_tolerance():
+@pytest.mark.parametrize("algo", [C.ALGO_SIMT, C.ALGO_MFMA])
+def test_2d_random_tolerance(algo):
     for s in (1, 2):
         x, w, b = si.random_case("2d", 2, 64, 64, 40, 72, dtype="f16", seed=s, device=DEV)
         x = torch.relu(x)
-        y = run_2d(x, w, b, s, "relu")
+        y = run_2d(x, w, b, s, "relu", algo=algo)
         m = metrics(bits(y), oracle_2d(x, w, b, s, "relu"), x.dtype)
-        _say("simt2d random s=%d %s" % (s, m))
+        _say("2d random algo=%d s=%d %s" % (algo, s, m))
         assert_within(m, activated=True)
 
 
@@ -132,27 +164,29 @@ def test_mfma_random_tolerance(Ci, Co, D, H, W):
 # ------------------------------------------------------------------------------------------
 # the workloads at full size
 # ------------------------------------------------------------------------------------------
-def test_c1_full_tensor():
+@pytest.mark.parametrize("algo", [C.ALGO_SIMT, C.ALGO_MFMA])
+def test_c1_full_tensor(algo):
     wl = si.WORKLOADS["c1"]
     x, w, b = si.make_inputs(wl, device=DEV)
-    y = run_2d(x, w, b, wl.stride, wl.epilogue, guarded=True)
+    y = run_2d(x, w, b, wl.stride, wl.epilogue, guarded=True, algo=algo)
     m = metrics(bits(y), oracle_2d(x, w, b, wl.stride, wl.epilogue), x.dtype)
-    _say("c1 %s" % m)
+    _say("c1 algo=%d %s" % (algo, m))
     assert_within(m, activated=True)
 
 
-@pytest.mark.parametrize("name", ["c2", "c2s2"])
-def test_c2_full_size_sampled(name):
+@pytest.mark.parametrize("name,algo", [(n, a) for n in ("c2", "c2s2")
+                                       for a in (C.ALGO_SIMT, C.ALGO_MFMA)])
+def test_c2_full_size_sampled(name, algo):
     wl = si.WORKLOADS[name]
     x, w, b = si.make_inputs(wl, device=DEV)
-    y = run_2d(x, w, b, wl.stride, wl.epilogue, guarded=True)
-    y2 = run_2d(x, w, b, wl.stride, wl.epilogue)
+    y = run_2d(x, w, b, wl.stride, wl.epilogue, guarded=True, algo=algo)
+    y2 = run_2d(x, w, b, wl.stride, wl.epilogue, algo=algo)
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "not deterministic"
     pts = sample_points_2d(wl.N, wl.H_out, wl.W_out, 400, seed=1)
     ref = oracle.conv2d_points(bits(x), bits(w), bits(b), pts, wl.stride, oracle.F16,
                                oracle.EPI_RELU, oracle.CHANNELS_FIRST)
     m = metrics(gather_2d(y, pts), ref, x.dtype)
-    _say("%s sampled %d %s" % (name, len(pts), m))
+    _say("%s algo=%d sampled %d %s" % (name, algo, len(pts), m))
     assert_within(m, activated=True)
 
 

@@ -32,6 +32,7 @@ EXPORTS = [
     ("conv_out_size", _I, [_I, _I]),
     ("conv3x3_fwd", _I, [_P, _P, _P, _P] + [_I] * 10 + [_P]),
     ("conv3x3_is_supported", _I, [_I] * 10),
+    ("conv3x3_select_algo", _I, [_I] * 9),
     ("conv3x3x3_fwd", _I, [_P, _P, _P, _P] + [_I] * 11 + [_P, _SZ, _P]),
     ("conv3x3x3_select_algo", _I, [_I] * 10),
     ("conv3x3x3_is_supported", _I, [_I] * 11),
@@ -132,6 +133,14 @@ def conv3x3_is_supported(N, C_in, C_out, H, W, stride=1, layout=LAYOUT_CHANNELS_
                          dtype=DTYPE_F16, epilogue=EPI_NONE, algo=ALGO_AUTO) -> int:
     return library().conv3x3_is_supported(N, C_in, C_out, H, W, stride, layout, dtype, epilogue,
                                           algo)
+
+
+def conv3x3_select_algo(N, C_in, C_out, H, W, stride=1, layout=LAYOUT_CHANNELS_FIRST,
+                        dtype=DTYPE_F16, algo=ALGO_AUTO) -> int:
+    r = library().conv3x3_select_algo(N, C_in, C_out, H, W, stride, layout, dtype, algo)
+    if r < 0:
+        _check(r)
+    return r
 
 
 def conv3x3x3_select_algo(N, C_in, C_out, D, H, W, stride=1, layout=LAYOUT_CHANNELS_LAST,

@@ -62,19 +62,38 @@ int check_2d(int N, int C_in, int C_out, int H, int W, int stride, int layout, i
     if (N < 0 || C_out < 0 || H < 0 || W < 0)
         return fail(CONV_E_INVAL, "negative size (N=%d C_out=%d H=%d W=%d)", N, C_out, H, W);
     if (C_in < 1) return fail(CONV_E_INVAL, "C_in must be >= 1 (got %d)", C_in);
-    if (algo != CONV_ALGO_AUTO && algo != CONV_ALGO_SIMT) {
+    if (algo != CONV_ALGO_AUTO && algo != CONV_ALGO_SIMT && algo != CONV_ALGO_MFMA) {
         if (algo < CONV_ALGO_AUTO || algo > CONV_ALGO_FUSED_HEAD)
             return fail(CONV_E_INVAL, "unknown algo %d", algo);
-        return fail(CONV_E_UNSUPPORTED, "2D convolution supports algo AUTO or SIMT (got %d)", algo);
+        return fail(CONV_E_UNSUPPORTED, "2D convolution supports algo AUTO, SIMT or MFMA (got %d)", algo);
     }
     if (layout != CONV_LAYOUT_CHANNELS_FIRST)
         return fail(CONV_E_UNSUPPORTED, "2D convolution supports the NCHW layout only");
+    if (algo == CONV_ALGO_MFMA) {
+        if (!cx::mfma2d_supported(C_in, C_out, H, W, stride))
+            return fail(CONV_E_UNSUPPORTED,
+                        "2D MFMA needs C_in a multiple of 8 up to 64, C_out up to 64 and W a "
+                        "multiple of 8 (got C_in=%d C_out=%d W=%d)", C_in, C_out, W);
+        if ((long long)C_in * H * W * 2 >= (1ll << 31) ||
+            (long long)C_out * ((H - 1) / stride + 1) * ((W - 1) / stride + 1) * 2 >= (1ll << 31))
+            return fail(CONV_E_UNSUPPORTED, "2D MFMA needs one image of x and of y below 2 GiB");
+    }
     const long long ho = (H - 1) / stride + 1, wo = (W - 1) / stride + 1;
     if ((long long)N * ((H + 31) / 32 + 1) * ((W + 31) / 32 + 1) * ((C_out + 15) / 16 + 1) >= (1ll << 31))
         return fail(CONV_E_UNSUPPORTED, "problem too large for one launch");
     (void)ho;
     (void)wo;
     return CONV_OK;
+}
+
+// The concrete 2D algorithm of a request that passed check_2d: MFMA when asked for, or for AUTO
+// when the matrix-core kernel applies and its sample fits the 32-bit buffer ranges; else SIMT.
+int select_2d(int C_in, int C_out, int H, int W, int stride, int algo) {
+    if (algo == CONV_ALGO_MFMA) return CONV_ALGO_MFMA;
+    if (algo == CONV_ALGO_SIMT) return CONV_ALGO_SIMT;
+    const bool fits = (long long)C_in * H * W * 2 < (1ll << 31) &&
+                      (long long)C_out * ((H - 1) / stride + 1) * ((W - 1) / stride + 1) * 2 < (1ll << 31);
+    return cx::mfma2d_supported(C_in, C_out, H, W, stride) && fits ? CONV_ALGO_MFMA : CONV_ALGO_SIMT;
 }
 
 // ---- 3D ------------------------------------------------------------------------------------
@@ -169,6 +188,14 @@ int conv3x3_is_supported(int N, int C_in, int C_out, int H, int W, int stride, i
     return st ? st : ok();
 }
 
+int conv3x3_select_algo(int N, int C_in, int C_out, int H, int W, int stride, int layout,
+                        int dtype, int algo) {
+    const int st = check_2d(N, C_in, C_out, H, W, stride, layout, dtype, CONV_EPI_NONE, algo);
+    if (st) return st;
+    ok();
+    return select_2d(C_in, C_out, H, W, stride, algo);
+}
+
 int conv3x3_fwd(const void *x, const void *w, const void *bias, void *y, int N, int C_in,
                 int C_out, int H, int W, int stride, int layout, int dtype, int epilogue,
                 int algo, void *stream) {
@@ -193,6 +220,11 @@ int conv3x3_fwd(const void *x, const void *w, const void *bias, void *y, int N, 
     p.x = x, p.w = w, p.bias = bias, p.y = y;
     p.N = N, p.C_in = C_in, p.C_out = C_out, p.H = H, p.W = W, p.Hout = Ho, p.Wout = Wo;
     p.stride = stride, p.bf16 = dtype == CONV_DTYPE_BF16, p.epilogue = epilogue;
+    if (select_2d(C_in, C_out, H, W, stride, algo) == CONV_ALGO_MFMA) {
+        const hipError_t e = cx::launch_mfma2d(p, (hipStream_t)stream);
+        if (e != hipSuccess) return fail(CONV_E_LAUNCH, "MFMA 2D launch failed: %s", hipGetErrorString(e));
+        return ok();
+    }
     const hipError_t e = cx::launch_simt2d(p, (hipStream_t)stream);
     if (e != hipSuccess) return fail(CONV_E_LAUNCH, "SIMT 2D launch failed: %s", hipGetErrorString(e));
     return ok();

@@ -18,6 +18,10 @@ struct Simt2dParams {
 };
 hipError_t launch_simt2d(const Simt2dParams &p, hipStream_t stream);
 
+// ---- 2D on the matrix cores (NCHW, C_in and C_out <= 64, C_in % 8 == 0, W % 8 == 0) ------
+bool mfma2d_supported(int C_in, int C_out, int H, int W, int stride);
+hipError_t launch_mfma2d(const Simt2dParams &p, hipStream_t stream);
+
 // ---- 3D MFMA implicit GEMM (NDHWC) ---------------------------------------------------------
 // Tile families; the host picks one per request.
 enum IgemmFamily {

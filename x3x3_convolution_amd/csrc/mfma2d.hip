@@ -1,0 +1,378 @@
+// 2D pad-1 3x3 convolution of narrow layers (C_in, C_out <= 64) on the matrix cores, NCHW.
+//
+//   y[n,co,oh,ow] = E( b[co] + sum_{ci,ky,kx} w[co,ci,ky,kx] * X[n,ci, s*oh-1+ky, s*ow-1+kx] )
+//
+// [taesd_conv.cuh.new, header comment: the operator contract (NCHW, fp16 storage, fp32
+// accumulation, pad 1, stride 1 or 2, optional bias and ReLU).]  The pages argue for a SIMT
+// kernel at C <= 64 because matrix tiles would be under-filled on their hardware; on gfx950 a
+// C = 64 layer at 256 x 256 has ~290 FLOP per compulsory byte, at the HBM / matrix-core ridge,
+// so here the contraction runs on v_mfma_f32_32x32x16 (fp32 accumulation) and the kernel is a
+// stream: input window in, output tile out.
+//
+// GEMM view per tile: rows = output channels (64, zero-padded), columns = output positions,
+// K = 9 taps x 64 input channels (zero-padded), ordered (tap, channel).  Lane l supplies row (A)
+// / column (B) l%32 with the 8 k values of half l/32 of a 16-wide k slice and receives
+// accumulator element i at row 8*(i/4) + 4*(l/32) + i%4, column l%32.
+//
+// Persistent workgroups (one per CU: the LDS holds the whole weight set) walk the tiles; in
+// each round the 256 workgroups take 256 consecutive tiles, each XCD a contiguous run of them
+// (horizontally adjacent tiles share halo columns in that XCD's L2).
+//   * Weights: read once per workgroup from OIHW and stored in LDS as 16-byte pieces of 8 input
+//     channels, piece (tap, q, row) at ((tap*4 + q%4)*64 + row) of the array of channel half
+//     q/4: a 32-row A fragment is 32 consecutive pieces.
+//   * Input: a tile is 32 output columns x TH output rows (16 at stride 1, 4 at stride 2) and
+//     runs as two 32-channel stages.  A stage's input window is loaded with 16-byte loads along
+//     W (8 columns of one channel), transposed in registers (8 x 8 halves) and written to LDS
+//     position-major: a position's 32 channels are four 16-byte pieces, stored XOR-permuted by
+//     (column/4) % 4, so a fragment read of 32 consecutive columns hits distinct bank groups.
+//     At stride 2 a window row holds its odd input columns first and its even ones after them
+//     (the taps kx = 0, 2 read the odd ones, kx = 1 the even ones), so those reads are unit
+//     stride too.  Two window buffers: the next stage's window is loaded while this one's
+//     MFMAs run, one barrier per stage.
+//   * Waves: each of the four owns all 64 rows and TH/4 output rows of the tile (4 blocks of 32
+//     positions at stride 1, one at stride 2).
+// Input columns are handled in aligned groups of 8, so W must be a multiple of 8 (checked by
+// the host); rows, columns and channels outside the tensor load as zero (the zero padding).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace cx {
+
+namespace {
+
+constexpr int kTW = 32;                  // output columns per tile
+constexpr int kRows = 64;                // GEMM rows (output channels, zero-padded)
+constexpr int kWPieces = 9 * 4 * kRows;  // weight pieces per 32-channel half (36 KiB)
+constexpr int kWinSlots = 2592;          // 16-byte slots per window buffer (40.5 KiB)
+constexpr uint32_t kOff = 0xFFFFFFFFu;   // past any buffer range; saturating adds keep it
+
+template <int S>
+struct M2Geom;
+template <>
+struct M2Geom<1> {
+    static constexpr int TH = 16;        // output rows per tile
+    static constexpr int NBW = 4;        // 32-position blocks per wave (output rows)
+    static constexpr int WRows = 18;     // window rows
+    static constexpr int RowPos = 36;    // window row stride in positions (34 used)
+    static constexpr int Groups = 6;     // 8-column load groups per window row
+    static constexpr int CommitAfter = 8;   // slice after which the next window is written
+};
+template <>
+struct M2Geom<2> {
+    static constexpr int TH = 4;
+    static constexpr int NBW = 1;
+    static constexpr int WRows = 9;
+    static constexpr int RowPos = 72;    // odd input columns at 0..32, even ones at 36..67
+    static constexpr int Groups = 9;
+    static constexpr int CommitAfter = 17;
+};
+static_assert(M2Geom<1>::WRows * M2Geom<1>::RowPos * 4 == kWinSlots, "window size");
+static_assert(M2Geom<2>::WRows * M2Geom<2>::RowPos * 4 == kWinSlots, "window size");
+static_assert(M2Geom<1>::WRows * M2Geom<1>::Groups * 4 <= 512, "two load units per thread");
+static_assert(M2Geom<2>::WRows * M2Geom<2>::Groups * 4 <= 512, "two load units per thread");
+
+struct Mfma2dKArgs {
+    const u16 *x, *w, *bias;
+    u16 *y;
+    int N, C_in, C_out, H, W, Hout, Wout;
+    int tiles_h, tiles_w, ntiles;
+    uint32_t x_img_bytes, y_img_bytes, w_bytes;
+};
+
+__device__ __forceinline__ int m2_slot(int r, int c, int piece, int row_pos) {
+    return (r * row_pos + c) * 4 + (piece ^ ((c >> 2) & 3));
+}
+__device__ __forceinline__ void m2_barrier() { asm volatile("s_barrier" ::: "memory"); }
+__device__ __forceinline__ void m2_touch(f32x16_t &v) { asm volatile("" : "+a"(v)::"memory"); }
+// dword i (a compile-time index) of a 16-byte vector
+__device__ __forceinline__ uint32_t m2_dword(const uint4 &v, int i) {
+    return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+// waits for this thread's LDS writes only (the window stores); loads are consumed by then and
+// global stores may still drain
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
+// halves h0 of a and h1 of b packed as (lo, hi)
+__device__ __forceinline__ uint32_t m2_pack(uint32_t a, int h0, uint32_t b, int h1) {
+    return ((a >> (16 * h0)) & 0xFFFFu) | (((b >> (16 * h1)) & 0xFFFFu) << 16);
+}
+
+template <bool BF, int S, int EPI>
+__global__ __launch_bounds__(256, 1) void mfma2d_kernel(Mfma2dKArgs a) {
+    using E = Elem<BF>;
+    using G = M2Geom<S>;
+    typedef typename E::vec8 vec8;
+    __shared__ __attribute__((aligned(16))) uint4 Wc0[kWPieces];    // input channels 0..31
+    __shared__ __attribute__((aligned(16))) uint4 Wc1[kWPieces];    // input channels 32..63
+    __shared__ __attribute__((aligned(16))) uint4 Win0[kWinSlots];  // stage of channels 0..31
+    __shared__ __attribute__((aligned(16))) uint4 Win1[kWinSlots];  // stage of channels 32..63
+    __shared__ float bias_s[kRows];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 31, hh = lane >> 5;
+    const int HW = a.H * a.W;
+
+    // ---- weights -> LDS, once per workgroup ----
+    // Unit (row m, piece q of 8 input channels) reads the 8 x 9 contiguous halves
+    // w[m][8q .. 8q+7][0..8] (144 bytes, 16-byte aligned since C_in % 8 == 0) and writes the
+    // nine taps' pieces.
+    {
+        const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)a.w, (short)0, (int)a.w_bytes, 0x00020000);
+        for (int u = tid; u < kRows * 8; u += 256) {
+            const int m = u & (kRows - 1), q = u >> 6;
+            const bool ok = m < a.C_out && 8 * q < a.C_in;
+            const uint32_t base = ok ? (uint32_t)((m * a.C_in + 8 * q) * 18) : kOff;
+            uint32_t h[36];
+#pragma unroll
+            for (int i = 0; i < 9; ++i) {
+                const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                    wr, __builtin_elementwise_add_sat(base, 16u * i), 0, 0));
+                h[4 * i] = v.x, h[4 * i + 1] = v.y, h[4 * i + 2] = v.z, h[4 * i + 3] = v.w;
+            }
+            uint4 *dst = q < 4 ? Wc0 : Wc1;
+#pragma unroll
+            for (int t = 0; t < 9; ++t) {
+                uint32_t d[4];
+#pragma unroll
+                for (int dd = 0; dd < 4; ++dd) {
+                    const int e0 = (2 * dd) * 9 + t, e1 = (2 * dd + 1) * 9 + t;   // half indices
+                    d[dd] = m2_pack(h[e0 >> 1], e0 & 1, h[e1 >> 1], e1 & 1);
+                }
+                dst[(t * 4 + (q & 3)) * kRows + m] = uint4{d[0], d[1], d[2], d[3]};
+            }
+        }
+        if (tid < kRows)
+            bias_s[tid] = (a.bias != nullptr && tid < a.C_out) ? E::to_f32(a.bias[tid]) : 0.f;
+    }
+
+    // ---- tiles of this workgroup ----
+    const int nwg = gridDim.x;
+    const int rank = (int)xcd_remap(blockIdx.x, (uint32_t)nwg);
+    const int my_tiles = rank < a.ntiles ? (a.ntiles - 1 - rank) / nwg + 1 : 0;
+    auto tile_coords = [&](int it, int &n, int &oh0, int &ow0) {
+        int t = it * nwg + rank;
+        const int tw = t % a.tiles_w;
+        t /= a.tiles_w;
+        const int th = t % a.tiles_h;
+        n = t / a.tiles_h;
+        oh0 = th * G::TH, ow0 = tw * kTW;
+    };
+
+    // ---- input window staging: unit u = (window row, 8-column group, channel octet) ----
+    constexpr int kUnits = G::WRows * G::Groups * 4;
+    uint4 sv[2][8];
+    // loads of the two units of this thread for stage (tile it, channel half c)
+    auto issue = [&](int it, int c) {
+        int n, oh0, ow0;
+        tile_coords(it, n, oh0, ow0);
+        const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(a.x + (size_t)n * a.C_in * HW), (short)0, (int)a.x_img_bytes, 0x00020000);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int u = tid + 256 * k;
+            const int o = u & 3, rg = u >> 2;
+            const int g = rg % G::Groups, r = rg / G::Groups;
+            const int ih = S * oh0 - 1 + r;
+            const int iw0 = S * ow0 - 8 + 8 * g;
+            const int ch0 = 32 * c + 8 * o;
+            const bool ok = u < kUnits && (unsigned)ih < (unsigned)a.H &&
+                            (unsigned)iw0 < (unsigned)a.W && ch0 < a.C_in;
+            const uint32_t base = ok ? (uint32_t)(((ch0 * a.H + ih) * a.W + iw0) * 2) : kOff;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                sv[k][e] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                    xr, __builtin_elementwise_add_sat(base, (uint32_t)(e * HW * 2)), 0, 0));
+        }
+    };
+    // transpose the two units to position-major pieces and write them into a window buffer
+    auto commit = [&](uint4 *win) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int u = tid + 256 * k;
+            const int o = u & 3, rg = u >> 2;
+            const int g = rg % G::Groups, r = rg / G::Groups;
+            if (u >= kUnits) continue;
+#pragma unroll
+            for (int x = 0; x < 8; ++x) {
+                int col;   // window column of input column iw0 + x, or -1
+                if constexpr (S == 1) {
+                    col = g == 0 ? (x == 7 ? 0 : -1)
+                                 : (g == G::Groups - 1 ? (x == 0 ? 33 : -1) : 1 + 8 * (g - 1) + x);
+                } else {
+                    col = g == 0 ? (x == 7 ? 0 : -1)
+                                 : ((x & 1) ? 4 * (g - 1) + (x + 1) / 2 : 36 + 4 * (g - 1) + x / 2);
+                }
+                if (col < 0) continue;
+                const int dw = x >> 1, hx = x & 1;
+                uint32_t d[4];
+#pragma unroll
+                for (int dd = 0; dd < 4; ++dd)
+                    d[dd] = m2_pack(m2_dword(sv[k][2 * dd], dw), hx, m2_dword(sv[k][2 * dd + 1], dw), hx);
+                win[m2_slot(r, col, o, G::RowPos)] = uint4{d[0], d[1], d[2], d[3]};
+            }
+        }
+    };
+
+    // ---- fragment addressing ----
+    // B: window slot of (row, column) for tap column kx and k16 slice sl; the row part of this
+    // wave and block is added as a compile-time offset plus the wave's base row.
+    int lslot[3][2];
+#pragma unroll
+    for (int kx = 0; kx < 3; ++kx)
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+            const int col = S == 1 ? j + kx : (kx == 1 ? 36 + j : j + kx / 2);
+            lslot[kx][sl] = m2_slot(S == 1 ? G::NBW * wave : 2 * wave, col, 2 * sl + hh, G::RowPos);
+        }
+    auto read_b = [&](const uint4 *win, int q, int nb) {
+        const int tap = q >> 1, sl = q & 1, ky = tap / 3, kx = tap % 3;
+        const int roff = S == 1 ? nb + ky : ky;
+        return __builtin_bit_cast(vec8, win[lslot[kx][sl] + roff * (G::RowPos * 4)]);
+    };
+    const int abase = hh * kRows + j;
+    auto read_a = [&](const uint4 *wc, int q, int mb) {
+        const int tap = q >> 1, sl = q & 1;
+        return __builtin_bit_cast(vec8, wc[abase + ((tap * 4 + 2 * sl) * kRows + mb * 32)]);
+    };
+
+    f32x16_t acc[2][G::NBW];
+    vec8 af[2][2], bq[2][G::NBW];
+    const float4 *bias4 = reinterpret_cast<const float4 *>(bias_s);
+
+    // run one 32-channel stage: 18 k16 slices (9 taps x 2), the next stage's window committed
+    // after slice CommitAfter
+    auto run_stage = [&](const uint4 *win, const uint4 *wc, uint4 *next_win, bool has_next) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) af[0][mb] = read_a(wc, 0, mb);
+#pragma unroll
+        for (int nb = 0; nb < G::NBW; ++nb) bq[0][nb] = read_b(win, 0, nb);
+#pragma unroll
+        for (int q = 0; q < 18; ++q) {
+            const int cb = q & 1;
+            if (q + 1 < 18) {
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb) af[cb ^ 1][mb] = read_a(wc, q + 1, mb);
+#pragma unroll
+                for (int nb = 0; nb < G::NBW; ++nb) bq[cb ^ 1][nb] = read_b(win, q + 1, nb);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < G::NBW; ++nb)
+                    acc[mb][nb] = E::mfma32x32x16(af[cb][mb], bq[cb][nb], acc[mb][nb]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (q == G::CommitAfter && has_next) commit(next_win);
+        }
+    };
+
+    if (my_tiles > 0) {
+        issue(0, 0);
+        commit(Win0);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // the weight pieces, bias and first window are written
+    m2_barrier();
+
+#pragma unroll 1
+    for (int it = 0; it < my_tiles; ++it) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < G::NBW; ++nb) {
+                acc[mb][nb] = f32x16_t{};
+                m2_touch(acc[mb][nb]);
+            }
+        // stage 0 (channels 0..31, window buffer 0) while the channels 32..63 window loads
+        issue(it, 1);
+        run_stage(Win0, Wc0, Win1, true);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        m2_barrier();
+        // stage 1 (channels 32..63, buffer 1) while the next tile's first window loads
+        const bool more = it + 1 < my_tiles;
+        if (more) issue(it + 1, 0);
+        run_stage(Win1, Wc1, Win0, more);
+
+        // ---- epilogue: bias + E, one rounding, 2-byte stores along W (rows past C_out,
+        // positions past the output go to an offset past the buffer range and are dropped) ----
+        int n, oh0, ow0;
+        tile_coords(it, n, oh0, ow0);
+        const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(a.y + (size_t)n * a.C_out * a.Hout * a.Wout), (short)0, (int)a.y_img_bytes,
+            0x00020000);
+        const int ow = ow0 + j;
+#pragma unroll
+        for (int nb = 0; nb < G::NBW; ++nb) {
+            const int oh = oh0 + (S == 1 ? G::NBW * wave + nb : wave);
+            const bool pos_ok = oh < a.Hout && ow < a.Wout;
+            const int pos = oh * a.Wout + ow;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                m2_touch(acc[mb][nb]);
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int co0 = mb * 32 + 8 * g4 + 4 * hh;
+                    const float4 bv = bias4[co0 >> 2];
+                    const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int co = co0 + i;
+                        const u16 r = E::from_f32(epilogue<EPI>(acc[mb][nb][4 * g4 + i] + bb[i]));
+                        const uint32_t off =
+                            pos_ok && co < a.C_out ? (uint32_t)((co * a.Hout * a.Wout + pos) * 2) : kOff;
+                        __builtin_amdgcn_raw_buffer_store_b16(r, yr, off, 0, 0);
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // this thread's window writes are done
+        m2_barrier();
+    }
+}
+
+}  // namespace
+
+bool mfma2d_supported(int C_in, int C_out, int H, int W, int stride) {
+    (void)H;
+    return C_in >= 1 && C_in <= 64 && C_in % 8 == 0 && C_out >= 1 && C_out <= 64 && W % 8 == 0 &&
+           (stride == 1 || stride == 2);
+}
+
+hipError_t launch_mfma2d(const Simt2dParams &p, hipStream_t stream) {
+    Mfma2dKArgs a{};
+    a.x = static_cast<const u16 *>(p.x);
+    a.w = static_cast<const u16 *>(p.w);
+    a.bias = static_cast<const u16 *>(p.bias);
+    a.y = static_cast<u16 *>(p.y);
+    a.N = p.N, a.C_in = p.C_in, a.C_out = p.C_out, a.H = p.H, a.W = p.W;
+    a.Hout = p.Hout, a.Wout = p.Wout;
+    const int TH = p.stride == 1 ? M2Geom<1>::TH : M2Geom<2>::TH;
+    a.tiles_h = (p.Hout + TH - 1) / TH;
+    a.tiles_w = (p.Wout + kTW - 1) / kTW;
+    a.ntiles = p.N * a.tiles_h * a.tiles_w;
+    a.x_img_bytes = (uint32_t)((size_t)p.C_in * p.H * p.W * 2);
+    a.y_img_bytes = (uint32_t)((size_t)p.C_out * p.Hout * p.Wout * 2);
+    a.w_bytes = (uint32_t)((size_t)p.C_out * p.C_in * 9 * 2);
+    const int grid = a.ntiles < 256 ? a.ntiles : 256;
+    if (grid == 0) return hipSuccess;
+#define CX_M2(BFV, SV, EPIV) mfma2d_kernel<BFV, SV, EPIV><<<dim3(grid), dim3(256), 0, stream>>>(a)
+#define CX_M2E(BFV, SV)                                     \
+    do {                                                    \
+        if (p.epilogue == EPI_RELU) CX_M2(BFV, SV, EPI_RELU);   \
+        else if (p.epilogue == EPI_CLAMP1) CX_M2(BFV, SV, EPI_CLAMP1); \
+        else CX_M2(BFV, SV, EPI_NONE);                      \
+    } while (0)
+    if (p.bf16) {
+        if (p.stride == 1) CX_M2E(true, 1);
+        else CX_M2E(true, 2);
+    } else {
+        if (p.stride == 1) CX_M2E(false, 1);
+        else CX_M2E(false, 2);
+    }
+#undef CX_M2E
+#undef CX_M2
+    return hipGetLastError();
+}
+
+}  // namespace cx
