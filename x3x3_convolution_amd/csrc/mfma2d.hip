@@ -55,7 +55,10 @@ struct M2Geom<1> {
     static constexpr int WRows = 18;     // window rows
     static constexpr int RowPos = 36;    // window row stride in positions (34 used)
     static constexpr int Groups = 6;     // 8-column load groups per window row
-    static constexpr int CommitAfter = 8;   // slice after which the next window is written
+    // the next window's column x (of both load units) is written after slice CommitFirst + x:
+    // late in the stage (its loads were issued before it) and one column per slice, so the
+    // transposes and LDS writes hide between the MFMAs
+    static constexpr int CommitFirst = 10;
 };
 template <>
 struct M2Geom<2> {
@@ -64,11 +67,12 @@ struct M2Geom<2> {
     static constexpr int WRows = 9;
     static constexpr int RowPos = 72;    // odd input columns at 0..32, even ones at 36..67
     static constexpr int Groups = 9;
-    static constexpr int CommitAfter = 17;
+    static constexpr int CommitFirst = 10;
 };
 static_assert(M2Geom<1>::WRows * M2Geom<1>::RowPos * 4 == kWinSlots, "window size");
 static_assert(M2Geom<2>::WRows * M2Geom<2>::RowPos * 4 == kWinSlots, "window size");
 static_assert(M2Geom<1>::WRows * M2Geom<1>::Groups * 4 <= 512, "two load units per thread");
+static_assert(M2Geom<1>::CommitFirst + 8 == 18 && M2Geom<2>::CommitFirst + 8 == 18, "8 columns");
 static_assert(M2Geom<2>::WRows * M2Geom<2>::Groups * 4 <= 512, "two load units per thread");
 
 struct Mfma2dKArgs {
@@ -161,8 +165,35 @@ __global__ __launch_bounds__(256, 1) void mfma2d_kernel(Mfma2dKArgs a) {
     };
 
     // ---- input window staging: unit u = (window row, 8-column group, channel octet) ----
+    // A thread owns units tid and tid + 256.  The LDS slot each of a unit's eight columns goes to
+    // does not depend on the tile, so it is computed once: columns outside the window (the
+    // unused part of the edge groups) and units past the window go to a column no fragment read
+    // touches (RowPos leaves spare columns in every row), which keeps the writes branch-free.
     constexpr int kUnits = G::WRows * G::Groups * 4;
+    constexpr int kTrash = S == 1 ? 34 : 33;
     uint4 sv[2][8];
+    int wslot[2][8];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int u = tid + 256 * k;
+        const int o = u & 3, rg = u >> 2;
+        const int g = rg % G::Groups;
+        const bool uok = u < kUnits;
+        const int r = uok ? rg / G::Groups : 0;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+            int col;
+            if constexpr (S == 1) {
+                col = g == 0 ? (x == 7 ? 0 : kTrash)
+                             : (g == G::Groups - 1 ? (x == 0 ? 33 : kTrash) : 1 + 8 * (g - 1) + x);
+            } else {
+                col = g == 0 ? (x == 7 ? 0 : kTrash)
+                             : ((x & 1) ? 4 * (g - 1) + (x + 1) / 2 : 36 + 4 * (g - 1) + x / 2);
+            }
+            if (!uok) col = kTrash;
+            wslot[k][x] = m2_slot(r, col, o, G::RowPos);
+        }
+    }
     // loads of the two units of this thread for stage (tile it, channel half c)
     auto issue = [&](int it, int c) {
         int n, oh0, ow0;
@@ -186,32 +217,19 @@ __global__ __launch_bounds__(256, 1) void mfma2d_kernel(Mfma2dKArgs a) {
                     xr, __builtin_elementwise_add_sat(base, (uint32_t)(e * HW * 2)), 0, 0));
         }
     };
-    // transpose the two units to position-major pieces and write them into a window buffer
-    auto commit = [&](uint4 *win) {
+    // column x of both units, transposed to one position's 8 channels each (v_perm picks the
+    // two halves) and written to a window buffer
+    auto commit_col = [&](uint4 *win, int x) {
+        const int dw = x >> 1;
+        const uint32_t sel = (x & 1) ? 0x07060302u : 0x05040100u;
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-            const int u = tid + 256 * k;
-            const int o = u & 3, rg = u >> 2;
-            const int g = rg % G::Groups, r = rg / G::Groups;
-            if (u >= kUnits) continue;
+            uint32_t d[4];
 #pragma unroll
-            for (int x = 0; x < 8; ++x) {
-                int col;   // window column of input column iw0 + x, or -1
-                if constexpr (S == 1) {
-                    col = g == 0 ? (x == 7 ? 0 : -1)
-                                 : (g == G::Groups - 1 ? (x == 0 ? 33 : -1) : 1 + 8 * (g - 1) + x);
-                } else {
-                    col = g == 0 ? (x == 7 ? 0 : -1)
-                                 : ((x & 1) ? 4 * (g - 1) + (x + 1) / 2 : 36 + 4 * (g - 1) + x / 2);
-                }
-                if (col < 0) continue;
-                const int dw = x >> 1, hx = x & 1;
-                uint32_t d[4];
-#pragma unroll
-                for (int dd = 0; dd < 4; ++dd)
-                    d[dd] = m2_pack(m2_dword(sv[k][2 * dd], dw), hx, m2_dword(sv[k][2 * dd + 1], dw), hx);
-                win[m2_slot(r, col, o, G::RowPos)] = uint4{d[0], d[1], d[2], d[3]};
-            }
+            for (int dd = 0; dd < 4; ++dd)
+                d[dd] = __builtin_amdgcn_perm(m2_dword(sv[k][2 * dd + 1], dw),
+                                              m2_dword(sv[k][2 * dd], dw), sel);
+            win[wslot[k][x]] = uint4{d[0], d[1], d[2], d[3]};
         }
     };
 
@@ -241,8 +259,8 @@ __global__ __launch_bounds__(256, 1) void mfma2d_kernel(Mfma2dKArgs a) {
     vec8 af[2][2], bq[2][G::NBW];
     const float4 *bias4 = reinterpret_cast<const float4 *>(bias_s);
 
-    // run one 32-channel stage: 18 k16 slices (9 taps x 2), the next stage's window committed
-    // after slice CommitAfter
+    // run one 32-channel stage: 18 k16 slices (9 taps x 2), the next stage's window written
+    // column by column after slices CommitFirst .. 17
     auto run_stage = [&](const uint4 *win, const uint4 *wc, uint4 *next_win, bool has_next) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) af[0][mb] = read_a(wc, 0, mb);
@@ -264,16 +282,18 @@ __global__ __launch_bounds__(256, 1) void mfma2d_kernel(Mfma2dKArgs a) {
                 for (int nb = 0; nb < G::NBW; ++nb)
                     acc[mb][nb] = E::mfma32x32x16(af[cb][mb], bq[cb][nb], acc[mb][nb]);
             __builtin_amdgcn_sched_barrier(0);
-            if (q == G::CommitAfter && has_next) commit(next_win);
+            if (q >= G::CommitFirst && has_next) commit_col(next_win, q - G::CommitFirst);
         }
     };
 
     if (my_tiles > 0) {
         issue(0, 0);
-        commit(Win0);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) commit_col(Win0, x);
     }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // the weight pieces, bias and first window are written
     m2_barrier();
+    if (my_tiles > 0) issue(0, 1);
 
 #pragma unroll 1
     for (int it = 0; it < my_tiles; ++it) {
@@ -284,8 +304,8 @@ __global__ __launch_bounds__(256, 1) void mfma2d_kernel(Mfma2dKArgs a) {
                 acc[mb][nb] = f32x16_t{};
                 m2_touch(acc[mb][nb]);
             }
-        // stage 0 (channels 0..31, window buffer 0) while the channels 32..63 window loads
-        issue(it, 1);
+        // stage 0 (channels 0..31, window buffer 0); the channels 32..63 window, loaded before
+        // the previous tile's stores, goes to buffer 1
         run_stage(Win0, Wc0, Win1, true);
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         m2_barrier();
@@ -293,20 +313,24 @@ __global__ __launch_bounds__(256, 1) void mfma2d_kernel(Mfma2dKArgs a) {
         const bool more = it + 1 < my_tiles;
         if (more) issue(it + 1, 0);
         run_stage(Win1, Wc1, Win0, more);
+        // The next tile's second window is loaded before this tile's stores: a wait for those
+        // loads then never has to wait for the stores to drain (both count in vmcnt).
+        if (more) issue(it + 1, 1);
 
-        // ---- epilogue: bias + E, one rounding, 2-byte stores along W (rows past C_out,
+        // ---- epilogue: bias + E, one rounding, 4-byte stores along W (rows past C_out,
         // positions past the output go to an offset past the buffer range and are dropped) ----
         int n, oh0, ow0;
         tile_coords(it, n, oh0, ow0);
         const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(a.y + (size_t)n * a.C_out * a.Hout * a.Wout), (short)0, (int)a.y_img_bytes,
             0x00020000);
-        const int ow = ow0 + j;
+        const bool odd = (j & 1) != 0;
+        const int ow_even = ow0 + (j & ~1);   // Wout is even (W % 8 == 0): pairs never straddle
 #pragma unroll
         for (int nb = 0; nb < G::NBW; ++nb) {
             const int oh = oh0 + (S == 1 ? G::NBW * wave + nb : wave);
-            const bool pos_ok = oh < a.Hout && ow < a.Wout;
-            const int pos = oh * a.Wout + ow;
+            const bool pos_ok = oh < a.Hout && ow_even < a.Wout;
+            const int pos_even = oh * a.Wout + ow_even;
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) {
                 m2_touch(acc[mb][nb]);
@@ -315,13 +339,24 @@ __global__ __launch_bounds__(256, 1) void mfma2d_kernel(Mfma2dKArgs a) {
                     const int co0 = mb * 32 + 8 * g4 + 4 * hh;
                     const float4 bv = bias4[co0 >> 2];
                     const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
+                    uint32_t r[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int co = co0 + i;
-                        const u16 r = E::from_f32(epilogue<EPI>(acc[mb][nb][4 * g4 + i] + bb[i]));
-                        const uint32_t off =
-                            pos_ok && co < a.C_out ? (uint32_t)((co * a.Hout * a.Wout + pos) * 2) : kOff;
-                        __builtin_amdgcn_raw_buffer_store_b16(r, yr, off, 0, 0);
+                    for (int i = 0; i < 4; ++i)
+                        r[i] = E::from_f32(epilogue<EPI>(acc[mb][nb][4 * g4 + i] + bb[i]));
+                    // Lanes j, j^1 pair up: the even lane stores channels co0, co0+2 at columns
+                    // (j, j+1), the odd lane channels co0+1, co0+3 at (j-1, j): one 4-byte store
+                    // per channel pair instead of two 2-byte ones.
+#pragma unroll
+                    for (int pr = 0; pr < 2; ++pr) {
+                        const uint32_t A = r[2 * pr], B = r[2 * pr + 1];
+                        const uint32_t send = odd ? A : B;
+                        const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
+                        const uint32_t packed = odd ? (recv | (B << 16)) : (A | (recv << 16));
+                        const int co = co0 + 2 * pr + (odd ? 1 : 0);
+                        const uint32_t off = pos_ok && co < a.C_out
+                                                 ? (uint32_t)((co * a.Hout * a.Wout + pos_even) * 2)
+                                                 : kOff;
+                        __builtin_amdgcn_raw_buffer_store_b32(packed, yr, off, 0, 0);
                     }
                 }
             }
