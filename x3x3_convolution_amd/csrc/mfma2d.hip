@@ -255,13 +255,62 @@ __global__ __launch_bounds__(256, 1) void mfma2d_kernel(Mfma2dKArgs a) {
         return __builtin_bit_cast(vec8, wc[abase + ((tap * 4 + 2 * sl) * kRows + mb * 32)]);
     };
 
-    f32x16_t acc[2][G::NBW];
+    // Two accumulator sets: a tile's results are stored while the next tile's first stage runs
+    // (its stores interleaved with the MFMAs), so the epilogue costs no matrix-core time.
+    f32x16_t accA[2][G::NBW], accB[2][G::NBW];
     vec8 af[2][2], bq[2][G::NBW];
     const float4 *bias4 = reinterpret_cast<const float4 *>(bias_s);
+    typedef f32x16_t AccSet[2][G::NBW];
 
-    // run one 32-channel stage: 18 k16 slices (9 taps x 2), the next stage's window written
-    // column by column after slices CommitFirst .. 17
-    auto run_stage = [&](const uint4 *win, const uint4 *wc, uint4 *next_win, bool has_next) {
+    // ---- epilogue part: bias + E, one rounding, 4-byte stores along W (rows past C_out,
+    // positions past the output go to an offset past the buffer range and are dropped).  Group
+    // gi = (block nb, block mb, 4-row group g4) of a finished tile's accumulators. ----
+    constexpr int kGroups = G::NBW * 2 * 4;
+    constexpr int kGroupsPerSlice = (kGroups + 15) / 16;
+    const bool odd = (j & 1) != 0;
+    auto store_group = [&](AccSet &pacc, int gi, int oh0, int ow0,
+                           const __amdgpu_buffer_rsrc_t &yr) __attribute__((always_inline)) {
+        const int nb = gi / 8, mb = (gi / 4) % 2, g4 = gi % 4;
+        const int ow_even = ow0 + (j & ~1);   // Wout is even (W % 8 == 0): pairs never straddle
+        const int oh = oh0 + (S == 1 ? G::NBW * wave + nb : wave);
+        const bool pos_ok = oh < a.Hout && ow_even < a.Wout;
+        const int pos_even = oh * a.Wout + ow_even;
+        if (g4 == 0) m2_touch(pacc[mb][nb]);
+        const int co0 = mb * 32 + 8 * g4 + 4 * hh;
+        const float4 bv = bias4[co0 >> 2];
+        const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
+        uint32_t r[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            r[i] = E::from_f32(epilogue<EPI>(pacc[mb][nb][4 * g4 + i] + bb[i]));
+        // Lanes j, j^1 pair up: the even lane stores channels co0, co0+2 at columns (j, j+1),
+        // the odd lane channels co0+1, co0+3 at (j-1, j): one 4-byte store per channel pair.
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+            const uint32_t A = r[2 * pr], B = r[2 * pr + 1];
+            const uint32_t send = odd ? A : B;
+            const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
+            const uint32_t packed = odd ? (recv | (B << 16)) : (A | (recv << 16));
+            const int co = co0 + 2 * pr + (odd ? 1 : 0);
+            const uint32_t off =
+                pos_ok && co < a.C_out ? (uint32_t)((co * a.Hout * a.Wout + pos_even) * 2) : kOff;
+            __builtin_amdgcn_raw_buffer_store_b32(packed, yr, off, 0, 0);
+        }
+    };
+    auto y_rsrc = [&](int n) {
+        return __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(a.y + (size_t)n * a.C_out * a.Hout * a.Wout), (short)0, (int)a.y_img_bytes,
+            0x00020000);
+    };
+
+    // run one 32-channel stage into cacc: 18 k16 slices (9 taps x 2); the next stage's window
+    // is written column by column after slices CommitFirst .. 17, and the previous tile's
+    // results (pacc, tile pit) are stored over the first slices when has_prev
+    auto run_stage = [&](AccSet &cacc, const uint4 *win, const uint4 *wc, uint4 *next_win,
+                         bool has_next, AccSet &pacc, int pit, bool has_prev) __attribute__((always_inline)) {
+        int pn = 0, poh0 = 0, pow0 = 0;
+        tile_coords(pit, pn, poh0, pow0);
+        const __amdgpu_buffer_rsrc_t yr = y_rsrc(pn);
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) af[0][mb] = read_a(wc, 0, mb);
 #pragma unroll
@@ -280,10 +329,41 @@ __global__ __launch_bounds__(256, 1) void mfma2d_kernel(Mfma2dKArgs a) {
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                 for (int nb = 0; nb < G::NBW; ++nb)
-                    acc[mb][nb] = E::mfma32x32x16(af[cb][mb], bq[cb][nb], acc[mb][nb]);
+                    cacc[mb][nb] = E::mfma32x32x16(af[cb][mb], bq[cb][nb], cacc[mb][nb]);
             __builtin_amdgcn_sched_barrier(0);
+            if (has_prev) {
+#pragma unroll
+                for (int k = 0; k < kGroupsPerSlice; ++k) {
+                    const int gi = q * kGroupsPerSlice + k;
+                    if (gi < kGroups) store_group(pacc, gi, poh0, pow0, yr);
+                }
+            }
             if (q >= G::CommitFirst && has_next) commit_col(next_win, q - G::CommitFirst);
         }
+    };
+    // one tile into cacc, storing the previous one's results (pacc) during its first stage
+    auto tile_body = [&](AccSet &cacc, int it, AccSet &pacc, bool has_prev) __attribute__((always_inline)) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < G::NBW; ++nb) {
+                cacc[mb][nb] = f32x16_t{};
+                m2_touch(cacc[mb][nb]);
+            }
+        // stage 0 (channels 0..31, window buffer 0); the channels 32..63 window, loaded before
+        // the previous tile's stores, goes to buffer 1
+        run_stage(cacc, Win0, Wc0, Win1, true, pacc, it - 1, has_prev);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        m2_barrier();
+        // stage 1 (channels 32..63, buffer 1) while the next tile's first window loads
+        const bool more = it + 1 < my_tiles;
+        if (more) issue(it + 1, 0);
+        run_stage(cacc, Win1, Wc1, Win0, more, pacc, it - 1, false);
+        // The next tile's second window is loaded before the stores of this tile go out (in
+        // the next tile's first stage), so waiting for those loads never waits for stores.
+        if (more) issue(it + 1, 1);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // this thread's window writes are done
+        m2_barrier();
     };
 
     if (my_tiles > 0) {
@@ -296,73 +376,23 @@ __global__ __launch_bounds__(256, 1) void mfma2d_kernel(Mfma2dKArgs a) {
     if (my_tiles > 0) issue(0, 1);
 
 #pragma unroll 1
-    for (int it = 0; it < my_tiles; ++it) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < G::NBW; ++nb) {
-                acc[mb][nb] = f32x16_t{};
-                m2_touch(acc[mb][nb]);
-            }
-        // stage 0 (channels 0..31, window buffer 0); the channels 32..63 window, loaded before
-        // the previous tile's stores, goes to buffer 1
-        run_stage(Win0, Wc0, Win1, true);
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-        m2_barrier();
-        // stage 1 (channels 32..63, buffer 1) while the next tile's first window loads
-        const bool more = it + 1 < my_tiles;
-        if (more) issue(it + 1, 0);
-        run_stage(Win1, Wc1, Win0, more);
-        // The next tile's second window is loaded before this tile's stores: a wait for those
-        // loads then never has to wait for the stores to drain (both count in vmcnt).
-        if (more) issue(it + 1, 1);
-
-        // ---- epilogue: bias + E, one rounding, 4-byte stores along W (rows past C_out,
-        // positions past the output go to an offset past the buffer range and are dropped) ----
+    for (int it = 0; it < my_tiles; it += 2) {
+        tile_body(accA, it, accB, it > 0);
+        if (it + 1 < my_tiles) tile_body(accB, it + 1, accA, true);
+    }
+    // the last tile's results
+    if (my_tiles > 0) {
+        const int last = my_tiles - 1;
         int n, oh0, ow0;
-        tile_coords(it, n, oh0, ow0);
-        const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(a.y + (size_t)n * a.C_out * a.Hout * a.Wout), (short)0, (int)a.y_img_bytes,
-            0x00020000);
-        const bool odd = (j & 1) != 0;
-        const int ow_even = ow0 + (j & ~1);   // Wout is even (W % 8 == 0): pairs never straddle
+        tile_coords(last, n, oh0, ow0);
+        const __amdgpu_buffer_rsrc_t yr = y_rsrc(n);
+        if ((last & 1) == 0) {
 #pragma unroll
-        for (int nb = 0; nb < G::NBW; ++nb) {
-            const int oh = oh0 + (S == 1 ? G::NBW * wave + nb : wave);
-            const bool pos_ok = oh < a.Hout && ow_even < a.Wout;
-            const int pos_even = oh * a.Wout + ow_even;
+            for (int gi = 0; gi < kGroups; ++gi) store_group(accA, gi, oh0, ow0, yr);
+        } else {
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                m2_touch(acc[mb][nb]);
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int co0 = mb * 32 + 8 * g4 + 4 * hh;
-                    const float4 bv = bias4[co0 >> 2];
-                    const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
-                    uint32_t r[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        r[i] = E::from_f32(epilogue<EPI>(acc[mb][nb][4 * g4 + i] + bb[i]));
-                    // Lanes j, j^1 pair up: the even lane stores channels co0, co0+2 at columns
-                    // (j, j+1), the odd lane channels co0+1, co0+3 at (j-1, j): one 4-byte store
-                    // per channel pair instead of two 2-byte ones.
-#pragma unroll
-                    for (int pr = 0; pr < 2; ++pr) {
-                        const uint32_t A = r[2 * pr], B = r[2 * pr + 1];
-                        const uint32_t send = odd ? A : B;
-                        const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
-                        const uint32_t packed = odd ? (recv | (B << 16)) : (A | (recv << 16));
-                        const int co = co0 + 2 * pr + (odd ? 1 : 0);
-                        const uint32_t off = pos_ok && co < a.C_out
-                                                 ? (uint32_t)((co * a.Hout * a.Wout + pos_even) * 2)
-                                                 : kOff;
-                        __builtin_amdgcn_raw_buffer_store_b32(packed, yr, off, 0, 0);
-                    }
-                }
-            }
+            for (int gi = 0; gi < kGroups; ++gi) store_group(accB, gi, oh0, ow0, yr);
         }
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // this thread's window writes are done
-        m2_barrier();
     }
 }
 
