@@ -268,33 +268,34 @@ __global__ __launch_bounds__(256, 1) void mfma2d_kernel(Mfma2dKArgs a) {
     constexpr int kGroups = G::NBW * 2 * 4;
     constexpr int kGroupsPerSlice = (kGroups + 15) / 16;
     const bool odd = (j & 1) != 0;
+    // per-lane constants of the stores: the lane's channel within a pair group (4*hh + odd) and
+    // the v_perm selector that puts its own half low (even lane) or high (odd lane)
+    const int HWo = a.Hout * a.Wout;
+    const uint32_t psel = odd ? 0x01000504u : 0x05040100u;
     auto store_group = [&](AccSet &pacc, int gi, int oh0, int ow0,
                            const __amdgpu_buffer_rsrc_t &yr) __attribute__((always_inline)) {
         const int nb = gi / 8, mb = (gi / 4) % 2, g4 = gi % 4;
         const int ow_even = ow0 + (j & ~1);   // Wout is even (W % 8 == 0): pairs never straddle
         const int oh = oh0 + (S == 1 ? G::NBW * wave + nb : wave);
-        const bool pos_ok = oh < a.Hout && ow_even < a.Wout;
-        const int pos_even = oh * a.Wout + ow_even;
+        // this lane's offset for channel 4*hh + odd of the group (rows past C_out fall past the
+        // image and are dropped by the range check; positions outside go to kOff)
+        const uint32_t lb = oh < a.Hout && ow_even < a.Wout
+                                ? (uint32_t)(((4 * hh + (odd ? 1 : 0)) * HWo + oh * a.Wout + ow_even) * 2)
+                                : kOff;
         if (g4 == 0) m2_touch(pacc[mb][nb]);
-        const int co0 = mb * 32 + 8 * g4 + 4 * hh;
-        const float4 bv = bias4[co0 >> 2];
-        const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
         uint32_t r[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            r[i] = E::from_f32(epilogue<EPI>(pacc[mb][nb][4 * g4 + i] + bb[i]));
-        // Lanes j, j^1 pair up: the even lane stores channels co0, co0+2 at columns (j, j+1),
-        // the odd lane channels co0+1, co0+3 at (j-1, j): one 4-byte store per channel pair.
+        for (int i = 0; i < 4; ++i) r[i] = E::from_f32(epilogue<EPI>(pacc[mb][nb][4 * g4 + i]));
+        // Lanes j, j^1 pair up: the even lane stores channels c, c+2 at columns (j, j+1), the
+        // odd lane channels c+1, c+3 at (j-1, j): one 4-byte store per channel pair.
 #pragma unroll
         for (int pr = 0; pr < 2; ++pr) {
             const uint32_t A = r[2 * pr], B = r[2 * pr + 1];
-            const uint32_t send = odd ? A : B;
+            const uint32_t keep = odd ? B : A, send = odd ? A : B;
             const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
-            const uint32_t packed = odd ? (recv | (B << 16)) : (A | (recv << 16));
-            const int co = co0 + 2 * pr + (odd ? 1 : 0);
-            const uint32_t off =
-                pos_ok && co < a.C_out ? (uint32_t)((co * a.Hout * a.Wout + pos_even) * 2) : kOff;
-            __builtin_amdgcn_raw_buffer_store_b32(packed, yr, off, 0, 0);
+            const uint32_t packed = __builtin_amdgcn_perm(recv, keep, psel);
+            const uint32_t uo = (uint32_t)((mb * 32 + 8 * g4 + 2 * pr) * HWo * 2);
+            __builtin_amdgcn_raw_buffer_store_b32(packed, yr, __builtin_elementwise_add_sat(lb, uo), 0, 0);
         }
     };
     auto y_rsrc = [&](int n) {
@@ -343,13 +344,22 @@ __global__ __launch_bounds__(256, 1) void mfma2d_kernel(Mfma2dKArgs a) {
     };
     // one tile into cacc, storing the previous one's results (pacc) during its first stage
     auto tile_body = [&](AccSet &cacc, int it, AccSet &pacc, bool has_prev) __attribute__((always_inline)) {
+        // the accumulators start at the bias of their channels (register i of block mb in
+        // lane half hh: channel mb*32 + 8*(i/4) + 4*hh + i%4)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 2; ++mb) {
+            f32x16_t b16;
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const float4 bv = bias4[(mb * 32 + 8 * g4 + 4 * hh) >> 2];
+                b16[4 * g4] = bv.x, b16[4 * g4 + 1] = bv.y, b16[4 * g4 + 2] = bv.z, b16[4 * g4 + 3] = bv.w;
+            }
 #pragma unroll
             for (int nb = 0; nb < G::NBW; ++nb) {
-                cacc[mb][nb] = f32x16_t{};
+                cacc[mb][nb] = b16;
                 m2_touch(cacc[mb][nb]);
             }
+        }
         // stage 0 (channels 0..31, window buffer 0); the channels 32..63 window, loaded before
         // the previous tile's stores, goes to buffer 1
         run_stage(cacc, Win0, Wc0, Win1, true, pacc, it - 1, has_prev);
@@ -399,9 +409,12 @@ __global__ __launch_bounds__(256, 1) void mfma2d_kernel(Mfma2dKArgs a) {
 }  // namespace
 
 bool mfma2d_supported(int C_in, int C_out, int H, int W, int stride) {
-    (void)H;
-    return C_in >= 1 && C_in <= 64 && C_in % 8 == 0 && C_out >= 1 && C_out <= 64 && W % 8 == 0 &&
-           (stride == 1 || stride == 2);
+    if (!(C_in >= 1 && C_in <= 64 && C_in % 8 == 0 && C_out >= 1 && C_out <= 64 && W % 8 == 0 &&
+          (stride == 1 || stride == 2)))
+        return false;
+    // store offsets are formed for all 64 (padded) output channels of an image: 32-bit safe
+    const long long hw_out = (long long)((H - 1) / stride + 1) * ((W - 1) / stride + 1);
+    return H >= 1 && 64 * hw_out * 2 < (1ll << 31);
 }
 
 hipError_t launch_mfma2d(const Simt2dParams &p, hipStream_t stream) {
