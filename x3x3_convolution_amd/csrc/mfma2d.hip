@@ -29,8 +29,9 @@
 //     (the taps kx = 0, 2 read the odd ones, kx = 1 the even ones), so those reads are unit
 //     stride too.  Two window buffers: the next stage's window is loaded while this one's
 //     MFMAs run, one barrier per stage.
-//   * Waves: each of the four owns all 64 rows and TH/4 output rows of the tile (4 blocks of 32
-//     positions at stride 1, one at stride 2).
+//   * Waves: each owns all 64 rows and TH / NWaves output rows of the tile: at stride 1 eight
+//     waves (two per SIMD, so one's vector work overlaps the other's MFMAs) of two 32-position
+//     blocks each, at stride 2 four waves of one block.
 // Input columns are handled in aligned groups of 8, so W must be a multiple of 8 (checked by
 // the host); rows, columns and channels outside the tensor load as zero (the zero padding).
 #include "common.hpp"
@@ -50,8 +51,9 @@ template <int S>
 struct M2Geom;
 template <>
 struct M2Geom<1> {
+    static constexpr int NWaves = 8;     // two waves per SIMD
     static constexpr int TH = 16;        // output rows per tile
-    static constexpr int NBW = 4;        // 32-position blocks per wave (output rows)
+    static constexpr int NBW = 2;        // 32-position blocks per wave (output rows)
     static constexpr int WRows = 18;     // window rows
     static constexpr int RowPos = 36;    // window row stride in positions (34 used)
     static constexpr int Groups = 6;     // 8-column load groups per window row
@@ -62,6 +64,7 @@ struct M2Geom<1> {
 };
 template <>
 struct M2Geom<2> {
+    static constexpr int NWaves = 4;
     static constexpr int TH = 4;
     static constexpr int NBW = 1;
     static constexpr int WRows = 9;
@@ -71,9 +74,9 @@ struct M2Geom<2> {
 };
 static_assert(M2Geom<1>::WRows * M2Geom<1>::RowPos * 4 == kWinSlots, "window size");
 static_assert(M2Geom<2>::WRows * M2Geom<2>::RowPos * 4 == kWinSlots, "window size");
-static_assert(M2Geom<1>::WRows * M2Geom<1>::Groups * 4 <= 512, "two load units per thread");
 static_assert(M2Geom<1>::CommitFirst + 8 == 18 && M2Geom<2>::CommitFirst + 8 == 18, "8 columns");
-static_assert(M2Geom<2>::WRows * M2Geom<2>::Groups * 4 <= 512, "two load units per thread");
+static_assert(M2Geom<1>::NWaves * M2Geom<1>::NBW == M2Geom<1>::TH, "waves cover the tile rows");
+static_assert(M2Geom<2>::NWaves * M2Geom<2>::NBW == M2Geom<2>::TH, "waves cover the tile rows");
 
 struct Mfma2dKArgs {
     const u16 *x, *w, *bias;
@@ -101,9 +104,10 @@ __device__ __forceinline__ uint32_t m2_pack(uint32_t a, int h0, uint32_t b, int 
 }
 
 template <bool BF, int S, int EPI>
-__global__ __launch_bounds__(256, 1) void mfma2d_kernel(Mfma2dKArgs a) {
+__global__ __launch_bounds__(64 * M2Geom<S>::NWaves, 1) void mfma2d_kernel(Mfma2dKArgs a) {
     using E = Elem<BF>;
     using G = M2Geom<S>;
+    constexpr int kThreads = 64 * G::NWaves;
     typedef typename E::vec8 vec8;
     __shared__ __attribute__((aligned(16))) uint4 Wc0[kWPieces];    // input channels 0..31
     __shared__ __attribute__((aligned(16))) uint4 Wc1[kWPieces];    // input channels 32..63
@@ -124,7 +128,7 @@ __global__ __launch_bounds__(256, 1) void mfma2d_kernel(Mfma2dKArgs a) {
     {
         const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
             (void *)a.w, (short)0, (int)a.w_bytes, 0x00020000);
-        for (int u = tid; u < kRows * 8; u += 256) {
+        for (int u = tid; u < kRows * 8; u += kThreads) {
             const int m = u & (kRows - 1), q = u >> 6;
             const bool ok = m < a.C_out && 8 * q < a.C_in;
             const uint32_t base = ok ? (uint32_t)((m * a.C_in + 8 * q) * 18) : kOff;
@@ -165,17 +169,18 @@ __global__ __launch_bounds__(256, 1) void mfma2d_kernel(Mfma2dKArgs a) {
     };
 
     // ---- input window staging: unit u = (window row, 8-column group, channel octet) ----
-    // A thread owns units tid and tid + 256.  The LDS slot each of a unit's eight columns goes to
+    // A thread owns units tid + k * kThreads.  The LDS slot each of a unit's eight columns goes to
     // does not depend on the tile, so it is computed once: columns outside the window (the
     // unused part of the edge groups) and units past the window go to a column no fragment read
     // touches (RowPos leaves spare columns in every row), which keeps the writes branch-free.
     constexpr int kUnits = G::WRows * G::Groups * 4;
+    constexpr int kUPT = (kUnits + kThreads - 1) / kThreads;   // load units per thread
     constexpr int kTrash = S == 1 ? 34 : 33;
-    uint4 sv[2][8];
-    int wslot[2][8];
+    uint4 sv[kUPT][8];
+    int wslot[kUPT][8];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int u = tid + 256 * k;
+    for (int k = 0; k < kUPT; ++k) {
+        const int u = tid + kThreads * k;
         const int o = u & 3, rg = u >> 2;
         const int g = rg % G::Groups;
         const bool uok = u < kUnits;
@@ -201,8 +206,8 @@ __global__ __launch_bounds__(256, 1) void mfma2d_kernel(Mfma2dKArgs a) {
         const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(a.x + (size_t)n * a.C_in * HW), (short)0, (int)a.x_img_bytes, 0x00020000);
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int u = tid + 256 * k;
+        for (int k = 0; k < kUPT; ++k) {
+            const int u = tid + kThreads * k;
             const int o = u & 3, rg = u >> 2;
             const int g = rg % G::Groups, r = rg / G::Groups;
             const int ih = S * oh0 - 1 + r;
@@ -223,7 +228,7 @@ __global__ __launch_bounds__(256, 1) void mfma2d_kernel(Mfma2dKArgs a) {
         const int dw = x >> 1;
         const uint32_t sel = (x & 1) ? 0x07060302u : 0x05040100u;
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < kUPT; ++k) {
             uint32_t d[4];
 #pragma unroll
             for (int dd = 0; dd < 4; ++dd)
@@ -434,7 +439,8 @@ hipError_t launch_mfma2d(const Simt2dParams &p, hipStream_t stream) {
     a.w_bytes = (uint32_t)((size_t)p.C_out * p.C_in * 9 * 2);
     const int grid = a.ntiles < 256 ? a.ntiles : 256;
     if (grid == 0) return hipSuccess;
-#define CX_M2(BFV, SV, EPIV) mfma2d_kernel<BFV, SV, EPIV><<<dim3(grid), dim3(256), 0, stream>>>(a)
+#define CX_M2(BFV, SV, EPIV) \
+    mfma2d_kernel<BFV, SV, EPIV><<<dim3(grid), dim3(64 * M2Geom<SV>::NWaves), 0, stream>>>(a)
 #define CX_M2E(BFV, SV)                                     \
     do {                                                    \
         if (p.epilogue == EPI_RELU) CX_M2(BFV, SV, EPI_RELU);   \
