@@ -129,6 +129,40 @@ int conv3x3x3_fwd(const void *x, const void *w_packed, const void *bias, void *y
                   int C_in, int C_out, int D, int H, int W, int stride, int layout, int dtype,
                   int epilogue, int algo, void *workspace, size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------------------------
+ * 3D over an input region: row bands with halo rows, frame chunks and causal temporal padding.
+ * [head.cu, head_stencil: an output band of rows [lo, lo+rows) of a global height, its input
+ * carrying g_off extra rows each side, zero padding decided by the global height; head.cu,
+ * commit summary: the decoder carries a few latent frames per pass to bound its memory.]
+ *
+ *   y[n,od,oh,ow,co] = E( b[co] + sum_{ci,kd,ky,kx} w[co,ci,kd,ky,kx]
+ *                                 * X[n, od+d_org-1+kd, oh+h_org-1+ky, ow-1+kx, ci] )
+ * for od < D_out, oh < H_out, ow < W, where X is x (N,D_in,H_in,W,C_in) NDHWC inside input frames
+ * [d_lo, d_hi) and rows [h_lo, h_hi) and columns [0, W), and zero everywhere else: frames and
+ * rows outside the valid ranges are never read, whatever they hold.  y is (N,D_out,H_out,W,
+ * C_out) NDHWC.  With D_in = D_out, H_in = H_out, origins 0 and the whole tensor valid this is
+ * conv3x3x3_fwd.  Examples:
+ *   - row band [lo, lo+rows) of a global height Hg, x holding global rows lo-g .. lo+rows+g-1:
+ *     H_out = rows, H_in = rows + 2g, h_org = g, h_lo = max(0, g-lo), h_hi = min(H_in, Hg+g-lo);
+ *   - causal temporal padding (output frame t reads frames t-2 .. t, zeros before frame 0):
+ *     D_in = D_out, d_org = -1, d_lo = 0, d_hi = D_in;
+ *   - the next chunk of a causal pass with the previous chunk's last two frames in front of x:
+ *     D_in = D_out + 2, d_org = 1, d_lo = 0, d_hi = D_in.
+ * Requirements beyond conv3x3x3_fwd's: 0 <= d_lo <= d_hi <= D_in, 0 <= h_lo <= h_hi <= H_in
+ * (else CONV_E_INVAL); every output frame reads at least one valid input frame, i.e. d_lo < d_hi,
+ * d_lo <= d_org + 1 and D_out + d_org - 1 <= d_hi (else CONV_E_UNSUPPORTED); SPLIT_HEAD only when
+ * input rows h_org-1 and H_out+h_org are outside [h_lo, h_hi) (its stencil reads the rows next
+ * to the band as zeros; FUSED_HEAD has no such limit).  The algorithm, the weight packing and the
+ * workspace are those of conv3x3x3_fwd for the OUTPUT extent: pass (N, C_in, C_out, D_out,
+ * H_out, W) to conv3x3x3_select_algo, _packed_weight_bytes, _pack_weights and _workspace_bytes.
+ * x, y and the workspace must not overlap.
+ * ---------------------------------------------------------------------------------------- */
+int conv3x3x3_fwd_region(const void *x, const void *w_packed, const void *bias, void *y, int N,
+                         int C_in, int C_out, int D_in, int H_in, int W, int D_out, int H_out,
+                         int d_org, int h_org, int d_lo, int d_hi, int h_lo, int h_hi, int layout,
+                         int dtype, int epilogue, int algo, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
 /* The concrete algorithm conv3x3x3_fwd runs for `algo` (AUTO resolved), or a negative status
  * if the request is unsupported. */
 int conv3x3x3_select_algo(int N, int C_in, int C_out, int D, int H, int W, int stride,

@@ -199,3 +199,52 @@ def test_no_device_reported_after_validation():
     assert f2d() == C.E_NODEVICE
     assert f3d() == C.E_NODEVICE
     assert "device" in cx.conv_last_error()
+
+
+def f3r(**kw):
+    """conv3x3x3_fwd_region with a valid default region: output (1, 4, 6, 8, 12) of a band
+    of rows [2, 8) with one halo row each side (H_in = 8) and two cached frames (D_in = 6)."""
+    a = dict(x=A, w=B, bias=None, y=A + (1 << 28), N=1, C_in=32, C_out=12, D_in=6, H_in=8, W=8,
+             D_out=4, H_out=6, d_org=1, h_org=1, d_lo=0, d_hi=6, h_lo=0, h_hi=8, layout=1,
+             dtype=1, epilogue=2, algo=C.ALGO_FUSED_HEAD, ws=None, wsb=0, stream=0)
+    a.update(kw)
+    return _st(cx.conv3x3x3_fwd_region, *[a[k] for k in (
+        "x", "w", "bias", "y", "N", "C_in", "C_out", "D_in", "H_in", "W", "D_out", "H_out",
+        "d_org", "h_org", "d_lo", "d_hi", "h_lo", "h_hi", "layout", "dtype", "epilogue", "algo",
+        "ws", "wsb", "stream")])
+
+
+def test_region_invalid_and_unsupported():
+    assert f3r(x=None) == C.E_INVAL
+    assert f3r(D_in=-1) == C.E_INVAL
+    assert f3r(d_lo=-1) == C.E_INVAL
+    assert f3r(d_hi=7) == C.E_INVAL              # past D_in
+    assert f3r(d_lo=4, d_hi=3) == C.E_INVAL
+    assert f3r(h_hi=9) == C.E_INVAL              # past H_in
+    assert f3r(h_lo=5, h_hi=4) == C.E_INVAL
+    # every output frame must read a valid frame
+    assert f3r(d_lo=3) == C.E_UNSUPPORTED       # frame 0 reads 0..2 only
+    assert f3r(d_hi=3) == C.E_UNSUPPORTED       # frame 3 reads 3..5 only
+    assert f3r(d_lo=2, d_hi=2) == C.E_UNSUPPORTED
+    assert f3r(d_org=4) == C.E_UNSUPPORTED       # frame 3 reads 6..8 only
+    assert f3r(d_org=-2) == C.E_UNSUPPORTED      # frame 0 reads -3..-1 only
+    assert f3r(algo=C.ALGO_SIMT) == C.E_UNSUPPORTED
+    assert f3r(C_in=20) == C.E_UNSUPPORTED
+    assert f3r(y=A + 16) == C.E_INVAL           # overlaps x (x is 6*8*8*32*2 bytes)
+    # the split head's stencil reads rows -1 and H_out as zero: not with halo rows that hold data
+    ws = cx.conv3x3x3_workspace_bytes(1, 32, 12, 4, 6, 8, 1, 1, 1, C.ALGO_SPLIT_HEAD)
+    assert ws == 4 * 6 * 8 * 112 * 2
+    assert f3r(algo=C.ALGO_SPLIT_HEAD, ws=WS, wsb=ws) == C.E_UNSUPPORTED
+    assert f3r(algo=C.ALGO_SPLIT_HEAD, ws=WS, wsb=ws, h_lo=1, h_hi=7) in (C.OK, C.E_NODEVICE)
+    assert f3r(algo=C.ALGO_SPLIT_HEAD, ws=None, h_lo=1, h_hi=7) == C.E_WORKSPACE
+    # empty outputs are no-ops once the region itself is well formed
+    assert f3r(x=None, y=None, D_out=0) == C.OK
+    assert f3r(x=None, y=None, D_out=0, d_hi=7) == C.E_INVAL
+
+
+def test_region_full_is_plain_validation():
+    """The full region goes through the same checks as conv3x3x3_fwd."""
+    full = dict(D_in=2, H_in=8, D_out=2, H_out=8, d_org=0, h_org=0, d_lo=0, d_hi=2, h_lo=0, h_hi=8)
+    for kw in (dict(), dict(x=None), dict(epilogue=-1), dict(C_in=20), dict(algo=C.ALGO_SIMT),
+               dict(algo=C.ALGO_SPLIT_HEAD), dict(algo=C.ALGO_MFMA, C_out=40), dict(y=A + 16)):
+        assert f3d(**{"algo": C.ALGO_FUSED_HEAD, **kw}) == f3r(**{**full, **kw}), kw

@@ -34,6 +34,7 @@ EXPORTS = [
     ("conv3x3_is_supported", _I, [_I] * 10),
     ("conv3x3_select_algo", _I, [_I] * 9),
     ("conv3x3x3_fwd", _I, [_P, _P, _P, _P] + [_I] * 11 + [_P, _SZ, _P]),
+    ("conv3x3x3_fwd_region", _I, [_P, _P, _P, _P] + [_I] * 18 + [_P, _SZ, _P]),
     ("conv3x3x3_select_algo", _I, [_I] * 10),
     ("conv3x3x3_is_supported", _I, [_I] * 11),
     ("conv3x3x3_workspace_bytes", _SZ, [_I] * 10),
@@ -184,6 +185,16 @@ def conv3x3x3_fwd(x, w_packed, bias, y, N, C_in, C_out, D, H, W, stride=1,
     return _check(library().conv3x3x3_fwd(_ptr(x), _ptr(w_packed), _ptr(bias), _ptr(y), N, C_in,
                                           C_out, D, H, W, stride, layout, dtype, epilogue, algo,
                                           _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def conv3x3x3_fwd_region(x, w_packed, bias, y, N, C_in, C_out, D_in, H_in, W, D_out, H_out,
+                         d_org, h_org, d_lo, d_hi, h_lo, h_hi, layout=LAYOUT_CHANNELS_LAST,
+                         dtype=DTYPE_BF16, epilogue=EPI_NONE, algo=ALGO_AUTO, workspace=None,
+                         workspace_bytes=0, stream=None):
+    return _check(library().conv3x3x3_fwd_region(
+        _ptr(x), _ptr(w_packed), _ptr(bias), _ptr(y), N, C_in, C_out, D_in, H_in, W, D_out, H_out,
+        d_org, h_org, d_lo, d_hi, h_lo, h_hi, layout, dtype, epilogue, algo, _ptr(workspace),
+        workspace_bytes, _stream(stream)))
 
 
 def conv_head_temporal(x, w_packed, g, N, C_in, C_out, D, H, W, dtype=DTYPE_BF16, stream=None):

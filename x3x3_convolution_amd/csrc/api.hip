@@ -139,11 +139,11 @@ int family_for(int algo, int C_in, int C_out, int H, int W) {
 size_t elem_bytes() { return 2; }
 
 hipError_t launch_head(const void *x, const void *w_packed, const void *bias, void *out, int N,
-                       int C_in, int C_out, int D, int H, int W, bool bf, bool fused, int epilogue,
-                       hipStream_t s) {
+                       int C_in, int C_out, int D, int H, int W, const cx::ConvRegion &rg, bool bf,
+                       bool fused, int epilogue, hipStream_t s) {
     cx::HeadGemmParams hp{};
     hp.x = x, hp.wp = w_packed, hp.bias = bias, hp.out = out;
-    hp.N = N, hp.C_in = C_in, hp.C_out = C_out, hp.D = D, hp.H = H, hp.W = W;
+    hp.N = N, hp.C_in = C_in, hp.C_out = C_out, hp.D = D, hp.H = H, hp.W = W, hp.rg = rg;
     hp.bf16 = bf, hp.fused = fused, hp.epilogue = epilogue;
     return cx::launch_head_gemm(hp, s);
 }
@@ -284,20 +284,56 @@ int conv3x3x3_pack_weights(const void *w_oidhw, void *w_packed, int N, int C_in,
     return ok();
 }
 
-int conv3x3x3_fwd(const void *x, const void *w_packed, const void *bias, void *y, int N,
-                  int C_in, int C_out, int D, int H, int W, int stride, int layout, int dtype,
-                  int epilogue, int algo, void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward pass of the 3D convolution over an input region (the full region for the plain
+// convolution).  D, H are the output extent; algorithm, packing and workspace follow from it.
+int fwd3d(const void *x, const void *w_packed, const void *bias, void *y, int N, int C_in,
+          int C_out, int D, int H, int W, const cx::ConvRegion &rg, int stride, int layout,
+          int dtype, int epilogue, int algo, void *workspace, size_t workspace_bytes,
+          void *stream) {
     if (epilogue < CONV_EPI_NONE || epilogue > CONV_EPI_CLAMP1)
         return fail(CONV_E_INVAL, "unknown epilogue %d", epilogue);
     const int a = select_3d(N, C_in, C_out, D, H, W, stride, layout, dtype, algo);
     if (a < 0) return a;
+    if (rg.D_in < 0 || rg.H_in < 0)
+        return fail(CONV_E_INVAL, "negative input extent (D_in=%d H_in=%d)", rg.D_in, rg.H_in);
+    if (rg.d_lo < 0 || rg.d_lo > rg.d_hi || rg.d_hi > rg.D_in || rg.h_lo < 0 || rg.h_lo > rg.h_hi ||
+        rg.h_hi > rg.H_in)
+        return fail(CONV_E_INVAL,
+                    "valid ranges must lie inside the input: 0 <= d_lo <= d_hi <= D_in and "
+                    "0 <= h_lo <= h_hi <= H_in (got d %d..%d of %d, h %d..%d of %d)",
+                    rg.d_lo, rg.d_hi, rg.D_in, rg.h_lo, rg.h_hi, rg.H_in);
     if (N == 0 || C_out == 0 || D == 0 || H == 0 || W == 0) return ok();
+    // output frame od reads input frames od + d_org - 1 .. od + d_org + 1
+    if (rg.d_lo >= rg.d_hi || rg.d_lo > rg.d_org + 1 || (long long)D + rg.d_org - 1 > rg.d_hi)
+        return fail(CONV_E_UNSUPPORTED,
+                    "every output frame must read at least one valid input frame (d_org=%d, valid "
+                    "frames %d..%d, D_out=%d)", rg.d_org, rg.d_lo, rg.d_hi, D);
+    const long long frame_in = (long long)rg.H_in * W * C_in * 2;
+    if ((long long)N * rg.D_in * rg.H_in * W >= (1ll << 31) / 8)
+        return fail(CONV_E_UNSUPPORTED, "input too large for one launch");
+    const bool head_algo = a == CONV_ALGO_SPLIT_HEAD || a == CONV_ALGO_FUSED_HEAD;
+    if (head_algo && (long long)rg.D_in * frame_in >= (1ll << 31))
+        return fail(CONV_E_UNSUPPORTED, "the head algorithms need one sample of x below 2 GiB");
+    const int family = family_for(a, C_in, C_out, H, W);
+    if (family == cx::IG_W32 && frame_in >= (1ll << 31))
+        return fail(CONV_E_UNSUPPORTED, "one input frame must stay below 2 GiB for this packing");
+    // the split head's stencil reads plane rows -1 and H as zeros
+    const bool row_edges_zero = (rg.h_org - 1 < rg.h_lo || rg.h_org - 1 >= rg.h_hi) &&
+                                ((long long)H + rg.h_org < rg.h_lo || (long long)H + rg.h_org >= rg.h_hi);
+    if (a == CONV_ALGO_SPLIT_HEAD && !row_edges_zero)
+        return fail(CONV_E_UNSUPPORTED,
+                    "the split head needs zero rows above and below the output band (use the fused head)");
     if (!x || !w_packed || !y) return fail(CONV_E_INVAL, "x, w_packed and y must be non-NULL");
     if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(y, 16))
         return fail(CONV_E_INVAL, "x, w_packed and y must be 16-byte aligned");
     if (bias && !aligned(bias, 2)) return fail(CONV_E_INVAL, "bias must be 2-byte aligned");
     const size_t P = (size_t)N * D * H * W;
-    const size_t xb = P * C_in * elem_bytes(), yb = P * C_out * elem_bytes();
+    const size_t xb = (size_t)N * rg.D_in * rg.H_in * W * C_in * elem_bytes();
+    const size_t yb = P * C_out * elem_bytes();
     if (overlaps(x, xb, y, yb)) return fail(CONV_E_INVAL, "x and y overlap (in-place is unsupported)");
     const size_t need = conv3x3x3_workspace_bytes(N, C_in, C_out, D, H, W, stride, layout, dtype, a);
     if (need > 0) {
@@ -313,26 +349,49 @@ int conv3x3x3_fwd(const void *x, const void *w_packed, const void *bias, void *y
     const bool bf = dtype == CONV_DTYPE_BF16;
     hipStream_t s = (hipStream_t)stream;
     if (a == CONV_ALGO_SPLIT_HEAD) {
-        hipError_t e = launch_head(x, w_packed, nullptr, workspace, N, C_in, C_out, D, H, W, bf, false, CONV_EPI_NONE, s);
+        hipError_t e = launch_head(x, w_packed, nullptr, workspace, N, C_in, C_out, D, H, W, rg, bf,
+                                   false, CONV_EPI_NONE, s);
         if (e != hipSuccess) return fail(CONV_E_LAUNCH, "split-head temporal launch failed: %s", hipGetErrorString(e));
         e = launch_stencil(workspace, bias, y, N, D, H, W, C_out, bf, epilogue, s);
         if (e != hipSuccess) return fail(CONV_E_LAUNCH, "split-head stencil launch failed: %s", hipGetErrorString(e));
         return ok();
     }
     if (a == CONV_ALGO_FUSED_HEAD) {
-        const hipError_t e = launch_head(x, w_packed, bias, y, N, C_in, C_out, D, H, W, bf, true, epilogue, s);
+        const hipError_t e = launch_head(x, w_packed, bias, y, N, C_in, C_out, D, H, W, rg, bf, true,
+                                         epilogue, s);
         if (e != hipSuccess) return fail(CONV_E_LAUNCH, "fused head launch failed: %s", hipGetErrorString(e));
         return ok();
     }
-    const cx::IgemmPlan pl = cx::plan_igemm(family_for(a, C_in, C_out, H, W), N, C_in, C_out, D, H, W);
+    const cx::IgemmPlan pl = cx::plan_igemm(family, N, C_in, C_out, D, H, W);
     cx::IgemmParams ip{};
     ip.x = x, ip.wp = w_packed, ip.bias = bias, ip.y = y;
     ip.partial = static_cast<float *>(pl.splits > 1 ? workspace : nullptr);
-    ip.N = N, ip.C_in = C_in, ip.D = D, ip.H = H, ip.W = W;
+    ip.N = N, ip.C_in = C_in, ip.D = D, ip.H = H, ip.W = W, ip.rg = rg;
     ip.Cy = C_out, ip.bf16 = bf, ip.epilogue = epilogue;
     const hipError_t e = cx::launch_igemm3d(pl, ip, s);
     if (e != hipSuccess) return fail(CONV_E_LAUNCH, "MFMA 3D launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int conv3x3x3_fwd(const void *x, const void *w_packed, const void *bias, void *y, int N,
+                  int C_in, int C_out, int D, int H, int W, int stride, int layout, int dtype,
+                  int epilogue, int algo, void *workspace, size_t workspace_bytes, void *stream) {
+    return fwd3d(x, w_packed, bias, y, N, C_in, C_out, D, H, W, cx::full_region(D, H), stride,
+                 layout, dtype, epilogue, algo, workspace, workspace_bytes, stream);
+}
+
+int conv3x3x3_fwd_region(const void *x, const void *w_packed, const void *bias, void *y, int N,
+                         int C_in, int C_out, int D_in, int H_in, int W, int D_out, int H_out,
+                         int d_org, int h_org, int d_lo, int d_hi, int h_lo, int h_hi, int layout,
+                         int dtype, int epilogue, int algo, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+    return fwd3d(x, w_packed, bias, y, N, C_in, C_out, D_out, H_out, W,
+                 cx::ConvRegion{D_in, H_in, d_org, h_org, d_lo, d_hi, h_lo, h_hi}, 1, layout, dtype,
+                 epilogue, algo, workspace, workspace_bytes, stream);
 }
 
 int conv_head_temporal(const void *x, const void *w_packed, void *g, int N, int C_in, int C_out,
@@ -350,7 +409,8 @@ int conv_head_temporal(const void *x, const void *w_packed, void *g, int N, int 
     int st = device_present();
     if (st) return st;
     const hipError_t e = launch_head(x, w_packed, nullptr, g, N, C_in, C_out, D, H, W,
-                                     dtype == CONV_DTYPE_BF16, false, CONV_EPI_NONE, (hipStream_t)stream);
+                                     cx::full_region(D, H), dtype == CONV_DTYPE_BF16, false,
+                                     CONV_EPI_NONE, (hipStream_t)stream);
     if (e != hipSuccess) return fail(CONV_E_LAUNCH, "head temporal launch failed: %s", hipGetErrorString(e));
     return ok();
 }

@@ -207,7 +207,9 @@ struct HeadGemmKArgs {
     const u16 *wp;
     const u16 *bias;
     u16 *out;          // the plane (PLANE) or y (FUSED)
-    int N, C_in, C_out, D, H, W;
+    int N, C_in, C_out, D, H, W;   // D, H: output extent
+    int D_in, H_in, d_org, h_org;  // input region (see ConvRegion)
+    int d_lo, d_hi, h_lo, h_hi;
     int nchunks;       // 32-channel stages per Z row, even (the padding reads zeros)
     int rows_per_band, bands, strips, strip_out, fgroups;
     uint32_t sample_bytes;  // bytes of one sample of x (buffer-resource range)
@@ -260,7 +262,8 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
     const int nstages = nsteps * nch;
 
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(a.x + (size_t)n * a.D * HW * a.C_in), (short)0, (int)a.sample_bytes, 0x00020000);
+        (void *)(a.x + (size_t)n * a.D_in * a.H_in * a.W * a.C_in), (short)0, (int)a.sample_bytes,
+        0x00020000);
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
         (void *)a.wp, (short)0, (int)a.wp_bytes, 0x00020000);
     // FUSED: one sample of y
@@ -287,16 +290,17 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
                 wr, (lds_void *)&abuf[piece], 16,
                 (uint32_t)((c * kHeadChunkPieces + piece + lane) * 16), 0, 0, 0);
         }
-        const int row = zrow0 + st;
-        const bool rok = (unsigned)row < (unsigned)a.H;
+        // Z row zr reads input row zr + h_org; window frame i is input frame f0 - 1 + i + d_org
+        const int row = zrow0 + st + a.h_org;
+        const bool rok = row >= a.h_lo && row < a.h_hi;
         const bool cok = 32 * c + 8 * bpiece < a.C_in;
 #pragma unroll
         for (int t = 0; t < kCopyB; ++t) {
             const int k = wave + 4 * t;
-            const int f = f0 - 1 + (k >> 3);
+            const int f = f0 - 1 + (k >> 3) + a.d_org;
             const int dw = 64 * (k & 1) + ((k >> 1) & 3);   // column of lane 0
-            const uint32_t up = rok && (unsigned)f < (unsigned)a.D
-                                    ? (uint32_t)((((size_t)f * a.H + row) * a.W * a.C_in + 32 * c) * 2u)
+            const uint32_t up = rok && f >= a.d_lo && f < a.d_hi
+                                    ? (uint32_t)((((size_t)f * a.H_in + row) * a.W * a.C_in + 32 * c) * 2u)
                                     : kOff;
             const bool ok = cok && (unsigned)(bw + dw) < (unsigned)a.W;
             const uint32_t off =
@@ -568,6 +572,8 @@ hipError_t launch_head_gemm(const HeadGemmParams &p, hipStream_t stream) {
     a.bias = static_cast<const u16 *>(p.bias);
     a.out = static_cast<u16 *>(p.out);
     a.N = p.N, a.C_in = p.C_in, a.C_out = p.C_out, a.D = p.D, a.H = p.H, a.W = p.W;
+    a.D_in = p.rg.D_in, a.H_in = p.rg.H_in, a.d_org = p.rg.d_org, a.h_org = p.rg.h_org;
+    a.d_lo = p.rg.d_lo, a.d_hi = p.rg.d_hi, a.h_lo = p.rg.h_lo, a.h_hi = p.rg.h_hi;
     const int packed_chunks = (p.C_in + 31) / 32;
     a.nchunks = (packed_chunks + 1) & ~1;   // the kernel runs stages in pairs
     a.strip_out = p.fused ? kWavePos - 2 : kWavePos;
@@ -588,7 +594,7 @@ hipError_t launch_head_gemm(const HeadGemmParams &p, hipStream_t stream) {
     }
     a.rows_per_band = (p.H + best_bands - 1) / best_bands;
     a.bands = (p.H + a.rows_per_band - 1) / a.rows_per_band;
-    a.sample_bytes = (uint32_t)((size_t)p.D * p.H * p.W * p.C_in * 2);
+    a.sample_bytes = (uint32_t)((size_t)p.rg.D_in * p.rg.H_in * p.W * p.C_in * 2);
     a.wp_bytes = (uint32_t)((size_t)packed_chunks * kHeadChunkPieces * 16);
     const long long wgs = cols * a.bands;
     a.total_wg = (uint32_t)wgs;

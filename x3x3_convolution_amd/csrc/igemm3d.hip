@@ -40,7 +40,9 @@ struct IgemmKArgs {
     const u16 *bias;
     u16 *y;
     float *partial;
-    int N, C_in, D, H, W;
+    int N, C_in, D, H, W;          // D, H: output extent
+    int D_in, H_in, d_org, h_org;  // input region (see ConvRegion)
+    int d_lo, d_hi, h_lo, h_hi;
     int Mrows, Mpad, Cy;
     int nchunks, chunks_per_split, splits;
     int tiles_h, tiles_w, mtiles;
@@ -125,9 +127,11 @@ __global__ __launch_bounds__(256, 2) void igemm3d_kernel(IgemmKArgs a) {
     const int oh0 = th * TH, ow0 = tw * TW;
     const int c_begin = split * a.chunks_per_split;
     const int c_end = min(a.nchunks, c_begin + a.chunks_per_split);
-    const int kd_lo = od == 0 ? 1 : 0;            // live temporal taps: frame od-1+kd in [0, D)
-    const int kd_hi = od == a.D - 1 ? 1 : 2;
-    const int nkd = kd_hi - kd_lo + 1;
+    // live temporal taps: input frame fi0 + kd inside [d_lo, d_hi)
+    const int fi0 = od + a.d_org - 1;
+    const int kd_lo = max(0, a.d_lo - fi0);
+    const int kd_hi = min(2, a.d_hi - 1 - fi0);
+    const int nkd = max(0, kd_hi - kd_lo + 1);
     const int nst = (c_end - c_begin) * nkd;
 
     f32x4_t acc[MB][NBW];
@@ -138,12 +142,12 @@ __global__ __launch_bounds__(256, 2) void igemm3d_kernel(IgemmKArgs a) {
 
     const int mrow_lane = mt * BM + wm * MB * 16 + (lane & 15);
     const int kofs = (lane >> 4) * 8;
-    const size_t frame_elems = (size_t)a.H * a.W * a.C_in;
+    const size_t frame_elems = (size_t)a.H_in * a.W * a.C_in;
 
     uint4 stg[PPT];
     auto fetch = [&](int s) {
         const int cc = c_begin + s / nkd, kd = kd_lo + s % nkd;
-        const u16 *base = a.x + ((size_t)n * a.D + (od - 1 + kd)) * frame_elems + cc * 32;
+        const u16 *base = a.x + ((size_t)n * a.D_in + (fi0 + kd)) * frame_elems + cc * 32;
 #pragma unroll
         for (int j = 0; j < PPT; ++j) {
             const int i = tid + j * 256;
@@ -151,8 +155,8 @@ __global__ __launch_bounds__(256, 2) void igemm3d_kernel(IgemmKArgs a) {
             if (PIECES % 256 == 0 || i < PIECES) {
                 const int q = i & 3, pos = i >> 2;
                 const int wh = pos / WW, ww = pos - wh * WW;
-                const int h = oh0 - 1 + wh, w = ow0 - 1 + ww;
-                if ((unsigned)h < (unsigned)a.H && (unsigned)w < (unsigned)a.W &&
+                const int h = oh0 - 1 + wh + a.h_org, w = ow0 - 1 + ww;
+                if (h >= a.h_lo && h < a.h_hi && (unsigned)w < (unsigned)a.W &&
                     cc * 32 + q * 8 < a.C_in)
                     v = *reinterpret_cast<const uint4 *>(base + ((size_t)h * a.W + w) * a.C_in + q * 8);
             }
@@ -343,14 +347,16 @@ __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
     const int oh0 = th * G::TH, ow0 = tw * G::TW;
     const int c_begin = split * a.chunks_per_split;
     const int c_end = min(a.nchunks, c_begin + a.chunks_per_split);
-    const int kd_lo = od == 0 ? 1 : 0;            // live temporal taps: frame od-1+kd in [0, D)
-    const int kd_hi = od == a.D - 1 ? 1 : 2;
-    const int nkd = kd_hi - kd_lo + 1;
+    // live temporal taps: input frame fi0 + kd inside [d_lo, d_hi)
+    const int fi0 = od + a.d_org - 1;
+    const int kd_lo = max(0, a.d_lo - fi0);
+    const int kd_hi = min(2, a.d_hi - 1 - fi0);
+    const int nkd = max(0, kd_hi - kd_lo + 1);
     const int nst = max(0, (c_end - c_begin) * nkd);
     const int mbase = mt * 256 + wave * 64;       // this wave's first GEMM row
     const bool mlive = mbase < a.Mrows;           // (all-padding waves compute zeros, store none)
 
-    const size_t frame_elems = (size_t)a.H * a.W * a.C_in;
+    const size_t frame_elems = (size_t)a.H_in * a.W * a.C_in;
     const uint32_t frame_bytes = (uint32_t)(frame_elems * 2);
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
         (void *)a.wp, (short)0, (int)(a.wp_bytes), 0x00020000);
@@ -367,7 +373,7 @@ __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
         int cc, kd;
         stage_coords(s, cc, kd);
         const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(a.x + ((size_t)n * a.D + (od - 1 + kd)) * frame_elems), (short)0,
+            (void *)(a.x + ((size_t)n * a.D_in + (fi0 + kd)) * frame_elems), (short)0,
             (int)frame_bytes, 0x00020000);
 #pragma unroll
         for (int t = 0; t < G::CopiesPerWave; ++t) {
@@ -376,9 +382,9 @@ __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
             const int pos = 16 * k + (lane >> 2);
             const int wh = pos / G::RowPos, ww = pos - wh * G::RowPos;
             const int piece = (lane & 3) ^ ((ww >> 2) & 3);
-            const int h = oh0 - 1 + wh, w = ow0 - 1 + ww;
-            const bool ok = ww < G::WW && pos < G::Pos && (unsigned)h < (unsigned)a.H && (unsigned)w < (unsigned)a.W &&
-                            cc * 32 + 8 * piece < a.C_in;
+            const int h = oh0 - 1 + wh + a.h_org, w = ow0 - 1 + ww;
+            const bool ok = ww < G::WW && pos < G::Pos && h >= a.h_lo && h < a.h_hi &&
+                            (unsigned)w < (unsigned)a.W && cc * 32 + 8 * piece < a.C_in;
             const uint32_t off = ok ? (uint32_t)(((h * a.W + w) * a.C_in + cc * 32 + 8 * piece) * 2) : 0xFFFFFFFFu;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)&dst[k * 64], 16, off, 0, 0, 0);
         }
@@ -736,6 +742,8 @@ hipError_t launch_igemm3d(const IgemmPlan &pl, const IgemmParams &p, hipStream_t
     ka.y = static_cast<u16 *>(p.y);
     ka.partial = p.partial;
     ka.N = p.N, ka.C_in = p.C_in, ka.D = p.D, ka.H = p.H, ka.W = p.W;
+    ka.D_in = p.rg.D_in, ka.H_in = p.rg.H_in, ka.d_org = p.rg.d_org, ka.h_org = p.rg.h_org;
+    ka.d_lo = p.rg.d_lo, ka.d_hi = p.rg.d_hi, ka.h_lo = p.rg.h_lo, ka.h_hi = p.rg.h_hi;
     ka.Mrows = pl.Mrows, ka.Mpad = pl.Mpad, ka.Cy = p.Cy;
     ka.nchunks = pl.nchunks, ka.chunks_per_split = pl.chunks_per_split, ka.splits = pl.splits;
     ka.tiles_h = pl.tiles_h, ka.tiles_w = pl.tiles_w, ka.mtiles = pl.mtiles;

@@ -22,6 +22,20 @@ hipError_t launch_simt2d(const Simt2dParams &p, hipStream_t stream);
 bool mfma2d_supported(int C_in, int C_out, int H, int W, int stride);
 hipError_t launch_mfma2d(const Simt2dParams &p, hipStream_t stream);
 
+// ---- 3D input regions ------------------------------------------------------------------------
+// Which input a 3D output reads: output frame od / row oh takes its temporal / vertical taps from
+// input frames od + d_org - 1 + kd and rows oh + h_org - 1 + ky of x (stored extent D_in x H_in
+// x W); only input frames [d_lo, d_hi) and rows [h_lo, h_hi) hold data, every other one reads as
+// zero.  The plain convolution is the full region: D_in = D, H_in = H, origins 0, valid ranges
+// the whole tensor.  Row bands with halo rows, frame chunks and causal temporal padding (with or
+// without the previous chunk's frames) are other regions of the same sum.
+struct ConvRegion {
+    int D_in, H_in;
+    int d_org, h_org;
+    int d_lo, d_hi, h_lo, h_hi;
+};
+inline ConvRegion full_region(int D, int H) { return ConvRegion{D, H, 0, 0, 0, D, 0, H}; }
+
 // ---- 3D MFMA implicit GEMM (NDHWC) ---------------------------------------------------------
 // Tile families; the host picks one per request.
 enum IgemmFamily {
@@ -57,7 +71,8 @@ struct IgemmParams {
     const void *x, *wp, *bias;
     void *y;           // output (C_out channels) or the split head's plane (112 channels)
     float *partial;    // split-K partials (splits > 1)
-    int N, C_in, D, H, W;
+    int N, C_in, D, H, W;   // D, H: output extent
+    ConvRegion rg;     // input region (full_region(D, H) for the plain convolution)
     int Cy;            // channel stride of y
     bool bf16;
     int epilogue;
@@ -102,7 +117,8 @@ __host__ __device__ inline void head_row_role(int m, int &tap, int &co) {
 struct HeadGemmParams {
     const void *x, *wp, *bias;
     void *out;         // the 112-channel plane (fused = false) or y (fused = true)
-    int N, C_in, C_out, D, H, W;
+    int N, C_in, C_out, D, H, W;   // D, H: output extent
+    ConvRegion rg;     // input region (full_region(D, H) for the plain convolution)
     bool bf16, fused;
     int epilogue;      // fused only
 };

@@ -78,3 +78,33 @@ class Conv3x3x3:
         C.conv3x3x3_fwd(x, self.w_packed, self.bias, y, N, Ci, Co, D, H, W, s, lay, dt, self.epi,
                         self.algo, self.workspace, self.ws_bytes, stream)
         return y
+
+    def region(self, x, D_in, H_in, d_org, h_org, d_lo, d_hi, h_lo, h_hi, y=None, stream=None):
+        """The convolution over an input region of x (N, D_in, H_in, W, C_in) into an output of
+        this plan's extent (N, D, H, W, C_out): conv3x3x3_fwd_region."""
+        if y is None:
+            y = torch.empty(self.out_shape(), dtype=self.torch_dtype, device=x.device)
+        N, Ci, Co, D, H, W, s, lay, dt = self._shape
+        C.conv3x3x3_fwd_region(x, self.w_packed, self.bias, y, N, Ci, Co, D_in, H_in, W, D, H,
+                               d_org, h_org, d_lo, d_hi, h_lo, h_hi, lay, dt, self.epi, self.algo,
+                               self.workspace, self.ws_bytes, stream)
+        return y
+
+
+def band_rows(lo, rows, halo, H_global):
+    """Region rows of an output band [lo, lo + rows) of a global height H_global whose input
+    holds global rows lo - halo .. lo + rows + halo - 1 (rows outside the global height may
+    hold anything): (H_in, h_org, h_lo, h_hi) for conv3x3x3_fwd_region."""
+    H_in = rows + 2 * halo
+    return H_in, halo, max(0, halo - lo), min(H_in, H_global + halo - lo)
+
+
+def causal_frames(D_out, cached):
+    """Region frames of a causal temporal pass (output frame t reads input frames t-2 .. t) over
+    D_out new frames, with `cached` (0..2) frames of the previous chunk stored in front of them
+    and zeros in place of the rest: (D_in, d_org, d_lo, d_hi) for conv3x3x3_fwd_region."""
+    if not 0 <= cached <= 2:
+        raise ValueError("cached must be 0, 1 or 2")
+    D_in = D_out + cached
+    return D_in, cached - 1, 0, D_in
+
