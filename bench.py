@@ -71,6 +71,11 @@ def parse():
     ap.add_argument("--algo", default="auto", choices=["auto", "mfma", "split", "fused"],
                     help="auto: time every head algorithm and report AUTO's choice; otherwise "
                          "time only the named one")
+    ap.add_argument("--region", default="none", choices=["none", "band8", "causal"],
+                    help="3D workloads only: time a region pass instead of the plain one -- "
+                         "band8: the middle eighth of the rows with a one-row halo each side "
+                         "(one GPU's share when the rows are split over eight); causal: every "
+                         "frame with causal temporal padding and two cached frames in front")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (used for profiler runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -307,6 +312,71 @@ def run_other(args, wl, stream):
     return wall_ms, roof
 
 
+def region_of(kind, D, H):
+    """(D_in, H_in, d_org, h_org, d_lo, d_hi, h_lo, h_hi, D_out, H_out, band_lo) of a region
+    pass over a workload of D frames and H rows."""
+    from x3x3_convolution_amd.plan import band_rows, causal_frames
+    if kind == "band8":
+        rows = H // 8
+        lo = 3 * rows
+        H_in, h_org, h_lo, h_hi = band_rows(lo, rows, 1, H)
+        return (D, H_in, 0, h_org, 0, D, h_lo, h_hi, D, rows, lo)
+    D_in, d_org, d_lo, d_hi = causal_frames(D, 2)
+    return (D_in, H, d_org, 0, d_lo, d_hi, 0, H, D, H, 0)
+
+
+def run_region(args, wl, stream):
+    """A region pass of a 3D workload (AUTO algorithm), timed like the plain pass."""
+    import torch
+
+    import synthetic_inputs as si
+    from x3x3_convolution_amd import conv as C
+    from x3x3_convolution_amd.plan import Conv3x3x3
+
+    D_in, H_in, d_org, h_org, d_lo, d_hi, h_lo, h_hi, D, H, lo = region_of(args.region, wl.D, wl.H)
+    _, w, b = si.make_inputs(wl, device="cpu")
+    w, b = w.cuda(), b.cuda()
+    g = torch.Generator("cpu").manual_seed(si.SEED_BASE + 7)
+    x = torch.randn((wl.N, D_in, H_in, wl.W, wl.C_in), generator=g).to(wl.torch_dtype).cuda()
+    op = Conv3x3x3(w, b, wl.N, D, H, wl.W, epilogue=wl.epilogue)
+    y = torch.empty(op.out_shape(), dtype=wl.torch_dtype, device="cuda")
+    kname = {C.ALGO_FUSED_HEAD: "head_fused", C.ALGO_SPLIT_HEAD: "head_split"}.get(op.algo, "igemm3d")
+
+    def live(n_out, org, lo_, hi_):
+        return sum(sum(1 for t in range(3) if lo_ <= o + org - 1 + t < hi_) for o in range(n_out))
+    flop = (2.0 * wl.C_in * wl.C_out * wl.N * live(D, d_org, d_lo, d_hi) * live(H, h_org, h_lo, h_hi)
+            * live_taps(wl.W))
+    nbytes = (x.numel() + y.numel() + w.numel() + b.numel()) * 2
+
+    def call():
+        op.region(x, D_in, H_in, d_org, h_org, d_lo, d_hi, h_lo, h_hi, y=y, stream=stream)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    tm = Timer(torch.cuda.current_stream())
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        s0 = tm.start()
+        call()
+        tm.stop(kname, s0)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    kms = tm.summary()[kname]
+    tflops, gbs = flop / (kms * 1e-3) / 1e12, nbytes / (kms * 1e-3) / 1e9
+    if kname == "igemm3d":
+        bound, ach, peak, unit = "mfma", tflops, MFMA_BF16_PEAK_TFS, "TFLOP/s"
+    else:
+        bound, ach, peak, unit = "hbm", gbs, HBM_PEAK_GBS, "GB/s"
+    roof = dict(kernel=kname, bound=bound, achieved=ach, peak=peak, unit=unit, frac=ach / peak,
+                hbm_gbs=gbs, mfma_tflops=tflops, mfma_frac=tflops / MFMA_BF16_PEAK_TFS,
+                algorithmic_flop=flop, algorithmic_bytes=nbytes, avg_launch_ms=kms,
+                traffic=None)
+    cfg = dict(workload="%s %s" % (wl.name, args.region), N=wl.N, C_in=wl.C_in, C_out=wl.C_out,
+               D_out=D, H_out=H, W=wl.W, D_in=D_in, H_in=H_in, d_org=d_org, h_org=h_org,
+               band_lo=lo, algo=kname)
+    return wall_ms, roof, cfg
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -330,7 +400,15 @@ def main():
     line = dict(metric=METRIC, n_gpus=1, steps=args.steps, warmup=args.warmup,
                 higher_is_better=False, scaling="weak", vs_baseline=None, dtype=wl.dtype,
                 data="synthetic (seeded; no trained weights or real activations)")
-    if wl.name == "c3":
+    if args.region != "none":
+        if wl.kind != "3d":
+            print("--region applies to the 3D workloads", file=sys.stderr)
+            sys.exit(2)
+        wall_ms, roof, cfg = run_region(args, wl, stream)
+        line.update(value=round(wall_ms, 4), unit="ms", ms_per_step=round(wall_ms, 4), config=cfg,
+                    roofline={k: (round(v, 6) if isinstance(v, float) else v)
+                              for k, v in roof.items()})
+    elif wl.name == "c3":
         chosen, pass_ms, roof, extra, tensors = run_head(args, wl, stream)
         line.update(value=round(pass_ms, 4), unit="ms", ms_per_step=round(pass_ms, 4),
                     config=dict(workload="wan2.2 output head 3x3x3 256->12, x [1,16,352,624,256] "

@@ -175,7 +175,8 @@ __global__ __launch_bounds__(256) void head_stencil_kernel(StencilKArgs a) {
 // ahead, and a single barrier per stage, placed before the stage's last step, publishes them to
 // every wave (each wave first waits for its own copies) and frees the buffers of stage g (every
 // wave has its last fragments of stage g in registers): the copies of stage g+2 go out right after
-// it, and the first fragments of stage g+1 are read while the last step's MFMAs run.
+// it, interleaved one by one with the last step's MFMAs, and the first fragments of stage g+1 are
+// read while those MFMAs run.  The copy offsets are formed without branches.
 //
 // PLANE mode stores Z, rounded to the storage type, as the 112-channel plane of the split head.
 // FUSED mode applies the nine-tap stencil in registers: the horizontal taps combine neighbouring
@@ -274,15 +275,24 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
     // B window copies: this wave issues copies k = wave + 4*t; lane i of copy k fills slot
     // 64*k + i = ((frame*4 + nb)*32 + column j)*4 + piece', with frame = k/8, nb = (k/2) % 4,
     // j = 16*(k%2) + i/4 and piece' = piece ^ ((j/4) % 4) -- the piece of lane i is therefore
-    // (i%4) ^ ((i/16) % 4) in every copy, and its column w0 + 4*(i/4) plus a part that depends
-    // on k alone.
+    // (i%4) ^ ((i/16) % 4) in every copy.  With k = wave + 4*t, copy t fills window frame t/2
+    // from column w0 + 4*(i/4) + dw, dw = 64*(wave%2) + wave/2 + 2*(t%2): the wave's twelve
+    // copies are six frames at two column offsets, and a lane's part of the source offset is one
+    // of two values fixed for the whole kernel (kOff where the column is outside the tensor).
     const int bpiece = (lane & 3) ^ ((lane >> 4) & 3);
-    const int bw = w0 + 4 * (lane >> 2);
-    const uint32_t bcolpart = (uint32_t)(bw * a.C_in + 8 * bpiece) * 2u;
-    // Copies of stage g (Z row g / nch, channel chunk g % nch) into one buffer pair.  Weight
-    // chunks past the packed ones (the even padding) lie past the resource range and copy zeros.
-    auto copy_stage = [&](int g, uint4 *abuf, uint4 *bbuf) {
-        const int st = g / nch, c = g - st * nch;
+    uint32_t bcol[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+        const int col = w0 + 4 * (lane >> 2) + 64 * (wave & 1) + (wave >> 1) + 2 * par;
+        bcol[par] = (unsigned)col < (unsigned)a.W ? (uint32_t)((col * a.C_in + 8 * bpiece) * 2) : kOff;
+    }
+    const uint32_t frame_bytes = (uint32_t)a.H_in * (uint32_t)a.W * (uint32_t)a.C_in * 2u;
+    const uint32_t row_bytes = (uint32_t)a.W * (uint32_t)a.C_in * 2u;
+    const int fw0 = f0 - 1 + a.d_org;   // input frame of window frame 0
+    // Copies of stage (Z row st, channel chunk c) into one buffer pair.  Weight chunks past the
+    // packed ones (the even padding) lie past the resource range and copy zeros.  Every offset
+    // is formed without branches: an invalid part is all ones, which the saturating add keeps.
+    auto copy_stage = [&](int st, int c, uint4 *abuf, uint4 *bbuf) __attribute__((always_inline)) {
 #pragma unroll
         for (int q = 0; q < kCopyA; ++q) {
             const int piece = (wave * kCopyA + q) * 64;
@@ -290,21 +300,19 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
                 wr, (lds_void *)&abuf[piece], 16,
                 (uint32_t)((c * kHeadChunkPieces + piece + lane) * 16), 0, 0, 0);
         }
-        // Z row zr reads input row zr + h_org; window frame i is input frame f0 - 1 + i + d_org
+        // Z row zr reads input row zr + h_org; window frame i is input frame fw0 + i
         const int row = zrow0 + st + a.h_org;
-        const bool rok = row >= a.h_lo && row < a.h_hi;
-        const bool cok = 32 * c + 8 * bpiece < a.C_in;
+        const uint32_t rok = (uint32_t)((row >= a.h_lo) & (row < a.h_hi));
+        const uint32_t rbase = (uint32_t)row * row_bytes + (uint32_t)(64 * c);
+        const uint32_t cmask = 0u - (uint32_t)(32 * c + 8 * bpiece >= a.C_in);   // ~0: no channels
+        const uint32_t colv[2] = {bcol[0] | cmask, bcol[1] | cmask};
 #pragma unroll
         for (int t = 0; t < kCopyB; ++t) {
             const int k = wave + 4 * t;
-            const int f = f0 - 1 + (k >> 3) + a.d_org;
-            const int dw = 64 * (k & 1) + ((k >> 1) & 3);   // column of lane 0
-            const uint32_t up = rok && f >= a.d_lo && f < a.d_hi
-                                    ? (uint32_t)((((size_t)f * a.H_in + row) * a.W * a.C_in + 32 * c) * 2u)
-                                    : kOff;
-            const bool ok = cok && (unsigned)(bw + dw) < (unsigned)a.W;
-            const uint32_t off =
-                ok ? __builtin_elementwise_add_sat(bcolpart + (uint32_t)(dw * a.C_in * 2), up) : kOff;
+            const int f = fw0 + (t >> 1);
+            const uint32_t fok = rok & (uint32_t)((f >= a.d_lo) & (f < a.d_hi));
+            const uint32_t up = ((uint32_t)f * frame_bytes + rbase) | (fok - 1u);
+            const uint32_t off = __builtin_elementwise_add_sat(colv[t & 1], up);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)&bbuf[k * 64], 16, off, 0, 0, 0);
         }
     };
@@ -347,9 +355,9 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
         for (int c = 0; c < kHalfCo; ++c) cA[nb][c] = cB[nb][c] = 0.f;
 
     // ---- prologue: stages 0 and 1 copied, stage 0 complete and published ----
-    copy_stage(0, As0, Bs0);
+    copy_stage(0, 0, As0, Bs0);
     if (nstages > 1) {
-        copy_stage(1, As1, Bs1);
+        copy_stage(0, 1, As1, Bs1);   // (nch is even, so stage 1 is chunk 1 of Z row 0)
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(kCopyA + kCopyB));
     } else {
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -365,7 +373,9 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
         for (int c2 = 0; c2 < nch; c2 += 2) {
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
-                const int g = st * nch + c2 + half;
+                // the stage two ahead: chunk c2 + half + 2 of this Z row, or of the next one
+                const int wrap = c2 + half + 2 >= nch;
+                const int st2 = st + wrap, c_2 = c2 + half + 2 - (wrap ? nch : 0);
                 uint4 *const ca = half == 0 ? As0 : As1;
                 uint4 *const cbb = half == 0 ? Bs0 : Bs1;
                 uint4 *const na = half == 0 ? As1 : As0;
@@ -376,14 +386,14 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
                     if (u + 1 < kSteps) {
                         read_frags(ca, cbb, u + 1, af[cur ^ 1], bf[cur ^ 1]);
                     } else {
-                        // Publish stage g+1 (its copies were issued one stage ago) and release
-                        // stage g: this wave's last fragments of stage g are in registers once
-                        // its reads are complete.  (Past the last stage the reads below are of a
-                        // stale buffer and never used; they keep every path's waits the same.)
+                        // Publish the next stage (its copies were issued one stage ago) and
+                        // release this one: this wave's last fragments of it are in registers
+                        // once its reads are complete.  (Past the last stage the reads below are
+                        // of a stale buffer and never used; they keep every path's waits the
+                        // same.)
                         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
                         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
                         wg_barrier();
-                        if (g + 2 < nstages) copy_stage(g + 2, ca, cbb);
                         read_frags(na, nbb, 0, af[cur ^ 1], bf[cur ^ 1]);
                     }
                     __builtin_amdgcn_sched_barrier(0);
@@ -400,6 +410,18 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
 #pragma unroll
                             for (int nb = 0; nb < kNB; ++nb)
                                 acc[mb][nb] = E::mfma32x32x16(af[cur][mb], bf[cur][nb], acc[mb][nb]);
+                    }
+                    if (u + 1 == kSteps) {
+                        // The copies of the stage two ahead go into this stage's buffers, one
+                        // between each two of this step's MFMAs, so they issue while the matrix
+                        // pipe runs.  Past the last stage they still run (in bounds: rows and
+                        // chunks that do not exist copy zeros) and nothing reads them.
+                        copy_stage(st2, c_2, ca, cbb);
+#pragma unroll
+                        for (int i = 0; i < kMB * kNB; ++i) {
+                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one buffer load
+                        }
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
