@@ -21,6 +21,9 @@ What pins each function (the tests under ``tests/test_oracle_*.py``):
   im2col-times-matrix form; hand-worked examples stored under tests/golden/.
 * ``head_split``: without rounding it equals ``conv3d`` (the split's algebra); with rounding the
   intermediate plane equals the encoded-then-decoded unrounded plane.
+* ``video_rgb8`` (``video.py``, numpy): the head output as 8-bit RGB pixels; quantisation against
+  exact rational arithmetic over every bf16 value, the pixel shuffle against
+  torch.nn.functional.pixel_shuffle.
 """
 from __future__ import annotations
 
@@ -278,3 +281,6 @@ def conv3d_points(*a, **k):
 
 def head_split(*a, **k):
     return default().head_split(*a, **k)
+
+
+from .video import pixel_shuffle2_nhwc, quantize_u8, video_rgb8  # noqa: E402,F401
