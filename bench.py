@@ -34,6 +34,7 @@ KERNEL_SOURCES = {             # dominant-kernel name -> the source file it is b
     "head_fused": "x3x3_convolution_amd/csrc/head.hip",
     "simt2d": "x3x3_convolution_amd/csrc/simt2d.hip",
     "mfma2d": "x3x3_convolution_amd/csrc/mfma2d.hip",
+    "video_rgb8": "x3x3_convolution_amd/csrc/video.hip",
 }
 
 
@@ -217,6 +218,28 @@ def run_head(args, wl, stream):
                     traffic=traffic_from_profiles("igemm3d", wl.name, "mfma"))
     chosen = {C.ALGO_SPLIT_HEAD: "split", C.ALGO_FUSED_HEAD: "fused"}.get(auto, "mfma")
     pass_ms = results[chosen]["ms_per_pass"]
+
+    # the step after the pass: the 12-channel output as 704x1248 RGB bytes (timed on its own,
+    # not part of the pass's value)
+    video = None
+    if wl.C_out == 12 and args.algo == "auto":
+        rgb = torch.empty((wl.N, wl.D, 2 * wl.H, 2 * wl.W, 3), dtype=torch.uint8, device="cuda")
+        for _ in range(args.warmup):
+            C.conv_video_rgb8(y, rgb, wl.N, wl.D, wl.H, wl.W, 12, C.DTYPE_BF16, stream)
+        torch.cuda.synchronize()
+        tm = Timer(torch.cuda.current_stream())
+        for _ in range(args.steps):
+            s0 = tm.start()
+            C.conv_video_rgb8(y, rgb, wl.N, wl.D, wl.H, wl.W, 12, C.DTYPE_BF16, stream)
+            tm.stop("video_rgb8", s0)
+        torch.cuda.synchronize()
+        vms = tm.summary()["video_rgb8"]
+        vbytes = yb + rgb.numel()
+        video = dict(kernel="video_rgb8_kernel", avg_launch_ms=round(vms, 5),
+                     algorithmic_bytes=vbytes, gbs=round(vbytes / (vms * 1e-3) / 1e9, 1),
+                     hbm_frac=round(vbytes / (vms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     traffic=traffic_from_profiles("video_rgb8", wl.name, "auto"))
+        del rgb
     extra = dict(
         pass_tflops=flop_live / (pass_ms * 1e-3) / 1e12,
         pass_gbs=((xb + 2 * gb + yb + wb + bb) if chosen == "split" else (xb + yb + wb + bb))
@@ -224,6 +247,8 @@ def run_head(args, wl, stream):
         algos={k: dict(ms_per_pass=round(v["ms_per_pass"], 4),
                        kernel_ms={kk: round(vv, 4) for kk, vv in v["kernel_ms"].items()})
                for k, v in results.items()})
+    if video is not None:
+        extra["video_step"] = video
     return chosen, pass_ms, roof, extra, (x, w, b)
 
 

@@ -190,6 +190,20 @@ int conv3x3x3_pack_weights(const void *w_oidhw, void *w_packed, int N, int C_in,
                            void *stream);
 
 /* ------------------------------------------------------------------------------------------
+ * The head's output as 8-bit RGB video frames.  [head.cu, header comment: the clamped
+ * 12-channel output is what the video writer consumes; commit summary: the decoded RGB video's
+ * frames are copied to the host once.]  The mapping is not given there; this library takes a
+ * factor-2 pixel shuffle and a linear [-1, 1] -> [0, 255] code:
+ *   rgb[n,d,2h+dy,2w+dx,c] = clamp(RNE(127.5 * (y[n,d,h,w,4c+2dy+dx] + 1)), 0, 255)
+ * rounded from the exact value (half to even), NaN -> 0, +inf -> 255, -inf -> 0.
+ * y: (N,D,H,W,C) NDHWC of `dtype` (device, 16-byte aligned), C must be 12 (else
+ * CONV_E_UNSUPPORTED); rgb: (N,D,2H,2W,3) uint8 (device; 16-byte aligned with W % 8 == 0 takes
+ * the widest stores).  y and rgb must not overlap.  Enqueued on `stream`.
+ * ---------------------------------------------------------------------------------------- */
+int conv_video_rgb8(const void *y, void *rgb, int N, int D, int H, int W, int C, int dtype,
+                    void *stream);
+
+/* ------------------------------------------------------------------------------------------
  * The split head's two stages as separate calls (conv3x3x3_fwd with CONV_ALGO_SPLIT_HEAD runs
  * both on one stream).  [head.cu: the temporal 3x1x1 convolution that writes the plane, and the
  * host function head_stencil(g, bias, out, ...) that sums it.]

@@ -248,3 +248,23 @@ def test_region_full_is_plain_validation():
     for kw in (dict(), dict(x=None), dict(epilogue=-1), dict(C_in=20), dict(algo=C.ALGO_SIMT),
                dict(algo=C.ALGO_SPLIT_HEAD), dict(algo=C.ALGO_MFMA, C_out=40), dict(y=A + 16)):
         assert f3d(**{"algo": C.ALGO_FUSED_HEAD, **kw}) == f3r(**{**full, **kw}), kw
+
+
+def test_video_invalid_and_empty():
+    ok = dict(y=A, rgb=A + (1 << 28), N=1, D=2, H=4, W=8, C=12, dtype=1, stream=0)
+
+    def fv(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return _st(cx.conv_video_rgb8, a["y"], a["rgb"], a["N"], a["D"], a["H"], a["W"], a["C"],
+                   a["dtype"], a["stream"])
+    assert fv(C=11) == C.E_UNSUPPORTED
+    assert fv(y=None) == C.E_INVAL
+    assert fv(rgb=None) == C.E_INVAL
+    assert fv(y=A + 8) == C.E_INVAL                 # misaligned
+    assert fv(rgb=A + 16) == C.E_INVAL              # overlaps y
+    assert fv(W=-1) == C.E_INVAL
+    assert fv(dtype=7) == C.E_INVAL
+    assert fv(y=None, rgb=None, D=0) == C.OK        # empty: no-op
+    if not HAS_GPU:
+        assert fv() == C.E_NODEVICE

@@ -13,4 +13,4 @@ from .conv import (  # noqa: F401
     conv3x3x3_pack_weights,
     conv3x3x3_packed_weight_bytes, conv3x3x3_select_algo, conv3x3x3_workspace_bytes,
     conv_abi_version, conv_head_stencil, conv_head_temporal, conv_last_error, conv_out_size,
-    conv_status_str, library, library_path)
+    conv_status_str, conv_video_rgb8, library, library_path)

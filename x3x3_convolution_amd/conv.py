@@ -42,6 +42,7 @@ EXPORTS = [
     ("conv3x3x3_pack_weights", _I, [_P, _P] + [_I] * 10 + [_P]),
     ("conv_head_temporal", _I, [_P, _P, _P] + [_I] * 7 + [_P]),
     ("conv_head_stencil", _I, [_P, _P, _P] + [_I] * 7 + [_P]),
+    ("conv_video_rgb8", _I, [_P, _P] + [_I] * 6 + [_P]),
 ]
 
 
@@ -206,3 +207,8 @@ def conv_head_stencil(g, bias, y, N, D, H, W, C_out, dtype=DTYPE_BF16, epilogue=
                       stream=None):
     return _check(library().conv_head_stencil(_ptr(g), _ptr(bias), _ptr(y), N, D, H, W, C_out,
                                               dtype, epilogue, _stream(stream)))
+
+
+def conv_video_rgb8(y, rgb, N, D, H, W, C=12, dtype=DTYPE_BF16, stream=None):
+    return _check(library().conv_video_rgb8(_ptr(y), _ptr(rgb), N, D, H, W, C, dtype,
+                                            _stream(stream)))

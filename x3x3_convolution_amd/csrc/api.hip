@@ -439,4 +439,30 @@ int conv_head_stencil(const void *g, const void *bias, void *y, int N, int D, in
     return ok();
 }
 
+int conv_video_rgb8(const void *y, void *rgb, int N, int D, int H, int W, int C, int dtype,
+                    void *stream) {
+    int st = check_common(1, CONV_LAYOUT_CHANNELS_LAST, dtype, CONV_EPI_NONE);
+    if (st) return st;
+    if (N < 0 || D < 0 || H < 0 || W < 0)
+        return fail(CONV_E_INVAL, "negative size (N=%d D=%d H=%d W=%d)", N, D, H, W);
+    if (C != 12)
+        return fail(CONV_E_UNSUPPORTED, "the video step takes 12 channels (3 colours x 2 x 2), got %d", C);
+    const long long pos = (long long)N * D * H * W;
+    if (pos == 0) return ok();
+    if ((long long)N * D * H * ((W + 255) / 256) >= (1ll << 31) || pos >= (1ll << 40))
+        return fail(CONV_E_UNSUPPORTED, "problem too large for one launch");
+    if (!y || !rgb) return fail(CONV_E_INVAL, "y and rgb must be non-NULL");
+    if (!aligned(y, 16)) return fail(CONV_E_INVAL, "y must be 16-byte aligned");
+    if (overlaps(y, (size_t)pos * 12 * elem_bytes(), rgb, (size_t)pos * 12))
+        return fail(CONV_E_INVAL, "y and rgb overlap");
+    st = device_present();
+    if (st) return st;
+    cx::VideoParams vp{};
+    vp.y = y, vp.rgb = rgb, vp.N = N, vp.D = D, vp.H = H, vp.W = W;
+    vp.bf16 = dtype == CONV_DTYPE_BF16;
+    const hipError_t e = cx::launch_video_rgb8(vp, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(CONV_E_LAUNCH, "video launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // extern "C"

@@ -124,4 +124,13 @@ struct HeadGemmParams {
 };
 hipError_t launch_head_gemm(const HeadGemmParams &p, hipStream_t stream);
 
+// ---- the head's 12-channel output as 8-bit RGB frames (factor-2 pixel shuffle) ------------
+struct VideoParams {
+    const void *y;     // (N, D, H, W, 12) NDHWC
+    void *rgb;         // (N, D, 2H, 2W, 3) uint8
+    int N, D, H, W;
+    bool bf16;
+};
+hipError_t launch_video_rgb8(const VideoParams &p, hipStream_t stream);
+
 }  // namespace cx
