@@ -351,7 +351,7 @@ def region_of(kind, D, H):
 
 
 def run_region(args, wl, stream):
-    """A region pass of a 3D workload (AUTO algorithm), timed like the plain pass."""
+    """A region pass of a 3D workload (the --algo algorithm), timed like the plain pass."""
     import torch
 
     import synthetic_inputs as si
@@ -363,7 +363,9 @@ def run_region(args, wl, stream):
     w, b = w.cuda(), b.cuda()
     g = torch.Generator("cpu").manual_seed(si.SEED_BASE + 7)
     x = torch.randn((wl.N, D_in, H_in, wl.W, wl.C_in), generator=g).to(wl.torch_dtype).cuda()
-    op = Conv3x3x3(w, b, wl.N, D, H, wl.W, epilogue=wl.epilogue)
+    algo = {"auto": C.ALGO_AUTO, "mfma": C.ALGO_MFMA, "split": C.ALGO_SPLIT_HEAD,
+            "fused": C.ALGO_FUSED_HEAD}[args.algo]
+    op = Conv3x3x3(w, b, wl.N, D, H, wl.W, epilogue=wl.epilogue, algo=algo)
     y = torch.empty(op.out_shape(), dtype=wl.torch_dtype, device="cuda")
     kname = {C.ALGO_FUSED_HEAD: "head_fused", C.ALGO_SPLIT_HEAD: "head_split"}.get(op.algo, "igemm3d")
 

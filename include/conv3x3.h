@@ -150,9 +150,10 @@ int conv3x3x3_fwd(const void *x, const void *w_packed, const void *bias, void *y
  *     D_in = D_out + 2, d_org = 1, d_lo = 0, d_hi = D_in.
  * Requirements beyond conv3x3x3_fwd's: 0 <= d_lo <= d_hi <= D_in, 0 <= h_lo <= h_hi <= H_in
  * (else CONV_E_INVAL); every output frame reads at least one valid input frame, i.e. d_lo < d_hi,
- * d_lo <= d_org + 1 and D_out + d_org - 1 <= d_hi (else CONV_E_UNSUPPORTED); SPLIT_HEAD only when
- * input rows h_org-1 and H_out+h_org are outside [h_lo, h_hi) (its stencil reads the rows next
- * to the band as zeros; FUSED_HEAD has no such limit).  The algorithm, the weight packing and the
+ * d_lo <= d_org + 1 and D_out + d_org - 1 <= d_hi (else CONV_E_UNSUPPORTED).  SPLIT_HEAD
+ * computes its plane for the output rows plus, when input rows h_org-1 or H_out+h_org hold
+ * data, the Z rows just above and below the band (head.cu's g_off = 1).  The algorithm, the
+ * weight packing and the
  * workspace are those of conv3x3x3_fwd for the OUTPUT extent: pass (N, C_in, C_out, D_out,
  * H_out, W) to conv3x3x3_select_algo, _packed_weight_bytes, _pack_weights and _workspace_bytes.
  * x, y and the workspace must not overlap.
@@ -172,8 +173,9 @@ int conv3x3x3_select_algo(int N, int C_in, int C_out, int D, int H, int W, int s
 int conv3x3x3_is_supported(int N, int C_in, int C_out, int D, int H, int W, int stride,
                            int layout, int dtype, int epilogue, int algo);
 
-/* Bytes of workspace conv3x3x3_fwd needs: the split head's intermediate plane
- * (N*D*H*W*112 elements of dtype), the split-K partial sums of the MFMA path for small
+/* Bytes of workspace conv3x3x3_fwd (and conv3x3x3_fwd_region for this output extent) needs:
+ * the split head's intermediate plane with room for one row above and below the output rows
+ * (N*D*(H+2)*W*112 elements of dtype), the split-K partial sums of the MFMA path for small
  * position counts (fp32), or 0.  Returns 0 for an unsupported request as well. */
 size_t conv3x3x3_workspace_bytes(int N, int C_in, int C_out, int D, int H, int W, int stride,
                                  int layout, int dtype, int algo);

@@ -128,7 +128,7 @@ def test_3d_invalid_and_unsupported():
     # the split head needs its plane in the workspace
     assert f3d(algo=C.ALGO_SPLIT_HEAD) == C.E_WORKSPACE
     need = cx.conv3x3x3_workspace_bytes(1, 32, 12, 2, 8, 8, 1, 1, 1, C.ALGO_SPLIT_HEAD)
-    assert need == 2 * 8 * 8 * 112 * 2
+    assert need == 2 * (8 + 2) * 8 * 112 * 2   # one plane row above and below the output rows
     assert f3d(algo=C.ALGO_SPLIT_HEAD, ws=WS, wsb=need - 1) == C.E_WORKSPACE
     assert f3d(algo=C.ALGO_SPLIT_HEAD, ws=WS + 4, wsb=need) == C.E_INVAL   # misaligned
     assert f3d(algo=C.ALGO_SPLIT_HEAD, ws=A, wsb=need) == C.E_INVAL        # overlaps x
@@ -168,7 +168,7 @@ def test_algo_selection_and_buffer_sizes():
     assert cx.conv3x3x3_workspace_bytes(1, 256, 12, 16, 352, 624, 1, 1, 1, 0) == 0
     assert cx.conv3x3x3_select_algo(1, 256, 256, 16, 176, 312, 1, 1, 1, 0) == C.ALGO_MFMA
     assert cx.conv3x3x3_workspace_bytes(1, 256, 12, 16, 352, 624, 1, 1, 1,
-                                        C.ALGO_SPLIT_HEAD) == 787218432
+                                        C.ALGO_SPLIT_HEAD) == 16 * 354 * 624 * 112 * 2
     # packed weights: 8 channel chunks x 27 taps x 16 rows x 32 (direct head)
     assert cx.conv3x3x3_packed_weight_bytes(1, 256, 12, 16, 352, 624, 1, 1, 1,
                                             C.ALGO_MFMA) == 8 * 27 * 16 * 32 * 2
@@ -231,12 +231,15 @@ def test_region_invalid_and_unsupported():
     assert f3r(algo=C.ALGO_SIMT) == C.E_UNSUPPORTED
     assert f3r(C_in=20) == C.E_UNSUPPORTED
     assert f3r(y=A + 16) == C.E_INVAL           # overlaps x (x is 6*8*8*32*2 bytes)
-    # the split head's stencil reads rows -1 and H_out as zero: not with halo rows that hold data
+    # the split head's plane carries a row above and below the band: the workspace covers it
     ws = cx.conv3x3x3_workspace_bytes(1, 32, 12, 4, 6, 8, 1, 1, 1, C.ALGO_SPLIT_HEAD)
-    assert ws == 4 * 6 * 8 * 112 * 2
-    assert f3r(algo=C.ALGO_SPLIT_HEAD, ws=WS, wsb=ws) == C.E_UNSUPPORTED
-    assert f3r(algo=C.ALGO_SPLIT_HEAD, ws=WS, wsb=ws, h_lo=1, h_hi=7) in (C.OK, C.E_NODEVICE)
+    assert ws == 4 * (6 + 2) * 8 * 112 * 2
+    expect = C.OK if HAS_GPU else C.E_NODEVICE
+    assert f3r(algo=C.ALGO_SPLIT_HEAD, ws=WS, wsb=ws, x=None) == C.E_INVAL
+    assert f3r(algo=C.ALGO_SPLIT_HEAD, ws=WS, wsb=ws - 1) == C.E_WORKSPACE
     assert f3r(algo=C.ALGO_SPLIT_HEAD, ws=None, h_lo=1, h_hi=7) == C.E_WORKSPACE
+    if not HAS_GPU:
+        assert f3r(algo=C.ALGO_SPLIT_HEAD, ws=WS, wsb=ws) == expect
     # empty outputs are no-ops once the region itself is well formed
     assert f3r(x=None, y=None, D_out=0) == C.OK
     assert f3r(x=None, y=None, D_out=0, d_hi=7) == C.E_INVAL

@@ -65,6 +65,7 @@ ALGOS = {
     "mfma_narrow": (24, 12, "bf16", C.ALGO_MFMA),
     "fused_head": (64, 12, "bf16", C.ALGO_FUSED_HEAD),
     "fused_head_co7": (40, 7, "bf16", C.ALGO_FUSED_HEAD),
+    "split_head": (32, 12, "bf16", C.ALGO_SPLIT_HEAD),
 }
 
 
@@ -134,8 +135,8 @@ def test_causal_chunk_of_a_row_band(name):
 
 
 def test_split_head_regions():
-    """The split head takes causal chunks and whole-height bands (zero rows next to the band),
-    and refuses a band with halo rows above it."""
+    """The split head on a causal chunk, a whole-height band (its plane needs no extra rows) and
+    a band with data above and below it (its plane carries one more Z row each side)."""
     N, Ci, Co, T, H, W = 1, 32, 12, 6, 9, 50
     Xall, w, b = si.integer_case("3d", N, Ci, Co, H, W, D=T, dtype="bf16", seed=11, device=DEV)
     want = _causal_reference(Xall, w, b, "clamp1")
@@ -150,12 +151,11 @@ def test_split_head_regions():
     H_in, h_org, h_lo, h_hi = band_rows(0, H, 1, H)
     y = _run(op, xs, D_in, H_in, d_org, h_org, d_lo, d_hi, h_lo, h_hi)
     assert_bit_exact(y, want[:, 2:6], x.dtype)
-    # a band whose row above holds data: the fused head's job
+    # a band whose rows above and below hold data
     op2 = Conv3x3x3(w, b, N, 4, 4, W, epilogue="clamp1", algo=C.ALGO_SPLIT_HEAD)
     H_in, h_org, h_lo, h_hi = band_rows(3, 4, 1, H)
-    with pytest.raises(C.ConvError) as ei:
-        op2.region(_stored_rows(x, 3, 4, 1), D_in, H_in, d_org, h_org, d_lo, d_hi, h_lo, h_hi)
-    assert ei.value.status == C.E_UNSUPPORTED
+    y = _run(op2, _stored_rows(x, 3, 4, 1), D_in, H_in, d_org, h_org, d_lo, d_hi, h_lo, h_hi)
+    assert_bit_exact(y, want[:, 2:6, 3:7], x.dtype)
 
 
 def test_region_split_k():

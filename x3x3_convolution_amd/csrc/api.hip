@@ -149,10 +149,11 @@ hipError_t launch_head(const void *x, const void *w_packed, const void *bias, vo
 }
 
 hipError_t launch_stencil(const void *g, const void *bias, void *y, int N, int D, int H, int W,
-                          int C_out, bool bf, int epilogue, hipStream_t s) {
+                          int C_out, int g_off, bool bf, int epilogue, hipStream_t s) {
     cx::StencilParams sp{};
     sp.g = g, sp.bias = bias, sp.y = y;
-    sp.N = N, sp.D = D, sp.H = H, sp.W = W, sp.C_out = C_out, sp.bf16 = bf, sp.epilogue = epilogue;
+    sp.N = N, sp.D = D, sp.H = H, sp.W = W, sp.C_out = C_out, sp.g_off = g_off;
+    sp.bf16 = bf, sp.epilogue = epilogue;
     return cx::launch_head_stencil(sp, s);
 }
 
@@ -251,8 +252,8 @@ size_t conv3x3x3_workspace_bytes(int N, int C_in, int C_out, int D, int H, int W
     const int a = select_3d(N, C_in, C_out, D, H, W, stride, layout, dtype, algo);
     if (a < 0) return 0;
     ok();
-    if (a == CONV_ALGO_SPLIT_HEAD)
-        return (size_t)N * D * H * W * cx::kHeadPlaneChannels * elem_bytes();
+    if (a == CONV_ALGO_SPLIT_HEAD)   // the plane, with room for one Z row above and below
+        return (size_t)N * D * (H + 2) * W * cx::kHeadPlaneChannels * elem_bytes();
     const cx::IgemmPlan pl = cx::plan_igemm(family_for(a, C_in, C_out, H, W), N, C_in, C_out, D, H, W);
     return cx::splitk_workspace_bytes(pl, N, D, H, W, C_out);
 }
@@ -321,12 +322,11 @@ int fwd3d(const void *x, const void *w_packed, const void *bias, void *y, int N,
     const int family = family_for(a, C_in, C_out, H, W);
     if (family == cx::IG_W32 && frame_in >= (1ll << 31))
         return fail(CONV_E_UNSUPPORTED, "one input frame must stay below 2 GiB for this packing");
-    // the split head's stencil reads plane rows -1 and H as zeros
+    // the split head's plane: the output rows alone when the Z rows next to them read no data
+    // (the stencil takes those as zero), else one more Z row above and below (g_off = 1)
     const bool row_edges_zero = (rg.h_org - 1 < rg.h_lo || rg.h_org - 1 >= rg.h_hi) &&
                                 ((long long)H + rg.h_org < rg.h_lo || (long long)H + rg.h_org >= rg.h_hi);
-    if (a == CONV_ALGO_SPLIT_HEAD && !row_edges_zero)
-        return fail(CONV_E_UNSUPPORTED,
-                    "the split head needs zero rows above and below the output band (use the fused head)");
+    const int g_off = row_edges_zero ? 0 : 1;
     if (!x || !w_packed || !y) return fail(CONV_E_INVAL, "x, w_packed and y must be non-NULL");
     if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(y, 16))
         return fail(CONV_E_INVAL, "x, w_packed and y must be 16-byte aligned");
@@ -349,10 +349,12 @@ int fwd3d(const void *x, const void *w_packed, const void *bias, void *y, int N,
     const bool bf = dtype == CONV_DTYPE_BF16;
     hipStream_t s = (hipStream_t)stream;
     if (a == CONV_ALGO_SPLIT_HEAD) {
-        hipError_t e = launch_head(x, w_packed, nullptr, workspace, N, C_in, C_out, D, H, W, rg, bf,
-                                   false, CONV_EPI_NONE, s);
+        cx::ConvRegion prg = rg;      // plane row z holds the Z row of output row z - g_off
+        prg.h_org -= g_off;
+        hipError_t e = launch_head(x, w_packed, nullptr, workspace, N, C_in, C_out, D, H + 2 * g_off,
+                                   W, prg, bf, false, CONV_EPI_NONE, s);
         if (e != hipSuccess) return fail(CONV_E_LAUNCH, "split-head temporal launch failed: %s", hipGetErrorString(e));
-        e = launch_stencil(workspace, bias, y, N, D, H, W, C_out, bf, epilogue, s);
+        e = launch_stencil(workspace, bias, y, N, D, H, W, C_out, g_off, bf, epilogue, s);
         if (e != hipSuccess) return fail(CONV_E_LAUNCH, "split-head stencil launch failed: %s", hipGetErrorString(e));
         return ok();
     }
@@ -433,7 +435,7 @@ int conv_head_stencil(const void *g, const void *bias, void *y, int N, int D, in
         return fail(CONV_E_INVAL, "g and y overlap");
     st = device_present();
     if (st) return st;
-    const hipError_t e = launch_stencil(g, bias, y, N, D, H, W, C_out, dtype == CONV_DTYPE_BF16,
+    const hipError_t e = launch_stencil(g, bias, y, N, D, H, W, C_out, 0, dtype == CONV_DTYPE_BF16,
                                         epilogue, (hipStream_t)stream);
     if (e != hipSuccess) return fail(CONV_E_LAUNCH, "head stencil launch failed: %s", hipGetErrorString(e));
     return ok();

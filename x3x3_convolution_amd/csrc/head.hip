@@ -1,8 +1,10 @@
 // Split head, stage 2: the nine-tap spatial stencil over the 112-channel intermediate plane.
 //
-//   y[n,d,h,w,co] = E( b[co] + sum_{ky,kx} g[n,d,h+ky-1,w+kx-1,(ky*3+kx)*C_out+co] ),
+//   y[n,d,h,w,co] = E( b[co] + sum_{ky,kx} g[n,d,h+g_off+ky-1,w+kx-1,(ky*3+kx)*C_out+co] ),
 //   g = 0 outside the plane (the 3x3x3 convolution's spatial zero padding), fp32 sum of the nine
-//   bf16/fp16 values, bias in fp32, one round-to-nearest-even on the store.
+//   bf16/fp16 values, bias in fp32, one round-to-nearest-even on the store.  The plane has
+//   gH = H + 2*g_off rows per frame: g_off = 1 carries the Z rows just above and below an output
+//   band (head.cu, head_stencil: a band's plane with g_off halo rows each side).
 // (FastVideo head.cu: header comment on the value path, and head_stencil_kernel for the channel
 // order (i*3+j)*12+c of the plane, i = row tap, j = column tap.)
 //
@@ -28,6 +30,7 @@ struct StencilKArgs {
     const u16 *bias;
     u16 *y;
     int N, D, H, W, C_out;
+    int g_off, gH;     // plane rows above the first output row; plane rows per frame
     int rows_per_band, bands, strips;
     uint32_t total_wg;
 };
@@ -48,7 +51,8 @@ __global__ __launch_bounds__(256) void head_stencil_kernel(StencilKArgs a) {
     const int w0 = strip * kStripW;
     const int h_begin = band * a.rows_per_band;
     const int h_end = min(a.H, h_begin + a.rows_per_band);
-    const size_t frame = ((size_t)n * a.D + d) * a.H;
+    const size_t frame = ((size_t)n * a.D + d) * a.H;          // first output row of the frame
+    const size_t gframe = ((size_t)n * a.D + d) * a.gH + a.g_off;   // plane row of output row 0
 
     // Row h of the plane (66 positions incl. the column halo) is fetched into registers one
     // iteration before it is needed and written to its ring slot (h mod 3) after a barrier.
@@ -62,9 +66,9 @@ __global__ __launch_bounds__(256) void head_stencil_kernel(StencilKArgs a) {
             if (i < kRowPieces) {
                 const int p = i / kPosPieces, q = i - p * kPosPieces;
                 const int w = w0 - 1 + p;
-                if ((unsigned)h < (unsigned)a.H && (unsigned)w < (unsigned)a.W)
+                if ((unsigned)(h + a.g_off) < (unsigned)a.gH && (unsigned)w < (unsigned)a.W)
                     v = *reinterpret_cast<const uint4 *>(
-                        a.g + ((frame + h) * a.W + w) * kHeadPlaneChannels + q * 8);
+                        a.g + ((gframe + h) * a.W + w) * kHeadPlaneChannels + q * 8);
             }
             rstg[j] = v;
         }
@@ -557,6 +561,7 @@ hipError_t launch_head_stencil(const StencilParams &p, hipStream_t stream) {
     a.bias = static_cast<const u16 *>(p.bias);
     a.y = static_cast<u16 *>(p.y);
     a.N = p.N, a.D = p.D, a.H = p.H, a.W = p.W, a.C_out = p.C_out;
+    a.g_off = p.g_off, a.gH = p.H + 2 * p.g_off;
     a.strips = (p.W + kStripW - 1) / kStripW;
     // Bands of rows: enough workgroups to cover the chip several times, each long enough that
     // the two halo rows it re-reads are a small fraction of its traffic.

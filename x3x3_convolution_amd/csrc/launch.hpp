@@ -88,6 +88,7 @@ struct StencilParams {
     const void *g, *bias;
     void *y;
     int N, D, H, W, C_out;
+    int g_off;         // plane rows carried above (and below) the H output rows: 0 or 1
     bool bf16;
     int epilogue;
 };
