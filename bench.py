@@ -239,7 +239,22 @@ def run_head(args, wl, stream):
                      algorithmic_bytes=vbytes, gbs=round(vbytes / (vms * 1e-3) / 1e9, 1),
                      hbm_frac=round(vbytes / (vms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      traffic=traffic_from_profiles("video_rgb8", wl.name, "auto"))
-        del rgb
+        # the fused head writing the RGB frames straight from its registers (no y round trip)
+        opf = Conv3x3x3(w, b, wl.N, wl.D, wl.H, wl.W, epilogue=wl.epilogue,
+                        algo=C.ALGO_FUSED_HEAD)
+        for _ in range(args.warmup):
+            opf.rgb8(x, rgb, stream=stream)
+        torch.cuda.synchronize()
+        tm = Timer(torch.cuda.current_stream())
+        for _ in range(args.steps):
+            s0 = tm.start()
+            opf.rgb8(x, rgb, stream=stream)
+            tm.stop("head_rgb8", s0)
+        torch.cuda.synchronize()
+        video["fused_head_rgb8_ms"] = round(tm.summary()["head_rgb8"], 5)
+        video["separate_head_plus_video_ms"] = round(results["fused"]["kernel_ms"]["head_fused"] + vms, 5) \
+            if "fused" in results else None
+        del rgb, opf
     extra = dict(
         pass_tflops=flop_live / (pass_ms * 1e-3) / 1e12,
         pass_gbs=((xb + 2 * gb + yb + wb + bb) if chosen == "split" else (xb + yb + wb + bb))

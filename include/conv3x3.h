@@ -205,6 +205,16 @@ int conv3x3x3_pack_weights(const void *w_oidhw, void *w_packed, int N, int C_in,
 int conv_video_rgb8(const void *y, void *rgb, int N, int D, int H, int W, int C, int dtype,
                     void *stream);
 
+/* The fused head (CONV_ALGO_FUSED_HEAD, C_out = 12) writing the RGB frames of its output directly:
+ * rgb equals conv_video_rgb8 applied to the y that conv3x3x3_fwd computes for the same
+ * arguments (each value rounded to `dtype`, then coded), but y is never stored.  x (N,D,H,W,C_in)
+ * NDHWC, w_packed from conv3x3x3_pack_weights(..., C_out = 12, ..., CONV_ALGO_FUSED_HEAD), bias
+ * (12) or NULL, rgb (N,D,2H,2W,3) uint8 (2-byte aligned; one sample below 2 GiB).  Requirements
+ * and errors otherwise as conv3x3x3_fwd with CONV_ALGO_FUSED_HEAD.  [head.cu, header comment:
+ * the clamped 12-channel output feeds the video writer.] */
+int conv3x3x3_head_rgb8(const void *x, const void *w_packed, const void *bias, void *rgb, int N,
+                        int C_in, int D, int H, int W, int dtype, int epilogue, void *stream);
+
 /* ------------------------------------------------------------------------------------------
  * The split head's two stages as separate calls (conv3x3x3_fwd with CONV_ALGO_SPLIT_HEAD runs
  * both on one stream).  [head.cu: the temporal 3x1x1 convolution that writes the plane, and the

@@ -271,3 +271,20 @@ def test_video_invalid_and_empty():
     assert fv(y=None, rgb=None, D=0) == C.OK        # empty: no-op
     if not HAS_GPU:
         assert fv() == C.E_NODEVICE
+
+
+def test_head_rgb8_invalid():
+    def fr(**kw):
+        a = dict(x=A, w=B, bias=None, rgb=A + (1 << 28), N=1, C_in=32, D=2, H=8, W=8, dtype=1,
+                 epilogue=2, stream=0)
+        a.update(kw)
+        return _st(cx.conv3x3x3_head_rgb8, *[a[k] for k in (
+            "x", "w", "bias", "rgb", "N", "C_in", "D", "H", "W", "dtype", "epilogue", "stream")])
+    assert fr(x=None) == C.E_INVAL
+    assert fr(rgb=A + (1 << 28) + 1) == C.E_INVAL     # odd address
+    assert fr(rgb=A + 64) == C.E_INVAL                # overlaps x
+    assert fr(C_in=20) == C.E_UNSUPPORTED
+    assert fr(epilogue=5) == C.E_INVAL
+    assert fr(x=None, rgb=None, D=0) == C.OK
+    if not HAS_GPU:
+        assert fr() == C.E_NODEVICE

@@ -101,3 +101,59 @@ def test_head_then_video_integer_exact():
     yref = oracle.decode(oracle.encode(oracle_3d(x, w, b, "clamp1"), oracle.BF16), oracle.BF16)
     want = oracle.video_rgb8(yref.reshape(N, D, H, W, Co))
     assert np.array_equal(got, want)
+
+
+def test_fused_rgb_head_integer_exact():
+    """conv3x3x3_head_rgb8 on integer inputs (exact head output) against the oracle's
+    convolution and video step; guard bands around the frames."""
+    N, Ci, D, H, W = 2, 40, 3, 11, 150
+    x, w, b = si.integer_case("3d", N, Ci, 12, H, W, D=D, dtype="bf16", seed=23, device=DEV)
+    w, b = w * 0.25, b * 0.25
+    op = Conv3x3x3(w, b, N, D, H, W, epilogue="clamp1", algo=C.ALGO_FUSED_HEAD)
+    n = N * D * 2 * H * 2 * W * 3
+    buf = torch.full((n + 2 * GUARD,), FILL, dtype=torch.uint8, device=DEV)
+    rgb = buf[GUARD:GUARD + n].view(N, D, 2 * H, 2 * W, 3)
+    op.rgb8(x, rgb)
+    torch.cuda.synchronize()
+    host = buf.cpu().numpy()
+    assert np.all(host[:GUARD] == FILL) and np.all(host[GUARD + n:] == FILL), "write outside rgb"
+    yref = oracle.decode(oracle.encode(oracle_3d(x, w, b, "clamp1"), oracle.BF16), oracle.BF16)
+    want = oracle.video_rgb8(yref.reshape(N, D, H, W, 12))
+    assert np.array_equal(host[GUARD:GUARD + n].reshape(want.shape), want)
+
+
+@pytest.mark.parametrize("shape", [(1, 5, 33, 140, 64), (1, 16, 352, 624, 256)],
+                         ids=["small", "c3_full"])
+def test_fused_rgb_head_random(shape):
+    """Random inputs: the fused RGB head's bytes equal the fused head followed by the video step
+    (the same arithmetic), and stay within the head's tolerance of the oracle's bytes (at most 3
+    codes: max|d| 1.6e-2 of the head's output times 127.5); sampled at full size."""
+    N, D, H, W, Ci = shape
+    _say("fused rgb head %s" % (shape,))
+    if shape[1] == 16:
+        x, w, b = si.make_inputs(si.WORKLOADS["c3"], device=DEV)
+    else:
+        x, w, b = si.random_case("3d", N, Ci, 12, H, W, D=D, dtype="bf16", seed=7, device=DEV)
+    op = Conv3x3x3(w, b, N, D, H, W, epilogue="clamp1", algo=C.ALGO_FUSED_HEAD)
+    rgb = op.rgb8(x)
+    y = op(x)
+    rgb2 = torch.empty_like(rgb)
+    C.conv_video_rgb8(y, rgb2, N, D, H, W, 12, C.DTYPE_BF16)
+    torch.cuda.synchronize()
+    assert torch.equal(rgb, rgb2)
+    if shape[1] == 16:
+        from gpu_support import sample_points_3d
+        pts = sample_points_3d(N, D, H, W, 400, seed=5)
+        yref = oracle.conv3d_points(bits(x), bits(w), bits(b), pts, 1, oracle.BF16,
+                                    oracle.EPI_CLAMP1, oracle.CHANNELS_LAST)
+        qref = oracle.quantize_u8(oracle.decode(oracle.encode(yref, oracle.BF16), oracle.BF16))
+        got = rgb.cpu().numpy()
+        for i, (n_, d_, h_, w_) in enumerate(pts):
+            for k in range(12):
+                c, dy, dx = k // 4, (k // 2) % 2, k % 2
+                assert abs(int(got[n_, d_, 2 * h_ + dy, 2 * w_ + dx, c]) - int(qref[i, k])) <= 3
+    else:
+        yref = oracle_3d(x, w, b, "clamp1")
+        want = oracle.video_rgb8(oracle.decode(oracle.encode(yref, oracle.BF16), oracle.BF16))
+        d = np.abs(rgb.cpu().numpy().astype(np.int32) - want.astype(np.int32))
+        assert d.max() <= 3 and d.mean() < 0.05, (d.max(), d.mean())

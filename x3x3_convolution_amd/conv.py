@@ -43,6 +43,7 @@ EXPORTS = [
     ("conv_head_temporal", _I, [_P, _P, _P] + [_I] * 7 + [_P]),
     ("conv_head_stencil", _I, [_P, _P, _P] + [_I] * 7 + [_P]),
     ("conv_video_rgb8", _I, [_P, _P] + [_I] * 6 + [_P]),
+    ("conv3x3x3_head_rgb8", _I, [_P, _P, _P, _P] + [_I] * 7 + [_P]),
 ]
 
 
@@ -212,3 +213,10 @@ def conv_head_stencil(g, bias, y, N, D, H, W, C_out, dtype=DTYPE_BF16, epilogue=
 def conv_video_rgb8(y, rgb, N, D, H, W, C=12, dtype=DTYPE_BF16, stream=None):
     return _check(library().conv_video_rgb8(_ptr(y), _ptr(rgb), N, D, H, W, C, dtype,
                                             _stream(stream)))
+
+
+def conv3x3x3_head_rgb8(x, w_packed, bias, rgb, N, C_in, D, H, W, dtype=DTYPE_BF16,
+                        epilogue=EPI_CLAMP1, stream=None):
+    return _check(library().conv3x3x3_head_rgb8(_ptr(x), _ptr(w_packed), _ptr(bias), _ptr(rgb),
+                                                N, C_in, D, H, W, dtype, epilogue,
+                                                _stream(stream)))

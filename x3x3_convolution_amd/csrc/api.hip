@@ -140,11 +140,11 @@ size_t elem_bytes() { return 2; }
 
 hipError_t launch_head(const void *x, const void *w_packed, const void *bias, void *out, int N,
                        int C_in, int C_out, int D, int H, int W, const cx::ConvRegion &rg, bool bf,
-                       bool fused, int epilogue, hipStream_t s) {
+                       bool fused, int epilogue, hipStream_t s, bool rgb = false) {
     cx::HeadGemmParams hp{};
     hp.x = x, hp.wp = w_packed, hp.bias = bias, hp.out = out;
     hp.N = N, hp.C_in = C_in, hp.C_out = C_out, hp.D = D, hp.H = H, hp.W = W, hp.rg = rg;
-    hp.bf16 = bf, hp.fused = fused, hp.epilogue = epilogue;
+    hp.bf16 = bf, hp.fused = fused, hp.epilogue = epilogue, hp.rgb = rgb;
     return cx::launch_head_gemm(hp, s);
 }
 
@@ -464,6 +464,32 @@ int conv_video_rgb8(const void *y, void *rgb, int N, int D, int H, int W, int C,
     vp.bf16 = dtype == CONV_DTYPE_BF16;
     const hipError_t e = cx::launch_video_rgb8(vp, (hipStream_t)stream);
     if (e != hipSuccess) return fail(CONV_E_LAUNCH, "video launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int conv3x3x3_head_rgb8(const void *x, const void *w_packed, const void *bias, void *rgb, int N,
+                        int C_in, int D, int H, int W, int dtype, int epilogue, void *stream) {
+    if (epilogue < CONV_EPI_NONE || epilogue > CONV_EPI_CLAMP1)
+        return fail(CONV_E_INVAL, "unknown epilogue %d", epilogue);
+    const int a = select_3d(N, C_in, 12, D, H, W, 1, CONV_LAYOUT_CHANNELS_LAST, dtype,
+                            CONV_ALGO_FUSED_HEAD);
+    if (a < 0) return a;
+    if (N == 0 || D == 0 || H == 0 || W == 0) return ok();
+    const size_t rgb_sample = (size_t)D * H * W * 12;
+    if (rgb_sample >= (1ull << 31))
+        return fail(CONV_E_UNSUPPORTED, "one sample of the RGB frames must stay below 2 GiB");
+    if (!x || !w_packed || !rgb) return fail(CONV_E_INVAL, "x, w_packed and rgb must be non-NULL");
+    if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(rgb, 2))
+        return fail(CONV_E_INVAL, "x and w_packed must be 16-byte and rgb 2-byte aligned");
+    if (bias && !aligned(bias, 2)) return fail(CONV_E_INVAL, "bias must be 2-byte aligned");
+    const size_t xb = (size_t)N * D * H * W * C_in * elem_bytes();
+    if (overlaps(x, xb, rgb, (size_t)N * rgb_sample)) return fail(CONV_E_INVAL, "x and rgb overlap");
+    int st = device_present();
+    if (st) return st;
+    const hipError_t e = launch_head(x, w_packed, bias, rgb, N, C_in, 12, D, H, W,
+                                     cx::full_region(D, H), dtype == CONV_DTYPE_BF16, true,
+                                     epilogue, (hipStream_t)stream, true);
+    if (e != hipSuccess) return fail(CONV_E_LAUNCH, "RGB head launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 

@@ -94,4 +94,18 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t i, uint32_t total) {
     return start + k;
 }
 
+// A value of the head's output as an 8-bit video code: clamp(RNE(127.5 * (v + 1)), 0, 255) of the
+// exact value, NaN -> 0 ([-1, 1] onto [0, 255]).  For every fp16/bf16 value v (fp32 denormals
+// kept) one fused multiply-add rounds the exact 127.5*v + 127.5 without moving it onto or across
+// a half-integer, except for tiny v, where it lands on the tie 127.5 itself and the sign of v
+// decides (checked over all 65536 patterns of both types).
+__device__ __forceinline__ uint32_t rgb_code(float v) {
+    const float t = __builtin_fmaf(v, 127.5f, 127.5f);
+    float q = __builtin_rintf(t);
+    if (v < 0.f && t == 127.5f) q = 127.f;
+    q = __builtin_fmaxf(q, 0.f);     // also NaN -> 0
+    q = __builtin_fminf(q, 255.f);
+    return (uint32_t)q;
+}
+
 }  // namespace cx

@@ -230,8 +230,12 @@ __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "mem
 // blocks unpacked at a time instead of all 256 accumulators.
 __device__ __forceinline__ void touch(f32x16_t &v) { asm volatile("" : "+a"(v)::"memory"); }
 
-// CO12: C_out == 12, every lane stores its six channels as one 12-byte vector.
-template <bool BF, bool FUSED, int EPI, bool CO12>
+// CO12: C_out == 12, every lane stores its six channels as one 12-byte vector.  RGB (FUSED and
+// CO12 only): instead of y, the 8-bit RGB pixels of the video step -- each value rounded to the
+// storage type first, then coded (rgb_code); position (h, w) gives pixels (2h+dy, 2w+dx), colour
+// c from channel 4c + 2dy + dx.  Lane half 0 (channels 0..5) writes pixel row 2h, half 1
+// (channels 6..11) row 2h+1; each takes the two codes it lacks from the other half.
+template <bool BF, bool FUSED, int EPI, bool CO12, bool RGB = false>
 __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
     using E = Elem<BF>;
     typedef typename E::vec8 vec8;
@@ -273,8 +277,9 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
         (void *)a.wp, (short)0, (int)a.wp_bytes, 0x00020000);
     // FUSED: one sample of y
     const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(a.out + (size_t)n * a.D * HW * a.C_out), (short)0, (int)(a.D * HW * a.C_out * 2),
-        0x00020000);
+        RGB ? (void *)(reinterpret_cast<uint8_t *>(a.out) + (size_t)n * a.D * HW * 12)
+            : (void *)(a.out + (size_t)n * a.D * HW * a.C_out),
+        (short)0, RGB ? (int)(a.D * HW * 12) : (int)(a.D * HW * a.C_out * 2), 0x00020000);
 
     // B window copies: this wave issues copies k = wave + 4*t; lane i of copy k fills slot
     // 64*k + i = ((frame*4 + nb)*32 + column j)*4 + piece', with frame = k/8, nb = (k/2) % 4,
@@ -534,7 +539,27 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
                 // not happen goes to an offset past the buffer range, where it is dropped
                 const uint32_t yoff =
                     (uint32_t)(((od * a.H + ho) * a.W + w) * a.C_out + kHalfCo * hh) * 2u;
-                if constexpr (CO12) {
+                if constexpr (RGB) {
+                    uint32_t q[kHalfCo];
+#pragma unroll
+                    for (int c = 0; c < kHalfCo; ++c) q[c] = rgb_code(E::to_f32(r6[c]));
+                    // half 0 lacks blue of row 2h (channels 8, 9), half 1 red of row 2h+1
+                    // (channels 2, 3): local channels 2 and 3 of the other half
+                    const uint32_t recv = (uint32_t)__builtin_amdgcn_ds_bpermute(
+                        (lane ^ 32) << 2, (int)(q[2] | (q[3] << 8)));
+                    const uint32_t r0 = recv & 0xFFu, r1 = (recv >> 8) & 0xFFu;
+                    // bytes R G B R G B of pixels (2h + hh, 2w) and (2h + hh, 2w + 1)
+                    const uint32_t p01 = hh == 0 ? (q[0] | (q[4] << 8)) : (r0 | (q[0] << 8));
+                    const uint32_t p23 = hh == 0 ? (r0 | (q[1] << 8)) : (q[4] | (r1 << 8));
+                    const uint32_t p45 = hh == 0 ? (q[5] | (r1 << 8)) : (q[1] | (q[5] << 8));
+                    const uint32_t roff =
+                        st_ok ? (uint32_t)(((od * 2 * a.H + 2 * ho + hh) * 2 * a.W + 2 * w) * 3) : kOff;
+                    __builtin_amdgcn_raw_buffer_store_b16((u16)p01, yr, roff, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16((u16)p23, yr,
+                                                          __builtin_elementwise_add_sat(roff, 2u), 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16((u16)p45, yr,
+                                                          __builtin_elementwise_add_sat(roff, 4u), 0, 0);
+                } else if constexpr (CO12) {
                     typedef uint32_t v3u __attribute__((ext_vector_type(3)));
                     const v3u v = {(uint32_t)r6[0] | ((uint32_t)r6[1] << 16),
                                    (uint32_t)r6[2] | ((uint32_t)r6[3] << 16),
@@ -631,7 +656,17 @@ hipError_t launch_head_gemm(const HeadGemmParams &p, hipStream_t stream) {
         if (p.C_out == 12) head_gemm_kernel<BFV, FV, EPIV, true><<<grid, block, 0, stream>>>(a);  \
         else head_gemm_kernel<BFV, FV, EPIV, false><<<grid, block, 0, stream>>>(a);    \
     } while (0)
-    if (!p.fused) {
+    if (p.rgb) {   // fused, C_out == 12
+        if (p.bf16) {
+            if (p.epilogue == EPI_RELU) head_gemm_kernel<true, true, EPI_RELU, true, true><<<grid, block, 0, stream>>>(a);
+            else if (p.epilogue == EPI_CLAMP1) head_gemm_kernel<true, true, EPI_CLAMP1, true, true><<<grid, block, 0, stream>>>(a);
+            else head_gemm_kernel<true, true, EPI_NONE, true, true><<<grid, block, 0, stream>>>(a);
+        } else {
+            if (p.epilogue == EPI_RELU) head_gemm_kernel<false, true, EPI_RELU, true, true><<<grid, block, 0, stream>>>(a);
+            else if (p.epilogue == EPI_CLAMP1) head_gemm_kernel<false, true, EPI_CLAMP1, true, true><<<grid, block, 0, stream>>>(a);
+            else head_gemm_kernel<false, true, EPI_NONE, true, true><<<grid, block, 0, stream>>>(a);
+        }
+    } else if (!p.fused) {
         if (p.bf16) CX_HG(true, false, EPI_NONE);
         else CX_HG(false, false, EPI_NONE);
     } else if (p.bf16) {

@@ -117,10 +117,12 @@ __host__ __device__ inline void head_row_role(int m, int &tap, int &co) {
 // ---- the head's temporal GEMM (packed like IG_TEMPORAL): plane output or fused stencil -----
 struct HeadGemmParams {
     const void *x, *wp, *bias;
-    void *out;         // the 112-channel plane (fused = false) or y (fused = true)
+    void *out;         // the 112-channel plane (fused = false), y (fused = true) or, with rgb,
+                       // the (N, D, 2H, 2W, 3) uint8 RGB frames of y
     int N, C_in, C_out, D, H, W;   // D, H: output extent
     ConvRegion rg;     // input region (full_region(D, H) for the plain convolution)
     bool bf16, fused;
+    bool rgb;          // fused and C_out == 12 only
     int epilogue;      // fused only
 };
 hipError_t launch_head_gemm(const HeadGemmParams &p, hipStream_t stream);

@@ -10,8 +10,7 @@
 // consecutive positions of one input row: each thread reads its position's 24 bytes, forms the
 // 12 bytes of its 2 x 2 pixel block and puts them into the two output rows staged in LDS; the
 // rows then leave in 16-byte stores (the two output rows of the block are 6*nw contiguous bytes
-// each).  The quantisation runs in fp64, where v*127.5 + 127.5 is exact for every fp16/bf16 value
-// except the tiny ones, whose sum rounds onto the tie 127.5 itself: the sign of v decides those.
+// each).  The code is rgb_code (common.hpp): exact for every fp16/bf16 value.
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -21,16 +20,6 @@ namespace cx {
 namespace {
 
 constexpr int kVidPos = 256;   // positions per workgroup
-
-__device__ __forceinline__ uint32_t code_u8(float v) {
-    const double d = (double)v;
-    const double t = __builtin_fma(d, 127.5, 127.5);
-    double q = __builtin_rint(t);
-    if (d < 0.0 && t == 127.5) q = 127.0;   // below the tie by less than the fp64 spacing
-    if (!(q >= 0.0)) q = 0.0;                // negative codes and NaN
-    if (q > 255.0) q = 255.0;
-    return (uint32_t)q;
-}
 
 template <bool BF>
 __global__ __launch_bounds__(256) void video_rgb8_kernel(const u16 *__restrict__ y,
@@ -55,7 +44,7 @@ __global__ __launch_bounds__(256) void video_rgb8_kernel(const u16 *__restrict__
         uint32_t q[12];
 #pragma unroll
         for (int k = 0; k < 12; ++k)
-            q[k] = code_u8(E::to_f32((u16)(v[k >> 1] >> (16 * (k & 1)))));
+            q[k] = rgb_code(E::to_f32((u16)(v[k >> 1] >> (16 * (k & 1)))));
         // pixel (2h + dy, 2w + dx), colour c <- channel 4c + 2dy + dx
 #pragma unroll
         for (int dy = 0; dy < 2; ++dy)

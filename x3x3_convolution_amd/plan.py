@@ -91,6 +91,19 @@ class Conv3x3x3:
         return y
 
 
+    def rgb8(self, x, rgb=None, stream=None):
+        """The fused head writing the RGB frames of its output (conv3x3x3_head_rgb8); the plan
+        must be a C_out = 12 fused head."""
+        if self.algo != C.ALGO_FUSED_HEAD or self.C_out != 12:
+            raise ValueError("rgb8 needs a fused head with 12 output channels")
+        N, Ci, Co, D, H, W, s, lay, dt = self._shape
+        if rgb is None:
+            rgb = torch.empty((N, D, 2 * H, 2 * W, 3), dtype=torch.uint8, device=x.device)
+        C.conv3x3x3_head_rgb8(x, self.w_packed, self.bias, rgb, N, Ci, D, H, W, dt, self.epi,
+                              stream)
+        return rgb
+
+
 def band_rows(lo, rows, halo, H_global):
     """Region rows of an output band [lo, lo + rows) of a global height H_global whose input
     holds global rows lo - halo .. lo + rows + halo - 1 (rows outside the global height may
