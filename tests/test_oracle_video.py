@@ -66,3 +66,18 @@ def test_video_rgb8_hand_example():
     assert rgb.shape == (1, 1, 2, 2, 3)
     assert rgb[0, 0].tolist() == [[[0, 255, 0], [255, 255, 0]],
                                   [[128, 255, 0], [64, 255, 191]]]
+
+
+def test_single_fp32_rounding_is_exact_for_fp16_and_bf16():
+    """The kernels code a value with one fp32 fused multiply-add (127.5*v + 127.5, rounded once),
+    a round-half-even, the sign rule for a result of exactly 127.5, and a clamp.  Emulated here
+    (the fp64 sum is exact or already at 127.5, so its fp32 rounding is the fma's): equal to the
+    exact oracle for every fp16 and bf16 pattern."""
+    for dt in (oracle.F16, oracle.BF16):
+        v = _all_values(dt)
+        with np.errstate(all="ignore"):
+            t = (v * 127.5 + 127.5).astype(np.float32)
+            q = np.rint(t).astype(np.float64)
+            q = np.where((v < 0) & (t == np.float32(127.5)), 127.0, q)
+            q = np.clip(np.where(np.isnan(q), 0.0, q), 0, 255).astype(np.uint8)
+        assert np.array_equal(q, oracle.quantize_u8(v))
