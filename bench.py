@@ -30,7 +30,7 @@ MFMA_BF16_PEAK_TFS = 2516.6    # MI355X dense bf16 matrix-core peak
 VALU_FP32_PEAK_TFS = 157.3     # MI355X fp32 vector peak (dot2/packed rate)
 KERNEL_SOURCES = {             # dominant-kernel name -> the source file it is built from
     "igemm3d": "x3x3_convolution_amd/csrc/igemm3d.hip",
-    "head_stencil": "x3x3_convolution_amd/csrc/head.hip",
+    "head_stencil": "x3x3_convolution_amd/csrc/stencil.hip",
     "head_fused": "x3x3_convolution_amd/csrc/head.hip",
     "simt2d": "x3x3_convolution_amd/csrc/simt2d.hip",
     "mfma2d": "x3x3_convolution_amd/csrc/mfma2d.hip",
