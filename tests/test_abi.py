@@ -178,9 +178,11 @@ def test_algo_selection_and_buffer_sizes():
                                                 algo) == 8 * 3 * 128 * 32 * 2
     # mid-decoder conv fills the chip without split-K: no workspace
     assert cx.conv3x3x3_workspace_bytes(1, 256, 256, 16, 176, 312, 1, 1, 1, 0) == 0
-    # the small low-res conv splits K over channel chunks: fp32 partials
-    ws = cx.conv3x3x3_workspace_bytes(1, 512, 512, 4, 44, 78, 1, 1, 1, 0)
-    assert ws > 0 and ws % (4 * 44 * 78 * 512 * 4) == 0
+    # the small low-res conv fills the chip with half-size (128-position) tiles: no split-K
+    assert cx.conv3x3x3_workspace_bytes(1, 512, 512, 4, 44, 78, 1, 1, 1, 0) == 0
+    # its first causal frame alone still splits K over channel chunks: fp32 partials
+    ws = cx.conv3x3x3_workspace_bytes(1, 512, 512, 1, 44, 78, 1, 1, 1, 0)
+    assert ws > 0 and ws % (44 * 78 * 512 * 4) == 0
     assert cx.conv3x3x3_workspace_bytes(1, 512, 512, 4, 44, 78, 1, 1, 1, 9) == 0  # invalid
     assert cx.conv3x3x3_packed_weight_bytes(1, 20, 12, 1, 4, 4, 1, 1, 1, 0) == 0  # unsupported
 

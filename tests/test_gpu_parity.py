@@ -113,6 +113,35 @@ def test_conv3d_integer_exact(case):
     assert_bit_exact(y, oracle_3d(x, w, b, epi), x.dtype)
 
 
+# The 32x32 MFMA family (C_out > 16) picks its tile -- 8x32, 16x16 (256 positions), 4x32 or 8x16
+# (128 positions) -- and split-K count from a cost model; these shapes reach each of the eight
+# (tile, split) combinations.  The workspace size says whether K is split.
+CASES_W32_TILES = [
+    # N, Ci, Co, D, H, W, epilogue, tile, split-K
+    (1, 32, 20, 1, 5, 13, "relu", "4x32", False),
+    (1, 64, 20, 1, 5, 13, "none", "4x32", True),
+    (2, 32, 20, 16, 33, 13, "clamp1", "8x16", False),
+    (2, 96, 20, 16, 9, 13, "none", "8x16", True),
+    (2, 32, 20, 16, 33, 17, "relu", "8x32", False),
+    (1, 96, 20, 16, 9, 33, "none", "8x32", True),
+    (2, 32, 260, 16, 33, 13, "none", "16x16", False),
+    (2, 96, 20, 16, 20, 13, "clamp1", "16x16", True),
+]
+
+
+@pytest.mark.parametrize("case", CASES_W32_TILES, ids=["%s-%s" % (c[7], "splitk" if c[8] else "nosplit")
+                                                       for c in CASES_W32_TILES])
+def test_conv3d_w32_tiles_integer_exact(case):
+    N, Ci, Co, D, H, W, epi, tile, splitk = case
+    _say("conv3d w32 tile %s" % (case,))
+    ws = C.conv3x3x3_workspace_bytes(N, Ci, Co, D, H, W, dtype=C.DTYPE_BF16, algo=C.ALGO_MFMA)
+    assert (ws > 0) == splitk
+    x, w, b = si.integer_case("3d", N, Ci, Co, H, W, D=D, dtype="bf16",
+                              seed=300 + CASES_W32_TILES.index(case), device=DEV)
+    y = run_3d(x, w, b, epi, C.ALGO_MFMA, guarded=True)
+    assert_bit_exact(y, oracle_3d(x, w, b, epi), x.dtype)
+
+
 def test_conv3d_no_bias_integer_exact():
     x, w, _ = si.integer_case("3d", 1, 32, 12, 5, 9, D=2, dtype="bf16", seed=3, device=DEV,
                               with_bias=False)

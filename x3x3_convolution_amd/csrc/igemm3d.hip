@@ -260,12 +260,15 @@ __global__ __launch_bounds__(256, 2) void igemm3d_kernel(IgemmKArgs a) {
 // one window buffer never overlaps reads from another, so the three buffers are separate objects
 // and the stage loop is unrolled by three.
 // ---------------------------------------------------------------------------------------------
-// Tile geometry by LW, the columns one 32-lane block spans: LW = 32 gives 8 x 32 positions per
-// workgroup (one row per block), LW = 16 gives 16 x 16 (two rows per block) for narrow frames.
-template <int LW>
+// Tile geometry by LW, the columns one 32-lane block spans, and NB, the 32-position blocks of a
+// tile: LW = 32 gives NB x 32 positions per workgroup (one row per block), LW = 16 gives
+// 2NB x 16 (two rows per block) for narrow frames.  NB = 8 (256 positions, all 256 accumulators
+// of a wave) is the default; NB = 4 halves the tile for convolutions with few positions, which
+// then fill the chip without splitting K.
+template <int LW, int NB_>
 struct W32Geom {
     static constexpr int R = 32 / LW;                    // rows per 32-position block
-    static constexpr int NB = 8;                         // 32-position blocks per tile
+    static constexpr int NB = NB_;                       // 32-position blocks per tile
     static constexpr int TH = NB * R, TW = LW;           // workgroup tile = every wave's tile
     static constexpr int WW = TW + 2;                    // window columns used
     static constexpr int RowPos = (WW + 3) / 4 * 4;      // window row stride (positions)
@@ -317,10 +320,10 @@ __device__ __forceinline__ uint32_t w32_block_order(uint32_t b, uint32_t total, 
     return le / (uint32_t)D;
 }
 
-template <bool BF, int EPI, bool SPLITK, int LW>
+template <bool BF, int EPI, bool SPLITK, int LW, int NB>
 __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
     using E = Elem<BF>;
-    using G = W32Geom<LW>;
+    using G = W32Geom<LW, NB>;
     typedef typename E::vec8 vec8;
     typedef __attribute__((address_space(3))) void lds_void;
     __shared__ __attribute__((aligned(16))) uint4 Win0[G::Slots];
@@ -628,13 +631,13 @@ hipError_t launch_family(const IgemmPlan &pl, const IgemmKArgs &ka, int epi, boo
     return hipGetLastError();
 }
 
-template <bool BF, int LW>
+template <bool BF, int LW, int NB>
 hipError_t launch_w32(const IgemmKArgs &ka, int epi, bool splitk, dim3 grid, hipStream_t s) {
     const dim3 block(256);
-    if (splitk) igemm32_kernel<BF, EPI_NONE, true, LW><<<grid, block, 0, s>>>(ka);
-    else if (epi == EPI_RELU) igemm32_kernel<BF, EPI_RELU, false, LW><<<grid, block, 0, s>>>(ka);
-    else if (epi == EPI_CLAMP1) igemm32_kernel<BF, EPI_CLAMP1, false, LW><<<grid, block, 0, s>>>(ka);
-    else igemm32_kernel<BF, EPI_NONE, false, LW><<<grid, block, 0, s>>>(ka);
+    if (splitk) igemm32_kernel<BF, EPI_NONE, true, LW, NB><<<grid, block, 0, s>>>(ka);
+    else if (epi == EPI_RELU) igemm32_kernel<BF, EPI_RELU, false, LW, NB><<<grid, block, 0, s>>>(ka);
+    else if (epi == EPI_CLAMP1) igemm32_kernel<BF, EPI_CLAMP1, false, LW, NB><<<grid, block, 0, s>>>(ka);
+    else igemm32_kernel<BF, EPI_NONE, false, LW, NB><<<grid, block, 0, s>>>(ka);
     return hipGetLastError();
 }
 
@@ -644,8 +647,14 @@ hipError_t launch_igemm_dtype(const IgemmPlan &pl, const IgemmKArgs &ka, int epi
     switch (pl.family) {
         case IG_W32: {
             const dim3 grid((unsigned)pl.workgroups);
-            if (pl.TW == 32) return launch_w32<BF, 32>(ka, epi, splitk, grid, s);
-            return launch_w32<BF, 16>(ka, epi, splitk, grid, s);
+            if (pl.TW == 32) {
+                if (pl.TH == 8) return launch_w32<BF, 32, 8>(ka, epi, splitk, grid, s);
+                if (pl.TH == 4) return launch_w32<BF, 32, 4>(ka, epi, splitk, grid, s);
+            } else if (pl.TW == 16) {
+                if (pl.TH == 16) return launch_w32<BF, 16, 8>(ka, epi, splitk, grid, s);
+                if (pl.TH == 8) return launch_w32<BF, 16, 4>(ka, epi, splitk, grid, s);
+            }
+            return hipErrorInvalidValue;
         }
         case IG_WIDE:
             return launch_family<BF, 4, 4, 2, 2, 8, 16>(pl, ka, epi, splitk, s);
@@ -669,16 +678,11 @@ IgemmPlan plan_igemm(int family, int N, int C_in, int C_out, int D, int H, int W
             pl.BM = 16, pl.TH = 8, pl.TW = 32, pl.ntaps = 27;
             pl.Mrows = C_out;
             break;
-        case IG_W32: {
-            // 8 x 32 tiles, or 16 x 16 when those compute fewer padded positions (narrow frames)
+        case IG_W32:   // tile geometry chosen with the split count below
             pl.BM = 256, pl.ntaps = 27;
             pl.Mrows = C_out;
-            const long long a32 = (long long)((H + 7) / 8) * 8 * ((W + 31) / 32) * 32;
-            const long long a16 = (long long)((H + 15) / 16) * 16 * ((W + 15) / 16) * 16;
-            if (a16 < a32) pl.TH = 16, pl.TW = 16;
-            else pl.TH = 8, pl.TW = 32;
+            pl.TH = 8, pl.TW = 32;
             break;
-        }
         default:   // the head kernels: 3 temporal taps x 128 rows (9 * C_out used)
             pl.BM = 128, pl.TH = 1, pl.TW = 256, pl.ntaps = 3;
             pl.Mrows = 128;
@@ -700,19 +704,30 @@ IgemmPlan plan_igemm(int family, int N, int C_in, int C_out, int D, int H, int W
     // Split K when the output alone cannot fill the 256 compute units a few times over.
     int splits = 1;
     if (family == IG_W32 && base > 0) {
-        // One workgroup per CU: pick the split count minimising rounds of 256 workgroups x
-        // (stages per workgroup + about one stage of prologue/epilogue) plus the fp32 partials'
-        // round trip (8 bytes per partial element at HBM speed: about one stage per 3.75 M).
+        // One workgroup per CU: pick the tile geometry and split count minimising rounds of 256
+        // workgroups x (stages per workgroup x the tile's cost per stage + about one stage of
+        // prologue/epilogue) plus the fp32 partials' round trip (8 bytes per partial element at
+        // HBM speed: about one stage per 3.75 M).  A 4-block tile does half the MFMAs of an
+        // 8-block one per stage for the same weight stream: about 0.55 of its time.
+        static const struct { int TH, TW; double cost; } geo[4] = {
+            {8, 32, 1.0}, {16, 16, 1.0}, {4, 32, 0.55}, {8, 16, 0.55}};
         const double taps = D >= 3 ? (3.0 * D - 2.0) / D : (D == 2 ? 2.0 : 1.0);
         const double part = (double)N * D * H * W * C_out / 3.75e6;
         double best = -1.0;
-        for (int sp = 1; sp <= pl.nchunks; ++sp) {
-            const int cps = (pl.nchunks + sp - 1) / sp;
-            const int se = (pl.nchunks + cps - 1) / cps;
-            if (se != sp) continue;
-            const long long rounds = (base * se + 255) / 256;
-            const double cost = rounds * (cps * taps + 1.0) + (se > 1 ? se * part : 0.0);
-            if (best < 0 || cost < best) best = cost, splits = se;
+        for (const auto &g : geo) {
+            const long long th = (H + g.TH - 1) / g.TH, tw = (W + g.TW - 1) / g.TW;
+            const long long gbase = (long long)N * D * th * tw * pl.mtiles;
+            for (int sp = 1; sp <= pl.nchunks; ++sp) {
+                const int cps = (pl.nchunks + sp - 1) / sp;
+                const int se = (pl.nchunks + cps - 1) / cps;
+                if (se != sp) continue;
+                const long long rounds = (gbase * se + 255) / 256;
+                const double cost = rounds * (cps * taps * g.cost + 1.0) + (se > 1 ? se * part : 0.0);
+                if (best < 0 || cost < best - 1e-9) {
+                    best = cost, splits = se;
+                    pl.TH = g.TH, pl.TW = g.TW, pl.tiles_h = (int)th, pl.tiles_w = (int)tw;
+                }
+            }
         }
     } else if (family != IG_TEMPORAL && base > 0 && base < 1024) {
         // (the 16x16 kernels run two workgroups per CU)
@@ -721,7 +736,7 @@ IgemmPlan plan_igemm(int family, int N, int C_in, int C_out, int D, int H, int W
     }
     pl.chunks_per_split = (pl.nchunks + splits - 1) / splits;
     pl.splits = (pl.nchunks + pl.chunks_per_split - 1) / pl.chunks_per_split;
-    pl.workgroups = base * pl.splits;
+    pl.workgroups = (long long)N * D * pl.tiles_h * pl.tiles_w * pl.mtiles * pl.splits;
     return pl;
 }
 
