@@ -57,10 +57,10 @@ struct M2Geom<1> {
     static constexpr int WRows = 18;     // window rows
     static constexpr int RowPos = 36;    // window row stride in positions (34 used)
     static constexpr int Groups = 6;     // 8-column load groups per window row
-    // the next window's column x (of both load units) is written after slice CommitFirst + x:
-    // late in the stage (its loads were issued before it) and one column per slice, so the
-    // transposes and LDS writes hide between the MFMAs
-    static constexpr int CommitFirst = 10;
+    // the next window's columns are written after slices CommitFirst .. 17, (8 / (18 -
+    // CommitFirst)) per slice: as late in the stage as possible (its loads were issued at the
+    // stage's start), the transposes and LDS writes hidden between the MFMAs
+    static constexpr int CommitFirst = 16;
 };
 template <>
 struct M2Geom<2> {
@@ -70,11 +70,12 @@ struct M2Geom<2> {
     static constexpr int WRows = 9;
     static constexpr int RowPos = 72;    // odd input columns at 0..32, even ones at 36..67
     static constexpr int Groups = 9;
-    static constexpr int CommitFirst = 10;
+    static constexpr int CommitFirst = 16;
 };
 static_assert(M2Geom<1>::WRows * M2Geom<1>::RowPos * 4 == kWinSlots, "window size");
 static_assert(M2Geom<2>::WRows * M2Geom<2>::RowPos * 4 == kWinSlots, "window size");
-static_assert(M2Geom<1>::CommitFirst + 8 == 18 && M2Geom<2>::CommitFirst + 8 == 18, "8 columns");
+static_assert(8 % (18 - M2Geom<1>::CommitFirst) == 0 && 8 % (18 - M2Geom<2>::CommitFirst) == 0,
+              "whole columns per slice");
 static_assert(M2Geom<1>::NWaves * M2Geom<1>::NBW == M2Geom<1>::TH, "waves cover the tile rows");
 static_assert(M2Geom<2>::NWaves * M2Geom<2>::NBW == M2Geom<2>::TH, "waves cover the tile rows");
 
@@ -310,7 +311,7 @@ __global__ __launch_bounds__(64 * M2Geom<S>::NWaves, 1) void mfma2d_kernel(Mfma2
     };
 
     // run one 32-channel stage into cacc: 18 k16 slices (9 taps x 2); the next stage's window
-    // is written column by column after slices CommitFirst .. 17, and the previous tile's
+    // is written a few columns at a time after slices CommitFirst .. 17, and the previous tile's
     // results (pacc, tile pit) are stored over the first slices when has_prev
     auto run_stage = [&](AccSet &cacc, const uint4 *win, const uint4 *wc, uint4 *next_win,
                          bool has_next, AccSet &pacc, int pit, bool has_prev) __attribute__((always_inline)) {
@@ -344,7 +345,11 @@ __global__ __launch_bounds__(64 * M2Geom<S>::NWaves, 1) void mfma2d_kernel(Mfma2
                     if (gi < kGroups) store_group(pacc, gi, poh0, pow0, yr);
                 }
             }
-            if (q >= G::CommitFirst && has_next) commit_col(next_win, q - G::CommitFirst);
+            if (q >= G::CommitFirst && has_next) {
+                constexpr int cps = 8 / (18 - G::CommitFirst);   // columns per slice
+#pragma unroll
+                for (int x = 0; x < cps; ++x) commit_col(next_win, (q - G::CommitFirst) * cps + x);
+            }
         }
     };
     // one tile into cacc, storing the previous one's results (pacc) during its first stage
