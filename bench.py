@@ -77,6 +77,8 @@ def parse():
                          "band8: the middle eighth of the rows with a one-row halo each side "
                          "(one GPU's share when the rows are split over eight); causal: every "
                          "frame with causal temporal padding and two cached frames in front")
+    ap.add_argument("--channels-last", action="store_true",
+                    help="2D workloads only: NHWC activations instead of NCHW")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (used for profiler runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -311,11 +313,14 @@ def run_other(args, wl, stream):
 
     x, w, b = si.make_inputs(wl, device="cuda")
     if wl.kind == "2d":
-        op = Conv3x3(w, b, wl.N, wl.H, wl.W, stride=wl.stride, epilogue=wl.epilogue)
+        if args.channels_last:
+            x = x.permute(0, 2, 3, 1).contiguous()
+        op = Conv3x3(w, b, wl.N, wl.H, wl.W, stride=wl.stride, epilogue=wl.epilogue,
+                     channels_last=args.channels_last)
         P = wl.N * wl.H_out * wl.W_out
         flop = 2.0 * wl.C_in * wl.C_out * wl.N * live_taps(wl.H, wl.stride) * live_taps(wl.W, wl.stride)
-        algo2d = C.conv3x3_select_algo(wl.N, wl.C_in, wl.C_out, wl.H, wl.W, wl.stride,
-                                       C.LAYOUT_CHANNELS_FIRST, C.DTYPE_F16, C.ALGO_AUTO)
+        algo2d = C.conv3x3_select_algo(wl.N, wl.C_in, wl.C_out, wl.H, wl.W, wl.stride, op.layout,
+                                       C.DTYPE_F16, C.ALGO_AUTO)
         if algo2d == C.ALGO_MFMA:
             # a stream at the HBM / matrix-core ridge: graded against HBM, MFMA reported beside
             kname, bound, peak, unit = "mfma2d", "hbm", HBM_PEAK_GBS, "GB/s"
@@ -346,7 +351,8 @@ def run_other(args, wl, stream):
     roof = dict(kernel=kname, bound=bound, achieved=ach, peak=peak, unit=unit, frac=ach / peak,
                 hbm_gbs=gbs, hbm_frac=gbs / HBM_PEAK_GBS, algorithmic_flop=flop,
                 algorithmic_bytes=nbytes, avg_launch_ms=kms, positions=P,
-                traffic=traffic_from_profiles(kname, wl.name, "auto"))
+                traffic=traffic_from_profiles(kname, wl.name,
+                                              "nhwc" if getattr(args, "channels_last", False) else "auto"))
     if kname == "mfma2d":
         roof.update(mfma_tflops=tflops, mfma_frac=tflops / MFMA_BF16_PEAK_TFS)
     return wall_ms, roof
@@ -464,9 +470,11 @@ def main():
             line["cpu_baseline"] = cpu_baseline(wl, tensors, args.cpu_seconds)
     else:
         wall_ms, roof = run_other(args, wl, stream)
+        layout = ("NHWC" if args.channels_last else "NCHW") if wl.kind == "2d" else "NDHWC"
         line.update(value=round(wall_ms, 4), unit="ms", ms_per_step=round(wall_ms, 4),
                     config=dict(workload=wl.name, N=wl.N, C_in=wl.C_in, C_out=wl.C_out, D=wl.D,
-                                H=wl.H, W=wl.W, stride=wl.stride, epilogue=wl.epilogue),
+                                H=wl.H, W=wl.W, stride=wl.stride, epilogue=wl.epilogue,
+                                layout=layout),
                     roofline={k: (round(v, 6) if isinstance(v, float) else v)
                               for k, v in roof.items()})
     print(json.dumps(line), flush=True)

@@ -96,9 +96,11 @@ int conv_out_size(int in, int stride);
 /* ------------------------------------------------------------------------------------------
  * 2D: x (N,C_in,H,W) NCHW, w (C_out,C_in,3,3) OIHW as stored by PyTorch (no packing), bias
  * (C_out) or NULL, y (N,C_out,H_out,W_out) NCHW; all of `dtype`.  stride 1 or 2.
- * Supported: layout CHANNELS_FIRST, dtype F16 or BF16; algo SIMT: any C_in/C_out >= 1; algo
- * MFMA: C_in % 8 == 0, C_in <= 64, C_out <= 64, W % 8 == 0, one image of x and of y below 2 GiB
- * (else CONV_E_UNSUPPORTED); AUTO: MFMA when it applies, else SIMT.
+ * layout CHANNELS_LAST: x (N,H,W,C_in) and y (N,H_out,W_out,C_out) NHWC, same w and bias.
+ * Supported: dtype F16 or BF16.  NCHW: algo SIMT: any C_in/C_out >= 1; algo MFMA: C_in % 8 ==
+ * 0, C_in <= 64, C_out <= 64, W % 8 == 0, one image of x and of y below 2 GiB (else
+ * CONV_E_UNSUPPORTED); AUTO: MFMA when it applies, else SIMT.  NHWC: MFMA only (AUTO selects
+ * it), C_in % 8 == 0, C_in <= 64, C_out <= 64, any W, one image of x and of y below 2 GiB.
  * [taesd_conv.cuh.new: operator contract in the header comment; the kernels' argument lists]
  * ---------------------------------------------------------------------------------------- */
 int conv3x3_fwd(const void *x, const void *w, const void *bias, void *y, int N, int C_in,

@@ -93,7 +93,11 @@ def test_2d_invalid_arguments():
     assert f2d(bias=A + 1) == C.E_INVAL         # misaligned bias
     assert f2d(y=A + 64) == C.E_INVAL           # overlaps x
     assert "overlap" in cx.conv_last_error()
-    assert f2d(layout=1) == C.E_UNSUPPORTED     # NHWC
+    # NHWC runs on the matrix-core kernel only: C_in a multiple of 8 up to 64, C_out up to 64
+    assert f2d(layout=1, algo=C.ALGO_SIMT) == C.E_UNSUPPORTED
+    assert f2d(layout=1, C_in=12) == C.E_UNSUPPORTED
+    assert f2d(layout=1, C_out=65) == C.E_UNSUPPORTED
+    assert f2d(layout=1, C_in=72) == C.E_UNSUPPORTED
     assert f2d(algo=C.ALGO_MFMA, C_in=12) == C.E_UNSUPPORTED     # C_in not a multiple of 8
     assert f2d(algo=C.ALGO_MFMA, C_in=72) == C.E_UNSUPPORTED     # C_in above 64
     assert f2d(algo=C.ALGO_MFMA, C_out=65) == C.E_UNSUPPORTED
@@ -150,11 +154,18 @@ def test_2d_algo_selection():
     assert cx.conv3x3_is_supported(1, 8, 8, 8, 20, 1, 0, 0, 1, C.ALGO_MFMA) == C.E_UNSUPPORTED
     with pytest.raises(C.ConvError):
         cx.conv3x3_select_algo(1, 8, 8, 8, 20, 1, 0, 0, C.ALGO_MFMA)
+    # NHWC: always the matrix-core kernel, any width
+    assert cx.conv3x3_select_algo(2, 8, 7, 13, 37, 1, 1, 0, C.ALGO_AUTO) == C.ALGO_MFMA
+    with pytest.raises(C.ConvError):
+        cx.conv3x3_select_algo(2, 8, 7, 13, 37, 1, 1, 0, C.ALGO_SIMT)
+    with pytest.raises(C.ConvError):
+        cx.conv3x3_select_algo(2, 5, 7, 13, 37, 1, 1, 0, C.ALGO_AUTO)
 
 
 def test_is_supported_matches_fwd_checks():
     assert cx.conv3x3_is_supported(8, 64, 64, 256, 256, 2, 0, 0, 1, 0) == C.OK
-    assert cx.conv3x3_is_supported(8, 64, 64, 256, 256, 2, 1, 0, 1, 0) == C.E_UNSUPPORTED
+    assert cx.conv3x3_is_supported(8, 64, 64, 256, 256, 2, 1, 0, 1, 0) == C.OK   # NHWC
+    assert cx.conv3x3_is_supported(8, 64, 64, 256, 256, 2, 1, 0, 1, C.ALGO_SIMT) == C.E_UNSUPPORTED
     assert cx.conv3x3x3_is_supported(1, 256, 12, 16, 352, 624, 1, 1, 1, 2, 0) == C.OK
     assert cx.conv3x3x3_is_supported(1, 256, 12, 16, 352, 624, 1, 1, 1, 2, C.ALGO_SPLIT_HEAD) == C.OK
     assert cx.conv3x3x3_is_supported(1, 256, 256, 16, 176, 312, 1, 1, 1, 0, C.ALGO_SPLIT_HEAD) == C.E_UNSUPPORTED
@@ -199,6 +210,8 @@ def test_pack_invalid():
 @pytest.mark.skipif(HAS_GPU, reason="checks the no-device path; a GPU is visible")
 def test_no_device_reported_after_validation():
     assert f2d() == C.E_NODEVICE
+    assert f2d(layout=1) == C.E_NODEVICE           # NHWC
+    assert f2d(layout=1, W=13, stride=2) == C.E_NODEVICE   # NHWC takes any width
     assert f3d() == C.E_NODEVICE
     assert "device" in cx.conv_last_error()
 

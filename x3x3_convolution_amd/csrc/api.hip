@@ -67,13 +67,16 @@ int check_2d(int N, int C_in, int C_out, int H, int W, int stride, int layout, i
             return fail(CONV_E_INVAL, "unknown algo %d", algo);
         return fail(CONV_E_UNSUPPORTED, "2D convolution supports algo AUTO, SIMT or MFMA (got %d)", algo);
     }
-    if (layout != CONV_LAYOUT_CHANNELS_FIRST)
-        return fail(CONV_E_UNSUPPORTED, "2D convolution supports the NCHW layout only");
-    if (algo == CONV_ALGO_MFMA) {
-        if (!cx::mfma2d_supported(C_in, C_out, H, W, stride))
+    const bool nhwc = layout == CONV_LAYOUT_CHANNELS_LAST;
+    if (nhwc && algo == CONV_ALGO_SIMT)
+        return fail(CONV_E_UNSUPPORTED, "the SIMT 2D kernel supports the NCHW layout only");
+    if (algo == CONV_ALGO_MFMA || nhwc) {
+        if (!cx::mfma2d_supported(C_in, C_out, H, W, stride, nhwc))
             return fail(CONV_E_UNSUPPORTED,
-                        "2D MFMA needs C_in a multiple of 8 up to 64, C_out up to 64 and W a "
-                        "multiple of 8 (got C_in=%d C_out=%d W=%d)", C_in, C_out, W);
+                        nhwc ? "2D NHWC needs C_in a multiple of 8 up to 64 and C_out up to 64 "
+                               "(got C_in=%d C_out=%d W=%d)"
+                             : "2D MFMA needs C_in a multiple of 8 up to 64, C_out up to 64 and W a "
+                               "multiple of 8 (got C_in=%d C_out=%d W=%d)", C_in, C_out, W);
         if ((long long)C_in * H * W * 2 >= (1ll << 31) ||
             (long long)C_out * ((H - 1) / stride + 1) * ((W - 1) / stride + 1) * 2 >= (1ll << 31))
             return fail(CONV_E_UNSUPPORTED, "2D MFMA needs one image of x and of y below 2 GiB");
@@ -86,14 +89,16 @@ int check_2d(int N, int C_in, int C_out, int H, int W, int stride, int layout, i
     return CONV_OK;
 }
 
-// The concrete 2D algorithm of a request that passed check_2d: MFMA when asked for, or for AUTO
-// when the matrix-core kernel applies and its sample fits the 32-bit buffer ranges; else SIMT.
-int select_2d(int C_in, int C_out, int H, int W, int stride, int algo) {
-    if (algo == CONV_ALGO_MFMA) return CONV_ALGO_MFMA;
+// The concrete 2D algorithm of a request that passed check_2d: MFMA when asked for or for NHWC
+// (which only the matrix-core kernel takes), or for AUTO when the matrix-core kernel applies and
+// its sample fits the 32-bit buffer ranges; else SIMT.
+int select_2d(int C_in, int C_out, int H, int W, int stride, int layout, int algo) {
+    if (algo == CONV_ALGO_MFMA || layout == CONV_LAYOUT_CHANNELS_LAST) return CONV_ALGO_MFMA;
     if (algo == CONV_ALGO_SIMT) return CONV_ALGO_SIMT;
     const bool fits = (long long)C_in * H * W * 2 < (1ll << 31) &&
                       (long long)C_out * ((H - 1) / stride + 1) * ((W - 1) / stride + 1) * 2 < (1ll << 31);
-    return cx::mfma2d_supported(C_in, C_out, H, W, stride) && fits ? CONV_ALGO_MFMA : CONV_ALGO_SIMT;
+    return cx::mfma2d_supported(C_in, C_out, H, W, stride, false) && fits ? CONV_ALGO_MFMA
+                                                                           : CONV_ALGO_SIMT;
 }
 
 // ---- 3D ------------------------------------------------------------------------------------
@@ -194,7 +199,7 @@ int conv3x3_select_algo(int N, int C_in, int C_out, int H, int W, int stride, in
     const int st = check_2d(N, C_in, C_out, H, W, stride, layout, dtype, CONV_EPI_NONE, algo);
     if (st) return st;
     ok();
-    return select_2d(C_in, C_out, H, W, stride, algo);
+    return select_2d(C_in, C_out, H, W, stride, layout, algo);
 }
 
 int conv3x3_fwd(const void *x, const void *w, const void *bias, void *y, int N, int C_in,
@@ -221,7 +226,8 @@ int conv3x3_fwd(const void *x, const void *w, const void *bias, void *y, int N, 
     p.x = x, p.w = w, p.bias = bias, p.y = y;
     p.N = N, p.C_in = C_in, p.C_out = C_out, p.H = H, p.W = W, p.Hout = Ho, p.Wout = Wo;
     p.stride = stride, p.bf16 = dtype == CONV_DTYPE_BF16, p.epilogue = epilogue;
-    if (select_2d(C_in, C_out, H, W, stride, algo) == CONV_ALGO_MFMA) {
+    p.nhwc = layout == CONV_LAYOUT_CHANNELS_LAST;
+    if (select_2d(C_in, C_out, H, W, stride, layout, algo) == CONV_ALGO_MFMA) {
         const hipError_t e = cx::launch_mfma2d(p, (hipStream_t)stream);
         if (e != hipSuccess) return fail(CONV_E_LAUNCH, "MFMA 2D launch failed: %s", hipGetErrorString(e));
         return ok();

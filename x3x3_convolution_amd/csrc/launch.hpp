@@ -14,12 +14,13 @@ struct Simt2dParams {
     void *y;
     int N, C_in, C_out, H, W, Hout, Wout, stride;
     bool bf16;
+    bool nhwc;         // channels-last x and y (matrix-core kernel only)
     int epilogue;
 };
 hipError_t launch_simt2d(const Simt2dParams &p, hipStream_t stream);
 
-// ---- 2D on the matrix cores (NCHW, C_in and C_out <= 64, C_in % 8 == 0, W % 8 == 0) ------
-bool mfma2d_supported(int C_in, int C_out, int H, int W, int stride);
+// ---- 2D on the matrix cores (C_in and C_out <= 64, C_in % 8 == 0; NCHW also W % 8 == 0) ----
+bool mfma2d_supported(int C_in, int C_out, int H, int W, int stride, bool nhwc);
 hipError_t launch_mfma2d(const Simt2dParams &p, hipStream_t stream);
 
 // ---- 3D input regions ------------------------------------------------------------------------

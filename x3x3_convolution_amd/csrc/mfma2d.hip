@@ -56,7 +56,8 @@ struct M2Geom<1> {
     static constexpr int NBW = 2;        // 32-position blocks per wave (output rows)
     static constexpr int WRows = 18;     // window rows
     static constexpr int RowPos = 36;    // window row stride in positions (34 used)
-    static constexpr int Groups = 6;     // 8-column load groups per window row
+    static constexpr int Groups = 6;     // 8-column load groups per window row (NCHW)
+    static constexpr int WCols = 34;     // window columns (NHWC: one load per position piece)
     // the next window's columns are written after slices CommitFirst .. 17, (8 / (18 -
     // CommitFirst)) per slice: as late in the stage as possible (its loads were issued at the
     // stage's start), the transposes and LDS writes hidden between the MFMAs
@@ -70,6 +71,7 @@ struct M2Geom<2> {
     static constexpr int WRows = 9;
     static constexpr int RowPos = 72;    // odd input columns at 0..32, even ones at 36..67
     static constexpr int Groups = 9;
+    static constexpr int WCols = 65;
     static constexpr int CommitFirst = 16;
 };
 static_assert(M2Geom<1>::WRows * M2Geom<1>::RowPos * 4 == kWinSlots, "window size");
@@ -104,7 +106,9 @@ __device__ __forceinline__ uint32_t m2_pack(uint32_t a, int h0, uint32_t b, int 
     return ((a >> (16 * h0)) & 0xFFFFu) | (((b >> (16 * h1)) & 0xFFFFu) << 16);
 }
 
-template <bool BF, int S, int EPI>
+// NHWC: channels-last x and y; C4 (NHWC only): C_out % 4 == 0, so a lane's four channels of a
+// position are stored as one 8-byte piece.
+template <bool BF, int S, int EPI, bool NHWC, bool C4>
 __global__ __launch_bounds__(64 * M2Geom<S>::NWaves, 1) void mfma2d_kernel(Mfma2dKArgs a) {
     using E = Elem<BF>;
     using G = M2Geom<S>;
@@ -169,38 +173,52 @@ __global__ __launch_bounds__(64 * M2Geom<S>::NWaves, 1) void mfma2d_kernel(Mfma2
         oh0 = th * G::TH, ow0 = tw * kTW;
     };
 
-    // ---- input window staging: unit u = (window row, 8-column group, channel octet) ----
-    // A thread owns units tid + k * kThreads.  The LDS slot each of a unit's eight columns goes to
-    // does not depend on the tile, so it is computed once: columns outside the window (the
-    // unused part of the edge groups) and units past the window go to a column no fragment read
-    // touches (RowPos leaves spare columns in every row), which keeps the writes branch-free.
-    constexpr int kUnits = G::WRows * G::Groups * 4;
+    // ---- input window staging ----
+    // NCHW: unit u = (window row, 8-column group, channel octet); a unit is eight 16-byte loads
+    // along W (8 columns of one channel each), transposed in registers.  NHWC: unit u = (window
+    // row, window column, 16-byte piece); a unit is one 16-byte load of 8 channels of one
+    // position, already in the LDS order.
+    // A thread owns units tid + k * kThreads.  The LDS slot a unit (column) goes to does not
+    // depend on the tile, so it is computed once: columns outside the window (the unused part of
+    // the NCHW edge groups) and units past the window go to a column no fragment read touches
+    // (RowPos leaves spare columns in every row), which keeps the writes branch-free.
+    constexpr int kUnits = NHWC ? G::WRows * G::WCols * 4 : G::WRows * G::Groups * 4;
     constexpr int kUPT = (kUnits + kThreads - 1) / kThreads;   // load units per thread
+    constexpr int kLoads = NHWC ? 1 : 8;                       // 16-byte loads per unit
     constexpr int kTrash = S == 1 ? 34 : 33;
-    uint4 sv[kUPT][8];
-    int wslot[kUPT][8];
+    uint4 sv[kUPT][kLoads];
+    int wslot[kUPT][kLoads];
+    // window column (input order, 0 = input column S*ow0 - 1) -> LDS column: at stride 2 the
+    // even window columns (taps kx = 0, 2) come first and the odd ones (kx = 1) from column 36
+    auto lds_col = [](int cw) { return S == 1 ? cw : ((cw & 1) ? 36 + (cw >> 1) : (cw >> 1)); };
 #pragma unroll
     for (int k = 0; k < kUPT; ++k) {
         const int u = tid + kThreads * k;
-        const int o = u & 3, rg = u >> 2;
-        const int g = rg % G::Groups;
         const bool uok = u < kUnits;
-        const int r = uok ? rg / G::Groups : 0;
+        if constexpr (NHWC) {
+            const int o = u & 3, pos = uok ? u >> 2 : 0;
+            const int r = pos / G::WCols, cw = pos - r * G::WCols;
+            wslot[k][0] = m2_slot(r, uok ? lds_col(cw) : kTrash, o, G::RowPos);
+        } else {
+            const int o = u & 3, rg = u >> 2;
+            const int g = rg % G::Groups;
+            const int r = uok ? rg / G::Groups : 0;
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-            int col;
-            if constexpr (S == 1) {
-                col = g == 0 ? (x == 7 ? 0 : kTrash)
-                             : (g == G::Groups - 1 ? (x == 0 ? 33 : kTrash) : 1 + 8 * (g - 1) + x);
-            } else {
-                col = g == 0 ? (x == 7 ? 0 : kTrash)
-                             : ((x & 1) ? 4 * (g - 1) + (x + 1) / 2 : 36 + 4 * (g - 1) + x / 2);
+            for (int x = 0; x < 8; ++x) {
+                int col;
+                if constexpr (S == 1) {
+                    col = g == 0 ? (x == 7 ? 0 : kTrash)
+                                 : (g == G::Groups - 1 ? (x == 0 ? 33 : kTrash) : 1 + 8 * (g - 1) + x);
+                } else {
+                    col = g == 0 ? (x == 7 ? 0 : kTrash)
+                                 : ((x & 1) ? 4 * (g - 1) + (x + 1) / 2 : 36 + 4 * (g - 1) + x / 2);
+                }
+                if (!uok) col = kTrash;
+                wslot[k][x] = m2_slot(r, col, o, G::RowPos);
             }
-            if (!uok) col = kTrash;
-            wslot[k][x] = m2_slot(r, col, o, G::RowPos);
         }
     }
-    // loads of the two units of this thread for stage (tile it, channel half c)
+    // loads of this thread's units for stage (tile it, channel half c)
     auto issue = [&](int it, int c) {
         int n, oh0, ow0;
         tile_coords(it, n, oh0, ow0);
@@ -209,33 +227,50 @@ __global__ __launch_bounds__(64 * M2Geom<S>::NWaves, 1) void mfma2d_kernel(Mfma2
 #pragma unroll
         for (int k = 0; k < kUPT; ++k) {
             const int u = tid + kThreads * k;
-            const int o = u & 3, rg = u >> 2;
-            const int g = rg % G::Groups, r = rg / G::Groups;
-            const int ih = S * oh0 - 1 + r;
-            const int iw0 = S * ow0 - 8 + 8 * g;
+            const int o = u & 3;
             const int ch0 = 32 * c + 8 * o;
-            const bool ok = u < kUnits && (unsigned)ih < (unsigned)a.H &&
-                            (unsigned)iw0 < (unsigned)a.W && ch0 < a.C_in;
-            const uint32_t base = ok ? (uint32_t)(((ch0 * a.H + ih) * a.W + iw0) * 2) : kOff;
+            if constexpr (NHWC) {
+                const int pos = u >> 2;
+                const int r = pos / G::WCols, cw = pos - r * G::WCols;
+                const int ih = S * oh0 - 1 + r, iw = S * ow0 - 1 + cw;
+                const bool ok = u < kUnits && (unsigned)ih < (unsigned)a.H &&
+                                (unsigned)iw < (unsigned)a.W && ch0 < a.C_in;
+                const uint32_t off = ok ? (uint32_t)(((ih * a.W + iw) * a.C_in + ch0) * 2) : kOff;
+                sv[k][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+            } else {
+                const int rg = u >> 2;
+                const int g = rg % G::Groups, r = rg / G::Groups;
+                const int ih = S * oh0 - 1 + r;
+                const int iw0 = S * ow0 - 8 + 8 * g;
+                const bool ok = u < kUnits && (unsigned)ih < (unsigned)a.H &&
+                                (unsigned)iw0 < (unsigned)a.W && ch0 < a.C_in;
+                const uint32_t base = ok ? (uint32_t)(((ch0 * a.H + ih) * a.W + iw0) * 2) : kOff;
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                sv[k][e] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                    xr, __builtin_elementwise_add_sat(base, (uint32_t)(e * HW * 2)), 0, 0));
+                for (int e = 0; e < 8; ++e)
+                    sv[k][e] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                        xr, __builtin_elementwise_add_sat(base, (uint32_t)(e * HW * 2)), 0, 0));
+            }
         }
     };
-    // column x of both units, transposed to one position's 8 channels each (v_perm picks the
-    // two halves) and written to a window buffer
+    // part x (0..7) of the loaded window into a window buffer.  NCHW: column x of every unit,
+    // transposed to one position's 8 channels each (v_perm picks the two halves).  NHWC: units
+    // [x*kUPT/8, (x+1)*kUPT/8) as they are.
     auto commit_col = [&](uint4 *win, int x) {
-        const int dw = x >> 1;
-        const uint32_t sel = (x & 1) ? 0x07060302u : 0x05040100u;
+        if constexpr (NHWC) {
 #pragma unroll
-        for (int k = 0; k < kUPT; ++k) {
-            uint32_t d[4];
+            for (int k = x * kUPT / 8; k < (x + 1) * kUPT / 8; ++k) win[wslot[k][0]] = sv[k][0];
+        } else {
+            const int dw = x >> 1;
+            const uint32_t sel = (x & 1) ? 0x07060302u : 0x05040100u;
 #pragma unroll
-            for (int dd = 0; dd < 4; ++dd)
-                d[dd] = __builtin_amdgcn_perm(m2_dword(sv[k][2 * dd + 1], dw),
-                                              m2_dword(sv[k][2 * dd], dw), sel);
-            win[wslot[k][x]] = uint4{d[0], d[1], d[2], d[3]};
+            for (int k = 0; k < kUPT; ++k) {
+                uint32_t d[4];
+#pragma unroll
+                for (int dd = 0; dd < 4; ++dd)
+                    d[dd] = __builtin_amdgcn_perm(m2_dword(sv[k][2 * dd + 1], dw),
+                                                  m2_dword(sv[k][2 * dd], dw), sel);
+                win[wslot[k][x]] = uint4{d[0], d[1], d[2], d[3]};
+            }
         }
     };
 
@@ -281,8 +316,31 @@ __global__ __launch_bounds__(64 * M2Geom<S>::NWaves, 1) void mfma2d_kernel(Mfma2
     auto store_group = [&](AccSet &pacc, int gi, int oh0, int ow0,
                            const __amdgpu_buffer_rsrc_t &yr) __attribute__((always_inline)) {
         const int nb = gi / 8, mb = (gi / 4) % 2, g4 = gi % 4;
-        const int ow_even = ow0 + (j & ~1);   // Wout is even (W % 8 == 0): pairs never straddle
         const int oh = oh0 + (S == 1 ? G::NBW * wave + nb : wave);
+        if constexpr (NHWC) {
+            // the lane's four consecutive channels m0 .. m0+3 of position (oh, ow0 + j): one
+            // 8-byte store (channels past C_out and positions outside go to kOff)
+            const int ow = ow0 + j;
+            const int m0 = mb * 32 + 8 * g4 + 4 * hh;
+            const uint32_t pb = oh < a.Hout && ow < a.Wout
+                                    ? (uint32_t)(((oh * a.Wout + ow) * a.C_out + m0) * 2) : kOff;
+            if (g4 == 0) m2_touch(pacc[mb][nb]);
+            uint32_t r[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r[i] = E::from_f32(epilogue<EPI>(pacc[mb][nb][4 * g4 + i]));
+            if constexpr (C4) {
+                typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+                const v2u v = {r[0] | (r[1] << 16), r[2] | (r[3] << 16)};
+                __builtin_amdgcn_raw_buffer_store_b64(v, yr, m0 < a.C_out ? pb : kOff, 0, 0);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    __builtin_amdgcn_raw_buffer_store_b16(
+                        (u16)r[i], yr, m0 + i < a.C_out ? __builtin_elementwise_add_sat(pb, 2u * i) : kOff, 0, 0);
+            }
+            return;
+        }
+        const int ow_even = ow0 + (j & ~1);   // Wout is even (W % 8 == 0): pairs never straddle
         // this lane's offset for channel 4*hh + odd of the group (rows past C_out fall past the
         // image and are dropped by the range check; positions outside go to kOff)
         const uint32_t lb = oh < a.Hout && ow_even < a.Wout
@@ -418,9 +476,9 @@ __global__ __launch_bounds__(64 * M2Geom<S>::NWaves, 1) void mfma2d_kernel(Mfma2
 
 }  // namespace
 
-bool mfma2d_supported(int C_in, int C_out, int H, int W, int stride) {
-    if (!(C_in >= 1 && C_in <= 64 && C_in % 8 == 0 && C_out >= 1 && C_out <= 64 && W % 8 == 0 &&
-          (stride == 1 || stride == 2)))
+bool mfma2d_supported(int C_in, int C_out, int H, int W, int stride, bool nhwc) {
+    if (!(C_in >= 1 && C_in <= 64 && C_in % 8 == 0 && C_out >= 1 && C_out <= 64 &&
+          (nhwc || W % 8 == 0) && (stride == 1 || stride == 2)))
         return false;
     // store offsets are formed for all 64 (padded) output channels of an image: 32-bit safe
     const long long hw_out = (long long)((H - 1) / stride + 1) * ((W - 1) / stride + 1);
@@ -444,8 +502,13 @@ hipError_t launch_mfma2d(const Simt2dParams &p, hipStream_t stream) {
     a.w_bytes = (uint32_t)((size_t)p.C_out * p.C_in * 9 * 2);
     const int grid = a.ntiles < 256 ? a.ntiles : 256;
     if (grid == 0) return hipSuccess;
-#define CX_M2(BFV, SV, EPIV) \
-    mfma2d_kernel<BFV, SV, EPIV><<<dim3(grid), dim3(64 * M2Geom<SV>::NWaves), 0, stream>>>(a)
+#define CX_M2(BFV, SV, EPIV)                                                                 \
+    do {                                                                                     \
+        const dim3 g_(grid), b_(64 * M2Geom<SV>::NWaves);                                    \
+        if (!p.nhwc) mfma2d_kernel<BFV, SV, EPIV, false, false><<<g_, b_, 0, stream>>>(a);  \
+        else if (p.C_out % 4 == 0) mfma2d_kernel<BFV, SV, EPIV, true, true><<<g_, b_, 0, stream>>>(a); \
+        else mfma2d_kernel<BFV, SV, EPIV, true, false><<<g_, b_, 0, stream>>>(a);         \
+    } while (0)
 #define CX_M2E(BFV, SV)                                     \
     do {                                                    \
         if (p.epilogue == EPI_RELU) CX_M2(BFV, SV, EPI_RELU);   \

@@ -25,26 +25,30 @@ def epi_code(e) -> int:
 
 
 class Conv3x3:
-    """2D pad-1 3x3 convolution over NCHW tensors of one fixed shape."""
+    """2D pad-1 3x3 convolution of one fixed shape over NCHW tensors, or NHWC ones with
+    channels_last=True (weights OIHW either way)."""
 
-    def __init__(self, w, bias, N, H, W, stride=1, epilogue="none", algo=C.ALGO_AUTO):
+    def __init__(self, w, bias, N, H, W, stride=1, epilogue="none", algo=C.ALGO_AUTO,
+                 channels_last=False):
         self.w, self.bias = w.contiguous(), None if bias is None else bias.contiguous()
         self.C_out, self.C_in = w.shape[0], w.shape[1]
         self.N, self.H, self.W, self.stride = N, H, W, stride
         self.dtype = dtype_code(w.dtype)
         self.epi = epi_code(epilogue)
         self.algo = algo
+        self.layout = C.LAYOUT_CHANNELS_LAST if channels_last else C.LAYOUT_CHANNELS_FIRST
         self.H_out, self.W_out = C.conv_out_size(H, stride), C.conv_out_size(W, stride)
 
     def out_shape(self):
+        if self.layout == C.LAYOUT_CHANNELS_LAST:
+            return (self.N, self.H_out, self.W_out, self.C_out)
         return (self.N, self.C_out, self.H_out, self.W_out)
 
     def __call__(self, x, y=None, stream=None):
         if y is None:
             y = torch.empty(self.out_shape(), dtype=self.w.dtype, device=x.device)
         C.conv3x3_fwd(x, self.w, self.bias, y, self.N, self.C_in, self.C_out, self.H, self.W,
-                      self.stride, C.LAYOUT_CHANNELS_FIRST, self.dtype, self.epi, self.algo,
-                      stream)
+                      self.stride, self.layout, self.dtype, self.epi, self.algo, stream)
         return y
 
 
