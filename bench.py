@@ -77,6 +77,8 @@ def parse():
                          "band8: the middle eighth of the rows with a one-row halo each side "
                          "(one GPU's share when the rows are split over eight); causal: every "
                          "frame with causal temporal padding and two cached frames in front")
+    ap.add_argument("--stride3d", type=int, default=1, choices=[1, 2],
+                    help="3D workloads other than the head: spatial stride (2 halves H and W)")
     ap.add_argument("--channels-last", action="store_true",
                     help="2D workloads only: NHWC activations instead of NCHW")
     ap.add_argument("--no-cpu-baseline", action="store_true",
@@ -327,9 +329,11 @@ def run_other(args, wl, stream):
         else:
             kname, bound, peak, unit = "simt2d", "alu", VALU_FP32_PEAK_TFS, "TFLOP/s"
     else:
-        op = Conv3x3x3(w, b, wl.N, wl.D, wl.H, wl.W, epilogue=wl.epilogue)
-        P = wl.N * wl.D * wl.H * wl.W
-        flop = 2.0 * wl.C_in * wl.C_out * wl.N * live_taps(wl.D) * live_taps(wl.H) * live_taps(wl.W)
+        s3 = args.stride3d
+        op = Conv3x3x3(w, b, wl.N, wl.D, wl.H, wl.W, epilogue=wl.epilogue, stride=s3)
+        P = wl.N * wl.D * op.H_out * op.W_out
+        flop = (2.0 * wl.C_in * wl.C_out * wl.N * live_taps(wl.D) * live_taps(wl.H, s3)
+                * live_taps(wl.W, s3))
         kname, bound, peak, unit = "igemm3d", "mfma", MFMA_BF16_PEAK_TFS, "TFLOP/s"
     y = torch.empty(op.out_shape(), dtype=wl.torch_dtype, device="cuda")
     nbytes = (x.numel() + y.numel() + w.numel() + b.numel()) * 2
@@ -351,8 +355,9 @@ def run_other(args, wl, stream):
     roof = dict(kernel=kname, bound=bound, achieved=ach, peak=peak, unit=unit, frac=ach / peak,
                 hbm_gbs=gbs, hbm_frac=gbs / HBM_PEAK_GBS, algorithmic_flop=flop,
                 algorithmic_bytes=nbytes, avg_launch_ms=kms, positions=P,
-                traffic=traffic_from_profiles(kname, wl.name,
-                                              "nhwc" if getattr(args, "channels_last", False) else "auto"))
+                traffic=traffic_from_profiles(
+                    kname, wl.name, "nhwc" if args.channels_last else
+                    ("stride2" if wl.kind == "3d" and args.stride3d == 2 else "auto")))
     if kname == "mfma2d":
         roof.update(mfma_tflops=tflops, mfma_frac=tflops / MFMA_BF16_PEAK_TFS)
     return wall_ms, roof
@@ -473,8 +478,9 @@ def main():
         layout = ("NHWC" if args.channels_last else "NCHW") if wl.kind == "2d" else "NDHWC"
         line.update(value=round(wall_ms, 4), unit="ms", ms_per_step=round(wall_ms, 4),
                     config=dict(workload=wl.name, N=wl.N, C_in=wl.C_in, C_out=wl.C_out, D=wl.D,
-                                H=wl.H, W=wl.W, stride=wl.stride, epilogue=wl.epilogue,
-                                layout=layout),
+                                H=wl.H, W=wl.W,
+                                stride=wl.stride if wl.kind == "2d" else args.stride3d,
+                                epilogue=wl.epilogue, layout=layout),
                     roofline={k: (round(v, 6) if isinstance(v, float) else v)
                               for k, v in roof.items()})
     print(json.dumps(line), flush=True)

@@ -120,9 +120,12 @@ int conv3x3_select_algo(int N, int C_in, int C_out, int H, int W, int stride, in
 /* ------------------------------------------------------------------------------------------
  * 3D: x (N,D,H,W,C_in) NDHWC, w_packed from conv3x3x3_pack_weights, bias (C_out) or NULL,
  * y (N,D,H_out,W_out,C_out) NDHWC.  Supported: layout CHANNELS_LAST, dtype BF16 or F16,
- * stride 1 (stride 2 returns CONV_E_UNSUPPORTED), C_in a multiple of 8.
- *   algo MFMA: any C_out >= 1.  algo SPLIT_HEAD / FUSED_HEAD: C_out <= 12 and one sample of x
- *   (D*H*W*C_in elements) below 2 GiB.  AUTO: see select_algo.
+ * C_in a multiple of 8, stride 1 or 2.  Stride 2 is spatial: H_out = (H-1)/2+1, W_out likewise,
+ * output (d, oh, ow) reads input rows 2*oh-1+ky and columns 2*ow-1+kx, the D frames keep stride
+ * 1 (the oracle's reading of a strided 3x3x3 video convolution); it runs on algo MFMA only
+ * (AUTO selects it) and needs one input frame below 2 GiB.
+ *   algo MFMA: any C_out >= 1.  algo SPLIT_HEAD / FUSED_HEAD: C_out <= 12, stride 1, and one
+ *   sample of x (D*H*W*C_in elements) below 2 GiB.  AUTO: see select_algo.
  * workspace: at least conv3x3x3_workspace_bytes(...) bytes (may be NULL when that is 0).
  * The same (shape, dtype, algo) arguments must be given to the size queries, to
  * conv3x3x3_pack_weights and to conv3x3x3_fwd.

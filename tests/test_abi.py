@@ -121,7 +121,8 @@ def test_3d_invalid_and_unsupported():
     assert f3d(y=A + 16) == C.E_INVAL
     assert f3d(w=B + 8) == C.E_INVAL
     assert f3d(layout=0) == C.E_UNSUPPORTED     # NCDHW
-    assert f3d(stride=2) == C.E_UNSUPPORTED
+    assert f3d(stride=2, algo=C.ALGO_FUSED_HEAD) == C.E_UNSUPPORTED   # heads: stride 1 only
+    assert f3d(stride=2, algo=C.ALGO_SPLIT_HEAD) == C.E_UNSUPPORTED
     assert f3d(C_in=20) == C.E_UNSUPPORTED      # not a multiple of 8
     assert f3d(algo=C.ALGO_SIMT) == C.E_UNSUPPORTED
     assert f3d(algo=C.ALGO_SPLIT_HEAD, C_out=13) == C.E_UNSUPPORTED
@@ -169,7 +170,8 @@ def test_is_supported_matches_fwd_checks():
     assert cx.conv3x3x3_is_supported(1, 256, 12, 16, 352, 624, 1, 1, 1, 2, 0) == C.OK
     assert cx.conv3x3x3_is_supported(1, 256, 12, 16, 352, 624, 1, 1, 1, 2, C.ALGO_SPLIT_HEAD) == C.OK
     assert cx.conv3x3x3_is_supported(1, 256, 256, 16, 176, 312, 1, 1, 1, 0, C.ALGO_SPLIT_HEAD) == C.E_UNSUPPORTED
-    assert cx.conv3x3x3_is_supported(1, 256, 256, 16, 176, 312, 2, 1, 1, 0, 0) == C.E_UNSUPPORTED
+    assert cx.conv3x3x3_is_supported(1, 256, 256, 16, 176, 312, 2, 1, 1, 0, 0) == C.OK   # stride 2
+    assert cx.conv3x3x3_is_supported(1, 256, 12, 16, 176, 312, 2, 1, 1, 2, C.ALGO_FUSED_HEAD) == C.E_UNSUPPORTED
 
 
 def test_algo_selection_and_buffer_sizes():
@@ -196,6 +198,12 @@ def test_algo_selection_and_buffer_sizes():
     assert ws > 0 and ws % (44 * 78 * 512 * 4) == 0
     assert cx.conv3x3x3_workspace_bytes(1, 512, 512, 4, 44, 78, 1, 1, 1, 9) == 0  # invalid
     assert cx.conv3x3x3_packed_weight_bytes(1, 20, 12, 1, 4, 4, 1, 1, 1, 0) == 0  # unsupported
+    # spatial stride 2: AUTO is the MFMA path (the 32x32 family, 256 packed rows, even for the
+    # head's 12 channels); the split-K partials cover the output positions
+    assert cx.conv3x3x3_select_algo(1, 256, 12, 16, 352, 624, 2, 1, 1, 0) == C.ALGO_MFMA
+    assert cx.conv3x3x3_packed_weight_bytes(1, 256, 12, 16, 352, 624, 2, 1, 1, 0) == 8 * 27 * 256 * 32 * 2
+    ws = cx.conv3x3x3_workspace_bytes(1, 64, 5, 1, 9, 9, 2, 1, 1, 0)
+    assert ws > 0 and ws % (5 * 5 * 5 * 4) == 0
 
 
 def test_pack_invalid():
@@ -210,6 +218,7 @@ def test_pack_invalid():
 @pytest.mark.skipif(HAS_GPU, reason="checks the no-device path; a GPU is visible")
 def test_no_device_reported_after_validation():
     assert f2d() == C.E_NODEVICE
+    assert f3d(stride=2) == C.E_NODEVICE           # spatial stride 2 on the MFMA path
     assert f2d(layout=1) == C.E_NODEVICE           # NHWC
     assert f2d(layout=1, W=13, stride=2) == C.E_NODEVICE   # NHWC takes any width
     assert f3d() == C.E_NODEVICE

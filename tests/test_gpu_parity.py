@@ -15,10 +15,11 @@ import torch
 
 import oracle
 import synthetic_inputs as si
-from gpu_support import (DEV, assert_bit_exact, assert_within, bits, gather_2d, gather_3d,
-                         metrics, oracle_2d, oracle_3d, run_2d, run_3d, sample_points_2d,
-                         sample_points_3d)
+from gpu_support import (DEV, EPI, alloc_guarded, assert_bit_exact, assert_within, bits,
+                         check_guards, gather_2d, gather_3d, metrics, odt, oracle_2d, oracle_3d,
+                         run_2d, run_3d, sample_points_2d, sample_points_3d)
 from x3x3_convolution_amd import conv as C
+from x3x3_convolution_amd.plan import Conv3x3x3
 
 pytestmark = pytest.mark.gpu
 
@@ -140,6 +141,61 @@ def test_conv3d_w32_tiles_integer_exact(case):
                               seed=300 + CASES_W32_TILES.index(case), device=DEV)
     y = run_3d(x, w, b, epi, C.ALGO_MFMA, guarded=True)
     assert_bit_exact(y, oracle_3d(x, w, b, epi), x.dtype)
+
+
+# Spatial stride 2 (H, W halve, frames keep stride 1): the 32x32 family's 128-position tiles
+# (4x32, 8x16) with the even/odd window columns; the first four shapes reach each (tile,
+# split-K) combination, the others vary C_in, C_out, dtype and ragged edges.
+CASES_S2 = [
+    # N, Ci, Co, D, H, W, dtype, epilogue, split-K (None: not asserted)
+    (1, 16, 5, 1, 9, 9, "bf16", "relu", False),
+    (1, 64, 5, 1, 9, 9, "bf16", "none", True),
+    (2, 16, 5, 16, 65, 9, "bf16", "clamp1", False),
+    (2, 96, 5, 16, 17, 9, "bf16", "none", True),
+    (1, 64, 130, 3, 33, 50, "f16", "relu", None),
+    (1, 32, 20, 5, 40, 65, "bf16", "none", None),
+    (2, 8, 64, 2, 17, 17, "bf16", "clamp1", None),
+    (1, 40, 300, 1, 2, 1, "bf16", "none", None),
+]
+
+
+def run_3d_s2(x, w, b, epilogue):
+    N, D, H, W, _ = x.shape
+    op = Conv3x3x3(w, b, N, D, H, W, epilogue=epilogue, algo=C.ALGO_AUTO, stride=2)
+    assert op.algo == C.ALGO_MFMA
+    buf, y = alloc_guarded(op.out_shape(), x.dtype)
+    op(x, y)
+    torch.cuda.synchronize()
+    check_guards(buf, y.numel())
+    return y, op
+
+
+def oracle_3d_s2(x, w, b, epilogue):
+    return oracle.conv3d(bits(x), bits(w), bits(b), 2, odt(x.dtype), EPI[epilogue],
+                         oracle.CHANNELS_LAST)
+
+
+@pytest.mark.parametrize("case", CASES_S2, ids=[str(c) for c in CASES_S2])
+def test_conv3d_stride2_integer_exact(case):
+    N, Ci, Co, D, H, W, dt, epi, splitk = case
+    _say("conv3d stride 2 int %s" % (case,))
+    x, w, b = si.integer_case("3d", N, Ci, Co, H, W, D=D, dtype=dt, seed=400 + CASES_S2.index(case),
+                              device=DEV)
+    y, op = run_3d_s2(x, w, b, epi)
+    assert y.shape == (N, D, (H - 1) // 2 + 1, (W - 1) // 2 + 1, Co)
+    if splitk is not None:
+        assert (op.ws_bytes > 0) == splitk
+    assert_bit_exact(y, oracle_3d_s2(x, w, b, epi), x.dtype)
+
+
+def test_conv3d_stride2_random_tolerance():
+    x, w, b = si.random_case("3d", 1, 256, 256, 24, 40, D=3, dtype="bf16", seed=8, device=DEV)
+    y, _ = run_3d_s2(x, w, b, "none")
+    y2, _ = run_3d_s2(x, w, b, "none")
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "not deterministic"
+    m = metrics(bits(y), oracle_3d_s2(x, w, b, "none"), x.dtype)
+    _say("stride 2 random %s" % (m,))
+    assert_within(m, activated=False)
 
 
 def test_conv3d_no_bias_integer_exact():

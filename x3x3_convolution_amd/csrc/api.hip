@@ -115,12 +115,21 @@ int select_3d(int N, int C_in, int C_out, int D, int H, int W, int stride, int l
         return fail(CONV_E_INVAL, "unknown algo %d", algo);
     if (layout != CONV_LAYOUT_CHANNELS_LAST)
         return fail(CONV_E_UNSUPPORTED, "3D convolution supports the NDHWC layout only");
-    if (stride != 1) return fail(CONV_E_UNSUPPORTED, "3D convolution supports stride 1 only");
     if (C_in % 8 != 0)
         return fail(CONV_E_UNSUPPORTED, "3D convolution needs C_in a multiple of 8 (got %d)", C_in);
     if (algo == CONV_ALGO_SIMT)
         return fail(CONV_E_UNSUPPORTED, "3D convolution has no SIMT algorithm");
     const bool head_algo = algo == CONV_ALGO_SPLIT_HEAD || algo == CONV_ALGO_FUSED_HEAD;
+    if (stride == 2) {   // spatial stride 2 (the temporal stride stays 1): the MFMA path only
+        if (head_algo)
+            return fail(CONV_E_UNSUPPORTED, "the head algorithms support stride 1 only");
+        if ((long long)H * W * C_in * 2 >= (1ll << 31))
+            return fail(CONV_E_UNSUPPORTED, "3D stride 2 needs one input frame below 2 GiB");
+        const long long pos = (long long)N * D * H * W;
+        if (pos >= (1ll << 31) / 8 || (long long)C_out * 27 * C_in >= (1ll << 31))
+            return fail(CONV_E_UNSUPPORTED, "problem too large for one launch");
+        return CONV_ALGO_MFMA;
+    }
     if (head_algo && C_out > kSplitHeadMaxCout)
         return fail(CONV_E_UNSUPPORTED, "the head algorithms need C_out <= %d (got %d)", kSplitHeadMaxCout, C_out);
     const long long pos = (long long)N * D * H * W;
@@ -135,10 +144,18 @@ int select_3d(int N, int C_in, int C_out, int D, int H, int W, int stride, int l
     return algo;
 }
 
-int family_for(int algo, int C_in, int C_out, int H, int W) {
+// The tile family of a request that passed select_3d (H, W: one input frame's extent).
+int family_for(int algo, int C_in, int C_out, int H, int W, int stride) {
     if (algo == CONV_ALGO_SPLIT_HEAD || algo == CONV_ALGO_FUSED_HEAD) return cx::IG_TEMPORAL;
+    if (stride == 2) return cx::IG_W32;
     if (C_out <= 16) return cx::IG_NARROW;
     return (long long)H * W * C_in * 2 < (1ll << 31) ? cx::IG_W32 : cx::IG_WIDE;
+}
+
+// The MFMA plan of a request given by its input extent (D, H, W) and stride.
+cx::IgemmPlan plan_for(int a, int N, int C_in, int C_out, int D, int H, int W, int stride) {
+    return cx::plan_igemm(family_for(a, C_in, C_out, H, W, stride), N, C_in, C_out, D,
+                          (H - 1) / stride + 1, (W - 1) / stride + 1, stride);
 }
 
 size_t elem_bytes() { return 2; }
@@ -260,8 +277,8 @@ size_t conv3x3x3_workspace_bytes(int N, int C_in, int C_out, int D, int H, int W
     ok();
     if (a == CONV_ALGO_SPLIT_HEAD)   // the plane, with room for one Z row above and below
         return (size_t)N * D * (H + 2) * W * cx::kHeadPlaneChannels * elem_bytes();
-    const cx::IgemmPlan pl = cx::plan_igemm(family_for(a, C_in, C_out, H, W), N, C_in, C_out, D, H, W);
-    return cx::splitk_workspace_bytes(pl, N, D, H, W, C_out);
+    const cx::IgemmPlan pl = plan_for(a, N, C_in, C_out, D, H, W, stride);
+    return cx::splitk_workspace_bytes(pl, N, D, (H - 1) / stride + 1, (W - 1) / stride + 1, C_out);
 }
 
 size_t conv3x3x3_packed_weight_bytes(int N, int C_in, int C_out, int D, int H, int W,
@@ -269,7 +286,7 @@ size_t conv3x3x3_packed_weight_bytes(int N, int C_in, int C_out, int D, int H, i
     const int a = select_3d(N, C_in, C_out, D, H, W, stride, layout, dtype, algo);
     if (a < 0) return 0;
     ok();
-    return cx::packed_bytes(cx::plan_igemm(family_for(a, C_in, C_out, H, W), N, C_in, C_out, D, H, W));
+    return cx::packed_bytes(plan_for(a, N, C_in, C_out, D, H, W, stride));
 }
 
 int conv3x3x3_pack_weights(const void *w_oidhw, void *w_packed, int N, int C_in, int C_out,
@@ -281,7 +298,7 @@ int conv3x3x3_pack_weights(const void *w_oidhw, void *w_packed, int N, int C_in,
     if (!w_oidhw || !w_packed) return fail(CONV_E_INVAL, "w_oidhw and w_packed must be non-NULL");
     if (!aligned(w_oidhw, 2) || !aligned(w_packed, 16))
         return fail(CONV_E_INVAL, "w_oidhw must be 2-byte and w_packed 16-byte aligned");
-    const cx::IgemmPlan pl = cx::plan_igemm(family_for(a, C_in, C_out, H, W), N, C_in, C_out, D, H, W);
+    const cx::IgemmPlan pl = plan_for(a, N, C_in, C_out, D, H, W, stride);
     if (overlaps(w_oidhw, (size_t)C_out * C_in * 27 * elem_bytes(), w_packed, cx::packed_bytes(pl)))
         return fail(CONV_E_INVAL, "w_oidhw and w_packed overlap");
     int st = device_present();
@@ -296,14 +313,19 @@ int conv3x3x3_pack_weights(const void *w_oidhw, void *w_packed, int N, int C_in,
 namespace {
 
 // The forward pass of the 3D convolution over an input region (the full region for the plain
-// convolution).  D, H are the output extent; algorithm, packing and workspace follow from it.
+// convolution).  D, H, W are the output extent, W_in the input width; at stride 2 (plain
+// convolution only) output row oh reads input rows 2*oh - 1 .. 2*oh + 1, column ow input columns
+// 2*ow - 1 .. 2*ow + 1.  Algorithm, packing and workspace follow from the request as the caller
+// states it to the size queries: the input extent and the stride.
 int fwd3d(const void *x, const void *w_packed, const void *bias, void *y, int N, int C_in,
-          int C_out, int D, int H, int W, const cx::ConvRegion &rg, int stride, int layout,
-          int dtype, int epilogue, int algo, void *workspace, size_t workspace_bytes,
+          int C_out, int D, int H, int W, int W_in, const cx::ConvRegion &rg, int stride,
+          int layout, int dtype, int epilogue, int algo, void *workspace, size_t workspace_bytes,
           void *stream) {
     if (epilogue < CONV_EPI_NONE || epilogue > CONV_EPI_CLAMP1)
         return fail(CONV_E_INVAL, "unknown epilogue %d", epilogue);
-    const int a = select_3d(N, C_in, C_out, D, H, W, stride, layout, dtype, algo);
+    // the request as the size queries see it: input extent (region calls: output extent)
+    const int Hq = stride == 1 ? H : rg.H_in, Wq = W_in;
+    const int a = select_3d(N, C_in, C_out, D, Hq, Wq, stride, layout, dtype, algo);
     if (a < 0) return a;
     if (rg.D_in < 0 || rg.H_in < 0)
         return fail(CONV_E_INVAL, "negative input extent (D_in=%d H_in=%d)", rg.D_in, rg.H_in);
@@ -319,13 +341,13 @@ int fwd3d(const void *x, const void *w_packed, const void *bias, void *y, int N,
         return fail(CONV_E_UNSUPPORTED,
                     "every output frame must read at least one valid input frame (d_org=%d, valid "
                     "frames %d..%d, D_out=%d)", rg.d_org, rg.d_lo, rg.d_hi, D);
-    const long long frame_in = (long long)rg.H_in * W * C_in * 2;
-    if ((long long)N * rg.D_in * rg.H_in * W >= (1ll << 31) / 8)
+    const long long frame_in = (long long)rg.H_in * W_in * C_in * 2;
+    if ((long long)N * rg.D_in * rg.H_in * W_in >= (1ll << 31) / 8)
         return fail(CONV_E_UNSUPPORTED, "input too large for one launch");
     const bool head_algo = a == CONV_ALGO_SPLIT_HEAD || a == CONV_ALGO_FUSED_HEAD;
     if (head_algo && (long long)rg.D_in * frame_in >= (1ll << 31))
         return fail(CONV_E_UNSUPPORTED, "the head algorithms need one sample of x below 2 GiB");
-    const int family = family_for(a, C_in, C_out, H, W);
+    const int family = family_for(a, C_in, C_out, Hq, Wq, stride);
     if (family == cx::IG_W32 && frame_in >= (1ll << 31))
         return fail(CONV_E_UNSUPPORTED, "one input frame must stay below 2 GiB for this packing");
     // the split head's plane: the output rows alone when the Z rows next to them read no data
@@ -338,10 +360,10 @@ int fwd3d(const void *x, const void *w_packed, const void *bias, void *y, int N,
         return fail(CONV_E_INVAL, "x, w_packed and y must be 16-byte aligned");
     if (bias && !aligned(bias, 2)) return fail(CONV_E_INVAL, "bias must be 2-byte aligned");
     const size_t P = (size_t)N * D * H * W;
-    const size_t xb = (size_t)N * rg.D_in * rg.H_in * W * C_in * elem_bytes();
+    const size_t xb = (size_t)N * rg.D_in * rg.H_in * W_in * C_in * elem_bytes();
     const size_t yb = P * C_out * elem_bytes();
     if (overlaps(x, xb, y, yb)) return fail(CONV_E_INVAL, "x and y overlap (in-place is unsupported)");
-    const size_t need = conv3x3x3_workspace_bytes(N, C_in, C_out, D, H, W, stride, layout, dtype, a);
+    const size_t need = conv3x3x3_workspace_bytes(N, C_in, C_out, D, Hq, Wq, stride, layout, dtype, a);
     if (need > 0) {
         if (!workspace || workspace_bytes < need)
             return fail(CONV_E_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
@@ -370,11 +392,11 @@ int fwd3d(const void *x, const void *w_packed, const void *bias, void *y, int N,
         if (e != hipSuccess) return fail(CONV_E_LAUNCH, "fused head launch failed: %s", hipGetErrorString(e));
         return ok();
     }
-    const cx::IgemmPlan pl = cx::plan_igemm(family, N, C_in, C_out, D, H, W);
+    const cx::IgemmPlan pl = cx::plan_igemm(family, N, C_in, C_out, D, H, W, stride);
     cx::IgemmParams ip{};
     ip.x = x, ip.wp = w_packed, ip.bias = bias, ip.y = y;
     ip.partial = static_cast<float *>(pl.splits > 1 ? workspace : nullptr);
-    ip.N = N, ip.C_in = C_in, ip.D = D, ip.H = H, ip.W = W, ip.rg = rg;
+    ip.N = N, ip.C_in = C_in, ip.D = D, ip.H = H, ip.W = W, ip.W_in = W_in, ip.rg = rg;
     ip.Cy = C_out, ip.bf16 = bf, ip.epilogue = epilogue;
     const hipError_t e = cx::launch_igemm3d(pl, ip, s);
     if (e != hipSuccess) return fail(CONV_E_LAUNCH, "MFMA 3D launch failed: %s", hipGetErrorString(e));
@@ -388,7 +410,9 @@ extern "C" {
 int conv3x3x3_fwd(const void *x, const void *w_packed, const void *bias, void *y, int N,
                   int C_in, int C_out, int D, int H, int W, int stride, int layout, int dtype,
                   int epilogue, int algo, void *workspace, size_t workspace_bytes, void *stream) {
-    return fwd3d(x, w_packed, bias, y, N, C_in, C_out, D, H, W, cx::full_region(D, H), stride,
+    // the output extent; the input region is the whole input
+    const int Ho = stride == 2 ? (H - 1) / 2 + 1 : H, Wo = stride == 2 ? (W - 1) / 2 + 1 : W;
+    return fwd3d(x, w_packed, bias, y, N, C_in, C_out, D, Ho, Wo, W, cx::full_region(D, H), stride,
                  layout, dtype, epilogue, algo, workspace, workspace_bytes, stream);
 }
 
@@ -397,7 +421,7 @@ int conv3x3x3_fwd_region(const void *x, const void *w_packed, const void *bias, 
                          int d_org, int h_org, int d_lo, int d_hi, int h_lo, int h_hi, int layout,
                          int dtype, int epilogue, int algo, void *workspace,
                          size_t workspace_bytes, void *stream) {
-    return fwd3d(x, w_packed, bias, y, N, C_in, C_out, D_out, H_out, W,
+    return fwd3d(x, w_packed, bias, y, N, C_in, C_out, D_out, H_out, W, W,
                  cx::ConvRegion{D_in, H_in, d_org, h_org, d_lo, d_hi, h_lo, h_hi}, 1, layout, dtype,
                  epilogue, algo, workspace, workspace_bytes, stream);
 }

@@ -40,7 +40,8 @@ struct IgemmKArgs {
     const u16 *bias;
     u16 *y;
     float *partial;
-    int N, C_in, D, H, W;          // D, H: output extent
+    int N, C_in, D, H, W;          // D, H, W: output extent
+    int W_in;                      // input width (W at stride 1)
     int D_in, H_in, d_org, h_org;  // input region (see ConvRegion)
     int d_lo, d_hi, h_lo, h_hi;
     int Mrows, Mpad, Cy;
@@ -265,14 +266,19 @@ __global__ __launch_bounds__(256, 2) void igemm3d_kernel(IgemmKArgs a) {
 // 2NB x 16 (two rows per block) for narrow frames.  NB = 8 (256 positions, all 256 accumulators
 // of a wave) is the default; NB = 4 halves the tile for convolutions with few positions, which
 // then fill the chip without splitting K.
-template <int LW, int NB_>
+template <int LW, int NB_, int S = 1>
 struct W32Geom {
     static constexpr int R = 32 / LW;                    // rows per 32-position block
     static constexpr int NB = NB_;                       // 32-position blocks per tile
     static constexpr int TH = NB * R, TW = LW;           // workgroup tile = every wave's tile
-    static constexpr int WW = TW + 2;                    // window columns used
-    static constexpr int RowPos = (WW + 3) / 4 * 4;      // window row stride (positions)
-    static constexpr int Pos = (TH + 2) * RowPos;        // window positions
+    // Window: stride 1 reads TH+2 input rows x TW+2 columns; stride 2 (spatial) reads 2TH+1 rows
+    // x 2TW+1 columns and stores a row's even window columns (taps kx = 0, 2) at LDS columns
+    // 0..TW and its odd ones (kx = 1) from column OddBase, so every tap reads unit-stride.
+    static constexpr int WH = S == 1 ? TH + 2 : 2 * TH + 1;            // window rows
+    static constexpr int WW = S == 1 ? TW + 2 : TW + 1;                // (even) columns used
+    static constexpr int OddBase = S == 1 ? 0 : (TW + 1 + 3) / 4 * 4;  // first odd column slot
+    static constexpr int RowPos = S == 1 ? (WW + 3) / 4 * 4 : OddBase + (TW + 3) / 4 * 4;
+    static constexpr int Pos = WH * RowPos;              // window positions
     static constexpr int Copies = (Pos * 4 + 63) / 64;   // DMA copies of 16 positions
     static constexpr int CopiesPerWave = (Copies + 3) / 4;
     static constexpr int Slots = Copies * 64;            // 16-byte pieces per window buffer
@@ -320,10 +326,10 @@ __device__ __forceinline__ uint32_t w32_block_order(uint32_t b, uint32_t total, 
     return le / (uint32_t)D;
 }
 
-template <bool BF, int EPI, bool SPLITK, int LW, int NB>
+template <bool BF, int EPI, bool SPLITK, int LW, int NB, int S>
 __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
     using E = Elem<BF>;
-    using G = W32Geom<LW, NB>;
+    using G = W32Geom<LW, NB, S>;
     typedef typename E::vec8 vec8;
     typedef __attribute__((address_space(3))) void lds_void;
     __shared__ __attribute__((aligned(16))) uint4 Win0[G::Slots];
@@ -359,7 +365,7 @@ __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
     const int mbase = mt * 256 + wave * 64;       // this wave's first GEMM row
     const bool mlive = mbase < a.Mrows;           // (all-padding waves compute zeros, store none)
 
-    const size_t frame_elems = (size_t)a.H_in * a.W * a.C_in;
+    const size_t frame_elems = (size_t)a.H_in * a.W_in * a.C_in;
     const uint32_t frame_bytes = (uint32_t)(frame_elems * 2);
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
         (void *)a.wp, (short)0, (int)(a.wp_bytes), 0x00020000);
@@ -385,10 +391,14 @@ __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
             const int pos = 16 * k + (lane >> 2);
             const int wh = pos / G::RowPos, ww = pos - wh * G::RowPos;
             const int piece = (lane & 3) ^ ((ww >> 2) & 3);
-            const int h = oh0 - 1 + wh + a.h_org, w = ow0 - 1 + ww;
-            const bool ok = ww < G::WW && pos < G::Pos && h >= a.h_lo && h < a.h_hi &&
-                            (unsigned)w < (unsigned)a.W && cc * 32 + 8 * piece < a.C_in;
-            const uint32_t off = ok ? (uint32_t)(((h * a.W + w) * a.C_in + cc * 32 + 8 * piece) * 2) : 0xFFFFFFFFu;
+            // LDS column ww holds window column cw (input column S*ow0 - 1 + cw)
+            const bool odd = S == 2 && ww >= G::OddBase;
+            const int cw = S == 1 ? ww : (odd ? 2 * (ww - G::OddBase) + 1 : 2 * ww);
+            const bool col_used = S == 1 ? ww < G::WW : (odd ? ww - G::OddBase < G::TW : ww < G::WW);
+            const int h = S * oh0 - 1 + wh + a.h_org, w = S * ow0 - 1 + cw;
+            const bool ok = col_used && pos < G::Pos && h >= a.h_lo && h < a.h_hi &&
+                            (unsigned)w < (unsigned)a.W_in && cc * 32 + 8 * piece < a.C_in;
+            const uint32_t off = ok ? (uint32_t)(((h * a.W_in + w) * a.C_in + cc * 32 + 8 * piece) * 2) : 0xFFFFFFFFu;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)&dst[k * 64], 16, off, 0, 0, 0);
         }
     };
@@ -414,11 +424,13 @@ __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
 #pragma unroll
     for (int kx = 0; kx < 3; ++kx)
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-            lslot[kx][k2] = w32_slot<G::RowPos>(pr, pc + kx, 2 * k2 + hh);
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const int col = S == 1 ? pc + kx : (kx == 1 ? G::OddBase + pc : pc + kx / 2);
+            lslot[kx][k2] = w32_slot<G::RowPos>(S * pr, col, 2 * k2 + hh);
+        }
     auto read_b = [&](const uint4 *win, int q, int nb) {
         const int tap = q / 2, ky = tap / 3, kx = tap % 3;
-        return __builtin_bit_cast(vec8, win[lslot[kx][q % 2] + (G::R * nb + ky) * (G::RowPos * 4)]);
+        return __builtin_bit_cast(vec8, win[lslot[kx][q % 2] + (S * G::R * nb + ky) * (G::RowPos * 4)]);
     };
 
     // (every launched workgroup has at least one stage: splits are never empty and every
@@ -631,13 +643,13 @@ hipError_t launch_family(const IgemmPlan &pl, const IgemmKArgs &ka, int epi, boo
     return hipGetLastError();
 }
 
-template <bool BF, int LW, int NB>
+template <bool BF, int LW, int NB, int S = 1>
 hipError_t launch_w32(const IgemmKArgs &ka, int epi, bool splitk, dim3 grid, hipStream_t s) {
     const dim3 block(256);
-    if (splitk) igemm32_kernel<BF, EPI_NONE, true, LW, NB><<<grid, block, 0, s>>>(ka);
-    else if (epi == EPI_RELU) igemm32_kernel<BF, EPI_RELU, false, LW, NB><<<grid, block, 0, s>>>(ka);
-    else if (epi == EPI_CLAMP1) igemm32_kernel<BF, EPI_CLAMP1, false, LW, NB><<<grid, block, 0, s>>>(ka);
-    else igemm32_kernel<BF, EPI_NONE, false, LW, NB><<<grid, block, 0, s>>>(ka);
+    if (splitk) igemm32_kernel<BF, EPI_NONE, true, LW, NB, S><<<grid, block, 0, s>>>(ka);
+    else if (epi == EPI_RELU) igemm32_kernel<BF, EPI_RELU, false, LW, NB, S><<<grid, block, 0, s>>>(ka);
+    else if (epi == EPI_CLAMP1) igemm32_kernel<BF, EPI_CLAMP1, false, LW, NB, S><<<grid, block, 0, s>>>(ka);
+    else igemm32_kernel<BF, EPI_NONE, false, LW, NB, S><<<grid, block, 0, s>>>(ka);
     return hipGetLastError();
 }
 
@@ -647,6 +659,11 @@ hipError_t launch_igemm_dtype(const IgemmPlan &pl, const IgemmKArgs &ka, int epi
     switch (pl.family) {
         case IG_W32: {
             const dim3 grid((unsigned)pl.workgroups);
+            if (pl.stride == 2) {   // 128-position tiles only (the stride-2 window is twice as big)
+                if (pl.TW == 32 && pl.TH == 4) return launch_w32<BF, 32, 4, 2>(ka, epi, splitk, grid, s);
+                if (pl.TW == 16 && pl.TH == 8) return launch_w32<BF, 16, 4, 2>(ka, epi, splitk, grid, s);
+                return hipErrorInvalidValue;
+            }
             if (pl.TW == 32) {
                 if (pl.TH == 8) return launch_w32<BF, 32, 8>(ka, epi, splitk, grid, s);
                 if (pl.TH == 4) return launch_w32<BF, 32, 4>(ka, epi, splitk, grid, s);
@@ -666,9 +683,10 @@ hipError_t launch_igemm_dtype(const IgemmPlan &pl, const IgemmKArgs &ka, int epi
 
 }  // namespace
 
-IgemmPlan plan_igemm(int family, int N, int C_in, int C_out, int D, int H, int W) {
+IgemmPlan plan_igemm(int family, int N, int C_in, int C_out, int D, int H, int W, int stride) {
     IgemmPlan pl{};
     pl.family = family;
+    pl.stride = stride;
     switch (family) {
         case IG_WIDE:
             pl.BM = 128, pl.TH = 8, pl.TW = 16, pl.ntaps = 27;
@@ -715,6 +733,7 @@ IgemmPlan plan_igemm(int family, int N, int C_in, int C_out, int D, int H, int W
         const double part = (double)N * D * H * W * C_out / 3.75e6;
         double best = -1.0;
         for (const auto &g : geo) {
+            if (stride == 2 && g.cost >= 1.0) continue;   // stride 2: 128-position tiles only
             const long long th = (H + g.TH - 1) / g.TH, tw = (W + g.TW - 1) / g.TW;
             const long long gbase = (long long)N * D * th * tw * pl.mtiles;
             for (int sp = 1; sp <= pl.nchunks; ++sp) {
@@ -756,7 +775,7 @@ hipError_t launch_igemm3d(const IgemmPlan &pl, const IgemmParams &p, hipStream_t
     ka.bias = static_cast<const u16 *>(p.bias);
     ka.y = static_cast<u16 *>(p.y);
     ka.partial = p.partial;
-    ka.N = p.N, ka.C_in = p.C_in, ka.D = p.D, ka.H = p.H, ka.W = p.W;
+    ka.N = p.N, ka.C_in = p.C_in, ka.D = p.D, ka.H = p.H, ka.W = p.W, ka.W_in = p.W_in;
     ka.D_in = p.rg.D_in, ka.H_in = p.rg.H_in, ka.d_org = p.rg.d_org, ka.h_org = p.rg.h_org;
     ka.d_lo = p.rg.d_lo, ka.d_hi = p.rg.d_hi, ka.h_lo = p.rg.h_lo, ka.h_hi = p.rg.h_hi;
     ka.Mrows = pl.Mrows, ka.Mpad = pl.Mpad, ka.Cy = p.Cy;

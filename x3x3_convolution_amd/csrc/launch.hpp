@@ -59,10 +59,12 @@ struct IgemmPlan {
     int chunks_per_split;
     int tiles_h, tiles_w, mtiles;
     long long workgroups;
+    int stride;        // spatial stride (2: the 32x32 family's 128-position tiles only)
 };
 
-// Plans the MFMA launch (tile family, split-K) for a request.  Pure host arithmetic.
-IgemmPlan plan_igemm(int family, int N, int C_in, int C_out, int D, int H, int W);
+// Plans the MFMA launch (tile family, split-K) for a request over the output extent (D, H, W).
+// Pure host arithmetic.
+IgemmPlan plan_igemm(int family, int N, int C_in, int C_out, int D, int H, int W, int stride);
 
 size_t packed_bytes(const IgemmPlan &pl);
 // fp32 split-K partial sums, or 0 when splits == 1.
@@ -72,8 +74,9 @@ struct IgemmParams {
     const void *x, *wp, *bias;
     void *y;           // output (C_out channels) or the split head's plane (112 channels)
     float *partial;    // split-K partials (splits > 1)
-    int N, C_in, D, H, W;   // D, H: output extent
-    ConvRegion rg;     // input region (full_region(D, H) for the plain convolution)
+    int N, C_in, D, H, W;   // D, H, W: output extent
+    int W_in;          // input width (W at stride 1)
+    ConvRegion rg;     // input region (full_region(D, H_in) for the plain convolution)
     int Cy;            // channel stride of y
     bool bf16;
     int epilogue;

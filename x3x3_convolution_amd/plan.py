@@ -53,16 +53,20 @@ class Conv3x3:
 
 
 class Conv3x3x3:
-    """3D pad-1 3x3x3 convolution over NDHWC tensors of one fixed shape (stride 1)."""
+    """3D pad-1 3x3x3 convolution over NDHWC tensors of one fixed input shape; stride 2 is
+    spatial (H, W halve, the D frames stay)."""
 
-    def __init__(self, w, bias, N, D, H, W, epilogue="none", algo=C.ALGO_AUTO, stream=None):
+    def __init__(self, w, bias, N, D, H, W, epilogue="none", algo=C.ALGO_AUTO, stream=None,
+                 stride=1):
         self.C_out, self.C_in = w.shape[0], w.shape[1]
         self.N, self.D, self.H, self.W = N, D, H, W
+        self.stride = stride
+        self.H_out, self.W_out = C.conv_out_size(H, stride), C.conv_out_size(W, stride)
         self.dtype = dtype_code(w.dtype)
         self.torch_dtype = w.dtype
         self.epi = epi_code(epilogue)
         self.bias = None if bias is None else bias.contiguous()
-        shape = (N, self.C_in, self.C_out, D, H, W, 1, C.LAYOUT_CHANNELS_LAST, self.dtype)
+        shape = (N, self.C_in, self.C_out, D, H, W, stride, C.LAYOUT_CHANNELS_LAST, self.dtype)
         self.algo = C.conv3x3x3_select_algo(*shape, algo)
         nbytes = C.conv3x3x3_packed_weight_bytes(*shape, self.algo)
         self.w_packed = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
@@ -73,7 +77,7 @@ class Conv3x3x3:
         self._shape = shape
 
     def out_shape(self):
-        return (self.N, self.D, self.H, self.W, self.C_out)
+        return (self.N, self.D, self.H_out, self.W_out, self.C_out)
 
     def __call__(self, x, y=None, stream=None):
         if y is None:
@@ -85,7 +89,9 @@ class Conv3x3x3:
 
     def region(self, x, D_in, H_in, d_org, h_org, d_lo, d_hi, h_lo, h_hi, y=None, stream=None):
         """The convolution over an input region of x (N, D_in, H_in, W, C_in) into an output of
-        this plan's extent (N, D, H, W, C_out): conv3x3x3_fwd_region."""
+        this plan's extent (N, D, H, W, C_out): conv3x3x3_fwd_region (stride 1)."""
+        if self.stride != 1:
+            raise ValueError("regions are stride-1 convolutions")
         if y is None:
             y = torch.empty(self.out_shape(), dtype=self.torch_dtype, device=x.device)
         N, Ci, Co, D, H, W, s, lay, dt = self._shape
