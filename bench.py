@@ -91,6 +91,8 @@ def parse():
 
 
 def copy_calibration():
+    """A plain 1 GiB device copy: the counter calibration (FETCH_SIZE / WRITE_SIZE of a known
+    byte count) and the HBM rate a plain stream reaches on this machine (HIP events)."""
     import torch
     n = 1 << 30
     a = torch.ones(n // 2, dtype=torch.int16, device="cuda")
@@ -98,7 +100,17 @@ def copy_calibration():
     for _ in range(3):
         b.copy_(a)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n}))
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    s.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                      "copy_ms": round(ms, 4), "copy_gbs": round(2 * n / (ms * 1e-3) / 1e9, 1),
+                      "copy_hbm_frac": round(2 * n / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}))
 
 
 class Timer:
