@@ -142,6 +142,7 @@ def test_3d_invalid_and_unsupported():
 def test_3d_empty_is_noop():
     for kw in (dict(N=0), dict(C_out=0), dict(D=0), dict(H=0), dict(W=0)):
         assert f3d(x=None, y=None, w=None, **kw) == C.OK
+        assert f3d(x=None, y=None, w=None, stride=2, **kw) == C.OK
 
 
 def test_2d_algo_selection():

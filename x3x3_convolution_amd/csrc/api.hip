@@ -152,10 +152,13 @@ int family_for(int algo, int C_in, int C_out, int H, int W, int stride) {
     return (long long)H * W * C_in * 2 < (1ll << 31) ? cx::IG_W32 : cx::IG_WIDE;
 }
 
+// Output extent of a pad-1, 3-tap dimension of a size that passed validation (0 stays 0).
+int out_extent(int in, int stride) { return in > 0 ? (in - 1) / stride + 1 : 0; }
+
 // The MFMA plan of a request given by its input extent (D, H, W) and stride.
 cx::IgemmPlan plan_for(int a, int N, int C_in, int C_out, int D, int H, int W, int stride) {
     return cx::plan_igemm(family_for(a, C_in, C_out, H, W, stride), N, C_in, C_out, D,
-                          (H - 1) / stride + 1, (W - 1) / stride + 1, stride);
+                          out_extent(H, stride), out_extent(W, stride), stride);
 }
 
 size_t elem_bytes() { return 2; }
@@ -278,7 +281,7 @@ size_t conv3x3x3_workspace_bytes(int N, int C_in, int C_out, int D, int H, int W
     if (a == CONV_ALGO_SPLIT_HEAD)   // the plane, with room for one Z row above and below
         return (size_t)N * D * (H + 2) * W * cx::kHeadPlaneChannels * elem_bytes();
     const cx::IgemmPlan pl = plan_for(a, N, C_in, C_out, D, H, W, stride);
-    return cx::splitk_workspace_bytes(pl, N, D, (H - 1) / stride + 1, (W - 1) / stride + 1, C_out);
+    return cx::splitk_workspace_bytes(pl, N, D, out_extent(H, stride), out_extent(W, stride), C_out);
 }
 
 size_t conv3x3x3_packed_weight_bytes(int N, int C_in, int C_out, int D, int H, int W,
@@ -411,7 +414,7 @@ int conv3x3x3_fwd(const void *x, const void *w_packed, const void *bias, void *y
                   int C_in, int C_out, int D, int H, int W, int stride, int layout, int dtype,
                   int epilogue, int algo, void *workspace, size_t workspace_bytes, void *stream) {
     // the output extent; the input region is the whole input
-    const int Ho = stride == 2 ? (H - 1) / 2 + 1 : H, Wo = stride == 2 ? (W - 1) / 2 + 1 : W;
+    const int Ho = stride == 2 ? out_extent(H, 2) : H, Wo = stride == 2 ? out_extent(W, 2) : W;
     return fwd3d(x, w_packed, bias, y, N, C_in, C_out, D, Ho, Wo, W, cx::full_region(D, H), stride,
                  layout, dtype, epilogue, algo, workspace, workspace_bytes, stream);
 }
