@@ -727,13 +727,14 @@ IgemmPlan plan_igemm(int family, int N, int C_in, int C_out, int D, int H, int W
         // prologue/epilogue) plus the fp32 partials' round trip (8 bytes per partial element at
         // HBM speed: about one stage per 3.75 M).  A 4-block tile does half the MFMAs of an
         // 8-block one per stage for the same weight stream: about 0.55 of its time.
-        static const struct { int TH, TW; double cost; } geo[4] = {
-            {8, 32, 1.0}, {16, 16, 1.0}, {4, 32, 0.55}, {8, 16, 0.55}};
+        // (stride 2 takes the 4-block tiles only: its window is twice as big)
+        static const struct { int TH, TW, NB; double cost; } geo[4] = {
+            {8, 32, 8, 1.0}, {16, 16, 8, 1.0}, {4, 32, 4, 0.55}, {8, 16, 4, 0.55}};
         const double taps = D >= 3 ? (3.0 * D - 2.0) / D : (D == 2 ? 2.0 : 1.0);
         const double part = (double)N * D * H * W * C_out / 3.75e6;
         double best = -1.0;
         for (const auto &g : geo) {
-            if (stride == 2 && g.cost >= 1.0) continue;   // stride 2: 128-position tiles only
+            if (stride == 2 && g.NB != 4) continue;
             const long long th = (H + g.TH - 1) / g.TH, tw = (W + g.TW - 1) / g.TW;
             const long long gbase = (long long)N * D * th * tw * pl.mtiles;
             for (int sp = 1; sp <= pl.nchunks; ++sp) {
