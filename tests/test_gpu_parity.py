@@ -7,6 +7,7 @@
 * the workloads at full size, in the launch configuration the benchmark times: sampled outputs
   within the tolerances, plus guard-band / NaN-poison and run-twice determinism checks.
 """
+import dataclasses
 import sys
 
 import numpy as np
@@ -294,6 +295,27 @@ def test_3d_full_size_sampled(name, algo):
                                epi[wl.epilogue], oracle.CHANNELS_LAST)
     m = metrics(gather_3d(y, pts), ref, x.dtype)
     _say("%s algo %d sampled %d %s" % (name, algo, len(pts), m))
+    assert_within(m, activated=wl.epilogue != "none")
+
+
+@pytest.mark.parametrize("name,D", [("c3", 32), ("c4", 160)])
+def test_3d_beyond_32bit_offsets(name, D):
+    """Inputs past 32-bit byte offsets: the output head over 32 frames (3.6 GB, one sample past
+    2 GiB, so AUTO leaves the head kernels -- which address a sample through a 32-bit range -- for
+    the MFMA path) and the mid-decoder conv over 160 frames (4.5 GB in and out).  Sampled outputs
+    in the first, middle and last frames against the oracle."""
+    wl = dataclasses.replace(si.WORKLOADS[name], D=D)
+    _say("beyond 32-bit offsets: %s D=%d" % (name, D))
+    algo = C.conv3x3x3_select_algo(wl.N, wl.C_in, wl.C_out, wl.D, wl.H, wl.W, 1,
+                                   C.LAYOUT_CHANNELS_LAST, C.DTYPE_BF16, C.ALGO_AUTO)
+    assert algo == C.ALGO_MFMA
+    x, w, b = si.make_inputs(wl, device=DEV)
+    y = run_3d(x, w, b, wl.epilogue, C.ALGO_AUTO, guarded=True)
+    pts = sample_points_3d(wl.N, wl.D, wl.H, wl.W, 100, seed=3)
+    ref = oracle.conv3d_points(bits(x), bits(w), bits(b), pts, 1, oracle.BF16, EPI[wl.epilogue],
+                               oracle.CHANNELS_LAST)
+    m = metrics(gather_3d(y, pts), ref, x.dtype)
+    _say("%s D=%d sampled %d %s" % (name, D, len(pts), m))
     assert_within(m, activated=wl.epilogue != "none")
 
 
