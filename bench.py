@@ -455,7 +455,7 @@ def run_region(args, wl, stream):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+        print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
