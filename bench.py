@@ -144,6 +144,22 @@ class Timer:
         return {k: sum(v) / len(v) for k, v in out.items()}
 
 
+def time_pack(op, w, stream, reps=5):
+    """The one-time repack of the OIDHW weights into the plan's order (not part of a pass):
+    average of a few re-packs, HIP events on the launch stream."""
+    import torch
+    from x3x3_convolution_amd import conv as C
+    wc = w.contiguous()
+    torch.cuda.synchronize()
+    tm = Timer(torch.cuda.current_stream())
+    for _ in range(reps):
+        s0 = tm.start()
+        C.conv3x3x3_pack_weights(wc, op.w_packed, *op._shape, op.algo, stream=stream)
+        tm.stop("pack", s0)
+    torch.cuda.synchronize()
+    return tm.summary()["pack"]
+
+
 def run_head(args, wl, stream):
     """Times every head algorithm; returns per-algorithm results and the AUTO choice."""
     import torch
@@ -168,7 +184,7 @@ def run_head(args, wl, stream):
     results = {}
     for name, code in algos.items():
         op = Conv3x3x3(w, b, wl.N, wl.D, wl.H, wl.W, epilogue=wl.epilogue, algo=code)
-        torch.cuda.synchronize()
+        pack_ms = time_pack(op, w, stream)
         if code == C.ALGO_SPLIT_HEAD:
             g = op.workspace
 
@@ -201,7 +217,7 @@ def run_head(args, wl, stream):
         torch.cuda.synchronize()
         wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
         k = tm.summary()
-        results[name] = dict(ms_per_pass=wall_ms, kernel_ms=k)
+        results[name] = dict(ms_per_pass=wall_ms, kernel_ms=k, weight_pack_ms=pack_ms)
         del op
         torch.cuda.empty_cache()
 
@@ -281,7 +297,8 @@ def run_head(args, wl, stream):
         pass_gbs=((xb + 2 * gb + yb + wb + bb) if chosen == "split" else (xb + yb + wb + bb))
         / (pass_ms * 1e-3) / 1e9,
         algos={k: dict(ms_per_pass=round(v["ms_per_pass"], 4),
-                       kernel_ms={kk: round(vv, 4) for kk, vv in v["kernel_ms"].items()})
+                       kernel_ms={kk: round(vv, 4) for kk, vv in v["kernel_ms"].items()},
+                       weight_pack_ms=round(v["weight_pack_ms"], 4))
                for k, v in results.items()})
     if video is not None:
         extra["video_step"] = video
@@ -348,6 +365,7 @@ def run_other(args, wl, stream):
     else:
         s3 = args.stride3d
         op = Conv3x3x3(w, b, wl.N, wl.D, wl.H, wl.W, epilogue=wl.epilogue, stride=s3)
+        pack_ms = time_pack(op, w, stream)
         P = wl.N * wl.D * op.H_out * op.W_out
         flop = (2.0 * wl.C_in * wl.C_out * wl.N * live_taps(wl.D) * live_taps(wl.H, s3)
                 * live_taps(wl.W, s3))
@@ -382,6 +400,8 @@ def run_other(args, wl, stream):
                     ("stride2" if wl.kind == "3d" and args.stride3d == 2 else "auto")))
     if kname == "mfma2d":
         roof.update(mfma_tflops=tflops, mfma_frac=tflops / MFMA_BF16_PEAK_TFS)
+    if wl.kind == "3d":
+        roof["weight_pack_ms"] = pack_ms
     return wall_ms, roof
 
 
