@@ -16,9 +16,11 @@
 // rows h-1, h, h+1.
 //
 // Keeping HBM busy: two rows are in flight in registers while a third is summed (two register
-// sets that alternate, so no copy between them ever waits on a load), and the bands are as tall
-// as the chip allows -- the whole grid is resident at once (three workgroups per CU by LDS), so
-// a band re-reads only its two halo rows and pays its pipeline start once.
+// sets that alternate, so no copy between them ever waits on a load), the plane is read with
+// non-temporal loads (it streams through once; caching it only evicts other lines), and the
+// bands are tall: the grid is sized to be resident at once at two workgroups per CU (the LDS
+// would hold three; two measured faster), so a band re-reads only its two halo rows and pays its
+// pipeline start once.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -31,8 +33,9 @@ constexpr int kRowPos = kStripW + 2;               // staged positions per row (
 constexpr int kPosPieces = kHeadPlaneChannels / 8;  // 16-byte pieces per position (14)
 constexpr int kRowPieces = kRowPos * kPosPieces;   // 924
 constexpr int kRPT = (kRowPieces + 255) / 256;     // pieces per thread and row (4)
-constexpr int kResidentPerCU = 3;                  // 3 x 48 KiB of LDS ring per CU
+constexpr int kResidentPerCU = 2;                  // workgroups per CU the grid is sized for
 constexpr uint32_t kNoPiece = 0xFFFFFFFFu;         // an offset past any buffer range
+constexpr int kCacheNT = 2;                        // buffer-op cache policy: non-temporal
 
 struct StencilKArgs {
     const u16 *g;
@@ -90,9 +93,10 @@ __global__ __launch_bounds__(256) void head_stencil_kernel(StencilKArgs a) {
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(gframe + (size_t)(ok ? gr : 0) * row_elems), (short)0,
             ok ? (int)row_bytes : 0, 0x00020000);
+        // non-temporal: every piece of the plane is read once (the halo rows twice, far apart)
 #pragma unroll
         for (int j = 0; j < kRPT; ++j)
-            r[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[j], 0, 0));
+            r[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[j], 0, kCacheNT));
     };
     auto commit = [&](int h, const uint4 (&r)[kRPT]) __attribute__((always_inline)) {
         uint4 *dst = ring[(h + 3) % 3];
@@ -187,9 +191,9 @@ hipError_t launch_head_stencil(const StencilParams &p, hipStream_t stream) {
         (long long)p.H * p.W * p.C_out * 2 >= (1ll << 31))
         return hipErrorInvalidValue;
     a.strips = (p.W + kStripW - 1) / kStripW;
-    // Bands of rows: as few as keep the grid within what the chip holds at once (256 CUs x
-    // kResidentPerCU), so every band is as tall as possible; more columns than that run as
-    // several rounds of whole-height bands.
+    // Bands of rows: as few as keep the grid within 256 CUs x kResidentPerCU workgroups, so
+    // every band is as tall as possible; more columns than that run as several rounds of
+    // whole-height bands.
     const long long cols = (long long)p.N * p.D * a.strips;
     long long bands = (256 * kResidentPerCU) / (cols > 0 ? cols : 1);
     if (bands < 1) bands = 1;
