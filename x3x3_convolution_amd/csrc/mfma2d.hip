@@ -29,9 +29,10 @@
 //     (the taps kx = 0, 2 read the odd ones, kx = 1 the even ones), so those reads are unit
 //     stride too.  Two window buffers: the next stage's window is loaded while this one's
 //     MFMAs run, one barrier per stage.
-//   * Waves: each owns all 64 rows and TH / NWaves output rows of the tile: at stride 1 eight
-//     waves (two per SIMD, so one's vector work overlaps the other's MFMAs) of two 32-position
-//     blocks each, at stride 2 four waves of one block.
+//   * Waves: eight per workgroup, two per SIMD, so one's vector work (window transposes,
+//     stores) overlaps the other's MFMAs.  At stride 1 each owns all 64 rows and two output
+//     rows (two 32-position blocks); at stride 2 each owns one output row and half the rows
+//     (32 output channels), since a stride-2 tile is four output rows.
 // Input columns are handled in aligned groups of 8, so W must be a multiple of 8 (checked by
 // the host); rows, columns and channels outside the tensor load as zero (the zero padding).
 #include "common.hpp"
@@ -54,6 +55,7 @@ struct M2Geom<1> {
     static constexpr int NWaves = 8;     // two waves per SIMD
     static constexpr int TH = 16;        // output rows per tile
     static constexpr int NBW = 2;        // 32-position blocks per wave (output rows)
+    static constexpr int MBW = 2;        // 32-row blocks per wave: all 64 output channels
     static constexpr int WRows = 18;     // window rows
     static constexpr int RowPos = 36;    // window row stride in positions (34 used)
     static constexpr int Groups = 6;     // 8-column load groups per window row (NCHW)
@@ -65,9 +67,10 @@ struct M2Geom<1> {
 };
 template <>
 struct M2Geom<2> {
-    static constexpr int NWaves = 4;
-    static constexpr int TH = 4;
+    static constexpr int NWaves = 8;     // two waves per SIMD; wave w: output row w/2, channels
+    static constexpr int TH = 4;         // 32*(w%2) .. +31
     static constexpr int NBW = 1;
+    static constexpr int MBW = 1;
     static constexpr int WRows = 9;
     static constexpr int RowPos = 72;    // odd input columns at 0..32, even ones at 36..67
     static constexpr int Groups = 9;
@@ -78,8 +81,10 @@ static_assert(M2Geom<1>::WRows * M2Geom<1>::RowPos * 4 == kWinSlots, "window siz
 static_assert(M2Geom<2>::WRows * M2Geom<2>::RowPos * 4 == kWinSlots, "window size");
 static_assert(8 % (18 - M2Geom<1>::CommitFirst) == 0 && 8 % (18 - M2Geom<2>::CommitFirst) == 0,
               "whole columns per slice");
-static_assert(M2Geom<1>::NWaves * M2Geom<1>::NBW == M2Geom<1>::TH, "waves cover the tile rows");
-static_assert(M2Geom<2>::NWaves * M2Geom<2>::NBW == M2Geom<2>::TH, "waves cover the tile rows");
+static_assert(M2Geom<1>::NWaves * M2Geom<1>::MBW / 2 * M2Geom<1>::NBW == M2Geom<1>::TH,
+              "waves cover the tile rows");
+static_assert(M2Geom<2>::NWaves * M2Geom<2>::MBW / 2 * M2Geom<2>::NBW == M2Geom<2>::TH,
+              "waves cover the tile rows");
 
 struct Mfma2dKArgs {
     const u16 *x, *w, *bias;
@@ -123,6 +128,10 @@ __global__ __launch_bounds__(64 * M2Geom<S>::NWaves, 1) void mfma2d_kernel(Mfma2
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // the wave's row group and first 32-row block: all 64 rows (MBW = 2) or half of them
+    constexpr int MBW = G::MBW;
+    const int wrow = MBW == 2 ? wave : wave >> 1;
+    const int mb0 = MBW == 2 ? 0 : (wave & 1);
     const int j = lane & 31, hh = lane >> 5;
     const int HW = a.H * a.W;
 
@@ -283,7 +292,7 @@ __global__ __launch_bounds__(64 * M2Geom<S>::NWaves, 1) void mfma2d_kernel(Mfma2
 #pragma unroll
         for (int sl = 0; sl < 2; ++sl) {
             const int col = S == 1 ? j + kx : (kx == 1 ? 36 + j : j + kx / 2);
-            lslot[kx][sl] = m2_slot(S == 1 ? G::NBW * wave : 2 * wave, col, 2 * sl + hh, G::RowPos);
+            lslot[kx][sl] = m2_slot(S == 1 ? G::NBW * wrow : 2 * wrow, col, 2 * sl + hh, G::RowPos);
         }
     auto read_b = [&](const uint4 *win, int q, int nb) {
         const int tap = q >> 1, sl = q & 1, ky = tap / 3, kx = tap % 3;
@@ -298,15 +307,15 @@ __global__ __launch_bounds__(64 * M2Geom<S>::NWaves, 1) void mfma2d_kernel(Mfma2
 
     // Two accumulator sets: a tile's results are stored while the next tile's first stage runs
     // (its stores interleaved with the MFMAs), so the epilogue costs no matrix-core time.
-    f32x16_t accA[2][G::NBW], accB[2][G::NBW];
-    vec8 af[2][2], bq[2][G::NBW];
+    f32x16_t accA[MBW][G::NBW], accB[MBW][G::NBW];
+    vec8 af[2][MBW], bq[2][G::NBW];
     const float4 *bias4 = reinterpret_cast<const float4 *>(bias_s);
-    typedef f32x16_t AccSet[2][G::NBW];
+    typedef f32x16_t AccSet[MBW][G::NBW];
 
     // ---- epilogue part: bias + E, one rounding, 4-byte stores along W (rows past C_out,
     // positions past the output go to an offset past the buffer range and are dropped).  Group
     // gi = (block nb, block mb, 4-row group g4) of a finished tile's accumulators. ----
-    constexpr int kGroups = G::NBW * 2 * 4;
+    constexpr int kGroups = G::NBW * MBW * 4;
     constexpr int kGroupsPerSlice = (kGroups + 15) / 16;
     const bool odd = (j & 1) != 0;
     // per-lane constants of the stores: the lane's channel within a pair group (4*hh + odd) and
@@ -315,8 +324,9 @@ __global__ __launch_bounds__(64 * M2Geom<S>::NWaves, 1) void mfma2d_kernel(Mfma2
     const uint32_t psel = odd ? 0x01000504u : 0x05040100u;
     auto store_group = [&](AccSet &pacc, int gi, int oh0, int ow0,
                            const __amdgpu_buffer_rsrc_t &yr) __attribute__((always_inline)) {
-        const int nb = gi / 8, mb = (gi / 4) % 2, g4 = gi % 4;
-        const int oh = oh0 + (S == 1 ? G::NBW * wave + nb : wave);
+        const int nb = gi / (4 * MBW), m = (gi / 4) % MBW, g4 = gi % 4;
+        const int mb = mb0 + m;
+        const int oh = oh0 + (S == 1 ? G::NBW * wrow + nb : wrow);
         if constexpr (NHWC) {
             // the lane's four consecutive channels m0 .. m0+3 of position (oh, ow0 + j): one
             // 8-byte store (channels past C_out and positions outside go to kOff)
@@ -324,10 +334,10 @@ __global__ __launch_bounds__(64 * M2Geom<S>::NWaves, 1) void mfma2d_kernel(Mfma2
             const int m0 = mb * 32 + 8 * g4 + 4 * hh;
             const uint32_t pb = oh < a.Hout && ow < a.Wout
                                     ? (uint32_t)(((oh * a.Wout + ow) * a.C_out + m0) * 2) : kOff;
-            if (g4 == 0) m2_touch(pacc[mb][nb]);
+            if (g4 == 0) m2_touch(pacc[m][nb]);
             uint32_t r[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) r[i] = E::from_f32(epilogue<EPI>(pacc[mb][nb][4 * g4 + i]));
+            for (int i = 0; i < 4; ++i) r[i] = E::from_f32(epilogue<EPI>(pacc[m][nb][4 * g4 + i]));
             if constexpr (C4) {
                 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
                 const v2u v = {r[0] | (r[1] << 16), r[2] | (r[3] << 16)};
@@ -346,10 +356,10 @@ __global__ __launch_bounds__(64 * M2Geom<S>::NWaves, 1) void mfma2d_kernel(Mfma2
         const uint32_t lb = oh < a.Hout && ow_even < a.Wout
                                 ? (uint32_t)(((4 * hh + (odd ? 1 : 0)) * HWo + oh * a.Wout + ow_even) * 2)
                                 : kOff;
-        if (g4 == 0) m2_touch(pacc[mb][nb]);
+        if (g4 == 0) m2_touch(pacc[m][nb]);
         uint32_t r[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) r[i] = E::from_f32(epilogue<EPI>(pacc[mb][nb][4 * g4 + i]));
+        for (int i = 0; i < 4; ++i) r[i] = E::from_f32(epilogue<EPI>(pacc[m][nb][4 * g4 + i]));
         // Lanes j, j^1 pair up: the even lane stores channels c, c+2 at columns (j, j+1), the
         // odd lane channels c+1, c+3 at (j-1, j): one 4-byte store per channel pair.
 #pragma unroll
@@ -377,7 +387,7 @@ __global__ __launch_bounds__(64 * M2Geom<S>::NWaves, 1) void mfma2d_kernel(Mfma2
         tile_coords(pit, pn, poh0, pow0);
         const __amdgpu_buffer_rsrc_t yr = y_rsrc(pn);
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) af[0][mb] = read_a(wc, 0, mb);
+        for (int m = 0; m < MBW; ++m) af[0][m] = read_a(wc, 0, mb0 + m);
 #pragma unroll
         for (int nb = 0; nb < G::NBW; ++nb) bq[0][nb] = read_b(win, 0, nb);
 #pragma unroll
@@ -385,16 +395,16 @@ __global__ __launch_bounds__(64 * M2Geom<S>::NWaves, 1) void mfma2d_kernel(Mfma2
             const int cb = q & 1;
             if (q + 1 < 18) {
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb) af[cb ^ 1][mb] = read_a(wc, q + 1, mb);
+                for (int m = 0; m < MBW; ++m) af[cb ^ 1][m] = read_a(wc, q + 1, mb0 + m);
 #pragma unroll
                 for (int nb = 0; nb < G::NBW; ++nb) bq[cb ^ 1][nb] = read_b(win, q + 1, nb);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+            for (int m = 0; m < MBW; ++m)
 #pragma unroll
                 for (int nb = 0; nb < G::NBW; ++nb)
-                    cacc[mb][nb] = E::mfma32x32x16(af[cb][mb], bq[cb][nb], cacc[mb][nb]);
+                    cacc[m][nb] = E::mfma32x32x16(af[cb][m], bq[cb][nb], cacc[m][nb]);
             __builtin_amdgcn_sched_barrier(0);
             if (has_prev) {
 #pragma unroll
@@ -415,7 +425,8 @@ __global__ __launch_bounds__(64 * M2Geom<S>::NWaves, 1) void mfma2d_kernel(Mfma2
         // the accumulators start at the bias of their channels (register i of block mb in
         // lane half hh: channel mb*32 + 8*(i/4) + 4*hh + i%4)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+        for (int m = 0; m < MBW; ++m) {
+            const int mb = mb0 + m;
             f32x16_t b16;
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
@@ -424,8 +435,8 @@ __global__ __launch_bounds__(64 * M2Geom<S>::NWaves, 1) void mfma2d_kernel(Mfma2
             }
 #pragma unroll
             for (int nb = 0; nb < G::NBW; ++nb) {
-                cacc[mb][nb] = b16;
-                m2_touch(cacc[mb][nb]);
+                cacc[m][nb] = b16;
+                m2_touch(cacc[m][nb]);
             }
         }
         // stage 0 (channels 0..31, window buffer 0); the channels 32..63 window, loaded before
