@@ -137,11 +137,20 @@ class Timer:
         e.record(self.stream)
         self.pairs.append((name, s, e))
 
-    def summary(self):
+    def times(self):
         out = {}
         for name, s, e in self.pairs:
             out.setdefault(name, []).append(s.elapsed_time(e))
-        return {k: sum(v) / len(v) for k, v in out.items()}
+        return out
+
+    def summary(self):
+        return {k: sum(v) / len(v) for k, v in self.times().items()}
+
+    def stats(self, name):
+        """median / min / p90 of one kernel's per-step times (ms)."""
+        v = sorted(self.times()[name])
+        return dict(median=round(v[len(v) // 2], 5), min=round(v[0], 5),
+                    p90=round(v[min(len(v) - 1, (9 * len(v)) // 10)], 5))
 
 
 def time_pack(op, w, stream, reps=5):
@@ -217,7 +226,8 @@ def run_head(args, wl, stream):
         torch.cuda.synchronize()
         wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
         k = tm.summary()
-        results[name] = dict(ms_per_pass=wall_ms, kernel_ms=k, weight_pack_ms=pack_ms)
+        results[name] = dict(ms_per_pass=wall_ms, kernel_ms=k, weight_pack_ms=pack_ms,
+                             kernel_stats={kk: tm.stats(kk) for kk in k})
         del op
         torch.cuda.empty_cache()
 
@@ -232,6 +242,7 @@ def run_head(args, wl, stream):
                     frac=ach / HBM_PEAK_GBS, mfma_tflops=flop_t / (kms * 1e-3) / 1e12,
                     mfma_frac=flop_t / (kms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
                     algorithmic_bytes=bytes_f, algorithmic_flop=flop_t, avg_launch_ms=kms,
+                    launch_ms_stats=results["fused"]["kernel_stats"]["head_fused"],
                     traffic=traffic_from_profiles("head_fused", wl.name, "fused"))
     elif auto == C.ALGO_SPLIT_HEAD:
         kms = results["split"]["kernel_ms"]["head_temporal"]
@@ -387,6 +398,7 @@ def run_other(args, wl, stream):
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     kms = tm.summary()[kname]
+    kstats = tm.stats(kname)
     if scratch is not None:
         wall_ms = kms    # the flushes are not part of the step
     tflops = flop / (kms * 1e-3) / 1e12
@@ -394,7 +406,7 @@ def run_other(args, wl, stream):
     ach = gbs if unit == "GB/s" else tflops
     roof = dict(kernel=kname, bound=bound, achieved=ach, peak=peak, unit=unit, frac=ach / peak,
                 hbm_gbs=gbs, hbm_frac=gbs / HBM_PEAK_GBS, algorithmic_flop=flop,
-                algorithmic_bytes=nbytes, avg_launch_ms=kms, positions=P,
+                algorithmic_bytes=nbytes, avg_launch_ms=kms, launch_ms_stats=kstats, positions=P,
                 traffic=traffic_from_profiles(
                     kname, wl.name, "nhwc" if args.channels_last else
                     ("stride2" if wl.kind == "3d" and args.stride3d == 2 else "auto")))
