@@ -20,6 +20,9 @@ namespace {
 // Matrix cores: v_mfma_f32_32x32x16 (one wave per SIMD keeps the pipe full with this shape).
 // Lane l supplies row (A) / column (B) l%32 with 8 k values (the k half l/32) of a 16-wide k
 // slice, and receives accumulator element i at row 8*(i/4) + 4*(l/32) + i%4, column l%32.
+// The ninth spatial tap (12 rows) runs on v_mfma_f32_16x16x32 instead of a fourth 32-row block
+// (of which it would use 12 rows): lane l supplies row / column l%16 with k values 8*(l/16) ..
+// +7 of a 32-wide k range and receives element i at row 4*(l/16) + i, column l%16.
 //
 // Work split: a workgroup is four waves on four consecutive output frames of one (band, strip);
 // each wave walks its band one row at a time.  Per row a wave computes a 128 x 128 tile (GEMM rows
@@ -28,12 +31,17 @@ namespace {
 // a position sit in the same lane (blocks nb-1, nb+1) except at nb = 0 / 3, where they are one
 // lane away (a DPP wavefront shift).
 //
-// Row roles (set by the weight packing): accumulator register i of block mb in lane half h is
-// slot t = 16*mb + i of that half; slot t < 54 holds spatial tap t/6 of output channel 6*h + t%6.
-// So every lane owns six output channels of its four positions, with all nine taps in registers.
+// Row roles (set by the weight packing): accumulator register i of block mb < 3 in lane half h
+// is slot t = 16*mb + i of that half, spatial tap t/6 of output channel 6*h + t%6 (taps 0..7).
+// Tap 8 is a 16-row tile per 16 columns: row 8*h + c (c < 6) is output channel 6*h + c.  The two
+// tiles of a 32-column block take their B operands from the block's two k16 fragments of one
+// temporal tap, rearranged by one lane swap (v_permlane16_swap: columns 0..15 of both slices in
+// one register, 16..31 in the other, k pieces in the order 0, 2, 1, 3); one more swap of their
+// results puts rows 8*h .. 8*h+7 of column j into lane j + 32*h.  So every lane owns six output channels of
+// its four positions, with all nine taps in registers.
 //
 // K runs in stages of 32 channels; a stage holds the three temporal taps, each as two k16 slices
-// (six steps of 4 x 4 MFMAs).  Both operands of a stage are copied global -> LDS by the buffer
+// (six steps of 3 x 4 32-row MFMAs, plus the tap-8 tiles' 2 x 4 after each odd step).  Both operands of a stage are copied global -> LDS by the buffer
 // unit itself (LDS DMA: no registers, 1 KiB per instruction) into one of two buffer pairs:
 //   * A (weights): 3 taps x 128 rows x 32 channels = 24 KiB, contiguous in the packing, which
 //     already holds the LDS order.
@@ -61,7 +69,9 @@ namespace {
 // two extra rows.  Nothing of Z is rounded or stored: the fused head keeps fp32 from the GEMM to
 // the epilogue.
 // ---------------------------------------------------------------------------------------------
-constexpr int kMB = 4;                  // 32-row blocks: 128 GEMM rows per temporal tap
+constexpr int kMB = 4;                  // 32-row blocks: 128 GEMM rows per temporal tap in LDS
+constexpr int kMB32 = 3;                // blocks on the 32x32 matrix cores (taps 0..7)
+constexpr int kRow8 = 32 * kMB32;       // first LDS row of the tap-8 tile (16 rows)
 constexpr int kNB = 4;                  // 32-column blocks per wave
 constexpr int kWavePos = 32 * kNB;      // 128 positions per wave and row
 constexpr int kSteps = 6;               // k16 steps per stage: 3 temporal taps x 2 slices
@@ -100,6 +110,40 @@ __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "mem
 // VGPRs only after this point, so an epilogue that walks the blocks in order keeps one or a few
 // blocks unpacked at a time instead of all 256 accumulators.
 __device__ __forceinline__ void touch(f32x16_t &v) { asm volatile("" : "+a"(v)::"memory"); }
+__device__ __forceinline__ void touch(f32x4_t &v) { asm volatile("" : "+a"(v)::"memory"); }
+
+// Swaps rows (16 lanes) 1 and 3 of a with rows 0 and 2 of b, in every register of a tile.
+__device__ __forceinline__ void swap_rows16(f32x4_t &a, f32x4_t &b) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 p = __builtin_bit_cast(u32x4, a), q = __builtin_bit_cast(u32x4, b);
+    u32x4 x, y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const auto r = __builtin_amdgcn_permlane16_swap(p[i], q[i], false, false);
+        x[i] = r[0];
+        y[i] = r[1];
+    }
+    a = __builtin_bit_cast(f32x4_t, x);
+    b = __builtin_bit_cast(f32x4_t, y);
+}
+// The tap-8 tiles' B operands from the two k16 fragments s0, s1 of a 32-column block (rows of
+// 16 lanes: s0 = [c0-15 k0-7 | c16-31 k0-7 | c0-15 k8-15 | c16-31 k8-15], s1 likewise for k16-31):
+// one row swap gives lo = columns 0..15 as [k0-7 | k16-23 | k8-15 | k24-31] and hi = columns
+// 16..31 in the same k order (the tile's A operand takes its k pieces in that order too).
+template <typename vec8>
+__device__ __forceinline__ void tile_operands(vec8 s0, vec8 s1, vec8 &lo, vec8 &hi) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 p = __builtin_bit_cast(u32x4, s0), q = __builtin_bit_cast(u32x4, s1);
+    u32x4 x, y;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const auto t = __builtin_amdgcn_permlane16_swap(p[d], q[d], false, false);
+        x[d] = t[0];
+        y[d] = t[1];
+    }
+    lo = __builtin_bit_cast(vec8, x);
+    hi = __builtin_bit_cast(vec8, y);
+}
 
 // CO12: C_out == 12, every lane stores its six channels as one 12-byte vector.  RGB (FUSED and
 // CO12 only): instead of y, the 8-bit RGB pixels of the video step -- each value rounded to the
@@ -205,20 +249,30 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
         lbase[sl] = j * 4 + ((2 * sl + hh) ^ ((j >> 2) & 3));
         lbaseB[sl] = lbase[sl] + wave * (kNB * 32 * 4);
     }
-    auto read_frags = [&](const uint4 *abuf, const uint4 *bbuf, int u, vec8 (&fa)[kMB],
-                          vec8 (&fb)[kNB]) {
+    // The tap-8 tile's A operand of temporal tap kd (16 rows x 32 channels): lane l reads row
+    // kRow8 + l%16, piece 0, 2, 1, 3 for l/16 = 0..3 (the B operands' k order); it is read with
+    // the odd step's fragments.
+    const int q8 = ((lane >> 4) & 1) * 2 + (lane >> 5);
+    const int lbase8 = (kRow8 + (lane & 15)) * 4 + (q8 ^ head_lds_swizzle(kRow8 + (lane & 15)));
+    auto read_frags = [&](const uint4 *abuf, const uint4 *bbuf, int u, vec8 (&fa)[kMB32],
+                          vec8 (&fb)[kNB], vec8 &fa8) {
         const int kd = u >> 1, sl = u & 1;
 #pragma unroll
-        for (int mb = 0; mb < kMB; ++mb)
+        for (int mb = 0; mb < kMB32; ++mb)
             fa[mb] = __builtin_bit_cast(vec8, abuf[lbase[sl] + (kd * 128 + mb * 32) * 4]);
+        if (sl == 1) fa8 = __builtin_bit_cast(vec8, abuf[lbase8 + kd * 128 * 4]);
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb)
             fb[nb] = __builtin_bit_cast(vec8, bbuf[lbaseB[sl] + (kd * kNB + nb) * 128]);
     };
 
-    f32x16_t acc[kMB][kNB];
-    vec8 af[2][kMB], bf[2][kNB];
+    // B fragments rotate through three sets (set u % 3 for step u), so that at an odd step the
+    // even step's fragments are still there for the tap-8 tiles.
+    f32x16_t acc[kMB32][kNB];
+    f32x4_t t8[kNB][2];
+    vec8 af[2][kMB32], bf[3][kNB], a8;
     const f32x16_t zero = {};
+    const f32x4_t zero4 = {};
 
     // FUSED: the bias of the lane's six output channels; the carried partial sums of every
     // output (cA: the output row before the next Z row, cB: the output row of the next Z row)
@@ -243,7 +297,7 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
     wg_barrier();
-    read_frags(As0, Bs0, 0, af[0], bf[0]);
+    read_frags(As0, Bs0, 0, af[0], bf[0], a8);
 
     // Stage g = st*nch + c uses buffer pair g % 2; each pass of the chunk loop runs an even and
     // the following odd stage.
@@ -262,9 +316,9 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
                 uint4 *const nbb = half == 0 ? Bs1 : Bs0;
 #pragma unroll
                 for (int u = 0; u < kSteps; ++u) {
-                    const int cur = u & 1;
+                    const int cur = u & 1, bs = u % 3;
                     if (u + 1 < kSteps) {
-                        read_frags(ca, cbb, u + 1, af[cur ^ 1], bf[cur ^ 1]);
+                        read_frags(ca, cbb, u + 1, af[cur ^ 1], bf[(u + 1) % 3], a8);
                     } else {
                         // Publish the next stage (its copies were issued one stage ago) and
                         // release this one: this wave's last fragments of it are in registers
@@ -274,22 +328,33 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
                         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
                         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
                         wg_barrier();
-                        read_frags(na, nbb, 0, af[cur ^ 1], bf[cur ^ 1]);
+                        read_frags(na, nbb, 0, af[cur ^ 1], bf[0], a8);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                     if (half == 0 && u == 0 && c2 == 0) {
                         // first step of a Z row: the accumulators start from zero
 #pragma unroll
-                        for (int mb = 0; mb < kMB; ++mb)
+                        for (int mb = 0; mb < kMB32; ++mb)
 #pragma unroll
                             for (int nb = 0; nb < kNB; ++nb)
-                                acc[mb][nb] = E::mfma32x32x16(af[cur][mb], bf[cur][nb], zero);
+                                acc[mb][nb] = E::mfma32x32x16(af[cur][mb], bf[bs][nb], zero);
                     } else {
 #pragma unroll
-                        for (int mb = 0; mb < kMB; ++mb)
+                        for (int mb = 0; mb < kMB32; ++mb)
 #pragma unroll
                             for (int nb = 0; nb < kNB; ++nb)
-                                acc[mb][nb] = E::mfma32x32x16(af[cur][mb], bf[cur][nb], acc[mb][nb]);
+                                acc[mb][nb] = E::mfma32x32x16(af[cur][mb], bf[bs][nb], acc[mb][nb]);
+                    }
+                    if (u & 1) {
+                        // tap 8 of temporal tap u/2: both k16 fragments are in registers
+                        const bool first8 = half == 0 && u == 1 && c2 == 0;
+#pragma unroll
+                        for (int nb = 0; nb < kNB; ++nb) {
+                            vec8 lo, hi;
+                            tile_operands(bf[(u + 2) % 3][nb], bf[bs][nb], lo, hi);
+                            t8[nb][0] = E::mfma16x16x32(a8, lo, first8 ? zero4 : t8[nb][0]);
+                            t8[nb][1] = E::mfma16x16x32(a8, hi, first8 ? zero4 : t8[nb][1]);
+                        }
                     }
                     if (u + 1 == kSteps) {
                         // The copies of the stage two ahead go into this stage's buffers, one
@@ -298,7 +363,7 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
                         // chunks that do not exist copy zeros) and nothing reads them.
                         copy_stage(st2, c_2, ca, cbb);
 #pragma unroll
-                        for (int i = 0; i < kMB * kNB; ++i) {
+                        for (int i = 0; i < kCopyA + kCopyB; ++i) {
                             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
                             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one buffer load
                         }
@@ -313,6 +378,9 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
         // one or two blocks are unpacked into registers at a time.
         const int zr = zrow0 + st;
         const size_t frame = (size_t)n * a.D + od;
+        // tap 8, channel c < 6 of lane half h: t8[nb][c / 4][c % 4] after this swap
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) swap_rows16(t8[nb][0], t8[nb][1]);
         if constexpr (!FUSED) {
             if (zr < h_end && od < a.D) {
 #pragma unroll
@@ -320,14 +388,17 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
                     const int w = w0 + 4 * j + nb;
                     u16 *dst = a.out + (frame * HW + (size_t)zr * a.W + w) * kPlaneCh;
 #pragma unroll
-                    for (int mb = 0; mb < kMB; ++mb) touch(acc[mb][nb]);
+                    for (int mb = 0; mb < kMB32; ++mb) touch(acc[mb][nb]);
+                    touch(t8[nb][0]), touch(t8[nb][1]);
 #pragma unroll
                     for (int tap = 0; tap < 9; ++tap) {
                         u16 r6[kHalfCo];
 #pragma unroll
                         for (int c = 0; c < kHalfCo; ++c) {
                             const int t = tap * kHalfCo + c;
-                            r6[c] = E::from_f32(acc[t >> 4][nb][t & 15]);
+                            const float v = tap < 8 ? acc[tap < 8 ? t >> 4 : 0][nb][t & 15]
+                                                    : t8[nb][c >> 2][c & 3];
+                            r6[c] = E::from_f32(v);
                         }
                         if (w < a.W) {
                             if constexpr (CO12) {
@@ -368,14 +439,15 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
                 if (16 * mb >= 9 * kHalfCo) continue;   // padding rows only
 #pragma unroll
                 for (int sb = 0; sb < kNB; ++sb) {
-                    touch(acc[mb][sb]);
+                    if (mb < kMB32) touch(acc[mb < kMB32 ? mb : 0][sb]);
+                    else touch(t8[sb][0]), touch(t8[sb][1]);
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int t = 16 * mb + i;
                         if (t >= 9 * kHalfCo) continue;
                         const int tap = t / kHalfCo, ky = tap / 3, kx = tap % 3, c = t % kHalfCo;
                         int nb = sb + 1 - kx;
-                        float v = acc[mb][sb][i];
+                        float v = mb < kMB32 ? acc[mb < kMB32 ? mb : 0][sb][i] : t8[sb][c >> 2][c & 3];
                         if (nb >= kNB) {   // to the next lane (it takes lane l-1)
                             nb = 0;
                             v = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(

@@ -106,15 +106,22 @@ constexpr int kHeadPlaneChannels = 112;  // 9 taps x 12 channels = 108, padded t
 // chunk with q = q' ^ head_lds_swizzle(r).
 constexpr int kHeadChunkPieces = 3 * 128 * 4;
 __host__ __device__ inline int head_lds_swizzle(int r) { return (r >> 2) & 3; }
-// Role of GEMM row m (0..127): the matrix-core accumulator layout puts row m into register
-// i = 4*((m%32)/8) + m%4 of 32-row block m/32 in lane half h = (m%8)/4; slot t = 16*(m/32) + i of
-// half h carries spatial tap t/6 (ky*3 + kx) of output channel 6*h + t%6.  Rows with t >= 54 are
-// padding (tap = -1).
+// Role of GEMM row m (0..127).  Rows 0..95 (taps 0..7): the 32x32 matrix-core accumulator
+// layout puts row m into register i = 4*((m%32)/8) + m%4 of 32-row block m/32 in lane half
+// h = (m%8)/4; slot t = 16*(m/32) + i of half h carries spatial tap t/6 (ky*3 + kx) of output
+// channel 6*h + t%6.  Rows 96..111: the 16-row tile of tap 8, row 96 + 8*h + c (c < 6) carrying
+// output channel 6*h + c.  Every other row is padding (tap = -1).
 __host__ __device__ inline void head_row_role(int m, int &tap, int &co) {
+    if (m >= 96) {
+        const int r = m - 96, h = (r >> 3) & 1, c = r & 7;
+        tap = (r < 16 && c < 6) ? 8 : -1;
+        co = 6 * h + c;
+        return;
+    }
     const int mb = m >> 5, rr = m & 31;
     const int h = (rr >> 2) & 1;
     const int t = 16 * mb + 4 * (rr >> 3) + (rr & 3);
-    tap = t < 54 ? t / 6 : -1;
+    tap = t / 6;
     co = 6 * h + t % 6;
 }
 
