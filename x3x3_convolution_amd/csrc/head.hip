@@ -13,8 +13,8 @@ namespace {
 
 // ---------------------------------------------------------------------------------------------
 // The head's temporal GEMM: Z[p, m] = sum_{kd, ci} Wt[m, (kd, ci)] * X[frame(p)-1+kd, h(p), w(p), ci]
-// where GEMM row m stands for one spatial tap (ky, kx) of one output channel co (108 of 128 rows
-// used), K = 3 * C_in.  [head.cu, header comment: the 3x1x1 convolution whose output channels
+// where GEMM row m stands for one spatial tap (ky, kx) of one output channel co (108 rows: 96 on
+// 32-row blocks, 12 in a 16-row tile), K = 3 * C_in.  [head.cu, header comment: the 3x1x1 convolution whose output channels
 // are the nine spatial taps.]
 //
 // Matrix cores: v_mfma_f32_32x32x16 (one wave per SIMD keeps the pipe full with this shape).
@@ -25,8 +25,8 @@ namespace {
 // +7 of a 32-wide k range and receives element i at row 4*(l/16) + i, column l%16.
 //
 // Work split: a workgroup is four waves on four consecutive output frames of one (band, strip);
-// each wave walks its band one row at a time.  Per row a wave computes a 128 x 128 tile (GEMM rows
-// x 128 columns of the row): 4 x 4 blocks of 32 x 32, all 256 accumulators.  Column block nb,
+// each wave walks its band one row at a time.  Per row a wave computes GEMM rows x 128 columns of
+// the row: 3 x 4 blocks of 32 x 32 (192 accumulators) and 8 tiles of 16 x 16 (32).  Column block nb,
 // lane column j holds position p = 4*j + nb of the wave's strip, so the horizontal neighbours of
 // a position sit in the same lane (blocks nb-1, nb+1) except at nb = 0 / 3, where they are one
 // lane away (a DPP wavefront shift).
