@@ -115,6 +115,23 @@ def test_conv3d_integer_exact(case):
     assert_bit_exact(y, oracle_3d(x, w, b, epi), x.dtype)
 
 
+# One spatial tap at a time through the head kernels.  The GEMM rows of the taps sit in different
+# places -- taps 0..7 in the 32-row accumulator blocks, tap 8 in the 16-row tile whose operands and
+# results are moved between lanes -- so with a weight tensor that is zero except at one (ky, kx),
+# a wrong row, lane or k order shows up as that whole tap wrong.  No clamp, so nothing saturates.
+@pytest.mark.parametrize("algo", [C.ALGO_SPLIT_HEAD, C.ALGO_FUSED_HEAD])
+@pytest.mark.parametrize("tap", range(9))
+def test_head_single_spatial_tap_exact(tap, algo):
+    ky, kx = divmod(tap, 3)
+    _say("head single tap (%d, %d) algo %d" % (ky, kx, algo))
+    x, w, b = si.integer_case("3d", 1, 32, 12, 9, 50, D=3, dtype="bf16", seed=700 + tap, device=DEV)
+    only = torch.zeros_like(w)
+    only[:, :, :, ky, kx] = w[:, :, :, ky, kx]
+    assert torch.count_nonzero(only) > 0
+    y = run_3d(x, only, b, "none", algo, guarded=True)
+    assert_bit_exact(y, oracle_3d(x, only, b, "none"), x.dtype)
+
+
 # The 32x32 MFMA family (C_out > 16) picks its tile -- 8x32, 16x16 (256 positions), 4x32 or 8x16
 # (128 positions) -- and split-K count from a cost model; these shapes reach each of the eight
 # (tile, split) combinations.  The workspace size says whether K is split.
