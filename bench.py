@@ -4,10 +4,19 @@
 The workload is the Wan2.2-style output head at its full size: x [1,16,352,624,256] bf16 NDHWC
 (channels-last) -> y [1,16,352,624,12], bias, clamp to [-1,1], seeded synthetic N(0,1)
 activations and N(0, 1/(27*256)) weights (no trained weights or real latents exist here).  One
-step is one head pass, computed by the algorithm AUTO selects; both head algorithms -- the direct
-27-tap MFMA implicit GEMM and the split head (3x1x1 temporal conv into a 112-channel plane, then
-the nine-tap stencil) -- are timed and reported.  Inputs are resident in HBM before the timed
-region; each step's launches run back to back on one stream.
+step is one head pass, computed by the algorithm AUTO selects; the three head algorithms -- the
+direct 27-tap MFMA implicit GEMM, the split head (3x1x1 temporal conv into a 112-channel plane,
+then the nine-tap stencil) and the fused head -- are timed and reported.  Inputs are resident in
+HBM before the timed region; each step's launches run back to back on one stream.
+
+The default line also carries:
+  * cpu_baseline: the oracle timed over one whole head pass on the host cores, and one thread
+    over the small 2D workload; parity: the pass's every output against that oracle pass;
+  * workloads: the other workloads (2D 16->16 and 64->64 at stride 1 and 2, the mid-decoder and
+    low-res 3D convolutions), each timed with the same protocol, with its roofline fraction and
+    its parity against the oracle (every output; a seeded sample of the mid-decoder conv);
+  * calibration: a plain 1 GiB device copy and a loop of nothing but matrix-core instructions,
+    what this machine's HBM and matrix cores sustain (context beside the published peaks).
 
 Prints one JSON line (see --help).  `--workload` times another of the synthetic workloads with
 the same protocol (for measurements outside the default line).
@@ -88,10 +97,13 @@ def parse():
                     help="2D workloads only: NHWC activations instead of NCHW")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (used for profiler runs)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--mfma-calibration", action="store_true",
+                    help="only run the matrix-core calibration loop (bf16 32x32x16 MFMAs on "
+                         "register operands) and exit")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="default line only: skip the other workloads' entries")
     return ap.parse_args()
 
 
@@ -113,9 +125,36 @@ def copy_calibration():
     e.record()
     torch.cuda.synchronize()
     ms = s.elapsed_time(e) / reps
-    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
-                      "copy_ms": round(ms, 4), "copy_gbs": round(2 * n / (ms * 1e-3) / 1e9, 1),
-                      "copy_hbm_frac": round(2 * n / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}))
+    del a, b
+    torch.cuda.empty_cache()
+    return {"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+            "copy_ms": round(ms, 4), "copy_gbs": round(2 * n / (ms * 1e-3) / 1e9, 1),
+            "copy_hbm_frac": round(2 * n / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def mfma_calibration(stream):
+    """The rate of a loop of nothing but bf16 32x32x16 MFMAs on register operands (one wave per
+    SIMD on every CU), timed with HIP events on the launch stream: what this machine's matrix
+    cores sustain under a pure matrix-core load, clock and power included.  A calibration beside
+    the published peak, not a denominator."""
+    import torch
+    from x3x3_convolution_amd import conv as C
+    wgs, iters = 256 * 8, 2000
+    out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        C.conv_calib_mfma_bf16(out, wgs, iters, stream)
+    torch.cuda.synchronize()
+    tm = Timer(torch.cuda.current_stream())
+    for _ in range(5):
+        s0 = tm.start()
+        C.conv_calib_mfma_bf16(out, wgs, iters, stream)
+        tm.stop("mfma", s0)
+    torch.cuda.synchronize()
+    ms = tm.stats("mfma")["median"]
+    flop = wgs * 4.0 * iters * 8 * 2 * 32 * 32 * 16
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"mfma_loop_flop": flop, "mfma_loop_ms": ms, "mfma_loop_tflops": round(tf, 1),
+            "mfma_loop_frac_of_peak": round(tf / MFMA_BF16_PEAK_TFS, 4)}
 
 
 class Timer:
@@ -313,41 +352,116 @@ def run_head(args, wl, stream):
                for k, v in results.items()})
     if video is not None:
         extra["video_step"] = video
-    return chosen, pass_ms, roof, extra, (x, w, b)
+    return chosen, pass_ms, roof, extra, (x, w, b), y
 
 
-def cpu_baseline(wl, tensors, target_s):
-    """The oracle timed on the host cores over a bounded random sample of output positions,
-    extrapolated to ms per full pass."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def parity_of(y_bits, ref, dtype_code, activated):
+    """d = y_gpu - y_oracle over the given outputs (the cpu_baseline leg's comparison): max|d|,
+    rms(d) and rel-rms = rms(d) / rms(y_oracle), with the workload text's bound."""
     import numpy as np
 
+    import oracle
+    g = oracle.decode(np.ascontiguousarray(y_bits), dtype_code).reshape(-1)
+    r = np.asarray(ref, np.float64).reshape(-1)
+    d = g - r
+    rms = float(np.sqrt(np.mean(d * d)))
+    out = dict(max_abs=float(np.max(np.abs(d))), rms=rms,
+               rel_rms=rms / max(float(np.sqrt(np.mean(r * r))), 1e-30), outputs=int(r.size),
+               finite=bool(np.all(np.isfinite(g))))
+    if activated:
+        out["bound"] = dict(max_abs=1.6e-2, rms=2e-3)
+        out["ok"] = out["finite"] and out["max_abs"] <= 1.6e-2 and out["rms"] <= 2e-3
+    else:
+        out["bound"] = dict(rel_rms=4e-3)
+        out["ok"] = out["finite"] and out["rel_rms"] <= 4e-3
+    for k in ("max_abs", "rms", "rel_rms"):
+        out[k] = float("%.4g" % out[k])
+    return out
+
+
+def cpu_baseline(wl, tensors, y):
+    """The cpu_baseline leg of the default line: the oracle (as it stands, plain loops, OpenMP
+    over output rows) timed on the host cores over one whole head pass, its output compared with
+    the GPU's at every output (parity of the line's value), and the oracle on one thread over
+    the small 2D workload."""
     import oracle
     import synthetic_inputs as si
 
     x, w, b = tensors
     xb, wbits, bbits = si.bits(x), si.bits(w), si.bits(b)
-    P = wl.N * wl.D * wl.H * wl.W
-    rng = np.random.default_rng(0)
-
-    def sample(n):
-        return np.stack([rng.integers(0, wl.N, n), rng.integers(0, wl.D, n),
-                         rng.integers(0, wl.H, n), rng.integers(0, wl.W, n)], 1).astype(np.int32)
     epi = {"none": oracle.EPI_NONE, "relu": oracle.EPI_RELU, "clamp1": oracle.EPI_CLAMP1}
-    cal = sample(256)
+    threads = oracle.max_threads()
     t0 = time.perf_counter()
-    oracle.conv3d_points(xb, wbits, bbits, cal, 1, oracle.BF16, epi[wl.epilogue],
-                         oracle.CHANNELS_LAST)
-    per_pt = max((time.perf_counter() - t0) / len(cal), 1e-7)
-    n = int(min(P, max(1024, target_s / per_pt)))
-    pts = sample(n)
-    t0 = time.perf_counter()
-    oracle.conv3d_points(xb, wbits, bbits, pts, 1, oracle.BF16, epi[wl.epilogue],
-                         oracle.CHANNELS_LAST)
+    ref = oracle.conv3d(xb, wbits, bbits, 1, oracle.BF16, epi[wl.epilogue], oracle.CHANNELS_LAST)
     dt = time.perf_counter() - t0
-    cores = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
-    return dict(value=dt / n * P * 1e3, unit="ms", cores=cores, kind="oracle",
-                sample="%d random output positions of the head pass (all 12 channels each), "
-                       "%.1f s wall, extrapolated to the %d positions of one pass" % (n, dt, P))
+    parity = parity_of(si.bits(y), ref, oracle.BF16, wl.epilogue != "none")
+    parity["positions"] = int(ref.size // wl.C_out)
+    del ref, xb
+    # one thread, the small 2D workload (input generation outside the timing)
+    c1 = si.WORKLOADS["c1"]
+    x1, w1, b1 = si.make_inputs(c1, device="cpu")
+    oracle.set_threads(1)
+    try:
+        t1 = time.perf_counter()
+        oracle.conv2d(si.bits(x1), si.bits(w1), si.bits(b1), c1.stride, oracle.F16,
+                      epi[c1.epilogue], oracle.CHANNELS_FIRST)
+        c1_ms = (time.perf_counter() - t1) * 1e3
+    finally:
+        oracle.set_threads(threads)
+    base = dict(value=round(dt * 1e3, 1), unit="ms", cores=threads, kind="oracle",
+                cpu_model=cpu_model(),
+                sample="one whole head pass (%d positions x %d channels), timed end to end; the "
+                       "oracle's OpenMP loops on %d threads" % (wl.N * wl.D * wl.H * wl.W,
+                                                               wl.C_out, threads),
+                single_thread_c1_ms=round(c1_ms, 2))
+    return base, parity
+
+
+def cpu_parity_sample(wl, tensors, y, full, channels_last=False):
+    """Part of the cpu_baseline leg: the oracle over a workload's outputs (all of them, or for the
+    largest one a seeded sample of positions) compared with the GPU's."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synthetic_inputs as si
+
+    x, w, b = tensors
+    epi = {"none": oracle.EPI_NONE, "relu": oracle.EPI_RELU, "clamp1": oracle.EPI_CLAMP1}[wl.epilogue]
+    od = oracle.F16 if wl.dtype == "f16" else oracle.BF16
+    t0 = time.perf_counter()
+    if wl.kind == "2d":
+        layout = oracle.CHANNELS_LAST if channels_last else oracle.CHANNELS_FIRST
+        ref = oracle.conv2d(si.bits(x), si.bits(w), si.bits(b), wl.stride, od, epi, layout)
+        got, n_pos = si.bits(y), wl.N * wl.H_out * wl.W_out
+    elif full:
+        ref = oracle.conv3d(si.bits(x), si.bits(w), si.bits(b), 1, od, epi, oracle.CHANNELS_LAST)
+        got, n_pos = si.bits(y), wl.N * wl.D * wl.H * wl.W
+    else:
+        rng = np.random.default_rng(11)
+        n_pos = 16384
+        pts = np.stack([rng.integers(0, wl.N, n_pos), rng.integers(0, wl.D, n_pos),
+                        rng.integers(0, wl.H, n_pos), rng.integers(0, wl.W, n_pos)], 1).astype(np.int32)
+        ref = oracle.conv3d_points(si.bits(x), si.bits(w), si.bits(b), pts, 1, od, epi,
+                                   oracle.CHANNELS_LAST)
+        idx = torch.from_numpy(pts.astype(np.int64)).to(y.device)
+        got = si.bits(y[idx[:, 0], idx[:, 1], idx[:, 2], idx[:, 3], :])
+    p = parity_of(got, ref, od, wl.epilogue != "none")
+    p["positions"] = int(n_pos)
+    p["sampled"] = not (full or wl.kind == "2d")
+    p["oracle_s"] = round(time.perf_counter() - t0, 2)
+    return p
 
 
 def run_other(args, wl, stream):
@@ -414,7 +528,51 @@ def run_other(args, wl, stream):
         roof.update(mfma_tflops=tflops, mfma_frac=tflops / MFMA_BF16_PEAK_TFS)
     if wl.kind == "3d":
         roof["weight_pack_ms"] = pack_ms
-    return wall_ms, roof
+        roof["mfma_tflops"] = tflops
+    return wall_ms, roof, y, (x, w, b)
+
+
+WORKLOAD_NOTES = {
+    "c1": "TAESD-style 2D conv 16->16, [1,16,64,64] fp16 NCHW, bias + ReLU (launch scale)",
+    "c2": "TAESD-style 2D conv 64->64, [8,64,256,256] fp16 NCHW, bias + ReLU",
+    "c2s2": "its stride-2 variant, [8,64,256,256] -> [8,64,128,128]",
+    "c4": "mid-decoder 3D conv 256->256, [1,256,16,176,312] bf16 NDHWC, bias, identity",
+    "c5": "low-res 3D conv 512->512, [1,512,4,44,78] bf16 NDHWC, bias, identity",
+    "c5d1": "the same at D=1 (the first causal frame)",
+}
+
+
+def run_workloads(args, stream):
+    """The other workloads, each timed with the default line's protocol (kernel time per step,
+    HIP events on the launch stream) and, in the cpu_baseline leg, compared with the oracle."""
+    import torch
+
+    import synthetic_inputs as si
+
+    out = {}
+    for name in ("c1", "c2", "c2s2", "c4", "c5", "c5d1"):
+        wl = si.WORKLOADS[name]
+        wall_ms, roof, y, tensors = run_other(args, wl, stream)
+        ent = dict(config=WORKLOAD_NOTES[name], kernel=roof["kernel"],
+                   ms=dict(avg=round(roof["avg_launch_ms"], 5), **roof["launch_ms_stats"]),
+                   bound=roof["bound"], achieved=round(roof["achieved"], 1), peak=roof["peak"],
+                   unit=roof["unit"], frac=round(roof["frac"], 4),
+                   hbm_gbs=round(roof["hbm_gbs"], 1), hbm_frac=round(roof["hbm_frac"], 4),
+                   algorithmic_flop=roof["algorithmic_flop"],
+                   algorithmic_bytes=roof["algorithmic_bytes"])
+        if "mfma_tflops" in roof:
+            ent["mfma_tflops"] = round(roof["mfma_tflops"], 1)
+            ent["mfma_frac"] = round(roof["mfma_tflops"] / MFMA_BF16_PEAK_TFS, 4)
+        if "weight_pack_ms" in roof:
+            ent["weight_pack_ms"] = round(roof["weight_pack_ms"], 4)
+        if not args.no_cpu_baseline:
+            ent["parity"] = cpu_parity_sample(wl, tensors, y, full=name != "c4",
+                                              channels_last=args.channels_last)
+        out[name] = ent
+        print("workload %s: %.4f ms" % (name, roof["avg_launch_ms"]), file=sys.stderr, flush=True)
+        del y, tensors
+        torch.cuda.empty_cache()
+    return out
 
 
 def region_of(kind, D, H):
@@ -491,7 +649,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
-        copy_calibration()
+        print(json.dumps(copy_calibration()))
         return
     import torch
 
@@ -503,6 +661,9 @@ def main():
     strm = torch.cuda.Stream()
     torch.cuda.set_stream(strm)
     stream = strm.cuda_stream
+    if args.mfma_calibration:
+        print(json.dumps(mfma_calibration(stream)))
+        return
     wl = si.WORKLOADS[args.workload]
     line = dict(metric=METRIC, n_gpus=1, steps=args.steps, warmup=args.warmup,
                 higher_is_better=False, scaling="weak", vs_baseline=None, dtype=wl.dtype,
@@ -516,7 +677,7 @@ def main():
                     roofline={k: (round(v, 6) if isinstance(v, float) else v)
                               for k, v in roof.items()})
     elif wl.name == "c3":
-        chosen, pass_ms, roof, extra, tensors = run_head(args, wl, stream)
+        chosen, pass_ms, roof, extra, tensors, y_head = run_head(args, wl, stream)
         line.update(value=round(pass_ms, 4), unit="ms", ms_per_step=round(pass_ms, 4),
                     config=dict(workload="wan2.2 output head 3x3x3 256->12, x [1,16,352,624,256] "
                                 "bf16 NDHWC, bias + clamp[-1,1], one 704x1248 head pass",
@@ -526,9 +687,15 @@ def main():
                               for k, v in roof.items()})
         line.update({k: (round(v, 4) if isinstance(v, float) else v) for k, v in extra.items()})
         if not args.no_cpu_baseline:
-            line["cpu_baseline"] = cpu_baseline(wl, tensors, args.cpu_seconds)
+            line["cpu_baseline"], line["parity"] = cpu_baseline(wl, tensors, y_head)
+            line["parity"]["algo"] = chosen   # y holds the last algorithm timed: AUTO's choice
+        del tensors, y_head
+        torch.cuda.empty_cache()
+        if not args.no_workloads and args.algo == "auto":
+            line["workloads"] = run_workloads(args, stream)
+            line["calibration"] = dict(copy_calibration(), **mfma_calibration(stream))
     else:
-        wall_ms, roof = run_other(args, wl, stream)
+        wall_ms, roof, _, _ = run_other(args, wl, stream)
         layout = ("NHWC" if args.channels_last else "NCHW") if wl.kind == "2d" else "NDHWC"
         line.update(value=round(wall_ms, 4), unit="ms", ms_per_step=round(wall_ms, 4),
                     config=dict(workload=wl.name, N=wl.N, C_in=wl.C_in, C_out=wl.C_out, D=wl.D,

@@ -82,6 +82,10 @@ def _bind(path: str):
     lib.oracle_conv2d_points.restype = ci
     lib.oracle_head_split.argtypes = [u16p, u16p, u16p, f64p, f64p] + [ci] * 10
     lib.oracle_head_split.restype = ci
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = ci
+    lib.oracle_set_threads.argtypes = [ci]
+    lib.oracle_set_threads.restype = None
     return lib
 
 
@@ -124,6 +128,14 @@ class Oracle:
 
     def __init__(self, path: str):
         self.lib = _bind(path)
+
+    def max_threads(self) -> int:
+        """Threads the OpenMP loops use (the calling thread's setting)."""
+        return self.lib.oracle_max_threads()
+
+    def set_threads(self, n: int) -> None:
+        """Sets the thread count of the OpenMP loops for the calling thread."""
+        self.lib.oracle_set_threads(int(n))
 
     def out_size(self, n: int, stride: int) -> int:
         return self.lib.oracle_out_size(int(n), int(stride))
@@ -253,6 +265,14 @@ def default() -> Oracle:
 
 def out_size(n, stride):
     return default().out_size(n, stride)
+
+
+def max_threads():
+    return default().max_threads()
+
+
+def set_threads(n):
+    return default().set_threads(n)
 
 
 def decode(bits, dtype):

@@ -397,3 +397,15 @@ int oracle_head_split(const uint16_t *x, const uint16_t *w, const uint16_t *b, d
     free(tab);
     return 0;
 }
+
+/* ---------------------------------------------------------------------------------------------
+ * Thread count of the OpenMP loops above (no arithmetic): the CPU-baseline timing reports how
+ * many threads the oracle used and times a single-threaded pass as well.
+ * ------------------------------------------------------------------------------------------- */
+#include <omp.h>
+
+int oracle_max_threads(void) { return omp_get_max_threads(); }
+
+void oracle_set_threads(int n) {
+    if (n > 0) omp_set_num_threads(n);
+}

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libconv3x3.so")
 SOURCES = ["api.hip", "simt2d.hip", "mfma2d.hip", "igemm3d.hip", "head.hip", "stencil.hip",
-           "video.hip"]
+           "video.hip", "calib.hip"]
 ARCH = "gfx950"
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
