@@ -59,10 +59,16 @@ enum { CONV_EPI_NONE = 0, CONV_EPI_RELU = 1, CONV_EPI_CLAMP1 = 2 };
  *   SPLIT_HEAD  3D, C_out <= 12, stride 1: 3x1x1 temporal conv into 9*C_out tap channels of a
  *               112-channel bf16/fp16 plane in the workspace, then a nine-tap stencil + bias +
  *               epilogue [head.cu, header comment and head_stencil_kernel].
- *   FUSED_HEAD  3D, C_out <= 12, stride 1: the same temporal GEMM and the same two roundings as
- *               SPLIT_HEAD, but the tap-channel rows stay in LDS and the stencil + bias +
- *               epilogue run in the same kernel, so the plane never goes to HBM; no workspace.
- *   AUTO: FUSED_HEAD when it applies, else MFMA. */
+ *   FUSED_HEAD  3D, C_out <= 12, stride 1: the same temporal GEMM as SPLIT_HEAD, but its tap
+ *               sums stay in the matrix cores' fp32 accumulator registers and the stencil + bias
+ *               + epilogue run in the same kernel: the 27 taps reach the output in fp32 and are
+ *               rounded once, on the store (like MFMA; only SPLIT_HEAD rounds the plane), and
+ *               the plane never goes to HBM; no workspace.  [head.cu, header comment: the split
+ *               of the 27-tap conv; its value path places the first rounding after the three
+ *               temporal taps, which this fused form leaves out.]
+ *   AUTO: 2D: MFMA when it applies, else SIMT.  3D: FUSED_HEAD when C_out <= 12 and stride 1,
+ *   else MFMA.  [taesd_conv.cuh.new header comment: direct kernels for the C <= 64 layers;
+ *   head.cu header comment: the split form for the 12-channel head.] */
 enum {
     CONV_ALGO_AUTO = 0,
     CONV_ALGO_SIMT = 1,
@@ -80,18 +86,54 @@ enum {
     CONV_E_LAUNCH = -5       /* the HIP runtime rejected a launch */
 };
 
-/* ABI version of the loaded library (CONV_ABI_VERSION it was built with). */
+/* ABI version of the loaded library (CONV_ABI_VERSION it was built with).  Library plumbing: no
+ * page defines it. */
 int conv_abi_version(void);
 
-/* Static text for a status code. */
+/* Static text for a status code.  [head.cu, head_stencil host function: every argument check
+ * fails with a message, and a rejected launch is reported after the launch.]  The pointer is to
+ * static storage; the caller never frees it. */
 const char *conv_status_str(int status);
 
-/* Detail of the last error on the calling thread ("" after a successful call). */
+/* Detail of the last error on the calling thread ("" after a successful call), the message the
+ * failed check wrote [head.cu, head_stencil host function: the checks' messages].  Thread-local
+ * storage owned by the library, valid until the thread's next call. */
 const char *conv_last_error(void);
 
 /* Output extent of a pad-1, 3-tap dimension: (in-1)/stride + 1 for in >= 1; 0 for in == 0;
- * -1 for a negative size or a stride outside {1, 2}. */
+ * -1 for a negative size or a stride outside {1, 2}.  [taesd_conv.cuh.new, taesd_conv3x3_impl:
+ * the window of output oh starts at input row oh*stride - 1, so the last output whose window
+ * still starts inside the padded input is (in-1)/stride; the extern "C" wrappers take H_out and
+ * W_out from the caller.] */
 int conv_out_size(int in, int stride);
+
+/* ------------------------------------------------------------------------------------------
+ * Region fields of the row bands and causal chunks of conv3x3x3_fwd_region (pure host
+ * arithmetic, no device work; for callers that shard rows or decode in chunks).
+ *
+ * conv_band_region: output rows [lo, lo + rows) of a frame of global height H_global, computed
+ * from an input tensor that holds global rows lo - g_off .. lo + rows + g_off - 1 (rows outside
+ * [0, H_global) may hold anything: they are never read).  [head.cu, head_stencil host function:
+ * an output band [lo, lo + rows) whose input carries g_off extra rows on each side, zero padding
+ * decided against the global height H_global, buffer bounds against the band.]  Writes
+ *   *H_in = rows + 2*g_off,  *h_org = g_off,
+ *   *h_lo = max(0, g_off - lo),  *h_hi = min(rows + 2*g_off, H_global + g_off - lo),
+ * the fields to pass to conv3x3x3_fwd_region with H_out = rows.  With g_off >= 1 the band's
+ * output equals rows [lo, lo + rows) of the convolution of the whole frame.  Returns CONV_OK, or
+ * CONV_E_INVAL (nothing written) for a NULL output pointer, lo < 0, rows < 0, g_off < 0 or
+ * lo + rows > H_global.
+ *
+ * conv_causal_region: a chunk of D_out new frames of a causal pass (output frame t reads input
+ * frames t-2 .. t, zeros before the first frame of the video), with `cached` (0, 1 or 2) frames
+ * of the previous chunk stored in front of the new ones in x.  [head.cu, commit summary: the
+ * decoder carries a few latent frames per pass to bound its memory.]  Writes
+ *   *D_in = D_out + cached,  *d_org = cached - 1,  *d_lo = 0,  *d_hi = D_out + cached.
+ * Returns CONV_OK, or CONV_E_INVAL (nothing written) for a NULL output pointer, D_out < 0 or
+ * cached outside 0..2.
+ * ---------------------------------------------------------------------------------------- */
+int conv_band_region(int lo, int rows, int g_off, int H_global, int *H_in, int *h_org, int *h_lo,
+                     int *h_hi);
+int conv_causal_region(int D_out, int cached, int *D_in, int *d_org, int *d_lo, int *d_hi);
 
 /* ------------------------------------------------------------------------------------------
  * 2D: x (N,C_in,H,W) NCHW, w (C_out,C_in,3,3) OIHW as stored by PyTorch (no packing), bias
@@ -108,12 +150,15 @@ int conv3x3_fwd(const void *x, const void *w, const void *bias, void *y, int N, 
                 int algo, void *stream);
 
 /* CONV_OK if conv3x3_fwd would accept this request (pointers aside), else the status it
- * would return. */
+ * would return.  Host-only, no device work.  [head.cu, commit summary: the ranks agree on whether
+ * every one of them could build the kernel before they take its path; this query is what each
+ * of them would contribute to that agreement.] */
 int conv3x3_is_supported(int N, int C_in, int C_out, int H, int W, int stride, int layout,
                          int dtype, int epilogue, int algo);
 
 /* The concrete 2D algorithm (CONV_ALGO_SIMT or CONV_ALGO_MFMA) conv3x3_fwd runs for this
- * request, or a negative status if it would reject it. */
+ * request, or a negative status if it would reject it.  [taesd_conv.cuh.new, header comment:
+ * which kernel serves the C <= 64 layers.] */
 int conv3x3_select_algo(int N, int C_in, int C_out, int H, int W, int stride, int layout,
                         int dtype, int algo);
 
@@ -124,8 +169,8 @@ int conv3x3_select_algo(int N, int C_in, int C_out, int H, int W, int stride, in
  * output (d, oh, ow) reads input rows 2*oh-1+ky and columns 2*ow-1+kx, the D frames keep stride
  * 1 (the oracle's reading of a strided 3x3x3 video convolution); it runs on algo MFMA only
  * (AUTO selects it) and needs one input frame below 2 GiB.
- *   algo MFMA: any C_out >= 1.  algo SPLIT_HEAD / FUSED_HEAD: C_out <= 12, stride 1, and one
- *   sample of x (D*H*W*C_in elements) below 2 GiB.  AUTO: see select_algo.
+ *   algo MFMA: any C_out >= 1.  algo SPLIT_HEAD / FUSED_HEAD: C_out <= 12, stride 1, any number
+ *   of frames, six input frames (6*H*W*C_in elements) below 2 GiB.  AUTO: see select_algo.
  * workspace: at least conv3x3x3_workspace_bytes(...) bytes (may be NULL when that is 0).
  * The same (shape, dtype, algo) arguments must be given to the size queries, to
  * conv3x3x3_pack_weights and to conv3x3x3_fwd.
@@ -170,28 +215,39 @@ int conv3x3x3_fwd_region(const void *x, const void *w_packed, const void *bias, 
                          size_t workspace_bytes, void *stream);
 
 /* The concrete algorithm conv3x3x3_fwd runs for `algo` (AUTO resolved), or a negative status
- * if the request is unsupported. */
+ * if the request is unsupported.  [head.cu, header comment: the 27-tap head computed directly or
+ * as the temporal conv + stencil split.] */
 int conv3x3x3_select_algo(int N, int C_in, int C_out, int D, int H, int W, int stride,
                           int layout, int dtype, int algo);
 
-/* CONV_OK if conv3x3x3_fwd would accept this request (pointers aside), else its status. */
+/* CONV_OK if conv3x3x3_fwd would accept this request (pointers aside), else its status.
+ * Host-only, no device work.  [head.cu, commit summary: the ranks' agreement on whether every
+ * one of them could build the kernel.] */
 int conv3x3x3_is_supported(int N, int C_in, int C_out, int D, int H, int W, int stride,
                            int layout, int dtype, int epilogue, int algo);
 
 /* Bytes of workspace conv3x3x3_fwd (and conv3x3x3_fwd_region for this output extent) needs:
  * the split head's intermediate plane with room for one row above and below the output rows
  * (N*D*(H+2)*W*112 elements of dtype), the split-K partial sums of the MFMA path for small
- * position counts (fp32), or 0.  Returns 0 for an unsupported request as well. */
+ * position counts (fp32), or 0.  Returns 0 for an unsupported request as well.  The caller
+ * allocates and frees the workspace.  [head.cu, head_stencil host function: the caller hands in
+ * the 112-channel plane g that the temporal conv wrote.] */
 size_t conv3x3x3_workspace_bytes(int N, int C_in, int C_out, int D, int H, int W, int stride,
                                  int layout, int dtype, int algo);
 
-/* Bytes of the packed weight buffer for this request (0 if unsupported). */
+/* Bytes of the packed weight buffer for this request (0 if unsupported).  [head.cu, header
+ * comment: the head's weight stays resident across the pass, so its layout is the kernel's
+ * choice.] */
 size_t conv3x3x3_packed_weight_bytes(int N, int C_in, int C_out, int D, int H, int W,
                                      int stride, int layout, int dtype, int algo);
 
 /* One-time repack of PyTorch Conv3d weights w_oidhw (C_out,C_in,3,3,3) of `dtype` (device
  * memory) into w_packed (device memory of conv3x3x3_packed_weight_bytes bytes), enqueued on
- * `stream`.  Weights are constant across passes, so this runs outside the timed pass. */
+ * `stream`.  Weights are constant across passes, so this runs outside the timed pass.  The
+ * caller owns both buffers; w_oidhw may be freed once the stream has passed this call.
+ * [head.cu, header comment: the weight is resident while the pass streams the activations.]
+ * Errors: CONV_E_INVAL for NULL or misaligned pointers or overlapping buffers, otherwise the
+ * status conv3x3x3_fwd would return for the request; nothing is enqueued on error. */
 int conv3x3x3_pack_weights(const void *w_oidhw, void *w_packed, int N, int C_in, int C_out,
                            int D, int H, int W, int stride, int layout, int dtype, int algo,
                            void *stream);
@@ -214,7 +270,7 @@ int conv_video_rgb8(const void *y, void *rgb, int N, int D, int H, int W, int C,
  * rgb equals conv_video_rgb8 applied to the y that conv3x3x3_fwd computes for the same
  * arguments (each value rounded to `dtype`, then coded), but y is never stored.  x (N,D,H,W,C_in)
  * NDHWC, w_packed from conv3x3x3_pack_weights(..., C_out = 12, ..., CONV_ALGO_FUSED_HEAD), bias
- * (12) or NULL, rgb (N,D,2H,2W,3) uint8 (2-byte aligned; one sample below 2 GiB).  Requirements
+ * (12) or NULL, rgb (N,D,2H,2W,3) uint8 (2-byte aligned).  Requirements
  * and errors otherwise as conv3x3x3_fwd with CONV_ALGO_FUSED_HEAD.  [head.cu, header comment:
  * the clamped 12-channel output feeds the video writer.] */
 int conv3x3x3_head_rgb8(const void *x, const void *w_packed, const void *bias, void *rgb, int N,
@@ -237,6 +293,16 @@ int conv_head_temporal(const void *x, const void *w_packed, void *g, int N, int 
                        int D, int H, int W, int dtype, void *stream);
 int conv_head_stencil(const void *g, const void *bias, void *y, int N, int D, int H, int W,
                       int C_out, int dtype, int epilogue, void *stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Measurement aid, not part of the convolution: enqueues `workgroups` workgroups of four waves,
+ * each wave issuing `iters` x 8 independent bf16 32x32x16 MFMAs on register operands (2 * 32 *
+ * 32 * 16 FLOP each), and writes one float per lane to `out` (device memory of workgroups * 256
+ * floats, caller-owned).  Timed by the caller, it gives the rate this machine's matrix cores
+ * sustain under a pure MFMA load.  Returns CONV_E_INVAL for a NULL `out`, workgroups outside
+ * 1..2^20 or iters < 1, CONV_E_LAUNCH if the launch is rejected.
+ * ---------------------------------------------------------------------------------------- */
+int conv_calib_mfma_bf16(void *out, int workgroups, int iters, void *stream);
 
 #ifdef __cplusplus
 }

@@ -127,9 +127,11 @@ def test_3d_invalid_and_unsupported():
     assert f3d(algo=C.ALGO_SIMT) == C.E_UNSUPPORTED
     assert f3d(algo=C.ALGO_SPLIT_HEAD, C_out=13) == C.E_UNSUPPORTED
     assert f3d(algo=C.ALGO_FUSED_HEAD, C_out=13) == C.E_UNSUPPORTED
-    # one sample of x must stay below 2 GiB for the head kernels' buffer addressing
-    assert cx.conv3x3x3_is_supported(1, 256, 12, 32, 352, 624, 1, 1, 1, 2, C.ALGO_FUSED_HEAD) == C.E_UNSUPPORTED
-    assert cx.conv3x3x3_select_algo(1, 256, 12, 32, 352, 624, 1, 1, 1, 0) == C.ALGO_MFMA
+    # a workgroup's six input frames must stay below 2 GiB for the head kernels' buffer
+    # addressing (the number of frames does not matter)
+    assert cx.conv3x3x3_is_supported(1, 256, 12, 32, 352, 624, 1, 1, 1, 2, C.ALGO_FUSED_HEAD) == C.OK
+    assert cx.conv3x3x3_is_supported(1, 256, 12, 1, 1400, 1024, 1, 1, 1, 2, C.ALGO_FUSED_HEAD) == C.E_UNSUPPORTED
+    assert cx.conv3x3x3_select_algo(1, 256, 12, 1, 1400, 1024, 1, 1, 1, 0) == C.ALGO_MFMA
     # the split head needs its plane in the workspace
     assert f3d(algo=C.ALGO_SPLIT_HEAD) == C.E_WORKSPACE
     need = cx.conv3x3x3_workspace_bytes(1, 32, 12, 2, 8, 8, 1, 1, 1, C.ALGO_SPLIT_HEAD)
@@ -313,3 +315,76 @@ def test_head_rgb8_invalid():
     assert fr(x=None, rgb=None, D=0) == C.OK
     if not HAS_GPU:
         assert fr() == C.E_NODEVICE
+
+
+def _band_by_enumeration(lo, rows, g_off, Hg):
+    """The band's region fields worked out row by row: input row r of the band holds global row
+    lo - g_off + r, and holds data exactly when that row lies inside the frame."""
+    H_in = rows + 2 * g_off
+    valid = [r for r in range(H_in) if 0 <= lo - g_off + r < Hg]
+    h_lo, h_hi = (valid[0], valid[-1] + 1) if valid else (0, 0)
+    return H_in, g_off, h_lo, h_hi
+
+
+def test_band_region_matches_row_enumeration():
+    for Hg in (1, 2, 5, 17, 44, 352):
+        for g_off in (0, 1, 2, 3):
+            for lo in range(0, Hg, max(1, Hg // 7)):
+                for rows in sorted({0, 1, 2, Hg - lo, (Hg - lo) // 2}):
+                    if rows < 0 or lo + rows > Hg:
+                        continue
+                    got = cx.conv_band_region(lo, rows, g_off, Hg)
+                    H_in, h_org, h_lo, h_hi = _band_by_enumeration(lo, rows, g_off, Hg)
+                    if h_lo == h_hi == 0 and got[2] >= got[3]:
+                        # no row of the band's input holds data: any empty range is the same
+                        assert got[:2] == (H_in, h_org)
+                        continue
+                    assert got == (H_in, h_org, h_lo, h_hi), (lo, rows, g_off, Hg)
+    # the python helper is the C entry point
+    from x3x3_convolution_amd.plan import band_rows
+    assert band_rows(132, 44, 1, 352) == cx.conv_band_region(132, 44, 1, 352) == (46, 1, 0, 46)
+    assert band_rows(0, 44, 1, 352) == (46, 1, 1, 46)
+    assert band_rows(308, 44, 1, 352) == (46, 1, 0, 45)
+
+
+def test_band_region_invalid():
+    for args in ((-1, 4, 1, 10), (0, -1, 1, 10), (0, 4, -1, 10), (7, 4, 1, 10)):
+        with pytest.raises(C.ConvError) as e:
+            cx.conv_band_region(*args)
+        assert e.value.status == C.E_INVAL
+    lib = cx.library()
+    import ctypes
+    o = ctypes.c_int()
+    assert lib.conv_band_region(0, 4, 1, 10, None, ctypes.byref(o), ctypes.byref(o),
+                                ctypes.byref(o)) == C.E_INVAL
+    assert lib.conv_causal_region(4, 1, ctypes.byref(o), None, ctypes.byref(o),
+                                  ctypes.byref(o)) == C.E_INVAL
+
+
+def test_causal_region_reads_the_causal_frames():
+    """Output frame t of a chunk must read stored frames holding video frames t-2 .. t of the
+    chunk (the cached frames of the previous chunk first), and nothing else."""
+    for D_out in (0, 1, 2, 5, 16):
+        for cached in (0, 1, 2):
+            D_in, d_org, d_lo, d_hi = cx.conv_causal_region(D_out, cached)
+            assert D_in == D_out + cached
+            for t in range(D_out):
+                # stored frame s holds chunk frame s - cached
+                read = [t + d_org - 1 + kd for kd in range(3)]
+                live = [s - cached for s in read if d_lo <= s < d_hi]
+                assert live == [f for f in (t - 2, t - 1, t) if f >= -cached], (D_out, cached, t)
+    for args in ((-1, 0), (4, 3), (4, -1)):
+        with pytest.raises(C.ConvError):
+            cx.conv_causal_region(*args)
+
+
+def test_head_any_number_of_frames():
+    """The head algorithms take any number of frames (a workgroup addresses only its own six
+    input and four output frames); only frames too large for that window leave them."""
+    for D in (16, 32, 200):
+        assert cx.conv3x3x3_select_algo(1, 256, 12, D, 352, 624, 1, 1, 1, 0) == C.ALGO_FUSED_HEAD
+        assert cx.conv3x3x3_is_supported(1, 256, 12, D, 352, 624, 1, 1, 1, 2, C.ALGO_SPLIT_HEAD) == C.OK
+    # six 2048x1024x256 frames are 6 GiB: past the window's 32-bit range
+    assert cx.conv3x3x3_select_algo(1, 256, 12, 2, 2048, 1024, 1, 1, 1, 0) == C.ALGO_MFMA
+    assert cx.conv3x3x3_is_supported(1, 256, 12, 2, 2048, 1024, 1, 1, 1, 2,
+                                     C.ALGO_FUSED_HEAD) == C.E_UNSUPPORTED

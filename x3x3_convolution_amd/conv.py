@@ -44,6 +44,9 @@ EXPORTS = [
     ("conv_head_stencil", _I, [_P, _P, _P] + [_I] * 7 + [_P]),
     ("conv_video_rgb8", _I, [_P, _P] + [_I] * 6 + [_P]),
     ("conv3x3x3_head_rgb8", _I, [_P, _P, _P, _P] + [_I] * 7 + [_P]),
+    ("conv_band_region", _I, [_I] * 4 + [ctypes.POINTER(ctypes.c_int)] * 4),
+    ("conv_causal_region", _I, [_I] * 2 + [ctypes.POINTER(ctypes.c_int)] * 4),
+    ("conv_calib_mfma_bf16", _I, [_P, _I, _I, _P]),
 ]
 
 
@@ -220,3 +223,24 @@ def conv3x3x3_head_rgb8(x, w_packed, bias, rgb, N, C_in, D, H, W, dtype=DTYPE_BF
     return _check(library().conv3x3x3_head_rgb8(_ptr(x), _ptr(w_packed), _ptr(bias), _ptr(rgb),
                                                 N, C_in, D, H, W, dtype, epilogue,
                                                 _stream(stream)))
+
+
+def conv_band_region(lo, rows, g_off, H_global):
+    """(H_in, h_org, h_lo, h_hi) of output rows [lo, lo + rows) of a frame of global height
+    H_global whose input holds g_off extra rows each side (conv_band_region)."""
+    out = [ctypes.c_int() for _ in range(4)]
+    _check(library().conv_band_region(lo, rows, g_off, H_global, *[ctypes.byref(o) for o in out]))
+    return tuple(o.value for o in out)
+
+
+def conv_causal_region(D_out, cached):
+    """(D_in, d_org, d_lo, d_hi) of a causal chunk of D_out frames with `cached` frames of the
+    previous chunk in front (conv_causal_region)."""
+    out = [ctypes.c_int() for _ in range(4)]
+    _check(library().conv_causal_region(D_out, cached, *[ctypes.byref(o) for o in out]))
+    return tuple(o.value for o in out)
+
+
+def conv_calib_mfma_bf16(out, workgroups, iters, stream=None):
+    """Enqueues the matrix-core calibration loop (a measurement aid, conv_calib_mfma_bf16)."""
+    return _check(library().conv_calib_mfma_bf16(_ptr(out), workgroups, iters, _stream(stream)))

@@ -104,6 +104,12 @@ int select_2d(int C_in, int C_out, int H, int W, int stride, int layout, int alg
 // ---- 3D ------------------------------------------------------------------------------------
 constexpr int kSplitHeadMaxCout = 12;  // 9 * C_out tap channels must fit the 112-channel plane
 
+// The head kernels' buffer ranges: a workgroup reads six input frames of H_in rows and writes
+// four output frames (at most 24 bytes per position: 12 channels, or the 12 RGB bytes).
+bool head_frames_fit(long long H_in, long long W, long long C_in) {
+    return 6 * H_in * W * C_in * 2 < (1ll << 31) && 4 * H_in * W * 24 < (1ll << 31);
+}
+
 int select_3d(int N, int C_in, int C_out, int D, int H, int W, int stride, int layout, int dtype,
               int algo) {
     int st = check_common(stride, layout, dtype, CONV_EPI_NONE);
@@ -135,12 +141,14 @@ int select_3d(int N, int C_in, int C_out, int D, int H, int W, int stride, int l
     const long long pos = (long long)N * D * H * W;
     if (pos >= (1ll << 31) / 8 || (long long)C_out * 27 * C_in >= (1ll << 31))
         return fail(CONV_E_UNSUPPORTED, "problem too large for one launch");
-    // the head kernels address one sample of x and of y through 32-bit buffer ranges
-    const bool sample_fits = (long long)D * H * W * (C_in > C_out ? C_in : C_out) * 2 < (1ll << 31);
-    if (head_algo && !sample_fits)
-        return fail(CONV_E_UNSUPPORTED, "the head algorithms need one sample of x and of y below 2 GiB");
+    // the head kernels address a workgroup's six input frames and four output frames through
+    // 32-bit buffer ranges (any number of frames)
+    if (head_algo && !head_frames_fit(H, W, C_in))
+        return fail(CONV_E_UNSUPPORTED, "the head algorithms need six input frames and four output "
+                    "frames below 2 GiB (H=%d W=%d C_in=%d)", H, W, C_in);
     if (algo == CONV_ALGO_AUTO)
-        return (C_out <= kSplitHeadMaxCout && sample_fits) ? CONV_ALGO_FUSED_HEAD : CONV_ALGO_MFMA;
+        return (C_out <= kSplitHeadMaxCout && head_frames_fit(H, W, C_in)) ? CONV_ALGO_FUSED_HEAD
+                                                                          : CONV_ALGO_MFMA;
     return algo;
 }
 
@@ -206,6 +214,41 @@ int conv_out_size(int in, int stride) {
     if (in < 0 || (stride != 1 && stride != 2)) return -1;
     if (in == 0) return 0;
     return (in - 1) / stride + 1;
+}
+
+int conv_band_region(int lo, int rows, int g_off, int H_global, int *H_in, int *h_org, int *h_lo,
+                     int *h_hi) {
+    if (!H_in || !h_org || !h_lo || !h_hi)
+        return fail(CONV_E_INVAL, "H_in, h_org, h_lo and h_hi must be non-NULL");
+    if (lo < 0 || rows < 0 || g_off < 0 || (long long)lo + rows > H_global)
+        return fail(CONV_E_INVAL,
+                    "a band needs lo >= 0, rows >= 0, g_off >= 0 and lo + rows <= H_global (got lo=%d "
+                    "rows=%d g_off=%d H_global=%d)", lo, rows, g_off, H_global);
+    if ((long long)rows + 2ll * g_off > 0x7FFFFFFF)
+        return fail(CONV_E_INVAL, "rows + 2*g_off overflows an int");
+    // input row r holds global row lo - g_off + r, which holds data when it lies in [0, H_global)
+    const int hin = rows + 2 * g_off;
+    const long long top = (long long)g_off - lo, bottom = (long long)H_global + g_off - lo;
+    *H_in = hin;
+    *h_org = g_off;
+    *h_lo = top > 0 ? (int)top : 0;
+    *h_hi = bottom < hin ? (int)bottom : hin;
+    return ok();
+}
+
+int conv_causal_region(int D_out, int cached, int *D_in, int *d_org, int *d_lo, int *d_hi) {
+    if (!D_in || !d_org || !d_lo || !d_hi)
+        return fail(CONV_E_INVAL, "D_in, d_org, d_lo and d_hi must be non-NULL");
+    if (D_out < 0 || cached < 0 || cached > 2 || D_out > 0x7FFFFFFF - 2)
+        return fail(CONV_E_INVAL, "a causal chunk needs D_out >= 0 and 0 <= cached <= 2 (got D_out=%d "
+                    "cached=%d)", D_out, cached);
+    // output frame t of the chunk reads stored frames t + cached - 2 .. t + cached: the cached
+    // frames first, zeros (frames before 0) where fewer than two are cached
+    *D_in = D_out + cached;
+    *d_org = cached - 1;
+    *d_lo = 0;
+    *d_hi = D_out + cached;
+    return ok();
 }
 
 int conv3x3_is_supported(int N, int C_in, int C_out, int H, int W, int stride, int layout,
@@ -348,8 +391,9 @@ int fwd3d(const void *x, const void *w_packed, const void *bias, void *y, int N,
     if ((long long)N * rg.D_in * rg.H_in * W_in >= (1ll << 31) / 8)
         return fail(CONV_E_UNSUPPORTED, "input too large for one launch");
     const bool head_algo = a == CONV_ALGO_SPLIT_HEAD || a == CONV_ALGO_FUSED_HEAD;
-    if (head_algo && (long long)rg.D_in * frame_in >= (1ll << 31))
-        return fail(CONV_E_UNSUPPORTED, "the head algorithms need one sample of x below 2 GiB");
+    if (head_algo && !head_frames_fit(rg.H_in, W_in, C_in))
+        return fail(CONV_E_UNSUPPORTED, "the head algorithms need six input frames below 2 GiB "
+                    "(H_in=%d W=%d C_in=%d)", rg.H_in, W_in, C_in);
     const int family = family_for(a, C_in, C_out, Hq, Wq, stride);
     if (family == cx::IG_W32 && frame_in >= (1ll << 31))
         return fail(CONV_E_UNSUPPORTED, "one input frame must stay below 2 GiB for this packing");
@@ -509,8 +553,6 @@ int conv3x3x3_head_rgb8(const void *x, const void *w_packed, const void *bias, v
     if (a < 0) return a;
     if (N == 0 || D == 0 || H == 0 || W == 0) return ok();
     const size_t rgb_sample = (size_t)D * H * W * 12;
-    if (rgb_sample >= (1ull << 31))
-        return fail(CONV_E_UNSUPPORTED, "one sample of the RGB frames must stay below 2 GiB");
     if (!x || !w_packed || !rgb) return fail(CONV_E_INVAL, "x, w_packed and rgb must be non-NULL");
     if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(rgb, 2))
         return fail(CONV_E_INVAL, "x and w_packed must be 16-byte and rgb 2-byte aligned");

@@ -117,17 +117,15 @@ class Conv3x3x3:
 def band_rows(lo, rows, halo, H_global):
     """Region rows of an output band [lo, lo + rows) of a global height H_global whose input
     holds global rows lo - halo .. lo + rows + halo - 1 (rows outside the global height may
-    hold anything): (H_in, h_org, h_lo, h_hi) for conv3x3x3_fwd_region."""
-    H_in = rows + 2 * halo
-    return H_in, halo, max(0, halo - lo), min(H_in, H_global + halo - lo)
+    hold anything): (H_in, h_org, h_lo, h_hi) for conv3x3x3_fwd_region (conv_band_region)."""
+    return C.conv_band_region(lo, rows, halo, H_global)
 
 
 def causal_frames(D_out, cached):
     """Region frames of a causal temporal pass (output frame t reads input frames t-2 .. t) over
     D_out new frames, with `cached` (0..2) frames of the previous chunk stored in front of them
-    and zeros in place of the rest: (D_in, d_org, d_lo, d_hi) for conv3x3x3_fwd_region."""
+    and zeros in place of the rest: (D_in, d_org, d_lo, d_hi) for conv3x3x3_fwd_region
+    (conv_causal_region)."""
     if not 0 <= cached <= 2:
         raise ValueError("cached must be 0, 1 or 2")
-    D_in = D_out + cached
-    return D_in, cached - 1, 0, D_in
-
+    return C.conv_causal_region(D_out, cached)
