@@ -102,6 +102,16 @@ CASES_3D_INT = [
     (1, 16, 12, 16, 40, 100, "bf16", "relu", C.ALGO_FUSED_HEAD),
     (1, 40, 7, 2, 33, 157, "bf16", "clamp1", C.ALGO_FUSED_HEAD),
     (1, 8, 12, 1, 1, 1, "bf16", "clamp1", C.ALGO_FUSED_HEAD),
+    # the head's production channel count (8 chunks: several chunk pairs per Z row, prefetches
+    # that stay in the row) and an odd chunk count (136 channels: 5 chunks padded to 6)
+    (1, 256, 12, 3, 9, 130, "bf16", "clamp1", C.ALGO_SPLIT_HEAD),
+    (1, 256, 12, 3, 9, 130, "bf16", "clamp1", C.ALGO_FUSED_HEAD),
+    (1, 136, 12, 3, 9, 130, "bf16", "none", C.ALGO_SPLIT_HEAD),
+    (1, 136, 12, 3, 9, 130, "bf16", "none", C.ALGO_FUSED_HEAD),
+    (1, 136, 5, 6, 11, 70, "f16", "relu", C.ALGO_FUSED_HEAD),
+    # more frame groups than one (the per-group input and output windows), a partial last group
+    (1, 16, 12, 22, 6, 40, "bf16", "clamp1", C.ALGO_FUSED_HEAD),
+    (1, 16, 12, 22, 6, 40, "bf16", "clamp1", C.ALGO_SPLIT_HEAD),
 ]
 
 
@@ -315,25 +325,44 @@ def test_3d_full_size_sampled(name, algo):
     assert_within(m, activated=wl.epilogue != "none")
 
 
-@pytest.mark.parametrize("name,D", [("c3", 32), ("c4", 160)])
-def test_3d_beyond_32bit_offsets(name, D):
-    """Inputs past 32-bit byte offsets: the output head over 32 frames (3.6 GB, one sample past
-    2 GiB, so AUTO leaves the head kernels -- which address a sample through a 32-bit range -- for
-    the MFMA path) and the mid-decoder conv over 160 frames (4.5 GB in and out).  Sampled outputs
-    in the first, middle and last frames against the oracle."""
+@pytest.mark.parametrize("name,D,algo", [("c3", 32, C.ALGO_FUSED_HEAD), ("c3", 32, C.ALGO_SPLIT_HEAD),
+                                         ("c4", 160, C.ALGO_MFMA)])
+def test_3d_beyond_32bit_offsets(name, D, algo):
+    """Inputs past 32-bit byte offsets: the output head over 32 frames (3.6 GB of input, on the
+    head kernels, which address each workgroup's six input and four output frames through their
+    own 32-bit ranges) and the mid-decoder conv over 160 frames (4.5 GB in and out).  Sampled
+    outputs in the first, middle and last frames against the oracle."""
     wl = dataclasses.replace(si.WORKLOADS[name], D=D)
-    _say("beyond 32-bit offsets: %s D=%d" % (name, D))
-    algo = C.conv3x3x3_select_algo(wl.N, wl.C_in, wl.C_out, wl.D, wl.H, wl.W, 1,
+    _say("beyond 32-bit offsets: %s D=%d algo %d" % (name, D, algo))
+    auto = C.conv3x3x3_select_algo(wl.N, wl.C_in, wl.C_out, wl.D, wl.H, wl.W, 1,
                                    C.LAYOUT_CHANNELS_LAST, C.DTYPE_BF16, C.ALGO_AUTO)
-    assert algo == C.ALGO_MFMA
+    assert auto == (C.ALGO_FUSED_HEAD if wl.C_out <= 12 else C.ALGO_MFMA)
     x, w, b = si.make_inputs(wl, device=DEV)
-    y = run_3d(x, w, b, wl.epilogue, C.ALGO_AUTO, guarded=True)
+    y = run_3d(x, w, b, wl.epilogue, algo, guarded=True)
     pts = sample_points_3d(wl.N, wl.D, wl.H, wl.W, 100, seed=3)
     ref = oracle.conv3d_points(bits(x), bits(w), bits(b), pts, 1, oracle.BF16, EPI[wl.epilogue],
                                oracle.CHANNELS_LAST)
     m = metrics(gather_3d(y, pts), ref, x.dtype)
-    _say("%s D=%d sampled %d %s" % (name, D, len(pts), m))
+    _say("%s D=%d algo %d sampled %d %s" % (name, D, algo, len(pts), m))
     assert_within(m, activated=wl.epilogue != "none")
+
+
+def test_3d_wide_frame_past_2gib():
+    """One input frame of 2 GiB (2048 x 2048 positions x 256 channels): past the 32x32 family's
+    per-frame range, so C_out > 16 runs on the 16x16x32 wide tiles, which address x with 64-bit
+    offsets.  Sampled outputs against the oracle."""
+    wl = si.Workload("wide", "3d", N=1, C_in=256, C_out=32, D=1, H=2048, W=2048, dtype="bf16",
+                     epilogue="none", x_dist="normal", w_var=1.0 / (27 * 256), x_id=61, w_id=61)
+    assert wl.H * wl.W * wl.C_in * 2 >= 1 << 31
+    _say("wide frame past 2 GiB: %s" % ((wl.N, wl.C_in, wl.C_out, wl.D, wl.H, wl.W),))
+    x, w, b = si.make_inputs(wl, device=DEV)
+    y = run_3d(x, w, b, wl.epilogue, C.ALGO_MFMA, guarded=True)
+    pts = sample_points_3d(wl.N, wl.D, wl.H, wl.W, 150, seed=4)
+    ref = oracle.conv3d_points(bits(x), bits(w), bits(b), pts, 1, oracle.BF16, EPI[wl.epilogue],
+                               oracle.CHANNELS_LAST)
+    m = metrics(gather_3d(y, pts), ref, x.dtype)
+    _say("wide frame sampled %d %s" % (len(pts), m))
+    assert_within(m, activated=False)
 
 
 def test_fused_head_at_least_as_accurate_as_split_head():
@@ -356,12 +385,14 @@ def test_fused_head_at_least_as_accurate_as_split_head():
     assert errs[C.ALGO_FUSED_HEAD] <= errs[C.ALGO_SPLIT_HEAD] * 1.02
 
 
-def test_split_head_plane_stage_matches_oracle_plane():
+@pytest.mark.parametrize("Co", [12, 5, 7])
+def test_split_head_plane_stage_matches_oracle_plane(Co):
     """The split head's first stage on its own (conv_head_temporal): the 112-channel plane must
-    equal the oracle's split-mode plane rounded to bf16, channels 108..111 zero (integer inputs,
-    so every sum is exact)."""
-    N, Ci, Co, D, H, W = 1, 32, 12, 3, 9, 50
-    x, w, b = si.integer_case("3d", N, Ci, Co, H, W, D=D, dtype="bf16", seed=77, device=DEV)
+    equal the oracle's split-mode plane rounded to bf16, and the channels past the 9*C_out tap
+    channels must be written as zero (g starts as a NaN sentinel; integer inputs, so every sum
+    is exact)."""
+    N, Ci, D, H, W = 1, 32, 3, 9, 50
+    x, w, b = si.integer_case("3d", N, Ci, Co, H, W, D=D, dtype="bf16", seed=77 + Co, device=DEV)
     from x3x3_convolution_amd.plan import Conv3x3x3
     op = Conv3x3x3(w, b, N, D, H, W, epilogue="clamp1", algo=C.ALGO_SPLIT_HEAD)
     g = torch.full((N, D, H, W, 112), 0x7FFF, dtype=torch.int16, device=DEV).view(torch.bfloat16)
@@ -370,5 +401,5 @@ def test_split_head_plane_stage_matches_oracle_plane():
     _, gref = oracle.head_split(bits(x), bits(w), bits(b), oracle.BF16, oracle.EPI_CLAMP1,
                                 oracle.CHANNELS_LAST, round_g=True, return_g=True)
     got = bits(g)
-    assert np.array_equal(got[..., :108], oracle.encode(gref, oracle.BF16))
-    assert np.all(got[..., 108:] == 0)
+    assert np.array_equal(got[..., :9 * Co], oracle.encode(gref, oracle.BF16))
+    assert np.all(got[..., 9 * Co:] == 0)

@@ -98,7 +98,7 @@ struct HeadGemmKArgs {
     int d_lo, d_hi, h_lo, h_hi;
     int nchunks;       // 32-channel stages per Z row, even (the padding reads zeros)
     int rows_per_band, bands, strips, strip_out, fgroups;
-    uint32_t sample_bytes;  // bytes of one sample of x (buffer-resource range)
+    uint32_t window_bytes;  // bytes of the six input frames of a workgroup (buffer-resource range)
     uint32_t wp_bytes;
     uint32_t total_wg;
 };
@@ -185,16 +185,25 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
     const int nch = a.nchunks;
     const int nstages = nsteps * nch;
 
+    // x through the six input frames the group's window covers: window frame i is input frame
+    // fw0 + i.  fw0 may lie before the first frame (or the window past the last one); those frames
+    // are never addressed (their copies take an offset past the range), so only the address
+    // arithmetic of the base reaches outside x.  Any number of frames works: only the window must
+    // fit the 32-bit range.
+    const int fw0 = f0 - 1 + a.d_org;
+    const long long frame_elems = (long long)a.H_in * a.W * a.C_in;
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(a.x + (size_t)n * a.D_in * a.H_in * a.W * a.C_in), (short)0, (int)a.sample_bytes,
-        0x00020000);
+        (void *)((uintptr_t)a.x + (uintptr_t)((((long long)n * a.D_in + fw0) * frame_elems) * 2)),
+        (short)0, (int)a.window_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
         (void *)a.wp, (short)0, (int)a.wp_bytes, 0x00020000);
-    // FUSED: one sample of y
+    // FUSED: y (or the RGB frames) through the group's four output frames f0 .. f0+3 (frames past
+    // the last one are never stored to)
+    const size_t frame0 = (size_t)n * a.D + f0;
     const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
-        RGB ? (void *)(reinterpret_cast<uint8_t *>(a.out) + (size_t)n * a.D * HW * 12)
-            : (void *)(a.out + (size_t)n * a.D * HW * a.C_out),
-        (short)0, RGB ? (int)(a.D * HW * 12) : (int)(a.D * HW * a.C_out * 2), 0x00020000);
+        RGB ? (void *)(reinterpret_cast<uint8_t *>(a.out) + frame0 * HW * 12)
+            : (void *)(a.out + frame0 * HW * a.C_out),
+        (short)0, RGB ? (int)(4 * HW * 12) : (int)(4 * HW * a.C_out * 2), 0x00020000);
 
     // B window copies: this wave issues copies k = wave + 4*t; lane i of copy k fills slot
     // 64*k + i = ((frame*4 + nb)*32 + column j)*4 + piece', with frame = k/8, nb = (k/2) % 4,
@@ -212,7 +221,6 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
     }
     const uint32_t frame_bytes = (uint32_t)a.H_in * (uint32_t)a.W * (uint32_t)a.C_in * 2u;
     const uint32_t row_bytes = (uint32_t)a.W * (uint32_t)a.C_in * 2u;
-    const int fw0 = f0 - 1 + a.d_org;   // input frame of window frame 0
     // Copies of stage (Z row st, channel chunk c) into one buffer pair.  Weight chunks past the
     // packed ones (the even padding) lie past the resource range and copy zeros.  Every offset
     // is formed without branches: an invalid part is all ones, which the saturating add keeps.
@@ -235,7 +243,7 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
             const int k = wave + 4 * t;
             const int f = fw0 + (t >> 1);
             const uint32_t fok = rok & (uint32_t)((f >= a.d_lo) & (f < a.d_hi));
-            const uint32_t up = ((uint32_t)f * frame_bytes + rbase) | (fok - 1u);
+            const uint32_t up = ((uint32_t)(t >> 1) * frame_bytes + rbase) | (fok - 1u);
             const uint32_t off = __builtin_elementwise_add_sat(colv[t & 1], up);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)&bbuf[k * 64], 16, off, 0, 0, 0);
         }
@@ -417,6 +425,11 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
                         }
                     }
                     if (CO12 && w < a.W && hh == 0) *reinterpret_cast<uint2 *>(dst + 108) = uint2{0u, 0u};
+                    if (!CO12 && w < a.W) {
+                        // channels past the 9*C_out tap channels are zero (the two lane halves
+                        // take alternate ones)
+                        for (int ch = 9 * a.C_out + hh; ch < kPlaneCh; ch += 2) dst[ch] = 0;
+                    }
                 }
             }
         } else {
@@ -478,10 +491,10 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
                 u16 r6[kHalfCo];
 #pragma unroll
                 for (int c = 0; c < kHalfCo; ++c) r6[c] = E::from_f32(epilogue<EPI>(o[c] + b6[c]));
-                // 32-bit offsets into the sample (below 2 GiB), no branches: a store that must
-                // not happen goes to an offset past the buffer range, where it is dropped
+                // 32-bit offsets into the group's four output frames, no branches: a store that
+                // must not happen goes to an offset past the buffer range, where it is dropped
                 const uint32_t yoff =
-                    (uint32_t)(((od * a.H + ho) * a.W + w) * a.C_out + kHalfCo * hh) * 2u;
+                    (uint32_t)(((wave * a.H + ho) * a.W + w) * a.C_out + kHalfCo * hh) * 2u;
                 if constexpr (RGB) {
                     uint32_t q[kHalfCo];
 #pragma unroll
@@ -496,7 +509,7 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
                     const uint32_t p23 = hh == 0 ? (r0 | (q[1] << 8)) : (q[4] | (r1 << 8));
                     const uint32_t p45 = hh == 0 ? (q[5] | (r1 << 8)) : (q[1] | (q[5] << 8));
                     const uint32_t roff =
-                        st_ok ? (uint32_t)(((od * 2 * a.H + 2 * ho + hh) * 2 * a.W + 2 * w) * 3) : kOff;
+                        st_ok ? (uint32_t)(((wave * 2 * a.H + 2 * ho + hh) * 2 * a.W + 2 * w) * 3) : kOff;
                     __builtin_amdgcn_raw_buffer_store_b16((u16)p01, yr, roff, 0, 0);
                     __builtin_amdgcn_raw_buffer_store_b16((u16)p23, yr,
                                                           __builtin_elementwise_add_sat(roff, 2u), 0, 0);
@@ -552,7 +565,7 @@ hipError_t launch_head_gemm(const HeadGemmParams &p, hipStream_t stream) {
     }
     a.rows_per_band = (p.H + best_bands - 1) / best_bands;
     a.bands = (p.H + a.rows_per_band - 1) / a.rows_per_band;
-    a.sample_bytes = (uint32_t)((size_t)p.rg.D_in * p.rg.H_in * p.W * p.C_in * 2);
+    a.window_bytes = (uint32_t)((size_t)kInFrames * p.rg.H_in * p.W * p.C_in * 2);
     a.wp_bytes = (uint32_t)((size_t)packed_chunks * kHeadChunkPieces * 16);
     const long long wgs = cols * a.bands;
     a.total_wg = (uint32_t)wgs;
