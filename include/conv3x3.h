@@ -295,6 +295,29 @@ int conv_head_stencil(const void *g, const void *bias, void *y, int N, int D, in
                       int C_out, int dtype, int epilogue, void *stream);
 
 /* ------------------------------------------------------------------------------------------
+ * For callers that cannot allocate device memory -- code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc: conv3x3x3_fwd with the same arguments and results, but
+ * without a workspace argument.  Where the request needs a workspace (the split-K partial sums of
+ * the MFMA path for small position counts, the split head's plane), it uses a static device
+ * array of CONV_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on until the
+ * process ends; nothing else is allocated, by the library or by any routine it calls.
+ *   - Returns CONV_E_WORKSPACE, with nothing enqueued, when the request needs more than
+ *     CONV_NOALLOC_SCRATCH_BYTES (conv3x3x3_workspace_bytes says how much it needs); other
+ *     errors as conv3x3x3_fwd.  AUTO resolves as in conv3x3x3_fwd (the fused head needs no
+ *     workspace; the split head's plane fits only small frames).
+ *   - Every call on a GPU shares that GPU's array, which keeps the last call's contents (no call
+ *     relies on them: every value read is written first in the same call).  Calls that overlap
+ *     on one GPU -- on different streams, or from different threads -- race on the array; the
+ *     caller orders them (one stream, or events).
+ *   - The first call on a device looks up the array's device address (no allocation, no work
+ *     enqueued); a caller that captures a graph makes one call before the capture.
+ * ---------------------------------------------------------------------------------------- */
+#define CONV_NOALLOC_SCRATCH_BYTES (32u << 20)
+int conv3x3x3_fwd_noalloc(const void *x, const void *w_packed, const void *bias, void *y, int N,
+                          int C_in, int C_out, int D, int H, int W, int stride, int layout,
+                          int dtype, int epilogue, int algo, void *stream);
+
+/* ------------------------------------------------------------------------------------------
  * Measurement aid, not part of the convolution: enqueues `workgroups` workgroups of four waves,
  * each wave issuing `iters` x 8 independent bf16 32x32x16 MFMAs on register operands (2 * 32 *
  * 32 * 16 FLOP each), and writes one float per lane to `out` (device memory of workgroups * 256

@@ -47,7 +47,9 @@ EXPORTS = [
     ("conv_band_region", _I, [_I] * 4 + [ctypes.POINTER(ctypes.c_int)] * 4),
     ("conv_causal_region", _I, [_I] * 2 + [ctypes.POINTER(ctypes.c_int)] * 4),
     ("conv_calib_mfma_bf16", _I, [_P, _I, _I, _P]),
+    ("conv3x3x3_fwd_noalloc", _I, [_P, _P, _P, _P] + [_I] * 11 + [_P]),
 ]
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class ConvError(RuntimeError):
@@ -244,3 +246,13 @@ def conv_causal_region(D_out, cached):
 def conv_calib_mfma_bf16(out, workgroups, iters, stream=None):
     """Enqueues the matrix-core calibration loop (a measurement aid, conv_calib_mfma_bf16)."""
     return _check(library().conv_calib_mfma_bf16(_ptr(out), workgroups, iters, _stream(stream)))
+
+
+def conv3x3x3_fwd_noalloc(x, w_packed, bias, y, N, C_in, C_out, D, H, W, stride=1,
+                          layout=LAYOUT_CHANNELS_LAST, dtype=DTYPE_BF16, epilogue=EPI_NONE,
+                          algo=ALGO_AUTO, stream=None):
+    """conv3x3x3_fwd without a workspace argument: the library's static per-device scratch
+    serves as the workspace (conv3x3x3_fwd_noalloc)."""
+    return _check(library().conv3x3x3_fwd_noalloc(_ptr(x), _ptr(w_packed), _ptr(bias), _ptr(y), N,
+                                                  C_in, C_out, D, H, W, stride, layout, dtype,
+                                                  epilogue, algo, _stream(stream)))

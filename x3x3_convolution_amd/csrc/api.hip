@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "conv3x3.h"
 #include "launch.hpp"
@@ -569,3 +570,70 @@ int conv3x3x3_head_rgb8(const void *x, const void *w_packed, const void *bias, v
 }
 
 }  // extern "C"
+
+// ---- allocation-free forward pass -------------------------------------------------------------
+// A static device array serves as the workspace of conv3x3x3_fwd_noalloc, so that callers that
+// cannot allocate (graph capture, serving loops) still reach the algorithms that need one (the
+// split-K partial sums of the MFMA path, the split head's plane when it fits).  Each GPU the
+// library runs on holds its own copy of the array until the process ends.  In host code the
+// array's name is only a stand-in: its device address is looked up once per device
+// (hipGetSymbolAddress, with that device current) and only that address is passed to kernels.
+namespace cx {
+__device__ __align__(256) unsigned char scratch[CONV_NOALLOC_SCRATCH_BYTES];
+}  // namespace cx
+
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)CONV_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device, once looked up
+
+// The scratch array's device address on the current device (nullptr and a message on failure).
+void *scratch_on_current_device(int *status) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        *status = fail(CONV_E_NODEVICE, "no current HIP device for the static scratch");
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(cx::scratch));
+        if (e != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            *status = fail(CONV_E_LAUNCH, "looking up the static scratch on device %d failed: %s", dev,
+                           hipGetErrorString(e));
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *status = CONV_OK;
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" int conv3x3x3_fwd_noalloc(const void *x, const void *w_packed, const void *bias, void *y,
+                                     int N, int C_in, int C_out, int D, int H, int W, int stride,
+                                     int layout, int dtype, int epilogue, int algo, void *stream) {
+    // the request's workspace, checked against the array before anything else touches a device
+    const int a = select_3d(N, C_in, C_out, D, H, W, stride, layout, dtype, algo);
+    if (a < 0) return a;
+    const size_t need = conv3x3x3_workspace_bytes(N, C_in, C_out, D, H, W, stride, layout, dtype, a);
+    if (need > kScratchBytes)
+        return fail(CONV_E_WORKSPACE,
+                    "this request needs %zu bytes of workspace; the static scratch of the "
+                    "allocation-free entry point holds %zu (use conv3x3x3_fwd with a workspace, or "
+                    "an algorithm that needs less)", need, kScratchBytes);
+    void *ws = nullptr;
+    if (need > 0) {
+        int st = device_present();
+        if (st) return st;
+        ws = scratch_on_current_device(&st);
+        if (!ws) return st;
+    }
+    return conv3x3x3_fwd(x, w_packed, bias, y, N, C_in, C_out, D, H, W, stride, layout, dtype,
+                         epilogue, a, ws, ws ? kScratchBytes : 0, stream);
+}
