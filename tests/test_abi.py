@@ -188,10 +188,12 @@ def test_algo_selection_and_buffer_sizes():
     # packed weights: 8 channel chunks x 27 taps x 16 rows x 32 (direct head)
     assert cx.conv3x3x3_packed_weight_bytes(1, 256, 12, 16, 352, 624, 1, 1, 1,
                                             C.ALGO_MFMA) == 8 * 27 * 16 * 32 * 2
-    # split and fused head: 8 chunks x 3 temporal taps x 128 rows (108 used) x 32
-    for algo in (C.ALGO_SPLIT_HEAD, C.ALGO_FUSED_HEAD):
-        assert cx.conv3x3x3_packed_weight_bytes(1, 256, 12, 16, 352, 624, 1, 1, 1,
-                                                algo) == 8 * 3 * 128 * 32 * 2
+    # split head: 8 chunks x 3 temporal taps x 128 rows (108 used) x 32; the fused head keeps
+    # three row versions of each chunk
+    assert cx.conv3x3x3_packed_weight_bytes(1, 256, 12, 16, 352, 624, 1, 1, 1,
+                                            C.ALGO_SPLIT_HEAD) == 8 * 3 * 128 * 32 * 2
+    assert cx.conv3x3x3_packed_weight_bytes(1, 256, 12, 16, 352, 624, 1, 1, 1,
+                                            C.ALGO_FUSED_HEAD) == 3 * 8 * 3 * 128 * 32 * 2
     # mid-decoder conv fills the chip without split-K: no workspace
     assert cx.conv3x3x3_workspace_bytes(1, 256, 256, 16, 176, 312, 1, 1, 1, 0) == 0
     # the small low-res conv fills the chip with half-size (128-position) tiles: no split-K

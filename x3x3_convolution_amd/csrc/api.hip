@@ -155,7 +155,8 @@ int select_3d(int N, int C_in, int C_out, int D, int H, int W, int stride, int l
 
 // The tile family of a request that passed select_3d (H, W: one input frame's extent).
 int family_for(int algo, int C_in, int C_out, int H, int W, int stride) {
-    if (algo == CONV_ALGO_SPLIT_HEAD || algo == CONV_ALGO_FUSED_HEAD) return cx::IG_TEMPORAL;
+    if (algo == CONV_ALGO_SPLIT_HEAD) return cx::IG_TEMPORAL;
+    if (algo == CONV_ALGO_FUSED_HEAD) return cx::IG_FUSED;
     if (stride == 2) return cx::IG_W32;
     if (C_out <= 16) return cx::IG_NARROW;
     return (long long)H * W * C_in * 2 < (1ll << 31) ? cx::IG_W32 : cx::IG_WIDE;

@@ -4,6 +4,8 @@
 // frames) reaches HBM.
 // (FastVideo head.cu: header comment -- the 27-tap output convolution as a 3x1x1 temporal
 // convolution whose output channels are the nine spatial taps, then a stencil sum.)
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -103,6 +105,27 @@ struct HeadGemmKArgs {
     uint32_t total_wg;
 };
 
+// 0.f through an asm the compiler cannot look into
+__device__ __forceinline__ float opaque_zero() {
+    float z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+    return z;
+}
+// v_permlane16_swap of one register pair: rows (16 lanes) 1 and 3 of a trade places with rows 0
+// and 2 of b.  Written out, since the compiler has merged separate swaps of different registers
+// into one; the waits cover the reads of values the preceding instructions just wrote.
+__device__ __forceinline__ void lane_swap16(float &a, float &b) {
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+// n mod 3 in 0..2 for any int n
+__device__ __forceinline__ int mod3(int n) { return ((n % 3) + 3) % 3; }
+// a + b saturated at 2^32 - 1 (one VALU instruction: the add's clamp bit); b uniform.  An
+// all-ones operand (an invalid part of a copy offset) stays past every buffer range.
+__device__ __forceinline__ uint32_t add_sat(uint32_t a, uint32_t b) {
+    uint32_t r;
+    asm("v_add_u32_e64 %0, %1, %2 clamp" : "=v"(r) : "v"(a), "s"(b));
+    return r;
+}
 // Workgroup barrier without a memory fence (the waits before it are explicit), kept in place
 // by the compiler.
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
@@ -225,16 +248,20 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
     // packed ones (the even padding) lie past the resource range and copy zeros.  Every offset
     // is formed without branches: an invalid part is all ones, which the saturating add keeps.
     auto copy_stage = [&](int st, int c, uint4 *abuf, uint4 *bbuf) __attribute__((always_inline)) {
+        // FUSED: the weight version of the stage's Z row (head_fused_role).  Chunks past the
+        // packed ones (the even padding) lie past the resource range and copy zeros.
+        const int cbase = FUSED ? (c * 3 + mod3(st)) * kHeadChunkPieces : c * kHeadChunkPieces;
 #pragma unroll
         for (int q = 0; q < kCopyA; ++q) {
             const int piece = (wave * kCopyA + q) * 64;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                wr, (lds_void *)&abuf[piece], 16,
-                (uint32_t)((c * kHeadChunkPieces + piece + lane) * 16), 0, 0, 0);
+                wr, (lds_void *)&abuf[piece], 16, (uint32_t)((cbase + piece + lane) * 16), 0, 0, 0);
         }
-        // Z row zr reads input row zr + h_org; window frame i is input frame fw0 + i
-        const int row = zrow0 + st + a.h_org;
-        const uint32_t rok = (uint32_t)((row >= a.h_lo) & (row < a.h_hi));
+        // Z row zr reads input row zr + h_org; window frame i is input frame fw0 + i.  The
+        // frame / row / chunk part of an offset is uniform (scalar registers); the column part
+        // is the lane's; one saturating add joins them.
+        const int row = __builtin_amdgcn_readfirstlane(zrow0 + st + a.h_org);
+        const bool rok = row >= a.h_lo && row < a.h_hi;
         const uint32_t rbase = (uint32_t)row * row_bytes + (uint32_t)(64 * c);
         const uint32_t cmask = 0u - (uint32_t)(32 * c + 8 * bpiece >= a.C_in);   // ~0: no channels
         const uint32_t colv[2] = {bcol[0] | cmask, bcol[1] | cmask};
@@ -242,10 +269,10 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
         for (int t = 0; t < kCopyB; ++t) {
             const int k = wave + 4 * t;
             const int f = fw0 + (t >> 1);
-            const uint32_t fok = rok & (uint32_t)((f >= a.d_lo) & (f < a.d_hi));
-            const uint32_t up = ((uint32_t)(t >> 1) * frame_bytes + rbase) | (fok - 1u);
-            const uint32_t off = __builtin_elementwise_add_sat(colv[t & 1], up);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)&bbuf[k * 64], 16, off, 0, 0, 0);
+            const bool fok = rok && f >= a.d_lo && f < a.d_hi;
+            const uint32_t up = fok ? (uint32_t)(t >> 1) * frame_bytes + rbase : kOff;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)&bbuf[k * 64], 16,
+                                                     add_sat(colv[t & 1], up), 0, 0, 0);
         }
     };
     // Fragment reads of step u (temporal tap u/2, k16 slice u%2): the per-lane part of the slot
@@ -290,11 +317,19 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
         const int co = kHalfCo * hh + c;
         b6[c] = (FUSED && a.bias != nullptr && co < a.C_out) ? E::to_f32(a.bias[co]) : 0.f;
     }
-    float cA[kNB][kHalfCo], cB[kNB][kHalfCo];
+    if constexpr (FUSED) {
+        // the three sets start empty; each is cleared again as its output row is read out
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb)
+        for (int nb = 0; nb < kNB; ++nb) {
 #pragma unroll
-        for (int c = 0; c < kHalfCo; ++c) cA[nb][c] = cB[nb][c] = 0.f;
+            for (int mb = 0; mb < kMB32; ++mb) {
+                acc[mb][nb] = zero;
+                touch(acc[mb][nb]);
+            }
+            t8[nb][0] = t8[nb][1] = zero4;
+            touch(t8[nb][0]), touch(t8[nb][1]);
+        }
+    }
 
     // ---- prologue: stages 0 and 1 copied, stage 0 complete and published ----
     copy_stage(0, 0, As0, Bs0);
@@ -309,8 +344,9 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
 
     // Stage g = st*nch + c uses buffer pair g % 2; each pass of the chunk loop runs an even and
     // the following odd stage.
-#pragma unroll 1
-    for (int st = 0; st < nsteps; ++st) {
+    // One Z row (band-local index st): every channel chunk, two stages per pass.
+    auto row_body = [&](auto K, int st) __attribute__((always_inline)) {
+        (void)K;
 #pragma unroll 1
         for (int c2 = 0; c2 < nch; c2 += 2) {
 #pragma unroll
@@ -339,13 +375,14 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
                         read_frags(na, nbb, 0, af[cur ^ 1], bf[0], a8);
                     }
                     __builtin_amdgcn_sched_barrier(0);
-                    if (half == 0 && u == 0 && c2 == 0) {
-                        // first step of a Z row: the accumulators start from zero
+                    if (!FUSED && half == 0 && u == 0 && c2 == 0) {
+                        // PLANE, first step of a Z row: every accumulator starts from zero
 #pragma unroll
                         for (int mb = 0; mb < kMB32; ++mb)
 #pragma unroll
                             for (int nb = 0; nb < kNB; ++nb)
-                                acc[mb][nb] = E::mfma32x32x16(af[cur][mb], bf[bs][nb], zero);
+                                acc[mb][nb] = E::mfma32x32x16(af[cur][mb], bf[bs][nb],
+                                                              FUSED ? acc[mb][nb] : zero);
                     } else {
 #pragma unroll
                         for (int mb = 0; mb < kMB32; ++mb)
@@ -355,7 +392,7 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
                     }
                     if (u & 1) {
                         // tap 8 of temporal tap u/2: both k16 fragments are in registers
-                        const bool first8 = half == 0 && u == 1 && c2 == 0;
+                        const bool first8 = !FUSED && half == 0 && u == 1 && c2 == 0;   // PLANE
 #pragma unroll
                         for (int nb = 0; nb < kNB; ++nb) {
                             vec8 lo, hi;
@@ -381,15 +418,18 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
             }
         }
 
-        // ---- row zr of Z is complete in this wave's accumulators ----
-        // The epilogues walk the accumulator blocks in order and read each value once, so only
-        // one or two blocks are unpacked into registers at a time.
+    };
+
+    // ---- row zr of Z is complete in this wave's accumulators ----
+    // PLANE: the epilogue walks the accumulator blocks in order and reads each value once, so
+    // only one or two blocks are unpacked into registers at a time.
+    auto plane_epilogue = [&](int st) __attribute__((always_inline)) {
         const int zr = zrow0 + st;
         const size_t frame = (size_t)n * a.D + od;
-        // tap 8, channel c < 6 of lane half h: t8[nb][c / 4][c % 4] after this swap
+        {
+            // tap 8, channel c < 6 of lane half h: t8[nb][c / 4][c % 4] after this swap
 #pragma unroll
-        for (int nb = 0; nb < kNB; ++nb) swap_rows16(t8[nb][0], t8[nb][1]);
-        if constexpr (!FUSED) {
+            for (int nb = 0; nb < kNB; ++nb) swap_rows16(t8[nb][0], t8[nb][1]);
             if (zr < h_end && od < a.D) {
 #pragma unroll
                 for (int nb = 0; nb < kNB; ++nb) {
@@ -432,35 +472,42 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
                     }
                 }
             }
-        } else {
-            // Output row zr-1 = cA + taps ky=2 of row zr; the next cA = cB + taps ky=1; the next
-            // cB = taps ky=0.  Position p takes tap (ky, kx) from position p + kx - 1, so the value
-            // of tap (ky, kx) in block sb feeds the position of block sb + 1 - kx of the same lane,
-            // or across a lane (wavefront shift): block 3 with kx = 0 feeds block 0 of the next
-            // lane, block 0 with kx = 2 block 3 of the previous lane.  The lanes that cross a lane
-            // half or the wave hold halo columns, which are not stored.  Every accumulator is read
-            // once, block by block, and added straight into the carried sums.
+        }
+    };
+    // FUSED, at the end of Z row st (band-local), whose output row st - 1 has set SD: see below.
+    auto fused_epilogue = [&](auto SD, int st) __attribute__((always_inline)) {
+        constexpr int sd = decltype(SD)::value;
+        const int zr = zrow0 + st;
+        {
+            // Output row zr - 1 is complete in set sd (head_fused_role): each of its
+            // 18 slots per position block holds one horizontal tap kx of one output channel,
+            // summed over the three vertical taps.  Position p takes tap kx from position
+            // p + kx - 1, so a slot of block sb feeds the output of block sb + 1 - kx of the same
+            // lane, or across a lane (wavefront shift): block 3 with kx = 0 feeds block 0 of the
+            // next lane, block 0 with kx = 2 block 3 of the previous lane.  The lanes that cross a
+            // lane half or the wave hold halo columns, which are not stored.  The set is cleared
+            // as it is read, for the output row three further on.
             const int ho = zr - 1;   // the output row this Z row completes
             const bool emit = ho >= h_begin && ho < h_end && od < a.D;
-            float n0[kNB][kHalfCo];
+            float osum[kNB][kHalfCo];
 #pragma unroll
             for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
-                for (int c = 0; c < kHalfCo; ++c) n0[nb][c] = 0.f;
-#pragma unroll
-            for (int mb = 0; mb < kMB; ++mb) {
-                if (16 * mb >= 9 * kHalfCo) continue;   // padding rows only
+                for (int c = 0; c < kHalfCo; ++c) osum[nb][c] = b6[c];
+            // a zero the compiler cannot see through, for the tap-8 tiles' register of the set
+            const float z = opaque_zero();
+            {
 #pragma unroll
                 for (int sb = 0; sb < kNB; ++sb) {
-                    if (mb < kMB32) touch(acc[mb < kMB32 ? mb : 0][sb]);
-                    else touch(t8[sb][0]), touch(t8[sb][1]);
+                    // register sd of the two tap-8 tiles: one lane swap gives this lane channels
+                    // 4 and 5 of its half (horizontal tap 2)
+                    float r[2] = {t8[sb][0][sd], t8[sb][1][sd]};
+                    lane_swap16(r[0], r[1]);
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int t = 16 * mb + i;
-                        if (t >= 9 * kHalfCo) continue;
-                        const int tap = t / kHalfCo, ky = tap / 3, kx = tap % 3, c = t % kHalfCo;
+                    for (int q = 0; q < 18; ++q) {
+                        const int kx = q / kHalfCo, c = q % kHalfCo;
                         int nb = sb + 1 - kx;
-                        float v = mb < kMB32 ? acc[mb < kMB32 ? mb : 0][sb][i] : t8[sb][c >> 2][c & 3];
+                        float v = q < 16 ? acc[sd][sb][q < 16 ? q : 0] : r[q - 16 > 0 ? 1 : 0];
                         if (nb >= kNB) {   // to the next lane (it takes lane l-1)
                             nb = 0;
                             v = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
@@ -470,27 +517,29 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
                             v = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
                                 0, __builtin_bit_cast(int, v), 0x130, 0xF, 0xF, false));
                         }
-                        if (ky == 2) cA[nb][c] += v;
-                        else if (ky == 1) cB[nb][c] += v;
-                        else n0[nb][c] += v;
+                        osum[nb][c] += v;
                     }
+                    // cleared for the output row three further on: the 32x32 block by a matrix
+                    // instruction of zeros (an ordinary accumulator result, so it stays in place),
+                    // the tiles' register directly
+                    vec8 za;   // zeros the compiler cannot see: one instruction per block
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        reinterpret_cast<float *>(&za)[e] = opaque_zero();
+                    acc[sd][sb] = E::mfma32x32x16(za, za, zero);
+                    t8[sb][0][sd] = z;
+                    t8[sb][1][sd] = z;
                 }
             }
 #pragma unroll
             for (int nb = 0; nb < kNB; ++nb) {
-                float o[kHalfCo];
-#pragma unroll
-                for (int c = 0; c < kHalfCo; ++c) {
-                    o[c] = cA[nb][c];
-                    cA[nb][c] = cB[nb][c];
-                    cB[nb][c] = n0[nb][c];
-                }
+                const float *o = osum[nb];
                 const int p = 4 * j + nb;
                 const int w = w0 + p;
                 const bool st_ok = emit && p >= 1 && p <= a.strip_out && w < a.W;
                 u16 r6[kHalfCo];
 #pragma unroll
-                for (int c = 0; c < kHalfCo; ++c) r6[c] = E::from_f32(epilogue<EPI>(o[c] + b6[c]));
+                for (int c = 0; c < kHalfCo; ++c) r6[c] = E::from_f32(epilogue<EPI>(o[c]));
                 // 32-bit offsets into the group's four output frames, no branches: a store that
                 // must not happen goes to an offset past the buffer range, where it is dropped
                 const uint32_t yoff =
@@ -529,6 +578,31 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
                 }
             }
         }
+    };
+
+    if constexpr (FUSED) {
+        // Sets are numbered from the band's first Z row: Z row st takes weight version st mod 3
+        // and completes output row st - 1 (band-local), whose set is (st - 1) mod 3.  Unrolled by
+        // three so that the set is a compile-time index.
+#pragma unroll 1
+        for (int st = 0; st < nsteps; st += 3) {
+            row_body(std::integral_constant<int, 0>{}, st);
+            fused_epilogue(std::integral_constant<int, 2>{}, st);
+            if (st + 1 < nsteps) {
+                row_body(std::integral_constant<int, 1>{}, st + 1);
+                fused_epilogue(std::integral_constant<int, 0>{}, st + 1);
+            }
+            if (st + 2 < nsteps) {
+                row_body(std::integral_constant<int, 2>{}, st + 2);
+                fused_epilogue(std::integral_constant<int, 1>{}, st + 2);
+            }
+        }
+    } else {
+#pragma unroll 1
+        for (int st = 0; st < nsteps; ++st) {
+            row_body(std::integral_constant<int, 0>{}, st);
+            plane_epilogue(st);
+        }
     }
     // no LDS copy may still be in flight when the workgroup's LDS is released
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -566,7 +640,7 @@ hipError_t launch_head_gemm(const HeadGemmParams &p, hipStream_t stream) {
     a.rows_per_band = (p.H + best_bands - 1) / best_bands;
     a.bands = (p.H + a.rows_per_band - 1) / a.rows_per_band;
     a.window_bytes = (uint32_t)((size_t)kInFrames * p.rg.H_in * p.W * p.C_in * 2);
-    a.wp_bytes = (uint32_t)((size_t)packed_chunks * kHeadChunkPieces * 16);
+    a.wp_bytes = (uint32_t)((size_t)packed_chunks * (p.fused ? 3 : 1) * kHeadChunkPieces * 16);
     const long long wgs = cols * a.bands;
     a.total_wg = (uint32_t)wgs;
     const dim3 grid((unsigned)wgs), block(256);

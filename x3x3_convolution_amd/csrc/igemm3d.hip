@@ -600,7 +600,7 @@ __global__ __launch_bounds__(256) void pack3d_kernel(const u16 *w, u16 *wp, int 
         const int cc = (int)(r / 27);
         const int ci = cc * 32 + k2 * 16 + k;
         if (ci < C_in && m < C_out) v = w[((size_t)m * C_in + ci) * 27 + tap];
-    } else if (family != IG_TEMPORAL) {
+    } else if (family != IG_TEMPORAL && family != IG_FUSED) {
         const int k = (int)(idx & 31);
         long long r = idx >> 5;
         const int m = (int)(r % Mpad);
@@ -610,15 +610,19 @@ __global__ __launch_bounds__(256) void pack3d_kernel(const u16 *w, u16 *wp, int 
         const int ci = cc * 32 + k;
         if (ci < C_in && m < C_out) v = w[((size_t)m * C_in + ci) * 27 + tap];
     } else {
-        const int cc = (int)(idx / (kHeadChunkPieces * 8));
-        const int rem = (int)(idx - (long long)cc * (kHeadChunkPieces * 8));
+        // IG_TEMPORAL: one row layout per chunk; IG_FUSED: three versions, version after chunk
+        const int nver = family == IG_FUSED ? 3 : 1;
+        const int cv = (int)(idx / (kHeadChunkPieces * 8));
+        const int cc = cv / nver, ver = cv - cc * nver;
+        const int rem = (int)(idx - (long long)cv * (kHeadChunkPieces * 8));
         const int slot = rem >> 3, e = rem & 7;
         const int r = slot >> 2;
         const int q = (slot & 3) ^ head_lds_swizzle(r);
         const int kd = r >> 7, m = r & 127;
         const int ci = cc * 32 + 8 * q + e;
         int tap, co;
-        head_row_role(m, tap, co);
+        if (family == IG_FUSED) head_fused_role(m, ver, tap, co);
+        else head_row_role(m, tap, co);
         if (ci < C_in && tap >= 0 && co < C_out)
             v = w[((size_t)co * C_in + ci) * 27 + kd * 9 + tap];
     }
@@ -701,8 +705,9 @@ IgemmPlan plan_igemm(int family, int N, int C_in, int C_out, int D, int H, int W
             pl.Mrows = C_out;
             pl.TH = 8, pl.TW = 32;
             break;
-        default:   // the head kernels: 3 temporal taps x 128 rows (9 * C_out used)
-            pl.BM = 128, pl.TH = 1, pl.TW = 256, pl.ntaps = 3;
+        default:   // the head kernels: 3 temporal taps x 128 rows (9 * C_out used); the fused
+                   // head's three row versions of them
+            pl.BM = 128, pl.TH = 1, pl.TW = 256, pl.ntaps = family == IG_FUSED ? 9 : 3;
             pl.Mrows = 128;
             break;
     }
@@ -710,7 +715,7 @@ IgemmPlan plan_igemm(int family, int N, int C_in, int C_out, int D, int H, int W
     pl.mtiles = pl.Mpad / pl.BM;
     // 32-channel chunks
     pl.nchunks = (C_in + 31) / 32;
-    if (family == IG_TEMPORAL) {
+    if (family == IG_TEMPORAL || family == IG_FUSED) {
         // 256 consecutive positions of one frame per workgroup (no spatial structure needed)
         pl.tiles_h = 1;
         pl.tiles_w = (int)(((long long)H * W + 255) / 256);
@@ -749,7 +754,7 @@ IgemmPlan plan_igemm(int family, int N, int C_in, int C_out, int D, int H, int W
                 }
             }
         }
-    } else if (family != IG_TEMPORAL && base > 0 && base < 1024) {
+    } else if (family != IG_TEMPORAL && family != IG_FUSED && base > 0 && base < 1024) {
         // (the 16x16 kernels run two workgroups per CU)
         splits = (int)((1024 + base - 1) / base);
         if (splits > pl.nchunks) splits = pl.nchunks;

@@ -43,8 +43,10 @@ enum IgemmFamily {
     IG_WIDE = 0,   // 128 output rows x 128 positions per workgroup: C_out > 16
     IG_NARROW = 1, // 16 output rows x 256 positions: C_out <= 16 (the direct head)
     IG_TEMPORAL = 2, // packing only: 3 temporal taps x 128 rows (9 taps x 12 channels), head kernels
-    IG_W32 = 3      // 256 output rows x 8x32 positions on 32x32x16 MFMA: C_out > 16, one frame of
+    IG_W32 = 3,     // 256 output rows x 8x32 positions on 32x32x16 MFMA: C_out > 16, one frame of
                     // x below 2 GiB (addressed through a 32-bit buffer range)
+    IG_FUSED = 4    // packing only: the fused head's three row versions (head_fused_role) of
+                    // 3 temporal taps x 128 rows per chunk
 };
 
 struct IgemmPlan {
@@ -125,7 +127,37 @@ __host__ __device__ inline void head_row_role(int m, int &tap, int &co) {
     co = 6 * h + t % 6;
 }
 
-// ---- the head's temporal GEMM (packed like IG_TEMPORAL): plane output or fused stencil -----
+// The fused head's rows: the accumulators carry the stencil's vertical sum from Z row to Z row.
+// Lane half hh of a wave holds three sets of 18 slots, set s = accumulator block s (16 slots) and
+// register s of the two tap-8 tiles (the tile rows 4g + s, g = 2hh + j, j = 0, 1: slots 16 + j);
+// slot q of a set holds horizontal tap kx = q / 6 of output channel 6hh + q % 6.  Set s belongs to
+// the output rows o = s (mod 3): Z row zr adds its vertical tap ky = zr - o + 1 to the sets of
+// output rows zr - 1, zr and zr + 1, so under the weight version v = zr mod 3 set s takes
+// ky = (v + 1 - s) mod 3.  Sets tap = ky * 3 + kx (-1 for a padding row) and co of GEMM row m.
+__host__ __device__ inline void head_fused_role(int m, int v, int &tap, int &co) {
+    int s, hh, q;
+    if (m < 96) {
+        const int rr = m & 31;
+        s = m >> 5;
+        hh = (rr >> 2) & 1;
+        q = 4 * (rr >> 3) + (rr & 3);
+    } else {
+        const int r8 = m - 96, g = r8 >> 2;
+        s = r8 & 3;
+        if (r8 >= 16 || s == 3) {
+            tap = -1, co = 0;
+            return;
+        }
+        hh = g >> 1;
+        q = 16 + (g & 1);
+    }
+    const int ky = (v + 1 - s + 3) % 3;
+    tap = ky * 3 + q / 6;
+    co = 6 * hh + q % 6;
+}
+
+// ---- the head's temporal GEMM (packed like IG_TEMPORAL / IG_FUSED): plane output or fused
+// stencil -----
 struct HeadGemmParams {
     const void *x, *wp, *bias;
     void *out;         // the 112-channel plane (fused = false), y (fused = true) or, with rgb,
