@@ -101,7 +101,7 @@ def parse():
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--mfma-calibration", action="store_true",
                     help="only run the matrix-core calibration loop (bf16 32x32x16 MFMAs on "
-                         "register operands) and exit")
+                         "register operands) and the global -> LDS copy rates, and exit")
     ap.add_argument("--no-workloads", action="store_true",
                     help="default line only: skip the other workloads' entries")
     return ap.parse_args()
@@ -155,6 +155,34 @@ def mfma_calibration(stream):
     tf = flop / (ms * 1e-3) / 1e12
     return {"mfma_loop_flop": flop, "mfma_loop_ms": ms, "mfma_loop_tflops": round(tf, 1),
             "mfma_loop_frac_of_peak": round(tf / MFMA_BF16_PEAK_TFS, 4)}
+
+
+def lds_dma_calibration(stream):
+    """The rate of global -> LDS copies (16 bytes per lane, the way the kernels stage operands)
+    with every CU busy: whole 128-byte lines and half lines (64 bytes, the pattern of a
+    32-channel slice of 256-channel positions), from an L2-resident 4 MiB source and from a
+    1 GiB source that streams from HBM."""
+    import torch
+    from x3x3_convolution_amd import conv as C
+    src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    wgs, iters = 256, 400
+    out = {}
+    for label, nbytes in (("l2", 4 << 20), ("hbm", 1 << 30)):
+        for whole in (1, 0):
+            C.conv_calib_lds_dma(src, nbytes, whole, wgs, iters, stream)
+            torch.cuda.synchronize()
+            tm = Timer(torch.cuda.current_stream())
+            for _ in range(3):
+                s0 = tm.start()
+                C.conv_calib_lds_dma(src, nbytes, whole, wgs, iters, stream)
+                tm.stop("dma", s0)
+            torch.cuda.synchronize()
+            ms = tm.stats("dma")["median"]
+            gbs = wgs * 4.0 * iters * 16 * 1024 / (ms * 1e-3) / 1e9
+            out["lds_dma_%s_%s_gbs" % (label, "whole_lines" if whole else "half_lines")] = round(gbs, 1)
+    del src
+    torch.cuda.empty_cache()
+    return out
 
 
 class Timer:
@@ -662,7 +690,7 @@ def main():
     torch.cuda.set_stream(strm)
     stream = strm.cuda_stream
     if args.mfma_calibration:
-        print(json.dumps(mfma_calibration(stream)))
+        print(json.dumps(dict(mfma_calibration(stream), **lds_dma_calibration(stream))))
         return
     wl = si.WORKLOADS[args.workload]
     line = dict(metric=METRIC, n_gpus=1, steps=args.steps, warmup=args.warmup,
@@ -693,7 +721,8 @@ def main():
         torch.cuda.empty_cache()
         if not args.no_workloads and args.algo == "auto":
             line["workloads"] = run_workloads(args, stream)
-            line["calibration"] = dict(copy_calibration(), **mfma_calibration(stream))
+            line["calibration"] = dict(copy_calibration(), **mfma_calibration(stream),
+                                       **lds_dma_calibration(stream))
     else:
         wall_ms, roof, _, _ = run_other(args, wl, stream)
         layout = ("NHWC" if args.channels_last else "NCHW") if wl.kind == "2d" else "NDHWC"

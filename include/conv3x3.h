@@ -327,6 +327,16 @@ int conv3x3x3_fwd_noalloc(const void *x, const void *w_packed, const void *bias,
  * ---------------------------------------------------------------------------------------- */
 int conv_calib_mfma_bf16(void *out, int workgroups, int iters, void *stream);
 
+/* Measurement aid, not part of the convolution: enqueues `workgroups` workgroups of four waves,
+ * each wave issuing iters x 16 global -> LDS copies of 1 KiB (16 bytes per lane) from `src`
+ * (device memory of src_bytes bytes, caller-owned, 1 MiB <= src_bytes < 2 GiB; only the first
+ * half plus one copy's span is read).  whole_lines != 0: each copy reads 1 KiB of consecutive
+ * bytes (eight whole 128-byte lines); 0: 16 pieces of 64 bytes 512 bytes apart (half lines).
+ * Timed by the caller, bytes = workgroups * 4 * iters * 16 KiB.  Returns CONV_E_INVAL for bad
+ * arguments, CONV_E_LAUNCH if the launch is rejected. */
+int conv_calib_lds_dma(const void *src, size_t src_bytes, int whole_lines, int workgroups,
+                       int iters, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -48,6 +48,7 @@ EXPORTS = [
     ("conv_causal_region", _I, [_I] * 2 + [ctypes.POINTER(ctypes.c_int)] * 4),
     ("conv_calib_mfma_bf16", _I, [_P, _I, _I, _P]),
     ("conv3x3x3_fwd_noalloc", _I, [_P, _P, _P, _P] + [_I] * 11 + [_P]),
+    ("conv_calib_lds_dma", _I, [_P, _SZ, _I, _I, _I, _P]),
 ]
 NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -256,3 +257,9 @@ def conv3x3x3_fwd_noalloc(x, w_packed, bias, y, N, C_in, C_out, D, H, W, stride=
     return _check(library().conv3x3x3_fwd_noalloc(_ptr(x), _ptr(w_packed), _ptr(bias), _ptr(y), N,
                                                   C_in, C_out, D, H, W, stride, layout, dtype,
                                                   epilogue, algo, _stream(stream)))
+
+
+def conv_calib_lds_dma(src, src_bytes, whole_lines, workgroups, iters, stream=None):
+    """Enqueues the global -> LDS copy calibration loop (a measurement aid, conv_calib_lds_dma)."""
+    return _check(library().conv_calib_lds_dma(_ptr(src), src_bytes, int(whole_lines),
+                                               workgroups, iters, _stream(stream)))

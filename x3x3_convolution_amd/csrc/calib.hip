@@ -1,7 +1,8 @@
-// Measurement aid, not part of the convolution: the rate the matrix cores reach on a loop of
-// nothing but bf16 32x32x16 MFMAs with register operands.  The benchmark reports it beside the
-// plain-copy rate as what this machine's matrix cores sustain (clock and power included); the
-// roofline fractions are still taken against the published peak.
+// Measurement aids, not part of the convolution: the rate the matrix cores reach on a loop of
+// nothing but bf16 32x32x16 MFMAs with register operands, and the rate of global -> LDS copies
+// (the way the kernels stage their operands) for whole and half cache lines.  The benchmark
+// reports them beside the plain-copy rate as what this machine sustains (clock and power
+// included); the roofline fractions are still taken against the published peaks.
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -38,8 +39,54 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(float *out, int iters) {
     out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// Global -> LDS copies (buffer_load ... lds, 16 bytes per lane): each wave keeps copying 16 KiB
+// slices of `src` into its own 16 KiB of LDS, up to 32 copies in flight.  LINE = 1: one copy
+// is 1 KiB of consecutive bytes (eight whole 128-byte lines); LINE = 0: 16 pieces of 64 bytes
+// 512 bytes apart (half lines, the pattern of a 32-channel slice of channels-last positions with
+// 256 channels).  Offsets stay inside the first half of `src` (plus one copy's span).
+template <int LINE>
+__global__ __launch_bounds__(256, 1) void lds_dma_kernel(const unsigned char *src,
+                                                        unsigned src_bytes, int iters) {
+    typedef __attribute__((address_space(3))) void lds_void;
+    __shared__ __attribute__((aligned(16))) uint4 buf[4][16][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void *)src, (short)0, (int)src_bytes, 0x00020000);
+    const unsigned span = src_bytes / 2;
+    const unsigned wbase = ((blockIdx.x * 4u + (unsigned)wave) * 2654435761u) % span;
+    const unsigned lo = LINE ? (unsigned)lane * 16u : (unsigned)(lane >> 2) * 512u + (lane & 3) * 16u;
+    const unsigned step = LINE ? 1024u : 8192u;
+#pragma unroll 1
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const unsigned off = ((wbase + (unsigned)(it * 16 + j) * step) % span) & ~15u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)&buf[wave][j][0], 16, off + lo,
+                                                     0, 0, 0);
+            if (j % 4 == 3)   // at most 32 copies in flight
+                __builtin_amdgcn_s_waitcnt((32 & 15) | ((32 >> 4) << 14) | (7 << 4) | (15 << 8));
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+}
+
 }  // namespace
 }  // namespace cx
+
+extern "C" int conv_calib_lds_dma(const void *src, size_t src_bytes, int whole_lines,
+                                  int workgroups, int iters, void *stream) {
+    if (!src || src_bytes < (1u << 20) || src_bytes > (1ull << 31) - 1 || workgroups < 1 ||
+        workgroups > (1 << 20) || iters < 1)
+        return CONV_E_INVAL;
+    const unsigned char *s = static_cast<const unsigned char *>(src);
+    if (whole_lines)
+        hipLaunchKernelGGL(cx::lds_dma_kernel<1>, dim3((unsigned)workgroups), dim3(256), 0,
+                           (hipStream_t)stream, s, (unsigned)src_bytes, iters);
+    else
+        hipLaunchKernelGGL(cx::lds_dma_kernel<0>, dim3((unsigned)workgroups), dim3(256), 0,
+                           (hipStream_t)stream, s, (unsigned)src_bytes, iters);
+    return hipGetLastError() == hipSuccess ? CONV_OK : CONV_E_LAUNCH;
+}
 
 extern "C" int conv_calib_mfma_bf16(void *out, int workgroups, int iters, void *stream) {
     if (!out || workgroups < 1 || iters < 1 || workgroups > (1 << 20))
