@@ -557,6 +557,7 @@ def run_other(args, wl, stream):
     if wl.kind == "3d":
         roof["weight_pack_ms"] = pack_ms
         roof["mfma_tflops"] = tflops
+        roof["plan"] = C.conv3x3x3_describe(wl.N, wl.C_in, wl.C_out, wl.D, wl.H, wl.W, s3)
     return wall_ms, roof, y, (x, w, b)
 
 

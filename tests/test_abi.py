@@ -2,6 +2,7 @@
 rejects every invalid request before it enqueues anything.  No compute calls (no GPU needed);
 fake device addresses are only passed on paths that fail validation or return before a launch.
 """
+import ctypes
 import os
 import re
 
@@ -198,9 +199,11 @@ def test_algo_selection_and_buffer_sizes():
     assert cx.conv3x3x3_workspace_bytes(1, 256, 256, 16, 176, 312, 1, 1, 1, 0) == 0
     # the small low-res conv fills the chip with half-size (128-position) tiles: no split-K
     assert cx.conv3x3x3_workspace_bytes(1, 512, 512, 4, 44, 78, 1, 1, 1, 0) == 0
-    # its first causal frame alone still splits K over channel chunks: fp32 partials
-    ws = cx.conv3x3x3_workspace_bytes(1, 512, 512, 1, 44, 78, 1, 1, 1, 0)
-    assert ws > 0 and ws % (44 * 78 * 512 * 4) == 0
+    # its first causal frame alone splits K over the four waves of each workgroup: no workspace
+    assert cx.conv3x3x3_workspace_bytes(1, 512, 512, 1, 44, 78, 1, 1, 1, 0) == 0
+    # fewer input channels over the same frame split K over workgroups: fp32 partials
+    ws = cx.conv3x3x3_workspace_bytes(1, 264, 96, 1, 44, 78, 1, 1, 1, 0)
+    assert ws > 0 and ws % (44 * 78 * 96 * 4) == 0
     assert cx.conv3x3x3_workspace_bytes(1, 512, 512, 4, 44, 78, 1, 1, 1, 9) == 0  # invalid
     assert cx.conv3x3x3_packed_weight_bytes(1, 20, 12, 1, 4, 4, 1, 1, 1, 0) == 0  # unsupported
     # spatial stride 2: AUTO is the MFMA path (the 32x32 family, 256 packed rows, even for the
@@ -390,3 +393,26 @@ def test_head_any_number_of_frames():
     assert cx.conv3x3x3_select_algo(1, 256, 12, 2, 2048, 1024, 1, 1, 1, 0) == C.ALGO_MFMA
     assert cx.conv3x3x3_is_supported(1, 256, 12, 2, 2048, 1024, 1, 1, 1, 2,
                                      C.ALGO_FUSED_HEAD) == C.E_UNSUPPORTED
+
+
+def test_describe_names_the_plan():
+    d = C.conv3x3x3_describe
+    assert d(1, 512, 512, 1, 44, 78) == "igemm32_kq tile=8x16 rows=64 splits=1 workgroups=240"
+    assert d(1, 512, 512, 4, 44, 78) == "igemm32 tile=8x16 rows=256 splits=1 workgroups=240"
+    assert d(1, 264, 96, 1, 44, 78) == "igemm32 tile=4x32 rows=256 splits=5 workgroups=165"
+    assert d(1, 256, 12, 16, 352, 624) == "fused_head"
+    assert d(1, 256, 12, 16, 352, 624, algo=C.ALGO_SPLIT_HEAD) == "split_head"
+    assert d(1, 256, 12, 16, 352, 624, algo=C.ALGO_MFMA).startswith("igemm16_narrow tile=8x32 rows=16 ")
+    assert d(1, 256, 12, 16, 352, 624, stride=2).startswith("igemm32 tile=4x32 rows=256 ")
+    # truncation: the full length comes back, the buffer holds what fits
+    lib = C.library()
+    buf = ctypes.create_string_buffer(8)
+    n = lib.conv3x3x3_describe(1, 512, 512, 1, 44, 78, 1, 1, 1, 0, buf, 8)
+    assert n == len("igemm32_kq tile=8x16 rows=64 splits=1 workgroups=240") and buf.value == b"igemm32"
+    # errors: no buffer, and what select_algo rejects
+    assert lib.conv3x3x3_describe(1, 512, 512, 1, 44, 78, 1, 1, 1, 0, None, 8) == C.E_INVAL
+    assert lib.conv3x3x3_describe(1, 512, 512, 1, 44, 78, 1, 1, 1, 0, buf, 0) == C.E_INVAL
+    rejected = lib.conv3x3x3_select_algo(1, 20, 12, 1, 4, 4, 1, 1, 1, 0)
+    assert rejected < 0 and lib.conv3x3x3_describe(1, 20, 12, 1, 4, 4, 1, 1, 1, 0, buf, 8) == rejected
+    with pytest.raises(C.ConvError):
+        d(1, 20, 12, 1, 4, 4)

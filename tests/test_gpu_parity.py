@@ -165,9 +165,39 @@ def test_conv3d_w32_tiles_integer_exact(case):
     _say("conv3d w32 tile %s" % (case,))
     ws = C.conv3x3x3_workspace_bytes(N, Ci, Co, D, H, W, dtype=C.DTYPE_BF16, algo=C.ALGO_MFMA)
     assert (ws > 0) == splitk
+    assert C.conv3x3x3_describe(N, Ci, Co, D, H, W, algo=C.ALGO_MFMA).startswith(
+        "igemm32 tile=%s rows=256 " % tile)
     x, w, b = si.integer_case("3d", N, Ci, Co, H, W, D=D, dtype="bf16",
                               seed=300 + CASES_W32_TILES.index(case), device=DEV)
     y = run_3d(x, w, b, epi, C.ALGO_MFMA, guarded=True)
+    assert_bit_exact(y, oracle_3d(x, w, b, epi), x.dtype)
+
+
+# The 32x32 family with K split over the four waves of a workgroup (64-row tiles, the partial
+# tiles summed through LDS, no workspace), where the cost model sends it: few positions, many
+# input channels.  Ragged chunk counts (264 channels: waves of 2, 2, 2, 3 chunks, the last chunk
+# a quarter full; 296: 2, 3, 2, 3), part-empty 64-row tiles (72, 100, 130 channels), ragged
+# frame edges, first and last frames with two temporal taps, both 128-position tiles and fp16.
+CASES_KQ = [
+    # N, Ci, Co, D, H, W, dtype, epilogue, tile
+    (1, 264, 72, 3, 36, 60, "bf16", "relu", "4x32"),
+    (1, 296, 130, 1, 50, 90, "bf16", "none", "4x32"),
+    (1, 256, 256, 2, 44, 78, "bf16", "clamp1", "8x16"),
+    (1, 488, 100, 3, 30, 50, "f16", "none", "4x32"),
+]
+
+
+@pytest.mark.parametrize("case", CASES_KQ, ids=[str(c) for c in CASES_KQ])
+def test_conv3d_kq_integer_exact(case):
+    N, Ci, Co, D, H, W, dt, epi, tile = case
+    _say("conv3d kq %s" % (case,))
+    dtype = C.DTYPE_F16 if dt == "f16" else C.DTYPE_BF16
+    assert C.conv3x3x3_workspace_bytes(N, Ci, Co, D, H, W, dtype=dtype, algo=C.ALGO_AUTO) == 0
+    assert C.conv3x3x3_describe(N, Ci, Co, D, H, W, dtype=dtype).startswith(
+        "igemm32_kq tile=%s rows=64 splits=1 " % tile)
+    x, w, b = si.integer_case("3d", N, Ci, Co, H, W, D=D, dtype=dt,
+                              seed=500 + CASES_KQ.index(case), device=DEV)
+    y = run_3d(x, w, b, epi, C.ALGO_AUTO, guarded=True)
     assert_bit_exact(y, oracle_3d(x, w, b, epi), x.dtype)
 
 

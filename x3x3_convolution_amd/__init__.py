@@ -8,9 +8,9 @@ from .conv import (  # noqa: F401
     ABI_VERSION, ALGO_AUTO, ALGO_FUSED_HEAD, ALGO_MFMA, ALGO_SIMT, ALGO_SPLIT_HEAD, DTYPE_BF16, DTYPE_F16,
     EPI_CLAMP1, EPI_NONE, EPI_RELU, LAYOUT_CHANNELS_FIRST, LAYOUT_CHANNELS_LAST, ConvError,
     E_INVAL, E_LAUNCH, E_NODEVICE, E_UNSUPPORTED, E_WORKSPACE, OK, conv3x3_fwd,
-    conv3x3_is_supported, conv3x3_select_algo, conv3x3x3_fwd, conv3x3x3_fwd_noalloc, conv3x3x3_fwd_region, conv3x3x3_head_rgb8,
-    conv3x3x3_is_supported,
+    conv3x3_is_supported, conv3x3_select_algo, conv3x3x3_describe, conv3x3x3_fwd,
+    conv3x3x3_fwd_noalloc, conv3x3x3_fwd_region, conv3x3x3_head_rgb8, conv3x3x3_is_supported,
     conv3x3x3_pack_weights,
     conv3x3x3_packed_weight_bytes, conv3x3x3_select_algo, conv3x3x3_workspace_bytes,
-    conv_abi_version, conv_band_region, conv_calib_mfma_bf16, conv_causal_region, conv_head_stencil, conv_head_temporal, conv_last_error, conv_out_size,
+    conv_abi_version, conv_band_region, conv_calib_lds_dma, conv_calib_mfma_bf16, conv_causal_region, conv_head_stencil, conv_head_temporal, conv_last_error, conv_out_size,
     conv_status_str, conv_video_rgb8, library, library_path)

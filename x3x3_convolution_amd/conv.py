@@ -49,6 +49,7 @@ EXPORTS = [
     ("conv_calib_mfma_bf16", _I, [_P, _I, _I, _P]),
     ("conv3x3x3_fwd_noalloc", _I, [_P, _P, _P, _P] + [_I] * 11 + [_P]),
     ("conv_calib_lds_dma", _I, [_P, _SZ, _I, _I, _I, _P]),
+    ("conv3x3x3_describe", _I, [_I] * 10 + [ctypes.c_char_p, _I]),
 ]
 NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -263,3 +264,13 @@ def conv_calib_lds_dma(src, src_bytes, whole_lines, workgroups, iters, stream=No
     """Enqueues the global -> LDS copy calibration loop (a measurement aid, conv_calib_lds_dma)."""
     return _check(library().conv_calib_lds_dma(_ptr(src), src_bytes, int(whole_lines),
                                                workgroups, iters, _stream(stream)))
+
+
+def conv3x3x3_describe(N, C_in, C_out, D, H, W, stride=1, layout=LAYOUT_CHANNELS_LAST,
+                       dtype=DTYPE_BF16, algo=ALGO_AUTO):
+    """The launch plan conv3x3x3_fwd would use for this request, as one line of text."""
+    buf = ctypes.create_string_buffer(256)
+    n = library().conv3x3x3_describe(N, C_in, C_out, D, H, W, stride, layout, dtype, algo, buf, 256)
+    if n < 0:
+        _check(n)
+    return buf.value.decode()

@@ -337,6 +337,26 @@ size_t conv3x3x3_packed_weight_bytes(int N, int C_in, int C_out, int D, int H, i
     return cx::packed_bytes(plan_for(a, N, C_in, C_out, D, H, W, stride));
 }
 
+int conv3x3x3_describe(int N, int C_in, int C_out, int D, int H, int W, int stride, int layout,
+                       int dtype, int algo, char *buf, int buf_len) {
+    const int a = select_3d(N, C_in, C_out, D, H, W, stride, layout, dtype, algo);
+    if (a < 0) return a;
+    if (!buf || buf_len < 1) return fail(CONV_E_INVAL, "buf must be non-NULL with buf_len >= 1");
+    char tmp[160];
+    if (a == CONV_ALGO_SPLIT_HEAD || a == CONV_ALGO_FUSED_HEAD) {
+        snprintf(tmp, sizeof tmp, "%s", a == CONV_ALGO_SPLIT_HEAD ? "split_head" : "fused_head");
+    } else {
+        const cx::IgemmPlan pl = plan_for(a, N, C_in, C_out, D, H, W, stride);
+        const char *k = pl.family == cx::IG_W32 ? (pl.kq ? "igemm32_kq" : "igemm32")
+                        : pl.family == cx::IG_WIDE ? "igemm16_wide" : "igemm16_narrow";
+        snprintf(tmp, sizeof tmp, "%s tile=%dx%d rows=%d splits=%d workgroups=%lld", k, pl.TH,
+                 pl.TW, pl.kq ? 64 : pl.BM, pl.splits, pl.workgroups);
+    }
+    snprintf(buf, (size_t)buf_len, "%s", tmp);
+    ok();
+    return (int)strlen(tmp);
+}
+
 int conv3x3x3_pack_weights(const void *w_oidhw, void *w_packed, int N, int C_in, int C_out,
                            int D, int H, int W, int stride, int layout, int dtype, int algo,
                            void *stream) {

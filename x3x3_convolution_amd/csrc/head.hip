@@ -71,7 +71,6 @@ namespace {
 // two extra rows.  Nothing of Z is rounded or stored: the fused head keeps fp32 from the GEMM to
 // the epilogue.
 // ---------------------------------------------------------------------------------------------
-constexpr int kMB = 4;                  // 32-row blocks: 128 GEMM rows per temporal tap in LDS
 constexpr int kMB32 = 3;                // blocks on the 32x32 matrix cores (taps 0..7)
 constexpr int kRow8 = 32 * kMB32;       // first LDS row of the tap-8 tile (16 rows)
 constexpr int kNB = 4;                  // 32-column blocks per wave

@@ -541,6 +541,238 @@ __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
     }
 }
 
+// The 27-tap convolution when the output alone cannot fill the chip but K is long (few positions,
+// many input channels): a workgroup computes one 64-row x 128-position tile, and its four waves
+// split K four ways instead of the workgroups.  Wave q walks its own quarter of the 32-channel
+// chunks with its own pair of window buffers in LDS and its own weight stream -- nothing is shared
+// in the K loop, so it has no barrier: a wave waits only for its own copies -- and afterwards the
+// four partial tiles are summed once through LDS, in the same order (wave 0, 1, 2, 3) for every
+// output, and wave q stores 32-position block q of the tile.  No fp32 partials leave the CU and
+// no second kernel runs.  Operand layout, window layout and weight packing are those of
+// igemm32_kernel (a 64-row tile is two of its 32-row fragments).
+template <bool BF, int EPI, int LW>
+__global__ __launch_bounds__(256, 1) void igemm32_kq_kernel(IgemmKArgs a) {
+    using E = Elem<BF>;
+    using G = W32Geom<LW, 4, 1>;
+    typedef typename E::vec8 vec8;
+    typedef __attribute__((address_space(3))) void lds_void;
+    // window buffer pair of each wave (even / odd stages); afterwards the partial tiles
+    __shared__ __attribute__((aligned(16))) uint4 Win0[4][G::Slots];
+    __shared__ __attribute__((aligned(16))) uint4 Win1[4][G::Slots];
+    static_assert(4 * G::Slots >= 2 * 6 * 256, "two waves' partial blocks fit one buffer set");
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int j = lane & 31, hh = lane >> 5;
+    const int pr = j / LW, pc = j % LW;
+
+    int od;
+    uint32_t lin = w32_block_order(blockIdx.x, a.total_wg, a.D, od);
+    const int mt = lin % a.mtiles;
+    lin /= a.mtiles;
+    const int tw = lin % a.tiles_w;
+    lin /= a.tiles_w;
+    const int th = lin % a.tiles_h;
+    lin /= a.tiles_h;
+    const int n = lin % a.N;
+
+    const int oh0 = th * G::TH, ow0 = tw * G::TW;
+    // this wave's quarter of the chunks (every wave has at least one: nchunks >= 4)
+    const int c_begin = (a.nchunks * wave) >> 2;
+    const int c_end = (a.nchunks * (wave + 1)) >> 2;
+    const int fi0 = od + a.d_org - 1;
+    const int kd_lo = max(0, a.d_lo - fi0);
+    const int kd_hi = min(2, a.d_hi - 1 - fi0);
+    const int nkd = max(0, kd_hi - kd_lo + 1);
+    const int nst = max(0, (c_end - c_begin) * nkd);
+    const int mbase = mt * 64;                    // the tile's first GEMM row
+
+    const size_t frame_elems = (size_t)a.H_in * a.W_in * a.C_in;
+    const uint32_t frame_bytes = (uint32_t)(frame_elems * 2);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)a.wp, (short)0, (int)(a.wp_bytes), 0x00020000);
+
+    auto stage_coords = [&](int s, int &cc, int &kd) {
+        cc = c_begin + s / nkd;
+        kd = kd_lo + s % nkd;
+    };
+    // The whole window of stage s, copied by this wave alone: lane i of copy k fills slot
+    // 64k + i = position 16k + i/4, piece (i%4) ^ ((column/4) % 4), as in igemm32_kernel.
+    auto copy_window = [&](int s, uint4 *dst) {
+        int cc, kd;
+        stage_coords(s, cc, kd);
+        const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(a.x + ((size_t)n * a.D_in + (fi0 + kd)) * frame_elems), (short)0,
+            (int)frame_bytes, 0x00020000);
+#pragma unroll
+        for (int k = 0; k < G::Copies; ++k) {
+            const int pos = 16 * k + (lane >> 2);
+            const int wh = pos / G::RowPos, ww = pos - wh * G::RowPos;
+            const int piece = (lane & 3) ^ ((ww >> 2) & 3);
+            const int h = oh0 - 1 + wh + a.h_org, w = ow0 - 1 + ww;
+            const bool ok = ww < G::WW && pos < G::Pos && h >= a.h_lo && h < a.h_hi &&
+                            (unsigned)w < (unsigned)a.W_in && cc * 32 + 8 * piece < a.C_in;
+            const uint32_t off = ok ? (uint32_t)(((h * a.W_in + w) * a.C_in + cc * 32 + 8 * piece) * 2) : 0xFFFFFFFFu;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)&dst[k * 64], 16, off, 0, 0, 0);
+        }
+    };
+    const uint32_t alane = (uint32_t)((mbase + j) * 32 + 16 * hh);
+    auto stage_abase = [&](int s) {
+        int cc, kd;
+        stage_coords(s, cc, kd);
+        return (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(cc * 27 + kd * 9) * 2u * a.Mpad * 32u));
+    };
+    const uint32_t slice_bytes = (uint32_t)a.Mpad * 32u;
+    auto load_a = [&](uint32_t sb, int q, vec8 (&dst)[2]) {
+        const uint32_t sbase = sb + (uint32_t)q * slice_bytes;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+            dst[mb] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(
+                wr, alane + mb * 1024u, sbase, 0));
+    };
+    int lslot[3][2];
+#pragma unroll
+    for (int kx = 0; kx < 3; ++kx)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) lslot[kx][k2] = w32_slot<G::RowPos>(pr, pc + kx, 2 * k2 + hh);
+    auto read_b = [&](const uint4 *win, int q, int nb) {
+        const int tap = q / 2, ky = tap / 3, kx = tap % 3;
+        return __builtin_bit_cast(vec8, win[lslot[kx][q % 2] + (G::R * nb + ky) * (G::RowPos * 4)]);
+    };
+
+    f32x16_t acc[2][4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            acc[mb][nb] = f32x16_t{};
+            w32_touch(acc[mb][nb]);
+        }
+    vec8 aq[kW32PD][2];
+    vec8 bq[2][4];
+
+    if (nst > 0) {
+        copy_window(0, Win0[wave]);
+        if (nst > 1) copy_window(1, Win1[wave]);
+        uint32_t sb_cur = stage_abase(0);
+#pragma unroll
+        for (int q = 0; q < kW32PD; ++q) load_a(sb_cur, q, aq[q]);
+        // window 0 complete (younger: window 1 and the weight loads)
+        if (nst > 1) __builtin_amdgcn_s_waitcnt(w32_waitcnt_vm(G::Copies + 2 * kW32PD));
+        else __builtin_amdgcn_s_waitcnt(w32_waitcnt_vm(2 * kW32PD));
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) bq[0][nb] = read_b(Win0[wave], 0, nb);
+
+        // Stage s reads buffer s % 2.  From stage 1 on, a stage starts by copying window s+1
+        // into the buffer stage s-1 read (its reads are complete); its last slice waits for
+        // that window -- younger than its copies are only this stage's 17 weight refills so
+        // far -- and reads the first fragments of stage s+1 from it.
+#pragma unroll 1
+        for (int s0 = 0; s0 < nst; s0 += 2) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int s = s0 + half;
+                if (half > 0 && s >= nst) break;              // uniform
+                uint4 *const cur = half == 0 ? Win0[wave] : Win1[wave];
+                uint4 *const nxt = half == 0 ? Win1[wave] : Win0[wave];
+                const bool more = s + 1 < nst;
+                if (s > 0 && more) {
+                    __builtin_amdgcn_s_waitcnt(kW32WaitLgkm0);
+                    copy_window(s + 1, nxt);
+                }
+                const uint32_t sb_next = more ? stage_abase(s + 1) : sb_cur;
+#pragma unroll
+                for (int q = 0; q < kW32Slices; ++q) {
+                    const int cb = q & 1;
+                    if (q + 1 < kW32Slices) {
+#pragma unroll
+                        for (int nb = 0; nb < 4; ++nb) bq[cb ^ 1][nb] = read_b(cur, q + 1, nb);
+                    } else {
+                        // (after the last stage these reads are of a stale buffer and never used)
+                        if (more) __builtin_amdgcn_s_waitcnt(w32_waitcnt_vm(2 * (kW32Slices - 1)));
+#pragma unroll
+                        for (int nb = 0; nb < 4; ++nb) bq[cb ^ 1][nb] = read_b(nxt, 0, nb);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                        for (int nb = 0; nb < 4; ++nb)
+                            acc[mb][nb] = E::mfma32x32x16(aq[q % kW32PD][mb], bq[cb][nb], acc[mb][nb]);
+                    if (q + kW32PD < kW32Slices) load_a(sb_cur, q + kW32PD, aq[q % kW32PD]);
+                    else load_a(sb_next, q + kW32PD - kW32Slices, aq[q % kW32PD]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                sb_cur = sb_next;
+            }
+        }
+    }
+    // every copy of this wave has landed and every wave is done with its windows
+    __builtin_amdgcn_s_waitcnt(w32_waitcnt_vm(0));
+    __builtin_amdgcn_s_waitcnt(kW32WaitLgkm0);
+    w32_barrier();
+
+    // Partial blocks: wave w leaves its blocks nb != w for their owner wave nb; block (w, nb, mb)
+    // is 256 float4 (element group g of lane l at 64g + l), waves 0, 1 in the first buffer set
+    // and 2, 3 in the second.
+    auto pblock = [&](int w, int nb, int mb) {
+        f32x4_t *base = reinterpret_cast<f32x4_t *>((w < 2) ? &Win0[0][0] : &Win1[0][0]);
+        const int kk = nb - (nb > w ? 1 : 0);
+        return base + (((w & 1) * 3 + kk) * 2 + mb) * 256;
+    };
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+        if (nb == wave) continue;   // uniform
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            w32_touch(acc[mb][nb]);
+            f32x4_t *dst = pblock(wave, nb, mb);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x16_t v = acc[mb][nb];
+                dst[64 * g + lane] = f32x4_t{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(kW32WaitLgkm0);
+    w32_barrier();
+
+    // Wave `wave` owns block nb = wave: sum over the four waves in order, bias, epilogue, store.
+    const size_t P = (size_t)a.N * a.D * a.H * a.W;
+    const int oh = oh0 + G::R * wave + pr, ow = ow0 + pc;
+    const bool inside = oh < a.H && ow < a.W;
+    const size_t pos = (((size_t)n * a.D + od) * a.H + oh) * a.W + ow;
+#pragma unroll
+    for (int nbq = 0; nbq < 4; ++nbq) {
+        if (nbq != wave) continue;   // uniform: the block index stays compile-time
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            w32_touch(acc[mb][nbq]);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x16_t own = acc[mb][nbq];
+                f32x4_t sum = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const f32x4_t v = w == nbq ? f32x4_t{own[4 * g], own[4 * g + 1], own[4 * g + 2], own[4 * g + 3]}
+                                               : pblock(w, nbq, mb)[64 * g + lane];
+                    sum = w == 0 ? v : sum + v;
+                }
+                const int m0 = mbase + mb * 32 + 8 * g + 4 * hh;
+                if (inside && m0 < a.Mrows) {
+                    float bv[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        bv[i] = (a.bias != nullptr && m0 + i < a.Mrows) ? E::to_f32(a.bias[m0 + i]) : 0.f;
+                    store_rows<BF, EPI, false>(a, f32x4_t{sum[0] + bv[0], sum[1] + bv[1],
+                                                          sum[2] + bv[2], sum[3] + bv[3]},
+                                               pos, 0, P, m0);
+                }
+            }
+        }
+    }
+}
+
 // Sums the split-K partials, adds the bias, applies the epilogue and rounds once.  One thread
 // per (position, 4 channels).
 template <bool BF, int EPI>
@@ -657,12 +889,27 @@ hipError_t launch_w32(const IgemmKArgs &ka, int epi, bool splitk, dim3 grid, hip
     return hipGetLastError();
 }
 
+template <bool BF, int LW>
+hipError_t launch_kq(const IgemmKArgs &ka, int epi, dim3 grid, hipStream_t s) {
+    const dim3 block(256);
+    if (epi == EPI_RELU) igemm32_kq_kernel<BF, EPI_RELU, LW><<<grid, block, 0, s>>>(ka);
+    else if (epi == EPI_CLAMP1) igemm32_kq_kernel<BF, EPI_CLAMP1, LW><<<grid, block, 0, s>>>(ka);
+    else igemm32_kq_kernel<BF, EPI_NONE, LW><<<grid, block, 0, s>>>(ka);
+    return hipGetLastError();
+}
+
 template <bool BF>
 hipError_t launch_igemm_dtype(const IgemmPlan &pl, const IgemmKArgs &ka, int epi, bool splitk,
                               hipStream_t s) {
     switch (pl.family) {
         case IG_W32: {
             const dim3 grid((unsigned)pl.workgroups);
+            if (pl.kq) {   // stride 1, 128-position tiles, no split-K
+                if (splitk || pl.stride != 1) return hipErrorInvalidValue;
+                if (pl.TW == 16 && pl.TH == 8) return launch_kq<BF, 16>(ka, epi, grid, s);
+                if (pl.TW == 32 && pl.TH == 4) return launch_kq<BF, 32>(ka, epi, grid, s);
+                return hipErrorInvalidValue;
+            }
             if (pl.stride == 2) {   // 128-position tiles only (the stride-2 window is twice as big)
                 if (pl.TW == 32 && pl.TH == 4) return launch_w32<BF, 32, 4, 2>(ka, epi, splitk, grid, s);
                 if (pl.TW == 16 && pl.TH == 8) return launch_w32<BF, 16, 4, 2>(ka, epi, splitk, grid, s);
@@ -749,11 +996,26 @@ IgemmPlan plan_igemm(int family, int N, int C_in, int C_out, int D, int H, int W
                 const long long rounds = (gbase * se + 255) / 256;
                 const double cost = rounds * (cps * taps * g.cost + 1.0) + (se > 1 ? se * part : 0.0);
                 if (best < 0 || cost < best - 1e-9) {
-                    best = cost, splits = se;
+                    best = cost, splits = se, pl.kq = 0;
                     pl.TH = g.TH, pl.TW = g.TW, pl.tiles_h = (int)th, pl.tiles_w = (int)tw;
                 }
             }
+            // The same tile with 64 output rows per workgroup and K split over its four waves
+            // (igemm32_kq_kernel): four times the workgroups of a 256-row tile, no partials;
+            // about a fifth of a stage to sum the four partial tiles through LDS.  Stride 1,
+            // and at least two chunks per wave.
+            if (stride == 1 && g.NB == 4 && pl.nchunks >= 8) {
+                const long long gq = (long long)N * D * th * tw * ((pl.Mrows + 63) / 64);
+                const long long rounds = (gq + 255) / 256;
+                const double cost = rounds * (((pl.nchunks + 3) / 4) * taps * g.cost + 1.2);
+                if (cost < best - 1e-9) {
+                    best = cost, splits = 1;
+                    pl.TH = g.TH, pl.TW = g.TW, pl.tiles_h = (int)th, pl.tiles_w = (int)tw;
+                    pl.kq = 1;
+                }
+            }
         }
+        if (pl.kq) pl.mtiles = (pl.Mrows + 63) / 64;
     } else if (family != IG_TEMPORAL && family != IG_FUSED && base > 0 && base < 1024) {
         // (the 16x16 kernels run two workgroups per CU)
         splits = (int)((1024 + base - 1) / base);

@@ -62,6 +62,7 @@ struct IgemmPlan {
     int tiles_h, tiles_w, mtiles;
     long long workgroups;
     int stride;        // spatial stride (2: the 32x32 family's 128-position tiles only)
+    int kq;            // 32x32 family: 1 = 64-row tiles whose four waves split K (no partials)
 };
 
 // Plans the MFMA launch (tile family, split-K) for a request over the output extent (D, H, W).
