@@ -113,15 +113,18 @@ __global__ __launch_bounds__(256, 2) void igemm3d_kernel(IgemmKArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % WM, wn = wave / WM;
 
+    // Each XCD takes a contiguous run of workgroups (xcd_remap), frame innermost: the frames of
+    // one tile run together on one XCD, so each input frame window, read by three output frames,
+    // comes from HBM about once and from that XCD's L2 after.
     uint32_t lin = xcd_remap(blockIdx.x, a.total_wg);
     const int mt = lin % a.mtiles;
     lin /= a.mtiles;
+    const int od = lin % a.D;
+    lin /= a.D;
     const int tw = lin % a.tiles_w;
     lin /= a.tiles_w;
     const int th = lin % a.tiles_h;
     lin /= a.tiles_h;
-    const int od = lin % a.D;
-    lin /= a.D;
     const int n = lin % a.N;
     const int split = lin / a.N;
 
