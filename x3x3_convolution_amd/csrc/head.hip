@@ -64,12 +64,16 @@ namespace {
 // read while those MFMAs run.  The copy offsets are formed without branches.
 //
 // PLANE mode stores Z, rounded to the storage type, as the 112-channel plane of the split head.
-// FUSED mode applies the nine-tap stencil in registers: the horizontal taps combine neighbouring
-// positions, the vertical taps are carried from row to row (two fp32 partial sums per output,
-// in registers), and bias + epilogue are applied once per output.  Output row h needs Z rows
-// h-1 .. h+1 and columns w-1 .. w+1, so a strip computes 128 columns for 126 outputs and a band
-// two extra rows.  Nothing of Z is rounded or stored: the fused head keeps fp32 from the GEMM to
-// the epilogue.
+// FUSED mode applies the nine-tap stencil in registers.  The vertical taps are summed by the
+// matrix cores themselves: the weights come in three row versions, and Z row zr takes version
+// zr mod 3, in which the accumulator slot of (kx, channel) in one of three rotating accumulator
+// sets holds the vertical tap that output row zr - 1, zr or zr + 1 needs -- so the three Z rows
+// an output row reads all add into the same registers.  When an output row is complete its set
+// is read out: the horizontal taps combine neighbouring positions, bias + epilogue are applied
+// once per output, and the set is cleared for the row three further on.  Output row h needs Z
+// rows h-1 .. h+1 and columns w-1 .. w+1, so a strip computes 128 columns for 126 outputs and a
+// band two extra rows.  Nothing of Z is rounded or stored: the fused head keeps fp32 from the
+// GEMM to the epilogue.
 // ---------------------------------------------------------------------------------------------
 constexpr int kMB32 = 3;                // blocks on the 32x32 matrix cores (taps 0..7)
 constexpr int kRow8 = 32 * kMB32;       // first LDS row of the tap-8 tile (16 rows)
@@ -308,8 +312,7 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
     const f32x16_t zero = {};
     const f32x4_t zero4 = {};
 
-    // FUSED: the bias of the lane's six output channels; the carried partial sums of every
-    // output (cA: the output row before the next Z row, cB: the output row of the next Z row)
+    // FUSED: the bias of the lane's six output channels
     float b6[kHalfCo];
 #pragma unroll
     for (int c = 0; c < kHalfCo; ++c) {
