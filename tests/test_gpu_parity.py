@@ -112,6 +112,12 @@ CASES_3D_INT = [
     # more frame groups than one (the per-group input and output windows), a partial last group
     (1, 16, 12, 22, 6, 40, "bf16", "clamp1", C.ALGO_FUSED_HEAD),
     (1, 16, 12, 22, 6, 40, "bf16", "clamp1", C.ALGO_SPLIT_HEAD),
+    # row ranges that run from the end of one strip into the next (several strips, a frame-group
+    # count that leaves ranges of a few rows), one and two samples
+    (1, 32, 12, 40, 37, 300, "bf16", "clamp1", C.ALGO_FUSED_HEAD),
+    (1, 32, 12, 40, 37, 300, "bf16", "clamp1", C.ALGO_SPLIT_HEAD),
+    (2, 16, 12, 32, 17, 380, "f16", "relu", C.ALGO_FUSED_HEAD),
+    (2, 16, 12, 32, 17, 380, "f16", "relu", C.ALGO_SPLIT_HEAD),
 ]
 
 

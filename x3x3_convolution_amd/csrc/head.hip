@@ -26,8 +26,10 @@ namespace {
 // (of which it would use 12 rows): lane l supplies row / column l%16 with k values 8*(l/16) ..
 // +7 of a 32-wide k range and receives element i at row 4*(l/16) + i, column l%16.
 //
-// Work split: a workgroup is four waves on four consecutive output frames of one (band, strip);
-// each wave walks its band one row at a time.  Per row a wave computes GEMM rows x 128 columns of
+// Work split: a workgroup is four waves on four consecutive output frames and one row range of
+// the strips (a band of rows of one strip, or the end of one strip and the start of the next --
+// the ranges are cut to near-equal cost so that every CU takes one); each wave walks its band one
+// row at a time.  Per row a wave computes GEMM rows x 128 columns of
 // the row: 3 x 4 blocks of 32 x 32 (192 accumulators) and 8 tiles of 16 x 16 (32).  Column block nb,
 // lane column j holds position p = 4*j + nb of the wave's strip, so the horizontal neighbours of
 // a position sit in the same lane (blocks nb-1, nb+1) except at nb = 0 / 3, where they are one
@@ -87,6 +89,7 @@ constexpr int kCopyB = kBPieces / 256;               // 12
 constexpr int kHalfCo = 6;              // output channels per lane half
 constexpr int kPlaneCh = kHeadPlaneChannels;
 constexpr uint32_t kOff = 0xFFFFFFFFu;  // an offset past any buffer range; saturating adds keep it
+constexpr int kMaxRanges = 256;         // row ranges per (sample, frame group)
 
 // s_waitcnt immediates: vmcnt is split over bits 3:0 and 15:14; expcnt / lgkmcnt left open.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -102,10 +105,14 @@ struct HeadGemmKArgs {
     int D_in, H_in, d_org, h_org;  // input region (see ConvRegion)
     int d_lo, d_hi, h_lo, h_hi;
     int nchunks;       // 32-channel stages per Z row, even (the padding reads zeros)
-    int rows_per_band, bands, strips, strip_out, fgroups;
+    int strips, strip_out, fgroups;
+    int ranges;        // row ranges per (sample, frame group)
     uint32_t window_bytes;  // bytes of the six input frames of a workgroup (buffer-resource range)
     uint32_t wp_bytes;
     uint32_t total_wg;
+    // Row range g covers positions [bound[g], bound[g+1]) of the strip-major (strip, output row)
+    // order of one frame group: output row h of strip s is position s*H + h.
+    int bound[kMaxRanges + 1];
 };
 
 // 0.f through an asm the compiler cannot look into
@@ -193,24 +200,15 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
     const int j = lane & 31, hh = lane >> 5;
 
     uint32_t lin = xcd_remap(blockIdx.x, a.total_wg);
-    const int fg = lin % a.fgroups;    // frame groups of one (strip, band) are consecutive: they
+    const int fg = lin % a.fgroups;    // frame groups of one row range are consecutive: they
     lin /= a.fgroups;                  // share input frames, so they run on one XCD's L2
-    const int strip = lin % a.strips;
-    lin /= a.strips;
-    const int band = lin % a.bands;
-    const int n = lin / a.bands;
+    const int range = lin % a.ranges;
+    const int n = lin / a.ranges;
     const int f0 = fg * 4;             // the group's first output frame
     const int od = f0 + wave;          // this wave's output frame (>= D: computes, stores nothing)
 
     const int HW = a.H * a.W;
-    const int w0 = FUSED ? strip * a.strip_out - 1 : strip * kWavePos;   // column of position 0
-    const int h_begin = band * a.rows_per_band;
-    const int h_end = min(a.H, h_begin + a.rows_per_band);
-    const int zrow0 = FUSED ? h_begin - 1 : h_begin;
-    const int nsteps = (h_end - h_begin) + (FUSED ? 2 : 0);   // Z rows, the same in every wave
     const int nch = a.nchunks;
-    const int nstages = nsteps * nch;
-
     // x through the six input frames the group's window covers: window frame i is input frame
     // fw0 + i.  fw0 may lie before the first frame (or the window past the last one); those frames
     // are never addressed (their copies take an offset past the range), so only the address
@@ -231,53 +229,9 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
             : (void *)(a.out + frame0 * HW * a.C_out),
         (short)0, RGB ? (int)(4 * HW * 12) : (int)(4 * HW * a.C_out * 2), 0x00020000);
 
-    // B window copies: this wave issues copies k = wave + 4*t; lane i of copy k fills slot
-    // 64*k + i = ((frame*4 + nb)*32 + column j)*4 + piece', with frame = k/8, nb = (k/2) % 4,
-    // j = 16*(k%2) + i/4 and piece' = piece ^ ((j/4) % 4) -- the piece of lane i is therefore
-    // (i%4) ^ ((i/16) % 4) in every copy.  With k = wave + 4*t, copy t fills window frame t/2
-    // from column w0 + 4*(i/4) + dw, dw = 64*(wave%2) + wave/2 + 2*(t%2): the wave's twelve
-    // copies are six frames at two column offsets, and a lane's part of the source offset is one
-    // of two values fixed for the whole kernel (kOff where the column is outside the tensor).
     const int bpiece = (lane & 3) ^ ((lane >> 4) & 3);
-    uint32_t bcol[2];
-#pragma unroll
-    for (int par = 0; par < 2; ++par) {
-        const int col = w0 + 4 * (lane >> 2) + 64 * (wave & 1) + (wave >> 1) + 2 * par;
-        bcol[par] = (unsigned)col < (unsigned)a.W ? (uint32_t)((col * a.C_in + 8 * bpiece) * 2) : kOff;
-    }
     const uint32_t frame_bytes = (uint32_t)a.H_in * (uint32_t)a.W * (uint32_t)a.C_in * 2u;
     const uint32_t row_bytes = (uint32_t)a.W * (uint32_t)a.C_in * 2u;
-    // Copies of stage (Z row st, channel chunk c) into one buffer pair.  Weight chunks past the
-    // packed ones (the even padding) lie past the resource range and copy zeros.  Every offset
-    // is formed without branches: an invalid part is all ones, which the saturating add keeps.
-    auto copy_stage = [&](int st, int c, uint4 *abuf, uint4 *bbuf) __attribute__((always_inline)) {
-        // FUSED: the weight version of the stage's Z row (head_fused_role).  Chunks past the
-        // packed ones (the even padding) lie past the resource range and copy zeros.
-        const int cbase = FUSED ? (c * 3 + mod3(st)) * kHeadChunkPieces : c * kHeadChunkPieces;
-#pragma unroll
-        for (int q = 0; q < kCopyA; ++q) {
-            const int piece = (wave * kCopyA + q) * 64;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                wr, (lds_void *)&abuf[piece], 16, (uint32_t)((cbase + piece + lane) * 16), 0, 0, 0);
-        }
-        // Z row zr reads input row zr + h_org; window frame i is input frame fw0 + i.  The
-        // frame / row / chunk part of an offset is uniform (scalar registers); the column part
-        // is the lane's; one saturating add joins them.
-        const int row = __builtin_amdgcn_readfirstlane(zrow0 + st + a.h_org);
-        const bool rok = row >= a.h_lo && row < a.h_hi;
-        const uint32_t rbase = (uint32_t)row * row_bytes + (uint32_t)(64 * c);
-        const uint32_t cmask = 0u - (uint32_t)(32 * c + 8 * bpiece >= a.C_in);   // ~0: no channels
-        const uint32_t colv[2] = {bcol[0] | cmask, bcol[1] | cmask};
-#pragma unroll
-        for (int t = 0; t < kCopyB; ++t) {
-            const int k = wave + 4 * t;
-            const int f = fw0 + (t >> 1);
-            const bool fok = rok && f >= a.d_lo && f < a.d_hi;
-            const uint32_t up = fok ? (uint32_t)(t >> 1) * frame_bytes + rbase : kOff;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)&bbuf[k * 64], 16,
-                                                     add_sat(colv[t & 1], up), 0, 0, 0);
-        }
-    };
     // Fragment reads of step u (temporal tap u/2, k16 slice u%2): the per-lane part of the slot
     // (row / column j, piece 2*slice + hh, permuted) plus a compile-time offset; B adds this
     // wave's first window frame.
@@ -319,295 +273,358 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
         const int co = kHalfCo * hh + c;
         b6[c] = (FUSED && a.bias != nullptr && co < a.C_out) ? E::to_f32(a.bias[co]) : 0.f;
     }
-    if constexpr (FUSED) {
-        // the three sets start empty; each is cleared again as its output row is read out
-#pragma unroll
-        for (int nb = 0; nb < kNB; ++nb) {
-#pragma unroll
-            for (int mb = 0; mb < kMB32; ++mb) {
-                acc[mb][nb] = zero;
-                touch(acc[mb][nb]);
-            }
-            t8[nb][0] = t8[nb][1] = zero4;
-            touch(t8[nb][0]), touch(t8[nb][1]);
-        }
-    }
 
-    // ---- prologue: stages 0 and 1 copied, stage 0 complete and published ----
-    copy_stage(0, 0, As0, Bs0);
-    if (nstages > 1) {
-        copy_stage(0, 1, As1, Bs1);   // (nch is even, so stage 1 is chunk 1 of Z row 0)
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kCopyA + kCopyB));
-    } else {
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    }
-    wg_barrier();
-    read_frags(As0, Bs0, 0, af[0], bf[0], a8);
-
-    // Stage g = st*nch + c uses buffer pair g % 2; each pass of the chunk loop runs an even and
-    // the following odd stage.
-    // One Z row (band-local index st): every channel chunk, two stages per pass.
-    auto row_body = [&](auto K, int st) __attribute__((always_inline)) {
-        (void)K;
+    // The workgroup's row range, one segment per strip it touches (one or two): each segment is
+    // a band of output rows [h_begin, h_end) of one strip, run as its own pipeline.
+    const int r_end = a.bound[range + 1];
 #pragma unroll 1
-        for (int c2 = 0; c2 < nch; c2 += 2) {
+    for (int rpos = a.bound[range]; rpos < r_end;) {
+        const int strip = rpos / a.H;
+        const int h_begin = rpos - strip * a.H;
+        const int h_end = min(a.H, h_begin + (r_end - rpos));
+        rpos += h_end - h_begin;
+        const int w0 = FUSED ? strip * a.strip_out - 1 : strip * kWavePos;   // column of position 0
+        const int zrow0 = FUSED ? h_begin - 1 : h_begin;
+        const int nsteps = (h_end - h_begin) + (FUSED ? 2 : 0);   // Z rows, the same in every wave
+        const int nstages = nsteps * nch;
+
+        // B window copies: this wave issues copies k = wave + 4*t; lane i of copy k fills slot
+        // 64*k + i = ((frame*4 + nb)*32 + column j)*4 + piece', with frame = k/8, nb = (k/2) % 4,
+        // j = 16*(k%2) + i/4 and piece' = piece ^ ((j/4) % 4) -- the piece of lane i is therefore
+        // (i%4) ^ ((i/16) % 4) in every copy.  With k = wave + 4*t, copy t fills window frame t/2
+        // from column w0 + 4*(i/4) + dw, dw = 64*(wave%2) + wave/2 + 2*(t%2): the wave's twelve
+        // copies are six frames at two column offsets, and a lane's part of the source offset is one
+        // of two values fixed for the whole kernel (kOff where the column is outside the tensor).
+        uint32_t bcol[2];
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                // the stage two ahead: chunk c2 + half + 2 of this Z row, or of the next one
-                const int wrap = c2 + half + 2 >= nch;
-                const int st2 = st + wrap, c_2 = c2 + half + 2 - (wrap ? nch : 0);
-                uint4 *const ca = half == 0 ? As0 : As1;
-                uint4 *const cbb = half == 0 ? Bs0 : Bs1;
-                uint4 *const na = half == 0 ? As1 : As0;
-                uint4 *const nbb = half == 0 ? Bs1 : Bs0;
+        for (int par = 0; par < 2; ++par) {
+            const int col = w0 + 4 * (lane >> 2) + 64 * (wave & 1) + (wave >> 1) + 2 * par;
+            bcol[par] = (unsigned)col < (unsigned)a.W ? (uint32_t)((col * a.C_in + 8 * bpiece) * 2) : kOff;
+        }
+        // Copies of stage (Z row st, channel chunk c) into one buffer pair.  Weight chunks past the
+        // packed ones (the even padding) lie past the resource range and copy zeros.  Every offset
+        // is formed without branches: an invalid part is all ones, which the saturating add keeps.
+        auto copy_stage = [&](int st, int c, uint4 *abuf, uint4 *bbuf) __attribute__((always_inline)) {
+            // FUSED: the weight version of the stage's Z row (head_fused_role).  Chunks past the
+            // packed ones (the even padding) lie past the resource range and copy zeros.
+            const int cbase = FUSED ? (c * 3 + mod3(st)) * kHeadChunkPieces : c * kHeadChunkPieces;
 #pragma unroll
-                for (int u = 0; u < kSteps; ++u) {
-                    const int cur = u & 1, bs = u % 3;
-                    if (u + 1 < kSteps) {
-                        read_frags(ca, cbb, u + 1, af[cur ^ 1], bf[(u + 1) % 3], a8);
-                    } else {
-                        // Publish the next stage (its copies were issued one stage ago) and
-                        // release this one: this wave's last fragments of it are in registers
-                        // once its reads are complete.  (Past the last stage the reads below are
-                        // of a stale buffer and never used; they keep every path's waits the
-                        // same.)
-                        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-                        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-                        wg_barrier();
-                        read_frags(na, nbb, 0, af[cur ^ 1], bf[0], a8);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                    if (!FUSED && half == 0 && u == 0 && c2 == 0) {
-                        // PLANE, first step of a Z row: every accumulator starts from zero
+            for (int q = 0; q < kCopyA; ++q) {
+                const int piece = (wave * kCopyA + q) * 64;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    wr, (lds_void *)&abuf[piece], 16, (uint32_t)((cbase + piece + lane) * 16), 0, 0, 0);
+            }
+            // Z row zr reads input row zr + h_org; window frame i is input frame fw0 + i.  The
+            // frame / row / chunk part of an offset is uniform (scalar registers); the column part
+            // is the lane's; one saturating add joins them.
+            const int row = __builtin_amdgcn_readfirstlane(zrow0 + st + a.h_org);
+            const bool rok = row >= a.h_lo && row < a.h_hi;
+            const uint32_t rbase = (uint32_t)row * row_bytes + (uint32_t)(64 * c);
+            const uint32_t cmask = 0u - (uint32_t)(32 * c + 8 * bpiece >= a.C_in);   // ~0: no channels
+            const uint32_t colv[2] = {bcol[0] | cmask, bcol[1] | cmask};
 #pragma unroll
-                        for (int mb = 0; mb < kMB32; ++mb)
+            for (int t = 0; t < kCopyB; ++t) {
+                const int k = wave + 4 * t;
+                const int f = fw0 + (t >> 1);
+                const bool fok = rok && f >= a.d_lo && f < a.d_hi;
+                const uint32_t up = fok ? (uint32_t)(t >> 1) * frame_bytes + rbase : kOff;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)&bbuf[k * 64], 16,
+                                                         add_sat(colv[t & 1], up), 0, 0, 0);
+            }
+        };
+        if constexpr (FUSED) {
+            // the three sets start empty; each is cleared again as its output row is read out
 #pragma unroll
-                            for (int nb = 0; nb < kNB; ++nb)
-                                acc[mb][nb] = E::mfma32x32x16(af[cur][mb], bf[bs][nb],
-                                                              FUSED ? acc[mb][nb] : zero);
-                    } else {
+            for (int nb = 0; nb < kNB; ++nb) {
 #pragma unroll
-                        for (int mb = 0; mb < kMB32; ++mb)
+                for (int mb = 0; mb < kMB32; ++mb) {
+                    acc[mb][nb] = zero;
+                    touch(acc[mb][nb]);
+                }
+                t8[nb][0] = t8[nb][1] = zero4;
+                touch(t8[nb][0]), touch(t8[nb][1]);
+            }
+        }
+
+        // ---- prologue: stages 0 and 1 copied, stage 0 complete and published ----
+        copy_stage(0, 0, As0, Bs0);
+        if (nstages > 1) {
+            copy_stage(0, 1, As1, Bs1);   // (nch is even, so stage 1 is chunk 1 of Z row 0)
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(kCopyA + kCopyB));
+        } else {
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        }
+        wg_barrier();
+        read_frags(As0, Bs0, 0, af[0], bf[0], a8);
+
+        // Stage g = st*nch + c uses buffer pair g % 2; each pass of the chunk loop runs an even and
+        // the following odd stage.
+        // One Z row (band-local index st): every channel chunk, two stages per pass.
+        auto row_body = [&](auto K, int st) __attribute__((always_inline)) {
+            (void)K;
+#pragma unroll 1
+            for (int c2 = 0; c2 < nch; c2 += 2) {
 #pragma unroll
-                            for (int nb = 0; nb < kNB; ++nb)
-                                acc[mb][nb] = E::mfma32x32x16(af[cur][mb], bf[bs][nb], acc[mb][nb]);
-                    }
-                    if (u & 1) {
-                        // tap 8 of temporal tap u/2: both k16 fragments are in registers
-                        const bool first8 = !FUSED && half == 0 && u == 1 && c2 == 0;   // PLANE
+                for (int half = 0; half < 2; ++half) {
+                    // the stage two ahead: chunk c2 + half + 2 of this Z row, or of the next one
+                    const int wrap = c2 + half + 2 >= nch;
+                    const int st2 = st + wrap, c_2 = c2 + half + 2 - (wrap ? nch : 0);
+                    uint4 *const ca = half == 0 ? As0 : As1;
+                    uint4 *const cbb = half == 0 ? Bs0 : Bs1;
+                    uint4 *const na = half == 0 ? As1 : As0;
+                    uint4 *const nbb = half == 0 ? Bs1 : Bs0;
 #pragma unroll
-                        for (int nb = 0; nb < kNB; ++nb) {
-                            vec8 lo, hi;
-                            tile_operands(bf[(u + 2) % 3][nb], bf[bs][nb], lo, hi);
-                            t8[nb][0] = E::mfma16x16x32(a8, lo, first8 ? zero4 : t8[nb][0]);
-                            t8[nb][1] = E::mfma16x16x32(a8, hi, first8 ? zero4 : t8[nb][1]);
+                    for (int u = 0; u < kSteps; ++u) {
+                        const int cur = u & 1, bs = u % 3;
+                        if (u + 1 < kSteps) {
+                            read_frags(ca, cbb, u + 1, af[cur ^ 1], bf[(u + 1) % 3], a8);
+                        } else {
+                            // Publish the next stage (its copies were issued one stage ago) and
+                            // release this one: this wave's last fragments of it are in registers
+                            // once its reads are complete.  (Past the last stage the reads below are
+                            // of a stale buffer and never used; they keep every path's waits the
+                            // same.)
+                            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+                            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+                            wg_barrier();
+                            read_frags(na, nbb, 0, af[cur ^ 1], bf[0], a8);
                         }
-                    }
-                    if (u + 1 == kSteps) {
-                        // The copies of the stage two ahead go into this stage's buffers, one
-                        // between each two of this step's MFMAs, so they issue while the matrix
-                        // pipe runs.  Past the last stage they still run (in bounds: rows and
-                        // chunks that do not exist copy zeros) and nothing reads them.
-                        copy_stage(st2, c_2, ca, cbb);
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (!FUSED && half == 0 && u == 0 && c2 == 0) {
+                            // PLANE, first step of a Z row: every accumulator starts from zero
 #pragma unroll
-                        for (int i = 0; i < kCopyA + kCopyB; ++i) {
-                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one buffer load
+                            for (int mb = 0; mb < kMB32; ++mb)
+#pragma unroll
+                                for (int nb = 0; nb < kNB; ++nb)
+                                    acc[mb][nb] = E::mfma32x32x16(af[cur][mb], bf[bs][nb],
+                                                                  FUSED ? acc[mb][nb] : zero);
+                        } else {
+#pragma unroll
+                            for (int mb = 0; mb < kMB32; ++mb)
+#pragma unroll
+                                for (int nb = 0; nb < kNB; ++nb)
+                                    acc[mb][nb] = E::mfma32x32x16(af[cur][mb], bf[bs][nb], acc[mb][nb]);
                         }
+                        if (u & 1) {
+                            // tap 8 of temporal tap u/2: both k16 fragments are in registers
+                            const bool first8 = !FUSED && half == 0 && u == 1 && c2 == 0;   // PLANE
+#pragma unroll
+                            for (int nb = 0; nb < kNB; ++nb) {
+                                vec8 lo, hi;
+                                tile_operands(bf[(u + 2) % 3][nb], bf[bs][nb], lo, hi);
+                                t8[nb][0] = E::mfma16x16x32(a8, lo, first8 ? zero4 : t8[nb][0]);
+                                t8[nb][1] = E::mfma16x16x32(a8, hi, first8 ? zero4 : t8[nb][1]);
+                            }
+                        }
+                        if (u + 1 == kSteps) {
+                            // The copies of the stage two ahead go into this stage's buffers, one
+                            // between each two of this step's MFMAs, so they issue while the matrix
+                            // pipe runs.  Past the last stage they still run (in bounds: rows and
+                            // chunks that do not exist copy zeros) and nothing reads them.
+                            copy_stage(st2, c_2, ca, cbb);
+#pragma unroll
+                            for (int i = 0; i < kCopyA + kCopyB; ++i) {
+                                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one buffer load
+                            }
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
                     }
-                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
-        }
 
-    };
+        };
 
-    // ---- row zr of Z is complete in this wave's accumulators ----
-    // PLANE: the epilogue walks the accumulator blocks in order and reads each value once, so
-    // only one or two blocks are unpacked into registers at a time.
-    auto plane_epilogue = [&](int st) __attribute__((always_inline)) {
-        const int zr = zrow0 + st;
-        const size_t frame = (size_t)n * a.D + od;
-        {
-            // tap 8, channel c < 6 of lane half h: t8[nb][c / 4][c % 4] after this swap
+        // ---- row zr of Z is complete in this wave's accumulators ----
+        // PLANE: the epilogue walks the accumulator blocks in order and reads each value once, so
+        // only one or two blocks are unpacked into registers at a time.
+        auto plane_epilogue = [&](int st) __attribute__((always_inline)) {
+            const int zr = zrow0 + st;
+            const size_t frame = (size_t)n * a.D + od;
+            {
+                // tap 8, channel c < 6 of lane half h: t8[nb][c / 4][c % 4] after this swap
 #pragma unroll
-            for (int nb = 0; nb < kNB; ++nb) swap_rows16(t8[nb][0], t8[nb][1]);
-            if (zr < h_end && od < a.D) {
+                for (int nb = 0; nb < kNB; ++nb) swap_rows16(t8[nb][0], t8[nb][1]);
+                if (zr < h_end && od < a.D) {
 #pragma unroll
-                for (int nb = 0; nb < kNB; ++nb) {
-                    const int w = w0 + 4 * j + nb;
-                    u16 *dst = a.out + (frame * HW + (size_t)zr * a.W + w) * kPlaneCh;
+                    for (int nb = 0; nb < kNB; ++nb) {
+                        const int w = w0 + 4 * j + nb;
+                        u16 *dst = a.out + (frame * HW + (size_t)zr * a.W + w) * kPlaneCh;
 #pragma unroll
-                    for (int mb = 0; mb < kMB32; ++mb) touch(acc[mb][nb]);
-                    touch(t8[nb][0]), touch(t8[nb][1]);
+                        for (int mb = 0; mb < kMB32; ++mb) touch(acc[mb][nb]);
+                        touch(t8[nb][0]), touch(t8[nb][1]);
 #pragma unroll
-                    for (int tap = 0; tap < 9; ++tap) {
-                        u16 r6[kHalfCo];
+                        for (int tap = 0; tap < 9; ++tap) {
+                            u16 r6[kHalfCo];
 #pragma unroll
-                        for (int c = 0; c < kHalfCo; ++c) {
-                            const int t = tap * kHalfCo + c;
-                            const float v = tap < 8 ? acc[tap < 8 ? t >> 4 : 0][nb][t & 15]
-                                                    : t8[nb][c >> 2][c & 3];
-                            r6[c] = E::from_f32(v);
-                        }
-                        if (w < a.W) {
-                            if constexpr (CO12) {
-                                uint3 v;
-                                v.x = (uint32_t)r6[0] | ((uint32_t)r6[1] << 16);
-                                v.y = (uint32_t)r6[2] | ((uint32_t)r6[3] << 16);
-                                v.z = (uint32_t)r6[4] | ((uint32_t)r6[5] << 16);
-                                *reinterpret_cast<uint3 *>(dst + tap * 12 + kHalfCo * hh) = v;
-                            } else {
+                            for (int c = 0; c < kHalfCo; ++c) {
+                                const int t = tap * kHalfCo + c;
+                                const float v = tap < 8 ? acc[tap < 8 ? t >> 4 : 0][nb][t & 15]
+                                                        : t8[nb][c >> 2][c & 3];
+                                r6[c] = E::from_f32(v);
+                            }
+                            if (w < a.W) {
+                                if constexpr (CO12) {
+                                    uint3 v;
+                                    v.x = (uint32_t)r6[0] | ((uint32_t)r6[1] << 16);
+                                    v.y = (uint32_t)r6[2] | ((uint32_t)r6[3] << 16);
+                                    v.z = (uint32_t)r6[4] | ((uint32_t)r6[5] << 16);
+                                    *reinterpret_cast<uint3 *>(dst + tap * 12 + kHalfCo * hh) = v;
+                                } else {
 #pragma unroll
-                                for (int c = 0; c < kHalfCo; ++c) {
-                                    const int co = kHalfCo * hh + c;
-                                    if (co < a.C_out) dst[tap * a.C_out + co] = r6[c];
+                                    for (int c = 0; c < kHalfCo; ++c) {
+                                        const int co = kHalfCo * hh + c;
+                                        if (co < a.C_out) dst[tap * a.C_out + co] = r6[c];
+                                    }
                                 }
                             }
                         }
-                    }
-                    if (CO12 && w < a.W && hh == 0) *reinterpret_cast<uint2 *>(dst + 108) = uint2{0u, 0u};
-                    if (!CO12 && w < a.W) {
-                        // channels past the 9*C_out tap channels are zero (the two lane halves
-                        // take alternate ones)
-                        for (int ch = 9 * a.C_out + hh; ch < kPlaneCh; ch += 2) dst[ch] = 0;
-                    }
-                }
-            }
-        }
-    };
-    // FUSED, at the end of Z row st (band-local), whose output row st - 1 has set SD: see below.
-    auto fused_epilogue = [&](auto SD, int st) __attribute__((always_inline)) {
-        constexpr int sd = decltype(SD)::value;
-        const int zr = zrow0 + st;
-        {
-            // Output row zr - 1 is complete in set sd (head_fused_role): each of its
-            // 18 slots per position block holds one horizontal tap kx of one output channel,
-            // summed over the three vertical taps.  Position p takes tap kx from position
-            // p + kx - 1, so a slot of block sb feeds the output of block sb + 1 - kx of the same
-            // lane, or across a lane (wavefront shift): block 3 with kx = 0 feeds block 0 of the
-            // next lane, block 0 with kx = 2 block 3 of the previous lane.  The lanes that cross a
-            // lane half or the wave hold halo columns, which are not stored.  The set is cleared
-            // as it is read, for the output row three further on.
-            const int ho = zr - 1;   // the output row this Z row completes
-            const bool emit = ho >= h_begin && ho < h_end && od < a.D;
-            float osum[kNB][kHalfCo];
-#pragma unroll
-            for (int nb = 0; nb < kNB; ++nb)
-#pragma unroll
-                for (int c = 0; c < kHalfCo; ++c) osum[nb][c] = b6[c];
-            // a zero the compiler cannot see through, for the tap-8 tiles' register of the set
-            const float z = opaque_zero();
-            {
-#pragma unroll
-                for (int sb = 0; sb < kNB; ++sb) {
-                    // register sd of the two tap-8 tiles: one lane swap gives this lane channels
-                    // 4 and 5 of its half (horizontal tap 2)
-                    float r[2] = {t8[sb][0][sd], t8[sb][1][sd]};
-                    lane_swap16(r[0], r[1]);
-#pragma unroll
-                    for (int q = 0; q < 18; ++q) {
-                        const int kx = q / kHalfCo, c = q % kHalfCo;
-                        int nb = sb + 1 - kx;
-                        float v = q < 16 ? acc[sd][sb][q < 16 ? q : 0] : r[q - 16 > 0 ? 1 : 0];
-                        if (nb >= kNB) {   // to the next lane (it takes lane l-1)
-                            nb = 0;
-                            v = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                0, __builtin_bit_cast(int, v), 0x138, 0xF, 0xF, false));
-                        } else if (nb < 0) {   // to the previous lane (it takes lane l+1)
-                            nb = kNB - 1;
-                            v = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                0, __builtin_bit_cast(int, v), 0x130, 0xF, 0xF, false));
+                        if (CO12 && w < a.W && hh == 0) *reinterpret_cast<uint2 *>(dst + 108) = uint2{0u, 0u};
+                        if (!CO12 && w < a.W) {
+                            // channels past the 9*C_out tap channels are zero (the two lane halves
+                            // take alternate ones)
+                            for (int ch = 9 * a.C_out + hh; ch < kPlaneCh; ch += 2) dst[ch] = 0;
                         }
-                        osum[nb][c] += v;
                     }
-                    // cleared for the output row three further on: the 32x32 block by a matrix
-                    // instruction of zeros (an ordinary accumulator result, so it stays in place),
-                    // the tiles' register directly
-                    vec8 za;   // zeros the compiler cannot see: one instruction per block
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        reinterpret_cast<float *>(&za)[e] = opaque_zero();
-                    acc[sd][sb] = E::mfma32x32x16(za, za, zero);
-                    t8[sb][0][sd] = z;
-                    t8[sb][1][sd] = z;
                 }
             }
+        };
+        // FUSED, at the end of Z row st (band-local), whose output row st - 1 has set SD: see below.
+        auto fused_epilogue = [&](auto SD, int st) __attribute__((always_inline)) {
+            constexpr int sd = decltype(SD)::value;
+            const int zr = zrow0 + st;
+            {
+                // Output row zr - 1 is complete in set sd (head_fused_role): each of its
+                // 18 slots per position block holds one horizontal tap kx of one output channel,
+                // summed over the three vertical taps.  Position p takes tap kx from position
+                // p + kx - 1, so a slot of block sb feeds the output of block sb + 1 - kx of the same
+                // lane, or across a lane (wavefront shift): block 3 with kx = 0 feeds block 0 of the
+                // next lane, block 0 with kx = 2 block 3 of the previous lane.  The lanes that cross a
+                // lane half or the wave hold halo columns, which are not stored.  The set is cleared
+                // as it is read, for the output row three further on.
+                const int ho = zr - 1;   // the output row this Z row completes
+                const bool emit = ho >= h_begin && ho < h_end && od < a.D;
+                float osum[kNB][kHalfCo];
 #pragma unroll
-            for (int nb = 0; nb < kNB; ++nb) {
-                const float *o = osum[nb];
-                const int p = 4 * j + nb;
-                const int w = w0 + p;
-                const bool st_ok = emit && p >= 1 && p <= a.strip_out && w < a.W;
-                u16 r6[kHalfCo];
+                for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
-                for (int c = 0; c < kHalfCo; ++c) r6[c] = E::from_f32(epilogue<EPI>(o[c]));
-                // 32-bit offsets into the group's four output frames, no branches: a store that
-                // must not happen goes to an offset past the buffer range, where it is dropped
-                const uint32_t yoff =
-                    (uint32_t)(((wave * a.H + ho) * a.W + w) * a.C_out + kHalfCo * hh) * 2u;
-                if constexpr (RGB) {
-                    uint32_t q[kHalfCo];
+                    for (int c = 0; c < kHalfCo; ++c) osum[nb][c] = b6[c];
+                // a zero the compiler cannot see through, for the tap-8 tiles' register of the set
+                const float z = opaque_zero();
+                {
 #pragma unroll
-                    for (int c = 0; c < kHalfCo; ++c) q[c] = rgb_code(E::to_f32(r6[c]));
-                    // half 0 lacks blue of row 2h (channels 8, 9), half 1 red of row 2h+1
-                    // (channels 2, 3): local channels 2 and 3 of the other half
-                    const uint32_t recv = (uint32_t)__builtin_amdgcn_ds_bpermute(
-                        (lane ^ 32) << 2, (int)(q[2] | (q[3] << 8)));
-                    const uint32_t r0 = recv & 0xFFu, r1 = (recv >> 8) & 0xFFu;
-                    // bytes R G B R G B of pixels (2h + hh, 2w) and (2h + hh, 2w + 1)
-                    const uint32_t p01 = hh == 0 ? (q[0] | (q[4] << 8)) : (r0 | (q[0] << 8));
-                    const uint32_t p23 = hh == 0 ? (r0 | (q[1] << 8)) : (q[4] | (r1 << 8));
-                    const uint32_t p45 = hh == 0 ? (q[5] | (r1 << 8)) : (q[1] | (q[5] << 8));
-                    const uint32_t roff =
-                        st_ok ? (uint32_t)(((wave * 2 * a.H + 2 * ho + hh) * 2 * a.W + 2 * w) * 3) : kOff;
-                    __builtin_amdgcn_raw_buffer_store_b16((u16)p01, yr, roff, 0, 0);
-                    __builtin_amdgcn_raw_buffer_store_b16((u16)p23, yr,
-                                                          __builtin_elementwise_add_sat(roff, 2u), 0, 0);
-                    __builtin_amdgcn_raw_buffer_store_b16((u16)p45, yr,
-                                                          __builtin_elementwise_add_sat(roff, 4u), 0, 0);
-                } else if constexpr (CO12) {
-                    typedef uint32_t v3u __attribute__((ext_vector_type(3)));
-                    const v3u v = {(uint32_t)r6[0] | ((uint32_t)r6[1] << 16),
-                                   (uint32_t)r6[2] | ((uint32_t)r6[3] << 16),
-                                   (uint32_t)r6[4] | ((uint32_t)r6[5] << 16)};
-                    __builtin_amdgcn_raw_buffer_store_b96(v, yr, st_ok ? yoff : kOff, 0, 0);
-                } else {
+                    for (int sb = 0; sb < kNB; ++sb) {
+                        // register sd of the two tap-8 tiles: one lane swap gives this lane channels
+                        // 4 and 5 of its half (horizontal tap 2)
+                        float r[2] = {t8[sb][0][sd], t8[sb][1][sd]};
+                        lane_swap16(r[0], r[1]);
 #pragma unroll
-                    for (int c = 0; c < kHalfCo; ++c)
-                        __builtin_amdgcn_raw_buffer_store_b16(
-                            r6[c], yr, st_ok && kHalfCo * hh + c < a.C_out ? yoff + 2u * c : kOff, 0, 0);
+                        for (int q = 0; q < 18; ++q) {
+                            const int kx = q / kHalfCo, c = q % kHalfCo;
+                            int nb = sb + 1 - kx;
+                            float v = q < 16 ? acc[sd][sb][q < 16 ? q : 0] : r[q - 16 > 0 ? 1 : 0];
+                            if (nb >= kNB) {   // to the next lane (it takes lane l-1)
+                                nb = 0;
+                                v = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                    0, __builtin_bit_cast(int, v), 0x138, 0xF, 0xF, false));
+                            } else if (nb < 0) {   // to the previous lane (it takes lane l+1)
+                                nb = kNB - 1;
+                                v = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                    0, __builtin_bit_cast(int, v), 0x130, 0xF, 0xF, false));
+                            }
+                            osum[nb][c] += v;
+                        }
+                        // cleared for the output row three further on: the 32x32 block by a matrix
+                        // instruction of zeros (an ordinary accumulator result, so it stays in place),
+                        // the tiles' register directly
+                        vec8 za;   // zeros the compiler cannot see: one instruction per block
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            reinterpret_cast<float *>(&za)[e] = opaque_zero();
+                        acc[sd][sb] = E::mfma32x32x16(za, za, zero);
+                        t8[sb][0][sd] = z;
+                        t8[sb][1][sd] = z;
+                    }
+                }
+#pragma unroll
+                for (int nb = 0; nb < kNB; ++nb) {
+                    const float *o = osum[nb];
+                    const int p = 4 * j + nb;
+                    const int w = w0 + p;
+                    const bool st_ok = emit && p >= 1 && p <= a.strip_out && w < a.W;
+                    u16 r6[kHalfCo];
+#pragma unroll
+                    for (int c = 0; c < kHalfCo; ++c) r6[c] = E::from_f32(epilogue<EPI>(o[c]));
+                    // 32-bit offsets into the group's four output frames, no branches: a store that
+                    // must not happen goes to an offset past the buffer range, where it is dropped
+                    const uint32_t yoff =
+                        (uint32_t)(((wave * a.H + ho) * a.W + w) * a.C_out + kHalfCo * hh) * 2u;
+                    if constexpr (RGB) {
+                        uint32_t q[kHalfCo];
+#pragma unroll
+                        for (int c = 0; c < kHalfCo; ++c) q[c] = rgb_code(E::to_f32(r6[c]));
+                        // half 0 lacks blue of row 2h (channels 8, 9), half 1 red of row 2h+1
+                        // (channels 2, 3): local channels 2 and 3 of the other half
+                        const uint32_t recv = (uint32_t)__builtin_amdgcn_ds_bpermute(
+                            (lane ^ 32) << 2, (int)(q[2] | (q[3] << 8)));
+                        const uint32_t r0 = recv & 0xFFu, r1 = (recv >> 8) & 0xFFu;
+                        // bytes R G B R G B of pixels (2h + hh, 2w) and (2h + hh, 2w + 1)
+                        const uint32_t p01 = hh == 0 ? (q[0] | (q[4] << 8)) : (r0 | (q[0] << 8));
+                        const uint32_t p23 = hh == 0 ? (r0 | (q[1] << 8)) : (q[4] | (r1 << 8));
+                        const uint32_t p45 = hh == 0 ? (q[5] | (r1 << 8)) : (q[1] | (q[5] << 8));
+                        const uint32_t roff =
+                            st_ok ? (uint32_t)(((wave * 2 * a.H + 2 * ho + hh) * 2 * a.W + 2 * w) * 3) : kOff;
+                        __builtin_amdgcn_raw_buffer_store_b16((u16)p01, yr, roff, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b16((u16)p23, yr,
+                                                              __builtin_elementwise_add_sat(roff, 2u), 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b16((u16)p45, yr,
+                                                              __builtin_elementwise_add_sat(roff, 4u), 0, 0);
+                    } else if constexpr (CO12) {
+                        typedef uint32_t v3u __attribute__((ext_vector_type(3)));
+                        const v3u v = {(uint32_t)r6[0] | ((uint32_t)r6[1] << 16),
+                                       (uint32_t)r6[2] | ((uint32_t)r6[3] << 16),
+                                       (uint32_t)r6[4] | ((uint32_t)r6[5] << 16)};
+                        __builtin_amdgcn_raw_buffer_store_b96(v, yr, st_ok ? yoff : kOff, 0, 0);
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < kHalfCo; ++c)
+                            __builtin_amdgcn_raw_buffer_store_b16(
+                                r6[c], yr, st_ok && kHalfCo * hh + c < a.C_out ? yoff + 2u * c : kOff, 0, 0);
+                    }
                 }
             }
-        }
-    };
+        };
 
-    if constexpr (FUSED) {
-        // Sets are numbered from the band's first Z row: Z row st takes weight version st mod 3
-        // and completes output row st - 1 (band-local), whose set is (st - 1) mod 3.  Unrolled by
-        // three so that the set is a compile-time index.
+        if constexpr (FUSED) {
+            // Sets are numbered from the band's first Z row: Z row st takes weight version st mod 3
+            // and completes output row st - 1 (band-local), whose set is (st - 1) mod 3.  Unrolled by
+            // three so that the set is a compile-time index.
 #pragma unroll 1
-        for (int st = 0; st < nsteps; st += 3) {
-            row_body(std::integral_constant<int, 0>{}, st);
-            fused_epilogue(std::integral_constant<int, 2>{}, st);
-            if (st + 1 < nsteps) {
-                row_body(std::integral_constant<int, 1>{}, st + 1);
-                fused_epilogue(std::integral_constant<int, 0>{}, st + 1);
+            for (int st = 0; st < nsteps; st += 3) {
+                row_body(std::integral_constant<int, 0>{}, st);
+                fused_epilogue(std::integral_constant<int, 2>{}, st);
+                if (st + 1 < nsteps) {
+                    row_body(std::integral_constant<int, 1>{}, st + 1);
+                    fused_epilogue(std::integral_constant<int, 0>{}, st + 1);
+                }
+                if (st + 2 < nsteps) {
+                    row_body(std::integral_constant<int, 2>{}, st + 2);
+                    fused_epilogue(std::integral_constant<int, 1>{}, st + 2);
+                }
             }
-            if (st + 2 < nsteps) {
-                row_body(std::integral_constant<int, 2>{}, st + 2);
-                fused_epilogue(std::integral_constant<int, 1>{}, st + 2);
+        } else {
+#pragma unroll 1
+            for (int st = 0; st < nsteps; ++st) {
+                row_body(std::integral_constant<int, 0>{}, st);
+                plane_epilogue(st);
             }
         }
-    } else {
-#pragma unroll 1
-        for (int st = 0; st < nsteps; ++st) {
-            row_body(std::integral_constant<int, 0>{}, st);
-            plane_epilogue(st);
-        }
+        // Before the next segment's first copies: every copy of this one has landed (the last
+        // stages issue copies that nothing reads) and every wave is done with its buffers.
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        wg_barrier();
     }
-    // no LDS copy may still be in flight when the workgroup's LDS is released
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
 
 }  // namespace
@@ -626,24 +643,76 @@ hipError_t launch_head_gemm(const HeadGemmParams &p, hipStream_t stream) {
     a.strip_out = p.fused ? kWavePos - 2 : kWavePos;
     a.strips = (p.W + a.strip_out - 1) / a.strip_out;
     a.fgroups = (p.D + 3) / 4;
-    // One workgroup per CU is resident (accumulators fill the register file).  Pick the band count
-    // that minimises (rounds of 256 workgroups) x (rows a wave computes, halo included).
-    const long long cols = (long long)p.N * a.fgroups * a.strips;
+    // Row ranges.  One workgroup per CU is resident (the accumulators fill the register file),
+    // and a workgroup's time is the number of Z rows it computes: its output rows plus, in FUSED
+    // mode, two halo rows for every strip its range touches.  The strip-major (strip, row) order
+    // of a frame group is cut into `ranges` contiguous pieces of near-equal cost, the same cut for
+    // every (sample, frame group), with the range count that minimises rounds of 256 workgroups x
+    // the largest piece.  A piece may run from the end of one strip into the next, so every CU
+    // can take one without the bands of a strip having to divide the rows evenly.
     const int halo = p.fused ? 2 : 0;
-    long long best = -1;
-    int best_bands = 1;
-    for (int bands = 1; bands <= p.H && bands <= 256; ++bands) {
-        const int rpb = (p.H + bands - 1) / bands;
-        const int real_bands = (p.H + rpb - 1) / rpb;
-        const long long rounds = (cols * real_bands + 255) / 256;
-        const long long cost = rounds * (rpb + halo);
-        if (best < 0 || cost < best) best = cost, best_bands = real_bands;
+    const long long groups = (long long)p.N * a.fgroups;   // (sample, frame group) pairs
+    const long long SH = (long long)a.strips * p.H;
+    // pieces needed when no piece costs more than K (greedy: fill each piece to K)
+    auto pieces_for = [&](long long K) {
+        long long count = 0, pos = 0;
+        while (pos < SH) {
+            long long cost = 0;
+            ++count;
+            while (pos < SH) {
+                const long long left = p.H - pos % p.H, room = K - cost - halo;
+                if (room <= 0) break;
+                const long long take = room < left ? room : left;
+                cost += take + halo;
+                pos += take;
+                if (take < left) break;
+            }
+        }
+        return count;
+    };
+    // the smallest largest-piece cost with at most R pieces
+    auto cost_for = [&](long long R) {
+        long long lo = halo + 1, hi = SH + (long long)a.strips * halo;
+        while (lo < hi) {
+            const long long mid = (lo + hi) / 2;
+            if (pieces_for(mid) <= R) hi = mid;
+            else lo = mid + 1;
+        }
+        return lo;
+    };
+    long long best = -1, ranges = 1;
+    const long long rmax = SH < kMaxRanges ? SH : kMaxRanges;
+    for (long long rounds = 1; rounds <= 4; ++rounds) {
+        long long R = 256 * rounds / groups;
+        if (R > rmax) R = rmax;
+        if (R < 1) R = 1;
+        const long long cost = (groups * R + 255) / 256 * cost_for(R);
+        if (best < 0 || cost < best) best = cost, ranges = R;
+        if (R == rmax) break;
     }
-    a.rows_per_band = (p.H + best_bands - 1) / best_bands;
-    a.bands = (p.H + a.rows_per_band - 1) / a.rows_per_band;
+    {
+        const long long K = cost_for(ranges);
+        long long pos = 0;
+        int g = 0;
+        a.bound[0] = 0;
+        while (pos < SH && g < kMaxRanges) {
+            long long cost = 0;
+            while (pos < SH) {
+                const long long left = p.H - pos % p.H, room = K - cost - halo;
+                if (room <= 0) break;
+                const long long take = room < left ? room : left;
+                cost += take + halo;
+                pos += take;
+                if (take < left) break;
+            }
+            a.bound[++g] = (int)pos;
+        }
+        for (int r = g + 1; r <= ranges; ++r) a.bound[r] = (int)SH;   // empty ranges
+        a.ranges = (int)ranges;
+    }
     a.window_bytes = (uint32_t)((size_t)kInFrames * p.rg.H_in * p.W * p.C_in * 2);
     a.wp_bytes = (uint32_t)((size_t)packed_chunks * (p.fused ? 3 : 1) * kHeadChunkPieces * 16);
-    const long long wgs = cols * a.bands;
+    const long long wgs = groups * a.ranges;
     a.total_wg = (uint32_t)wgs;
     const dim3 grid((unsigned)wgs), block(256);
 #define CX_HG(BFV, FV, EPIV)                                                          \
