@@ -310,9 +310,13 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
             const int cbase = FUSED ? (c * 3 + mod3(st)) * kHeadChunkPieces : c * kHeadChunkPieces;
 #pragma unroll
             for (int q = 0; q < kCopyA; ++q) {
-                const int piece = (wave * kCopyA + q) * 64;
+                // copy k fills LDS rows 16k .. 16k+15; rows 112 .. 127 of each temporal tap (k = 7
+                // mod 8) are never read, so their copy takes an offset past the range: no traffic
+                const int k = wave * kCopyA + q;
+                const int piece = k * 64;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    wr, (lds_void *)&abuf[piece], 16, (uint32_t)((cbase + piece + lane) * 16), 0, 0, 0);
+                    wr, (lds_void *)&abuf[piece], 16,
+                    (k & 7) == 7 ? kOff : (uint32_t)((cbase + piece + lane) * 16), 0, 0, 0);
             }
             // Z row zr reads input row zr + h_org; window frame i is input frame fw0 + i.  The
             // frame / row / chunk part of an offset is uniform (scalar registers); the column part
