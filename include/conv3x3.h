@@ -243,10 +243,11 @@ size_t conv3x3x3_packed_weight_bytes(int N, int C_in, int C_out, int D, int H, i
 
 /* A one-line description of the launch plan conv3x3x3_fwd would use for this request, written
  * to buf (host memory of buf_len bytes, caller-owned; truncated to buf_len - 1 characters and
- * NUL-terminated): "fused_head", "split_head", or the MFMA kernel ("igemm32", "igemm32_kq" when
- * the four waves of a workgroup split K, "igemm16_wide", "igemm16_narrow") with its position
- * tile (rows x columns of one frame), output rows per workgroup, split-K factor and workgroup
- * count.  Returns the full length of the description, or a negative status (CONV_E_INVAL for a
+ * NUL-terminated): "fused_head" / "split_head" with the head's work split (strips of 126 / 128
+ * positions, groups of four frames, row ranges per frame group, the largest range's Z rows,
+ * workgroups), or the MFMA kernel ("igemm32", "igemm32_kq" when the four waves of a workgroup
+ * split K, "igemm16_wide", "igemm16_narrow") with its position tile (rows x columns of one
+ * frame), output rows per workgroup, split-K factor and workgroup count.  Returns the full length of the description, or a negative status (CONV_E_INVAL for a
  * NULL buf or buf_len < 1, else what conv3x3x3_select_algo returns).  Host-only.  [head.cu,
  * header comment: which of the head's forms, direct or split, a pass runs.] */
 int conv3x3x3_describe(int N, int C_in, int C_out, int D, int H, int W, int stride, int layout,

@@ -400,8 +400,11 @@ def test_describe_names_the_plan():
     assert d(1, 512, 512, 1, 44, 78) == "igemm32_kq tile=8x16 rows=64 splits=1 workgroups=240"
     assert d(1, 512, 512, 4, 44, 78) == "igemm32 tile=8x16 rows=256 splits=1 workgroups=240"
     assert d(1, 264, 96, 1, 44, 78) == "igemm32 tile=4x32 rows=256 splits=5 workgroups=165"
-    assert d(1, 256, 12, 16, 352, 624) == "fused_head"
-    assert d(1, 256, 12, 16, 352, 624, algo=C.ALGO_SPLIT_HEAD) == "split_head"
+    # the head: 5 strips of 126 positions, 4 frame groups, 64 row ranges of <= 30 Z rows each
+    assert d(1, 256, 12, 16, 352, 624) == (
+        "fused_head strips=5 frame_groups=4 row_ranges=64 z_rows=30 workgroups=256")
+    assert d(1, 256, 12, 16, 352, 624, algo=C.ALGO_SPLIT_HEAD).startswith(
+        "split_head strips=5 frame_groups=4 row_ranges=64 ")
     assert d(1, 256, 12, 16, 352, 624, algo=C.ALGO_MFMA).startswith("igemm16_narrow tile=8x32 rows=16 ")
     assert d(1, 256, 12, 16, 352, 624, stride=2).startswith("igemm32 tile=4x32 rows=256 ")
     # truncation: the full length comes back, the buffer holds what fits
@@ -416,3 +419,33 @@ def test_describe_names_the_plan():
     assert rejected < 0 and lib.conv3x3x3_describe(1, 20, 12, 1, 4, 4, 1, 1, 1, 0, buf, 8) == rejected
     with pytest.raises(C.ConvError):
         d(1, 20, 12, 1, 4, 4)
+
+
+def _head_plan(N, D, H, W, fused=True):
+    txt = C.conv3x3x3_describe(N, 32, 12, D, H, W,
+                               algo=C.ALGO_FUSED_HEAD if fused else C.ALGO_SPLIT_HEAD)
+    f = dict(kv.split("=") for kv in txt.split()[1:])
+    return {k: int(v) for k, v in f.items()}
+
+
+@pytest.mark.parametrize("shape", [(1, 16, 352, 624), (1, 40, 37, 300), (2, 32, 17, 380),
+                                   (1, 3, 9, 50), (1, 16, 44, 624), (1, 200, 352, 624),
+                                   (3, 7, 1, 1), (1, 64, 1000, 130)])
+@pytest.mark.parametrize("fused", [True, False])
+def test_head_row_ranges_cover_and_balance(shape, fused):
+    """The head's row ranges: one workgroup per (sample, frame group, range); no range costs more
+    than a strip's rows plus its halo would if every range were a whole band of equal height, and
+    the ranges fit the 256-workgroup rounds the plan chose."""
+    N, D, H, W = shape
+    p = _head_plan(N, D, H, W, fused)
+    strip_out = 126 if fused else 128
+    halo = 2 if fused else 0
+    assert p["strips"] == -(-W // strip_out) and p["frame_groups"] == -(-D // 4)
+    assert p["workgroups"] == N * p["frame_groups"] * p["row_ranges"]
+    assert 1 <= p["row_ranges"] <= min(256, p["strips"] * H)
+    # lower bound: the average cost; upper bound: whole bands of ceil(rows / ranges) rows
+    total = p["strips"] * H
+    assert p["z_rows"] >= -(-total // p["row_ranges"]) + halo
+    assert p["z_rows"] <= -(-total // p["row_ranges"]) + 2 * halo + 1
+    # at most four rounds of 256 workgroups
+    assert p["workgroups"] <= 4 * 256 or p["row_ranges"] == 1

@@ -344,7 +344,13 @@ int conv3x3x3_describe(int N, int C_in, int C_out, int D, int H, int W, int stri
     if (!buf || buf_len < 1) return fail(CONV_E_INVAL, "buf must be non-NULL with buf_len >= 1");
     char tmp[160];
     if (a == CONV_ALGO_SPLIT_HEAD || a == CONV_ALGO_FUSED_HEAD) {
-        snprintf(tmp, sizeof tmp, "%s", a == CONV_ALGO_SPLIT_HEAD ? "split_head" : "fused_head");
+        // the temporal GEMM's launch (the split head's plane holds the output rows: a plain
+        // convolution's rows above and below read padding)
+        const bool fused = a == CONV_ALGO_FUSED_HEAD;
+        const cx::HeadRangePlan rp = cx::plan_head_ranges(N, D, H, W, fused);
+        snprintf(tmp, sizeof tmp, "%s strips=%d frame_groups=%d row_ranges=%d z_rows=%d workgroups=%lld",
+                 fused ? "fused_head" : "split_head", rp.strips, rp.fgroups, rp.ranges,
+                 rp.max_z_rows, rp.workgroups);
     } else {
         const cx::IgemmPlan pl = plan_for(a, N, C_in, C_out, D, H, W, stride);
         const char *k = pl.family == cx::IG_W32 ? (pl.kq ? "igemm32_kq" : "igemm32")

@@ -89,7 +89,7 @@ constexpr int kCopyB = kBPieces / 256;               // 12
 constexpr int kHalfCo = 6;              // output channels per lane half
 constexpr int kPlaneCh = kHeadPlaneChannels;
 constexpr uint32_t kOff = 0xFFFFFFFFu;  // an offset past any buffer range; saturating adds keep it
-constexpr int kMaxRanges = 256;         // row ranges per (sample, frame group)
+constexpr int kMaxRanges = kHeadMaxRanges;   // row ranges per (sample, frame group)
 
 // s_waitcnt immediates: vmcnt is split over bits 3:0 and 15:14; expcnt / lgkmcnt left open.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -633,50 +633,44 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
 
 }  // namespace
 
-hipError_t launch_head_gemm(const HeadGemmParams &p, hipStream_t stream) {
-    HeadGemmKArgs a{};
-    a.x = static_cast<const u16 *>(p.x);
-    a.wp = static_cast<const u16 *>(p.wp);
-    a.bias = static_cast<const u16 *>(p.bias);
-    a.out = static_cast<u16 *>(p.out);
-    a.N = p.N, a.C_in = p.C_in, a.C_out = p.C_out, a.D = p.D, a.H = p.H, a.W = p.W;
-    a.D_in = p.rg.D_in, a.H_in = p.rg.H_in, a.d_org = p.rg.d_org, a.h_org = p.rg.h_org;
-    a.d_lo = p.rg.d_lo, a.d_hi = p.rg.d_hi, a.h_lo = p.rg.h_lo, a.h_hi = p.rg.h_hi;
-    const int packed_chunks = (p.C_in + 31) / 32;
-    a.nchunks = (packed_chunks + 1) & ~1;   // the kernel runs stages in pairs
-    a.strip_out = p.fused ? kWavePos - 2 : kWavePos;
-    a.strips = (p.W + a.strip_out - 1) / a.strip_out;
-    a.fgroups = (p.D + 3) / 4;
-    // Row ranges.  One workgroup per CU is resident (the accumulators fill the register file),
-    // and a workgroup's time is the number of Z rows it computes: its output rows plus, in FUSED
-    // mode, two halo rows for every strip its range touches.  The strip-major (strip, row) order
-    // of a frame group is cut into `ranges` contiguous pieces of near-equal cost, the same cut for
-    // every (sample, frame group), with the range count that minimises rounds of 256 workgroups x
-    // the largest piece.  A piece may run from the end of one strip into the next, so every CU
-    // can take one without the bands of a strip having to divide the rows evenly.
-    const int halo = p.fused ? 2 : 0;
-    const long long groups = (long long)p.N * a.fgroups;   // (sample, frame group) pairs
-    const long long SH = (long long)a.strips * p.H;
-    // pieces needed when no piece costs more than K (greedy: fill each piece to K)
+// Row ranges.  One workgroup per CU is resident (the accumulators fill the register file), and
+// a workgroup's time is the number of Z rows it computes: its output rows plus, in FUSED mode, two
+// halo rows for every strip its range touches.  The strip-major (strip, row) order of a frame
+// group is cut into `ranges` contiguous pieces of near-equal cost, the same cut for every
+// (sample, frame group), with the range count that minimises rounds of 256 workgroups x the
+// largest piece.  A piece may run from the end of one strip into the next, so every CU can take
+// one without the bands of a strip having to divide the rows evenly.
+HeadRangePlan plan_head_ranges(int N, int D, int H, int W, bool fused) {
+    HeadRangePlan rp{};
+    rp.strip_out = fused ? kWavePos - 2 : kWavePos;
+    rp.strips = (W + rp.strip_out - 1) / rp.strip_out;
+    rp.fgroups = (D + 3) / 4;
+    const int halo = fused ? 2 : 0;
+    const long long groups = (long long)N * rp.fgroups;   // (sample, frame group) pairs
+    const long long SH = (long long)rp.strips * H;
+    if (groups <= 0 || SH <= 0) return rp;
+    // fills one piece from position pos with cost at most K (greedy), returning its cost
+    auto fill = [&](long long &pos, long long K) {
+        long long cost = 0;
+        while (pos < SH) {
+            const long long left = H - pos % H, room = K - cost - halo;
+            if (room <= 0) break;
+            const long long take = room < left ? room : left;
+            cost += take + halo;
+            pos += take;
+            if (take < left) break;
+        }
+        return cost;
+    };
+    // pieces needed when no piece costs more than K
     auto pieces_for = [&](long long K) {
         long long count = 0, pos = 0;
-        while (pos < SH) {
-            long long cost = 0;
-            ++count;
-            while (pos < SH) {
-                const long long left = p.H - pos % p.H, room = K - cost - halo;
-                if (room <= 0) break;
-                const long long take = room < left ? room : left;
-                cost += take + halo;
-                pos += take;
-                if (take < left) break;
-            }
-        }
+        while (pos < SH) fill(pos, K), ++count;
         return count;
     };
     // the smallest largest-piece cost with at most R pieces
     auto cost_for = [&](long long R) {
-        long long lo = halo + 1, hi = SH + (long long)a.strips * halo;
+        long long lo = halo + 1, hi = SH + (long long)rp.strips * halo;
         while (lo < hi) {
             const long long mid = (lo + hi) / 2;
             if (pieces_for(mid) <= R) hi = mid;
@@ -694,29 +688,39 @@ hipError_t launch_head_gemm(const HeadGemmParams &p, hipStream_t stream) {
         if (best < 0 || cost < best) best = cost, ranges = R;
         if (R == rmax) break;
     }
-    {
-        const long long K = cost_for(ranges);
-        long long pos = 0;
-        int g = 0;
-        a.bound[0] = 0;
-        while (pos < SH && g < kMaxRanges) {
-            long long cost = 0;
-            while (pos < SH) {
-                const long long left = p.H - pos % p.H, room = K - cost - halo;
-                if (room <= 0) break;
-                const long long take = room < left ? room : left;
-                cost += take + halo;
-                pos += take;
-                if (take < left) break;
-            }
-            a.bound[++g] = (int)pos;
-        }
-        for (int r = g + 1; r <= ranges; ++r) a.bound[r] = (int)SH;   // empty ranges
-        a.ranges = (int)ranges;
+    const long long K = cost_for(ranges);
+    long long pos = 0, worst = 0;
+    int g = 0;
+    rp.bound[0] = 0;
+    while (pos < SH && g < kMaxRanges) {
+        const long long c = fill(pos, K);
+        if (c > worst) worst = c;
+        rp.bound[++g] = (int)pos;
     }
+    for (int r = g + 1; r <= ranges; ++r) rp.bound[r] = (int)SH;   // empty ranges
+    rp.ranges = (int)ranges;
+    rp.max_z_rows = (int)worst;
+    rp.workgroups = groups * ranges;
+    return rp;
+}
+
+hipError_t launch_head_gemm(const HeadGemmParams &p, hipStream_t stream) {
+    HeadGemmKArgs a{};
+    a.x = static_cast<const u16 *>(p.x);
+    a.wp = static_cast<const u16 *>(p.wp);
+    a.bias = static_cast<const u16 *>(p.bias);
+    a.out = static_cast<u16 *>(p.out);
+    a.N = p.N, a.C_in = p.C_in, a.C_out = p.C_out, a.D = p.D, a.H = p.H, a.W = p.W;
+    a.D_in = p.rg.D_in, a.H_in = p.rg.H_in, a.d_org = p.rg.d_org, a.h_org = p.rg.h_org;
+    a.d_lo = p.rg.d_lo, a.d_hi = p.rg.d_hi, a.h_lo = p.rg.h_lo, a.h_hi = p.rg.h_hi;
+    const int packed_chunks = (p.C_in + 31) / 32;
+    a.nchunks = (packed_chunks + 1) & ~1;   // the kernel runs stages in pairs
+    const HeadRangePlan rp = plan_head_ranges(p.N, p.D, p.H, p.W, p.fused);
+    a.strip_out = rp.strip_out, a.strips = rp.strips, a.fgroups = rp.fgroups, a.ranges = rp.ranges;
+    for (int r = 0; r <= rp.ranges; ++r) a.bound[r] = rp.bound[r];
     a.window_bytes = (uint32_t)((size_t)kInFrames * p.rg.H_in * p.W * p.C_in * 2);
     a.wp_bytes = (uint32_t)((size_t)packed_chunks * (p.fused ? 3 : 1) * kHeadChunkPieces * 16);
-    const long long wgs = groups * a.ranges;
+    const long long wgs = rp.workgroups;
     a.total_wg = (uint32_t)wgs;
     const dim3 grid((unsigned)wgs), block(256);
 #define CX_HG(BFV, FV, EPIV)                                                          \

@@ -171,6 +171,19 @@ struct HeadGemmParams {
 };
 hipError_t launch_head_gemm(const HeadGemmParams &p, hipStream_t stream);
 
+// How the head kernels divide a request (pure host arithmetic).  A workgroup takes four
+// consecutive output frames (a frame group) and one row range of the strip-major (strip, output
+// row) order: range g is positions [bound[g], bound[g+1]), output row h of strip s being position
+// s*H + h.  max_z_rows is the largest range's cost in Z rows (its output rows plus, fused, two
+// halo rows per strip it touches).
+constexpr int kHeadMaxRanges = 256;
+struct HeadRangePlan {
+    int strip_out, strips, fgroups, ranges, max_z_rows;
+    long long workgroups;
+    int bound[kHeadMaxRanges + 1];
+};
+HeadRangePlan plan_head_ranges(int N, int D, int H, int W, bool fused);
+
 // ---- the head's 12-channel output as 8-bit RGB frames (factor-2 pixel shuffle) ------------
 struct VideoParams {
     const void *y;     // (N, D, H, W, 12) NDHWC
