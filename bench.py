@@ -185,6 +185,31 @@ def lds_dma_calibration(stream):
     return out
 
 
+def lds_read_calibration(stream):
+    """The rate of conflict-free LDS reads (16 bytes per lane) with 8 and 16 waves per CU: what
+    the LDS can deliver to fragment reads, summed over the chip (TB/s; divided by 256 CUs and
+    the clock it is bytes per clock per CU)."""
+    import torch
+    from x3x3_convolution_amd import conv as C
+    wgs, iters = 256 * 4, 4000
+    out = torch.empty(wgs * 512 * 4, dtype=torch.int32, device="cuda")
+    res = {}
+    for waves in (4, 8):
+        C.conv_calib_lds_read(out, wgs, waves, iters, stream)
+        torch.cuda.synchronize()
+        tm = Timer(torch.cuda.current_stream())
+        for _ in range(3):
+            s0 = tm.start()
+            C.conv_calib_lds_read(out, wgs, waves, iters, stream)
+            tm.stop("lds", s0)
+        torch.cuda.synchronize()
+        ms = tm.stats("lds")["median"]
+        tbs = wgs * waves * 64 * 16 * 8.0 * iters / (ms * 1e-3) / 1e12
+        res["lds_read_%dwaves_per_cu_tbs" % (2 * waves)] = round(tbs, 1)
+    del out
+    return res
+
+
 class Timer:
     """HIP events on one stream around a sequence of launches."""
 
@@ -691,7 +716,8 @@ def main():
     torch.cuda.set_stream(strm)
     stream = strm.cuda_stream
     if args.mfma_calibration:
-        print(json.dumps(dict(mfma_calibration(stream), **lds_dma_calibration(stream))))
+        print(json.dumps(dict(mfma_calibration(stream), **lds_dma_calibration(stream),
+                              **lds_read_calibration(stream))))
         return
     wl = si.WORKLOADS[args.workload]
     line = dict(metric=METRIC, n_gpus=1, steps=args.steps, warmup=args.warmup,
@@ -723,7 +749,8 @@ def main():
         if not args.no_workloads and args.algo == "auto":
             line["workloads"] = run_workloads(args, stream)
             line["calibration"] = dict(copy_calibration(), **mfma_calibration(stream),
-                                       **lds_dma_calibration(stream))
+                                       **lds_dma_calibration(stream),
+                                       **lds_read_calibration(stream))
     else:
         wall_ms, roof, _, _ = run_other(args, wl, stream)
         layout = ("NHWC" if args.channels_last else "NCHW") if wl.kind == "2d" else "NDHWC"

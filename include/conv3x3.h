@@ -349,6 +349,14 @@ int conv_calib_mfma_bf16(void *out, int workgroups, int iters, void *stream);
 int conv_calib_lds_dma(const void *src, size_t src_bytes, int whole_lines, int workgroups,
                        int iters, void *stream);
 
+/* Measurement aid, not part of the convolution: enqueues `workgroups` workgroups of `waves`
+ * waves (4 or 8; 64 KiB of LDS each, so two share a CU), each wave issuing iters x 8
+ * conflict-free 16-byte-per-lane LDS reads of 1 KiB; `out` (device memory, caller-owned) takes
+ * workgroups * waves * 64 * 16 bytes of folded values.  Timed by the caller, bytes = workgroups
+ * * waves * 64 * 16 * 8 * iters.  Returns CONV_E_INVAL for bad arguments, CONV_E_LAUNCH if the
+ * launch is rejected. */
+int conv_calib_lds_read(void *out, int workgroups, int waves, int iters, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

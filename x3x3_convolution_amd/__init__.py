@@ -12,5 +12,5 @@ from .conv import (  # noqa: F401
     conv3x3x3_fwd_noalloc, conv3x3x3_fwd_region, conv3x3x3_head_rgb8, conv3x3x3_is_supported,
     conv3x3x3_pack_weights,
     conv3x3x3_packed_weight_bytes, conv3x3x3_select_algo, conv3x3x3_workspace_bytes,
-    conv_abi_version, conv_band_region, conv_calib_lds_dma, conv_calib_mfma_bf16, conv_causal_region, conv_head_stencil, conv_head_temporal, conv_last_error, conv_out_size,
+    conv_abi_version, conv_band_region, conv_calib_lds_dma, conv_calib_lds_read, conv_calib_mfma_bf16, conv_causal_region, conv_head_stencil, conv_head_temporal, conv_last_error, conv_out_size,
     conv_status_str, conv_video_rgb8, library, library_path)

@@ -50,6 +50,7 @@ EXPORTS = [
     ("conv3x3x3_fwd_noalloc", _I, [_P, _P, _P, _P] + [_I] * 11 + [_P]),
     ("conv_calib_lds_dma", _I, [_P, _SZ, _I, _I, _I, _P]),
     ("conv3x3x3_describe", _I, [_I] * 10 + [ctypes.c_char_p, _I]),
+    ("conv_calib_lds_read", _I, [_P, _I, _I, _I, _P]),
 ]
 NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -274,3 +275,9 @@ def conv3x3x3_describe(N, C_in, C_out, D, H, W, stride=1, layout=LAYOUT_CHANNELS
     if n < 0:
         _check(n)
     return buf.value.decode()
+
+
+def conv_calib_lds_read(out, workgroups, waves, iters, stream=None):
+    """Enqueues the LDS read-rate calibration loop (a measurement aid, conv_calib_lds_read)."""
+    return _check(library().conv_calib_lds_read(_ptr(out), workgroups, waves, iters,
+                                                _stream(stream)))

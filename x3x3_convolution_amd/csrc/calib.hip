@@ -1,6 +1,7 @@
 // Measurement aids, not part of the convolution: the rate the matrix cores reach on a loop of
-// nothing but bf16 32x32x16 MFMAs with register operands, and the rate of global -> LDS copies
-// (the way the kernels stage their operands) for whole and half cache lines.  The benchmark
+// nothing but bf16 32x32x16 MFMAs with register operands, the rate of global -> LDS copies
+// (the way the kernels stage their operands) for whole and half cache lines, and the rate of
+// conflict-free LDS reads.  The benchmark
 // reports them beside the plain-copy rate as what this machine sustains (clock and power
 // included); the roofline fractions are still taken against the published peaks.
 #include <hip/hip_runtime.h>
@@ -70,8 +71,45 @@ __global__ __launch_bounds__(256, 1) void lds_dma_kernel(const unsigned char *sr
     __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
 }
 
+// LDS reads: every wave keeps reading 1 KiB slices (16 bytes per lane, conflict-free: the 64
+// lanes read 1 KiB of consecutive bytes) of a 64 KiB LDS array, eight per iteration, folding the
+// values into one register so that nothing is dropped.  WAVES waves per workgroup; with 64 KiB
+// per workgroup two workgroups share a CU.
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void lds_read_kernel(uint4 *out, int iters) {
+    __shared__ uint4 buf[4096];
+    for (int i = threadIdx.x; i < 4096; i += 64 * WAVES) buf[i] = uint4{(unsigned)i, 1u, 2u, 3u};
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint4 acc = {0u, 0u, 0u, 0u};
+    int base = wave * 512 + lane;
+#pragma unroll 1
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const uint4 v = buf[(base + s * 64) & 4095];
+            acc.x ^= v.x, acc.y ^= v.y, acc.z ^= v.z, acc.w ^= v.w;
+        }
+        base += 512;
+    }
+    out[(size_t)blockIdx.x * 64 * WAVES + threadIdx.x] = acc;
+}
+
 }  // namespace
 }  // namespace cx
+
+extern "C" int conv_calib_lds_read(void *out, int workgroups, int waves, int iters, void *stream) {
+    if (!out || workgroups < 1 || workgroups > (1 << 20) || iters < 1 || (waves != 4 && waves != 8))
+        return CONV_E_INVAL;
+    uint4 *o = static_cast<uint4 *>(out);
+    if (waves == 4)
+        hipLaunchKernelGGL(cx::lds_read_kernel<4>, dim3((unsigned)workgroups), dim3(256), 0,
+                           (hipStream_t)stream, o, iters);
+    else
+        hipLaunchKernelGGL(cx::lds_read_kernel<8>, dim3((unsigned)workgroups), dim3(512), 0,
+                           (hipStream_t)stream, o, iters);
+    return hipGetLastError() == hipSuccess ? CONV_OK : CONV_E_LAUNCH;
+}
 
 extern "C" int conv_calib_lds_dma(const void *src, size_t src_bytes, int whole_lines,
                                   int workgroups, int iters, void *stream) {
