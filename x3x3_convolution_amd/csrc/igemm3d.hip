@@ -30,9 +30,6 @@ namespace cx {
 
 namespace {
 
-// Elements per LDS window position: 32 channels + 8 padding (80 bytes) so that the 16 positions
-// one fragment reads fall on distinct bank groups.
-constexpr int kPosStride = 40;
 
 struct IgemmKArgs {
     const u16 *x;
@@ -105,7 +102,12 @@ __global__ __launch_bounds__(256, 2) void igemm3d_kernel(IgemmKArgs a) {
     constexpr int PIECES = FPOS * 4;       // 16-byte pieces of one staged window
     constexpr int PPT = (PIECES + 255) / 256;
     constexpr int PD = 3;                  // weight-fragment prefetch distance (taps)
-    __shared__ __attribute__((aligned(16))) u16 win[2][FPOS * kPosStride];
+    // A window position is 64 bytes (32 channels) in four 16-byte pieces, stored XOR-permuted by
+    // (column / 4) % 4, and window rows are RowPos positions apart (a multiple of 4): any 16
+    // consecutive columns of a row -- what one fragment read takes -- fall on distinct bank
+    // groups.
+    constexpr int RowPos = (WW + 3) / 4 * 4;
+    __shared__ __attribute__((aligned(16))) uint4 win[2][WH * RowPos * 4];
     __shared__ float bias_s[BM];   // this workgroup's output rows (0 past C_out / no bias)
 
     const int tid = threadIdx.x;
@@ -167,12 +169,19 @@ __global__ __launch_bounds__(256, 2) void igemm3d_kernel(IgemmKArgs a) {
             stg[j] = v;
         }
     };
+    // the LDS slot of this thread's pieces (the same in every stage)
+    int cslot[PPT];
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+        const int i = tid + j * 256, q = i & 3, pos = i >> 2;
+        const int wh = pos / WW, ww = pos - wh * WW;
+        cslot[j] = (wh * RowPos + ww) * 4 + (q ^ ((ww >> 2) & 3));
+    }
     auto commit = [&](int buf) {
 #pragma unroll
         for (int j = 0; j < PPT; ++j) {
             const int i = tid + j * 256;
-            if (PIECES % 256 == 0 || i < PIECES)
-                *reinterpret_cast<uint4 *>(&win[buf][(i >> 2) * kPosStride + (i & 3) * 8]) = stg[j];
+            if (PIECES % 256 == 0 || i < PIECES) win[buf][cslot[j]] = stg[j];
         }
     };
     auto load_a = [&](int s, int j, vec8 *dst) {
@@ -195,11 +204,19 @@ __global__ __launch_bounds__(256, 2) void igemm3d_kernel(IgemmKArgs a) {
     }
     __syncthreads();
 
+    // B fragment slot of lane column (lane & 15) + kx, piece lane / 16, in window row 0 and block
+    // column 0; block columns are multiples of 16, which keep the swizzle
+    int bslot[3];
+#pragma unroll
+    for (int kx = 0; kx < 3; ++kx) {
+        const int col = (lane & 15) + kx;
+        bslot[kx] = col * 4 + ((lane >> 4) ^ ((col >> 2) & 3));
+    }
     for (int s = 0; s < nst; ++s) {
         const int buf = s & 1;
         const bool more = s + 1 < nst;
         if (more) fetch(s + 1);
-        const u16 *wsrc = win[buf];
+        const uint4 *wsrc = win[buf];
 #pragma unroll
         for (int j = 0; j < 9; ++j) {
             const int ky = j / 3, kx = j % 3;
@@ -207,8 +224,7 @@ __global__ __launch_bounds__(256, 2) void igemm3d_kernel(IgemmKArgs a) {
             for (int nb = 0; nb < NBW; ++nb) {
                 const int blk = wn * NBW + nb;
                 const int r = blk / NBLK_ROW, c0 = (blk % NBLK_ROW) * 16;
-                const vec8 B = *reinterpret_cast<const vec8 *>(
-                    wsrc + ((r + ky) * WW + c0 + (lane & 15) + kx) * kPosStride + kofs);
+                const vec8 B = __builtin_bit_cast(vec8, wsrc[bslot[kx] + ((r + ky) * RowPos + c0) * 4]);
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
                     acc[mb][nb] = E::mfma16x16x32(aq[j % PD][mb], B, acc[mb][nb]);
