@@ -229,7 +229,10 @@ int conv3x3x3_is_supported(int N, int C_in, int C_out, int D, int H, int W, int 
 /* Bytes of workspace conv3x3x3_fwd (and conv3x3x3_fwd_region for this output extent) needs:
  * the split head's intermediate plane with room for one row above and below the output rows
  * (N*D*(H+2)*W*112 elements of dtype), the split-K partial sums of the MFMA path for small
- * position counts (fp32), or 0.  Returns 0 for an unsupported request as well.  The caller
+ * position counts (fp32), the stream-K partial tiles and per-tile arrival counters of the MFMA
+ * path where a single round of whole tiles would leave compute units idle (256 KiB per
+ * workgroup, at most 256 of them, + 4 bytes per tile; the counters are cleared by a small kernel
+ * the call enqueues first, so the workspace needs no initial contents), or 0.  Returns 0 for an unsupported request as well.  The caller
  * allocates and frees the workspace.  [head.cu, head_stencil host function: the caller hands in
  * the 112-channel plane g that the temporal conv wrote.] */
 size_t conv3x3x3_workspace_bytes(int N, int C_in, int C_out, int D, int H, int W, int stride,
@@ -310,7 +313,8 @@ int conv_head_stencil(const void *g, const void *bias, void *y, int N, int D, in
  * For callers that cannot allocate device memory -- code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc: conv3x3x3_fwd with the same arguments and results, but
  * without a workspace argument.  Where the request needs a workspace (the split-K partial sums of
- * the MFMA path for small position counts, the split head's plane), it uses a static device
+ * the MFMA path for small position counts, its stream-K partial tiles and arrival counters --
+ * up to 64 MiB plus 4 bytes per tile --, the split head's plane), it uses a static device
  * array of CONV_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on until the
  * process ends; nothing else is allocated, by the library or by any routine it calls.
  *   - Returns CONV_E_WORKSPACE, with nothing enqueued, when the request needs more than
@@ -324,7 +328,7 @@ int conv_head_stencil(const void *g, const void *bias, void *y, int N, int D, in
  *   - The first call on a device looks up the array's device address (no allocation, no work
  *     enqueued); a caller that captures a graph makes one call before the capture.
  * ---------------------------------------------------------------------------------------- */
-#define CONV_NOALLOC_SCRATCH_BYTES (32u << 20)
+#define CONV_NOALLOC_SCRATCH_BYTES (80u << 20)
 int conv3x3x3_fwd_noalloc(const void *x, const void *w_packed, const void *bias, void *y, int N,
                           int C_in, int C_out, int D, int H, int W, int stride, int layout,
                           int dtype, int epilogue, int algo, void *stream);

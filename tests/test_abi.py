@@ -197,8 +197,11 @@ def test_algo_selection_and_buffer_sizes():
                                             C.ALGO_FUSED_HEAD) == 3 * 8 * 3 * 128 * 32 * 2
     # mid-decoder conv fills the chip without split-K: no workspace
     assert cx.conv3x3x3_workspace_bytes(1, 256, 256, 16, 176, 312, 1, 1, 1, 0) == 0
-    # the small low-res conv fills the chip with half-size (128-position) tiles: no split-K
-    assert cx.conv3x3x3_workspace_bytes(1, 512, 512, 4, 44, 78, 1, 1, 1, 0) == 0
+    # the small low-res conv: one round of 240 half-size (128-position) tiles would wait for
+    # the interior frames' three temporal taps, so 240 stream-K workgroups share the stages:
+    # two 128 KiB partial slots per workgroup, then one counter per tile (60 tiles x 4 frames)
+    assert cx.conv3x3x3_workspace_bytes(1, 512, 512, 4, 44, 78, 1, 1, 1, 0) == (
+        240 * 2 * 256 * 128 * 4 + 60 * 4 * 4)
     # its first causal frame alone splits K over the four waves of each workgroup: no workspace
     assert cx.conv3x3x3_workspace_bytes(1, 512, 512, 1, 44, 78, 1, 1, 1, 0) == 0
     # fewer input channels over the same frame split K over workgroups: fp32 partials
@@ -398,7 +401,7 @@ def test_head_any_number_of_frames():
 def test_describe_names_the_plan():
     d = C.conv3x3x3_describe
     assert d(1, 512, 512, 1, 44, 78) == "igemm32_kq tile=8x16 rows=64 splits=1 workgroups=240"
-    assert d(1, 512, 512, 4, 44, 78) == "igemm32 tile=8x16 rows=256 splits=1 workgroups=240"
+    assert d(1, 512, 512, 4, 44, 78) == "igemm32_sk tile=8x16 rows=256 splits=1 workgroups=240"
     assert d(1, 264, 96, 1, 44, 78) == "igemm32 tile=4x32 rows=256 splits=5 workgroups=165"
     # the head: 5 strips of 126 positions, 4 frame groups, 64 row ranges of <= 30 Z rows each
     assert d(1, 256, 12, 16, 352, 624) == (

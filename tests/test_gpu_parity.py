@@ -182,14 +182,14 @@ def test_conv3d_w32_tiles_integer_exact(case):
 # The 32x32 family with K split over the four waves of a workgroup (64-row tiles, the partial
 # tiles summed through LDS, no workspace), where the cost model sends it: few positions, many
 # input channels.  Ragged chunk counts (264 channels: waves of 2, 2, 2, 3 chunks, the last chunk
-# a quarter full; 296: 2, 3, 2, 3), part-empty 64-row tiles (72, 100, 130 channels), ragged
+# a quarter full; 296: 2, 3, 2, 3), part-empty 64-row tiles (72, 130 channels), ragged
 # frame edges, first and last frames with two temporal taps, both 128-position tiles and fp16.
 CASES_KQ = [
     # N, Ci, Co, D, H, W, dtype, epilogue, tile
     (1, 264, 72, 3, 36, 60, "bf16", "relu", "4x32"),
     (1, 296, 130, 1, 50, 90, "bf16", "none", "4x32"),
     (1, 256, 256, 2, 44, 78, "bf16", "clamp1", "8x16"),
-    (1, 488, 100, 3, 30, 50, "f16", "none", "4x32"),
+    (1, 488, 72, 3, 36, 60, "f16", "none", "4x32"),
 ]
 
 
@@ -205,6 +205,46 @@ def test_conv3d_kq_integer_exact(case):
                               seed=500 + CASES_KQ.index(case), device=DEV)
     y = run_3d(x, w, b, epi, C.ALGO_AUTO, guarded=True)
     assert_bit_exact(y, oracle_3d(x, w, b, epi), x.dtype)
+
+
+# The 32x32 family's stream-K schedule, where the cost model sends it: one round of whole
+# 256-row tiles would wait for the interior frames' tiles (three temporal taps), and K is long.
+# About one workgroup per tile, each taking an equal share of all tiles' stages; a tile split
+# between workgroups is summed from fp32 partials by the piece that ends last, in K order.  Both
+# 128-position tiles, part-empty second 256-row tiles (300 and 384 channels: padding waves compute
+# zeros and store nothing), 184 to 256 workgroups, three to five frames, fp16, and the low-res
+# 512 -> 512 convolution itself.
+CASES_SK = [
+    # N, Ci, Co, D, H, W, dtype, epilogue, tile
+    (1, 416, 384, 5, 44, 33, "bf16", "relu", "4x32"),
+    (1, 416, 300, 4, 44, 78, "f16", "none", "8x16"),
+    (1, 416, 300, 5, 36, 78, "bf16", "clamp1", "8x16"),
+    (1, 448, 384, 3, 44, 78, "f16", "relu", "8x16"),
+    (1, 512, 512, 4, 44, 78, "bf16", "none", "8x16"),
+]
+
+
+@pytest.mark.parametrize("case", CASES_SK, ids=[str(c) for c in CASES_SK])
+def test_conv3d_stream_k_integer_exact(case):
+    N, Ci, Co, D, H, W, dt, epi, tile = case
+    _say("conv3d stream-K %s" % (case,))
+    dtype = C.DTYPE_F16 if dt == "f16" else C.DTYPE_BF16
+    assert C.conv3x3x3_workspace_bytes(N, Ci, Co, D, H, W, dtype=dtype, algo=C.ALGO_AUTO) > 0
+    assert C.conv3x3x3_describe(N, Ci, Co, D, H, W, dtype=dtype).startswith(
+        "igemm32_sk tile=%s rows=256 splits=1 " % tile)
+    x, w, b = si.integer_case("3d", N, Ci, Co, H, W, D=D, dtype=dt,
+                              seed=700 + CASES_SK.index(case), device=DEV)
+    op = Conv3x3x3(w, b, N, D, H, W, epilogue=epi, algo=C.ALGO_AUTO)
+    op.workspace.fill_(0xA5)   # counters and slots start as garbage: the call clears what it needs
+    ys = []
+    for _ in range(2):         # the second call finds the first one's partials and counters
+        buf, y = alloc_guarded(op.out_shape(), x.dtype)
+        op(x, y)
+        torch.cuda.synchronize()
+        check_guards(buf, y.numel())
+        ys.append(y)
+    assert_bit_exact(ys[0], oracle_3d(x, w, b, epi), x.dtype)
+    assert torch.equal(ys[0].view(torch.int16), ys[1].view(torch.int16))
 
 
 # Spatial stride 2 (H, W halve, frames keep stride 1): the 32x32 family's 128-position tiles

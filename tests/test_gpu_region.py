@@ -174,6 +174,27 @@ def test_region_split_k():
     assert_bit_exact(y, want, x.dtype)
 
 
+def test_region_stream_k():
+    """The stream-K schedule (where the cost model sends 416 -> 300 channels over 5 frames of
+    36 x 78): its stage order counts each output frame's live temporal taps in the region, so a
+    causal first chunk (frames 0 and 1 with one and two taps) and a later chunk with two cached
+    frames (three taps everywhere) divide differently; both on a band of rows at the bottom
+    edge."""
+    N, Ci, Co, T, Hg, W = 1, 416, 300, 10, 38, 78
+    Xall, w, b = si.integer_case("3d", N, Ci, Co, Hg, W, D=T, dtype="bf16", seed=17, device=DEV)
+    want = _causal_reference(Xall, w, b, "relu")
+    lo, rows = 2, 36
+    op = Conv3x3x3(w, b, N, 5, rows, W, epilogue="relu", algo=C.ALGO_AUTO)
+    assert C.conv3x3x3_describe(N, Ci, Co, 5, rows, W).startswith("igemm32_sk ")
+    H_in, h_org, h_lo, h_hi = band_rows(lo, rows, 1, Hg)
+    for t0, cached in ((0, 0), (5, 2)):
+        D_in, d_org, d_lo, d_hi = causal_frames(5, cached)
+        x = _stored_rows(Xall[:, t0 - cached:t0 + 5].contiguous(), lo, rows, 1)
+        _say("region stream-K frames %d..%d cached %d" % (t0, t0 + 5, cached))
+        y = _run(op, x, D_in, H_in, d_org, h_org, d_lo, d_hi, h_lo, h_hi)
+        assert_bit_exact(y, want[:, t0:t0 + 5, lo:lo + rows], x.dtype)
+
+
 def test_full_region_equals_plain_call():
     """conv3x3x3_fwd_region over the full region is conv3x3x3_fwd, bit for bit (random inputs,
     AUTO algorithm: the fused head at C_out = 12)."""

@@ -56,6 +56,17 @@ def test_noalloc_without_workspace_and_split_plane():
         assert_bit_exact(y, oracle_3d(x, w, b, "clamp1"), x.dtype)
 
 
+def test_noalloc_stream_k():
+    # the MFMA path's stream-K schedule: partial tiles and arrival counters in the scratch (the
+    # counters cleared by the call itself), against conv3x3x3_fwd and the oracle
+    x, w, b = si.integer_case("3d", 1, 416, 300, 36, 78, D=5, dtype="bf16", seed=903, device=DEV)
+    assert C.conv3x3x3_describe(1, 416, 300, 5, 36, 78).startswith("igemm32_sk ")
+    op, ref, y = _both(x, w, b, "relu")
+    assert 0 < op.ws_bytes <= C.NOALLOC_SCRATCH_BYTES
+    assert torch.equal(ref.view(torch.int16), y.view(torch.int16))
+    assert_bit_exact(y, oracle_3d(x, w, b, "relu"), x.dtype)
+
+
 def test_noalloc_refuses_more_than_the_scratch():
     N, Ci, Co, D, H, W = 1, 256, 12, 16, 352, 624
     need = C.conv3x3x3_workspace_bytes(N, Ci, Co, D, H, W, algo=C.ALGO_SPLIT_HEAD)

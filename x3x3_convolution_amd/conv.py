@@ -52,7 +52,7 @@ EXPORTS = [
     ("conv3x3x3_describe", _I, [_I] * 10 + [ctypes.c_char_p, _I]),
     ("conv_calib_lds_read", _I, [_P, _I, _I, _I, _P]),
 ]
-NOALLOC_SCRATCH_BYTES = 32 << 20
+NOALLOC_SCRATCH_BYTES = 80 << 20
 
 
 class ConvError(RuntimeError):

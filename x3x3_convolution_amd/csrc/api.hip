@@ -353,7 +353,7 @@ int conv3x3x3_describe(int N, int C_in, int C_out, int D, int H, int W, int stri
                  rp.max_z_rows, rp.workgroups);
     } else {
         const cx::IgemmPlan pl = plan_for(a, N, C_in, C_out, D, H, W, stride);
-        const char *k = pl.family == cx::IG_W32 ? (pl.kq ? "igemm32_kq" : "igemm32")
+        const char *k = pl.family == cx::IG_W32 ? (pl.kq ? "igemm32_kq" : pl.sk ? "igemm32_sk" : "igemm32")
                         : pl.family == cx::IG_WIDE ? "igemm16_wide" : "igemm16_narrow";
         snprintf(tmp, sizeof tmp, "%s tile=%dx%d rows=%d splits=%d workgroups=%lld", k, pl.TH,
                  pl.TW, pl.kq ? 64 : pl.BM, pl.splits, pl.workgroups);
@@ -470,7 +470,7 @@ int fwd3d(const void *x, const void *w_packed, const void *bias, void *y, int N,
     const cx::IgemmPlan pl = cx::plan_igemm(family, N, C_in, C_out, D, H, W, stride);
     cx::IgemmParams ip{};
     ip.x = x, ip.wp = w_packed, ip.bias = bias, ip.y = y;
-    ip.partial = static_cast<float *>(pl.splits > 1 ? workspace : nullptr);
+    ip.partial = static_cast<float *>(pl.splits > 1 || pl.sk ? workspace : nullptr);
     ip.N = N, ip.C_in = C_in, ip.D = D, ip.H = H, ip.W = W, ip.W_in = W_in, ip.rg = rg;
     ip.Cy = C_out, ip.bf16 = bf, ip.epilogue = epilogue;
     const hipError_t e = cx::launch_igemm3d(pl, ip, s);

@@ -46,6 +46,11 @@ struct IgemmKArgs {
     int tiles_h, tiles_w, mtiles;
     uint32_t total_wg;
     uint32_t wp_bytes;   // packed weights (buffer-resource range of the 32x32 kernel)
+    // stream-K (igemm32 with SK): partial slots in `partial`, one arrival counter per tile
+    unsigned *sk_count;
+    int sk_groups;       // workgroups (a multiple of 8)
+    uint32_t sk_total;   // stages in the stream-K order
+    int sk_unit_stages;  // stages of one (output-row tile, sample, spatial tile) over all frames
 };
 
 // Stores four rows m0..m0+3 of one accumulator column (bias already added): fp32 partials for
@@ -315,6 +320,9 @@ __device__ __forceinline__ void w32_barrier() { asm volatile("s_barrier" ::: "me
 __device__ __forceinline__ void w32_touch(f32x16_t &v) { asm volatile("" : "+a"(v)::"memory"); }
 __device__ constexpr int w32_waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int kW32WaitLgkm0 = 15 | (3 << 14) | (7 << 4);
+// cache-policy operand of the buffer intrinsics: sc1 (device scope)
+constexpr int kCpolSc1 = 16;
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 // Block order.  Workgroups dispatch round-robin over the 8 XCDs (block b to XCD b % 8), each XCD
 // with its own L2.  XCD x takes a contiguous share of the tiles whose frame has all three temporal
@@ -345,217 +353,394 @@ __device__ __forceinline__ uint32_t w32_block_order(uint32_t b, uint32_t total, 
     return le / (uint32_t)D;
 }
 
-template <bool BF, int EPI, bool SPLITK, int LW, int NB, int S>
+// Stream-K order (SK): the stages of all tiles form one list -- output-row tile outermost, then
+// sample and spatial tile, then frame, then the tile's own stages (chunk, live temporal tap) --
+// and logical workgroup g of G takes the stages [g*S/G, (g+1)*S/G) of the S in the list.  Logical
+// workgroups g of one XCD are consecutive (block b runs on XCD b % 8).  Within a spatial tile the
+// frames run in the order 1, 0, 2, 3, ..., D-1 (D >= 3): a three-tap frame, then a two-tap one,
+// so that with G about the number of tiles a range is most of one tile and the end or the start
+// of its neighbour, and the workgroups of an XCD walk K nearly together (their weight stream
+// stays in its L2).
+__device__ __forceinline__ uint32_t sk_bound(uint32_t h, uint32_t total, uint32_t G) {
+    return (uint32_t)((uint64_t)h * total / G);
+}
+// the logical workgroup whose range holds stage xs
+__device__ __forceinline__ uint32_t sk_owner(uint32_t xs, uint32_t total, uint32_t G) {
+    return (uint32_t)(((uint64_t)(xs + 1) * G - 1) / total);
+}
+__host__ __device__ __forceinline__ int sk_frame(int i, int D) { return D >= 3 && i < 2 ? 1 - i : i; }
+
+// SK = false: one workgroup per (tile, K split), as w32_block_order assigns.  SK = true
+// (stream-K): a.sk_groups workgroups, each walking its range of the stream-K order as segments
+// (a tile's stages inside the range); a segment that is a whole tile is stored directly, the
+// pieces of a split tile meet through fp32 partials (see the end of the segment loop).
+template <bool BF, int EPI, bool SPLITK, int LW, int NB, int S, bool SK = false>
 __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
     using E = Elem<BF>;
     using G = W32Geom<LW, NB, S>;
     typedef typename E::vec8 vec8;
     typedef __attribute__((address_space(3))) void lds_void;
+    static_assert(!(SK && SPLITK), "stream-K sums its own pieces");
     __shared__ __attribute__((aligned(16))) uint4 Win0[G::Slots];
     __shared__ __attribute__((aligned(16))) uint4 Win1[G::Slots];
     __shared__ __attribute__((aligned(16))) uint4 Win2[G::Slots];
     __shared__ float bias_s[256];   // this workgroup's 256 output rows (0 past C_out / no bias)
+    __shared__ int sk_last;         // (SK) this workgroup's piece was the last of its tile to end
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int j = lane & 31, hh = lane >> 5;
     const int pr = j / LW, pc = j % LW;      // row / column of lane column j in its block
 
-    int od;
-    uint32_t lin = w32_block_order(blockIdx.x, a.total_wg, a.D, od);
-    const int mt = lin % a.mtiles;
-    lin /= a.mtiles;
-    const int tw = lin % a.tiles_w;
-    lin /= a.tiles_w;
-    const int th = lin % a.tiles_h;
-    lin /= a.tiles_h;
-    const int n = lin % a.N;
-    const int split = lin / a.N;
-
-    const int oh0 = th * G::TH, ow0 = tw * G::TW;
-    const int c_begin = split * a.chunks_per_split;
-    const int c_end = min(a.nchunks, c_begin + a.chunks_per_split);
-    // live temporal taps: input frame fi0 + kd inside [d_lo, d_hi)
-    const int fi0 = od + a.d_org - 1;
-    const int kd_lo = max(0, a.d_lo - fi0);
-    const int kd_hi = min(2, a.d_hi - 1 - fi0);
-    const int nkd = max(0, kd_hi - kd_lo + 1);
-    const int nst = max(0, (c_end - c_begin) * nkd);
-    const int mbase = mt * 256 + wave * 64;       // this wave's first GEMM row
-    const bool mlive = mbase < a.Mrows;           // (all-padding waves compute zeros, store none)
-
     const size_t frame_elems = (size_t)a.H_in * a.W_in * a.C_in;
     const uint32_t frame_bytes = (uint32_t)(frame_elems * 2);
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
         (void *)a.wp, (short)0, (int)(a.wp_bytes), 0x00020000);
 
-    auto stage_coords = [&](int s, int &cc, int &kd) {
-        cc = c_begin + s / nkd;
-        kd = kd_lo + s % nkd;
-    };
-    // Window copies: this wave issues copies k = wave + 4*t; lane i of copy k fills slot 64k + i
-    // = position 16k + i/4 (row, column = position / RowPos, % RowPos), piece (i%4) ^
-    // ((column/4) % 4).
-    // The source offsets are recomputed per stage (a few ALU operations) rather than kept live.
-    auto copy_window = [&](int s, uint4 *dst) {
-        int cc, kd;
-        stage_coords(s, cc, kd);
-        const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(a.x + ((size_t)n * a.D_in + (fi0 + kd)) * frame_elems), (short)0,
-            (int)frame_bytes, 0x00020000);
-#pragma unroll
-        for (int t = 0; t < G::CopiesPerWave; ++t) {
-            const int k = wave + 4 * t;
-            if (G::Copies % 4 != 0 && k >= G::Copies) break;   // wave-uniform
-            const int pos = 16 * k + (lane >> 2);
-            const int wh = pos / G::RowPos, ww = pos - wh * G::RowPos;
-            const int piece = (lane & 3) ^ ((ww >> 2) & 3);
-            // LDS column ww holds window column cw (input column S*ow0 - 1 + cw)
-            const bool odd = S == 2 && ww >= G::OddBase;
-            const int cw = S == 1 ? ww : (odd ? 2 * (ww - G::OddBase) + 1 : 2 * ww);
-            const bool col_used = S == 1 ? ww < G::WW : (odd ? ww - G::OddBase < G::TW : ww < G::WW);
-            const int h = S * oh0 - 1 + wh + a.h_org, w = S * ow0 - 1 + cw;
-            const bool ok = col_used && pos < G::Pos && h >= a.h_lo && h < a.h_hi &&
-                            (unsigned)w < (unsigned)a.W_in && cc * 32 + 8 * piece < a.C_in;
-            const uint32_t off = ok ? (uint32_t)(((h * a.W_in + w) * a.C_in + cc * 32 + 8 * piece) * 2) : 0xFFFFFFFFu;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)&dst[k * 64], 16, off, 0, 0, 0);
+    // (SK) logical workgroup g and its range [x, x_end) of the stream-K order
+    uint32_t g = 0, x = 0, x_end = 0;
+    if constexpr (SK) {
+        const uint32_t G = (uint32_t)a.sk_groups;   // a multiple of 8
+        g = (blockIdx.x % 8u) * (G / 8u) + blockIdx.x / 8u;
+        x = sk_bound(g, a.sk_total, G);
+        x_end = sk_bound(g + 1, a.sk_total, G);
+    }
+#pragma unroll 1
+    for (;;) {
+        int od, mt, n, th, tw, split = 0, kd_lo, nkd, sbase, nst;
+        uint32_t t0 = 0, tile_len = 0, seg_hi = 0, tile_id = 0;   // (SK) the segment's tile
+        if constexpr (SK) {
+            if (x >= x_end) break;
+            const uint32_t u = x / (uint32_t)a.sk_unit_stages;
+            const uint32_t rem = x - u * (uint32_t)a.sk_unit_stages;
+            // the frame whose stages hold rem (every frame has at least one live tap)
+            uint32_t cum = 0;
+            od = -1, kd_lo = 0, nkd = 0;
+            for (int i = 0; i < a.D; ++i) {
+                const int f = sk_frame(i, a.D);
+                const int fi = f + a.d_org - 1;
+                const int lo = max(0, a.d_lo - fi), hi = min(2, a.d_hi - 1 - fi);
+                const uint32_t st = (uint32_t)(a.nchunks * max(0, hi - lo + 1));
+                if (rem < cum + st) {
+                    od = f, kd_lo = lo, nkd = hi - lo + 1, tile_len = st;
+                    break;
+                }
+                cum += st;
+            }
+            if (od < 0) break;   // (not reached: the host sizes the order from the same taps)
+            sbase = (int)(rem - cum);
+            t0 = x - (uint32_t)sbase;
+            seg_hi = min(tile_len, x_end - t0);
+            nst = (int)seg_hi - sbase;
+            const uint32_t nsp = (uint32_t)a.N * a.tiles_h * a.tiles_w;
+            mt = (int)(u / nsp);
+            uint32_t sp = u - (uint32_t)mt * nsp;
+            tw = (int)(sp % (uint32_t)a.tiles_w);
+            sp /= (uint32_t)a.tiles_w;
+            th = (int)(sp % (uint32_t)a.tiles_h);
+            n = (int)(sp / (uint32_t)a.tiles_h);
+            tile_id = u * (uint32_t)a.D + (uint32_t)od;
+        } else {
+            uint32_t lin = w32_block_order(blockIdx.x, a.total_wg, a.D, od);
+            mt = lin % a.mtiles;
+            lin /= a.mtiles;
+            tw = lin % a.tiles_w;
+            lin /= a.tiles_w;
+            th = lin % a.tiles_h;
+            lin /= a.tiles_h;
+            n = lin % a.N;
+            split = lin / a.N;
+            const int c_begin = split * a.chunks_per_split;
+            const int c_end = min(a.nchunks, c_begin + a.chunks_per_split);
+            // live temporal taps: input frame fi0 + kd inside [d_lo, d_hi)
+            const int fi = od + a.d_org - 1;
+            kd_lo = max(0, a.d_lo - fi);
+            const int kd_hi = min(2, a.d_hi - 1 - fi);
+            nkd = max(0, kd_hi - kd_lo + 1);
+            sbase = c_begin * nkd;
+            nst = max(0, (c_end - c_begin) * nkd);
         }
-    };
-    // weight fragments of slice q (tap q/2, k half q%2) of the stage whose first slice starts at
-    // scalar offset sb: 2 blocks of 32 rows; the per-lane part of the offset is fixed
-    const uint32_t alane = (uint32_t)((mbase + j) * 32 + 16 * hh);
-    auto stage_abase = [&](int s) {
-        int cc, kd;
-        stage_coords(s, cc, kd);
-        return (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(cc * 27 + kd * 9) * 2u * a.Mpad * 32u));
-    };
-    const uint32_t slice_bytes = (uint32_t)a.Mpad * 32u;   // one k16 slice of all rows
-    auto load_a = [&](uint32_t sb, int q, vec8 (&dst)[2]) {
-        const uint32_t sbase = sb + (uint32_t)q * slice_bytes;
+
+        const int oh0 = th * G::TH, ow0 = tw * G::TW;
+        const int fi0 = od + a.d_org - 1;
+        const int mbase = mt * 256 + wave * 64;       // this wave's first GEMM row
+        const bool mlive = mbase < a.Mrows;           // (all-padding waves compute zeros, store none)
+
+        // stage s of this segment is stage sbase + s of its tile: chunk t / nkd, temporal tap
+        // kd_lo + t % nkd
+        auto stage_coords = [&](int s, int &cc, int &kd) {
+            const int t = sbase + s;
+            cc = t / nkd;
+            kd = kd_lo + t % nkd;
+        };
+        // Window copies: this wave issues copies k = wave + 4*t; lane i of copy k fills slot 64k + i
+        // = position 16k + i/4 (row, column = position / RowPos, % RowPos), piece (i%4) ^
+        // ((column/4) % 4).
+        // The source offsets are recomputed per stage (a few ALU operations) rather than kept live.
+        auto copy_window = [&](int s, uint4 *dst) {
+            int cc, kd;
+            stage_coords(s, cc, kd);
+            const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(a.x + ((size_t)n * a.D_in + (fi0 + kd)) * frame_elems), (short)0,
+                (int)frame_bytes, 0x00020000);
+#pragma unroll
+            for (int t = 0; t < G::CopiesPerWave; ++t) {
+                const int k = wave + 4 * t;
+                if (G::Copies % 4 != 0 && k >= G::Copies) break;   // wave-uniform
+                const int pos = 16 * k + (lane >> 2);
+                const int wh = pos / G::RowPos, ww = pos - wh * G::RowPos;
+                const int piece = (lane & 3) ^ ((ww >> 2) & 3);
+                // LDS column ww holds window column cw (input column S*ow0 - 1 + cw)
+                const bool odd = S == 2 && ww >= G::OddBase;
+                const int cw = S == 1 ? ww : (odd ? 2 * (ww - G::OddBase) + 1 : 2 * ww);
+                const bool col_used = S == 1 ? ww < G::WW : (odd ? ww - G::OddBase < G::TW : ww < G::WW);
+                const int h = S * oh0 - 1 + wh + a.h_org, w = S * ow0 - 1 + cw;
+                const bool ok = col_used && pos < G::Pos && h >= a.h_lo && h < a.h_hi &&
+                                (unsigned)w < (unsigned)a.W_in && cc * 32 + 8 * piece < a.C_in;
+                const uint32_t off = ok ? (uint32_t)(((h * a.W_in + w) * a.C_in + cc * 32 + 8 * piece) * 2) : 0xFFFFFFFFu;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)&dst[k * 64], 16, off, 0, 0, 0);
+            }
+        };
+        // weight fragments of slice q (tap q/2, k half q%2) of the stage whose first slice starts at
+        // scalar offset sb: 2 blocks of 32 rows; the per-lane part of the offset is fixed
+        const uint32_t alane = (uint32_t)((mbase + j) * 32 + 16 * hh);
+        auto stage_abase = [&](int s) {
+            int cc, kd;
+            stage_coords(s, cc, kd);
+            return (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(cc * 27 + kd * 9) * 2u * a.Mpad * 32u));
+        };
+        const uint32_t slice_bytes = (uint32_t)a.Mpad * 32u;   // one k16 slice of all rows
+        auto load_a = [&](uint32_t sb, int q, vec8 (&dst)[2]) {
+            const uint32_t sbase = sb + (uint32_t)q * slice_bytes;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+                dst[mb] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(
+                    wr, alane + mb * 1024u, sbase, 0));
+        };
+        // B fragment of slice q, block nb (rows R*nb .. +R-1 of the tile) from a window
+        // buffer: a per-lane slot for (kx, k half) -- six values -- plus a compile-time row offset
+        int lslot[3][2];
+#pragma unroll
+        for (int kx = 0; kx < 3; ++kx)
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                const int col = S == 1 ? pc + kx : (kx == 1 ? G::OddBase + pc : pc + kx / 2);
+                lslot[kx][k2] = w32_slot<G::RowPos>(S * pr, col, 2 * k2 + hh);
+            }
+        auto read_b = [&](const uint4 *win, int q, int nb) {
+            const int tap = q / 2, ky = tap / 3, kx = tap % 3;
+            return __builtin_bit_cast(vec8, win[lslot[kx][q % 2] + (S * G::R * nb + ky) * (G::RowPos * 4)]);
+        };
+
+        // (every launched workgroup has at least one stage: splits are never empty and every
+        // output frame has a live temporal tap)
+        f32x16_t acc[2][G::NB];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
-            dst[mb] = __builtin_bit_cast(vec8, __builtin_amdgcn_raw_buffer_load_b128(
-                wr, alane + mb * 1024u, sbase, 0));
-    };
-    // B fragment of slice q, block nb (rows R*nb .. +R-1 of the tile) from a window
-    // buffer: a per-lane slot for (kx, k half) -- six values -- plus a compile-time row offset
-    int lslot[3][2];
 #pragma unroll
-    for (int kx = 0; kx < 3; ++kx)
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-            const int col = S == 1 ? pc + kx : (kx == 1 ? G::OddBase + pc : pc + kx / 2);
-            lslot[kx][k2] = w32_slot<G::RowPos>(S * pr, col, 2 * k2 + hh);
+            for (int nb = 0; nb < G::NB; ++nb) {
+                acc[mb][nb] = f32x16_t{};
+                w32_touch(acc[mb][nb]);   // keeps the accumulators in AGPRs from the start
+            }
+        vec8 aq[kW32PD][2];
+        vec8 bq[2][G::NB];
+
+        {
+            const int m = mt * 256 + threadIdx.x;
+            bias_s[threadIdx.x] = (!SPLITK && a.bias != nullptr && m < a.Mrows) ? E::to_f32(a.bias[m]) : 0.f;
         }
-    auto read_b = [&](const uint4 *win, int q, int nb) {
-        const int tap = q / 2, ky = tap / 3, kx = tap % 3;
-        return __builtin_bit_cast(vec8, win[lslot[kx][q % 2] + (S * G::R * nb + ky) * (G::RowPos * 4)]);
-    };
+        copy_window(0, Win0);
+        if (nst > 1) copy_window(1, Win1);
+        if (nst > 2) copy_window(2, Win2);
+        uint32_t sb_cur = stage_abase(0);
+#pragma unroll
+        for (int q = 0; q < kW32PD; ++q) load_a(sb_cur, q, aq[q]);
+        // windows 0..2 complete: younger than them are only the weight loads
+        __builtin_amdgcn_s_waitcnt(w32_waitcnt_vm(kW32PD * 2));
+        w32_barrier();
+#pragma unroll
+        for (int nb = 0; nb < G::NB; ++nb) bq[0][nb] = read_b(Win0, 0, nb);
 
-    // (every launched workgroup has at least one stage: splits are never empty and every
-    // output frame has a live temporal tap)
-    f32x16_t acc[2][G::NB];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < G::NB; ++nb) {
-            acc[mb][nb] = f32x16_t{};
-            w32_touch(acc[mb][nb]);   // keeps the accumulators in AGPRs from the start
-        }
-    vec8 aq[kW32PD][2];
-    vec8 bq[2][G::NB];
-
-    {
-        const int m = mt * 256 + threadIdx.x;
-        bias_s[threadIdx.x] = (!SPLITK && a.bias != nullptr && m < a.Mrows) ? E::to_f32(a.bias[m]) : 0.f;
-    }
-    copy_window(0, Win0);
-    if (nst > 1) copy_window(1, Win1);
-    if (nst > 2) copy_window(2, Win2);
-    uint32_t sb_cur = stage_abase(0);
-#pragma unroll
-    for (int q = 0; q < kW32PD; ++q) load_a(sb_cur, q, aq[q]);
-    // windows 0..2 complete: younger than them are only the weight loads
-    __builtin_amdgcn_s_waitcnt(w32_waitcnt_vm(kW32PD * 2));
-    w32_barrier();
-#pragma unroll
-    for (int nb = 0; nb < G::NB; ++nb) bq[0][nb] = read_b(Win0, 0, nb);
-
-    // Stage s computes from window buffer s % 3.  Window s+1 is complete for every wave from the
-    // barrier that ends stage s-1 on, so the last slice of stage s already reads the first
-    // fragments of stage s+1 and the MFMA pipe runs through the stage boundary.  The barrier that
-    // ends stage s says every wave is done with window s (its buffer then takes window s+3) and
-    // has its own copies of window s+2 complete.
+        // Stage s computes from window buffer s % 3.  Window s+1 is complete for every wave from the
+        // barrier that ends stage s-1 on, so the last slice of stage s already reads the first
+        // fragments of stage s+1 and the MFMA pipe runs through the stage boundary.  The barrier that
+        // ends stage s says every wave is done with window s (its buffer then takes window s+3) and
+        // has its own copies of window s+2 complete.
 #pragma unroll 1
-    for (int s0 = 0; s0 < nst; s0 += 3) {
+        for (int s0 = 0; s0 < nst; s0 += 3) {
 #pragma unroll
-        for (int third = 0; third < 3; ++third) {
-            const int s = s0 + third;
-            if (third > 0 && s >= nst) break;              // uniform
-            uint4 *const cur = third == 0 ? Win0 : third == 1 ? Win1 : Win2;
-            uint4 *const nxt = third == 0 ? Win1 : third == 1 ? Win2 : Win0;
-            const bool more = s + 1 < nst;
-            // weights of the next stage (a stage past the last re-reads this one's, never used)
-            const uint32_t sb_next = more ? stage_abase(s + 1) : sb_cur;
+            for (int third = 0; third < 3; ++third) {
+                const int s = s0 + third;
+                if (third > 0 && s >= nst) break;              // uniform
+                uint4 *const cur = third == 0 ? Win0 : third == 1 ? Win1 : Win2;
+                uint4 *const nxt = third == 0 ? Win1 : third == 1 ? Win2 : Win0;
+                const bool more = s + 1 < nst;
+                // weights of the next stage (a stage past the last re-reads this one's, never used)
+                const uint32_t sb_next = more ? stage_abase(s + 1) : sb_cur;
 #pragma unroll
-            for (int q = 0; q < kW32Slices; ++q) {
-                const int cb = q & 1;
-                if (q + 1 < kW32Slices) {
+                for (int q = 0; q < kW32Slices; ++q) {
+                    const int cb = q & 1;
+                    if (q + 1 < kW32Slices) {
 #pragma unroll
-                    for (int nb = 0; nb < G::NB; ++nb) bq[cb ^ 1][nb] = read_b(cur, q + 1, nb);
-                } else {
-                    // (after the last stage these reads are of a stale buffer and never used;
-                    // issuing them anyway keeps the wait counts the same on every path)
+                        for (int nb = 0; nb < G::NB; ++nb) bq[cb ^ 1][nb] = read_b(cur, q + 1, nb);
+                    } else {
+                        // (after the last stage these reads are of a stale buffer and never used;
+                        // issuing them anyway keeps the wait counts the same on every path)
 #pragma unroll
-                    for (int nb = 0; nb < G::NB; ++nb) bq[cb ^ 1][nb] = read_b(nxt, 0, nb);
+                        for (int nb = 0; nb < G::NB; ++nb) bq[cb ^ 1][nb] = read_b(nxt, 0, nb);
+                    }
+                    // the next slice's reads go out before this slice's MFMAs (left to itself the
+                    // scheduler sinks them behind the MFMAs and single-buffers the fragments)
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                        for (int nb = 0; nb < G::NB; ++nb)
+                            acc[mb][nb] = E::mfma32x32x16(aq[q % kW32PD][mb], bq[cb][nb], acc[mb][nb]);
+                    // refill the ring slot with the slice kW32PD ahead (in the next stage when past
+                    // this one)
+                    if (q + kW32PD < kW32Slices) load_a(sb_cur, q + kW32PD, aq[q % kW32PD]);
+                    else load_a(sb_next, q + kW32PD - kW32Slices, aq[q % kW32PD]);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                // the next slice's reads go out before this slice's MFMAs (left to itself the
-                // scheduler sinks them behind the MFMAs and single-buffers the fragments)
-                __builtin_amdgcn_sched_barrier(0);
+                if (more) {
+                    // own copies of window s+2 complete: they were issued after the previous
+                    // barrier, and only this stage's weight loads (2 per slice) came after them
+                    __builtin_amdgcn_s_waitcnt(w32_waitcnt_vm(2 * kW32Slices));
+                    __builtin_amdgcn_s_waitcnt(kW32WaitLgkm0);
+                    w32_barrier();
+                    if (s + 3 < nst) copy_window(s + 3, cur);
+                }
+                sb_cur = sb_next;
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(w32_waitcnt_vm(0));
+
+        const size_t P = (size_t)a.N * a.D * a.H * a.W;
+        if (!SK || (sbase == 0 && seg_hi == tile_len)) {   // a whole tile: store it
+#pragma unroll
+            for (int nb = 0; nb < G::NB; ++nb) {
+                const int oh = oh0 + G::R * nb + pr, ow = ow0 + pc;
+                const bool inside = oh < a.H && ow < a.W;
+                const size_t pos = (((size_t)n * a.D + od) * a.H + oh) * a.W + ow;
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb) {
+                    w32_touch(acc[mb][nb]);
+                    if (inside && mlive) {
+#pragma unroll
+                        for (int gq = 0; gq < 4; ++gq) {
+                            const f32x16_t v = acc[mb][nb];
+                            const int m0 = mbase + mb * 32 + 8 * gq + 4 * hh;
+                            const float4 bv = *reinterpret_cast<const float4 *>(&bias_s[m0 - mt * 256]);
+                            store_rows<BF, EPI, SPLITK>(a, f32x4_t{v[4 * gq] + bv.x, v[4 * gq + 1] + bv.y,
+                                                                  v[4 * gq + 2] + bv.z, v[4 * gq + 3] + bv.w},
+                                                       pos, split, P, m0);
+                        }
+                    }
+                }
+            }
+        } else if constexpr (SK) {
+            // A piece of a split tile.  The tile's pieces are held by logical workgroups gf .. gl in
+            // K order; each writes its fp32 partial tile to a slot of its own (slot 1 of gf -- the
+            // piece that starts the tile is the last segment of its workgroup -- and slot 0 of every
+            // later one, for which it is the first segment), then takes a ticket from the tile's
+            // arrival counter.  The piece that draws the last ticket sums the np pieces in K order
+            // -- its own from registers, the others from their slots -- so the sum does not depend
+            // on which piece ends last, adds the bias, applies the epilogue and stores.  The
+            // counters are cleared before the launch.
+            // Coherence across XCDs (each has its own L2) without flushing or invalidating the L2s
+            // (their weight and window lines are what the other workgroups run on): the partial
+            // tiles are written and read with device-scope accesses (sc1, write-through /
+            // coherent read, as relaxed device-scope atomics are), a piece's stores are complete
+            // (vmcnt 0) before its ticket is taken, and the ticket is a device-scope atomic.
+            constexpr int kChunks = 2 * G::NB * 4;   // 16-byte parts of a lane's accumulators
+            constexpr uint32_t kSlotBytes = kChunks * 256 * 16;
+            const uint32_t ng = (uint32_t)a.sk_groups;
+            const uint32_t gf = sk_owner(t0, a.sk_total, ng), gl = sk_owner(t0 + tile_len - 1, a.sk_total, ng);
+            const int np = (int)(gl - gf) + 1, me = (int)(g - gf);
+            const __amdgpu_buffer_rsrc_t pr_rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)a.partial, (short)0, (int)(2 * ng * kSlotBytes), 0x00020000);
+            // byte offset of this thread's part c of piece p's slot
+            auto slot_off = [&](int p, int c) {
+                return ((gf + (uint32_t)p) * 2u + (p == 0 ? 1u : 0u)) * kSlotBytes +
+                       (uint32_t)(c * 256 + (int)threadIdx.x) * 16u;
+            };
+            if (mlive) {
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                    for (int nb = 0; nb < G::NB; ++nb)
-                        acc[mb][nb] = E::mfma32x32x16(aq[q % kW32PD][mb], bq[cb][nb], acc[mb][nb]);
-                // refill the ring slot with the slice kW32PD ahead (in the next stage when past
-                // this one)
-                if (q + kW32PD < kW32Slices) load_a(sb_cur, q + kW32PD, aq[q % kW32PD]);
-                else load_a(sb_next, q + kW32PD - kW32Slices, aq[q % kW32PD]);
-                __builtin_amdgcn_sched_barrier(0);
+                    for (int nb = 0; nb < G::NB; ++nb) {
+                        w32_touch(acc[mb][nb]);
+                        const f32x16_t v = acc[mb][nb];
+#pragma unroll
+                        for (int gq = 0; gq < 4; ++gq)
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                __builtin_bit_cast(u32x4_t, f32x4_t{v[4 * gq], v[4 * gq + 1], v[4 * gq + 2], v[4 * gq + 3]}),
+                                pr_rs, slot_off(me, (mb * G::NB + nb) * 4 + gq), 0, kCpolSc1);
+                    }
             }
-            if (more) {
-                // own copies of window s+2 complete: they were issued after the previous
-                // barrier, and only this stage's weight loads (2 per slice) came after them
-                __builtin_amdgcn_s_waitcnt(w32_waitcnt_vm(2 * kW32Slices));
-                __builtin_amdgcn_s_waitcnt(kW32WaitLgkm0);
-                w32_barrier();
-                if (s + 3 < nst) copy_window(s + 3, cur);
-            }
-            sb_cur = sb_next;
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(w32_waitcnt_vm(0));
-
-    const size_t P = (size_t)a.N * a.D * a.H * a.W;
+            __builtin_amdgcn_s_waitcnt(w32_waitcnt_vm(0));
+            __syncthreads();
+            if (threadIdx.x == 0)
+                sk_last = __hip_atomic_fetch_add(a.sk_count + tile_id, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(np - 1);
+            __syncthreads();
+            if (__builtin_amdgcn_readfirstlane(sk_last)) {
+                if (mlive) {
 #pragma unroll
-    for (int nb = 0; nb < G::NB; ++nb) {
-        const int oh = oh0 + G::R * nb + pr, ow = ow0 + pc;
-        const bool inside = oh < a.H && ow < a.W;
-        const size_t pos = (((size_t)n * a.D + od) * a.H + oh) * a.W + ow;
+                    for (int mb = 0; mb < 2; ++mb) {
+                        f32x4_t sum[G::NB][4] = {};
+                        // pieces before this one, then this one, then the pieces after it
+                        auto add_slot = [&](int p) {
+                            f32x4_t ld[G::NB][4];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            w32_touch(acc[mb][nb]);
-            if (inside && mlive) {
+                            for (int nb = 0; nb < G::NB; ++nb)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x16_t v = acc[mb][nb];
-                    const int m0 = mbase + mb * 32 + 8 * g + 4 * hh;
-                    const float4 bv = *reinterpret_cast<const float4 *>(&bias_s[m0 - mt * 256]);
-                    store_rows<BF, EPI, SPLITK>(a, f32x4_t{v[4 * g] + bv.x, v[4 * g + 1] + bv.y,
-                                                          v[4 * g + 2] + bv.z, v[4 * g + 3] + bv.w},
-                                               pos, split, P, m0);
+                                for (int gq = 0; gq < 4; ++gq)
+                                    ld[nb][gq] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                        pr_rs, slot_off(p, (mb * G::NB + nb) * 4 + gq), 0, kCpolSc1));
+#pragma unroll
+                            for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+                                for (int gq = 0; gq < 4; ++gq) sum[nb][gq] = p == 0 ? ld[nb][gq] : sum[nb][gq] + ld[nb][gq];
+                        };
+#pragma unroll 1
+                        for (int p = 0; p < me; ++p) add_slot(p);
+#pragma unroll
+                        for (int nb = 0; nb < G::NB; ++nb) {
+                            w32_touch(acc[mb][nb]);
+                            const f32x16_t v = acc[mb][nb];
+#pragma unroll
+                            for (int gq = 0; gq < 4; ++gq) {
+                                const f32x4_t own = f32x4_t{v[4 * gq], v[4 * gq + 1], v[4 * gq + 2], v[4 * gq + 3]};
+                                sum[nb][gq] = me == 0 ? own : sum[nb][gq] + own;
+                            }
+                        }
+#pragma unroll 1
+                        for (int p = me + 1; p < np; ++p) add_slot(p);
+#pragma unroll
+                        for (int nb = 0; nb < G::NB; ++nb) {
+                            const int oh = oh0 + G::R * nb + pr, ow = ow0 + pc;
+                            if (oh >= a.H || ow >= a.W) continue;
+                            const size_t pos = (((size_t)n * a.D + od) * a.H + oh) * a.W + ow;
+#pragma unroll
+                            for (int gq = 0; gq < 4; ++gq) {
+                                const int m0 = mbase + mb * 32 + 8 * gq + 4 * hh;
+                                const float4 bv = *reinterpret_cast<const float4 *>(&bias_s[m0 - mt * 256]);
+                                const f32x4_t v = sum[nb][gq];
+                                store_rows<BF, EPI, false>(a, f32x4_t{v[0] + bv.x, v[1] + bv.y, v[2] + bv.z, v[3] + bv.w},
+                                                           pos, 0, P, m0);
+                            }
+                        }
+                    }
                 }
             }
+        }
+        if constexpr (!SK) {
+            break;
+        } else {
+            x = t0 + seg_hi;
+            __syncthreads();   // the next segment rewrites bias_s and the window buffers
         }
     }
 }
@@ -908,6 +1093,31 @@ hipError_t launch_w32(const IgemmKArgs &ka, int epi, bool splitk, dim3 grid, hip
     return hipGetLastError();
 }
 
+// Clears the stream-K arrival counters (a kernel, not a memset: the launch pair stays
+// capturable in a graph).
+__global__ __launch_bounds__(256) void sk_clear_kernel(unsigned *count, long long n) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) count[i] = 0u;
+}
+
+template <bool BF, int LW>
+hipError_t launch_sk_tile(const IgemmKArgs &ka, int epi, hipStream_t s) {
+    const dim3 grid((unsigned)ka.sk_groups), block(256);
+    if (epi == EPI_RELU) igemm32_kernel<BF, EPI_RELU, false, LW, 4, 1, true><<<grid, block, 0, s>>>(ka);
+    else if (epi == EPI_CLAMP1) igemm32_kernel<BF, EPI_CLAMP1, false, LW, 4, 1, true><<<grid, block, 0, s>>>(ka);
+    else igemm32_kernel<BF, EPI_NONE, false, LW, 4, 1, true><<<grid, block, 0, s>>>(ka);
+    return hipGetLastError();
+}
+
+// stream-K: stride 1, the 4-block tiles (8 x 16 or 4 x 32)
+template <bool BF>
+hipError_t launch_sk(const IgemmPlan &pl, const IgemmKArgs &ka, int epi, hipStream_t s) {
+    if (pl.splits != 1 || pl.stride != 1 || pl.kq) return hipErrorInvalidValue;
+    if (pl.TW == 16 && pl.TH == 8) return launch_sk_tile<BF, 16>(ka, epi, s);
+    if (pl.TW == 32 && pl.TH == 4) return launch_sk_tile<BF, 32>(ka, epi, s);
+    return hipErrorInvalidValue;
+}
+
 template <bool BF, int LW>
 hipError_t launch_kq(const IgemmKArgs &ka, int epi, dim3 grid, hipStream_t s) {
     const dim3 block(256);
@@ -1002,8 +1212,12 @@ IgemmPlan plan_igemm(int family, int N, int C_in, int C_out, int D, int H, int W
         static const struct { int TH, TW, NB; double cost; } geo[4] = {
             {8, 32, 8, 1.0}, {16, 16, 8, 1.0}, {4, 32, 4, 0.55}, {8, 16, 4, 0.55}};
         const double taps = D >= 3 ? (3.0 * D - 2.0) / D : (D == 2 ? 2.0 : 1.0);
+        const int max_taps = D >= 3 ? 3 : D;
         const double part = (double)N * D * H * W * C_out / 3.75e6;
         double best = -1.0;
+        // the chosen plan's rounds and per-round terms (for its one-round makespan below)
+        long long best_rounds = 0;
+        double best_units = 0.0, best_extra = 0.0;
         for (const auto &g : geo) {
             if (stride == 2 && g.NB != 4) continue;
             const long long th = (H + g.TH - 1) / g.TH, tw = (W + g.TW - 1) / g.TW;
@@ -1013,10 +1227,12 @@ IgemmPlan plan_igemm(int family, int N, int C_in, int C_out, int D, int H, int W
                 const int se = (pl.nchunks + cps - 1) / cps;
                 if (se != sp) continue;
                 const long long rounds = (gbase * se + 255) / 256;
-                const double cost = rounds * (cps * taps * g.cost + 1.0) + (se > 1 ? se * part : 0.0);
+                const double extra = se > 1 ? se * part / rounds : 0.0;
+                const double cost = rounds * (cps * taps * g.cost + 1.0 + extra);
                 if (best < 0 || cost < best - 1e-9) {
                     best = cost, splits = se, pl.kq = 0;
                     pl.TH = g.TH, pl.TW = g.TW, pl.tiles_h = (int)th, pl.tiles_w = (int)tw;
+                    best_rounds = rounds, best_units = cps * g.cost, best_extra = 1.0 + extra;
                 }
             }
             // The same tile with 64 output rows per workgroup and K split over its four waves
@@ -1031,6 +1247,31 @@ IgemmPlan plan_igemm(int family, int N, int C_in, int C_out, int D, int H, int W
                     best = cost, splits = 1;
                     pl.TH = g.TH, pl.TW = g.TW, pl.tiles_h = (int)th, pl.tiles_w = (int)tw;
                     pl.kq = 1;
+                    best_rounds = rounds, best_units = ((pl.nchunks + 3) / 4) * g.cost, best_extra = 1.2;
+                }
+            }
+        }
+        // Stream-K (igemm32_kernel<..., SK>) on the 4-block tiles, one workgroup per tile (the
+        // count rounded up to a multiple of 8, at most one round): the workgroups take equal
+        // shares of all tiles' stages, so the makespan is the average tile, where a plan that
+        // runs in one round ends with its longest workgroups -- the interior frames' three
+        // temporal taps, not the average the costs above use.  About 3.5 stages of overhead:
+        // more prologues, the partials' round trip and the launch that clears the counters.
+        // Stride 1.
+        if (stride == 1 && best > 0) {
+            double made = best_rounds == 1 ? best_units * max_taps + best_extra : best;
+            const long long frame_taps = D >= 3 ? 3LL * D - 2 : (D == 2 ? 4 : 1);
+            for (const auto &g : geo) {
+                if (g.NB != 4) continue;
+                const long long th = (H + g.TH - 1) / g.TH, tw = (W + g.TW - 1) / g.TW;
+                const long long tiles = (long long)N * D * th * tw * pl.mtiles;
+                const long long G = (tiles + 7) / 8 * 8;
+                const long long total = (long long)N * th * tw * pl.mtiles * pl.nchunks * frame_taps;
+                if (G > (long long)kSkMaxGroups || total >= (1LL << 31)) continue;
+                const double cost = (double)((total + G - 1) / G) * g.cost + 3.5;
+                if (cost < made - 1e-9) {
+                    made = cost, splits = 1, pl.kq = 0, pl.sk = (int)G;
+                    pl.TH = g.TH, pl.TW = g.TW, pl.tiles_h = (int)th, pl.tiles_w = (int)tw;
                 }
             }
         }
@@ -1042,7 +1283,8 @@ IgemmPlan plan_igemm(int family, int N, int C_in, int C_out, int D, int H, int W
     }
     pl.chunks_per_split = (pl.nchunks + splits - 1) / splits;
     pl.splits = (pl.nchunks + pl.chunks_per_split - 1) / pl.chunks_per_split;
-    pl.workgroups = (long long)N * D * pl.tiles_h * pl.tiles_w * pl.mtiles * pl.splits;
+    pl.workgroups = pl.sk ? (long long)pl.sk
+                          : (long long)N * D * pl.tiles_h * pl.tiles_w * pl.mtiles * pl.splits;
     return pl;
 }
 
@@ -1050,7 +1292,15 @@ size_t packed_bytes(const IgemmPlan &pl) {
     return (size_t)pl.nchunks * pl.ntaps * pl.Mpad * 32 * sizeof(u16);
 }
 
+// Stream-K: two partial slots per workgroup (the 4-block tile's 256 rows x 128 positions in
+// fp32, 128 KiB each), then one arrival counter per tile.
+static size_t sk_slots_bytes(const IgemmPlan &pl) { return (size_t)pl.sk * 2 * (2 * 4 * 4 * 256) * 16; }
+static long long sk_tiles(const IgemmPlan &pl, int N, int D) {
+    return (long long)N * pl.tiles_h * pl.tiles_w * pl.mtiles * D;
+}
+
 size_t splitk_workspace_bytes(const IgemmPlan &pl, int N, int D, int H, int W, int C_out) {
+    if (pl.sk) return sk_slots_bytes(pl) + (size_t)sk_tiles(pl, N, D) * sizeof(unsigned);
     if (pl.splits <= 1) return 0;
     return (size_t)pl.splits * N * D * H * W * C_out * sizeof(float);
 }
@@ -1070,6 +1320,30 @@ hipError_t launch_igemm3d(const IgemmPlan &pl, const IgemmParams &p, hipStream_t
     ka.tiles_h = pl.tiles_h, ka.tiles_w = pl.tiles_w, ka.mtiles = pl.mtiles;
     ka.total_wg = (uint32_t)pl.workgroups;
     ka.wp_bytes = (uint32_t)packed_bytes(pl);
+    if (pl.sk) {
+        // the stream-K order's length: every (output-row tile, sample, spatial tile) has the
+        // live temporal taps of each output frame times the chunks
+        long long unit = 0;
+        for (int od = 0; od < p.D; ++od) {
+            const int fi = od + p.rg.d_org - 1;
+            const int lo = fi < p.rg.d_lo ? p.rg.d_lo - fi : 0;
+            const int hi = p.rg.d_hi - 1 - fi < 2 ? p.rg.d_hi - 1 - fi : 2;
+            if (hi < lo) return hipErrorInvalidValue;   // (the region checks rule this out)
+            unit += (long long)pl.nchunks * (hi - lo + 1);
+        }
+        const long long tiles = sk_tiles(pl, p.N, p.D);
+        const long long total = unit * (tiles / p.D);
+        if (p.partial == nullptr || total <= 0 || total >= (1LL << 31) || unit >= (1LL << 31))
+            return hipErrorInvalidValue;
+        ka.sk_count = reinterpret_cast<unsigned *>(reinterpret_cast<char *>(p.partial) + sk_slots_bytes(pl));
+        ka.sk_groups = pl.sk;
+        ka.sk_total = (uint32_t)total;
+        ka.sk_unit_stages = (int)unit;
+        sk_clear_kernel<<<dim3((unsigned)((tiles + 255) / 256)), dim3(256), 0, stream>>>(ka.sk_count, tiles);
+        const hipError_t e = p.bf16 ? launch_sk<true>(pl, ka, p.epilogue, stream)
+                                    : launch_sk<false>(pl, ka, p.epilogue, stream);
+        return e;
+    }
     const bool splitk = pl.splits > 1;
     hipError_t e = p.bf16 ? launch_igemm_dtype<true>(pl, ka, p.epilogue, splitk, stream)
                           : launch_igemm_dtype<false>(pl, ka, p.epilogue, splitk, stream);

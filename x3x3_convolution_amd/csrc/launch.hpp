@@ -63,7 +63,13 @@ struct IgemmPlan {
     long long workgroups;
     int stride;        // spatial stride (2: the 32x32 family's 128-position tiles only)
     int kq;            // 32x32 family: 1 = 64-row tiles whose four waves split K (no partials)
+    int sk;            // 32x32 family: > 0 = stream-K with this many workgroups (they share the
+                       // stages of all tiles evenly; split tiles meet through fp32 partials in the
+                       // workspace), 0 = off
 };
+
+// Most workgroups of a stream-K launch: one round on the chip's 256 compute units.
+constexpr int kSkMaxGroups = 256;
 
 // Plans the MFMA launch (tile family, split-K) for a request over the output extent (D, H, W).
 // Pure host arithmetic.
