@@ -92,6 +92,13 @@ CASES_3D_INT = [
     (1, 64, 130, 4, 9, 17, "f16", "none", C.ALGO_MFMA),
     (1, 8, 12, 16, 128, 128, "bf16", "clamp1", C.ALGO_MFMA),     # no split-K, narrow tiles
     (1, 8, 129, 16, 64, 64, "bf16", "relu", C.ALGO_MFMA),        # no split-K, wide tiles
+    # the direct head's 64-channel stages: K split to one chunk per workgroup (the stage's second
+    # chunk empty), five chunks of which the last holds 8 channels, 24 channels (three pieces of
+    # one chunk), and 136 channels split 3 + 2 chunks (a full pair, a half pair, a full pair)
+    (1, 256, 12, 3, 20, 70, "bf16", "relu", C.ALGO_MFMA),
+    (1, 136, 7, 4, 9, 33, "f16", "none", C.ALGO_MFMA),
+    (2, 24, 16, 2, 17, 40, "bf16", "clamp1", C.ALGO_MFMA),
+    (1, 136, 12, 16, 64, 128, "bf16", "relu", C.ALGO_MFMA),
     (1, 32, 12, 3, 9, 50, "bf16", "clamp1", C.ALGO_SPLIT_HEAD),
     (2, 64, 5, 1, 7, 130, "bf16", "none", C.ALGO_SPLIT_HEAD),
     (1, 8, 12, 4, 70, 64, "f16", "clamp1", C.ALGO_SPLIT_HEAD),

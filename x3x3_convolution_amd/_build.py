@@ -43,7 +43,8 @@ def build(extra_flags=(), jobs: int = 4) -> str:
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         list(ex.map(lambda so: _compile(so[0], so[1], extra_flags), zip(SOURCES, objs)))
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = ["hipcc", "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+    # (--no-undefined: a kernel whose host stub was not emitted fails here, not at load time)
+    cmd = ["hipcc", "--offload-arch=" + ARCH, "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)

@@ -158,7 +158,8 @@ int family_for(int algo, int C_in, int C_out, int H, int W, int stride) {
     if (algo == CONV_ALGO_SPLIT_HEAD) return cx::IG_TEMPORAL;
     if (algo == CONV_ALGO_FUSED_HEAD) return cx::IG_FUSED;
     if (stride == 2) return cx::IG_W32;
-    if (C_out <= 16) return cx::IG_NARROW;
+    // (the narrow kernel addresses a window of ten input rows through one 32-bit range)
+    if (C_out <= 16 && 10LL * W * C_in * 2 < (1LL << 31)) return cx::IG_NARROW;
     return (long long)H * W * C_in * 2 < (1ll << 31) ? cx::IG_W32 : cx::IG_WIDE;
 }
 

@@ -264,6 +264,242 @@ __global__ __launch_bounds__(256, 2) void igemm3d_kernel(IgemmKArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// The 27-tap convolution for narrow outputs (C_out <= 16: the direct head) on 16x16x32 MFMA.
+// What limits this form is the vector-memory address unit, which costs per cache line touched:
+// a 32-channel slice of a 256-channel position is half a line, and every wave loading its own
+// weight fragments multiplies their lines by four.  So:
+//   * K runs in stages of 64 channels (two 32-channel chunks) of one live temporal tap: a window
+//     position is then a whole 128-byte line, and one LDS-DMA copy (buffer_load ... lds, 16 bytes
+//     per lane, 1 KiB of LDS) moves 8 whole lines.  Window: (TH+2) x (TW+2) = 10 x 34 positions.
+//   * The stage's weights (2 chunks x 9 spatial taps x 16 rows x 32 channels = 18 KiB) are copied
+//     into LDS once per workgroup by the same DMA, instead of once per wave into registers.
+//   * Both live in two buffer sets (separate objects, the stage loop unrolled by two): the copies
+//     of stage s+1 go out one by one between the MFMAs of the first steps of stage s and are
+//     waited for at its end, one barrier per stage.  ~123 KiB of LDS: one workgroup (4 waves)
+//     per CU.
+//   * Wave w owns 4 output rows x 16 columns of the 8 x 32 tile (rows 4*(w/2).., columns
+//     16*(w%2)..): a window fragment of row wr and column shift kx feeds the vertical taps ky of
+//     up to three of its rows, so a wave reads 18 window fragments per 32 channels for 36 MFMAs.
+// LDS layouts (16-byte pieces): window position (row, col) at (row * 34 + col) * 8, its piece p
+// (channels 8p..8p+7 of the stage) in slot p ^ ((col >> 1) & 7) -- any 16 consecutive columns of
+// one piece fall on distinct bank groups; weight fragment (chunk half h, tap t) at (9h + t) * 64,
+// row m's piece p in slot 4m + (p ^ ((m >> 2) & 3)).  The DMA fetches, for each LDS slot, the
+// global piece that belongs there: the permutations stay inside one line, so copies remain whole
+// lines.  Zero padding (rows, columns, channels, the second chunk past the range) is an offset
+// past the buffer range: the copy fetches nothing and writes zeros.
+// Addressing: the window of a stage is one 32-bit buffer range from its first valid input row
+// (at most ten rows of the frame), so frames of any size work.
+constexpr int kNarTH = 8, kNarTW = 32;                   // output tile
+constexpr int kNarRowPos = kNarTW + 2;                   // window row length (even)
+constexpr int kNarPos = (kNarTH + 2) * kNarRowPos;       // 340 window positions
+constexpr int kNarWinCopies = (kNarPos + 7) / 8;         // 43 DMA copies of 8 positions
+constexpr int kNarWinSlots = kNarWinCopies * 64;
+constexpr int kNarACopies = 18;                          // 2 chunks x 9 taps, 1 KiB each
+constexpr int kNarWinPerWave = (kNarWinCopies + 3) / 4;  // 11
+constexpr int kNarAPerWave = (kNarACopies + 3) / 4;      // 5
+constexpr int kNarCopiesPerWave = kNarWinPerWave + kNarAPerWave;   // 16
+constexpr int kNarWaitVm0 = (7 << 4) | (15 << 8);        // s_waitcnt vmcnt(0), nothing else
+
+template <bool BF, int EPI, bool SPLITK>
+__global__ __launch_bounds__(256, 1) void igemm3d_narrow_kernel(IgemmKArgs a) {
+    using E = Elem<BF>;
+    typedef typename E::vec8 vec8;
+    typedef __attribute__((address_space(3))) void lds_void;
+    __shared__ __attribute__((aligned(16))) uint4 Win0[kNarWinSlots];
+    __shared__ __attribute__((aligned(16))) uint4 Win1[kNarWinSlots];
+    __shared__ __attribute__((aligned(16))) uint4 Wa0[kNarACopies * 64];
+    __shared__ __attribute__((aligned(16))) uint4 Wa1[kNarACopies * 64];
+    __shared__ __attribute__((aligned(16))) float bias_s[16];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // frame innermost, as igemm3d_kernel: the three output frames that read an input frame window
+    // run together on one XCD
+    uint32_t lin = xcd_remap(blockIdx.x, a.total_wg);
+    lin /= a.mtiles;   // (one 16-row tile)
+    const int od = lin % a.D;
+    lin /= a.D;
+    const int tw = lin % a.tiles_w;
+    lin /= a.tiles_w;
+    const int th = lin % a.tiles_h;
+    lin /= a.tiles_h;
+    const int n = lin % a.N;
+    const int split = lin / a.N;
+
+    const int oh0 = th * kNarTH, ow0 = tw * kNarTW;
+    const int c_begin = split * a.chunks_per_split;
+    const int c_end = min(a.nchunks, c_begin + a.chunks_per_split);
+    const int fi0 = od + a.d_org - 1;
+    const int kd_lo = max(0, a.d_lo - fi0);
+    const int kd_hi = min(2, a.d_hi - 1 - fi0);
+    const int nkd = max(0, kd_hi - kd_lo + 1);
+    const int npairs = (c_end - c_begin + 1) / 2;
+    const int nst = max(0, npairs * nkd);
+
+    // the window's input rows: oh0 - 1 + h_org + row, valid inside [h_lo, h_hi); the buffer range
+    // starts at the first valid one
+    const int wrow0 = oh0 - 1 + a.h_org;
+    const int hbase = max(a.h_lo, wrow0);
+    const int hlast = min(a.h_hi, wrow0 + kNarTH + 2);   // exclusive
+    const uint32_t row_bytes = (uint32_t)a.W * (uint32_t)a.C_in * 2u;
+    const uint32_t win_range = hlast > hbase ? (uint32_t)(hlast - hbase) * row_bytes : 0u;
+    const size_t frame_elems = (size_t)a.H_in * a.W * a.C_in;
+
+    // per-lane parts of this wave's window copies: copy k = wave + 4t, lane i -> position
+    // 8k + i/8, LDS slot piece i%8 <- global piece (i%8) ^ ((col >> 1) & 7)
+    uint32_t woff[kNarWinPerWave];
+    int wpiece[kNarWinPerWave];
+#pragma unroll
+    for (int t = 0; t < kNarWinPerWave; ++t) {
+        const int k = wave + 4 * t;
+        const int P = 8 * k + (lane >> 3);
+        const int row = P / kNarRowPos, col = P - row * kNarRowPos;
+        const int p = (lane & 7) ^ ((col >> 1) & 7);
+        const int h = wrow0 + row, w = ow0 - 1 + col;
+        const bool ok = k < kNarWinCopies && P < kNarPos && h >= hbase && h < hlast &&
+                        (unsigned)w < (unsigned)a.W;
+        woff[t] = ok ? (uint32_t)(h - hbase) * row_bytes + ((uint32_t)w * a.C_in + 8u * p) * 2u : 0xFFFFFFFFu;
+        wpiece[t] = p;
+    }
+    // per-lane part of the weight copies: row lane/4, slot lane%4 <- piece (lane%4) ^ ((row>>2)&3)
+    const uint32_t alane = (uint32_t)((lane >> 2) * 64 + (((lane & 3) ^ ((lane >> 4) & 3)) * 16));
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)a.wp, (short)0, (int)(a.wp_bytes), 0x00020000);
+
+    // stage s: chunk pair j = s / nkd (chunks cc0, cc0 + 1 of [c_begin, c_end)), temporal tap
+    // kd = kd_lo + s % nkd
+    // The copies of a stage, kNarCopiesPerWave per wave: window copies t < kNarWinPerWave
+    // (copy k = wave + 4t), then weight copies (fragment q = wave + 4u: chunk half q / 9, tap
+    // q % 9).  stage_copies fixes a stage's uniform parts, copy_one issues one copy.
+    struct StageCopies {
+        const u16 *xbase;  // the stage's window rows (their first valid row)
+        int pmax;          // pieces of the stage that hold input channels of the range's chunks
+        uint32_t cdelta;   // byte offset of the stage's first channel in a position
+        uint32_t abase;    // byte offset of fragment (chunk cc0, tap kd*9) in the packing
+        bool second;       // the stage's second chunk lies in the range
+    };
+    auto stage_copies = [&](int s) {
+        StageCopies c;
+        const int j = s / nkd, kd = kd_lo + s % nkd;
+        const int cc0 = c_begin + 2 * j;
+        c.second = cc0 + 1 < c_end;
+        c.pmax = min(c.second ? 8 : 4, (a.C_in - 32 * cc0 + 7) / 8);
+        c.xbase = a.x + (((size_t)n * a.D_in + (fi0 + kd)) * frame_elems + ((size_t)hbase * a.W) * a.C_in);
+        c.cdelta = (uint32_t)cc0 * 64u;   // 32 channels x 2 bytes per chunk
+        c.abase = (uint32_t)((cc0 * 27 + kd * 9) * a.Mpad) * 64u;
+        return c;
+    };
+    auto copy_one = [&](const StageCopies &c, int i, uint4 *win, uint4 *wa) {
+        if (i < kNarWinPerWave) {
+            const int k = wave + 4 * i;
+            if (kNarWinCopies % 4 != 0 && k >= kNarWinCopies) return;   // wave-uniform
+            const uint32_t off = wpiece[i] < c.pmax && woff[i] != 0xFFFFFFFFu ? woff[i] + c.cdelta : 0xFFFFFFFFu;
+            const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)c.xbase, (short)0, (int)win_range, 0x00020000);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)&win[k * 64], 16, off, 0, 0, 0);
+        } else {
+            const int q = wave + 4 * (i - kNarWinPerWave);
+            if (q >= kNarACopies) return;   // wave-uniform
+            const int hq = q / 9, tq = q - 9 * hq;
+            const bool live = hq == 0 || c.second;
+            const uint32_t frag = c.abase + (uint32_t)((hq * 27 + tq) * a.Mpad) * 64u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void *)&wa[q * 64], 16,
+                                                     live ? frag + alane : 0xFFFFFFFFu, 0, 0, 0);
+        }
+    };
+
+    // fragment reads: weight (h, tap) of row lane%16, piece lane/16; window (row, column shift
+    // kx, chunk half h) of column c0 + kx + lane%16, piece 4h + lane/16
+    const int cb = wave & 1, r0 = 4 * (wave >> 1);
+    const int aslot = (lane & 15) * 4 + ((lane >> 4) ^ ((lane >> 2) & 3));
+    int bslot[2][3];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int kx = 0; kx < 3; ++kx) {
+            const int col = 16 * cb + kx + (lane & 15);
+            const int p = 4 * h + (lane >> 4);
+            bslot[h][kx] = (r0 * kNarRowPos + col) * 8 + (p ^ ((col >> 1) & 7));
+        }
+
+    f32x4_t acc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // One stage's MFMAs from (win, wa): 36 steps (chunk half h, window row wrr, column shift kx),
+    // each one window fragment and the MFMAs of the up to three output rows it feeds.  Fragments
+    // are read two steps ahead (a ring of three); the weight fragments of both halves at the
+    // start.  With `next`, the copies of the next stage into (nwin, nwa) go out one after each
+    // of the first 16 steps, between the MFMAs (issued in one burst they hold up the matrix
+    // pipe; issued later they have less of the stage to land).
+    auto compute = [&](const uint4 *win, const uint4 *wa, bool next, const StageCopies &c,
+                       uint4 *nwin, uint4 *nwa) {
+        constexpr int kSteps = 36;
+        auto read_b = [&](int it) {
+            const int h = it / 18, wrr = (it % 18) / 3, kx = it % 3;
+            return __builtin_bit_cast(vec8, win[bslot[h][kx] + wrr * (kNarRowPos * 8)]);
+        };
+        vec8 A[2][9];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int t = 0; t < 9; ++t) A[h][t] = __builtin_bit_cast(vec8, wa[(9 * h + t) * 64 + aslot]);
+        vec8 Bq[3];
+        Bq[0] = read_b(0);
+        Bq[1] = read_b(1);
+#pragma unroll
+        for (int it = 0; it < kSteps; ++it) {
+            const int h = it / 18, wrr = (it % 18) / 3, kx = it % 3;
+            if (it + 2 < kSteps) Bq[(it + 2) % 3] = read_b(it + 2);
+#pragma unroll
+            for (int ky = 0; ky < 3; ++ky) {
+                const int r = wrr - ky;
+                if (r >= 0 && r < 4) acc[r] = E::mfma16x16x32(A[h][ky * 3 + kx], Bq[it % 3], acc[r]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (it < kNarCopiesPerWave && next) copy_one(c, it, nwin, nwa);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    if (tid < 16) bias_s[tid] = (!SPLITK && a.bias != nullptr && tid < a.Mrows) ? E::to_f32(a.bias[tid]) : 0.f;
+    if (nst > 0) {
+        const StageCopies c0 = stage_copies(0);
+#pragma unroll
+        for (int i = 0; i < kNarCopiesPerWave; ++i) copy_one(c0, i, Win0, Wa0);
+    }
+    __builtin_amdgcn_s_waitcnt(kNarWaitVm0);
+    __syncthreads();
+#pragma unroll 1
+    for (int s = 0; s < nst; s += 2) {
+        const StageCopies c1 = stage_copies(s + 1 < nst ? s + 1 : s);
+        compute(Win0, Wa0, s + 1 < nst, c1, Win1, Wa1);
+        __builtin_amdgcn_s_waitcnt(kNarWaitVm0);
+        __syncthreads();
+        if (s + 1 >= nst) break;
+        const StageCopies c2 = stage_copies(s + 2 < nst ? s + 2 : s);
+        compute(Win1, Wa1, s + 2 < nst, c2, Win0, Wa0);
+        __builtin_amdgcn_s_waitcnt(kNarWaitVm0);
+        __syncthreads();
+    }
+
+    const size_t P = (size_t)a.N * a.D * a.H * a.W;
+    const int m0 = 4 * (lane >> 4);
+    const float4 bv = *reinterpret_cast<const float4 *>(&bias_s[m0]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int oh = oh0 + r0 + r, ow = ow0 + 16 * cb + (lane & 15);
+        if (oh >= a.H || ow >= a.W) continue;
+        const size_t pos = (((size_t)n * a.D + od) * a.H + oh) * a.W + ow;
+        store_rows<BF, EPI, SPLITK>(a, f32x4_t{acc[r][0] + bv.x, acc[r][1] + bv.y, acc[r][2] + bv.z,
+                                              acc[r][3] + bv.w},
+                                   pos, split, P, m0);
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
 // The 27-tap convolution for wide outputs (C_out > 16) on v_mfma_f32_32x32x16: one wave per SIMD
 // keeps that pipe full.  Each wave owns a 64 x 256 tile (2 x 8 blocks, all 256 accumulators): per
 // k16 slice it takes two weight fragments from L2 and eight input fragments from LDS, so the four
@@ -1155,8 +1391,14 @@ hipError_t launch_igemm_dtype(const IgemmPlan &pl, const IgemmKArgs &ka, int epi
         }
         case IG_WIDE:
             return launch_family<BF, 4, 4, 2, 2, 8, 16>(pl, ka, epi, splitk, s);
-        case IG_NARROW:
-            return launch_family<BF, 1, 4, 1, 4, 8, 32>(pl, ka, epi, splitk, s);
+        case IG_NARROW: {
+            const dim3 grid((unsigned)pl.workgroups), block(256);
+            if (splitk) igemm3d_narrow_kernel<BF, EPI_NONE, true><<<grid, block, 0, s>>>(ka);
+            else if (epi == EPI_RELU) igemm3d_narrow_kernel<BF, EPI_RELU, false><<<grid, block, 0, s>>>(ka);
+            else if (epi == EPI_CLAMP1) igemm3d_narrow_kernel<BF, EPI_CLAMP1, false><<<grid, block, 0, s>>>(ka);
+            else igemm3d_narrow_kernel<BF, EPI_NONE, false><<<grid, block, 0, s>>>(ka);
+            return hipGetLastError();
+        }
     }
     return hipErrorInvalidValue;
 }

@@ -41,7 +41,8 @@ inline ConvRegion full_region(int D, int H) { return ConvRegion{D, H, 0, 0, 0, D
 // Tile families; the host picks one per request.
 enum IgemmFamily {
     IG_WIDE = 0,   // 128 output rows x 128 positions per workgroup: C_out > 16
-    IG_NARROW = 1, // 16 output rows x 256 positions: C_out <= 16 (the direct head)
+    IG_NARROW = 1, // 16 output rows x 256 positions: C_out <= 16 (the direct head), rows of x
+                   // below 2 GiB / 10
     IG_TEMPORAL = 2, // packing only: 3 temporal taps x 128 rows (9 taps x 12 channels), head kernels
     IG_W32 = 3,     // 256 output rows x 8x32 positions on 32x32x16 MFMA: C_out > 16, one frame of
                     // x below 2 GiB (addressed through a 32-bit buffer range)
