@@ -99,6 +99,10 @@ CASES_3D_INT = [
     (1, 136, 7, 4, 9, 33, "f16", "none", C.ALGO_MFMA),
     (2, 24, 16, 2, 17, 40, "bf16", "clamp1", C.ALGO_MFMA),
     (1, 136, 12, 16, 64, 128, "bf16", "relu", C.ALGO_MFMA),
+    # frame groups: 13 frames as 8 + 5 (eight per workgroup, a part-empty last group), 9 frames as
+    # 4 + 4 + 1 (four per workgroup)
+    (1, 40, 12, 13, 9, 40, "bf16", "relu", C.ALGO_MFMA),
+    (1, 72, 5, 9, 11, 36, "f16", "clamp1", C.ALGO_MFMA),
     (1, 32, 12, 3, 9, 50, "bf16", "clamp1", C.ALGO_SPLIT_HEAD),
     (2, 64, 5, 1, 7, 130, "bf16", "none", C.ALGO_SPLIT_HEAD),
     (1, 8, 12, 4, 70, 64, "f16", "clamp1", C.ALGO_SPLIT_HEAD),

@@ -23,6 +23,8 @@
 // rows 4*(l/16)..4*(l/16)+3 of column l%16 of D.  Only the row/column assignment matters for
 // correctness -- A and B share the same k assignment, so any permutation of k inside a 32-chunk
 // cancels in the dot product.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -265,62 +267,88 @@ __global__ __launch_bounds__(256, 2) void igemm3d_kernel(IgemmKArgs a) {
 
 // ---------------------------------------------------------------------------------------------
 // The 27-tap convolution for narrow outputs (C_out <= 16: the direct head) on 16x16x32 MFMA.
-// What limits this form is the vector-memory address unit, which costs per cache line touched:
-// a 32-channel slice of a 256-channel position is half a line, and every wave loading its own
-// weight fragments multiplies their lines by four.  So:
-//   * K runs in stages of 64 channels (two 32-channel chunks) of one live temporal tap: a window
-//     position is then a whole 128-byte line, and one LDS-DMA copy (buffer_load ... lds, 16 bytes
-//     per lane, 1 KiB of LDS) moves 8 whole lines.  Window: (TH+2) x (TW+2) = 10 x 34 positions.
-//   * The stage's weights (2 chunks x 9 spatial taps x 16 rows x 32 channels = 18 KiB) are copied
-//     into LDS once per workgroup by the same DMA, instead of once per wave into registers.
-//   * Both live in two buffer sets (separate objects, the stage loop unrolled by two): the copies
-//     of stage s+1 go out one by one between the MFMAs of the first steps of stage s and are
-//     waited for at its end, one barrier per stage.  ~123 KiB of LDS: one workgroup (4 waves)
-//     per CU.
-//   * Wave w owns 4 output rows x 16 columns of the 8 x 32 tile (rows 4*(w/2).., columns
-//     16*(w%2)..): a window fragment of row wr and column shift kx feeds the vertical taps ky of
-//     up to three of its rows, so a wave reads 18 window fragments per 32 channels for 36 MFMAs.
+// What limits this form is the vector memory path's line requests (each costs about an L2
+// latency divided by the requests a CU keeps in flight), so the kernel is built to request few
+// lines per output:
+//   * Channels run in stages of 64 (a pair of 32-channel chunks): a window position is then one
+//     whole 128-byte line, and one LDS-DMA copy (buffer_load ... lds, 16 bytes per lane, 1 KiB of
+//     LDS) moves 8 whole lines.  Window: (TH+2) x (TW+2) = 10 x 34 positions.
+//   * A workgroup takes NF (4 or 8) consecutive output frames of an 8 x 32 tile and walks the
+//     NF + 2 input frames they read: each input window is copied once and applied to every output
+//     frame that reads it (temporal taps kd = 0, 1, 2 of frames i, i-1, i-2), instead of once per
+//     output frame and tap.
+//   * The weights of a pair (2 chunks x 27 taps x 16 rows x 32 channels) sit in three LDS slots,
+//     one per temporal tap (18 KiB each), copied once per workgroup and pair by the same DMA.
+//     Slot kd is last read at input frame NF-1+kd of a pair, so the next pair's taps 0 and 1
+//     are copied during its last two input frames and tap 2 during the next pair's first one --
+//     no stall between pairs.
+//   * Windows are double-buffered (separate objects; input frames 0..NF+1 of a pair are fully
+//     unrolled, so every buffer and slot is known at compile time): the copies of the next
+//     window go out one by one between the MFMAs of the first steps of the current one and are
+//     waited for at its end, one barrier per input frame.  ~140 KiB of LDS: one workgroup
+//     (4 waves) per CU.
+//   * Wave w owns 4 output rows x 16 columns of the tile (rows 4*(w/2).., columns 16*(w%2)..) in
+//     each of the NF frames: a window fragment of row wr and column shift kx feeds the
+//     vertical taps ky of up to three of its rows in up to three output frames.
 // LDS layouts (16-byte pieces): window position (row, col) at (row * 34 + col) * 8, its piece p
-// (channels 8p..8p+7 of the stage) in slot p ^ ((col >> 1) & 7) -- any 16 consecutive columns of
-// one piece fall on distinct bank groups; weight fragment (chunk half h, tap t) at (9h + t) * 64,
-// row m's piece p in slot 4m + (p ^ ((m >> 2) & 3)).  The DMA fetches, for each LDS slot, the
-// global piece that belongs there: the permutations stay inside one line, so copies remain whole
-// lines.  Zero padding (rows, columns, channels, the second chunk past the range) is an offset
-// past the buffer range: the copy fetches nothing and writes zeros.
-// Addressing: the window of a stage is one 32-bit buffer range from its first valid input row
-// (at most ten rows of the frame), so frames of any size work.
+// (channels 8p..8p+7 of the pair) in slot p ^ ((col >> 1) & 7) -- any 16 consecutive columns of
+// one piece fall on distinct bank groups; weight fragment (chunk half h, spatial tap t) of a
+// temporal-tap slot at (9h + t) * 64, row m's piece p in slot 4m + (p ^ ((m >> 2) & 3)).  The DMA
+// fetches, for each LDS slot, the global piece that belongs there: the permutations stay inside
+// one line, so copies remain whole lines.  Zero padding (rows, columns, frames, channels, the
+// second chunk past the range) is an offset past the buffer range: the copy fetches nothing and
+// writes zeros.
+// Addressing: a window is one 32-bit buffer range from its first valid input row (at most ten
+// rows of one frame), so frames of any size work.
+// output frames per workgroup: 8 where that leaves few frame slots empty, else 4
+__host__ __device__ constexpr int narrow_frames(int D) { return D >= 8 && (D % 8 == 0 || D % 8 > 4) ? 8 : 4; }
 constexpr int kNarTH = 8, kNarTW = 32;                   // output tile
 constexpr int kNarRowPos = kNarTW + 2;                   // window row length (even)
 constexpr int kNarPos = (kNarTH + 2) * kNarRowPos;       // 340 window positions
 constexpr int kNarWinCopies = (kNarPos + 7) / 8;         // 43 DMA copies of 8 positions
 constexpr int kNarWinSlots = kNarWinCopies * 64;
-constexpr int kNarACopies = 18;                          // 2 chunks x 9 taps, 1 KiB each
+constexpr int kNarACopies = 18;                          // 2 chunks x 9 spatial taps, 1 KiB each
 constexpr int kNarWinPerWave = (kNarWinCopies + 3) / 4;  // 11
 constexpr int kNarAPerWave = (kNarACopies + 3) / 4;      // 5
-constexpr int kNarCopiesPerWave = kNarWinPerWave + kNarAPerWave;   // 16
 constexpr int kNarWaitVm0 = (7 << 4) | (15 << 8);        // s_waitcnt vmcnt(0), nothing else
 
-template <bool BF, int EPI, bool SPLITK>
+// The uniform parts of one window copy and of one temporal tap's weight copies of
+// igemm3d_narrow_kernel (at namespace scope: the host pass emits no launch stub for a kernel
+// template with local struct types).
+struct WinCopy {
+    const u16 *xbase;  // the window's rows (its first valid one)
+    int pmax;          // pieces holding input channels of the range's chunks (0: none)
+    uint32_t cdelta;   // byte offset of the pair's first channel in a position
+};
+struct WCopy {
+    uint32_t abase;    // byte offset of fragment (chunk cc0, tap kd*9) in the packing
+    bool second;       // the pair's second chunk lies in the range
+    bool live;         // there is such a copy
+};
+
+template <bool BF, int EPI, bool SPLITK, int NF>
 __global__ __launch_bounds__(256, 1) void igemm3d_narrow_kernel(IgemmKArgs a) {
     using E = Elem<BF>;
     typedef typename E::vec8 vec8;
     typedef __attribute__((address_space(3))) void lds_void;
+    static_assert(NF == 4 || NF == 8, "four or eight output frames per workgroup");
+    constexpr int kStages = NF + 2;   // input frames per pair
     __shared__ __attribute__((aligned(16))) uint4 Win0[kNarWinSlots];
     __shared__ __attribute__((aligned(16))) uint4 Win1[kNarWinSlots];
-    __shared__ __attribute__((aligned(16))) uint4 Wa0[kNarACopies * 64];
-    __shared__ __attribute__((aligned(16))) uint4 Wa1[kNarACopies * 64];
+    __shared__ __attribute__((aligned(16))) uint4 Wk0[kNarACopies * 64];
+    __shared__ __attribute__((aligned(16))) uint4 Wk1[kNarACopies * 64];
+    __shared__ __attribute__((aligned(16))) uint4 Wk2[kNarACopies * 64];
     __shared__ __attribute__((aligned(16))) float bias_s[16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    // frame innermost, as igemm3d_kernel: the three output frames that read an input frame window
-    // run together on one XCD
+    // frame group innermost: consecutive groups of a tile share two input frames in L2
     uint32_t lin = xcd_remap(blockIdx.x, a.total_wg);
-    lin /= a.mtiles;   // (one 16-row tile)
-    const int od = lin % a.D;
-    lin /= a.D;
+    const int fgroups = (a.D + NF - 1) / NF;
+    const int fg = lin % fgroups;
+    lin /= fgroups;
     const int tw = lin % a.tiles_w;
     lin /= a.tiles_w;
     const int th = lin % a.tiles_h;
@@ -329,14 +357,11 @@ __global__ __launch_bounds__(256, 1) void igemm3d_narrow_kernel(IgemmKArgs a) {
     const int split = lin / a.N;
 
     const int oh0 = th * kNarTH, ow0 = tw * kNarTW;
+    const int od0 = fg * NF;
     const int c_begin = split * a.chunks_per_split;
     const int c_end = min(a.nchunks, c_begin + a.chunks_per_split);
-    const int fi0 = od + a.d_org - 1;
-    const int kd_lo = max(0, a.d_lo - fi0);
-    const int kd_hi = min(2, a.d_hi - 1 - fi0);
-    const int nkd = max(0, kd_hi - kd_lo + 1);
     const int npairs = (c_end - c_begin + 1) / 2;
-    const int nst = max(0, npairs * nkd);
+    const int fw0 = od0 - 1 + a.d_org;   // input frame of window i = fw0 + i
 
     // the window's input rows: oh0 - 1 + h_org + row, valid inside [h_lo, h_hi); the buffer range
     // starts at the first valid one
@@ -368,50 +393,47 @@ __global__ __launch_bounds__(256, 1) void igemm3d_narrow_kernel(IgemmKArgs a) {
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
         (void *)a.wp, (short)0, (int)(a.wp_bytes), 0x00020000);
 
-    // stage s: chunk pair j = s / nkd (chunks cc0, cc0 + 1 of [c_begin, c_end)), temporal tap
-    // kd = kd_lo + s % nkd
-    // The copies of a stage, kNarCopiesPerWave per wave: window copies t < kNarWinPerWave
-    // (copy k = wave + 4t), then weight copies (fragment q = wave + 4u: chunk half q / 9, tap
-    // q % 9).  stage_copies fixes a stage's uniform parts, copy_one issues one copy.
-    struct StageCopies {
-        const u16 *xbase;  // the stage's window rows (their first valid row)
-        int pmax;          // pieces of the stage that hold input channels of the range's chunks
-        uint32_t cdelta;   // byte offset of the stage's first channel in a position
-        uint32_t abase;    // byte offset of fragment (chunk cc0, tap kd*9) in the packing
-        bool second;       // the stage's second chunk lies in the range
-    };
-    auto stage_copies = [&](int s) {
-        StageCopies c;
-        const int j = s / nkd, kd = kd_lo + s % nkd;
-        const int cc0 = c_begin + 2 * j;
-        c.second = cc0 + 1 < c_end;
-        c.pmax = min(c.second ? 8 : 4, (a.C_in - 32 * cc0 + 7) / 8);
-        c.xbase = a.x + (((size_t)n * a.D_in + (fi0 + kd)) * frame_elems + ((size_t)hbase * a.W) * a.C_in);
+    // The copies one input frame's stage issues, at most kNarWinPerWave + kNarAPerWave per wave:
+    // the next window (pair jw, input frame iw) and, for some stages, one temporal tap's weights
+    // (pair ja, tap kda).  window() / weights() fix their uniform parts, copy_one issues copy i.
+    auto window = [&](int jw, int iw) {
+        WinCopy c;
+        const int cc0 = c_begin + 2 * jw;
+        const int f = fw0 + iw;
+        const bool fok = jw < npairs && f >= a.d_lo && f < a.d_hi;
+        c.pmax = fok ? min(cc0 + 1 < c_end ? 8 : 4, (a.C_in - 32 * cc0 + 7) / 8) : 0;
+        c.xbase = a.x + (((size_t)n * a.D_in + (fok ? f : 0)) * frame_elems + ((size_t)hbase * a.W) * a.C_in);
         c.cdelta = (uint32_t)cc0 * 64u;   // 32 channels x 2 bytes per chunk
-        c.abase = (uint32_t)((cc0 * 27 + kd * 9) * a.Mpad) * 64u;
         return c;
     };
-    auto copy_one = [&](const StageCopies &c, int i, uint4 *win, uint4 *wa) {
+    auto weights = [&](int ja, int kda) {
+        WCopy c;
+        const int cc0 = c_begin + 2 * ja;
+        c.live = ja < npairs;
+        c.second = cc0 + 1 < c_end;
+        c.abase = (uint32_t)((cc0 * 27 + kda * 9) * a.Mpad) * 64u;
+        return c;
+    };
+    auto copy_one = [&](int i, const WinCopy &cw, uint4 *win, const WCopy &ca, uint4 *wk) {
         if (i < kNarWinPerWave) {
             const int k = wave + 4 * i;
             if (kNarWinCopies % 4 != 0 && k >= kNarWinCopies) return;   // wave-uniform
-            const uint32_t off = wpiece[i] < c.pmax && woff[i] != 0xFFFFFFFFu ? woff[i] + c.cdelta : 0xFFFFFFFFu;
+            const uint32_t off = wpiece[i] < cw.pmax && woff[i] != 0xFFFFFFFFu ? woff[i] + cw.cdelta : 0xFFFFFFFFu;
             const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)c.xbase, (short)0, (int)win_range, 0x00020000);
+                (void *)cw.xbase, (short)0, (int)win_range, 0x00020000);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)&win[k * 64], 16, off, 0, 0, 0);
-        } else {
+        } else if (ca.live) {
             const int q = wave + 4 * (i - kNarWinPerWave);
             if (q >= kNarACopies) return;   // wave-uniform
             const int hq = q / 9, tq = q - 9 * hq;
-            const bool live = hq == 0 || c.second;
-            const uint32_t frag = c.abase + (uint32_t)((hq * 27 + tq) * a.Mpad) * 64u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void *)&wa[q * 64], 16,
-                                                     live ? frag + alane : 0xFFFFFFFFu, 0, 0, 0);
+            const uint32_t frag = ca.abase + (uint32_t)((hq * 27 + tq) * a.Mpad) * 64u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void *)&wk[q * 64], 16,
+                                                     hq == 0 || ca.second ? frag + alane : 0xFFFFFFFFu, 0, 0, 0);
         }
     };
 
-    // fragment reads: weight (h, tap) of row lane%16, piece lane/16; window (row, column shift
-    // kx, chunk half h) of column c0 + kx + lane%16, piece 4h + lane/16
+    // fragment reads: weight (h, spatial tap) of row lane%16, piece lane/16; window (row, column
+    // shift kx, chunk half h) of column c0 + kx + lane%16, piece 4h + lane/16
     const int cb = wave & 1, r0 = 4 * (wave >> 1);
     const int aslot = (lane & 15) * 4 + ((lane >> 4) ^ ((lane >> 2) & 3));
     int bslot[2][3];
@@ -424,78 +446,126 @@ __global__ __launch_bounds__(256, 1) void igemm3d_narrow_kernel(IgemmKArgs a) {
             bslot[h][kx] = (r0 * kNarRowPos + col) * 8 + (p ^ ((col >> 1) & 7));
         }
 
-    f32x4_t acc[4];
+    f32x4_t acc[NF][4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int o = 0; o < NF; ++o)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[o][r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // One stage's MFMAs from (win, wa): 36 steps (chunk half h, window row wrr, column shift kx),
-    // each one window fragment and the MFMAs of the up to three output rows it feeds.  Fragments
-    // are read two steps ahead (a ring of three); the weight fragments of both halves at the
-    // start.  With `next`, the copies of the next stage into (nwin, nwa) go out one after each
-    // of the first 16 steps, between the MFMAs (issued in one burst they hold up the matrix
-    // pipe; issued later they have less of the stage to land).
-    auto compute = [&](const uint4 *win, const uint4 *wa, bool next, const StageCopies &c,
-                       uint4 *nwin, uint4 *nwa) {
+    // Input frame I of a pair from window win: output frame o = I - kd takes temporal tap kd for
+    // each kd with 0 <= o < NF.  36 steps (chunk half h, window row wrr, column shift kx), each
+    // one window fragment -- read two steps ahead -- and the MFMAs it feeds; the weight fragments
+    // of the live taps at the start of each half.  The stage's copies (ncopy of them) go out one
+    // after each of the first steps.
+    auto stage = [&](auto Ic, const uint4 *win, int ncopy, const WinCopy &cw, uint4 *nwin,
+                     const WCopy &ca, uint4 *wk) {
+        constexpr int I = decltype(Ic)::value;
+        constexpr bool live0 = I < NF, live1 = I >= 1 && I - 1 < NF, live2 = I >= 2;
+        const uint4 *wks[3] = {Wk0, Wk1, Wk2};
         constexpr int kSteps = 36;
         auto read_b = [&](int it) {
             const int h = it / 18, wrr = (it % 18) / 3, kx = it % 3;
             return __builtin_bit_cast(vec8, win[bslot[h][kx] + wrr * (kNarRowPos * 8)]);
         };
-        vec8 A[2][9];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int t = 0; t < 9; ++t) A[h][t] = __builtin_bit_cast(vec8, wa[(9 * h + t) * 64 + aslot]);
+        vec8 A[3][9];
         vec8 Bq[3];
         Bq[0] = read_b(0);
         Bq[1] = read_b(1);
 #pragma unroll
         for (int it = 0; it < kSteps; ++it) {
             const int h = it / 18, wrr = (it % 18) / 3, kx = it % 3;
+            if (it % 18 == 0) {
+#pragma unroll
+                for (int kd = 0; kd < 3; ++kd) {
+                    if (!(kd == 0 ? live0 : kd == 1 ? live1 : live2)) continue;
+#pragma unroll
+                    for (int t = 0; t < 9; ++t)
+                        A[kd][t] = __builtin_bit_cast(vec8, wks[kd][(9 * h + t) * 64 + aslot]);
+                }
+            }
             if (it + 2 < kSteps) Bq[(it + 2) % 3] = read_b(it + 2);
 #pragma unroll
-            for (int ky = 0; ky < 3; ++ky) {
-                const int r = wrr - ky;
-                if (r >= 0 && r < 4) acc[r] = E::mfma16x16x32(A[h][ky * 3 + kx], Bq[it % 3], acc[r]);
+            for (int kd = 0; kd < 3; ++kd) {
+                if (!(kd == 0 ? live0 : kd == 1 ? live1 : live2)) continue;
+                const int o = I - kd;
+#pragma unroll
+                for (int ky = 0; ky < 3; ++ky) {
+                    const int r = wrr - ky;
+                    if (r >= 0 && r < 4) acc[o][r] = E::mfma16x16x32(A[kd][ky * 3 + kx], Bq[it % 3], acc[o][r]);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (it < kNarCopiesPerWave && next) copy_one(c, it, nwin, nwa);
+            if (it < ncopy) copy_one(it, cw, nwin, ca, wk);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
     if (tid < 16) bias_s[tid] = (!SPLITK && a.bias != nullptr && tid < a.Mrows) ? E::to_f32(a.bias[tid]) : 0.f;
-    if (nst > 0) {
-        const StageCopies c0 = stage_copies(0);
+    constexpr int kAll = kNarWinPerWave + kNarAPerWave;
+    if (npairs > 0) {
+        // pair 0's first window and its temporal taps 0 and 1 (tap 2 follows with input frame 0)
+        const WinCopy w0 = window(0, 0);
+        const WCopy none{0u, false, false};
+        const WCopy t0 = weights(0, 0), t1 = weights(0, 1);
 #pragma unroll
-        for (int i = 0; i < kNarCopiesPerWave; ++i) copy_one(c0, i, Win0, Wa0);
+        for (int i = 0; i < kNarWinPerWave; ++i) copy_one(i, w0, Win0, none, Wk0);
+#pragma unroll
+        for (int i = kNarWinPerWave; i < kAll; ++i) copy_one(i, w0, Win0, t0, Wk0);
+#pragma unroll
+        for (int i = kNarWinPerWave; i < kAll; ++i) copy_one(i, w0, Win0, t1, Wk1);
     }
     __builtin_amdgcn_s_waitcnt(kNarWaitVm0);
     __syncthreads();
+    // the stage of input frame I of pair j: its window is in Win{I % 2}; it copies the next
+    // window (frame I+1, or frame 0 of pair j+1) into the other buffer, and weights: tap 2 of pair
+    // j with frame 0, taps 0 and 1 of pair j+1 with frames NF and NF+1.
+    auto run = [&](auto Ic, int j) {
+        constexpr int I = decltype(Ic)::value;
+        const bool last = I + 1 == kStages;
+        const WinCopy cw = window(last ? j + 1 : j, last ? 0 : I + 1);
+        const int kda = I == 0 ? 2 : (I == NF ? 0 : (I == NF + 1 ? 1 : -1));
+        const WCopy ca = kda < 0 ? WCopy{0u, false, false} : weights(kda == 2 ? j : j + 1, kda);
+        uint4 *wk = kda == 0 ? Wk0 : (kda == 1 ? Wk1 : Wk2);
+        const int ncopy = kda < 0 ? kNarWinPerWave : kAll;
+        if constexpr (I % 2 == 0) stage(Ic, Win0, ncopy, cw, Win1, ca, wk);
+        else stage(Ic, Win1, ncopy, cw, Win0, ca, wk);
+        __builtin_amdgcn_s_waitcnt(kNarWaitVm0);
+        __syncthreads();
+    };
+    using std::integral_constant;
 #pragma unroll 1
-    for (int s = 0; s < nst; s += 2) {
-        const StageCopies c1 = stage_copies(s + 1 < nst ? s + 1 : s);
-        compute(Win0, Wa0, s + 1 < nst, c1, Win1, Wa1);
-        __builtin_amdgcn_s_waitcnt(kNarWaitVm0);
-        __syncthreads();
-        if (s + 1 >= nst) break;
-        const StageCopies c2 = stage_copies(s + 2 < nst ? s + 2 : s);
-        compute(Win1, Wa1, s + 2 < nst, c2, Win0, Wa0);
-        __builtin_amdgcn_s_waitcnt(kNarWaitVm0);
-        __syncthreads();
+    for (int j = 0; j < npairs; ++j) {
+        run(integral_constant<int, 0>{}, j);
+        run(integral_constant<int, 1>{}, j);
+        run(integral_constant<int, 2>{}, j);
+        run(integral_constant<int, 3>{}, j);
+        run(integral_constant<int, 4>{}, j);
+        run(integral_constant<int, 5>{}, j);
+        if constexpr (kStages > 6) {
+            run(integral_constant<int, 6>{}, j);
+            run(integral_constant<int, 7>{}, j);
+            run(integral_constant<int, 8>{}, j);
+            run(integral_constant<int, 9>{}, j);
+        }
     }
+    static_assert(kStages == 6 || kStages == 10, "the pair loop above runs input frames 0..kStages-1");
 
     const size_t P = (size_t)a.N * a.D * a.H * a.W;
     const int m0 = 4 * (lane >> 4);
     const float4 bv = *reinterpret_cast<const float4 *>(&bias_s[m0]);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int oh = oh0 + r0 + r, ow = ow0 + 16 * cb + (lane & 15);
-        if (oh >= a.H || ow >= a.W) continue;
-        const size_t pos = (((size_t)n * a.D + od) * a.H + oh) * a.W + ow;
-        store_rows<BF, EPI, SPLITK>(a, f32x4_t{acc[r][0] + bv.x, acc[r][1] + bv.y, acc[r][2] + bv.z,
-                                              acc[r][3] + bv.w},
-                                   pos, split, P, m0);
+    for (int o = 0; o < NF; ++o) {
+        const int od = od0 + o;
+        if (od >= a.D) break;   // (uniform)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int oh = oh0 + r0 + r, ow = ow0 + 16 * cb + (lane & 15);
+            if (oh >= a.H || ow >= a.W) continue;
+            const size_t pos = (((size_t)n * a.D + od) * a.H + oh) * a.W + ow;
+            store_rows<BF, EPI, SPLITK>(a, f32x4_t{acc[o][r][0] + bv.x, acc[o][r][1] + bv.y,
+                                                  acc[o][r][2] + bv.z, acc[o][r][3] + bv.w},
+                                       pos, split, P, m0);
+        }
     }
 }
 
@@ -1319,6 +1389,16 @@ hipError_t launch_family(const IgemmPlan &pl, const IgemmKArgs &ka, int epi, boo
     return hipGetLastError();
 }
 
+template <bool BF, int F>
+hipError_t launch_narrow(const IgemmPlan &pl, const IgemmKArgs &ka, int epi, bool splitk, hipStream_t s) {
+    const dim3 grid((unsigned)pl.workgroups), block(256);
+    if (splitk) igemm3d_narrow_kernel<BF, EPI_NONE, true, F><<<grid, block, 0, s>>>(ka);
+    else if (epi == EPI_RELU) igemm3d_narrow_kernel<BF, EPI_RELU, false, F><<<grid, block, 0, s>>>(ka);
+    else if (epi == EPI_CLAMP1) igemm3d_narrow_kernel<BF, EPI_CLAMP1, false, F><<<grid, block, 0, s>>>(ka);
+    else igemm3d_narrow_kernel<BF, EPI_NONE, false, F><<<grid, block, 0, s>>>(ka);
+    return hipGetLastError();
+}
+
 template <bool BF, int LW, int NB, int S = 1>
 hipError_t launch_w32(const IgemmKArgs &ka, int epi, bool splitk, dim3 grid, hipStream_t s) {
     const dim3 block(256);
@@ -1391,14 +1471,9 @@ hipError_t launch_igemm_dtype(const IgemmPlan &pl, const IgemmKArgs &ka, int epi
         }
         case IG_WIDE:
             return launch_family<BF, 4, 4, 2, 2, 8, 16>(pl, ka, epi, splitk, s);
-        case IG_NARROW: {
-            const dim3 grid((unsigned)pl.workgroups), block(256);
-            if (splitk) igemm3d_narrow_kernel<BF, EPI_NONE, true><<<grid, block, 0, s>>>(ka);
-            else if (epi == EPI_RELU) igemm3d_narrow_kernel<BF, EPI_RELU, false><<<grid, block, 0, s>>>(ka);
-            else if (epi == EPI_CLAMP1) igemm3d_narrow_kernel<BF, EPI_CLAMP1, false><<<grid, block, 0, s>>>(ka);
-            else igemm3d_narrow_kernel<BF, EPI_NONE, false><<<grid, block, 0, s>>>(ka);
-            return hipGetLastError();
-        }
+        case IG_NARROW:
+            return narrow_frames(ka.D) == 8 ? launch_narrow<BF, 8>(pl, ka, epi, splitk, s)
+                                            : launch_narrow<BF, 4>(pl, ka, epi, splitk, s);
     }
     return hipErrorInvalidValue;
 }
@@ -1441,7 +1516,9 @@ IgemmPlan plan_igemm(int family, int N, int C_in, int C_out, int D, int H, int W
         pl.tiles_h = (H + pl.TH - 1) / pl.TH;
         pl.tiles_w = (W + pl.TW - 1) / pl.TW;
     }
-    const long long base = (long long)N * D * pl.tiles_h * pl.tiles_w * pl.mtiles;
+    // (the narrow kernel takes narrow_frames(D) output frames per workgroup)
+    const int dunits = family == IG_NARROW ? (D + narrow_frames(D) - 1) / narrow_frames(D) : D;
+    const long long base = (long long)N * dunits * pl.tiles_h * pl.tiles_w * pl.mtiles;
     // Split K when the output alone cannot fill the 256 compute units a few times over.
     int splits = 1;
     if (family == IG_W32 && base > 0) {
@@ -1526,7 +1603,7 @@ IgemmPlan plan_igemm(int family, int N, int C_in, int C_out, int D, int H, int W
     pl.chunks_per_split = (pl.nchunks + splits - 1) / splits;
     pl.splits = (pl.nchunks + pl.chunks_per_split - 1) / pl.chunks_per_split;
     pl.workgroups = pl.sk ? (long long)pl.sk
-                          : (long long)N * D * pl.tiles_h * pl.tiles_w * pl.mtiles * pl.splits;
+                          : (long long)N * dunits * pl.tiles_h * pl.tiles_w * pl.mtiles * pl.splits;
     return pl;
 }
 
