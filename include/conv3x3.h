@@ -23,7 +23,9 @@
  *     workspace must be 16-byte aligned; bias 2-byte aligned.  x and y must not overlap.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work is enqueued
  *     on it and the call returns without synchronising.  Multi-launch algorithms order their
- *     launches on that stream.
+ *     launches on that stream.  A workspace holds one call's intermediate state (plane,
+ *     partial sums, stream-K arrival counters) while that call runs: calls that may run at the
+ *     same time (on different streams) need workspaces of their own.
  *   - All argument checks happen before anything is enqueued; on error nothing is launched
  *     and conv_last_error() returns a message.  A kernel fault surfaces at the caller's next
  *     synchronisation, as with any HIP launch.
