@@ -129,6 +129,16 @@ CASES_3D_INT = [
     (1, 32, 12, 40, 37, 300, "bf16", "clamp1", C.ALGO_SPLIT_HEAD),
     (2, 16, 12, 32, 17, 380, "f16", "relu", C.ALGO_FUSED_HEAD),
     (2, 16, 12, 32, 17, 380, "f16", "relu", C.ALGO_SPLIT_HEAD),
+    # the production channel count (C_in 256) in more shapes: fp16, two frame groups (the second
+    # part-empty) over two strips; C_out 7 on two samples; ranges that cross strips; a single
+    # position
+    (1, 256, 12, 5, 13, 140, "f16", "relu", C.ALGO_FUSED_HEAD),
+    (1, 256, 12, 5, 13, 140, "f16", "relu", C.ALGO_SPLIT_HEAD),
+    (2, 256, 7, 4, 10, 60, "bf16", "none", C.ALGO_FUSED_HEAD),
+    (2, 256, 7, 4, 10, 60, "bf16", "none", C.ALGO_SPLIT_HEAD),
+    (1, 256, 12, 40, 37, 300, "bf16", "clamp1", C.ALGO_FUSED_HEAD),
+    (1, 256, 12, 40, 37, 300, "bf16", "clamp1", C.ALGO_SPLIT_HEAD),
+    (1, 256, 12, 1, 1, 1, "bf16", "clamp1", C.ALGO_FUSED_HEAD),
 ]
 
 
@@ -146,12 +156,14 @@ def test_conv3d_integer_exact(case):
 # places -- taps 0..7 in the 32-row accumulator blocks, tap 8 in the 16-row tile whose operands and
 # results are moved between lanes -- so with a weight tensor that is zero except at one (ky, kx),
 # a wrong row, lane or k order shows up as that whole tap wrong.  No clamp, so nothing saturates.
+# C_in 32 (one chunk pair per Z row) and the production 256 (four pairs).
+@pytest.mark.parametrize("ci", [32, 256])
 @pytest.mark.parametrize("algo", [C.ALGO_SPLIT_HEAD, C.ALGO_FUSED_HEAD])
 @pytest.mark.parametrize("tap", range(9))
-def test_head_single_spatial_tap_exact(tap, algo):
+def test_head_single_spatial_tap_exact(tap, algo, ci):
     ky, kx = divmod(tap, 3)
-    _say("head single tap (%d, %d) algo %d" % (ky, kx, algo))
-    x, w, b = si.integer_case("3d", 1, 32, 12, 9, 50, D=3, dtype="bf16", seed=700 + tap, device=DEV)
+    _say("head single tap (%d, %d) algo %d C_in %d" % (ky, kx, algo, ci))
+    x, w, b = si.integer_case("3d", 1, ci, 12, 9, 50, D=3, dtype="bf16", seed=700 + tap, device=DEV)
     only = torch.zeros_like(w)
     only[:, :, :, ky, kx] = w[:, :, :, ky, kx]
     assert torch.count_nonzero(only) > 0
