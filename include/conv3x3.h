@@ -68,8 +68,8 @@ enum { CONV_EPI_NONE = 0, CONV_EPI_RELU = 1, CONV_EPI_CLAMP1 = 2 };
  *               the plane never goes to HBM; no workspace.  [head.cu, header comment: the split
  *               of the 27-tap conv; its value path places the first rounding after the three
  *               temporal taps, which this fused form leaves out.]
- *   AUTO: 2D: MFMA when it applies, else SIMT.  3D: FUSED_HEAD when C_out <= 12 and stride 1,
- *   else MFMA.  [taesd_conv.cuh.new header comment: direct kernels for the C <= 64 layers;
+ *   AUTO: 2D: MFMA when it applies, else SIMT.  3D: FUSED_HEAD when C_out <= 12, stride 1 and
+ *   the head's frame windows fit (see conv3x3x3_fwd), else MFMA.  [taesd_conv.cuh.new header comment: direct kernels for the C <= 64 layers;
  *   head.cu header comment: the split form for the 12-channel head.] */
 enum {
     CONV_ALGO_AUTO = 0,
@@ -172,7 +172,8 @@ int conv3x3_select_algo(int N, int C_in, int C_out, int H, int W, int stride, in
  * 1 (the oracle's reading of a strided 3x3x3 video convolution); it runs on algo MFMA only
  * (AUTO selects it) and needs one input frame below 2 GiB.
  *   algo MFMA: any C_out >= 1.  algo SPLIT_HEAD / FUSED_HEAD: C_out <= 12, stride 1, any number
- *   of frames, six input frames (6*H*W*C_in elements) below 2 GiB.  AUTO: see select_algo.
+ *   of frames; a workgroup's six input frames (6*H*W*C_in elements) and four output frames
+ *   (4*H*W*12 elements) each below 2 GiB.  AUTO: see select_algo.
  * workspace: at least conv3x3x3_workspace_bytes(...) bytes (may be NULL when that is 0).
  * The same (shape, dtype, algo) arguments must be given to the size queries, to
  * conv3x3x3_pack_weights and to conv3x3x3_fwd.
@@ -251,8 +252,9 @@ size_t conv3x3x3_packed_weight_bytes(int N, int C_in, int C_out, int D, int H, i
  * NUL-terminated): "fused_head" / "split_head" with the head's work split (strips of 126 / 128
  * positions, groups of four frames, row ranges per frame group, the largest range's Z rows,
  * workgroups), or the MFMA kernel ("igemm32", "igemm32_kq" when the four waves of a workgroup
- * split K, "igemm16_wide", "igemm16_narrow") with its position tile (rows x columns of one
- * frame), output rows per workgroup, split-K factor and workgroup count.  Returns the full length of the description, or a negative status (CONV_E_INVAL for a
+ * split K, "igemm32_sk" for the stream-K schedule, "igemm16_wide", "igemm16_narrow") with its
+ * position tile (rows x columns of one frame), output rows per workgroup, split-K factor and
+ * workgroup count.  Returns the full length of the description, or a negative status (CONV_E_INVAL for a
  * NULL buf or buf_len < 1, else what conv3x3x3_select_algo returns).  Host-only.  [head.cu,
  * header comment: which of the head's forms, direct or split, a pass runs.] */
 int conv3x3x3_describe(int N, int C_in, int C_out, int D, int H, int W, int stride, int layout,
