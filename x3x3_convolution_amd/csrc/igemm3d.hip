@@ -1069,6 +1069,7 @@ __global__ __launch_bounds__(256, 1) void igemm32_kq_kernel(IgemmKArgs a) {
     // window buffer pair of each wave (even / odd stages); afterwards the partial tiles
     __shared__ __attribute__((aligned(16))) uint4 Win0[4][G::Slots];
     __shared__ __attribute__((aligned(16))) uint4 Win1[4][G::Slots];
+    __shared__ __attribute__((aligned(16))) float bias_s[64];   // the tile's 64 rows (0 past C_out)
     static_assert(4 * G::Slots >= 2 * 6 * 256, "two waves' partial blocks fit one buffer set");
 
     const int lane = threadIdx.x & 63;
@@ -1160,6 +1161,11 @@ __global__ __launch_bounds__(256, 1) void igemm32_kq_kernel(IgemmKArgs a) {
         }
     vec8 aq[kW32PD][2];
     vec8 bq[2][4];
+    // the bias now, into LDS (read after the barriers below), not as loads in the epilogue
+    if (threadIdx.x < 64) {
+        const int m = mbase + (int)threadIdx.x;
+        bias_s[threadIdx.x] = (a.bias != nullptr && m < a.Mrows) ? E::to_f32(a.bias[m]) : 0.f;
+    }
 
     if (nst > 0) {
         copy_window(0, Win0[wave]);
@@ -1270,12 +1276,9 @@ __global__ __launch_bounds__(256, 1) void igemm32_kq_kernel(IgemmKArgs a) {
                 }
                 const int m0 = mbase + mb * 32 + 8 * g + 4 * hh;
                 if (inside && m0 < a.Mrows) {
-                    float bv[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        bv[i] = (a.bias != nullptr && m0 + i < a.Mrows) ? E::to_f32(a.bias[m0 + i]) : 0.f;
-                    store_rows<BF, EPI, false>(a, f32x4_t{sum[0] + bv[0], sum[1] + bv[1],
-                                                          sum[2] + bv[2], sum[3] + bv[3]},
+                    const float4 bv = *reinterpret_cast<const float4 *>(&bias_s[m0 - mbase]);
+                    store_rows<BF, EPI, false>(a, f32x4_t{sum[0] + bv.x, sum[1] + bv.y,
+                                                          sum[2] + bv.z, sum[3] + bv.w},
                                                pos, 0, P, m0);
                 }
             }
