@@ -1168,12 +1168,14 @@ __global__ __launch_bounds__(256, 1) void igemm32_kq_kernel(IgemmKArgs a) {
     }
 
     if (nst > 0) {
+        // window 0, the first weight slices, then window 1: the first MFMAs wait for neither
+        // window 1 nor (loads complete in order) anything issued after what they read
         copy_window(0, Win0[wave]);
-        if (nst > 1) copy_window(1, Win1[wave]);
         uint32_t sb_cur = stage_abase(0);
 #pragma unroll
         for (int q = 0; q < kW32PD; ++q) load_a(sb_cur, q, aq[q]);
-        // window 0 complete (younger: window 1 and the weight loads)
+        if (nst > 1) copy_window(1, Win1[wave]);
+        // window 0 complete (younger: the weight loads and window 1)
         if (nst > 1) __builtin_amdgcn_s_waitcnt(w32_waitcnt_vm(G::Copies + 2 * kW32PD));
         else __builtin_amdgcn_s_waitcnt(w32_waitcnt_vm(2 * kW32PD));
 #pragma unroll
