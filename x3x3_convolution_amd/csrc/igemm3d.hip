@@ -991,7 +991,40 @@ __global__ __launch_bounds__(256, 1) void igemm32_kernel(IgemmKArgs a) {
                 sk_last = __hip_atomic_fetch_add(a.sk_count + tile_id, 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(np - 1);
             __syncthreads();
-            if (__builtin_amdgcn_readfirstlane(sk_last)) {
+            if (__builtin_amdgcn_readfirstlane(sk_last) && mlive && np == 2) {
+                // Two pieces (the usual split): the other piece's whole slot in one burst of loads
+                // -- one round trip instead of one per 32-row block -- then own + other, which
+                // (addition commuting) are the same bits as the K-order sum, whichever piece
+                // ended last.
+                f32x4_t ld[2][G::NB][4];
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+                        for (int gq = 0; gq < 4; ++gq)
+                            ld[mb][nb][gq] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                pr_rs, slot_off(1 - me, (mb * G::NB + nb) * 4 + gq), 0, kCpolSc1));
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < G::NB; ++nb) {
+                        w32_touch(acc[mb][nb]);
+                        const f32x16_t v = acc[mb][nb];
+                        const int oh = oh0 + G::R * nb + pr, ow = ow0 + pc;
+                        if (oh >= a.H || ow >= a.W) continue;
+                        const size_t pos = (((size_t)n * a.D + od) * a.H + oh) * a.W + ow;
+#pragma unroll
+                        for (int gq = 0; gq < 4; ++gq) {
+                            const f32x4_t o = ld[mb][nb][gq];
+                            const int m0 = mbase + mb * 32 + 8 * gq + 4 * hh;
+                            const float4 bv = *reinterpret_cast<const float4 *>(&bias_s[m0 - mt * 256]);
+                            store_rows<BF, EPI, false>(a, f32x4_t{(v[4 * gq] + o[0]) + bv.x, (v[4 * gq + 1] + o[1]) + bv.y,
+                                                                  (v[4 * gq + 2] + o[2]) + bv.z, (v[4 * gq + 3] + o[3]) + bv.w},
+                                                       pos, 0, P, m0);
+                        }
+                    }
+            } else if (__builtin_amdgcn_readfirstlane(sk_last)) {
                 if (mlive) {
 #pragma unroll
                     for (int mb = 0; mb < 2; ++mb) {
