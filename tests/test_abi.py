@@ -165,6 +165,13 @@ def test_2d_algo_selection():
         cx.conv3x3_select_algo(2, 8, 7, 13, 37, 1, 1, 0, C.ALGO_SIMT)
     with pytest.raises(C.ConvError):
         cx.conv3x3_select_algo(2, 5, 7, 13, 37, 1, 1, 0, C.ALGO_AUTO)
+    # one image of x (64 x 4096 x W fp16) just below and just above 2 GiB: the matrix-core kernel
+    # addresses an image through one 32-bit range, so past it AUTO falls back to SIMT (which takes
+    # any size) and an explicit MFMA request is refused
+    assert 64 * 4096 * 4088 * 2 < 1 << 31 <= 64 * 4096 * 4104 * 2
+    assert cx.conv3x3_select_algo(3, 64, 64, 4096, 4088, 1, 0, 0, C.ALGO_AUTO) == C.ALGO_MFMA
+    assert cx.conv3x3_select_algo(3, 64, 64, 4096, 4104, 1, 0, 0, C.ALGO_AUTO) == C.ALGO_SIMT
+    assert cx.conv3x3_is_supported(3, 64, 64, 4096, 4104, 1, 0, 0, 1, C.ALGO_MFMA) == C.E_UNSUPPORTED
 
 
 def test_is_supported_matches_fwd_checks():

@@ -402,6 +402,26 @@ def test_c2_full_size_sampled(name, algo):
     assert_within(m, activated=True)
 
 
+@pytest.mark.parametrize("algo", [C.ALGO_SIMT, C.ALGO_MFMA])
+def test_2d_largest_image_sampled(algo):
+    """The largest 2D image the matrix-core kernel takes: 64 channels of 4096 x 4088 fp16, just
+    below 2 GiB per image of x and of y (one 32-bit buffer range each), three images so that the
+    last one's addresses cross 4 GiB.  Sampled outputs of every image against the oracle; the
+    SIMT kernel on the same input."""
+    wl = dataclasses.replace(si.WORKLOADS["c2"], N=3, H=4096, W=4088)
+    assert wl.C_in * wl.H * wl.W * 2 < 1 << 31 < 2 * wl.C_in * wl.H * wl.W * 2
+    _say("largest 2D image: %s algo %d" % ((wl.N, wl.C_in, wl.C_out, wl.H, wl.W), algo))
+    x, w, b = si.make_inputs(wl, device=DEV)
+    y = run_2d(x, w, b, wl.stride, wl.epilogue, guarded=True, algo=algo)
+    pts = sample_points_2d(wl.N, wl.H_out, wl.W_out, 150, seed=5)
+    pts = np.concatenate([pts, np.array([[1, 0, 0], [1, wl.H - 1, wl.W - 1]], np.int32)])
+    ref = oracle.conv2d_points(bits(x), bits(w), bits(b), pts, wl.stride, oracle.F16,
+                               oracle.EPI_RELU, oracle.CHANNELS_FIRST)
+    m = metrics(gather_2d(y, pts), ref, x.dtype)
+    _say("largest 2D image algo=%d sampled %d %s" % (algo, len(pts), m))
+    assert_within(m, activated=True)
+
+
 @pytest.mark.parametrize("name,algo", [("c3", C.ALGO_MFMA), ("c3", C.ALGO_SPLIT_HEAD),
                                        ("c3", C.ALGO_FUSED_HEAD),
                                        ("c4", C.ALGO_MFMA), ("c5", C.ALGO_MFMA),
