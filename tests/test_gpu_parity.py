@@ -445,12 +445,13 @@ def test_3d_full_size_sampled(name, algo):
 
 
 @pytest.mark.parametrize("name,D,algo", [("c3", 32, C.ALGO_FUSED_HEAD), ("c3", 32, C.ALGO_SPLIT_HEAD),
-                                         ("c4", 160, C.ALGO_MFMA)])
+                                         ("c3", 32, C.ALGO_MFMA), ("c4", 160, C.ALGO_MFMA)])
 def test_3d_beyond_32bit_offsets(name, D, algo):
     """Inputs past 32-bit byte offsets: the output head over 32 frames (3.6 GB of input, on the
     head kernels, which address each workgroup's six input and four output frames through their
-    own 32-bit ranges) and the mid-decoder conv over 160 frames (4.5 GB in and out).  Sampled
-    outputs in the first, middle and last frames against the oracle."""
+    own 32-bit ranges, and on the direct 27-tap kernel, which addresses ten input rows at a time)
+    and the mid-decoder conv over 160 frames (4.5 GB in and out).  Sampled outputs in the first,
+    middle and last frames against the oracle."""
     wl = dataclasses.replace(si.WORKLOADS[name], D=D)
     _say("beyond 32-bit offsets: %s D=%d algo %d" % (name, D, algo))
     auto = C.conv3x3x3_select_algo(wl.N, wl.C_in, wl.C_out, wl.D, wl.H, wl.W, 1,
