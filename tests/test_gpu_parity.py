@@ -236,7 +236,8 @@ def test_conv3d_kq_integer_exact(case):
 # between workgroups is summed from fp32 partials by the piece that ends last, in K order.  Both
 # 128-position tiles, part-empty second 256-row tiles (300 and 384 channels: padding waves compute
 # zeros and store nothing), 184 to 256 workgroups, three to five frames, fp16, and the low-res
-# 512 -> 512 convolution itself.
+# 512 -> 512 convolution itself.  Tiles split in two (the one-burst sum) in every case, and in
+# three (the general K-order sum) in the first, third and fourth (16 to 24 such tiles each).
 CASES_SK = [
     # N, Ci, Co, D, H, W, dtype, epilogue, tile
     (1, 416, 384, 5, 44, 33, "bf16", "relu", "4x32"),
