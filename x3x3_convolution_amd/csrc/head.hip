@@ -127,6 +127,12 @@ __device__ __forceinline__ float opaque_zero() {
 __device__ __forceinline__ void lane_swap16(float &a, float &b) {
     asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
 }
+// v_permlane32_swap of one register pair: lanes 32..63 of a trade places with lanes 0..31 of b
+// (so with a = b = v, lane l of b (l < 32) and of a (l >= 32) holds v of lane l ^ 32).  Written
+// out like lane_swap16.
+__device__ __forceinline__ void lane_swap32(uint32_t &a, uint32_t &b) {
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
 // n mod 3 in 0..2 for any int n
 __device__ __forceinline__ int mod3(int n) { return ((n % 3) + 3) % 3; }
 // a + b saturated at 2^32 - 1 (one VALU instruction: the add's clamp bit); b uniform.  An
@@ -568,9 +574,11 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
 #pragma unroll
                         for (int c = 0; c < kHalfCo; ++c) q[c] = rgb_code(E::to_f32(r6[c]));
                         // half 0 lacks blue of row 2h (channels 8, 9), half 1 red of row 2h+1
-                        // (channels 2, 3): local channels 2 and 3 of the other half
-                        const uint32_t recv = (uint32_t)__builtin_amdgcn_ds_bpermute(
-                            (lane ^ 32) << 2, (int)(q[2] | (q[3] << 8)));
+                        // (channels 2, 3): local channels 2 and 3 of the other half, taken from
+                        // lane l ^ 32 by one lane swap (a VALU instruction, no LDS round trip)
+                        uint32_t sa = q[2] | (q[3] << 8), sb = sa;
+                        lane_swap32(sa, sb);
+                        const uint32_t recv = hh ? sa : sb;
                         const uint32_t r0 = recv & 0xFFu, r1 = (recv >> 8) & 0xFFu;
                         // bytes R G B R G B of pixels (2h + hh, 2w) and (2h + hh, 2w + 1)
                         const uint32_t p01 = hh == 0 ? (q[0] | (q[4] << 8)) : (r0 | (q[0] << 8));
@@ -578,11 +586,14 @@ __global__ __launch_bounds__(256, 1) void head_gemm_kernel(HeadGemmKArgs a) {
                         const uint32_t p45 = hh == 0 ? (q[5] | (r1 << 8)) : (q[1] | (q[5] << 8));
                         const uint32_t roff =
                             st_ok ? (uint32_t)(((wave * 2 * a.H + 2 * ho + hh) * 2 * a.W + 2 * w) * 3) : kOff;
-                        __builtin_amdgcn_raw_buffer_store_b16((u16)p01, yr, roff, 0, 0);
-                        __builtin_amdgcn_raw_buffer_store_b16((u16)p23, yr,
-                                                              __builtin_elementwise_add_sat(roff, 2u), 0, 0);
-                        __builtin_amdgcn_raw_buffer_store_b16((u16)p45, yr,
-                                                              __builtin_elementwise_add_sat(roff, 4u), 0, 0);
+                        // the six bytes as one 4-byte and one 2-byte store: 4 + 2 where the run
+                        // starts 4-byte aligned, else 2 + 4 (a store that must not happen keeps
+                        // an offset past the range)
+                        const bool al = (roff & 3u) == 0;
+                        __builtin_amdgcn_raw_buffer_store_b32(al ? (p01 | (p23 << 16)) : (p23 | (p45 << 16)), yr,
+                                                              al ? roff : __builtin_elementwise_add_sat(roff, 2u), 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b16((u16)(al ? p45 : p01), yr,
+                                                              al ? __builtin_elementwise_add_sat(roff, 4u) : roff, 0, 0);
                     } else if constexpr (CO12) {
                         typedef uint32_t v3u __attribute__((ext_vector_type(3)));
                         const v3u v = {(uint32_t)r6[0] | ((uint32_t)r6[1] << 16),
