@@ -602,7 +602,8 @@ int conv3x3x3_head_rgb8(const void *x, const void *w_packed, const void *bias, v
 // ---- allocation-free forward pass -------------------------------------------------------------
 // A static device array serves as the workspace of conv3x3x3_fwd_noalloc, so that callers that
 // cannot allocate (graph capture, serving loops) still reach the algorithms that need one (the
-// split-K partial sums of the MFMA path, the split head's plane when it fits).  Each GPU the
+// MFMA path's split-K partial sums and its stream-K partial tiles and arrival counters, which a
+// kernel clears at every call; the split head's plane when it fits).  Each GPU the
 // library runs on holds its own copy of the array until the process ends.  In host code the
 // array's name is only a stand-in: its device address is looked up once per device
 // (hipGetSymbolAddress, with that device current) and only that address is passed to kernels.
