@@ -16,7 +16,8 @@ The default line also carries:
     low-res 3D convolutions), each timed with the same protocol, with its roofline fraction and
     its parity against the oracle (every output; a seeded sample of the mid-decoder conv);
   * calibration: a plain 1 GiB device copy and a loop of nothing but matrix-core instructions,
-    what this machine's HBM and matrix cores sustain (context beside the published peaks).
+    what this machine's HBM and matrix cores sustain (context beside the published peaks),
+    and the time of a launch that does almost nothing (the floor of any one-launch figure).
 
 Prints one JSON line (see --help).  `--workload` times another of the synthetic workloads with
 the same protocol (for measurements outside the default line).
@@ -136,7 +137,8 @@ def mfma_calibration(stream):
     """The rate of a loop of nothing but bf16 32x32x16 MFMAs on register operands (one wave per
     SIMD on every CU), timed with HIP events on the launch stream: what this machine's matrix
     cores sustain under a pure matrix-core load, clock and power included.  A calibration beside
-    the published peak, not a denominator."""
+    the published peak, not a denominator.  The same kernel with one pass of its loop, on one
+    and on 240 workgroups, gives the time of a launch with almost no work."""
     import torch
     from x3x3_convolution_amd import conv as C
     wgs, iters = 256 * 8, 2000
@@ -153,8 +155,21 @@ def mfma_calibration(stream):
     ms = tm.stats("mfma")["median"]
     flop = wgs * 4.0 * iters * 8 * 2 * 32 * 32 * 16
     tf = flop / (ms * 1e-3) / 1e12
-    return {"mfma_loop_flop": flop, "mfma_loop_ms": ms, "mfma_loop_tflops": round(tf, 1),
-            "mfma_loop_frac_of_peak": round(tf / MFMA_BF16_PEAK_TFS, 4)}
+    floor = {}
+    for w in (1, 240):
+        # the same kernel with one pass of its loop: what one launch costs with (almost) no work,
+        # timed like the workloads (back to back, HIP events on the launch stream)
+        for _ in range(3):
+            C.conv_calib_mfma_bf16(out, w, 1, stream)
+        torch.cuda.synchronize()
+        for _ in range(20):
+            s0 = tm.start()
+            C.conv_calib_mfma_bf16(out, w, 1, stream)
+            tm.stop(f"floor{w}", s0)
+        torch.cuda.synchronize()
+        floor[f"launch_floor_ms_{w}wg"] = round(tm.stats(f"floor{w}")["median"], 5)
+    return dict({"mfma_loop_flop": flop, "mfma_loop_ms": ms, "mfma_loop_tflops": round(tf, 1),
+                 "mfma_loop_frac_of_peak": round(tf / MFMA_BF16_PEAK_TFS, 4)}, **floor)
 
 
 def lds_dma_calibration(stream):
