@@ -132,6 +132,12 @@ CASES_3D_INT = [
     # the production channel count (C_in 256) in more shapes: fp16, two frame groups (the second
     # part-empty) over two strips; C_out 7 on two samples; ranges that cross strips; a single
     # position
+    # long K: the head's stages over 16 chunks per Z row; K split 32 and 64 ways (one chunk per
+    # split, the reduce over that many partials)
+    (1, 512, 12, 3, 9, 130, "bf16", "clamp1", C.ALGO_FUSED_HEAD),
+    (1, 512, 12, 3, 9, 130, "bf16", "clamp1", C.ALGO_SPLIT_HEAD),
+    (1, 1024, 40, 2, 5, 9, "bf16", "relu", C.ALGO_MFMA),
+    (1, 2048, 64, 1, 8, 16, "f16", "none", C.ALGO_MFMA),
     (1, 256, 12, 5, 13, 140, "f16", "relu", C.ALGO_FUSED_HEAD),
     (1, 256, 12, 5, 13, 140, "f16", "relu", C.ALGO_SPLIT_HEAD),
     (2, 256, 7, 4, 10, 60, "bf16", "none", C.ALGO_FUSED_HEAD),
