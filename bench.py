@@ -7,7 +7,9 @@ activations and N(0, 1/(27*256)) weights (no trained weights or real latents exi
 step is one head pass, computed by the algorithm AUTO selects; the three head algorithms -- the
 direct 27-tap MFMA implicit GEMM, the split head (3x1x1 temporal conv into a 112-channel plane,
 then the nine-tap stencil) and the fused head -- are timed and reported.  Inputs are resident in
-HBM before the timed region; each step's launches run back to back on one stream.
+HBM before the timed region; each step's launches run back to back on one stream.  Every timed
+region follows untimed warm-up steps -- at least --warmup of them and at least --settle-ms of
+them -- so the chip's clock has settled under that load before the timing starts.
 
 The default line also carries:
   * cpu_baseline: the oracle timed over one whole head pass on the host cores, and one thread
@@ -48,6 +50,25 @@ KERNEL_SOURCES = {             # dominant-kernel name -> the source file it is b
 }
 
 
+def warm_up(step, args):
+    """Untimed steps before a timed region: at least args.warmup of them, in doubling batches
+    until at least args.settle_ms of wall time has passed.  After an idle spell (another
+    workload's oracle check, the process start) the chip's clock under a new load takes tens of
+    ms to settle -- per-launch times first rise, then fall below where they started -- so a
+    fixed handful of steps would time the transient instead of the sustained rate.  Returns the
+    number of steps run."""
+    import torch
+    n, batch = 0, max(1, args.warmup)
+    t0 = time.perf_counter()
+    while n < args.warmup or (time.perf_counter() - t0) * 1e3 < args.settle_ms:
+        for _ in range(batch):
+            step()
+        n += batch
+        batch *= 2
+        torch.cuda.synchronize()
+    return n
+
+
 def live_taps(n, stride=1):
     """Sum over output coordinates of the taps that land inside a pad-1 3-tap dimension."""
     nout = (n - 1) // stride + 1
@@ -77,6 +98,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="keep warming up (past --warmup steps) until this many ms of untimed "
+                         "launches have run: after an idle spell the clock under a new load goes "
+                         "through a transient of up to ~100 ms before it settles")
     ap.add_argument("--workload", default="c3",
                     choices=["c3", "c4", "c5", "c5d1", "c1", "c2", "c2s2"])
     ap.add_argument("--algo", default="auto", choices=["auto", "mfma", "split", "fused"],
@@ -323,9 +348,7 @@ def run_head(args, wl, stream):
                 op(x, y, stream=stream)
                 if tm:
                     tm.stop(kname, s0)
-        for _ in range(args.warmup):
-            step()
-        torch.cuda.synchronize()
+        nwarm = warm_up(step, args)
         tm = Timer(torch.cuda.current_stream())
         t0 = time.perf_counter()
         for _ in range(args.steps):
@@ -334,7 +357,7 @@ def run_head(args, wl, stream):
         wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
         k = tm.summary()
         results[name] = dict(ms_per_pass=wall_ms, kernel_ms=k, weight_pack_ms=pack_ms,
-                             kernel_stats={kk: tm.stats(kk) for kk in k})
+                             kernel_stats={kk: tm.stats(kk) for kk in k}, warmup_steps=nwarm)
         del op
         torch.cuda.empty_cache()
 
@@ -379,9 +402,8 @@ def run_head(args, wl, stream):
     video = None
     if wl.C_out == 12 and args.algo == "auto":
         rgb = torch.empty((wl.N, wl.D, 2 * wl.H, 2 * wl.W, 3), dtype=torch.uint8, device="cuda")
-        for _ in range(args.warmup):
-            C.conv_video_rgb8(y, rgb, wl.N, wl.D, wl.H, wl.W, 12, C.DTYPE_BF16, stream)
-        torch.cuda.synchronize()
+        warm_up(lambda: C.conv_video_rgb8(y, rgb, wl.N, wl.D, wl.H, wl.W, 12, C.DTYPE_BF16,
+                                          stream), args)
         tm = Timer(torch.cuda.current_stream())
         for _ in range(args.steps):
             s0 = tm.start()
@@ -397,9 +419,7 @@ def run_head(args, wl, stream):
         # the fused head writing the RGB frames straight from its registers (no y round trip)
         opf = Conv3x3x3(w, b, wl.N, wl.D, wl.H, wl.W, epilogue=wl.epilogue,
                         algo=C.ALGO_FUSED_HEAD)
-        for _ in range(args.warmup):
-            opf.rgb8(x, rgb, stream=stream)
-        torch.cuda.synchronize()
+        warm_up(lambda: opf.rgb8(x, rgb, stream=stream), args)
         tm = Timer(torch.cuda.current_stream())
         for _ in range(args.steps):
             s0 = tm.start()
@@ -416,7 +436,8 @@ def run_head(args, wl, stream):
         / (pass_ms * 1e-3) / 1e9,
         algos={k: dict(ms_per_pass=round(v["ms_per_pass"], 4),
                        kernel_ms={kk: round(vv, 4) for kk, vv in v["kernel_ms"].items()},
-                       weight_pack_ms=round(v["weight_pack_ms"], 4))
+                       weight_pack_ms=round(v["weight_pack_ms"], 4),
+                       warmup_steps=v["warmup_steps"])
                for k, v in results.items()})
     if video is not None:
         extra["video_step"] = video
@@ -565,8 +586,7 @@ def run_other(args, wl, stream):
         kname, bound, peak, unit = "igemm3d", "mfma", MFMA_BF16_PEAK_TFS, "TFLOP/s"
     y = torch.empty(op.out_shape(), dtype=wl.torch_dtype, device="cuda")
     nbytes = (x.numel() + y.numel() + w.numel() + b.numel()) * 2
-    for _ in range(args.warmup):
-        op(x, y, stream=stream)
+    nwarm = warm_up(lambda: op(x, y, stream=stream), args)
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if args.flush else None
     torch.cuda.synchronize()
     tm = Timer(torch.cuda.current_stream())
@@ -589,6 +609,7 @@ def run_other(args, wl, stream):
     roof = dict(kernel=kname, bound=bound, achieved=ach, peak=peak, unit=unit, frac=ach / peak,
                 hbm_gbs=gbs, hbm_frac=gbs / HBM_PEAK_GBS, algorithmic_flop=flop,
                 algorithmic_bytes=nbytes, avg_launch_ms=kms, launch_ms_stats=kstats, positions=P,
+                warmup_steps=nwarm,
                 traffic=traffic_from_profiles(
                     kname, wl.name, "nhwc" if args.channels_last else
                     ("stride2" if wl.kind == "3d" and args.stride3d == 2 else "auto")))
@@ -628,7 +649,8 @@ def run_workloads(args, stream):
                    unit=roof["unit"], frac=round(roof["frac"], 4),
                    hbm_gbs=round(roof["hbm_gbs"], 1), hbm_frac=round(roof["hbm_frac"], 4),
                    algorithmic_flop=roof["algorithmic_flop"],
-                   algorithmic_bytes=roof["algorithmic_bytes"])
+                   algorithmic_bytes=roof["algorithmic_bytes"],
+                   warmup_steps=roof["warmup_steps"])
         if "mfma_tflops" in roof:
             ent["mfma_tflops"] = round(roof["mfma_tflops"], 1)
             ent["mfma_frac"] = round(roof["mfma_tflops"] / MFMA_BF16_PEAK_TFS, 4)
@@ -684,9 +706,7 @@ def run_region(args, wl, stream):
 
     def call():
         op.region(x, D_in, H_in, d_org, h_org, d_lo, d_hi, h_lo, h_hi, y=y, stream=stream)
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
+    warm_up(call, args)
     tm = Timer(torch.cuda.current_stream())
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -736,6 +756,7 @@ def main():
         return
     wl = si.WORKLOADS[args.workload]
     line = dict(metric=METRIC, n_gpus=1, steps=args.steps, warmup=args.warmup,
+                warmup_settle_ms=args.settle_ms,
                 higher_is_better=False, scaling="weak", vs_baseline=None, dtype=wl.dtype,
                 data="synthetic (seeded; no trained weights or real activations)")
     if args.region != "none":
