@@ -27,6 +27,7 @@ the same protocol (for measurements outside the default line).
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -48,6 +49,21 @@ KERNEL_SOURCES = {             # dominant-kernel name -> the source file it is b
     "mfma2d": "x3x3_convolution_amd/csrc/mfma2d.hip",
     "video_rgb8": "x3x3_convolution_amd/csrc/video.hip",
 }
+
+
+class no_gc:
+    """Python's cyclic garbage collector off for a timed region, after a collection just before
+    it: a full collection inside a short timed loop costs tens of ms of host time, which the wall
+    time per step would otherwise carry."""
+
+    def __enter__(self):
+        gc.collect()
+        gc.disable()
+        return self
+
+    def __exit__(self, *exc):
+        gc.enable()
+        return False
 
 
 def warm_up(step, args):
@@ -350,11 +366,12 @@ def run_head(args, wl, stream):
                     tm.stop(kname, s0)
         nwarm = warm_up(step, args)
         tm = Timer(torch.cuda.current_stream())
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            step(tm)
-        torch.cuda.synchronize()
-        wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        with no_gc():
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                step(tm)
+            torch.cuda.synchronize()
+            wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
         k = tm.summary()
         results[name] = dict(ms_per_pass=wall_ms, kernel_ms=k, weight_pack_ms=pack_ms,
                              kernel_stats={kk: tm.stats(kk) for kk in k}, warmup_steps=nwarm)
@@ -590,15 +607,16 @@ def run_other(args, wl, stream):
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if args.flush else None
     torch.cuda.synchronize()
     tm = Timer(torch.cuda.current_stream())
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        if scratch is not None:
-            scratch.fill_(1)
-        s = tm.start()
-        op(x, y, stream=stream)
-        tm.stop(kname, s)
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    with no_gc():
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            if scratch is not None:
+                scratch.fill_(1)
+            s = tm.start()
+            op(x, y, stream=stream)
+            tm.stop(kname, s)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     kms = tm.summary()[kname]
     kstats = tm.stats(kname)
     if scratch is not None:
@@ -688,10 +706,13 @@ def run_region(args, wl, stream):
     from x3x3_convolution_amd.plan import Conv3x3x3
 
     D_in, H_in, d_org, h_org, d_lo, d_hi, h_lo, h_hi, D, H, lo = region_of(args.region, wl.D, wl.H)
-    _, w, b = si.make_inputs(wl, device="cpu")
-    w, b = w.cuda(), b.cuda()
-    g = torch.Generator("cpu").manual_seed(si.SEED_BASE + 7)
-    x = torch.randn((wl.N, D_in, H_in, wl.W, wl.C_in), generator=g).to(wl.torch_dtype).cuda()
+    # drawn on the GPU: a multi-threaded draw of this size on the host runs the process into its
+    # CPU quota, and the throttling that follows lands in the timed steps
+    _, w, b = si.make_inputs(wl, device="cuda")
+    torch.cuda.empty_cache()
+    g = torch.Generator("cuda").manual_seed(si.SEED_BASE + 7)
+    x = torch.randn((wl.N, D_in, H_in, wl.W, wl.C_in), generator=g, device="cuda",
+                    dtype=torch.float32).to(wl.torch_dtype)
     algo = {"auto": C.ALGO_AUTO, "mfma": C.ALGO_MFMA, "split": C.ALGO_SPLIT_HEAD,
             "fused": C.ALGO_FUSED_HEAD}[args.algo]
     op = Conv3x3x3(w, b, wl.N, D, H, wl.W, epilogue=wl.epilogue, algo=algo)
@@ -708,13 +729,14 @@ def run_region(args, wl, stream):
         op.region(x, D_in, H_in, d_org, h_org, d_lo, d_hi, h_lo, h_hi, y=y, stream=stream)
     warm_up(call, args)
     tm = Timer(torch.cuda.current_stream())
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        s0 = tm.start()
-        call()
-        tm.stop(kname, s0)
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    with no_gc():
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            s0 = tm.start()
+            call()
+            tm.stop(kname, s0)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     kms = tm.summary()[kname]
     tflops, gbs = flop / (kms * 1e-3) / 1e12, nbytes / (kms * 1e-3) / 1e9
     if kname == "igemm3d":
