@@ -52,12 +52,12 @@ KERNEL_SOURCES = {             # dominant-kernel name -> the source file it is b
 
 
 class no_gc:
-    """Python's cyclic garbage collector off for a timed region, after a collection just before
-    it: a full collection inside a short timed loop costs tens of ms of host time, which the wall
-    time per step would otherwise carry."""
+    """Python's cyclic garbage collector off for a timed region: a full collection costs tens of
+    ms of host time, which the wall time per step would otherwise carry.  No collection runs at
+    the start either: the GPU would sit idle meanwhile, and after an idle spell of that length
+    the clock goes through its transient again, right in the timed steps."""
 
     def __enter__(self):
-        gc.collect()
         gc.disable()
         return self
 
